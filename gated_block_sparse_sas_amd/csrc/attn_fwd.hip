@@ -1,0 +1,256 @@
+// attn_fwd.hip -- dense-active gated causal attention forward (training).
+//
+// For query t (block c = t/64) and key u <= t:
+//   logit = sm_scale <q_t, k_u> + beta_{t, u/64},
+//   beta_{t,j} = sel_scale <qs_t, ks_j> - lam_t  (j < c),   beta_{t,c} = 0,
+//   o_t = softmax_u(logit) v,   lse_t = log sum_u exp(logit).
+// SAS abstracts (NeurIPS poster page, Hugging Face page): the gate enters the
+// attention softmax in log form, every context unit stays active in training,
+// the current block is always retained; the authors fuse it into a
+// FlashAttention-style kernel so the T x T matrix is never materialised.
+//
+// gfx950 design (bf16 in, fp32 accumulate):
+//  * workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
+//    32 consecutive rows.  Key tiles are 64 keys = one gate block, so the gate
+//    bias is a single scalar per (row, tile).
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the accumulator puts one query
+//    per lane (column) and 16 keys per 32-key M-tile in registers, so the
+//    row max / row sum are in-lane, plus one exchange between the two
+//    32-lane halves.  Q stays in registers as the B operand for the whole
+//    kernel.
+//  * O^T = V^T P^T: P never leaves registers.  The B-operand k slots of a lane
+//    are exactly the keys its S^T accumulator holds (two runs of 4), and the
+//    V^T operand is read from LDS with the same key order.
+//  * LDS: K tile row-major [64][d+8], V tile transposed [d][64+8] (padding
+//    keeps the 16-byte and 8-byte operand reads bank-conflict free).  The next
+//    tile's global loads are issued before the current tile's MFMAs.
+//  * the gate bias of (row, tile) is recomputed in-kernel: the lane's half of
+//    qs (ds/2 values in registers) times the wave-uniform ks row, one
+//    cross-half add; lam comes from the gate kernel.
+//  * exp2 domain throughout; tiles past a wave's last block are skipped, the
+//    only masked tiles are the (at most two) diagonal ones.
+#include "sas_device.h"
+#include "sas_internal.h"
+
+namespace sas {
+
+template <int HD, int DS>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
+    bf16* __restrict__ o, float* __restrict__ lse, Dims D, int nqt, int xcd_groups) {
+  constexpr int KP = HD + 8;       // padded K row (elements)
+  constexpr int VP = kBlock + 8;   // padded V^T row
+  constexpr int KS = HD / 16;      // k-steps over the head dim
+  constexpr int DM = HD / 32;      // 32-row M-tiles of O^T
+  constexpr int KCH = kBlock * HD / 8 / 256;  // 16-byte K chunks per thread
+  constexpr int VITEMS = 16 * (HD / 8);       // (4 keys x 8 dims) V items
+  constexpr int VIT = (VITEMS + 255) / 256;
+  __shared__ __align__(16) bf16 Ks[kBlock * KP];
+  __shared__ __align__(16) bf16 Vt[HD * VP];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const QTile tm = map_q_tile(blockIdx.x, nqt, D, xcd_groups);
+  const int b = tm.b, h = tm.h, qt = tm.qt;
+  const int g = h / D.hpg, sh = h / D.hps;
+  const int wq0 = qt * 128 + wave * 32;
+  const int qi = wq0 + l32;
+  const int qc = min(qi, D.tq - 1);
+  const int t = D.qoff + qc;
+  const int c = t / kBlock;
+  const int c_lo = (D.qoff + min(wq0, D.tq - 1)) / kBlock;
+  const int c_hi = (D.qoff + min(wq0 + 31, D.tq - 1)) / kBlock;
+  const int c_end = (D.qoff + min(qt * 128 + 127, D.tq - 1)) / kBlock;
+
+  const size_t qrow = ((size_t)b * D.hq + h) * D.tq + qc;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(q + qrow * HD + 16 * s + 8 * hh);
+  float qsv[DS / 2];
+#pragma unroll
+  for (int e = 0; e < DS / 2; ++e) qsv[e] = to_f32(qs[qrow * DS + hh * (DS / 2) + e]);
+  const float lam_t = c > 0 ? lam[qrow] : 0.f;
+  const bf16* ksb = ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS + hh * (DS / 2);
+  const bf16* kb = k + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
+  const bf16* vb = v + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
+  const float c1 = D.sm_scale * kLog2e;
+
+  f32x16 oacc[DM];
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const bf16x8 zero8 = bf16x8{};
+  bf16x8 kreg[KCH];
+  bf16x8 vreg[VIT][4];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int x = 0; x < KCH; ++x) {
+      const int id = tid + 256 * x, r = id / (HD / 8), cc = id % (HD / 8);
+      const int key = j * kBlock + r;
+      kreg[x] = key < D.tk ? *(const bf16x8*)(kb + (size_t)key * HD + cc * 8) : zero8;
+    }
+#pragma unroll
+    for (int x = 0; x < VIT; ++x) {
+      const int id = tid + 256 * x;
+      if (id < VITEMS) {
+        const int kg = id % 16, dc = id / 16;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const int key = j * kBlock + kg * 4 + i2;
+          vreg[x][i2] = key < D.tk ? *(const bf16x8*)(vb + (size_t)key * HD + dc * 8) : zero8;
+        }
+      }
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int x = 0; x < KCH; ++x) {
+      const int id = tid + 256 * x, r = id / (HD / 8), cc = id % (HD / 8);
+      *(bf16x8*)&Ks[r * KP + cc * 8] = kreg[x];
+    }
+#pragma unroll
+    for (int x = 0; x < VIT; ++x) {
+      const int id = tid + 256 * x;
+      if (id < VITEMS) {
+        const int kg = id % 16, dc = id / 16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16x4 w = {vreg[x][0][e], vreg[x][1][e], vreg[x][2][e], vreg[x][3][e]};
+          *(bf16x4*)&Vt[(dc * 8 + e) * VP + kg * 4] = w;
+        }
+      }
+    }
+  };
+
+  gload(0);
+  for (int j = 0; j <= c_end; ++j) {
+    __syncthreads();
+    sstore();
+    __syncthreads();
+    if (j < c_end) gload(j + 1);
+    if (j > c_hi) continue;  // past this wave's last block
+
+    // log2-domain gate bias of this lane's row for block j
+    float bias2 = 0.f;
+    if (j < c_hi) {
+      const bf16* kr = ksb + (size_t)j * DS;
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS / 2; ++e) part = fmaf(qsv[e], to_f32(kr[e]), part);
+      part += __shfl_xor(part, 32);
+      if (j < c) bias2 = (D.sel_scale * part - lam_t) * kLog2e;
+    }
+
+    // S^T tile: two 32-key M-tiles x 32 queries
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 a = *(const bf16x8*)&Ks[(32 * mt + l32) * KP + 16 * s + 8 * hh];
+        sacc[mt] = mfma32(a, qf[s], sacc[mt]);
+      }
+    }
+    const bool nomask = j < c_lo;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = fmaf(sacc[mt][r], c1, bias2);
+        if (!nomask) {
+          const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
+          if (u > t) x = -INFINITY;
+        }
+        sacc[mt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(sacc[mt][r] - m_new);
+        sacc[mt][r] = p;
+        psum += p;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (bf16)sacc[mt][8 * pp + e];
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) {
+          const bf16* vp = &Vt[(32 * dm + l32) * VP + 32 * mt + 16 * pp + 4 * hh];
+          const bf16x4 lo = *(const bf16x4*)vp;
+          const bf16x4 hi = *(const bf16x4*)(vp + 8);
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[dm] = mfma32(a, pb, oacc[dm]);
+        }
+      }
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 32);
+  if (qi < D.tq) {
+    const float inv = 1.f / l_run;
+    bf16* orow = o + qrow * HD;
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(oacc[dm][4 * rr + e] * inv);
+        *(bf16x4*)(orow + 32 * dm + 8 * rr + 4 * hh) = w;
+      }
+    }
+    if (hh == 0) lse[qrow] = (m_run + log2f(l_run)) * kLn2;
+  }
+}
+
+template <int HD, int DS>
+static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const void* qs,
+                               const void* ks, const float* lam, void* o, float* lse,
+                               const Dims& D, hipStream_t st) {
+  const int nqt = (D.tq + 127) / 128;
+  const int groups = D.batch * D.hkv;
+  const int xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
+  const unsigned grid = (unsigned)(D.batch * D.hq * nqt);
+  hipLaunchKernelGGL((attn_fwd_kernel<HD, DS>), dim3(grid), dim3(256), 0, st, (const bf16*)q,
+                     (const bf16*)k, (const bf16*)v, (const bf16*)qs, (const bf16*)ks, lam,
+                     (bf16*)o, lse, D, nqt, xcd_groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const void* qs,
+                           const void* ks, const float* lam, void* o, float* lse, const Dims& D,
+                           hipStream_t st) {
+#define SAS_FWD_CASE(HDV, DSV) \
+  if (D.d == HDV && D.ds == DSV) return launch_fwd_t<HDV, DSV>(q, k, v, qs, ks, lam, o, lse, D, st);
+  SAS_FWD_CASE(128, 32)
+  SAS_FWD_CASE(128, 16)
+  SAS_FWD_CASE(128, 64)
+  SAS_FWD_CASE(64, 32)
+  SAS_FWD_CASE(64, 16)
+  SAS_FWD_CASE(64, 64)
+#undef SAS_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sas

@@ -1,0 +1,119 @@
+// gate.hip -- selector scores and the gate normaliser (training step 1).
+//
+// z[t,j] = sel_scale * <qs[t], ks[j]> for the historical blocks j < c(t);
+// lam[t] = log sum_j exp z[t,j]; optionally beta[t,j] = z - lam (j < c),
+// 0 (j = c), -inf (j > c).  SAS paper abstracts (NeurIPS poster page,
+// Hugging Face page): the gate is a softmax over the historical blocks and its
+// log enters the attention logits; the current block is always retained.
+//
+// Layout: one lane per query row.  Rows of a wave are consecutive positions,
+// so the block index j is uniform across the wave and every ks row is a
+// wave-uniform (scalar-cache) load.  HBM traffic is one qs row in and one
+// float out per query row; ks (<= a few hundred KB) stays in cache.
+#include "sas_device.h"
+#include "sas_internal.h"
+
+namespace sas {
+
+template <int DS, typename ST>
+__global__ __launch_bounds__(256) void gate_lse_kernel(const ST* __restrict__ qs,
+                                                       const ST* __restrict__ ks,
+                                                       float* __restrict__ lam, Dims D) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int wave_first = blockIdx.x * 256 + (threadIdx.x & ~63);
+  if (wave_first >= D.tq) return;  // whole wave past the end
+  const int ic = i < D.tq ? i : D.tq - 1;
+  const int c = (D.qoff + ic) / kBlock;
+  const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / kBlock;  // wave max of c
+  const size_t row = ((size_t)b * D.hq + h) * D.tq + ic;
+  float qsv[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
+  const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
+  const float zs = D.sel_scale * kLog2e;  // scores kept in log2 units
+  float m = -INFINITY, s = 0.f;
+  for (int j0 = 0; j0 < cw; j0 += 8) {
+    float zz[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = j0 + k;
+      zz[k] = -INFINITY;
+      if (j < cw) {
+        const float z = zs * sel_dot<DS>(qsv, ksb + (size_t)j * DS);
+        if (j < c) zz[k] = z;
+      }
+    }
+    float mc = zz[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mc = fmaxf(mc, zz[k]);
+    const float mn = fmaxf(m, mc);
+    if (mn == -INFINITY) continue;
+    float acc = s * exp2f(m - mn);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += exp2f(zz[k] - mn);
+    s = acc;
+    m = mn;
+  }
+  if (i < D.tq) lam[row] = c == 0 ? -INFINITY : (m + log2f(s)) * kLn2;
+}
+
+// beta[t, j] for every (row, j): one thread per entry, rows along blockIdx.y.
+template <int DS, typename ST>
+__global__ __launch_bounds__(256) void gate_bias_kernel(const ST* __restrict__ qs,
+                                                        const ST* __restrict__ ks,
+                                                        const float* __restrict__ lam,
+                                                        float* __restrict__ beta, Dims D) {
+  const size_t row = blockIdx.y + (size_t)gridDim.y * blockIdx.z;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (row >= (size_t)D.batch * D.hq * D.tq || j >= D.nb) return;
+  const int i = (int)(row % D.tq);
+  const int h = (int)((row / D.tq) % D.hq);
+  const int b = (int)(row / ((size_t)D.tq * D.hq));
+  const int c = (D.qoff + i) / kBlock;
+  float out;
+  if (j < c) {
+    float qsv[DS];
+#pragma unroll
+    for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
+    const ST* ksr = ks + (((size_t)b * D.hks + h / D.hps) * D.nb + j) * DS;
+    out = D.sel_scale * sel_dot<DS>(qsv, ksr) - lam[row];
+  } else {
+    out = j == c ? 0.f : -INFINITY;
+  }
+  beta[row * D.nb + j] = out;
+}
+
+template <int DS, typename ST>
+static hipError_t launch_gate_t(const void* qs, const void* ks, float* lam, float* beta,
+                                const Dims& D, hipStream_t st) {
+  dim3 grid((D.tq + 255) / 256, D.hq, D.batch);
+  hipLaunchKernelGGL((gate_lse_kernel<DS, ST>), grid, dim3(256), 0, st, (const ST*)qs,
+                     (const ST*)ks, lam, D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !beta) return e;
+  const size_t rows = (size_t)D.batch * D.hq * D.tq;
+  const unsigned gy = rows < 65535 ? (unsigned)rows : 65535u;
+  const unsigned gz = (unsigned)((rows + gy - 1) / gy);
+  dim3 g2((D.nb + 255) / 256, gy, gz);
+  hipLaunchKernelGGL((gate_bias_kernel<DS, ST>), g2, dim3(256), 0, st, (const ST*)qs,
+                     (const ST*)ks, (const float*)lam, beta, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate(const void* qs, const void* ks, float* lam, float* beta, const Dims& D,
+                       bool sel_bf16, hipStream_t st) {
+#define SAS_GATE_CASE(DSV)                                                      \
+  case DSV:                                                                     \
+    return sel_bf16 ? launch_gate_t<DSV, bf16>(qs, ks, lam, beta, D, st)        \
+                    : launch_gate_t<DSV, float>(qs, ks, lam, beta, D, st);
+  switch (D.ds) {
+    SAS_GATE_CASE(16)
+    SAS_GATE_CASE(32)
+    SAS_GATE_CASE(64)
+  }
+#undef SAS_GATE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sas

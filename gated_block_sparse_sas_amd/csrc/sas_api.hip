@@ -1,0 +1,191 @@
+// sas_api.hip -- the C ABI of libsas.so: argument checks and dispatch.
+//
+// Every check runs on the host before anything is enqueued; a failing call
+// writes nothing and launches nothing.  Calls never synchronise, allocate or
+// keep state.  Entry points and semantics are documented in include/sas.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/sas.h"
+#include "sas_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+sas_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return SAS_OK;
+  g_last_hip = (int32_t)e;
+  return SAS_ERR_HIP;
+}
+
+bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Resolves and validates a shape.  `need_sel` checks the selector sizes too.
+sas_status resolve(const sas_shape* s, sas::Dims* D) {
+  if (!s) return SAS_ERR_NULL;
+  if ((s->dtype != SAS_F32 && s->dtype != SAS_BF16) ||
+      (s->sel_dtype != SAS_F32 && s->sel_dtype != SAS_BF16))
+    return SAS_ERR_DTYPE;
+  if (s->dtype != s->sel_dtype) return SAS_ERR_DTYPE;
+  const int hks = s->hks > 0 ? s->hks : s->hkv;
+  if (s->batch < 0 || s->hq < 1 || s->hkv < 1 || hks < 1 || s->tq < 1 || s->tk < 1 ||
+      s->d < 1 || s->ds < 1 || s->block < 1)
+    return SAS_ERR_SHAPE;
+  if (s->tq > s->tk || s->hq % s->hkv != 0 || s->hq % hks != 0) return SAS_ERR_SHAPE;
+  if (!(s->sm_scale <= 0.f || isfinite(s->sm_scale)) ||
+      !(s->sel_scale <= 0.f || isfinite(s->sel_scale)) || isnan(s->sm_scale) ||
+      isnan(s->sel_scale))
+    return SAS_ERR_SHAPE;
+  if (s->block != sas::kBlock || s->tk % sas::kBlock != 0) return SAS_ERR_UNSUPPORTED;
+  if (s->d != 64 && s->d != 128) return SAS_ERR_UNSUPPORTED;
+  if (s->ds != 16 && s->ds != 32 && s->ds != 64) return SAS_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)s->batch * s->hq * s->tq;
+  const int64_t keys = (int64_t)s->batch * s->hkv * s->tk;
+  if (rows >= (int64_t)1 << 31 || keys >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
+  D->batch = s->batch;
+  D->hq = s->hq;
+  D->hkv = s->hkv;
+  D->hks = hks;
+  D->tq = s->tq;
+  D->tk = s->tk;
+  D->d = s->d;
+  D->ds = s->ds;
+  D->nb = s->tk / sas::kBlock;
+  D->qoff = s->tk - s->tq;
+  D->hpg = s->hq / s->hkv;
+  D->hps = s->hq / hks;
+  D->sm_scale = s->sm_scale > 0.f ? s->sm_scale : 1.0f / sqrtf((float)s->d);
+  D->sel_scale = s->sel_scale > 0.f ? s->sel_scale : 1.0f / sqrtf((float)s->ds);
+  return SAS_OK;
+}
+
+sas_status check_ptrs(std::initializer_list<const void*> req) {
+  for (const void* p : req)
+    if (!p) return SAS_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned(p)) return SAS_ERR_ALIGN;
+  return SAS_OK;
+}
+
+sas_status check_opt(std::initializer_list<const void*> opt) {
+  for (const void* p : opt)
+    if (p && !aligned(p)) return SAS_ERR_ALIGN;
+  return SAS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sas_status_string(sas_status st) {
+  switch (st) {
+    case SAS_OK: return "ok";
+    case SAS_ERR_NULL: return "required pointer is NULL";
+    case SAS_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case SAS_ERR_DTYPE: return "unknown or mismatched dtype";
+    case SAS_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SAS_ERR_UNSUPPORTED: return "valid shape not supported by this build";
+    case SAS_ERR_WORKSPACE: return "workspace missing or too small";
+    case SAS_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t sas_last_hip_error(void) { return g_last_hip; }
+
+sas_status sas_gate_scores(const sas_shape* shape, const void* qs, const void* ks,
+                           float* gate_lse, float* gate_bias, void* stream) {
+  sas::Dims D;
+  sas_status r = resolve(shape, &D);
+  if (r != SAS_OK) return r;
+  if ((r = check_ptrs({qs, ks, gate_lse})) != SAS_OK) return r;
+  if ((r = check_opt({gate_bias})) != SAS_OK) return r;
+  if (D.batch == 0) return SAS_OK;
+  return hip_status(sas::launch_gate(qs, ks, gate_lse, gate_bias, D,
+                                     shape->sel_dtype == SAS_BF16, (hipStream_t)stream));
+}
+
+sas_status sas_attn_fwd(const sas_shape* shape, const void* q, const void* k, const void* v,
+                        const void* qs, const void* ks, const float* gate_lse, void* o,
+                        float* lse, void* stream) {
+  sas::Dims D;
+  sas_status r = resolve(shape, &D);
+  if (r != SAS_OK) return r;
+  if ((r = check_ptrs({q, k, v, qs, ks, gate_lse, o, lse})) != SAS_OK) return r;
+  if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
+  if (D.batch == 0) return SAS_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (shape->dtype == SAS_BF16)
+    return hip_status(sas::launch_fwd_bf16(q, k, v, qs, ks, gate_lse, o, lse, D, st));
+  return hip_status(sas::launch_fwd_f32(q, k, v, qs, ks, gate_lse, o, lse, D, st));
+}
+
+sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse, const void* qs,
+                        const void* ks, const float* gate_lse, void* dq, void* dk, void* dv,
+                        void* dqs, void* dks, float* dz, void* ws, size_t* ws_bytes,
+                        void* stream) {
+  sas::Dims D;
+  sas_status r = resolve(shape, &D);
+  if (r != SAS_OK) return r;
+  if (!ws_bytes) return SAS_ERR_NULL;
+  if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
+  const sas::BwdWs W = sas::bwd_workspace(D, dz == nullptr);
+  if (!ws) {
+    *ws_bytes = W.total;
+    return SAS_OK;
+  }
+  if ((r = check_ptrs({q, k, v, o, dout, lse, qs, ks, gate_lse, dq, dk, dv, dqs, dks, ws})) !=
+      SAS_OK)
+    return r;
+  if ((r = check_opt({dz})) != SAS_OK) return r;
+  if (*ws_bytes < W.total) return SAS_ERR_WORKSPACE;
+  if (D.batch == 0) return SAS_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (shape->dtype == SAS_BF16)
+    return hip_status(sas::launch_bwd_bf16(q, k, v, o, dout, lse, qs, ks, gate_lse, dq, dk, dv,
+                                           dqs, dks, dz, (char*)ws, W, D, st));
+  return hip_status(sas::launch_bwd_f32(q, k, v, o, dout, lse, qs, ks, gate_lse, dq, dk, dv, dqs,
+                                        dks, dz, (char*)ws, W, D, st));
+}
+
+sas_status sas_topk_blocks(const sas_shape* shape, int32_t topk, int32_t renorm, const void* qs,
+                           const void* ks, int32_t* idx, float* bias, void* stream) {
+  sas::Dims D;
+  sas_status r = resolve(shape, &D);
+  if (r != SAS_OK) return r;
+  if (topk < 1 || (renorm != 0 && renorm != 1)) return SAS_ERR_SHAPE;
+  if ((r = check_ptrs({qs, ks, idx, bias})) != SAS_OK) return r;
+  if (!sas::topk_supported(D, topk)) return SAS_ERR_UNSUPPORTED;
+  if ((int64_t)D.batch * D.hq * D.tq * topk >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
+  if (D.batch == 0) return SAS_OK;
+  return hip_status(sas::launch_topk(qs, ks, topk, renorm, idx, bias, D,
+                                     shape->sel_dtype == SAS_BF16, (hipStream_t)stream));
+}
+
+sas_status sas_sparse_fwd(const sas_shape* shape, int32_t topk, const void* q, const void* k,
+                          const void* v, const int32_t* idx, const float* bias, void* o,
+                          float* lse, void* ws, size_t* ws_bytes, void* stream) {
+  sas::Dims D;
+  sas_status r = resolve(shape, &D);
+  if (r != SAS_OK) return r;
+  if (topk < 1) return SAS_ERR_SHAPE;
+  if (!ws_bytes) return SAS_ERR_NULL;
+  if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
+  if ((int64_t)D.batch * D.hq * D.tq * topk >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
+  const size_t need = sas::sparse_workspace(D, topk);
+  if (!ws) {
+    *ws_bytes = need;
+    return SAS_OK;
+  }
+  if ((r = check_ptrs({q, k, v, idx, bias, o, ws})) != SAS_OK) return r;
+  if ((r = check_opt({lse})) != SAS_OK) return r;
+  if (*ws_bytes < need) return SAS_ERR_WORKSPACE;
+  if (D.batch == 0) return SAS_OK;
+  return hip_status(sas::launch_sparse(q, k, v, idx, bias, o, lse, (char*)ws, *ws_bytes, topk,
+                                       D, shape->dtype == SAS_BF16, (hipStream_t)stream));
+}
+
+}  // extern "C"

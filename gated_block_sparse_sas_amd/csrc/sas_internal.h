@@ -1,0 +1,49 @@
+// sas_internal.h -- launchers shared between the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "sas_device.h"
+
+namespace sas {
+
+// Step 1: gate normaliser lam (and optional full log-gate matrix).
+hipError_t launch_gate(const void* qs, const void* ks, float* lam, float* beta, const Dims& D,
+                       bool sel_bf16, hipStream_t st);
+
+// Step 2: dense-active gated forward.
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const void* qs,
+                           const void* ks, const float* lam, void* o, float* lse, const Dims& D,
+                           hipStream_t st);
+hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, const void* qs,
+                          const void* ks, const float* lam, void* o, float* lse, const Dims& D,
+                          hipStream_t st);
+
+// Steps 3-4: backward.  Workspace layout is decided by bwd_workspace().
+struct BwdWs {
+  size_t total;
+  size_t off_delta;  // float [rows]          D = <dO, O>
+  size_t off_dz;     // float [rows, nb]      only when the caller passes no dz
+  size_t off_dks;    // float [b, hks, nb, ds] fp32 accumulator of dks
+};
+BwdWs bwd_workspace(const Dims& D, bool need_dz);
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, const void* qs, const void* ks,
+                           const float* lam, void* dq, void* dk, void* dv, void* dqs, void* dks,
+                           float* dz, char* ws, const BwdWs& W, const Dims& D, hipStream_t st);
+hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, const void* qs, const void* ks,
+                          const float* lam, void* dq, void* dk, void* dv, void* dqs, void* dks,
+                          float* dz, char* ws, const BwdWs& W, const Dims& D, hipStream_t st);
+
+// Step 5: top-K blocks.
+bool topk_supported(const Dims& D, int K);
+hipError_t launch_topk(const void* qs, const void* ks, int K, int renorm, int* idx, float* bias,
+                       const Dims& D, bool sel_bf16, hipStream_t st);
+
+// Steps 6-7: sparse forward.
+size_t sparse_workspace(const Dims& D, int K);
+hipError_t launch_sparse(const void* q, const void* k, const void* v, const int* idx,
+                         const float* bias, void* o, float* lse, char* ws, size_t ws_bytes,
+                         int K, const Dims& D, bool bf16_io, hipStream_t st);
+
+}  // namespace sas

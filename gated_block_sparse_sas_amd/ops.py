@@ -1,0 +1,203 @@
+"""Python binding of libsas.so: argument marshalling only.
+
+Each function takes torch tensors on the GPU (PyTorch provides device memory
+and the current stream), allocates the outputs, and calls the C entry point of
+the same name declared in ``include/sas.h``.  No step of the computation runs
+here.  If ``libsas.so`` is missing or a call returns an error status, the call
+raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsas.so")
+_lib = None
+
+SAS_F32, SAS_BF16 = 0, 1
+_STATUS = {0: "SAS_OK", 1: "SAS_ERR_NULL", 2: "SAS_ERR_SHAPE", 3: "SAS_ERR_DTYPE",
+           4: "SAS_ERR_ALIGN", 5: "SAS_ERR_UNSUPPORTED", 6: "SAS_ERR_WORKSPACE",
+           7: "SAS_ERR_HIP"}
+EXPORTS = ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_topk_blocks",
+           "sas_sparse_fwd", "sas_status_string", "sas_last_hip_error")
+
+
+class SasError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__("%s failed: %s (%s)" % (fn, _STATUS.get(code, code), msg))
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    """Mirror of ``sas_shape``."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+        ("hks", ctypes.c_int32), ("tq", ctypes.c_int32), ("tk", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("ds", ctypes.c_int32), ("block", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float), ("sel_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32), ("sel_dtype", ctypes.c_int32),
+    ]
+
+
+def load():
+    """Load libsas.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsas.so not built: run gated_block_sparse_sas_amd/build.py")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, SZ = ctypes.c_void_p, ctypes.c_void_p
+        I32 = ctypes.c_int32
+        lib.sas_gate_scores.argtypes = [P, P, P, P, P, P]
+        lib.sas_attn_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P]
+        lib.sas_attn_bwd.argtypes = [P] * 17 + [SZ, P]
+        lib.sas_topk_blocks.argtypes = [P, I32, I32, P, P, P, P, P]
+        lib.sas_sparse_fwd.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P]
+        for n in ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_topk_blocks",
+                  "sas_sparse_fwd"):
+            getattr(lib, n).restype = ctypes.c_int
+        lib.sas_status_string.argtypes = [ctypes.c_int]
+        lib.sas_status_string.restype = ctypes.c_char_p
+        lib.sas_last_hip_error.restype = ctypes.c_int32
+        _lib = lib
+    return _lib
+
+
+def _check(fn, code):
+    if code != 0:
+        lib = load()
+        msg = lib.sas_status_string(code).decode()
+        if code == 7:
+            msg += ", hipError %d" % lib.sas_last_hip_error()
+        raise SasError(fn, code, msg)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SAS_BF16
+    if t.dtype == torch.float32:
+        return SAS_F32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous (BHSD)")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def make_shape(batch, hq, hkv, tq, tk, d, ds, block=64, hks=0, sm_scale=0.0, sel_scale=0.0,
+               dtype=SAS_BF16, sel_dtype=None) -> Shape:
+    return Shape(batch, hq, hkv, hks, tq, tk, d, ds, block, float(sm_scale or 0.0),
+                 float(sel_scale or 0.0), dtype, dtype if sel_dtype is None else sel_dtype)
+
+
+def shape_of(q, k, qs, ks, block=64, sm_scale=None, sel_scale=None) -> Shape:
+    b, hq, tq, d = q.shape
+    _, hkv, tk, _ = k.shape
+    ds = qs.shape[-1]
+    hks = ks.shape[1]
+    return make_shape(b, hq, hkv, tq, tk, d, ds, block, hks, sm_scale, sel_scale, _dt(q),
+                      _dt(qs))
+
+
+def gate_scores(qs, ks, tk, block=64, sel_scale=None, with_bias=False):
+    """Gate normaliser lam [B,Hq,Tq] (and the log-gate matrix if asked)."""
+    b, hq, tq, ds = qs.shape
+    hks = ks.shape[1]
+    sh = make_shape(b, hq, hks, tq, tk, 64, ds, block, hks, 0.0, sel_scale, _dt(qs), _dt(qs))
+    lam = torch.empty((b, hq, tq), dtype=torch.float32, device=qs.device)
+    beta = (torch.empty((b, hq, tq, tk // block), dtype=torch.float32, device=qs.device)
+            if with_bias else None)
+    _check("sas_gate_scores", load().sas_gate_scores(ctypes.byref(sh), _p(qs), _p(ks), _p(lam),
+                                                     _p(beta), _stream(qs)))
+    return (lam, beta) if with_bias else lam
+
+
+def attn_fwd(q, k, v, qs, ks, gate_lse, block=64, sm_scale=None, sel_scale=None):
+    """Dense-active gated forward.  Returns (o, lse)."""
+    sh = shape_of(q, k, qs, ks, block, sm_scale, sel_scale)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check("sas_attn_fwd", load().sas_attn_fwd(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(qs),
+                                               _p(ks), _p(gate_lse), _p(o), _p(lse), _stream(q)))
+    return o, lse
+
+
+def bwd_workspace_bytes(sh: Shape, with_dz=True) -> int:
+    n = ctypes.c_size_t(0)
+    dz_dummy = ctypes.c_void_p(16) if with_dz else None
+    _check("sas_attn_bwd", load().sas_attn_bwd(ctypes.byref(sh), *([None] * 14), dz_dummy, None,
+                                               ctypes.byref(n), None))
+    return n.value
+
+
+def attn_bwd(q, k, v, o, dout, lse, qs, ks, gate_lse, block=64, sm_scale=None, sel_scale=None,
+             with_dz=True, ws=None):
+    """Backward of :func:`attn_fwd`.  Returns dict dq, dk, dv, dqs, dks, dz."""
+    sh = shape_of(q, k, qs, ks, block, sm_scale, sel_scale)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dqs = torch.empty_like(qs)
+    dks = torch.empty_like(ks)
+    dz = (torch.empty(q.shape[:3] + (k.shape[2] // block,), dtype=torch.float32,
+                      device=q.device) if with_dz else None)
+    need = bwd_workspace_bytes(sh, with_dz)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(ws.numel())
+    _check("sas_attn_bwd", load().sas_attn_bwd(
+        ctypes.byref(sh), _p(q), _p(k), _p(v), _p(o), _p(dout), _p(lse), _p(qs), _p(ks),
+        _p(gate_lse), _p(dq), _p(dk), _p(dv), _p(dqs), _p(dks), _p(dz), _p(ws), ctypes.byref(n),
+        _stream(q)))
+    return dict(dq=dq, dk=dk, dv=dv, dqs=dqs, dks=dks, dz=dz)
+
+
+def topk_blocks(qs, ks, topk, tk, block=64, renorm=0, sel_scale=None):
+    """Top-K historical blocks per row.  Returns (idx int32, bias float32)."""
+    b, hq, tq, ds = qs.shape
+    hks = ks.shape[1]
+    sh = make_shape(b, hq, hks, tq, tk, 64, ds, block, hks, 0.0, sel_scale, _dt(qs), _dt(qs))
+    idx = torch.empty((b, hq, tq, topk), dtype=torch.int32, device=qs.device)
+    bias = torch.empty((b, hq, tq, topk), dtype=torch.float32, device=qs.device)
+    _check("sas_topk_blocks", load().sas_topk_blocks(ctypes.byref(sh), int(topk), int(renorm),
+                                                     _p(qs), _p(ks), _p(idx), _p(bias),
+                                                     _stream(qs)))
+    return idx, bias
+
+
+def sparse_workspace_bytes(sh: Shape, topk: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("sas_sparse_fwd", load().sas_sparse_fwd(ctypes.byref(sh), int(topk), *([None] * 7),
+                                                   None, ctypes.byref(n), None))
+    return n.value
+
+
+def sparse_fwd(q, k, v, idx, bias, block=64, sm_scale=None, ws=None, with_lse=True):
+    """Top-K sparse forward (prefill or decode).  Returns (o, lse)."""
+    b, hq, tq, d = q.shape
+    _, hkv, tk, _ = k.shape
+    topk = idx.shape[-1]
+    sh = make_shape(b, hq, hkv, tq, tk, d, 32, block, hkv, sm_scale, 0.0, _dt(q), _dt(q))
+    o = torch.empty_like(q)
+    lse = torch.empty((b, hq, tq), dtype=torch.float32, device=q.device) if with_lse else None
+    need = sparse_workspace_bytes(sh, topk)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(ws.numel())
+    _check("sas_sparse_fwd", load().sas_sparse_fwd(
+        ctypes.byref(sh), int(topk), _p(q), _p(k), _p(v), _p(idx), _p(bias), _p(o), _p(lse),
+        _p(ws), ctypes.byref(n), _stream(q)))
+    return o, lse

@@ -1,0 +1,144 @@
+/*
+ * sas.h -- C ABI of libsas.so: SAS gated block-sparse attention on MI355X
+ * (gfx950).
+ *
+ * Method: "SAS: Simple Attention Sparsification via End-to-End Optimization
+ * of Context Ranking" (authors' abstract, NeurIPS 2026 poster page and
+ * Hugging Face papers page).  A lightweight selector gives every past context
+ * block a continuous score; the scores are normalised with a softmax over the
+ * query's historical blocks; the log of that gate is added to every attention
+ * logit of the block inside the attention softmax (logit injection, blog
+ * "SAS Learns Token Importance for Sparse Attention", section "The Logit
+ * Injection Mechanism").  The current block is always kept with zero bias.
+ * Training attends every block (dense-active); inference keeps the current
+ * block plus the top-K historical blocks (hard Top-K under an attention
+ * budget, both abstracts).
+ *
+ * Score function (the pages leave it open; this library fixes it):
+ *   z[t,j]   = sel_scale * <qs[t], ks[s(h), j]>          for j < c(t)
+ *   lam[t]   = log sum_{j<c(t)} exp z[t,j]               (-inf if c(t) = 0)
+ *   beta[t,j]= z[t,j] - lam[t] (j < c(t)),  0 (j = c(t))
+ *   logit[t,u] = sm_scale * <q[t], k[u]> + beta[t, u/block],  u <= t
+ *
+ * Conventions for every entry point
+ *  - Tensors are dense, contiguous BHSD device buffers owned by the caller:
+ *      q, o, dq, dout [batch, hq,  tq, d]     k, v, dk, dv [batch, hkv, tk, d]
+ *      qs, dqs        [batch, hq,  tq, ds]    ks, dks      [batch, hks, nb, ds]
+ *      lse, gate_lse  [batch, hq,  tq]        (float32)
+ *      dz, gate_bias  [batch, hq,  tq, nb]    (float32)
+ *      idx, bias      [batch, hq,  tq, topk]  (int32 / float32)
+ *    with nb = tk / block.  Query row i sits at absolute position
+ *    t = (tk - tq) + i; its block is c(t) = t / block.
+ *  - Query head h reads kv head h / (hq / hkv) and selector-key head
+ *    h / (hq / hks).
+ *  - dtype selects the element type of q, k, v, o, dout, dq, dk, dv;
+ *    sel_dtype that of qs, ks, dqs, dks (both SAS_BF16 or both SAS_F32).
+ *    Softmax statistics and accumulation are float32.
+ *  - All pointers must be 16-byte aligned.  `stream` is a hipStream_t
+ *    (NULL = the default stream).  Calls only enqueue work: they never
+ *    synchronise, never allocate and keep no state between calls, so they are
+ *    re-entrant; the results are valid once the stream reaches them.
+ *  - Workspace: calls that take (ws, ws_bytes) use a size query.  With
+ *    ws == NULL they write the bytes they need to *ws_bytes, return SAS_OK and
+ *    launch nothing.  Otherwise *ws_bytes is the size of ws and must be at
+ *    least that much (SAS_ERR_WORKSPACE if not).
+ *  - Errors: every argument is checked on the host before anything is
+ *    enqueued; a failed check returns a status, writes nothing and launches
+ *    nothing.  Valid but unsupported shapes return SAS_ERR_UNSUPPORTED (there
+ *    is no slow fallback).  A failed launch returns SAS_ERR_HIP; faults inside
+ *    kernels surface at the caller's next synchronisation.
+ *  - Supported: block == 64, tk % 64 == 0, d in {64, 128}, ds in {16, 32, 64},
+ *    hq % hkv == 0, hq % hks == 0, 1 <= tq <= tk.  batch == 0 is an empty call.
+ */
+#ifndef SAS_H
+#define SAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAS_OK = 0,
+  SAS_ERR_NULL = 1,        /* a required pointer is NULL                  */
+  SAS_ERR_SHAPE = 2,       /* sizes inconsistent or out of range          */
+  SAS_ERR_DTYPE = 3,       /* unknown dtype / dtype combination           */
+  SAS_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned            */
+  SAS_ERR_UNSUPPORTED = 5, /* valid but not implemented for this shape    */
+  SAS_ERR_WORKSPACE = 6,   /* workspace missing or too small              */
+  SAS_ERR_HIP = 7          /* a HIP launch failed                         */
+} sas_status;
+
+typedef enum { SAS_F32 = 0, SAS_BF16 = 1 } sas_dtype;
+
+typedef struct {
+  int32_t batch, hq, hkv, hks; /* hks <= 0 means hks = hkv                      */
+  int32_t tq, tk;              /* training / prefill: tq == tk; decode: tq == 1 */
+  int32_t d, ds, block;        /* head dim, selector dim, block size             */
+  float sm_scale;              /* <= 0 means 1/sqrt(d)                           */
+  float sel_scale;             /* <= 0 means 1/sqrt(ds)                          */
+  int32_t dtype, sel_dtype;    /* sas_dtype                                      */
+} sas_shape;
+
+/* Selector scores and gate normaliser (training forward, step 1).
+ * Computes lam[t] (gate_lse, required) and, if gate_bias != NULL, the full
+ * log-gate matrix beta [batch,hq,tq,nb]: z - lam for j < c(t), 0 at j = c(t),
+ * -inf for j > c(t).  Source: both abstracts (normalised softmax gates over
+ * historical context, current block always retained). */
+sas_status sas_gate_scores(const sas_shape* shape, const void* qs, const void* ks,
+                           float* gate_lse, float* gate_bias, void* stream);
+
+/* Dense-active gated attention forward (training, every block attended, each
+ * historical block with its log-gate).  Inputs q, k, v, qs, ks and gate_lse
+ * (from sas_gate_scores); outputs o and lse[t] = log sum_u exp logit[t,u]
+ * (kept for the backward).  Source: NeurIPS abstract (gate in log form inside
+ * the softmax, all units active in training, FlashAttention-style kernel). */
+sas_status sas_attn_fwd(const sas_shape* shape, const void* q, const void* k, const void* v,
+                        const void* qs, const void* ks, const float* gate_lse, void* o,
+                        float* lse, void* stream);
+
+/* Backward of sas_attn_fwd given dout.  Outputs dq, dk, dv (dk, dv summed
+ * over the query heads of each kv head), dqs, dks (summed over the heads
+ * sharing a selector head) and dz = dL/dz [batch,hq,tq,nb] (0 for j >= c(t)),
+ * the gradient reaching the selector scores.  dz may be NULL (it then lives in
+ * the workspace).  Source: blog, "The Logit Injection Mechanism" (gradients
+ * reach the selector through the softmax), NeurIPS abstract. */
+sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse, const void* qs,
+                        const void* ks, const float* gate_lse, void* dq, void* dk, void* dv,
+                        void* dqs, void* dks, float* dz, void* ws, size_t* ws_bytes,
+                        void* stream);
+
+/* Hard Top-K of the historical blocks of every query row (inference budget):
+ * the min(topk, c(t)) blocks with the largest z, ordered by z descending and
+ * block index ascending on ties; idx pads with -1 and bias with -inf.
+ * bias = z - lam (renorm == 0, the training log-gate of the block) or
+ * z - log sum_{selected} exp z (renorm == 1).  1 <= topk.
+ * Source: both abstracts (selector + hard Top-K; budget = attended units per
+ * query); the budget counts historical blocks, the current block is extra. */
+sas_status sas_topk_blocks(const sas_shape* shape, int32_t topk, int32_t renorm, const void* qs,
+                           const void* ks, int32_t* idx, float* bias, void* stream);
+
+/* Top-K sparse attention forward (prefill: tq == tk; decode: tq == 1; any
+ * 1 <= tq <= tk): every row attends its current block (causal, bias 0) plus
+ * the blocks in idx with the matching bias.  idx entries must be -1 or
+ * distinct blocks j < c(t); other entries are skipped (never read out of
+ * bounds).  lse may be NULL.  Source: NeurIPS abstract (a small set of context
+ * units per query under a fixed budget); blog, "Implementation and
+ * Efficiency" (only part of the blocks is computed). */
+sas_status sas_sparse_fwd(const sas_shape* shape, int32_t topk, const void* q, const void* k,
+                          const void* v, const int32_t* idx, const float* bias, void* o,
+                          float* lse, void* ws, size_t* ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* sas_status_string(sas_status status);
+
+/* Last HIP error code seen by this thread's most recent SAS_ERR_HIP (0 if none). */
+int32_t sas_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAS_H */
