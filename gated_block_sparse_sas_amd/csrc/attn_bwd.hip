@@ -1,0 +1,641 @@
+// attn_bwd.hip -- backward of the dense-active gated attention.
+//
+// With P = softmax of the gated logits, O = P V and upstream dO:
+//   D_t = <dO_t, O_t>,  dP = dO V^T,  dS = P o (dP - D)
+//   dQ = sm_scale dS K,  dK = sm_scale dS^T Q,  dV = P^T dO   (dK, dV summed over
+//   the query heads of each kv head)
+//   dbeta_{t,j} = sum_{u in block j} dS_{t,u}                    (j < c(t))
+//   dz_{t,j} = dbeta_{t,j} - g_{t,j} sum_{j'<c(t)} dbeta_{t,j'},  g = exp(beta)
+//   dqs_t = sel_scale sum_j dz_{t,j} ks_j,  dks_j = sel_scale sum_t dz_{t,j} qs_t
+// SAS (blog "SAS Learns Token Importance for Sparse Attention", "The Logit
+// Injection Mechanism"; NeurIPS abstract): because the gate sits in the logits,
+// the loss gradient reaches the selector scores through the softmax.
+//
+// Kernels:
+//  * bwd_dq (query-stationary, same tiling as the forward): S^T, dP^T, dQ^T
+//    with the query in the MFMA column, so dbeta is an in-lane row sum.  Key
+//    tiles run from the diagonal down, so sum_j dbeta_{t,j} is known (it equals
+//    minus the row sum of dS over the current block, because every row of dS
+//    sums to zero) before the first historical tile: dz and dqs are produced on
+//    the fly and dz is written once.  D is computed here and kept for bwd_dkdv.
+//  * bwd_dkdv (key-stationary): 128 keys per workgroup, 32 per wave, K and V
+//    in registers; loops over the query heads of the group and the query tiles
+//    at or after the keys.  S = Q K^T with the key in the MFMA column, so P and
+//    dS feed dV^T += dO^T P and dK^T += Q^T dS straight from registers; Q and
+//    dO are staged in LDS both row-major and transposed.
+//  * dks: a reduction over rows of dz^T qs into an fp32 accumulator.
+#include "sas_device.h"
+#include "sas_internal.h"
+
+#include <algorithm>
+
+namespace sas {
+
+// --------------------------------------------------------------------------
+// Query-stationary: dQ, D, dz, dqs.
+// --------------------------------------------------------------------------
+template <int HD, int DS>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
+    const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
+    bf16* __restrict__ dq, bf16* __restrict__ dqs, float* __restrict__ dz,
+    float* __restrict__ delta, Dims D, int nqt, int xcd_groups) {
+  constexpr int KP = HD + 8;
+  constexpr int TP = kBlock + 8;
+  constexpr int KS = HD / 16;
+  constexpr int DM = HD / 32;
+  constexpr int ITEMS = 16 * (HD / 8);  // (4 keys x 8 dims) items per tile
+  constexpr int IT = (ITEMS + 255) / 256;
+  __shared__ __align__(16) bf16 Ks[kBlock * KP];
+  __shared__ __align__(16) bf16 Vs[kBlock * KP];
+  __shared__ __align__(16) bf16 Kt[HD * TP];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const QTile tm = map_q_tile(blockIdx.x, nqt, D, xcd_groups);
+  const int b = tm.b, h = tm.h, qt = tm.qt;
+  const int g = h / D.hpg, sh = h / D.hps;
+  const int wq0 = qt * 128 + wave * 32;
+  const int qi = wq0 + l32;
+  const bool valid = qi < D.tq;
+  const int qc = min(qi, D.tq - 1);
+  const int t = D.qoff + qc;
+  const int c = t / kBlock;
+  const int c_hi = (D.qoff + min(wq0 + 31, D.tq - 1)) / kBlock;
+  const int c_lo = (D.qoff + min(wq0, D.tq - 1)) / kBlock;
+  const int c_end = (D.qoff + min(qt * 128 + 127, D.tq - 1)) / kBlock;
+  const size_t row = ((size_t)b * D.hq + h) * D.tq + qc;
+
+  // zero dz[row, j] for j >= c(row) for this workgroup's rows (coalesced)
+  for (int r = 0; r < 128; ++r) {
+    const int i = qt * 128 + r;
+    if (i >= D.tq) break;
+    const int cr = (D.qoff + i) / kBlock;
+    float* zr = dz + (((size_t)b * D.hq + h) * D.tq + i) * D.nb;
+    for (int j = cr + tid; j < D.nb; j += 256) zr[j] = 0.f;
+  }
+
+  bf16x8 qf[KS], df[KS];
+  float dlt = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = *(const bf16x8*)(q + row * HD + 16 * s + 8 * hh);
+    df[s] = *(const bf16x8*)(dout + row * HD + 16 * s + 8 * hh);
+    const bf16x8 of = *(const bf16x8*)(o + row * HD + 16 * s + 8 * hh);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dlt = fmaf(to_f32(df[s][e]), to_f32(of[e]), dlt);
+  }
+  dlt += __shfl_xor(dlt, 32);
+  if (valid && hh == 0) delta[row] = dlt;
+  float qsv[DS / 2];
+#pragma unroll
+  for (int e = 0; e < DS / 2; ++e) qsv[e] = to_f32(qs[row * DS + hh * (DS / 2) + e]);
+  const float lam_t = c > 0 ? lam[row] : 0.f;
+  const float l2 = lse[row] * kLog2e;
+  const bf16* ksb = ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS + hh * (DS / 2);
+  const bf16* kb = k + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
+  const bf16* vb = v + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
+  const float c1 = D.sm_scale * kLog2e;
+
+  f32x16 dqacc[DM];
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm) dqacc[dm] = f32x16{};
+  float dqsacc[DS / 2];
+#pragma unroll
+  for (int e = 0; e < DS / 2; ++e) dqsacc[e] = 0.f;
+  float sdb = 0.f;  // sum over history of dbeta for this row
+
+  const bf16x8 zero8 = bf16x8{};
+  bf16x8 kreg[IT][4], vreg[IT][4];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int x = 0; x < IT; ++x) {
+      const int id = tid + 256 * x;
+      if (id < ITEMS) {
+        const int kg = id % 16, dc = id / 16;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const int key = j * kBlock + kg * 4 + i2;
+          const bool in = key < D.tk;
+          kreg[x][i2] = in ? *(const bf16x8*)(kb + (size_t)key * HD + dc * 8) : zero8;
+          vreg[x][i2] = in ? *(const bf16x8*)(vb + (size_t)key * HD + dc * 8) : zero8;
+        }
+      }
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int x = 0; x < IT; ++x) {
+      const int id = tid + 256 * x;
+      if (id < ITEMS) {
+        const int kg = id % 16, dc = id / 16;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          *(bf16x8*)&Ks[(kg * 4 + i2) * KP + dc * 8] = kreg[x][i2];
+          *(bf16x8*)&Vs[(kg * 4 + i2) * KP + dc * 8] = vreg[x][i2];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16x4 w = {kreg[x][0][e], kreg[x][1][e], kreg[x][2][e], kreg[x][3][e]};
+          *(bf16x4*)&Kt[(dc * 8 + e) * TP + kg * 4] = w;
+        }
+      }
+    }
+  };
+
+  gload(c_end);
+  for (int j = c_end; j >= 0; --j) {
+    __syncthreads();
+    sstore();
+    __syncthreads();
+    if (j > 0) gload(j - 1);
+    if (j > c_hi) continue;
+
+    float bias2 = 0.f;
+    float ksv[DS / 2];
+    if (j < c_hi) {
+      const bf16* kr = ksb + (size_t)j * DS;
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS / 2; ++e) {
+        ksv[e] = to_f32(kr[e]);
+        part = fmaf(qsv[e], ksv[e], part);
+      }
+      part += __shfl_xor(part, 32);
+      if (j < c) bias2 = (D.sel_scale * part - lam_t) * kLog2e;
+    }
+    const float off = bias2 - l2;
+
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    f32x16 pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 a = *(const bf16x8*)&Ks[(32 * mt + l32) * KP + 16 * s + 8 * hh];
+        sacc[mt] = mfma32(a, qf[s], sacc[mt]);
+        const bf16x8 av = *(const bf16x8*)&Vs[(32 * mt + l32) * KP + 16 * s + 8 * hh];
+        pacc[mt] = mfma32(av, df[s], pacc[mt]);
+      }
+    }
+    const bool nomask = j < c_lo;
+    float dsum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2f(fmaf(sacc[mt][r], c1, off));
+        if (!nomask) {
+          const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
+          if (u > t) p = 0.f;
+        }
+        const float ds = p * (pacc[mt][r] - dlt);
+        sacc[mt][r] = ds;
+        dsum += ds;
+      }
+    }
+    dsum += __shfl_xor(dsum, 32);
+    if (j == c) {
+      sdb = -dsum;  // sum_{j'<c} dbeta = - sum over the current block of dS
+    } else if (j < c) {
+      const float dzv = dsum - exp2f(bias2) * sdb;
+      if (valid && hh == 0) dz[row * D.nb + j] = dzv;
+#pragma unroll
+      for (int e = 0; e < DS / 2; ++e) dqsacc[e] = fmaf(dzv, ksv[e], dqsacc[e]);
+    }
+
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        bf16x8 sb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sb[e] = (bf16)sacc[mt][8 * pp + e];
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) {
+          const bf16* kp = &Kt[(32 * dm + l32) * TP + 32 * mt + 16 * pp + 4 * hh];
+          const bf16x4 lo = *(const bf16x4*)kp;
+          const bf16x4 hi = *(const bf16x4*)(kp + 8);
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          dqacc[dm] = mfma32(a, sb, dqacc[dm]);
+        }
+      }
+    }
+  }
+
+  if (valid) {
+    bf16* qr = dq + row * HD;
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(dqacc[dm][4 * rr + e] * D.sm_scale);
+        *(bf16x4*)(qr + 32 * dm + 8 * rr + 4 * hh) = w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < DS / 2; ++e)
+      dqs[row * DS + hh * (DS / 2) + e] = (bf16)(dqsacc[e] * D.sel_scale);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Key-stationary: dK, dV.
+// --------------------------------------------------------------------------
+template <int HD, int DS>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, const bf16* __restrict__ qs, const bf16* __restrict__ ks,
+    const float* __restrict__ lam, bf16* __restrict__ dk, bf16* __restrict__ dv, Dims D,
+    int nkt, int xcd_groups) {
+  constexpr int KP = HD + 8;
+  constexpr int TP = 64 + 8;
+  constexpr int KS = HD / 16;
+  constexpr int DM = HD / 32;
+  constexpr int ITEMS = 16 * (HD / 8);  // (4 rows x 8 dims) items per 64-row tile
+  constexpr int IT = (ITEMS + 255) / 256;
+  __shared__ __align__(16) bf16 Qs[64 * KP];
+  __shared__ __align__(16) bf16 Os[64 * KP];  // dO rows
+  __shared__ __align__(16) bf16 Qt[HD * TP];
+  __shared__ __align__(16) bf16 Ot[HD * TP];  // dO^T
+  __shared__ float offs[2][64];                // log2 offset of (block, row)
+  __shared__ float dls[64];                    // D of row
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  // work item: (b, kv head g, key tile kt), key tiles issued longest first
+  int b, g, kt;
+  {
+    const int L = blockIdx.x;
+    if (xcd_groups > 0) {
+      const int xcd = L & 7, s = L >> 3;
+      const int rank = s / xcd_groups, gi = s % xcd_groups;
+      const int G = gi * 8 + xcd;
+      b = G / D.hkv;
+      g = G % D.hkv;
+      kt = rank;
+    } else {
+      const int bg = D.batch * D.hkv;
+      kt = L / bg;
+      b = (L % bg) / D.hkv;
+      g = L % D.hkv;
+    }
+  }
+  const int kbase = kt * 128;
+  const int key = kbase + wave * 32 + l32;  // this lane's key (column)
+  const int blk0 = kbase / kBlock;          // first of the two blocks
+  const int wblk = wave >> 1;               // this wave's block (0/1 within the tile)
+  const bool key_ok = key < D.tk;
+  const size_t kvrow = ((size_t)b * D.hkv + g) * D.tk + (key_ok ? key : D.tk - 1);
+
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kf[s] = *(const bf16x8*)(k + kvrow * HD + 16 * s + 8 * hh);
+    vf[s] = *(const bf16x8*)(v + kvrow * HD + 16 * s + 8 * hh);
+  }
+  f32x16 dkacc[DM], dvacc[DM];
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm) {
+    dkacc[dm] = f32x16{};
+    dvacc[dm] = f32x16{};
+  }
+  const float c1 = D.sm_scale * kLog2e;
+  const int i_first = max(0, kbase - D.qoff);  // first row that can see a key of the tile
+  const int qt0 = i_first / 64;
+  const int nqt64 = (D.tq + 63) / 64;
+  const int n_items = D.hpg * (nqt64 - qt0);
+  if (kbase >= D.tk) return;
+
+  const bf16x8 zero8 = bf16x8{};
+  bf16x8 qreg[IT][4], oreg[IT][4];
+  auto gload = [&](int it) {
+    const int hl = it / (nqt64 - qt0), qtile = qt0 + it % (nqt64 - qt0);
+    const int h = g * D.hpg + hl;
+    const size_t base = ((size_t)b * D.hq + h) * D.tq;
+#pragma unroll
+    for (int x = 0; x < IT; ++x) {
+      const int id = tid + 256 * x;
+      if (id < ITEMS) {
+        const int rg = id % 16, dc = id / 16;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const int i = qtile * 64 + rg * 4 + i2;
+          const bool in = i < D.tq;
+          qreg[x][i2] = in ? *(const bf16x8*)(q + (base + i) * HD + dc * 8) : zero8;
+          oreg[x][i2] = in ? *(const bf16x8*)(dout + (base + i) * HD + dc * 8) : zero8;
+        }
+      }
+    }
+  };
+  auto sstore = [&](int it) {
+#pragma unroll
+    for (int x = 0; x < IT; ++x) {
+      const int id = tid + 256 * x;
+      if (id < ITEMS) {
+        const int rg = id % 16, dc = id / 16;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          *(bf16x8*)&Qs[(rg * 4 + i2) * KP + dc * 8] = qreg[x][i2];
+          *(bf16x8*)&Os[(rg * 4 + i2) * KP + dc * 8] = oreg[x][i2];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16x4 w = {qreg[x][0][e], qreg[x][1][e], qreg[x][2][e], qreg[x][3][e]};
+          *(bf16x4*)&Qt[(dc * 8 + e) * TP + rg * 4] = w;
+          bf16x4 w2 = {oreg[x][0][e], oreg[x][1][e], oreg[x][2][e], oreg[x][3][e]};
+          *(bf16x4*)&Ot[(dc * 8 + e) * TP + rg * 4] = w2;
+        }
+      }
+    }
+    // per-row offsets for the two blocks of this key tile, and D
+    const int hl = it / (nqt64 - qt0), qtile = qt0 + it % (nqt64 - qt0);
+    const int h = g * D.hpg + hl;
+    if (tid < 128) {
+      const int r = tid & 63, bl = tid >> 6;
+      const int i = qtile * 64 + r;
+      const int blk = blk0 + bl;
+      float off = -INFINITY;
+      if (i < D.tq && blk < D.nb) {
+        const size_t rw = ((size_t)b * D.hq + h) * D.tq + i;
+        const int t = D.qoff + i;
+        const int c = t / kBlock;
+        const float l2 = lse[rw] * kLog2e;
+        if (blk == c) {
+          off = -l2;
+        } else if (blk < c) {
+          const bf16* qsr = qs + rw * DS;
+          const bf16* ksr = ks + (((size_t)b * D.hks + h / D.hps) * D.nb + blk) * DS;
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < DS; ++e) acc = fmaf(to_f32(qsr[e]), to_f32(ksr[e]), acc);
+          off = (D.sel_scale * acc - lam[rw]) * kLog2e - l2;
+        }
+      }
+      offs[bl][r] = off;
+    } else if (tid < 192) {
+      const int r = tid - 128;
+      const int i = qtile * 64 + r;
+      dls[r] = i < D.tq ? delta[((size_t)b * D.hq + h) * D.tq + i] : 0.f;
+    }
+  };
+
+  gload(0);
+  for (int it = 0; it < n_items; ++it) {
+    __syncthreads();
+    sstore(it);
+    __syncthreads();
+    if (it + 1 < n_items) gload(it + 1);
+    const int qtile = qt0 + it % (nqt64 - qt0);
+    const int row0 = qtile * 64;
+    // skip if every row of the tile is before this wave's keys
+    if (D.qoff + min(row0 + 63, D.tq - 1) < kbase + wave * 32) continue;
+
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    f32x16 pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int mq = 0; mq < 2; ++mq) {
+        const bf16x8 a = *(const bf16x8*)&Qs[(32 * mq + l32) * KP + 16 * s + 8 * hh];
+        sacc[mq] = mfma32(a, kf[s], sacc[mq]);
+        const bf16x8 ao = *(const bf16x8*)&Os[(32 * mq + l32) * KP + 16 * s + 8 * hh];
+        pacc[mq] = mfma32(ao, vf[s], pacc[mq]);
+      }
+    }
+    const bool nomask = D.qoff + row0 >= kbase + 127;
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = 32 * mq + (r / 4) * 8 + 4 * hh + (r % 4);
+        float p = exp2f(fmaf(sacc[mq][r], c1, offs[wblk][rr]));
+        if (!nomask && key > D.qoff + row0 + rr) p = 0.f;
+        sacc[mq][r] = p;
+        pacc[mq][r] = p * (pacc[mq][r] - dls[rr]);
+      }
+    }
+    // dV^T += dO^T P ;  dK^T += Q^T dS
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        bf16x8 pb, sb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[e] = (bf16)sacc[mq][8 * pp + e];
+          sb[e] = (bf16)pacc[mq][8 * pp + e];
+        }
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) {
+          const int off = (32 * dm + l32) * TP + 32 * mq + 16 * pp + 4 * hh;
+          const bf16x4 olo = *(const bf16x4*)&Ot[off];
+          const bf16x4 ohi = *(const bf16x4*)&Ot[off + 8];
+          dvacc[dm] = mfma32(__builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7), pb,
+                             dvacc[dm]);
+          const bf16x4 qlo = *(const bf16x4*)&Qt[off];
+          const bf16x4 qhi = *(const bf16x4*)&Qt[off + 8];
+          dkacc[dm] = mfma32(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), sb,
+                             dkacc[dm]);
+        }
+      }
+    }
+  }
+
+  if (key_ok) {
+    bf16* kr = dk + kvrow * HD;
+    bf16* vr = dv + kvrow * HD;
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        bf16x4 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = (bf16)(dkacc[dm][4 * rr + e] * D.sm_scale);
+          wv[e] = (bf16)dvacc[dm][4 * rr + e];
+        }
+        *(bf16x4*)(kr + 32 * dm + 8 * rr + 4 * hh) = wk;
+        *(bf16x4*)(vr + 32 * dm + 8 * rr + 4 * hh) = wv;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// dks[b, s, j, :] = sel_scale * sum over rows (h of s, t with c(t) > j) of
+// dz[t, j] qs[t, :].  Grid: (64-block tile, 256-row chunk, b * hks); the
+// partial sums of a chunk go to an fp32 accumulator with atomics.
+// --------------------------------------------------------------------------
+template <int DS, typename ST>
+__global__ __launch_bounds__(256) void dks_kernel(const float* __restrict__ dz,
+                                                  const ST* __restrict__ qs,
+                                                  float* __restrict__ acc, Dims D) {
+  __shared__ float zs[64][65];
+  __shared__ float qv[64][DS + 1];
+  const int tid = threadIdx.x;
+  const int j0 = blockIdx.x * 64;
+  const int bs = blockIdx.z, b = bs / D.hks, s = bs % D.hks;
+  const int nrows = D.hps * D.tq;  // rows of this selector head
+  const int r0 = blockIdx.y * 256;
+  // rows before the first query that has block j0 in its history add nothing
+  const int i_min = max(0, (j0 + 1) * kBlock - D.qoff);
+  constexpr int EP = DS / 4;  // outputs per thread: block jj = tid/4, EP dims
+  const int jj = tid >> 2, e0 = (tid & 3) * EP;
+  float a[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e) a[e] = 0.f;
+  for (int sub = 0; sub < 256; sub += 64) {
+    const int rbase = r0 + sub;
+    if (rbase >= nrows) break;
+    __syncthreads();
+    // stage 64 rows x 64 blocks of dz and 64 rows of qs
+    for (int x = tid; x < 64 * 64; x += 256) {
+      const int r = x >> 6, jc = x & 63;
+      const int rr = rbase + r;
+      float val = 0.f;
+      if (rr < nrows) {
+        const int hl = rr / D.tq, i = rr % D.tq;
+        if (i >= i_min && j0 + jc < D.nb) {
+          const size_t row = ((size_t)b * D.hq + s * D.hps + hl) * D.tq + i;
+          val = dz[row * D.nb + j0 + jc];
+        }
+      }
+      zs[r][jc] = val;
+    }
+    for (int x = tid; x < 64 * DS; x += 256) {
+      const int r = x / DS, e = x % DS;
+      const int rr = rbase + r;
+      float val = 0.f;
+      if (rr < nrows) {
+        const int hl = rr / D.tq, i = rr % D.tq;
+        const size_t row = ((size_t)b * D.hq + s * D.hps + hl) * D.tq + i;
+        val = to_f32(qs[row * DS + e]);
+      }
+      qv[r][e] = val;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < 64; ++r) {
+      const float zv = zs[r][jj];
+#pragma unroll
+      for (int e = 0; e < EP; ++e) a[e] = fmaf(zv, qv[r][e0 + e], a[e]);
+    }
+  }
+  if (j0 + jj < D.nb) {
+    float* out = acc + (((size_t)b * D.hks + s) * D.nb + j0 + jj) * DS + e0;
+#pragma unroll
+    for (int e = 0; e < EP; ++e)
+      if (a[e] != 0.f) atomicAdd(out + e, a[e]);
+  }
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+template <typename ST>
+__global__ void scale_convert_kernel(const float* __restrict__ src, ST* __restrict__ dst,
+                                     float scale, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = from_f32<ST>(src[i] * scale);
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdWs bwd_workspace(const Dims& D, bool need_dz) {
+  BwdWs W;
+  const size_t rows = (size_t)D.batch * D.hq * D.tq;
+  size_t off = 0;
+  W.off_delta = off;
+  off += align256(rows * sizeof(float));
+  W.off_dz = off;
+  if (need_dz) off += align256(rows * (size_t)D.nb * sizeof(float));
+  W.off_dks = off;
+  off += align256((size_t)D.batch * D.hks * D.nb * D.ds * sizeof(float));
+  W.total = off;
+  return W;
+}
+
+template <typename ST>
+hipError_t launch_dks(const float* dz, const void* qs, float* acc, void* dks, const Dims& D,
+                      hipStream_t st) {
+  const size_t n = (size_t)D.batch * D.hks * D.nb * D.ds;
+  const unsigned fg = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(fg), dim3(256), 0, st, acc, n);
+  dim3 grid((D.nb + 63) / 64, (D.hps * D.tq + 255) / 256, D.batch * D.hks);
+  switch (D.ds) {
+    case 16:
+      hipLaunchKernelGGL((dks_kernel<16, ST>), grid, dim3(256), 0, st, dz, (const ST*)qs, acc, D);
+      break;
+    case 32:
+      hipLaunchKernelGGL((dks_kernel<32, ST>), grid, dim3(256), 0, st, dz, (const ST*)qs, acc, D);
+      break;
+    case 64:
+      hipLaunchKernelGGL((dks_kernel<64, ST>), grid, dim3(256), 0, st, dz, (const ST*)qs, acc, D);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((scale_convert_kernel<ST>), dim3(fg), dim3(256), 0, st, (const float*)acc,
+                     (ST*)dks, D.sel_scale, n);
+  return hipGetLastError();
+}
+template hipError_t launch_dks<float>(const float*, const void*, float*, void*, const Dims&,
+                                      hipStream_t);
+
+template <int HD, int DS>
+static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse, const void* qs,
+                               const void* ks, const float* lam, void* dq, void* dk, void* dv,
+                               void* dqs, void* dks, float* dz, char* ws, const BwdWs& W,
+                               const Dims& D, hipStream_t st) {
+  float* delta = (float*)(ws + W.off_delta);
+  float* dzp = dz ? dz : (float*)(ws + W.off_dz);
+  float* acc = (float*)(ws + W.off_dks);
+  const int groups = D.batch * D.hkv;
+  const int xg = groups % 8 == 0 ? groups / 8 : 0;
+  const int nqt = (D.tq + 127) / 128;
+  hipLaunchKernelGGL((bwd_dq_kernel<HD, DS>), dim3(D.batch * D.hq * nqt), dim3(256), 0, st,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)o,
+                     (const bf16*)dout, lse, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dq,
+                     (bf16*)dqs, dzp, delta, D, nqt, xg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkt = (D.tk + 127) / 128;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<HD, DS>), dim3(groups * nkt), dim3(256), 0, st,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
+                     (const float*)delta, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dk,
+                     (bf16*)dv, D, nkt, xg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_dks<bf16>(dzp, qs, acc, dks, D, st);
+}
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, const void* qs, const void* ks,
+                           const float* lam, void* dq, void* dk, void* dv, void* dqs, void* dks,
+                           float* dz, char* ws, const BwdWs& W, const Dims& D, hipStream_t st) {
+#define SAS_BWD_CASE(HDV, DSV)                                                                  \
+  if (D.d == HDV && D.ds == DSV)                                                                \
+    return launch_bwd_t<HDV, DSV>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, dz, \
+                                  ws, W, D, st);
+  SAS_BWD_CASE(128, 32)
+  SAS_BWD_CASE(128, 16)
+  SAS_BWD_CASE(128, 64)
+  SAS_BWD_CASE(64, 32)
+  SAS_BWD_CASE(64, 16)
+  SAS_BWD_CASE(64, 64)
+#undef SAS_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sas

@@ -5,13 +5,6 @@ hipError_t launch_fwd_f32(const void*, const void*, const void*, const void*, co
                           const float*, void*, float*, const Dims&, hipStream_t) {
   return hipErrorNotSupported;
 }
-BwdWs bwd_workspace(const Dims&, bool) { return BwdWs{0, 0, 0, 0}; }
-hipError_t launch_bwd_bf16(const void*, const void*, const void*, const void*, const void*,
-                           const float*, const void*, const void*, const float*, void*, void*,
-                           void*, void*, void*, float*, char*, const BwdWs&, const Dims&,
-                           hipStream_t) {
-  return hipErrorNotSupported;
-}
 hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, const void*,
                           const float*, const void*, const void*, const float*, void*, void*,
                           void*, void*, void*, float*, char*, const BwdWs&, const Dims&,
