@@ -11,9 +11,4 @@ hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, co
                           hipStream_t) {
   return hipErrorNotSupported;
 }
-size_t sparse_workspace(const Dims&, int) { return 0; }
-hipError_t launch_sparse(const void*, const void*, const void*, const int*, const float*, void*,
-                         float*, char*, size_t, int, const Dims&, bool, hipStream_t) {
-  return hipErrorNotSupported;
-}
 }  // namespace sas

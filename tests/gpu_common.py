@@ -23,12 +23,24 @@ def oshape(w: synth.Workload) -> OracleShape:
     return OracleShape(w.batch, w.hq, w.hkv, w.tq, w.tk, w.d, w.ds, w.block, hks=w.kheads)
 
 
+class LazyF64(dict):
+    """Exact fp64 copies of the stored inputs, converted on first use."""
+
+    def __init__(self, cpu):
+        super().__init__()
+        self._cpu = cpu
+
+    def __missing__(self, n):
+        a = synth.to_f64(self._cpu[n])
+        self[n] = a
+        return a
+
+
 def inputs(w: synth.Workload, names=("q", "k", "v", "qs", "ks", "dout")):
     """CPU tensors (storage dtype), device copies and exact fp64 copies."""
     cpu = synth.draw_all(w, names)
     dev = {n: t.to(DEV) for n, t in cpu.items()}
-    f64 = {n: synth.to_f64(t) for n, t in cpu.items()}
-    return cpu, dev, f64
+    return cpu, dev, LazyF64(cpu)
 
 
 def max_abs(a, b) -> float:
