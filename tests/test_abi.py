@@ -1,0 +1,162 @@
+"""Host-side checks of libsas.so (no GPU needed, no kernel is launched).
+
+* the library loads and exports every function ``include/sas.h`` declares;
+* every argument check returns its documented status before any launch;
+* the workspace size queries answer without launching anything.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_block_sparse_sas_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sas.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        from gated_block_sparse_sas_amd import build
+        build.build()
+    return ops.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sas_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) >= {"sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_topk_blocks",
+                          "sas_sparse_fwd", "sas_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(ops.EXPORTS) == set(names)
+
+
+def test_oracle_exports(oracle_mod):
+    lib = ctypes.CDLL(oracle_mod.build(force=False))
+    text = open(os.path.join(ROOT, "oracle", "sas_oracle.h")).read()
+    for n in set(re.findall(r"\b(oracle_[a-z_]+)\s*\(", text)):
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.sas_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.sas_status_string(99).decode() == "unknown status"
+
+
+# Fake, 16-byte aligned device addresses: every call below fails a host check
+# (or is a size query / empty call) before any pointer is dereferenced.
+A = ctypes.c_void_p(0x10000)
+MIS = ctypes.c_void_p(0x10004)
+STREAM = None
+
+
+def shape(**kw):
+    base = dict(batch=1, hq=4, hkv=2, tq=256, tk=256, d=128, ds=32, block=64, hks=0, sm_scale=0.0,
+                sel_scale=0.0, dtype=ops.SAS_BF16)
+    base.update(kw)
+    return ops.make_shape(**base)
+
+
+def fwd(lib, sh, **ptrs):
+    p = dict(q=A, k=A, v=A, qs=A, ks=A, lam=A, o=A, lse=A)
+    p.update(ptrs)
+    return lib.sas_attn_fwd(ctypes.byref(sh) if sh is not None else None, p["q"], p["k"], p["v"],
+                            p["qs"], p["ks"], p["lam"], p["o"], p["lse"], STREAM)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=3), 2),                 # hq % hkv
+    (dict(hks=3), 2),                # hq % hks
+    (dict(tq=300), 2),               # tq > tk
+    (dict(tq=0), 2),
+    (dict(batch=-1), 2),
+    (dict(dtype=7), 3),
+    (dict(sel_dtype=ops.SAS_F32), 3),  # mixed dtypes
+    (dict(block=32), 5),
+    (dict(tk=250, tq=250), 5),       # tk % 64
+    (dict(d=96), 5),
+    (dict(ds=24), 5),
+    (dict(dtype=ops.SAS_F32, sel_dtype=ops.SAS_F32, d=128), 5),  # fp32 path is d=64 only
+])
+def test_fwd_shape_checks(lib, kw, code):
+    assert fwd(lib, shape(**kw)) == code
+
+
+def test_fwd_pointer_checks(lib):
+    assert fwd(lib, None) == 1
+    for n in ("q", "k", "v", "qs", "ks", "lam", "o", "lse"):
+        assert fwd(lib, shape(), **{n: None}) == 1, n
+        assert fwd(lib, shape(), **{n: MIS}) == 4, n
+
+
+def test_empty_batch_is_noop(lib):
+    assert fwd(lib, shape(batch=0)) == 0
+    assert lib.sas_gate_scores(ctypes.byref(shape(batch=0)), A, A, A, None, STREAM) == 0
+
+
+def test_gate_checks(lib):
+    assert lib.sas_gate_scores(ctypes.byref(shape()), None, A, A, None, STREAM) == 1
+    assert lib.sas_gate_scores(ctypes.byref(shape()), A, A, A, MIS, STREAM) == 4
+
+
+def test_topk_checks(lib):
+    sh = shape()
+    assert lib.sas_topk_blocks(ctypes.byref(sh), 0, 0, A, A, A, A, STREAM) == 2
+    assert lib.sas_topk_blocks(ctypes.byref(sh), 4, 2, A, A, A, A, STREAM) == 2
+    assert lib.sas_topk_blocks(ctypes.byref(sh), 4, 0, A, A, None, A, STREAM) == 1
+    assert lib.sas_topk_blocks(ctypes.byref(sh), 4, 0, A, A, A, MIS, STREAM) == 4
+    big = shape(tk=1 << 20, tq=64)  # nb + K floats of LDS per row exceed the kernel's limit
+    assert lib.sas_topk_blocks(ctypes.byref(big), 4, 0, A, A, A, A, STREAM) == 5
+
+
+def bwd(lib, sh, ws, n, **ptrs):
+    names = ("q", "k", "v", "o", "dout", "lse", "qs", "ks", "lam", "dq", "dk", "dv", "dqs", "dks")
+    p = {k: A for k in names}
+    p.update(ptrs)
+    dz = ptrs.get("dz", A)
+    return lib.sas_attn_bwd(ctypes.byref(sh), *[p[k] for k in names], dz, ws,
+                            ctypes.byref(n) if n is not None else None, STREAM)
+
+
+def test_bwd_workspace_query_and_checks(lib):
+    sh = shape()
+    n = ctypes.c_size_t(0)
+    assert bwd(lib, sh, None, n) == 0
+    rows = 1 * 4 * 256
+    need_min = rows * 4 + 1 * 2 * 4 * 32 * 4  # delta + dks accumulator
+    assert n.value >= need_min
+    n2 = ctypes.c_size_t(0)
+    assert bwd(lib, sh, None, n2, dz=None) == 0
+    assert n2.value >= n.value + rows * 4 * 4  # dz kept in the workspace
+    small = ctypes.c_size_t(n.value - 1)
+    assert bwd(lib, sh, A, small) == 6
+    assert bwd(lib, sh, A, None) == 1
+    ok = ctypes.c_size_t(n.value)
+    assert bwd(lib, sh, A, ok, dq=None) == 1
+    assert bwd(lib, sh, A, ok, dks=MIS) == 4
+
+
+def test_sparse_workspace_query_and_checks(lib):
+    sh = shape()
+    n = ctypes.c_size_t(0)
+    assert lib.sas_sparse_fwd(ctypes.byref(sh), 4, *([None] * 7), None, ctypes.byref(n),
+                              STREAM) == 0
+    assert n.value >= 1 * 4 * 256 * 5 * 4
+    small = ctypes.c_size_t(n.value - 1)
+    assert lib.sas_sparse_fwd(ctypes.byref(sh), 4, A, A, A, A, A, A, None, A,
+                              ctypes.byref(small), STREAM) == 6
+    assert lib.sas_sparse_fwd(ctypes.byref(sh), 0, A, A, A, A, A, A, None, A,
+                              ctypes.byref(n), STREAM) == 2
+    assert lib.sas_sparse_fwd(ctypes.byref(sh), 4, A, A, A, None, A, A, None, A,
+                              ctypes.byref(n), STREAM) == 1
