@@ -1,0 +1,253 @@
+#!/usr/bin/env python
+"""Benchmark of the SAS gated block-sparse attention hot path on one MI355X.
+
+One step is one pass of the whole hot path on resident synthetic inputs:
+  train_32k          gate normaliser -> gated forward -> backward (dq, dk, dv,
+                     dz, dqs, dks): batch 1, 32 query / 8 kv heads, d 128,
+                     T 32768, 64-token blocks, selector dim 32, bf16
+  prefill_32k_top16  top-K block selection -> top-K sparse forward (K = 16)
+  decode_64k_top8    top-K selection -> sparse decode, 16 sequences x 64k keys
+The headline value is the training fwd+bwd rate at 32k in TFLOP/s counting
+attended (row, key) pairs only (forward 4*d flop per pair, backward 10*d).
+Times come from HIP events recorded on the stream the kernels run on.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "gated-attn fwd+bwd TFLOP/s @32k bf16 (% MFMA peak); top-K sparse fwd TFLOP/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(tq, tk):
+    """Attended (row, key) pairs of one head of dense causal attention."""
+    qoff = tk - tq
+    return sum(qoff + i + 1 for i in range(tq))
+
+
+def sparse_pairs(w):
+    """Attended pairs of one head under a top-K block budget (current block
+    causal + min(K, c) full historical blocks)."""
+    tot = 0
+    for i in range(w.tq):
+        t = w.tk - w.tq + i
+        c = t // w.block
+        tot += min(w.topk, c) * w.block + (t - c * w.block + 1)
+    return tot
+
+
+def cpu_baseline(T: int):
+    """The fp64 oracle, timed on a bounded sample of the 32k training job."""
+    import numpy as np
+    import oracle
+    from gated_block_sparse_sas_amd import synth
+    oracle.build(force=False)
+    w = synth.WORKLOADS["train_32k"]
+    cpu = synth.draw_all(w)
+    # causal prefix of T tokens of kv group 0 (query heads 0..3)
+    hpg = w.hq // w.hkv
+    x = {
+        "q": synth.to_f64(cpu["q"][:, :hpg, :T]),
+        "k": synth.to_f64(cpu["k"][:, :1, :T]),
+        "v": synth.to_f64(cpu["v"][:, :1, :T]),
+        "qs": synth.to_f64(cpu["qs"][:, :hpg, :T]),
+        "ks": synth.to_f64(cpu["ks"][:, :1, :T // w.block]),
+        "dout": synth.to_f64(cpu["dout"][:, :hpg, :T]),
+    }
+    S = oracle.OracleShape(1, hpg, 1, T, T, w.d, w.ds, w.block)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(S, x["q"], x["k"], x["v"], x["qs"], x["ks"])
+    oracle.attn_bwd(S, x["q"], x["k"], x["v"], x["dout"], x["qs"], x["ks"])
+    dt = time.perf_counter() - t0
+    flop = 14.0 * w.d * hpg * causal_pairs(T, T)
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": ("fp64 oracle forward+backward (dq, dk, dv, dz, dqs, dks) on the causal "
+                   "prefix of %d tokens of kv group 0 (4 query heads) of train_32k; %.1f s; "
+                   "attended flop counted as on the GPU" % (T, dt)),
+        "seconds": dt,
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-sample-t", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (heads and batch "
+              "shard with no exchange; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_block_sparse_sas_amd import ops, synth
+    ops.load()  # raises if libsas.so is missing: there is no fallback
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = synth.WORKLOADS
+    wt, wp, wd = W["train_32k"], W["prefill_32k_top16"], W["decode_64k_top8"]
+
+    t0 = time.time()
+    tr = {n: t.to(dev) for n, t in synth.draw_all(wt).items()}
+    pf = {n: t.to(dev) for n, t in synth.draw_all(wp, ("q", "k", "v", "qs", "ks")).items()}
+    dc = {n: t.to(dev) for n, t in synth.draw_all(wd, ("q", "k", "v", "qs", "ks")).items()}
+    torch.cuda.synchronize()
+    log("inputs resident in HBM (%.1f s)" % (time.time() - t0))
+
+    sh_t = ops.shape_of(tr["q"], tr["k"], tr["qs"], tr["ks"])
+    ws_t = torch.empty(ops.bwd_workspace_bytes(sh_t), dtype=torch.uint8, device=dev)
+    sh_p = ops.make_shape(1, wp.hq, wp.hkv, wp.tq, wp.tk, wp.d, wp.ds, 64, wp.hkv)
+    ws_p = torch.empty(ops.sparse_workspace_bytes(sh_p, wp.topk), dtype=torch.uint8, device=dev)
+    sh_d = ops.make_shape(wd.batch, wd.hq, wd.hkv, wd.tq, wd.tk, wd.d, wd.ds, 64, wd.hkv)
+    ws_d = torch.empty(ops.sparse_workspace_bytes(sh_d, wd.topk), dtype=torch.uint8, device=dev)
+
+    names = ["start", "gate", "fwd", "bwd_dq", "bwd_dkdv", "bwd_dks", "bwd", "pf_topk",
+             "pf_partial", "pf_sparse", "dc_topk", "dc_partial", "dc_sparse"]
+
+    def step(ev):
+        E = {n: ev[n] for n in names}
+        E["start"].record()
+        lam = ops.gate_scores(tr["qs"], tr["ks"], wt.tk)
+        E["gate"].record()
+        o, lse = ops.attn_fwd(tr["q"], tr["k"], tr["v"], tr["qs"], tr["ks"], lam)
+        E["fwd"].record()
+        ops.attn_bwd(tr["q"], tr["k"], tr["v"], o, tr["dout"], lse, tr["qs"], tr["ks"], lam,
+                     ws=ws_t, events=[E["bwd_dq"], E["bwd_dkdv"], E["bwd_dks"]])
+        E["bwd"].record()
+        idx, bias = ops.topk_blocks(pf["qs"], pf["ks"], wp.topk, wp.tk)
+        E["pf_topk"].record()
+        ops.sparse_fwd(pf["q"], pf["k"], pf["v"], idx, bias, ws=ws_p, events=[E["pf_partial"]])
+        E["pf_sparse"].record()
+        idx, bias = ops.topk_blocks(dc["qs"], dc["ks"], wd.topk, wd.tk)
+        E["dc_topk"].record()
+        ops.sparse_fwd(dc["q"], dc["k"], dc["v"], idx, bias, ws=ws_d, events=[E["dc_partial"]])
+        E["dc_sparse"].record()
+
+    def new_events():
+        return {n: torch.cuda.Event(enable_timing=True) for n in names}
+
+    for i in range(args.warmup):
+        step(new_events())
+    torch.cuda.synchronize()
+    log("warmup done (%d steps)" % args.warmup)
+
+    evs = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    log("timed %d steps in %.3f s" % (args.steps, wall))
+
+    def dur(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)  # ms
+
+    part = {
+        "gate": dur("start", "gate"), "fwd": dur("gate", "fwd"),
+        "bwd_dq": dur("fwd", "bwd_dq"), "bwd_dkdv": dur("bwd_dq", "bwd_dkdv"),
+        "bwd_dks": dur("bwd_dkdv", "bwd_dks"), "bwd": dur("fwd", "bwd"),
+        "prefill_topk": dur("bwd", "pf_topk"), "prefill_partial": dur("pf_topk", "pf_partial"),
+        "prefill_sparse": dur("pf_topk", "pf_sparse"), "decode_topk": dur("pf_sparse", "dc_topk"),
+        "decode_partial": dur("dc_topk", "dc_partial"),
+        "decode_sparse": dur("dc_topk", "dc_sparse"),
+    }
+    step_ms = dur("start", "dc_sparse")
+
+    pairs_t = wt.batch * wt.hq * causal_pairs(wt.tq, wt.tk)
+    fl_fwd = 4.0 * wt.d * pairs_t
+    fl_bwd = 10.0 * wt.d * pairs_t
+    t_train = part["gate"] + part["fwd"] + part["bwd"]
+    value = (fl_fwd + fl_bwd) / (t_train * 1e-3) / 1e12
+    pairs_p = wp.batch * wp.hq * sparse_pairs(wp)
+    fl_sp = 4.0 * wp.d * pairs_p
+    sp_tflops = fl_sp / (part["prefill_sparse"] * 1e-3) / 1e12
+    dec_blocks = wd.batch * wd.hq * (min(wd.topk, (wd.tk - 1) // 64) + 1)
+    dec_bytes = dec_blocks * 2 * 64 * wd.d * 2  # K and V of every attended block, bf16
+    dec_gbps = dec_bytes / (part["decode_sparse"] * 1e-3) / 1e9
+
+    # dominant kernel: the key-stationary backward kernel (dK, dV): S, dP, dV
+    # and dK over every attended pair = 8*d flop per pair
+    kern = {"bwd_dkdv": (8.0 * wt.d * pairs_t, part["bwd_dkdv"]),
+            "fwd": (fl_fwd, part["fwd"]),
+            "bwd_dq": (6.0 * wt.d * pairs_t, part["bwd_dq"])}
+    dom = max(kern, key=lambda n: kern[n][1])
+    kflop, kms = kern[dom]
+    achieved = kflop / (kms * 1e-3) / 1e12
+    roofline = {
+        "kernel": {"bwd_dkdv": "bwd_dkdv_kernel<128,32>", "fwd": "attn_fwd_kernel<128,32>",
+                   "bwd_dq": "bwd_dq_kernel<128,32>"}[dom],
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "avg_ms": round(kms, 4),
+        "per_unit": {"bwd_dkdv": "8*d flop per attended pair (S, dP, dV, dK)",
+                     "fwd": "4*d flop per attended pair (S, PV)",
+                     "bwd_dq": "6*d flop per attended pair (S, dP, dQ)"}[dom],
+        "units_per_launch": pairs_t,
+    }
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs shaped like the pages' 32k workloads)",
+        "config": {"workload": "train_32k", "batch": wt.batch, "hq": wt.hq, "hkv": wt.hkv,
+                   "seq_len": wt.tq, "d": wt.d, "block": wt.block, "ds": wt.ds,
+                   "also_in_step": ["prefill_32k_top16", "decode_64k_top8"]},
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "train_ms": round(t_train, 3),
+        "parts_ms": {k: round(v, 4) for k, v in part.items()},
+        "sparse_prefill": {"workload": "prefill_32k_top16", "tflops": round(sp_tflops, 2),
+                           "ms": round(part["prefill_sparse"], 3),
+                           "topk_ms": round(part["prefill_topk"], 3),
+                           "attended_pairs": pairs_p},
+        "decode": {"workload": "decode_64k_top8", "ms": round(part["decode_sparse"], 4),
+                   "topk_ms": round(part["decode_topk"], 4), "kv_bytes": dec_bytes,
+                   "GBps": round(dec_gbps, 1),
+                   "frac_hbm": round(dec_gbps / PEAK_HBM_GBPS, 4)},
+        "roofline": roofline,
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a %d-token sample ..." % args.cpu_sample_t)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_t)
+        log("cpu baseline: %.1f s" % out["cpu_baseline"]["seconds"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -597,7 +597,7 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                                const void* dout, const float* lse, const void* qs,
                                const void* ks, const float* lam, void* dq, void* dk, void* dv,
                                void* dqs, void* dks, float* dz, char* ws, const BwdWs& W,
-                               const Dims& D, hipStream_t st) {
+                               const Dims& D, const StageEvents& E, hipStream_t st) {
   float* delta = (float*)(ws + W.off_delta);
   float* dzp = dz ? dz : (float*)(ws + W.off_dz);
   float* acc = (float*)(ws + W.off_dks);
@@ -610,6 +610,7 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                      (bf16*)dqs, dzp, delta, D, nqt, xg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  E.record(0, st);
   const int nkt = (D.tk + 127) / 128;
   hipLaunchKernelGGL((bwd_dkdv_kernel<HD, DS>), dim3(groups * nkt), dim3(256), 0, st,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
@@ -617,17 +618,21 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                      (bf16*)dv, D, nkt, xg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_dks<bf16>(dzp, qs, acc, dks, D, st);
+  E.record(1, st);
+  e = launch_dks<bf16>(dzp, qs, acc, dks, D, st);
+  E.record(2, st);
+  return e;
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, const void* qs, const void* ks,
                            const float* lam, void* dq, void* dk, void* dv, void* dqs, void* dks,
-                           float* dz, char* ws, const BwdWs& W, const Dims& D, hipStream_t st) {
+                           float* dz, char* ws, const BwdWs& W, const Dims& D,
+                           const StageEvents& E, hipStream_t st) {
 #define SAS_BWD_CASE(HDV, DSV)                                                                  \
   if (D.d == HDV && D.ds == DSV)                                                                \
     return launch_bwd_t<HDV, DSV>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, dz, \
-                                  ws, W, D, st);
+                                  ws, W, D, E, st);
   SAS_BWD_CASE(128, 32)
   SAS_BWD_CASE(128, 16)
   SAS_BWD_CASE(128, 64)

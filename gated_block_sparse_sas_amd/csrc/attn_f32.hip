@@ -295,7 +295,8 @@ template <int DS>
 static hipError_t bwd_f32_t(const void* q, const void* k, const void* v, const void* o,
                             const void* dout, const float* lse, const void* qs, const void* ks,
                             const float* lam, void* dq, void* dk, void* dv, void* dqs, void* dks,
-                            float* dz, char* ws, const BwdWs& W, const Dims& D, hipStream_t st) {
+                            float* dz, char* ws, const BwdWs& W, const Dims& D,
+                            const StageEvents& E, hipStream_t st) {
   float* delta = (float*)(ws + W.off_delta);
   float* dzp = dz ? dz : (float*)(ws + W.off_dz);
   float* acc = (float*)(ws + W.off_dks);
@@ -306,6 +307,7 @@ static hipError_t bwd_f32_t(const void* q, const void* k, const void* v, const v
                      D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  E.record(0, st);
   dim3 g2(D.nb, D.hkv, D.batch);
   hipLaunchKernelGGL((bwd_dkdv_f32_kernel<64, DS>), g2, dim3(64), 0, st, (const float*)q,
                      (const float*)k, (const float*)v, (const float*)dout, lse,
@@ -313,21 +315,25 @@ static hipError_t bwd_f32_t(const void* q, const void* k, const void* v, const v
                      (float*)dv, D);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_dks<float>(dzp, qs, acc, dks, D, st);
+  E.record(1, st);
+  e = launch_dks<float>(dzp, qs, acc, dks, D, st);
+  E.record(2, st);
+  return e;
 }
 
 hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, const void* qs, const void* ks,
                           const float* lam, void* dq, void* dk, void* dv, void* dqs, void* dks,
-                          float* dz, char* ws, const BwdWs& W, const Dims& D, hipStream_t st) {
+                          float* dz, char* ws, const BwdWs& W, const Dims& D,
+                          const StageEvents& E, hipStream_t st) {
   if (D.d != 64) return hipErrorInvalidValue;
   switch (D.ds) {
     case 16:
-      return bwd_f32_t<16>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, dz, ws, W, D, st);
+      return bwd_f32_t<16>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, dz, ws, W, D, E, st);
     case 32:
-      return bwd_f32_t<32>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, dz, ws, W, D, st);
+      return bwd_f32_t<32>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, dz, ws, W, D, E, st);
     case 64:
-      return bwd_f32_t<64>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, dz, ws, W, D, st);
+      return bwd_f32_t<64>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, dz, ws, W, D, E, st);
   }
   return hipErrorInvalidValue;
 }

@@ -122,11 +122,11 @@ sas_status sas_attn_fwd(const sas_shape* shape, const void* q, const void* k, co
   return hip_status(sas::launch_fwd_f32(q, k, v, qs, ks, gate_lse, o, lse, D, st));
 }
 
-sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, const void* v,
-                        const void* o, const void* dout, const float* lse, const void* qs,
-                        const void* ks, const float* gate_lse, void* dq, void* dk, void* dv,
-                        void* dqs, void* dks, float* dz, void* ws, size_t* ws_bytes,
-                        void* stream) {
+static sas_status attn_bwd_impl(const sas_shape* shape, const void* q, const void* k,
+                                const void* v, const void* o, const void* dout, const float* lse,
+                                const void* qs, const void* ks, const float* gate_lse, void* dq,
+                                void* dk, void* dv, void* dqs, void* dks, float* dz, void* ws,
+                                size_t* ws_bytes, const sas::StageEvents& E, void* stream) {
   sas::Dims D;
   sas_status r = resolve(shape, &D);
   if (r != SAS_OK) return r;
@@ -146,9 +146,28 @@ sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, co
   hipStream_t st = (hipStream_t)stream;
   if (shape->dtype == SAS_BF16)
     return hip_status(sas::launch_bwd_bf16(q, k, v, o, dout, lse, qs, ks, gate_lse, dq, dk, dv,
-                                           dqs, dks, dz, (char*)ws, W, D, st));
+                                           dqs, dks, dz, (char*)ws, W, D, E, st));
   return hip_status(sas::launch_bwd_f32(q, k, v, o, dout, lse, qs, ks, gate_lse, dq, dk, dv, dqs,
-                                        dks, dz, (char*)ws, W, D, st));
+                                        dks, dz, (char*)ws, W, D, E, st));
+}
+
+sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse, const void* qs,
+                        const void* ks, const float* gate_lse, void* dq, void* dk, void* dv,
+                        void* dqs, void* dks, float* dz, void* ws, size_t* ws_bytes,
+                        void* stream) {
+  return attn_bwd_impl(shape, q, k, v, o, dout, lse, qs, ks, gate_lse, dq, dk, dv, dqs, dks, dz,
+                       ws, ws_bytes, sas::StageEvents{nullptr, 0}, stream);
+}
+
+sas_status sas_attn_bwd_ev(const sas_shape* shape, const void* q, const void* k, const void* v,
+                           const void* o, const void* dout, const float* lse, const void* qs,
+                           const void* ks, const float* gate_lse, void* dq, void* dk, void* dv,
+                           void* dqs, void* dks, float* dz, void* ws, size_t* ws_bytes,
+                           void* const* events, int32_t n_events, void* stream) {
+  if (n_events < 0 || n_events > 3) return SAS_ERR_SHAPE;
+  return attn_bwd_impl(shape, q, k, v, o, dout, lse, qs, ks, gate_lse, dq, dk, dv, dqs, dks, dz,
+                       ws, ws_bytes, sas::StageEvents{events, n_events}, stream);
 }
 
 sas_status sas_topk_blocks(const sas_shape* shape, int32_t topk, int32_t renorm, const void* qs,
@@ -165,16 +184,17 @@ sas_status sas_topk_blocks(const sas_shape* shape, int32_t topk, int32_t renorm,
                                      shape->sel_dtype == SAS_BF16, (hipStream_t)stream));
 }
 
-sas_status sas_sparse_fwd(const sas_shape* shape, int32_t topk, const void* q, const void* k,
-                          const void* v, const int32_t* idx, const float* bias, void* o,
-                          float* lse, void* ws, size_t* ws_bytes, void* stream) {
+static sas_status sparse_fwd_impl(const sas_shape* shape, int32_t topk, const void* q,
+                                  const void* k, const void* v, const int32_t* idx,
+                                  const float* bias, void* o, float* lse, void* ws,
+                                  size_t* ws_bytes, const sas::StageEvents& E, void* stream) {
   sas::Dims D;
   sas_status r = resolve(shape, &D);
   if (r != SAS_OK) return r;
   if (topk < 1) return SAS_ERR_SHAPE;
   if (!ws_bytes) return SAS_ERR_NULL;
   if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
-  if ((int64_t)D.batch * D.hq * D.tq * topk >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
+  if ((int64_t)D.batch * D.hq * D.tq * (topk + 1) >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
   const size_t need = sas::sparse_workspace(D, topk);
   if (!ws) {
     *ws_bytes = need;
@@ -185,7 +205,23 @@ sas_status sas_sparse_fwd(const sas_shape* shape, int32_t topk, const void* q, c
   if (*ws_bytes < need) return SAS_ERR_WORKSPACE;
   if (D.batch == 0) return SAS_OK;
   return hip_status(sas::launch_sparse(q, k, v, idx, bias, o, lse, (char*)ws, *ws_bytes, topk,
-                                       D, shape->dtype == SAS_BF16, (hipStream_t)stream));
+                                       D, shape->dtype == SAS_BF16, E, (hipStream_t)stream));
+}
+
+sas_status sas_sparse_fwd(const sas_shape* shape, int32_t topk, const void* q, const void* k,
+                          const void* v, const int32_t* idx, const float* bias, void* o,
+                          float* lse, void* ws, size_t* ws_bytes, void* stream) {
+  return sparse_fwd_impl(shape, topk, q, k, v, idx, bias, o, lse, ws, ws_bytes,
+                         sas::StageEvents{nullptr, 0}, stream);
+}
+
+sas_status sas_sparse_fwd_ev(const sas_shape* shape, int32_t topk, const void* q, const void* k,
+                             const void* v, const int32_t* idx, const float* bias, void* o,
+                             float* lse, void* ws, size_t* ws_bytes, void* const* events,
+                             int32_t n_events, void* stream) {
+  if (n_events < 0 || n_events > 1) return SAS_ERR_SHAPE;
+  return sparse_fwd_impl(shape, topk, q, k, v, idx, bias, o, lse, ws, ws_bytes,
+                         sas::StageEvents{events, n_events}, stream);
 }
 
 }  // extern "C"

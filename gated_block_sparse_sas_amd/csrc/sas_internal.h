@@ -6,6 +6,15 @@
 
 namespace sas {
 
+// Optional caller-owned events recorded between the kernels of one call.
+struct StageEvents {
+  void* const* ev;
+  int n;
+  void record(int i, hipStream_t st) const {
+    if (ev && i < n && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], st);
+  }
+};
+
 // Step 1: gate normaliser lam (and optional full log-gate matrix).
 hipError_t launch_gate(const void* qs, const void* ks, float* lam, float* beta, const Dims& D,
                        bool sel_bf16, hipStream_t st);
@@ -29,11 +38,13 @@ BwdWs bwd_workspace(const Dims& D, bool need_dz);
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, const void* qs, const void* ks,
                            const float* lam, void* dq, void* dk, void* dv, void* dqs, void* dks,
-                           float* dz, char* ws, const BwdWs& W, const Dims& D, hipStream_t st);
+                           float* dz, char* ws, const BwdWs& W, const Dims& D,
+                           const StageEvents& E, hipStream_t st);
 hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, const void* qs, const void* ks,
                           const float* lam, void* dq, void* dk, void* dv, void* dqs, void* dks,
-                          float* dz, char* ws, const BwdWs& W, const Dims& D, hipStream_t st);
+                          float* dz, char* ws, const BwdWs& W, const Dims& D,
+                          const StageEvents& E, hipStream_t st);
 
 // Step 5: top-K blocks.
 bool topk_supported(const Dims& D, int K);
@@ -44,6 +55,7 @@ hipError_t launch_topk(const void* qs, const void* ks, int K, int renorm, int* i
 size_t sparse_workspace(const Dims& D, int K);
 hipError_t launch_sparse(const void* q, const void* k, const void* v, const int* idx,
                          const float* bias, void* o, float* lse, char* ws, size_t ws_bytes,
-                         int K, const Dims& D, bool bf16_io, hipStream_t st);
+                         int K, const Dims& D, bool bf16_io, const StageEvents& E,
+                         hipStream_t st);
 
 }  // namespace sas

@@ -132,7 +132,7 @@ size_t sparse_workspace(const Dims& D, int K) {
 template <int HD, typename T>
 static hipError_t launch_sparse_t(const void* q, const void* k, const void* v, const int* idx,
                                   const float* bias, void* o, float* lse, char* ws, int K,
-                                  const Dims& D, hipStream_t st) {
+                                  const Dims& D, const StageEvents& E, hipStream_t st) {
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
   const size_t pairs = rows * (K + 1);
   float* plse = (float*)ws;
@@ -143,6 +143,7 @@ static hipError_t launch_sparse_t(const void* q, const void* k, const void* v, c
                      (const T*)k, (const T*)v, idx, bias, plse, po, D, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  E.record(0, st);
   hipLaunchKernelGGL((sparse_combine_kernel<HD, T>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
                      0, st, (const float*)plse, (const T*)po, (T*)o, lse, D, K);
   return hipGetLastError();
@@ -150,14 +151,15 @@ static hipError_t launch_sparse_t(const void* q, const void* k, const void* v, c
 
 hipError_t launch_sparse(const void* q, const void* k, const void* v, const int* idx,
                          const float* bias, void* o, float* lse, char* ws, size_t ws_bytes,
-                         int K, const Dims& D, bool bf16_io, hipStream_t st) {
+                         int K, const Dims& D, bool bf16_io, const StageEvents& E,
+                         hipStream_t st) {
   (void)ws_bytes;
   if (D.d == 128)
-    return bf16_io ? launch_sparse_t<128, bf16>(q, k, v, idx, bias, o, lse, ws, K, D, st)
-                   : launch_sparse_t<128, float>(q, k, v, idx, bias, o, lse, ws, K, D, st);
+    return bf16_io ? launch_sparse_t<128, bf16>(q, k, v, idx, bias, o, lse, ws, K, D, E, st)
+                   : launch_sparse_t<128, float>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
   if (D.d == 64)
-    return bf16_io ? launch_sparse_t<64, bf16>(q, k, v, idx, bias, o, lse, ws, K, D, st)
-                   : launch_sparse_t<64, float>(q, k, v, idx, bias, o, lse, ws, K, D, st);
+    return bf16_io ? launch_sparse_t<64, bf16>(q, k, v, idx, bias, o, lse, ws, K, D, E, st)
+                   : launch_sparse_t<64, float>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
   return hipErrorInvalidValue;
 }
 

@@ -22,8 +22,9 @@ SAS_F32, SAS_BF16 = 0, 1
 _STATUS = {0: "SAS_OK", 1: "SAS_ERR_NULL", 2: "SAS_ERR_SHAPE", 3: "SAS_ERR_DTYPE",
            4: "SAS_ERR_ALIGN", 5: "SAS_ERR_UNSUPPORTED", 6: "SAS_ERR_WORKSPACE",
            7: "SAS_ERR_HIP"}
-EXPORTS = ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_topk_blocks",
-           "sas_sparse_fwd", "sas_status_string", "sas_last_hip_error")
+EXPORTS = ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_attn_bwd_ev",
+           "sas_topk_blocks", "sas_sparse_fwd", "sas_sparse_fwd_ev", "sas_status_string",
+           "sas_last_hip_error")
 
 
 class SasError(RuntimeError):
@@ -58,8 +59,10 @@ def load():
         lib.sas_attn_bwd.argtypes = [P] * 17 + [SZ, P]
         lib.sas_topk_blocks.argtypes = [P, I32, I32, P, P, P, P, P]
         lib.sas_sparse_fwd.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P]
+        lib.sas_attn_bwd_ev.argtypes = [P] * 17 + [SZ, P, I32, P]
+        lib.sas_sparse_fwd_ev.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P, I32, P]
         for n in ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_topk_blocks",
-                  "sas_sparse_fwd"):
+                  "sas_sparse_fwd", "sas_attn_bwd_ev", "sas_sparse_fwd_ev"):
             getattr(lib, n).restype = ctypes.c_int
         lib.sas_status_string.argtypes = [ctypes.c_int]
         lib.sas_status_string.restype = ctypes.c_char_p
@@ -143,9 +146,22 @@ def bwd_workspace_bytes(sh: Shape, with_dz=True) -> int:
     return n.value
 
 
+def _events(events):
+    if not events:
+        return None, 0
+    for e in events:
+        if e is not None and not e.cuda_event:
+            e.record()  # torch creates the hipEvent on first record; the library re-records it
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) if e is not None
+                                            else None for e in events])
+    return arr, len(events)
+
+
 def attn_bwd(q, k, v, o, dout, lse, qs, ks, gate_lse, block=64, sm_scale=None, sel_scale=None,
-             with_dz=True, ws=None):
-    """Backward of :func:`attn_fwd`.  Returns dict dq, dk, dv, dqs, dks, dz."""
+             with_dz=True, ws=None, events=None):
+    """Backward of :func:`attn_fwd`.  Returns dict dq, dk, dv, dqs, dks, dz.
+    ``events``: optional torch.cuda.Event list recorded between the kernels
+    (see ``sas_attn_bwd_ev``)."""
     sh = shape_of(q, k, qs, ks, block, sm_scale, sel_scale)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -158,10 +174,11 @@ def attn_bwd(q, k, v, o, dout, lse, qs, ks, gate_lse, block=64, sm_scale=None, s
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     n = ctypes.c_size_t(ws.numel())
-    _check("sas_attn_bwd", load().sas_attn_bwd(
+    ev, nev = _events(events)
+    _check("sas_attn_bwd", load().sas_attn_bwd_ev(
         ctypes.byref(sh), _p(q), _p(k), _p(v), _p(o), _p(dout), _p(lse), _p(qs), _p(ks),
         _p(gate_lse), _p(dq), _p(dk), _p(dv), _p(dqs), _p(dks), _p(dz), _p(ws), ctypes.byref(n),
-        _stream(q)))
+        ev, nev, _stream(q)))
     return dict(dq=dq, dk=dk, dv=dv, dqs=dqs, dks=dks, dz=dz)
 
 
@@ -185,7 +202,8 @@ def sparse_workspace_bytes(sh: Shape, topk: int) -> int:
     return n.value
 
 
-def sparse_fwd(q, k, v, idx, bias, block=64, sm_scale=None, ws=None, with_lse=True):
+def sparse_fwd(q, k, v, idx, bias, block=64, sm_scale=None, ws=None, with_lse=True,
+               events=None):
     """Top-K sparse forward (prefill or decode).  Returns (o, lse)."""
     b, hq, tq, d = q.shape
     _, hkv, tk, _ = k.shape
@@ -197,7 +215,8 @@ def sparse_fwd(q, k, v, idx, bias, block=64, sm_scale=None, ws=None, with_lse=Tr
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     n = ctypes.c_size_t(ws.numel())
-    _check("sas_sparse_fwd", load().sas_sparse_fwd(
+    ev, nev = _events(events)
+    _check("sas_sparse_fwd", load().sas_sparse_fwd_ev(
         ctypes.byref(sh), int(topk), _p(q), _p(k), _p(v), _p(idx), _p(bias), _p(o), _p(lse),
-        _p(ws), ctypes.byref(n), _stream(q)))
+        _p(ws), ctypes.byref(n), ev, nev, _stream(q)))
     return o, lse

@@ -132,6 +132,25 @@ sas_status sas_sparse_fwd(const sas_shape* shape, int32_t topk, const void* q, c
                           const void* v, const int32_t* idx, const float* bias, void* o,
                           float* lse, void* ws, size_t* ws_bytes, void* stream);
 
+/* Same as sas_attn_bwd, and records caller-owned hipEvent_t handles on
+ * `stream` at stage boundaries, for timing single kernels:
+ *   events[0] after the query-stationary kernel (dq, dz, dqs),
+ *   events[1] after the key-stationary kernel (dk, dv),
+ *   events[2] after the dks reduction.
+ * n_events may be 0..3; NULL entries are skipped.  Used by the benchmark. */
+sas_status sas_attn_bwd_ev(const sas_shape* shape, const void* q, const void* k, const void* v,
+                           const void* o, const void* dout, const float* lse, const void* qs,
+                           const void* ks, const float* gate_lse, void* dq, void* dk, void* dv,
+                           void* dqs, void* dks, float* dz, void* ws, size_t* ws_bytes,
+                           void* const* events, int32_t n_events, void* stream);
+
+/* Same as sas_sparse_fwd, and records events[0] (if n_events >= 1 and non-NULL)
+ * after the partial kernel, before the merge.  Used by the benchmark. */
+sas_status sas_sparse_fwd_ev(const sas_shape* shape, int32_t topk, const void* q, const void* k,
+                             const void* v, const int32_t* idx, const float* bias, void* o,
+                             float* lse, void* ws, size_t* ws_bytes, void* const* events,
+                             int32_t n_events, void* stream);
+
 /* Static text for a status code. */
 const char* sas_status_string(sas_status status);
 
