@@ -28,6 +28,7 @@
 #include "sas_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace sas {
 
@@ -51,7 +52,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   __shared__ __align__(16) bf16 Vs[kBlock * KP];
   __shared__ __align__(16) bf16 Kt[HD * TP];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const QTile tm = map_q_tile(blockIdx.x, nqt, D, xcd_groups);
   const int b = tm.b, h = tm.h, qt = tm.qt;
@@ -179,27 +181,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
         pacc[mt] = mfma32(av, df[s], pacc[mt]);
       }
     }
-    const bool nomask = j < c_lo;
     float dsum = 0.f;
+    auto softmax_ds = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = exp2f(fmaf(sacc[mt][r], c1, off));
-        if (!nomask) {
-          const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
-          if (u > t) p = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float p = exp2_raw(fmaf(sacc[mt][r], c1, off));
+          if constexpr (MASK) {
+            const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
+            if (u > t) p = 0.f;
+          }
+          const float ds = p * (pacc[mt][r] - dlt);
+          sacc[mt][r] = ds;
+          dsum += ds;
         }
-        const float ds = p * (pacc[mt][r] - dlt);
-        sacc[mt][r] = ds;
-        dsum += ds;
       }
-    }
+    };
+    if (j < c_lo)
+      softmax_ds(std::false_type{});
+    else
+      softmax_ds(std::true_type{});
     dsum += __shfl_xor(dsum, 32);
     if (j == c) {
       sdb = -dsum;  // sum_{j'<c} dbeta = - sum over the current block of dS
     } else if (j < c) {
-      const float dzv = dsum - exp2f(bias2) * sdb;
+      const float dzv = dsum - exp2_raw(bias2) * sdb;
       if (valid && hh == 0) dz[row * D.nb + j] = dzv;
 #pragma unroll
       for (int e = 0; e < DS / 2; ++e) dqsacc[e] = fmaf(dzv, ksv[e], dqsacc[e]);
@@ -263,10 +271,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   __shared__ __align__(16) bf16 Os[64 * KP];  // dO rows
   __shared__ __align__(16) bf16 Qt[HD * TP];
   __shared__ __align__(16) bf16 Ot[HD * TP];  // dO^T
-  __shared__ float offs[2][64];                // log2 offset of (block, row)
-  __shared__ float dls[64];                    // D of row
+  __shared__ __align__(16) float offs[2][64];  // log2 offset of (block, row)
+  __shared__ __align__(16) float dls[64];      // D of row
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   // work item: (b, kv head g, key tile kt), key tiles issued longest first
   int b, g, kt;
@@ -409,17 +418,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       }
     }
     const bool nomask = D.qoff + row0 >= kbase + 127;
+    auto softmax_ds = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int mq = 0; mq < 2; ++mq) {
+      for (int mq = 0; mq < 2; ++mq) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = 32 * mq + (r / 4) * 8 + 4 * hh + (r % 4);
-        float p = exp2f(fmaf(sacc[mq][r], c1, offs[wblk][rr]));
-        if (!nomask && key > D.qoff + row0 + rr) p = 0.f;
-        sacc[mq][r] = p;
-        pacc[mq][r] = p * (pacc[mq][r] - dls[rr]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rb = 32 * mq + r4 * 8 + 4 * hh;  // 4 consecutive rows
+          const f32x4 of4 = *(const f32x4*)&offs[wblk][rb];
+          const f32x4 dl4 = *(const f32x4*)&dls[rb];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = r4 * 4 + e;
+            float p = exp2_raw(fmaf(sacc[mq][r], c1, of4[e]));
+            if constexpr (MASK) {
+              if (key > D.qoff + row0 + rb + e) p = 0.f;
+            }
+            sacc[mq][r] = p;
+            pacc[mq][r] = p * (pacc[mq][r] - dl4[e]);
+          }
+        }
       }
-    }
+    };
+    if (nomask)
+      softmax_ds(std::false_type{});
+    else
+      softmax_ds(std::true_type{});
     // dV^T += dO^T P ;  dK^T += Q^T dS
 #pragma unroll
     for (int mq = 0; mq < 2; ++mq) {

@@ -21,7 +21,7 @@
 //  * O^T = V^T P^T: P never leaves registers.  The B-operand k slots of a lane
 //    are exactly the keys its S^T accumulator holds (two runs of 4), and the
 //    V^T operand is read from LDS with the same key order.
-//  * LDS: K tile row-major [64][d+8], V tile transposed [d][64+8] (padding
+//  * LDS: K tile row-major [64][d+8], V tile transposed [d][64+4] (padding
 //    keeps the 16-byte and 8-byte operand reads bank-conflict free).  The next
 //    tile's global loads are issued before the current tile's MFMAs.
 //  * the gate bias of (row, tile) is recomputed in-kernel: the lane's half of
@@ -32,6 +32,8 @@
 #include "sas_device.h"
 #include "sas_internal.h"
 
+#include <type_traits>
+
 namespace sas {
 
 template <int HD, int DS>
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
     bf16* __restrict__ o, float* __restrict__ lse, Dims D, int nqt, int xcd_groups) {
   constexpr int KP = HD + 8;       // padded K row (elements)
-  constexpr int VP = kBlock + 8;   // padded V^T row
+  constexpr int VP = kBlock + 4;   // padded V^T row (34 dwords: conflict-free b64 reads)
   constexpr int KS = HD / 16;      // k-steps over the head dim
   constexpr int DM = HD / 32;      // 32-row M-tiles of O^T
   constexpr int KCH = kBlock * HD / 8 / 256;  // 16-byte K chunks per thread
@@ -49,7 +51,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __shared__ __align__(16) bf16 Ks[kBlock * KP];
   __shared__ __align__(16) bf16 Vt[HD * VP];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const QTile tm = map_q_tile(blockIdx.x, nqt, D, xcd_groups);
   const int b = tm.b, h = tm.h, qt = tm.qt;
@@ -124,16 +127,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     }
   };
 
-  gload(0);
-  for (int j = 0; j <= c_end; ++j) {
-    __syncthreads();
-    sstore();
-    __syncthreads();
-    if (j < c_end) gload(j + 1);
-    if (j > c_hi) continue;  // past this wave's last block
-
-    // log2-domain gate bias of this lane's row for block j
-    float bias2 = 0.f;
+  // One key tile.  MASK: causal mask and per-lane block test (only the at
+  // most two tiles that hold some lane's current block need it).
+  auto tile = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    float bias2 = 0.f;  // log2-domain gate bias of this lane's row for block j
     if (j < c_hi) {
       const bf16* kr = ksb + (size_t)j * DS;
       float part = 0.f;
@@ -142,7 +140,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       part += __shfl_xor(part, 32);
       if (j < c) bias2 = (D.sel_scale * part - lam_t) * kLog2e;
     }
-
     // S^T tile: two 32-key M-tiles x 32 queries
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -153,38 +150,43 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         sacc[mt] = mfma32(a, qf[s], sacc[mt]);
       }
     }
-    const bool nomask = j < c_lo;
+    // row max on the raw scores (c1 > 0, bias2 is constant over the tile)
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = fmaf(sacc[mt][r], c1, bias2);
-        if (!nomask) {
+        if constexpr (MASK) {
           const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
-          if (u > t) x = -INFINITY;
+          if (u > t) sacc[mt][r] = -INFINITY;
         }
-        sacc[mt][r] = x;
-        mx = fmaxf(mx, x);
+        mx = fmaxf(mx, sacc[mt][r]);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    mx = fmaf(mx, c1, bias2);
+    // Lazy rescaling: the running max only moves when it grows by more than
+    // 8 (log2 units) in some row of the wave, so P <= 2^8 between updates.
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_raw(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
+      m_run = m_new;
+    }
+    const float off = bias2 - m_run;
     float psum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(sacc[mt][r] - m_new);
+        const float p = exp2_raw(fmaf(sacc[mt][r], c1, off));
         sacc[mt][r] = p;
         psum += p;
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
+    l_run += psum;
 
     // O^T += V^T P^T
 #pragma unroll
@@ -204,6 +206,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         }
       }
     }
+  };
+
+  gload(0);
+  for (int j = 0; j <= c_end; ++j) {
+    __syncthreads();
+    sstore();
+    __syncthreads();
+    if (j < c_end) gload(j + 1);
+    if (j > c_hi) continue;  // past this wave's last block
+    if (j < c_lo)
+      tile(j, std::false_type{});
+    else
+      tile(j, std::true_type{});
   }
 
   l_run += __shfl_xor(l_run, 32);

@@ -38,6 +38,37 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Row-major bf16 tiles in LDS with 256-byte rows (d = 128) use an XOR swizzle
+// of the 16-byte chunks: logical chunk c of row r sits at physical chunk
+// c ^ swz(r).  swz permutes the bits of r % 16 so that (a) 16 consecutive
+// rows read at one logical chunk hit 16 distinct chunks (the 16-byte MFMA
+// operand reads) and (b) 4 consecutive rows (aligned to 4) read at an even
+// chunk pair hit 8 distinct chunks (the transposing 8-byte reads).
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+__device__ __forceinline__ int swz_off(int row, int col) {  // element offset of (row, col)
+  return row * 128 + ((((col >> 3) ^ swz16(row)) << 3) | (col & 7));
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// i receives element i % 4 of the 8-byte vectors read by lanes i/4 + 4k,
+// k = 0..3.  If lane 4k + a of a group points at row R0 + k, columns
+// C0 + 4a .. C0 + 4a + 3, lane i ends up with column C0 + i of rows R0..R0+3.
+__device__ __forceinline__ bf16x4 ds_read_tr(const bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// s_waitcnt vmcnt(0) (all of this wave's global loads, including the
+// global-to-LDS ones, have landed); other counters untouched.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 2^x with the hardware exponential (v_exp_f32): no range reduction, so
+// arguments below -126 give 0 or denormals; used on softmax exponents <= 8.
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
