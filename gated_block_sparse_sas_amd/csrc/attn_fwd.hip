@@ -36,11 +36,17 @@
 
 namespace sas {
 
-template <int HD, int DS>
+// SPARSE = true turns the kernel into the merge step of the top-K sparse
+// forward: each row attends only its current block (causal), then folds in
+// the K per-block partials (log-sum-exp, normalised output) computed by the
+// block-stationary kernel in sparse.hip.
+template <int HD, int DS, bool SPARSE = false>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
-    bf16* __restrict__ o, float* __restrict__ lse, Dims D, int nqt, int xcd_groups) {
+    bf16* __restrict__ o, float* __restrict__ lse, Dims D, int nqt, int xcd_groups,
+    const int* __restrict__ sp_idx = nullptr, const float* __restrict__ sp_lse = nullptr,
+    const bf16* __restrict__ sp_o = nullptr, int sp_k = 0) {
   constexpr int KP = HD + 8;       // padded K row (elements)
   constexpr int VP = kBlock + 4;   // padded V^T row (34 dwords: conflict-free b64 reads)
   constexpr int KS = HD / 16;      // k-steps over the head dim
@@ -66,14 +72,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const int c_hi = (D.qoff + min(wq0 + 31, D.tq - 1)) / kBlock;
   const int c_end = (D.qoff + min(qt * 128 + 127, D.tq - 1)) / kBlock;
 
+  // first tile: 0, or in sparse mode the first current block of the workgroup
+  const int j_begin = SPARSE ? (D.qoff + min(qt * 128, D.tq - 1)) / kBlock : 0;
+
   const size_t qrow = ((size_t)b * D.hq + h) * D.tq + qc;
   bf16x8 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(q + qrow * HD + 16 * s + 8 * hh);
   float qsv[DS / 2];
 #pragma unroll
-  for (int e = 0; e < DS / 2; ++e) qsv[e] = to_f32(qs[qrow * DS + hh * (DS / 2) + e]);
-  const float lam_t = c > 0 ? lam[qrow] : 0.f;
+  for (int e = 0; e < DS / 2; ++e) qsv[e] = SPARSE ? 0.f : to_f32(qs[qrow * DS + hh * (DS / 2) + e]);
+  const float lam_t = (!SPARSE && c > 0) ? lam[qrow] : 0.f;
   const bf16* ksb = ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS + hh * (DS / 2);
   const bf16* kb = k + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
   const bf16* vb = v + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
@@ -132,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   auto tile = [&](int j, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     float bias2 = 0.f;  // log2-domain gate bias of this lane's row for block j
-    if (j < c_hi) {
+    if (!SPARSE && j < c_hi) {
       const bf16* kr = ksb + (size_t)j * DS;
       float part = 0.f;
 #pragma unroll
@@ -158,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int r = 0; r < 16; ++r) {
         if constexpr (MASK) {
           const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
-          if (u > t) sacc[mt][r] = -INFINITY;
+          if (u > t || (SPARSE && j != c)) sacc[mt][r] = -INFINITY;
         }
         mx = fmaxf(mx, sacc[mt][r]);
       }
@@ -175,7 +184,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
       m_run = m_new;
     }
-    const float off = bias2 - m_run;
+    // (m_run is -inf only for a row with no visible key yet: all p are 0)
+    const float off = bias2 - (m_run == -INFINITY ? 0.f : m_run);
     float psum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -208,20 +218,56 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     }
   };
 
-  gload(0);
-  for (int j = 0; j <= c_end; ++j) {
+  gload(j_begin);
+  for (int j = j_begin; j <= c_end; ++j) {
     __syncthreads();
     sstore();
     __syncthreads();
     if (j < c_end) gload(j + 1);
     if (j > c_hi) continue;  // past this wave's last block
-    if (j < c_lo)
+    if (!SPARSE && j < c_lo)
       tile(j, std::false_type{});
     else
       tile(j, std::true_type{});
   }
 
   l_run += __shfl_xor(l_run, 32);
+  if constexpr (SPARSE) {
+    // merge the current block (m_run, l_run, oacc) with the row's partials
+    const float lcur = m_run + log2f(l_run);
+    const int* ir = sp_idx + qrow * sp_k;
+    float M = lcur;
+    for (int s2 = 0; s2 < sp_k; ++s2) {
+      const int jj = ir[s2];
+      if (jj >= 0 && jj < c) M = fmaxf(M, sp_lse[qrow * sp_k + s2] * kLog2e);
+    }
+    float S = exp2_raw(lcur - M);
+    for (int s2 = 0; s2 < sp_k; ++s2) {
+      const int jj = ir[s2];
+      if (jj >= 0 && jj < c) S += exp2_raw(sp_lse[qrow * sp_k + s2] * kLog2e - M);
+    }
+    const float L2 = M + log2f(S);
+    const float wcur = exp2_raw(lcur - L2) / l_run;
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) oacc[dm] *= wcur;
+    for (int s2 = 0; s2 < sp_k; ++s2) {
+      const int jj = ir[s2];
+      if (!(jj >= 0 && jj < c)) continue;
+      const float wsl = exp2_raw(sp_lse[qrow * sp_k + s2] * kLog2e - L2);
+      const bf16* src = sp_o + (qrow * sp_k + s2) * HD;
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const bf16x4 pv = *(const bf16x4*)(src + 32 * dm + 8 * rr + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[dm][4 * rr + e] = fmaf(wsl, to_f32(pv[e]), oacc[dm][4 * rr + e]);
+        }
+      }
+    }
+    m_run = L2;
+    l_run = 1.f;
+  }
   if (qi < D.tq) {
     const float inv = 1.f / l_run;
     bf16* orow = o + qrow * HD;
@@ -235,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         *(bf16x4*)(orow + 32 * dm + 8 * rr + 4 * hh) = w;
       }
     }
-    if (hh == 0) lse[qrow] = (m_run + log2f(l_run)) * kLn2;
+    if (hh == 0 && lse != nullptr) lse[qrow] = (m_run + log2f(l_run)) * kLn2;
   }
 }
 
@@ -251,6 +297,30 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, cons
                      (const bf16*)k, (const bf16*)v, (const bf16*)qs, (const bf16*)ks, lam,
                      (bf16*)o, lse, D, nqt, xcd_groups);
   return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t launch_sparse_merge_t(const void* q, const void* k, const void* v,
+                                        const int* idx, const float* plse, const void* po,
+                                        void* o, float* lse_out, int K, const Dims& D,
+                                        hipStream_t st) {
+  const int nqt = (D.tq + 127) / 128;
+  const int groups = D.batch * D.hkv;
+  const int xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
+  const unsigned grid = (unsigned)(D.batch * D.hq * nqt);
+  hipLaunchKernelGGL((attn_fwd_kernel<HD, 16, true>), dim3(grid), dim3(256), 0, st,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)nullptr,
+                     (const bf16*)nullptr, (const float*)nullptr, (bf16*)o, lse_out, D, nqt,
+                     xcd_groups, idx, plse, (const bf16*)po, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_merge(const void* q, const void* k, const void* v, const int* idx,
+                               const float* plse, const void* po, void* o, float* lse,
+                               int K, const Dims& D, hipStream_t st) {
+  if (D.d == 128) return launch_sparse_merge_t<128>(q, k, v, idx, plse, po, o, lse, K, D, st);
+  if (D.d == 64) return launch_sparse_merge_t<64>(q, k, v, idx, plse, po, o, lse, K, D, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const void* qs,

@@ -15,8 +15,20 @@
 // to the workspace; a combine pass merges the K+1 partials of each row by
 // their log-sum-exp.  Entries of idx that are not blocks before c(t) are
 // skipped, so no out-of-range block is ever read.
+//
+// Block-stationary path (prefill, tq >= 128): selection is per token, so the
+// rows of a query tile pick nearly disjoint blocks and a per-tile union of
+// blocks would stream almost all of K/V.  Instead the (row, slot) pairs are
+// inverted into per-(batch, kv head, block) lists (count, scan, scatter);
+// one workgroup per 128-pair chunk of a list loads that block's K and V once,
+// gathers the 128 query rows and runs S^T = K Q^T and O^T = V^T P^T on the
+// MFMA units, writing a normalised partial and its log-sum-exp per pair.  The
+// merge pass (the forward kernel in sparse mode) attends each row's causal
+// current block and folds the partials in.
 #include "sas_device.h"
 #include "sas_internal.h"
+
+#include <algorithm>
 
 namespace sas {
 
@@ -123,10 +135,288 @@ __global__ __launch_bounds__(256) void sparse_combine_kernel(const float* __rest
   if (lse && lane == 0) lse[row] = L;
 }
 
+// ---------------------------------------------------------------------------
+// Block-stationary prefill.
+// ---------------------------------------------------------------------------
+constexpr int kChunk = 128;  // pairs per workgroup of the partial kernel
+
+__global__ void sp_zero_kernel(int* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+// Inversion of the (row, slot) pairs into per-(batch, kv head, block) lists.
+// A workgroup takes kPairsWG consecutive pairs of one (batch, query head), so
+// every pair it sees falls in the nb buckets of one (batch, kv head): it
+// histograms them in LDS and touches each global counter once.
+constexpr int kPairsWG = 4096;
+
+__global__ __launch_bounds__(256) void sp_count_kernel(const int* __restrict__ idx,
+                                                       int* __restrict__ count, Dims D, int K) {
+  extern __shared__ int hist[];  // nb counters
+  const int bh = blockIdx.y, b = bh / D.hq, h = bh % D.hq;
+  const size_t per_bh = (size_t)D.tq * K;
+  const size_t p0 = (size_t)blockIdx.x * kPairsWG;
+  const size_t p1 = min(per_bh, p0 + kPairsWG);
+  for (int x = threadIdx.x; x < D.nb; x += 256) hist[x] = 0;
+  __syncthreads();
+  const int* ib = idx + (size_t)bh * per_bh;
+  for (size_t pp = p0 + threadIdx.x; pp < p1; pp += 256) {
+    const int j = ib[pp];
+    const int c = (D.qoff + (int)(pp / K)) / kBlock;
+    if (j >= 0 && j < c) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
+  int* cb = count + (size_t)(b * D.hkv + h / D.hpg) * D.nb;
+  for (int x = threadIdx.x; x < D.nb; x += 256)
+    if (hist[x]) atomicAdd(&cb[x], hist[x]);
+}
+
+// Exclusive scans of count (-> start) and of ceil(count / kChunk) (-> cstart,
+// with cstart[n] = number of chunks), one workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void sp_scan_kernel(const int* __restrict__ count,
+                                                       int* __restrict__ start,
+                                                       int* __restrict__ cstart, int n) {
+  __shared__ int s1[1024], s2[1024];
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int a = 0, c = 0;
+  for (int i = lo; i < hi; ++i) {
+    a += count[i];
+    c += (count[i] + kChunk - 1) / kChunk;
+  }
+  s1[tid] = a;
+  s2[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int x1 = tid >= off ? s1[tid - off] : 0;
+    const int x2 = tid >= off ? s2[tid - off] : 0;
+    __syncthreads();
+    s1[tid] += x1;
+    s2[tid] += x2;
+    __syncthreads();
+  }
+  a = s1[tid] - a;  // exclusive prefix of this thread's range
+  c = s2[tid] - c;
+  for (int i = lo; i < hi; ++i) {
+    start[i] = a;
+    cstart[i] = c;
+    a += count[i];
+    c += (count[i] + kChunk - 1) / kChunk;
+  }
+  if (tid == 1023) cstart[n] = s2[1023];
+}
+
+// Same decomposition as sp_count_kernel: local histogram, one global
+// reservation per (workgroup, block), then each pair takes a local rank.
+__global__ __launch_bounds__(256) void sp_fill_kernel(const int* __restrict__ idx,
+                                                      const int* __restrict__ start,
+                                                      int* __restrict__ cursor,
+                                                      int* __restrict__ list, Dims D, int K) {
+  extern __shared__ int sh[];  // hist[nb] then base[nb]
+  int* hist = sh;
+  int* base = sh + D.nb;
+  const int bh = blockIdx.y, b = bh / D.hq, h = bh % D.hq;
+  const size_t per_bh = (size_t)D.tq * K;
+  const size_t p0 = (size_t)blockIdx.x * kPairsWG;
+  const size_t p1 = min(per_bh, p0 + kPairsWG);
+  for (int x = threadIdx.x; x < D.nb; x += 256) hist[x] = 0;
+  __syncthreads();
+  const int* ib = idx + (size_t)bh * per_bh;
+  for (size_t pp = p0 + threadIdx.x; pp < p1; pp += 256) {
+    const int j = ib[pp];
+    const int c = (D.qoff + (int)(pp / K)) / kBlock;
+    if (j >= 0 && j < c) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
+  const size_t bucket0 = (size_t)(b * D.hkv + h / D.hpg) * D.nb;
+  for (int x = threadIdx.x; x < D.nb; x += 256) {
+    const int n = hist[x];
+    base[x] = n ? start[bucket0 + x] + atomicAdd(&cursor[bucket0 + x], n) : 0;
+    hist[x] = 0;
+  }
+  __syncthreads();
+  for (size_t pp = p0 + threadIdx.x; pp < p1; pp += 256) {
+    const int j = ib[pp];
+    const int c = (D.qoff + (int)(pp / K)) / kBlock;
+    if (j >= 0 && j < c) list[base[j] + atomicAdd(&hist[j], 1)] = (int)((size_t)bh * per_bh + pp);
+  }
+}
+
+// One workgroup = one chunk of <= 128 pairs of one (batch, kv head, block):
+// wave w takes pairs 32w .. 32w+31; K row-major and V transposed in LDS.
+template <int HD>
+__global__ __launch_bounds__(256, 2) void sp_partial_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ bias, const int* __restrict__ list, const int* __restrict__ start,
+    const int* __restrict__ count, const int* __restrict__ cstart, float* __restrict__ plse,
+    bf16* __restrict__ po, Dims D, int K, int nbk) {
+  constexpr int KP = HD + 8, VP = kBlock + 4, KS = HD / 16, DM = HD / 32;
+  __shared__ __align__(16) bf16 Ks[kBlock * KP];
+  __shared__ __align__(16) bf16 Vt[HD * VP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int w = blockIdx.x;
+  if (w >= cstart[nbk]) return;
+  // bucket of this chunk: largest bk with cstart[bk] <= w (uniform binary search)
+  int lo = 0, hi = nbk - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cstart[mid] <= w) lo = mid; else hi = mid - 1;
+  }
+  const int bk = lo;
+  const int ci = w - cstart[bk];
+  const int n = min(kChunk, count[bk] - ci * kChunk);
+  const int j = bk % D.nb, bg = bk / D.nb;  // bg = b * hkv + g
+  const bf16* kb = k + ((size_t)bg * D.tk + (size_t)j * kBlock) * HD;
+  const bf16* vb = v + ((size_t)bg * D.tk + (size_t)j * kBlock) * HD;
+  // stage K (row-major) and V (transposed)
+  for (int x = tid; x < kBlock * HD / 8; x += 256) {
+    const int r = x / (HD / 8), cc = x % (HD / 8);
+    *(bf16x8*)&Ks[r * KP + cc * 8] = *(const bf16x8*)(kb + (size_t)r * HD + cc * 8);
+  }
+  for (int x = tid; x < 16 * (HD / 8); x += 256) {
+    const int kg = x % 16, dc = x / 16;
+    bf16x8 rv[4];
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) rv[i2] = *(const bf16x8*)(vb + (size_t)(kg * 4 + i2) * HD + dc * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bf16x4 wv = {rv[0][e], rv[1][e], rv[2][e], rv[3][e]};
+      *(bf16x4*)&Vt[(dc * 8 + e) * VP + kg * 4] = wv;
+    }
+  }
+  // this lane's pair
+  const int pi = wave * 32 + l32;
+  const bool valid = pi < n;
+  const int pair = list[start[bk] + ci * kChunk + (valid ? pi : 0)];
+  const size_t row = (size_t)pair / K;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(q + row * HD + 16 * s + 8 * hh);
+  const float bias2 = bias[pair] * kLog2e;
+  const float c1 = D.sm_scale * kLog2e;
+  __syncthreads();
+  if (wave * 32 >= n) return;  // no pair for this wave
+
+  f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const bf16x8 a = *(const bf16x8*)&Ks[(32 * mt + l32) * KP + 16 * s + 8 * hh];
+      sacc[mt] = mfma32(a, qf[s], sacc[mt]);
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m2 = fmaf(mx, c1, bias2);  // row max in log2 units (finite unless bias is -inf)
+  const float off = bias2 - (m2 == -INFINITY ? 0.f : m2);
+  float l = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_raw(fmaf(sacc[mt][r], c1, off));
+      sacc[mt][r] = p;
+      l += p;
+    }
+  l += __shfl_xor(l, 32);
+  f32x16 oacc[DM];
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (bf16)sacc[mt][8 * pp + e];
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) {
+        const bf16* vp = &Vt[(32 * dm + l32) * VP + 32 * mt + 16 * pp + 4 * hh];
+        const bf16x4 lo4 = *(const bf16x4*)vp;
+        const bf16x4 hi4 = *(const bf16x4*)(vp + 8);
+        oacc[dm] = mfma32(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[dm]);
+      }
+    }
+  }
+  if (!valid) return;
+  const bool live = l > 0.f && m2 != -INFINITY;
+  const float inv = live ? 1.f / l : 0.f;
+  bf16* dst = po + (size_t)pair * HD;
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      bf16x4 wv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wv[e] = (bf16)(oacc[dm][4 * rr + e] * inv);
+      *(bf16x4*)(dst + 32 * dm + 8 * rr + 4 * hh) = wv;
+    }
+  }
+  if (hh == 0) plse[pair] = live ? (m2 + log2f(l)) * kLn2 : -INFINITY;
+}
+
+// The block path histograms blocks in LDS: nb <= 8192 (64 KB for the fill).
+static bool use_block_path(const Dims& D) { return D.tq >= 128 && D.nb <= 8192; }
+
+// Workspace: pair path  [plse (rows x (K+1)) | po (rows x (K+1) x d)];
+// block path [count | cursor | start | cstart | list (rows x K) | plse | po (rows x K x d)].
 size_t sparse_workspace(const Dims& D, int K) {
-  const size_t pairs = (size_t)D.batch * D.hq * D.tq * (K + 1);
+  const size_t rows = (size_t)D.batch * D.hq * D.tq;
+  if (use_block_path(D)) {
+    const size_t nbk = (size_t)D.batch * D.hkv * D.nb;
+    const size_t pairs = rows * K;
+    return 3 * align256s(nbk * 4) + align256s((nbk + 1) * 4) + align256s(pairs * 4) +
+           align256s(pairs * 4) + align256s(pairs * D.d * 2);
+  }
+  const size_t pairs = rows * (K + 1);
   const size_t esz = 4;  // partial outputs are stored in the io dtype (<= 4 bytes)
   return align256s(pairs * sizeof(float)) + align256s(pairs * D.d * esz);
+}
+
+template <int HD>
+static hipError_t launch_block_path(const void* q, const void* k, const void* v, const int* idx,
+                                    const float* bias, void* o, float* lse, char* ws, int K,
+                                    const Dims& D, const StageEvents& E, hipStream_t st) {
+  const size_t rows = (size_t)D.batch * D.hq * D.tq;
+  const size_t pairs = rows * K;
+  const int nbk = D.batch * D.hkv * D.nb;
+  char* p = ws;
+  int* count = (int*)p;  p += align256s((size_t)nbk * 4);
+  int* cursor = (int*)p; p += align256s((size_t)nbk * 4);
+  int* start = (int*)p;  p += align256s((size_t)nbk * 4);
+  int* cstart = (int*)p; p += align256s((size_t)(nbk + 1) * 4);
+  int* list = (int*)p;   p += align256s(pairs * 4);
+  float* plse = (float*)p; p += align256s(pairs * 4);
+  bf16* po = (bf16*)p;
+  const unsigned zg = (unsigned)std::min<size_t>((2 * (size_t)nbk + 255) / 256, 4096);
+  hipLaunchKernelGGL(sp_zero_kernel, dim3(zg), dim3(256), 0, st, count, (size_t)nbk);
+  hipLaunchKernelGGL(sp_zero_kernel, dim3(zg), dim3(256), 0, st, cursor, (size_t)nbk);
+  const dim3 ig((unsigned)(((size_t)D.tq * K + kPairsWG - 1) / kPairsWG), D.batch * D.hq);
+  hipLaunchKernelGGL(sp_count_kernel, ig, dim3(256), (size_t)D.nb * 4, st, idx, count, D, K);
+  hipLaunchKernelGGL(sp_scan_kernel, dim3(1), dim3(1024), 0, st, (const int*)count, start, cstart,
+                     nbk);
+  hipLaunchKernelGGL(sp_fill_kernel, ig, dim3(256), (size_t)D.nb * 8, st, idx, (const int*)start,
+                     cursor, list, D, K);
+  // upper bound on the number of chunks; workgroups past the real count exit
+  const size_t max_chunks = pairs / kChunk + (size_t)nbk;
+  hipLaunchKernelGGL((sp_partial_kernel<HD>), dim3((unsigned)max_chunks), dim3(256), 0, st,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, bias, (const int*)list,
+                     (const int*)start, (const int*)count, (const int*)cstart, plse, po, D, K,
+                     nbk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  E.record(0, st);
+  return launch_sparse_merge(q, k, v, idx, plse, po, o, lse, K, D, st);
 }
 
 template <int HD, typename T>
@@ -154,6 +444,10 @@ hipError_t launch_sparse(const void* q, const void* k, const void* v, const int*
                          int K, const Dims& D, bool bf16_io, const StageEvents& E,
                          hipStream_t st) {
   (void)ws_bytes;
+  if (bf16_io && use_block_path(D)) {
+    if (D.d == 128) return launch_block_path<128>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
+    if (D.d == 64) return launch_block_path<64>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
+  }
   if (D.d == 128)
     return bf16_io ? launch_sparse_t<128, bf16>(q, k, v, idx, bias, o, lse, ws, K, D, E, st)
                    : launch_sparse_t<128, float>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);

@@ -116,9 +116,113 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const ST* __restrict__ q
   }
 }
 
+// Lane-per-row variant for many rows and K <= 32: the 64 rows of a wave are
+// consecutive positions of one (batch, head), so every ks row is a
+// wave-uniform load.  Each lane keeps its best KMAX (>= K) blocks sorted in
+// registers; blocks arrive in ascending order and enter only when strictly
+// better than the current last entry, which reproduces the (z desc, j asc)
+// order of the wave-per-row kernel.  Scores use the same sel_dot routine.
+template <int DS, typename ST, int KMAX>
+__global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ qs,
+                                                        const ST* __restrict__ ks, int K,
+                                                        int renorm, int* __restrict__ idx,
+                                                        float* __restrict__ bias, Dims D) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int wave_first = __builtin_amdgcn_readfirstlane(blockIdx.x * 256 + (threadIdx.x & ~63));
+  if (wave_first >= D.tq) return;
+  const int ic = min(i, D.tq - 1);
+  const int c = (D.qoff + ic) / kBlock;
+  const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / kBlock;  // wave max of c
+  const size_t row = ((size_t)b * D.hq + h) * D.tq + ic;
+  float qsv[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
+  const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
+  float tz[KMAX];
+  int tj[KMAX];
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) {
+    tz[r] = -INFINITY;
+    tj[r] = -1;
+  }
+  float m = -INFINITY, s = 0.f;  // log2-domain running log-sum-exp of z
+  for (int j0 = 0; j0 < cw; j0 += 8) {
+    float zz[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int j = j0 + kk;
+      zz[kk] = (j < cw) ? D.sel_scale * sel_dot<DS>(qsv, ksb + (size_t)j * DS) : -INFINITY;
+      if (j >= c) zz[kk] = -INFINITY;
+    }
+    float mc = zz[0];
+#pragma unroll
+    for (int kk = 1; kk < 8; ++kk) mc = fmaxf(mc, zz[kk]);
+    const float mn = fmaxf(m, mc * kLog2e);
+    if (mn != -INFINITY) {
+      float acc = s * exp2f(m - mn);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) acc += exp2f(zz[kk] * kLog2e - mn);
+      s = acc;
+      m = mn;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const float z = zz[kk];
+      if (z > tz[KMAX - 1]) {
+        tz[KMAX - 1] = z;
+        tj[KMAX - 1] = j0 + kk;
+#pragma unroll
+        for (int r = KMAX - 1; r > 0; --r) {
+          if (tz[r] > tz[r - 1]) {
+            const float fz = tz[r];
+            tz[r] = tz[r - 1];
+            tz[r - 1] = fz;
+            const int fj = tj[r];
+            tj[r] = tj[r - 1];
+            tj[r - 1] = fj;
+          }
+        }
+      }
+    }
+  }
+  if (i >= D.tq) return;
+  const int n = c < K ? c : K;
+  float norm = c == 0 ? -INFINITY : (m + log2f(s)) * kLn2;
+  if (renorm) {
+    float mm = tz[0];
+    float ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r)
+      if (r < n) ss += exp2f((tz[r] - mm) * kLog2e);
+    norm = n == 0 ? -INFINITY : mm + log2f(ss) * kLn2;
+  }
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) {
+    if (r < K) {
+      idx[row * K + r] = r < n ? tj[r] : -1;
+      bias[row * K + r] = r < n ? tz[r] - norm : -INFINITY;
+    }
+  }
+}
+
 template <int DS, typename ST>
 static hipError_t launch_topk_t(const void* qs, const void* ks, int K, int renorm, int* idx,
                                 float* bias, const Dims& D, hipStream_t st) {
+  const size_t nrows_all = (size_t)D.batch * D.hq * D.tq;
+  if (nrows_all >= 16384 && K <= 32 && D.hq <= 65535 && D.batch <= 65535) {
+    dim3 grid((D.tq + 255) / 256, D.hq, D.batch);
+    if (K <= 8)
+      hipLaunchKernelGGL((topk_lane_kernel<DS, ST, 8>), grid, dim3(256), 0, st, (const ST*)qs,
+                         (const ST*)ks, K, renorm, idx, bias, D);
+    else if (K <= 16)
+      hipLaunchKernelGGL((topk_lane_kernel<DS, ST, 16>), grid, dim3(256), 0, st, (const ST*)qs,
+                         (const ST*)ks, K, renorm, idx, bias, D);
+    else
+      hipLaunchKernelGGL((topk_lane_kernel<DS, ST, 32>), grid, dim3(256), 0, st, (const ST*)qs,
+                         (const ST*)ks, K, renorm, idx, bias, D);
+    return hipGetLastError();
+  }
   const size_t per = (size_t)(D.nb + K) * sizeof(float);
   int wpg = 4;
   while (wpg > 1 && per * wpg > 65536) wpg >>= 1;
