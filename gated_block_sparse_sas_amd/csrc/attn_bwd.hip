@@ -492,6 +492,199 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 }
 
 // --------------------------------------------------------------------------
+// Key-stationary dK, dV for d = 128 on 16x16x32 MFMA tiles: a workgroup owns
+// one 64-key block (one gate block), each wave 16 keys whose K and V rows
+// stay in registers as B operands; the 16 x 128 dK and dV accumulators are
+// 32 registers each, so the kernel runs three waves per SIMD with no
+// accumulator spills.  32-row Q and dO tiles stream global -> LDS with direct
+// loads into two buffers; the transposed operands (dO^T for dV, Q^T for dK)
+// come from transposing LDS reads of the same row-major tiles.  LDS rows are
+// 76 dwords apart: the 16-row 16-byte reads and the 4-row transposing reads
+// both land on disjoint banks.
+// --------------------------------------------------------------------------
+template <int DS>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, const bf16* __restrict__ qs, const bf16* __restrict__ ks,
+    const float* __restrict__ lam, bf16* __restrict__ dk, bf16* __restrict__ dv, Dims D,
+    int xcd_groups) {
+  constexpr int HD = 128, QT = 32, SL = 19, P = SL * 8, TE = QT * P;
+  constexpr int NI = (QT * SL + 63) / 64;  // direct-load instructions per tile and tensor
+  __shared__ __align__(16) bf16 Q0[TE];
+  __shared__ __align__(16) bf16 Q1[TE];
+  __shared__ __align__(16) bf16 O0[TE];
+  __shared__ __align__(16) bf16 O1[TE];
+  __shared__ __align__(16) float F0[2 * QT];  // log2 offset of each row, then D
+  __shared__ __align__(16) float F1[2 * QT];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const int k4 = i16 >> 2, a4 = i16 & 3;
+  int b, g, j;
+  {
+    const int L = blockIdx.x;
+    int G;
+    if (xcd_groups > 0) {
+      const int xcd = L & 7, s = L >> 3;
+      G = (s % xcd_groups) * 8 + xcd;
+      j = s / xcd_groups;
+    } else {
+      const int bg = D.batch * D.hkv;
+      j = L / bg;
+      G = L % bg;
+    }
+    b = G / D.hkv;
+    g = G % D.hkv;
+  }
+  const int key0 = j * kBlock + wave * 16;
+  const int key = key0 + i16;
+  const size_t kvrow = ((size_t)b * D.hkv + g) * D.tk + key;
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    kf[s] = *(const bf16x8*)(k + kvrow * HD + 32 * s + 8 * g4);
+    vf[s] = *(const bf16x8*)(v + kvrow * HD + 32 * s + 8 * g4);
+  }
+  f32x4 dka[8], dva[8];
+#pragma unroll
+  for (int dm = 0; dm < 8; ++dm) {
+    dka[dm] = f32x4{};
+    dva[dm] = f32x4{};
+  }
+  const float c1 = D.sm_scale * kLog2e;
+  const int qt0 = max(0, j * kBlock - D.qoff) / QT;
+  const int nqt = (D.tq + QT - 1) / QT;
+  const int per_h = nqt - qt0;
+  const int nitems = D.hpg * per_h;
+
+  auto issue = [&](int it, bf16* Qd, bf16* Od) {
+    const int hl = it / per_h, i0 = (qt0 + it % per_h) * QT;
+    const size_t rbase = ((size_t)b * D.hq + g * D.hpg + hl) * D.tq;
+    for (int x = wave; x < NI; x += 4) {
+      const int sl = x * 64 + lane;
+      if (sl < QT * SL) {
+        const int r = sl / SL, ch = sl % SL;
+        const size_t off = (rbase + min(i0 + r, D.tq - 1)) * HD + (ch < 16 ? ch : 0) * 8;
+        __builtin_amdgcn_global_load_lds(q + off, Qd + x * 512, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(dout + off, Od + x * 512, 16, 0, 0);
+      }
+    }
+  };
+  // per-row data of item it: threads 0..31 the log2 offset (gate bias of block
+  // j minus the row's log-sum-exp; -inf where the block is not visible),
+  // threads 32..63 D.
+  auto prep = [&](int it) -> float {
+    const int hl = it / per_h, i0 = (qt0 + it % per_h) * QT;
+    const int h = g * D.hpg + hl;
+    const int r = tid & 31, i = i0 + r;
+    if (tid >= 2 * QT || i >= D.tq) return tid < QT ? -INFINITY : 0.f;
+    const size_t rw = ((size_t)b * D.hq + h) * D.tq + i;
+    if (tid >= QT) return delta[rw];
+    const int c = (D.qoff + i) / kBlock;
+    if (j > c) return -INFINITY;
+    const float l2 = lse[rw] * kLog2e;
+    if (j == c) return -l2;
+    const bf16* qsr = qs + rw * DS;
+    const bf16* ksr = ks + (((size_t)b * D.hks + h / D.hps) * D.nb + j) * DS;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) acc = fmaf(to_f32(qsr[e]), to_f32(ksr[e]), acc);
+    return (D.sel_scale * acc - lam[rw]) * kLog2e - l2;
+  };
+
+  auto compute = [&](int it, const bf16* Qs, const bf16* Os, const float* Fs) {
+    const int i0 = (qt0 + it % per_h) * QT;
+    if (D.qoff + min(i0 + QT - 1, D.tq - 1) < key0) return;  // every row before these keys
+    const bool mask = D.qoff + i0 < key0 + 15;
+    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+    f32x4 pacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int mq = 0; mq < 2; ++mq) {
+        const int o = (16 * mq + i16) * P + 32 * s + 8 * g4;
+        sacc[mq] = mfma16(*(const bf16x8*)&Qs[o], kf[s], sacc[mq]);
+        pacc[mq] = mfma16(*(const bf16x8*)&Os[o], vf[s], pacc[mq]);
+      }
+    }
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq) {
+      const f32x4 of = *(const f32x4*)&Fs[16 * mq + 4 * g4];
+      const f32x4 dl = *(const f32x4*)&Fs[QT + 16 * mq + 4 * g4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = exp2_raw(fmaf(sacc[mq][r], c1, of[r]));
+        if (mask && key > D.qoff + i0 + 16 * mq + 4 * g4 + r) p = 0.f;
+        sacc[mq][r] = p;
+        pacc[mq][r] = p * (pacc[mq][r] - dl[r]);
+      }
+    }
+    // B operands over the 32 rows: slots 0..3 = rows 4*g4 + r, 4..7 = 16 + 4*g4 + r
+    bf16x8 pb, sb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pb[r] = (bf16)sacc[0][r];
+      pb[4 + r] = (bf16)sacc[1][r];
+      sb[r] = (bf16)pacc[0][r];
+      sb[4 + r] = (bf16)pacc[1][r];
+    }
+    const int t0 = (4 * g4 + k4) * P + 4 * a4;
+#pragma unroll
+    for (int dm = 0; dm < 8; ++dm) {
+      const bf16x4 olo = ds_read_tr(&Os[t0 + 16 * dm]);
+      const bf16x4 ohi = ds_read_tr(&Os[t0 + 16 * P + 16 * dm]);
+      dva[dm] = mfma16(__builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7), pb, dva[dm]);
+      const bf16x4 qlo = ds_read_tr(&Qs[t0 + 16 * dm]);
+      const bf16x4 qhi = ds_read_tr(&Qs[t0 + 16 * P + 16 * dm]);
+      dka[dm] = mfma16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), sb, dka[dm]);
+    }
+  };
+
+  if (nitems > 0) {
+    float pv = prep(0);
+    issue(0, Q0, O0);
+    wait_vmem();
+    if (tid < 2 * QT) F0[tid] = pv;
+    __syncthreads();
+    // unrolled by two so that both buffers' code sits in one loop body
+    for (int it = 0; it < nitems; it += 2) {
+      if (it + 1 < nitems) {
+        pv = prep(it + 1);  // its loads go out before the tile's direct loads
+        issue(it + 1, Q1, O1);
+      }
+      compute(it, Q0, O0, F0);
+      wait_vmem();
+      if (it + 1 < nitems && tid < 2 * QT) F1[tid] = pv;
+      __syncthreads();
+      if (it + 1 >= nitems) break;
+      if (it + 2 < nitems) {
+        pv = prep(it + 2);
+        issue(it + 2, Q0, O0);
+      }
+      compute(it + 1, Q1, O1, F1);
+      wait_vmem();
+      if (it + 2 < nitems && tid < 2 * QT) F0[tid] = pv;
+      __syncthreads();
+    }
+  }
+  bf16* kr = dk + kvrow * HD + 4 * g4;
+  bf16* vr = dv + kvrow * HD + 4 * g4;
+#pragma unroll
+  for (int dm = 0; dm < 8; ++dm) {
+    bf16x4 wk, wv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      wk[r] = (bf16)(dka[dm][r] * D.sm_scale);
+      wv[r] = (bf16)dva[dm][r];
+    }
+    *(bf16x4*)(kr + 16 * dm) = wk;
+    *(bf16x4*)(vr + 16 * dm) = wv;
+  }
+}
+
+// --------------------------------------------------------------------------
 // dks[b, s, j, :] = sel_scale * sum over rows (h of s, t with c(t) > j) of
 // dz[t, j] qs[t, :].  Grid: (64-block tile, 256-row chunk, b * hks); the
 // partial sums of a chunk go to an fp32 accumulator with atomics.
@@ -635,6 +828,18 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   E.record(0, st);
+  if constexpr (HD == 128) {
+    hipLaunchKernelGGL((bwd_dkdv16_kernel<DS>), dim3(groups * D.nb), dim3(256), 0, st,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
+                       (const float*)delta, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dk,
+                       (bf16*)dv, D, xg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    E.record(1, st);
+    e = launch_dks<bf16>(dzp, qs, acc, dks, D, st);
+    E.record(2, st);
+    return e;
+  }
   const int nkt = (D.tk + 127) / 128;
   hipLaunchKernelGGL((bwd_dkdv_kernel<HD, DS>), dim3(groups * nkt), dim3(256), 0, st,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,

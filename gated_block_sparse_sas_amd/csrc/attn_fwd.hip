@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __shared__ __align__(16) bf16 Vt[HD * VP];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wave = tid >> 6;  // (a wave-uniform copy here costs registers: keep it per lane)
   const int l32 = lane & 31, hh = lane >> 5;
   const QTile tm = map_q_tile(blockIdx.x, nqt, D, xcd_groups);
   const int b = tm.b, h = tm.h, qt = tm.qt;
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       m_run = m_new;
     }
     // (m_run is -inf only for a row with no visible key yet: all p are 0)
-    const float off = bias2 - (m_run == -INFINITY ? 0.f : m_run);
+    const float off = bias2 - ((SPARSE && m_run == -INFINITY) ? 0.f : m_run);
     float psum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {

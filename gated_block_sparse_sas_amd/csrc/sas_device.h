@@ -37,6 +37,11 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// 16x16x32: A lane l = row l%16, k 8(l/16)..+7; B lane l = column l%16, same k;
+// D lane l = column l%16, rows 4(l/16)..+3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
