@@ -252,6 +252,212 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 }
 
 // --------------------------------------------------------------------------
+// Query-stationary dQ, D, dz, dqs for d = 128 on 16x16x32 MFMA tiles: a
+// workgroup owns 64 query rows, each wave 16 (the query sits in the MFMA
+// column, so D, the dS row sums and the selector terms are per-lane values
+// plus two cross-group adds).  64-key K and V tiles (and the block's ks row)
+// stream global -> LDS with direct loads into two buffers, diagonal tile
+// first; K^T for dQ^T = K^T dS^T comes from transposing reads of the K tile.
+// --------------------------------------------------------------------------
+template <int DS>
+__global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
+    const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
+    bf16* __restrict__ dq, bf16* __restrict__ dqs, float* __restrict__ dz,
+    float* __restrict__ delta, Dims D, int nqt, int xcd_groups) {
+  constexpr int HD = 128, SL = 19, P = SL * 8, TE = kBlock * P;
+  constexpr int NI = (kBlock * SL + 63) / 64;  // direct loads per tile and tensor
+  constexpr int WI = (NI + 3) / 4;             // ... per wave
+  constexpr int DQ = DS / 4;                   // selector dims per lane group
+  __shared__ __align__(16) bf16 K0[TE];
+  __shared__ __align__(16) bf16 K1[TE];
+  __shared__ __align__(16) bf16 V0[TE];
+  __shared__ __align__(16) bf16 V1[TE];
+  __shared__ __align__(16) bf16 S0[DS];
+  __shared__ __align__(16) bf16 S1[DS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const int k4 = i16 >> 2, a4 = i16 & 3;
+  const QTile tm = map_q_tile(blockIdx.x, nqt, D, xcd_groups);
+  const int b = tm.b, h = tm.h, qt = tm.qt;
+  const int g = h / D.hpg, sh = h / D.hps;
+  const int wq0 = qt * 64 + wave * 16;
+  const int qi = wq0 + i16;
+  const bool valid = qi < D.tq;
+  const int qc = min(qi, D.tq - 1);
+  const int t = D.qoff + qc;
+  const int c = t / kBlock;
+  const int c_lo = (D.qoff + min(wq0, D.tq - 1)) / kBlock;
+  const int c_hi = (D.qoff + min(wq0 + 15, D.tq - 1)) / kBlock;
+  const int c_end = (D.qoff + min(qt * 64 + 63, D.tq - 1)) / kBlock;
+  const size_t row = ((size_t)b * D.hq + h) * D.tq + qc;
+
+  // zero dz[row, j] for j >= c(row) (coalesced over the workgroup's rows)
+  for (int r = 0; r < 64; ++r) {
+    const int i = qt * 64 + r;
+    if (i >= D.tq) break;
+    const int cr = (D.qoff + i) / kBlock;
+    float* zr = dz + (((size_t)b * D.hq + h) * D.tq + i) * D.nb;
+    for (int jj = cr + tid; jj < D.nb; jj += 256) zr[jj] = 0.f;
+  }
+
+  bf16x8 qf[4], df[4];
+  float dlt = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    qf[s] = *(const bf16x8*)(q + row * HD + 32 * s + 8 * g4);
+    df[s] = *(const bf16x8*)(dout + row * HD + 32 * s + 8 * g4);
+    const bf16x8 of = *(const bf16x8*)(o + row * HD + 32 * s + 8 * g4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dlt = fmaf(to_f32(df[s][e]), to_f32(of[e]), dlt);
+  }
+  dlt += __shfl_xor(dlt, 16);
+  dlt += __shfl_xor(dlt, 32);
+  if (valid && g4 == 0) delta[row] = dlt;
+  float qsv[DQ], dqsa[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) {
+    qsv[e] = to_f32(qs[row * DS + g4 * DQ + e]);
+    dqsa[e] = 0.f;
+  }
+  const float lam_t = c > 0 ? lam[row] : 0.f;
+  const float l2 = lse[row] * kLog2e;
+  const bf16* ksb = ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS;
+  const bf16* kb = k + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
+  const bf16* vb = v + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
+  const float c1 = D.sm_scale * kLog2e;
+  f32x4 dqa[8];
+#pragma unroll
+  for (int dm = 0; dm < 8; ++dm) dqa[dm] = f32x4{};
+  float sdb = 0.f;
+
+  unsigned toff[WI];  // per-lane element offsets of this wave's direct loads in a tile
+#pragma unroll
+  for (int x = 0; x < WI; ++x) {
+    const int sl = (wave + 4 * x) * 64 + lane, ch = sl % SL;
+    toff[x] = (sl / SL) * HD + (ch < 16 ? ch : 0) * 8;
+  }
+  auto issue = [&](int j, bf16* Kd, bf16* Vd, bf16* Sd) {
+    if (wave == 0 && lane < DS / 8)
+      __builtin_amdgcn_global_load_lds(ksb + (size_t)j * DS + lane * 8, Sd, 16, 0, 0);
+    const bf16* kt = kb + (size_t)j * kBlock * HD;
+    const bf16* vt = vb + (size_t)j * kBlock * HD;
+#pragma unroll
+    for (int x = 0; x < WI; ++x) {
+      const int ins = wave + 4 * x;
+      if (ins < NI && ins * 64 + lane < kBlock * SL) {
+        __builtin_amdgcn_global_load_lds(kt + toff[x], Kd + ins * 512, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + toff[x], Vd + ins * 512, 16, 0, 0);
+      }
+    }
+  };
+
+  auto compute = [&](int j, const bf16* Ks, const bf16* Vs, const bf16* Ss) {
+    if (j > c_hi) return;
+    float bias2 = 0.f;
+    float ksv[DQ];
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) ksv[e] = to_f32(Ss[g4 * DQ + e]);
+    if (j < c_hi) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) part = fmaf(qsv[e], ksv[e], part);
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (j < c) bias2 = (D.sel_scale * part - lam_t) * kLog2e;
+    }
+    const float off = bias2 - l2;
+    f32x4 sacc[4], pacc[4];
+#pragma unroll
+    for (int mk = 0; mk < 4; ++mk) {
+      sacc[mk] = f32x4{};
+      pacc[mk] = f32x4{};
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int mk = 0; mk < 4; ++mk) {
+        const int oo = (16 * mk + i16) * P + 32 * s + 8 * g4;
+        sacc[mk] = mfma16(*(const bf16x8*)&Ks[oo], qf[s], sacc[mk]);
+        pacc[mk] = mfma16(*(const bf16x8*)&Vs[oo], df[s], pacc[mk]);
+      }
+    }
+    const bool mask = j >= c_lo;
+    float dsum = 0.f;
+#pragma unroll
+    for (int mk = 0; mk < 4; ++mk) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = exp2_raw(fmaf(sacc[mk][r], c1, off));
+        if (mask && (j * kBlock + 16 * mk + 4 * g4 + r > t || j > c)) p = 0.f;
+        const float ds = p * (pacc[mk][r] - dlt);
+        sacc[mk][r] = ds;
+        dsum += ds;
+      }
+    }
+    dsum += __shfl_xor(dsum, 16);
+    dsum += __shfl_xor(dsum, 32);
+    if (j == c) {
+      sdb = -dsum;  // sum_{j'<c} dbeta = - sum over the current block of dS
+    } else if (j < c) {
+      const float dzv = dsum - exp2_raw(bias2) * sdb;
+      if (valid && g4 == 0) dz[row * D.nb + j] = dzv;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) dqsa[e] = fmaf(dzv, ksv[e], dqsa[e]);
+    }
+    // dQ^T += K^T dS^T over two 32-key steps; B slots: keys 32ks + 4g4 + r, +16
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst) {
+      bf16x8 sb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sb[r] = (bf16)sacc[2 * kst][r];
+        sb[4 + r] = (bf16)sacc[2 * kst + 1][r];
+      }
+      const int t0 = (32 * kst + 4 * g4 + k4) * P + 4 * a4;
+#pragma unroll
+      for (int dm = 0; dm < 8; ++dm) {
+        const bf16x4 lo = ds_read_tr(&Ks[t0 + 16 * dm]);
+        const bf16x4 hi = ds_read_tr(&Ks[t0 + 16 * P + 16 * dm]);
+        dqa[dm] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), sb, dqa[dm]);
+      }
+    }
+  };
+
+  const int ntiles = c_end + 1;  // tiles c_end, c_end - 1, ..., 0
+  issue(c_end, K0, V0, S0);
+  wait_vmem();
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    if (it + 1 < ntiles) issue(c_end - it - 1, K1, V1, S1);
+    compute(c_end - it, K0, V0, S0);
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 >= ntiles) break;
+    if (it + 2 < ntiles) issue(c_end - it - 2, K0, V0, S0);
+    compute(c_end - it - 1, K1, V1, S1);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  if (valid) {
+    bf16* qr = dq + row * HD + 4 * g4;
+#pragma unroll
+    for (int dm = 0; dm < 8; ++dm) {
+      bf16x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = (bf16)(dqa[dm][r] * D.sm_scale);
+      *(bf16x4*)(qr + 16 * dm) = w;
+    }
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) dqs[row * DS + g4 * DQ + e] = (bf16)(dqsa[e] * D.sel_scale);
+  }
+}
+
+// --------------------------------------------------------------------------
 // Key-stationary: dK, dV.
 // --------------------------------------------------------------------------
 template <int HD, int DS>
@@ -820,12 +1026,21 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   float* acc = (float*)(ws + W.off_dks);
   const int groups = D.batch * D.hkv;
   const int xg = groups % 8 == 0 ? groups / 8 : 0;
+  hipError_t e;
+  if constexpr (HD == 128) {
+    const int nqt64 = (D.tq + 63) / 64;
+    hipLaunchKernelGGL((bwd_dq16_kernel<DS>), dim3(D.batch * D.hq * nqt64), dim3(256), 0, st,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)o,
+                       (const bf16*)dout, lse, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dq,
+                       (bf16*)dqs, dzp, delta, D, nqt64, xg);
+  } else {
   const int nqt = (D.tq + 127) / 128;
   hipLaunchKernelGGL((bwd_dq_kernel<HD, DS>), dim3(D.batch * D.hq * nqt), dim3(256), 0, st,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)o,
                      (const bf16*)dout, lse, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dq,
                      (bf16*)dqs, dzp, delta, D, nqt, xg);
-  hipError_t e = hipGetLastError();
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   E.record(0, st);
   if constexpr (HD == 128) {
