@@ -266,8 +266,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
     const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
     bf16* __restrict__ dq, bf16* __restrict__ dqs, float* __restrict__ dz,
     float* __restrict__ delta, Dims D, int nqt, int xcd_groups) {
-  constexpr int HD = 128, SL = 19, P = SL * 8, TE = kBlock * P;
-  constexpr int NI = (kBlock * SL + 63) / 64;  // direct loads per tile and tensor
+  constexpr int HD = 128, TS = kBlock * 18, TE = TS * 8;  // tile slots, elements
+  constexpr int NI = TS / 64;                  // direct loads per tile and tensor
   constexpr int WI = (NI + 3) / 4;             // ... per wave
   constexpr int DQ = DS / 4;                   // selector dims per lane group
   __shared__ __align__(16) bf16 K0[TE];
@@ -336,10 +336,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
 
   unsigned toff[WI];  // per-lane element offsets of this wave's direct loads in a tile
 #pragma unroll
-  for (int x = 0; x < WI; ++x) {
-    const int sl = (wave + 4 * x) * 64 + lane, ch = sl % SL;
-    toff[x] = (sl / SL) * HD + (ch < 16 ? ch : 0) * 8;
-  }
+  for (int x = 0; x < WI; ++x) toff[x] = tslot_src(min((wave + 4 * x) * 64 + lane, TS - 1));
   auto issue = [&](int j, bf16* Kd, bf16* Vd, bf16* Sd) {
     if (wave == 0 && lane < DS / 8)
       __builtin_amdgcn_global_load_lds(ksb + (size_t)j * DS + lane * 8, Sd, 16, 0, 0);
@@ -348,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
 #pragma unroll
     for (int x = 0; x < WI; ++x) {
       const int ins = wave + 4 * x;
-      if (ins < NI && ins * 64 + lane < kBlock * SL) {
+      if (ins < NI) {
         __builtin_amdgcn_global_load_lds(kt + toff[x], Kd + ins * 512, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vt + toff[x], Vd + ins * 512, 16, 0, 0);
       }
@@ -380,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int mk = 0; mk < 4; ++mk) {
-        const int oo = (16 * mk + i16) * P + 32 * s + 8 * g4;
+        const int oo = trow(i16) + 2304 * mk + 32 * s + 8 * g4;
         sacc[mk] = mfma16(*(const bf16x8*)&Ks[oo], qf[s], sacc[mk]);
         pacc[mk] = mfma16(*(const bf16x8*)&Vs[oo], df[s], pacc[mk]);
       }
@@ -417,11 +414,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
         sb[r] = (bf16)sacc[2 * kst][r];
         sb[4 + r] = (bf16)sacc[2 * kst + 1][r];
       }
-      const int t0 = (32 * kst + 4 * g4 + k4) * P + 4 * a4;
+      const int t0 = trow(4 * g4 + k4) + 4608 * kst + 4 * a4, t1 = t0 + 2304;
 #pragma unroll
       for (int dm = 0; dm < 8; ++dm) {
         const bf16x4 lo = ds_read_tr(&Ks[t0 + 16 * dm]);
-        const bf16x4 hi = ds_read_tr(&Ks[t0 + 16 * P + 16 * dm]);
+        const bf16x4 hi = ds_read_tr(&Ks[t1 + 16 * dm]);
         dqa[dm] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), sb, dqa[dm]);
       }
     }
@@ -704,9 +701,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // 32 registers each, so the kernel runs three waves per SIMD with no
 // accumulator spills.  32-row Q and dO tiles stream global -> LDS with direct
 // loads into two buffers; the transposed operands (dO^T for dV, Q^T for dK)
-// come from transposing LDS reads of the same row-major tiles.  LDS rows are
-// 76 dwords apart: the 16-row 16-byte reads and the 4-row transposing reads
-// both land on disjoint banks.
+// come from transposing LDS reads of the same row-major tiles, laid out by
+// trow() so that both kinds of read hit disjoint banks.
 // --------------------------------------------------------------------------
 template <int DS>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
@@ -715,8 +711,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     const float* __restrict__ delta, const bf16* __restrict__ qs, const bf16* __restrict__ ks,
     const float* __restrict__ lam, bf16* __restrict__ dk, bf16* __restrict__ dv, Dims D,
     int xcd_groups) {
-  constexpr int HD = 128, QT = 32, SL = 19, P = SL * 8, TE = QT * P;
-  constexpr int NI = (QT * SL + 63) / 64;  // direct-load instructions per tile and tensor
+  constexpr int HD = 128, QT = 32, TS = QT * 18, TE = TS * 8;  // tile slots, elements
+  constexpr int NI = TS / 64;              // direct-load instructions per tile and tensor
   __shared__ __align__(16) bf16 Q0[TE];
   __shared__ __align__(16) bf16 Q1[TE];
   __shared__ __align__(16) bf16 O0[TE];
@@ -769,13 +765,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     const int hl = it / per_h, i0 = (qt0 + it % per_h) * QT;
     const size_t rbase = ((size_t)b * D.hq + g * D.hpg + hl) * D.tq;
     for (int x = wave; x < NI; x += 4) {
-      const int sl = x * 64 + lane;
-      if (sl < QT * SL) {
-        const int r = sl / SL, ch = sl % SL;
-        const size_t off = (rbase + min(i0 + r, D.tq - 1)) * HD + (ch < 16 ? ch : 0) * 8;
-        __builtin_amdgcn_global_load_lds(q + off, Qd + x * 512, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(dout + off, Od + x * 512, 16, 0, 0);
-      }
+      const unsigned so = tslot_src(x * 64 + lane);
+      const int r = so / HD;
+      const size_t off = (rbase + min(i0 + r, D.tq - 1)) * HD + (so % HD);
+      __builtin_amdgcn_global_load_lds(q + off, Qd + x * 512, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dout + off, Od + x * 512, 16, 0, 0);
     }
   };
   // per-row data of item it: threads 0..31 the log2 offset (gate bias of block
@@ -810,7 +804,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int mq = 0; mq < 2; ++mq) {
-        const int o = (16 * mq + i16) * P + 32 * s + 8 * g4;
+        const int o = trow(i16) + 2304 * mq + 32 * s + 8 * g4;
         sacc[mq] = mfma16(*(const bf16x8*)&Qs[o], kf[s], sacc[mq]);
         pacc[mq] = mfma16(*(const bf16x8*)&Os[o], vf[s], pacc[mq]);
       }
@@ -836,14 +830,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
       sb[r] = (bf16)pacc[0][r];
       sb[4 + r] = (bf16)pacc[1][r];
     }
-    const int t0 = (4 * g4 + k4) * P + 4 * a4;
+    const int t0 = trow(4 * g4 + k4) + 4 * a4, t1 = t0 + 2304;
 #pragma unroll
     for (int dm = 0; dm < 8; ++dm) {
       const bf16x4 olo = ds_read_tr(&Os[t0 + 16 * dm]);
-      const bf16x4 ohi = ds_read_tr(&Os[t0 + 16 * P + 16 * dm]);
+      const bf16x4 ohi = ds_read_tr(&Os[t1 + 16 * dm]);
       dva[dm] = mfma16(__builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7), pb, dva[dm]);
       const bf16x4 qlo = ds_read_tr(&Qs[t0 + 16 * dm]);
-      const bf16x4 qhi = ds_read_tr(&Qs[t0 + 16 * P + 16 * dm]);
+      const bf16x4 qhi = ds_read_tr(&Qs[t1 + 16 * dm]);
       dka[dm] = mfma16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), sb, dka[dm]);
     }
   };

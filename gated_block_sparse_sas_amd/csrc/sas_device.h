@@ -66,6 +66,21 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// LDS layout of 128-wide bf16 tiles that are read both as 16-byte MFMA row
+// operands (16 consecutive rows per instruction) and by transposing 8-byte
+// reads (16 rows, 32 lanes = 8 rows per pass): rows 144 elements (72 dwords)
+// apart.  Measured with SQ_LDS_BANK_CONFLICT on gfx950, this pitch gives no
+// bank conflicts for either kind of read, where 68 and 76 dwords conflict on
+// both.  Direct global -> LDS loads fill it 18 slots of 16 bytes per row: 16
+// data slots and 2 padding slots.
+__device__ __forceinline__ constexpr int trow(int r) { return 144 * r; }
+// Element offset, within a row-major [rows][128] global tile, of the data the
+// direct load of LDS slot s carries (padding slots reload chunk 0 of their row).
+__device__ __forceinline__ unsigned tslot_src(int s) {
+  const int r = s / 18, ch = s % 18;
+  return (unsigned)(r * 128 + (ch < 16 ? ch : 0) * 8);
+}
+
 // s_waitcnt vmcnt(0) (all of this wave's global loads, including the
 // global-to-LDS ones, have landed); other counters untouched.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
