@@ -17,6 +17,7 @@ Times come from HIP events recorded on the stream the kernels run on.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -90,6 +91,43 @@ def cpu_baseline(T: int):
     }
 
 
+# Kernel symbol of each timed part, as a profiler lists it, and the sources it
+# is built from (a change to any of them voids stored HBM-traffic counters).
+KERNELS = {
+    "bwd_dkdv": ("bwd_dkdv16_kernel<32>", ("attn_bwd.hip", "sas_device.h", "sas_internal.h")),
+    "bwd_dq": ("bwd_dq16_kernel<32>", ("attn_bwd.hip", "sas_device.h", "sas_internal.h")),
+    "fwd": ("attn_fwd_kernel<128, 32, false>", ("attn_fwd.hip", "sas_device.h", "sas_internal.h")),
+}
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "gated_block_sparse_sas_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(part):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the factor a plain copy
+    of known size gave).  None when no summary exists or the kernel's sources
+    changed after the counters were taken."""
+    name, files = KERNELS[part]
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s_train_32k.md" % part)
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("record: "):
+                rec = json.loads(line[len("record: "):])
+    if rec is None or rec.get("kernel") != name or rec.get("src") != source_digest(files):
+        return None
+    return round(rec["fetch_kib"] * rec["fetch_factor"] * 1024 +
+                 rec["write_kib"] * rec["write_factor"] * 1024)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +135,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-sample-t", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, one plain device copy of this many MiB "
+                         "(the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -201,10 +242,11 @@ def main():
     kflop, kms = kern[dom]
     achieved = kflop / (kms * 1e-3) / 1e12
     roofline = {
-        "kernel": {"bwd_dkdv": "bwd_dkdv_kernel<128,32>", "fwd": "attn_fwd_kernel<128,32>",
-                   "bwd_dq": "bwd_dq_kernel<128,32>"}[dom],
+        "kernel": KERNELS[dom][0],
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": stored_traffic(dom),
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
         "avg_ms": round(kms, 4),
         "per_unit": {"bwd_dkdv": "8*d flop per attended pair (S, dP, dV, dK)",
                      "fwd": "4*d flop per attended pair (S, PV)",
@@ -242,6 +284,15 @@ def main():
         "roofline": roofline,
         "wall_s_timed": round(wall, 3),
     }
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy of %d MiB done" % args.calib_copy_mib)
+        del src, dst
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a %d-token sample ..." % args.cpu_sample_t)
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_t)

@@ -719,6 +719,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
   __shared__ __align__(16) bf16 O1[TE];
   __shared__ __align__(16) float F0[2 * QT];  // log2 offset of each row, then D
   __shared__ __align__(16) float F1[2 * QT];
+  // raw row data of the next item, each wave its own 8 rows: qs rows, the ks
+  // row of block j for the item's selector head, and lse, lam, D
+  __shared__ __align__(16) bf16 RQ[4 * 8 * DS];
+  __shared__ __align__(16) bf16 RK[4 * DS];
+  __shared__ __align__(16) float RS[4 * 32];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -760,10 +765,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
   const int nqt = (D.tq + QT - 1) / QT;
   const int per_h = nqt - qt0;
   const int nitems = D.hpg * per_h;
+  constexpr int CH = DS / 8;  // 16-byte chunks of a selector row
+  bf16* const rq = RQ + wave * 8 * DS;
+  bf16* const rk = RK + wave * DS;
+  float* const rs = RS + wave * 32;
 
+  // direct loads of item it: the Q and dO tiles (all waves), and this wave's
+  // raw row data (rows 8 wave .. 8 wave + 7 of the tile)
   auto issue = [&](int it, bf16* Qd, bf16* Od) {
     const int hl = it / per_h, i0 = (qt0 + it % per_h) * QT;
-    const size_t rbase = ((size_t)b * D.hq + g * D.hpg + hl) * D.tq;
+    const int h = g * D.hpg + hl;
+    const size_t rbase = ((size_t)b * D.hq + h) * D.tq;
     for (int x = wave; x < NI; x += 4) {
       const unsigned so = tslot_src(x * 64 + lane);
       const int r = so / HD;
@@ -771,27 +783,50 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
       __builtin_amdgcn_global_load_lds(q + off, Qd + x * 512, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(dout + off, Od + x * 512, 16, 0, 0);
     }
+    const size_t rw0 = rbase + min(i0 + 8 * wave + lane / CH, D.tq - 1);
+    if (lane < 8 * CH)
+      __builtin_amdgcn_global_load_lds(qs + rw0 * DS + (lane % CH) * 8, rq, 16, 0, 0);
+    if (lane < CH)
+      __builtin_amdgcn_global_load_lds(
+          ks + (((size_t)b * D.hks + h / D.hps) * D.nb + j) * DS + lane * 8, rk, 16, 0, 0);
+    // lanes 0-7 lse, 8-15 lam, 16-23 D of the wave's rows (4 bytes per lane)
+    const size_t rw = rbase + min(i0 + 8 * wave + (lane & 7), D.tq - 1);
+    if (lane < 8)
+      __builtin_amdgcn_global_load_lds(lse + rw, rs, 4, 0, 0);
+    else if (lane < 16)
+      __builtin_amdgcn_global_load_lds(lam + rw, rs, 4, 0, 0);
+    else if (lane < 24)
+      __builtin_amdgcn_global_load_lds(delta + rw, rs, 4, 0, 0);
   };
-  // per-row data of item it: threads 0..31 the log2 offset (gate bias of block
-  // j minus the row's log-sum-exp; -inf where the block is not visible),
-  // threads 32..63 D.
-  auto prep = [&](int it) -> float {
-    const int hl = it / per_h, i0 = (qt0 + it % per_h) * QT;
-    const int h = g * D.hpg + hl;
-    const int r = tid & 31, i = i0 + r;
-    if (tid >= 2 * QT || i >= D.tq) return tid < QT ? -INFINITY : 0.f;
-    const size_t rw = ((size_t)b * D.hq + h) * D.tq + i;
-    if (tid >= QT) return delta[rw];
-    const int c = (D.qoff + i) / kBlock;
-    if (j > c) return -INFINITY;
-    const float l2 = lse[rw] * kLog2e;
-    if (j == c) return -l2;
-    const bf16* qsr = qs + rw * DS;
-    const bf16* ksr = ks + (((size_t)b * D.hks + h / D.hps) * D.nb + j) * DS;
+  // per-row data of item it from this wave's raw data (after its loads have
+  // landed): F[r] = log2 offset of row r (gate bias of block j minus the row's
+  // log-sum-exp; -inf where the block is not visible), F[QT + r] = D.  Eight
+  // lanes share a row's selector dot product.
+  auto rowdata = [&](int it, float* Fd) {
+    const int i0 = (qt0 + it % per_h) * QT;
+    const int rr = lane >> 3, part = lane & 7;
+    constexpr int PE = DS / 8;  // selector dims per lane
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < DS; ++e) acc = fmaf(to_f32(qsr[e]), to_f32(ksr[e]), acc);
-    return (D.sel_scale * acc - lam[rw]) * kLog2e - l2;
+    for (int e = 0; e < PE; ++e)
+      acc = fmaf(to_f32(rq[rr * DS + part * PE + e]), to_f32(rk[part * PE + e]), acc);
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (part == 0) {
+      const int r = 8 * wave + rr, i = i0 + r;
+      const int c = (D.qoff + i) / kBlock;
+      const float l2 = rs[rr] * kLog2e;
+      float off;
+      if (i >= D.tq || j > c)
+        off = -INFINITY;
+      else if (j == c)
+        off = -l2;
+      else
+        off = (D.sel_scale * acc - rs[8 + rr]) * kLog2e - l2;
+      Fd[r] = off;
+      Fd[QT + r] = rs[16 + rr];
+    }
   };
 
   auto compute = [&](int it, const bf16* Qs, const bf16* Os, const float* Fs) {
@@ -843,29 +878,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
   };
 
   if (nitems > 0) {
-    float pv = prep(0);
     issue(0, Q0, O0);
     wait_vmem();
-    if (tid < 2 * QT) F0[tid] = pv;
+    rowdata(0, F0);
     __syncthreads();
     // unrolled by two so that both buffers' code sits in one loop body
     for (int it = 0; it < nitems; it += 2) {
-      if (it + 1 < nitems) {
-        pv = prep(it + 1);  // its loads go out before the tile's direct loads
-        issue(it + 1, Q1, O1);
-      }
+      if (it + 1 < nitems) issue(it + 1, Q1, O1);
       compute(it, Q0, O0, F0);
       wait_vmem();
-      if (it + 1 < nitems && tid < 2 * QT) F1[tid] = pv;
+      if (it + 1 < nitems) rowdata(it + 1, F1);
       __syncthreads();
       if (it + 1 >= nitems) break;
-      if (it + 2 < nitems) {
-        pv = prep(it + 2);
-        issue(it + 2, Q0, O0);
-      }
+      if (it + 2 < nitems) issue(it + 2, Q0, O0);
       compute(it + 1, Q1, O1, F1);
       wait_vmem();
-      if (it + 2 < nitems && tid < 2 * QT) F0[tid] = pv;
+      if (it + 2 < nitems) rowdata(it + 2, F0);
       __syncthreads();
     }
   }
