@@ -699,10 +699,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // one 64-key block (one gate block), each wave 16 keys whose K and V rows
 // stay in registers as B operands; the 16 x 128 dK and dV accumulators are
 // 32 registers each, so the kernel runs three waves per SIMD with no
-// accumulator spills.  32-row Q and dO tiles stream global -> LDS with direct
+// accumulator spills.  Work items are (query head of the group, 32-row query
+// tile).  The Q and dO tiles of an item stream global -> LDS with direct
 // loads into two buffers; the transposed operands (dO^T for dV, Q^T for dK)
 // come from transposing LDS reads of the same row-major tiles, laid out by
-// trow() so that both kinds of read hit disjoint banks.
+// trow() so that both kinds of read hit disjoint banks.  Each wave also loads
+// the raw per-row data (qs, the block's ks row, lse, lam, D) of its 8 rows
+// two items ahead and turns it into the row offsets of the next item after
+// its products, so no wave waits on a global load inside the loop.
 // --------------------------------------------------------------------------
 template <int DS>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
@@ -713,17 +717,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     int xcd_groups) {
   constexpr int HD = 128, QT = 32, TS = QT * 18, TE = TS * 8;  // tile slots, elements
   constexpr int NI = TS / 64;              // direct-load instructions per tile and tensor
+  constexpr int XI = (NI + 3) / 4;         // ... per wave (at most)
+  constexpr int CH = DS / 8;               // 16-byte chunks of a selector row
   __shared__ __align__(16) bf16 Q0[TE];
   __shared__ __align__(16) bf16 Q1[TE];
   __shared__ __align__(16) bf16 O0[TE];
   __shared__ __align__(16) bf16 O1[TE];
   __shared__ __align__(16) float F0[2 * QT];  // log2 offset of each row, then D
   __shared__ __align__(16) float F1[2 * QT];
-  // raw row data of the next item, each wave its own 8 rows: qs rows, the ks
-  // row of block j for the item's selector head, and lse, lam, D
-  __shared__ __align__(16) bf16 RQ[4 * 8 * DS];
-  __shared__ __align__(16) bf16 RK[4 * DS];
-  __shared__ __align__(16) float RS[4 * 32];
+  // raw row data of the next two items (two buffers), each wave its own 8
+  // rows: qs rows, the ks row of block j for the item's selector head, and
+  // lse, lam, D
+  __shared__ __align__(16) bf16 RQ[2][4 * 8 * DS];
+  __shared__ __align__(16) bf16 RK[2][4 * DS];
+  __shared__ __align__(16) float RS[2][4 * 32];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -762,35 +769,71 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
   }
   const float c1 = D.sm_scale * kLog2e;
   const int qt0 = max(0, j * kBlock - D.qoff) / QT;
-  const int nqt = (D.tq + QT - 1) / QT;
-  const int per_h = nqt - qt0;
+  const int per_h = (D.tq + QT - 1) / QT - qt0;
   const int nitems = D.hpg * per_h;
-  constexpr int CH = DS / 8;  // 16-byte chunks of a selector row
-  bf16* const rq = RQ + wave * 8 * DS;
-  bf16* const rk = RK + wave * DS;
-  float* const rs = RS + wave * 32;
 
-  // direct loads of item it: the Q and dO tiles (all waves), and this wave's
-  // raw row data (rows 8 wave .. 8 wave + 7 of the tile)
-  auto issue = [&](int it, bf16* Qd, bf16* Od) {
-    const int hl = it / per_h, i0 = (qt0 + it % per_h) * QT;
-    const int h = g * D.hpg + hl;
-    const size_t rbase = ((size_t)b * D.hq + h) * D.tq;
-    for (int x = wave; x < NI; x += 4) {
-      const unsigned so = tslot_src(x * 64 + lane);
-      const int r = so / HD;
-      const size_t off = (rbase + min(i0 + r, D.tq - 1)) * HD + (so % HD);
-      __builtin_amdgcn_global_load_lds(q + off, Qd + x * 512, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(dout + off, Od + x * 512, 16, 0, 0);
+  // byte offsets, within a tile, of this lane's direct loads (row clamp aside)
+  unsigned toff[XI];
+  int trw[XI];
+#pragma unroll
+  for (int x = 0; x < XI; ++x) {
+    const unsigned so = tslot_src(min((wave + 4 * x) * 64 + lane, TS - 1));
+    trw[x] = so / HD;
+    toff[x] = so * 2;
+  }
+
+  // work item: head hl of the group, query tile t (rows i0 = (qt0 + t) QT ..)
+  struct Item {
+    int hl, t;
+  };
+  auto next = [&](Item x) {
+    if (++x.t == per_h) {
+      x.t = 0;
+      ++x.hl;
     }
-    const size_t rw0 = rbase + min(i0 + 8 * wave + lane / CH, D.tq - 1);
+    return x;
+  };
+  auto row0 = [&](Item x) { return (qt0 + x.t) * QT; };
+  auto head_row = [&](Item x) { return ((size_t)b * D.hq + g * D.hpg + x.hl) * D.tq; };
+
+  // direct loads of an item's Q and dO tiles (all waves); rows past the end
+  // reload the last row
+  auto issue = [&](Item x, bf16* Qd, bf16* Od) {
+    const int i0 = row0(x);
+    const size_t base = (head_row(x) + i0) * HD * 2;
+    const char* const qb = (const char*)q + base;
+    const char* const ob = (const char*)dout + base;
+    const bool tail = i0 + QT > D.tq;
+    const int rmax = D.tq - 1 - i0;
+#pragma unroll
+    for (int xi = 0; xi < XI; ++xi) {
+      const int ins = wave + 4 * xi;
+      if (ins < NI) {
+        unsigned off = toff[xi];
+        if (tail && trw[xi] > rmax) off -= (unsigned)(trw[xi] - rmax) * HD * 2;
+        __builtin_amdgcn_global_load_lds(qb + off, Qd + ins * 512, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ob + off, Od + ins * 512, 16, 0, 0);
+      }
+    }
+  };
+  // direct loads of this wave's raw row data of an item (rows 8 wave ..
+  // 8 wave + 7 of the tile) into raw buffer rb
+  auto issue_raw = [&](Item x, int rb) {
+    const int i0 = row0(x);
+    const size_t hr = head_row(x);
+    bf16* const rq = RQ[rb] + wave * 8 * DS;
+    bf16* const rk = RK[rb] + wave * DS;
+    float* const rs = RS[rb] + wave * 32;
+    const size_t rw0 = hr + min(i0 + 8 * wave + lane / CH, D.tq - 1);
     if (lane < 8 * CH)
       __builtin_amdgcn_global_load_lds(qs + rw0 * DS + (lane % CH) * 8, rq, 16, 0, 0);
-    if (lane < CH)
+    if (lane < CH) {
+      const int h = g * D.hpg + x.hl;
       __builtin_amdgcn_global_load_lds(
           ks + (((size_t)b * D.hks + h / D.hps) * D.nb + j) * DS + lane * 8, rk, 16, 0, 0);
+    }
     // lanes 0-7 lse, 8-15 lam, 16-23 D of the wave's rows (4 bytes per lane)
-    const size_t rw = rbase + min(i0 + 8 * wave + (lane & 7), D.tq - 1);
+    const size_t rw = hr + min(i0 + 8 * wave + (lane & 7), D.tq - 1);
     if (lane < 8)
       __builtin_amdgcn_global_load_lds(lse + rw, rs, 4, 0, 0);
     else if (lane < 16)
@@ -798,21 +841,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     else if (lane < 24)
       __builtin_amdgcn_global_load_lds(delta + rw, rs, 4, 0, 0);
   };
-  // per-row data of item it from this wave's raw data (after its loads have
+  // row data of an item from this wave's raw buffer rb (after its loads have
   // landed): F[r] = log2 offset of row r (gate bias of block j minus the row's
   // log-sum-exp; -inf where the block is not visible), F[QT + r] = D.  Eight
   // lanes share a row's selector dot product.
-  auto rowdata = [&](int it, float* Fd) {
-    const int i0 = (qt0 + it % per_h) * QT;
-    const int rr = lane >> 3, part = lane & 7;
+  auto rowdata = [&](Item x, int rb, float* Fd) {
+    const int i0 = row0(x);
     constexpr int PE = DS / 8;  // selector dims per lane
+    const int rr = lane >> 3, part = lane & 7;
+    const bf16* const rq = RQ[rb] + wave * 8 * DS + rr * DS + part * PE;
+    const bf16* const rk = RK[rb] + wave * DS + part * PE;
+    const float* const rs = RS[rb] + wave * 32;
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < PE; ++e)
-      acc = fmaf(to_f32(rq[rr * DS + part * PE + e]), to_f32(rk[part * PE + e]), acc);
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
+    for (int e = 0; e < PE; e += 2) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      acc = __builtin_amdgcn_fdot2_f32_bf16(*(const bf16x2*)(rq + e), *(const bf16x2*)(rk + e),
+                                            acc, false);
+    }
+    acc = sum8_dpp(acc);
     if (part == 0) {
       const int r = 8 * wave + rr, i = i0 + r;
       const int c = (D.qoff + i) / kBlock;
@@ -829,10 +876,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     }
   };
 
-  auto compute = [&](int it, const bf16* Qs, const bf16* Os, const float* Fs) {
-    const int i0 = (qt0 + it % per_h) * QT;
+  auto compute = [&](Item x, const bf16* Qs, const bf16* Os, const float* Fs) {
+    const int i0 = row0(x);
     if (D.qoff + min(i0 + QT - 1, D.tq - 1) < key0) return;  // every row before these keys
-    const bool mask = D.qoff + i0 < key0 + 15;
+    // keys after a row's position are cut: slot (16 mq + r) of this lane is
+    // cut when it is below mlim (no cut away from the diagonal)
+    const int mlim = D.qoff + i0 < key0 + 15 ? key - (D.qoff + i0 + 4 * g4) : -1;
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
     f32x4 pacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
@@ -851,7 +900,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float p = exp2_raw(fmaf(sacc[mq][r], c1, of[r]));
-        if (mask && key > D.qoff + i0 + 16 * mq + 4 * g4 + r) p = 0.f;
+        if (16 * mq + r < mlim) p = 0.f;
         sacc[mq][r] = p;
         pacc[mq][r] = p * (pacc[mq][r] - dl[r]);
       }
@@ -878,23 +927,34 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
   };
 
   if (nitems > 0) {
-    issue(0, Q0, O0);
+    Item cur{0, 0};
+    const Item second = next(cur);
+    issue_raw(cur, 0);
+    if (nitems > 1) issue_raw(second, 1);
+    issue(cur, Q0, O0);
     wait_vmem();
-    rowdata(0, F0);
+    rowdata(cur, 0, F0);
     __syncthreads();
-    // unrolled by two so that both buffers' code sits in one loop body
+    // Item it: the tiles of it + 1 and the raw row data of it + 2 load while
+    // it computes; then the row data of it + 1 is formed from raw data that
+    // landed in the previous item, with no wait on this item's loads.
+    // Unrolled by two so that both buffers' code sits in one loop body.
     for (int it = 0; it < nitems; it += 2) {
-      if (it + 1 < nitems) issue(it + 1, Q1, O1);
-      compute(it, Q0, O0, F0);
+      const Item n1 = next(cur), n2 = next(n1), n3 = next(n2);
+      if (it + 1 < nitems) issue(n1, Q1, O1);
+      if (it + 2 < nitems) issue_raw(n2, 0);
+      compute(cur, Q0, O0, F0);
+      if (it + 1 < nitems) rowdata(n1, 1, F1);
       wait_vmem();
-      if (it + 1 < nitems) rowdata(it + 1, F1);
       __syncthreads();
       if (it + 1 >= nitems) break;
-      if (it + 2 < nitems) issue(it + 2, Q0, O0);
-      compute(it + 1, Q1, O1, F1);
+      if (it + 2 < nitems) issue(n2, Q0, O0);
+      if (it + 3 < nitems) issue_raw(n3, 1);
+      compute(n1, Q1, O1, F1);
+      if (it + 2 < nitems) rowdata(n2, 0, F0);
       wait_vmem();
-      if (it + 2 < nitems) rowdata(it + 2, F0);
       __syncthreads();
+      cur = n2;
     }
   }
   bf16* kr = dk + kvrow * HD + 4 * g4;

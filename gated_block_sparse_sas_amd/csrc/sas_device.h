@@ -81,6 +81,15 @@ __device__ __forceinline__ unsigned tslot_src(int s) {
   return (unsigned)(r * 128 + (ch < 16 ? ch : 0) * 8);
 }
 
+// Sum over each aligned group of 8 lanes, every lane of the group receiving it
+// (DPP: swap neighbours, swap pairs within a quad, then mirror within 8 lanes).
+__device__ __forceinline__ float sum8_dpp(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  return x;
+}
+
 // s_waitcnt vmcnt(0) (all of this wave's global loads, including the
 // global-to-LDS ones, have landed); other counters untouched.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
