@@ -382,15 +382,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
         pacc[mk] = mfma16(*(const bf16x8*)&Vs[oo], df[s], pacc[mk]);
       }
     }
-    const bool mask = j >= c_lo;
+    float pv[4][4];
+#pragma unroll
+    for (int mk = 0; mk < 4; ++mk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[mk][r] = exp2_raw(fmaf(sacc[mk][r], c1, off));
+    if (j >= c_lo) {  // tile meets some row's block: cut keys after the row (or the block)
+      const int mlim = j < c ? kBlock : (j > c ? -1 : t - j * kBlock - 4 * g4);
+#pragma unroll
+      for (int mk = 0; mk < 4; ++mk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * mk + r > mlim) pv[mk][r] = 0.f;
+    }
     float dsum = 0.f;
 #pragma unroll
     for (int mk = 0; mk < 4; ++mk) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float p = exp2_raw(fmaf(sacc[mk][r], c1, off));
-        if (mask && (j * kBlock + 16 * mk + 4 * g4 + r > t || j > c)) p = 0.f;
-        const float ds = p * (pacc[mk][r] - dlt);
+        const float ds = pv[mk][r] * (pacc[mk][r] - dlt);
         sacc[mk][r] = ds;
         dsum += ds;
       }
