@@ -25,8 +25,8 @@
 //    keeps the 16-byte and 8-byte operand reads bank-conflict free).  The next
 //    tile's global loads are issued before the current tile's MFMAs.
 //  * the gate bias of (row, tile) is recomputed in-kernel: the lane's half of
-//    qs (ds/2 values in registers) times the wave-uniform ks row, one
-//    cross-half add; lam comes from the gate kernel.
+//    qs (ds/2 values in registers) times the block's ks row (staged in LDS
+//    with the tile), one cross-half add; lam comes from the gate kernel.
 //  * exp2 domain throughout; tiles past a wave's last block are skipped, the
 //    only masked tiles are the (at most two) diagonal ones.
 #include "sas_device.h"
@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   constexpr int VIT = (VITEMS + 255) / 256;
   __shared__ __align__(16) bf16 Ks[kBlock * KP];
   __shared__ __align__(16) bf16 Vt[HD * VP];
+  __shared__ __align__(16) bf16 Ksel[DS];  // ks row of the tile's block
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;  // (a wave-uniform copy here costs registers: keep it per lane)
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
   for (int e = 0; e < DS / 2; ++e) qsv[e] = SPARSE ? 0.f : to_f32(qs[qrow * DS + hh * (DS / 2) + e]);
   const float lam_t = (!SPARSE && c > 0) ? lam[qrow] : 0.f;
-  const bf16* ksb = ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS + hh * (DS / 2);
+  const bf16* ksb0 = SPARSE ? ks : ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS;
   const bf16* kb = k + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
   const bf16* vb = v + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
   const float c1 = D.sm_scale * kLog2e;
@@ -96,7 +97,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const bf16x8 zero8 = bf16x8{};
   bf16x8 kreg[KCH];
   bf16x8 vreg[VIT][4];
+  bf16x8 sreg = zero8;  // threads 0 .. DS/8-1: a chunk of the next block's ks row
   auto gload = [&](int j) {
+    if (!SPARSE && tid < DS / 8 && j < D.nb) sreg = *(const bf16x8*)(ksb0 + (size_t)j * DS + tid * 8);
 #pragma unroll
     for (int x = 0; x < KCH; ++x) {
       const int id = tid + 256 * x, r = id / (HD / 8), cc = id % (HD / 8);
@@ -117,6 +120,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     }
   };
   auto sstore = [&]() {
+    if (!SPARSE && tid < DS / 8) *(bf16x8*)&Ksel[tid * 8] = sreg;
 #pragma unroll
     for (int x = 0; x < KCH; ++x) {
       const int id = tid + 256 * x, r = id / (HD / 8), cc = id % (HD / 8);
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     constexpr bool MASK = decltype(mask_tag)::value;
     float bias2 = 0.f;  // log2-domain gate bias of this lane's row for block j
     if (!SPARSE && j < c_hi) {
-      const bf16* kr = ksb + (size_t)j * DS;
+      const bf16* kr = Ksel + hh * (DS / 2);
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < DS / 2; ++e) part = fmaf(qsv[e], to_f32(kr[e]), part);
