@@ -21,9 +21,10 @@
 //  * O^T = V^T P^T: P never leaves registers.  The B-operand k slots of a lane
 //    are exactly the keys its S^T accumulator holds (two runs of 4), and the
 //    V^T operand is read from LDS with the same key order.
-//  * LDS: K tile row-major [64][d+8], V tile transposed [d][64+4] (padding
-//    keeps the 16-byte and 8-byte operand reads bank-conflict free).  The next
-//    tile's global loads are issued before the current tile's MFMAs.
+//  * LDS: K and V tiles row-major, double-buffered, filled by direct
+//    global -> LDS loads issued one tile ahead; V^T operands come from
+//    transposing LDS reads.  Row pitches keep both kinds of operand read
+//    bank-conflict free.
 //  * the gate bias of (row, tile) is recomputed in-kernel: the lane's half of
 //    qs (ds/2 values in registers) times the block's ks row (staged in LDS
 //    with the tile), one cross-half add; lam comes from the gate kernel.
@@ -47,16 +48,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     bf16* __restrict__ o, float* __restrict__ lse, Dims D, int nqt, int xcd_groups,
     const int* __restrict__ sp_idx = nullptr, const float* __restrict__ sp_lse = nullptr,
     const bf16* __restrict__ sp_o = nullptr, int sp_k = 0) {
-  constexpr int KP = HD + 8;       // padded K row (elements)
-  constexpr int VP = kBlock + 4;   // padded V^T row (34 dwords: conflict-free b64 reads)
+  constexpr int DC = HD / 8;             // 16-byte chunks of a row
+  constexpr int SK = DC + 1;             // LDS slots per K row (one pad slot)
+  constexpr int SV = HD == 128 ? 18 : 10;  // LDS slots per V row (pads)
+  constexpr int KP = SK * 8, VP = SV * 8;  // row pitches (elements)
+  constexpr int NK = kBlock * SK / 64, NV = kBlock * SV / 64;  // direct loads per tile
   constexpr int KS = HD / 16;      // k-steps over the head dim
   constexpr int DM = HD / 32;      // 32-row M-tiles of O^T
-  constexpr int KCH = kBlock * HD / 8 / 256;  // 16-byte K chunks per thread
-  constexpr int VITEMS = 16 * (HD / 8);       // (4 keys x 8 dims) V items
-  constexpr int VIT = (VITEMS + 255) / 256;
-  __shared__ __align__(16) bf16 Ks[kBlock * KP];
-  __shared__ __align__(16) bf16 Vt[HD * VP];
-  __shared__ __align__(16) bf16 Ksel[DS];  // ks row of the tile's block
+  // Key tiles are double-buffered and filled by direct global -> LDS loads:
+  // K row-major at a 17/9-slot pitch (conflict-free 16-byte operand reads),
+  // V row-major at an 18/10-slot pitch, read transposed (V^T operand) by
+  // transposing 8-byte reads that are conflict-free at that pitch.
+  __shared__ __align__(16) bf16 K0[kBlock * KP];
+  __shared__ __align__(16) bf16 K1[kBlock * KP];
+  __shared__ __align__(16) bf16 V0[kBlock * VP];
+  __shared__ __align__(16) bf16 V1[kBlock * VP];
+  __shared__ __align__(16) bf16 S0[DS];  // ks row of the tile's block
+  __shared__ __align__(16) bf16 S1[DS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;  // (a wave-uniform copy here costs registers: keep it per lane)
@@ -80,9 +88,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   bf16x8 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(q + qrow * HD + 16 * s + 8 * hh);
-  float qsv[DS / 2];
+  // this lane's half of the row's qs, as bf16 pairs for packed dot products
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 qsv[DS / 4];
 #pragma unroll
-  for (int e = 0; e < DS / 2; ++e) qsv[e] = SPARSE ? 0.f : to_f32(qs[qrow * DS + hh * (DS / 2) + e]);
+  for (int e = 0; e < DS / 4; ++e)
+    qsv[e] = SPARSE ? bf16x2{} : *(const bf16x2*)(qs + qrow * DS + hh * (DS / 2) + 2 * e);
   const float lam_t = (!SPARSE && c > 0) ? lam[qrow] : 0.f;
   const bf16* ksb0 = SPARSE ? ks : ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS;
   const bf16* kb = k + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
@@ -94,67 +105,34 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const bf16x8 zero8 = bf16x8{};
-  bf16x8 kreg[KCH];
-  bf16x8 vreg[VIT][4];
-  bf16x8 sreg = zero8;  // threads 0 .. DS/8-1: a chunk of the next block's ks row
-  auto gload = [&](int j) {
-    if (!SPARSE && tid < DS / 8 && j < D.nb) sreg = *(const bf16x8*)(ksb0 + (size_t)j * DS + tid * 8);
-#pragma unroll
-    for (int x = 0; x < KCH; ++x) {
-      const int id = tid + 256 * x, r = id / (HD / 8), cc = id % (HD / 8);
-      const int key = j * kBlock + r;
-      kreg[x] = key < D.tk ? *(const bf16x8*)(kb + (size_t)key * HD + cc * 8) : zero8;
-    }
-#pragma unroll
-    for (int x = 0; x < VIT; ++x) {
-      const int id = tid + 256 * x;
-      if (id < VITEMS) {
-        const int kg = id % 16, dc = id / 16;
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-          const int key = j * kBlock + kg * 4 + i2;
-          vreg[x][i2] = key < D.tk ? *(const bf16x8*)(vb + (size_t)key * HD + dc * 8) : zero8;
-        }
-      }
+  // direct loads of key tile j (every wave takes every fourth instruction):
+  // K, and separately V with the block's ks row
+  auto issue_k = [&](int j, bf16* Kd) __attribute__((always_inline)) {
+    const bf16* kt = kb + (size_t)j * kBlock * HD;
+    for (int x = wave; x < NK; x += 4) {
+      const int sl = x * 64 + lane, r = sl / SK, ch = sl % SK;
+      __builtin_amdgcn_global_load_lds(kt + r * HD + (ch < DC ? ch : 0) * 8, Kd + x * 512, 16, 0,
+                                       0);
     }
   };
-  auto sstore = [&]() {
-    if (!SPARSE && tid < DS / 8) *(bf16x8*)&Ksel[tid * 8] = sreg;
-#pragma unroll
-    for (int x = 0; x < KCH; ++x) {
-      const int id = tid + 256 * x, r = id / (HD / 8), cc = id % (HD / 8);
-      *(bf16x8*)&Ks[r * KP + cc * 8] = kreg[x];
+  auto issue_v = [&](int j, bf16* Vd, bf16* Sd) __attribute__((always_inline)) {
+    const bf16* vt = vb + (size_t)j * kBlock * HD;
+    for (int x = wave; x < NV; x += 4) {
+      const int sl = x * 64 + lane, r = sl / SV, ch = sl % SV;
+      __builtin_amdgcn_global_load_lds(vt + r * HD + (ch < DC ? ch : 0) * 8, Vd + x * 512, 16, 0,
+                                       0);
     }
-#pragma unroll
-    for (int x = 0; x < VIT; ++x) {
-      const int id = tid + 256 * x;
-      if (id < VITEMS) {
-        const int kg = id % 16, dc = id / 16;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bf16x4 w = {vreg[x][0][e], vreg[x][1][e], vreg[x][2][e], vreg[x][3][e]};
-          *(bf16x4*)&Vt[(dc * 8 + e) * VP + kg * 4] = w;
-        }
-      }
-    }
+    if (!SPARSE && tid < DS / 8)
+      __builtin_amdgcn_global_load_lds(ksb0 + (size_t)j * DS + tid * 8, Sd, 16, 0, 0);
   };
+  // per-lane part of the transposing V^T reads: lane 4k + a of each 16-lane
+  // group points at key row 4 hh + k, columns 16 ((lane >> 4) & 1) + 4 a
+  const int vbase = (4 * hh + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // One key tile.  MASK: causal mask and per-lane block test (only the at
-  // most two tiles that hold some lane's current block need it).
-  auto tile = [&](int j, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    float bias2 = 0.f;  // log2-domain gate bias of this lane's row for block j
-    if (!SPARSE && j < c_hi) {
-      const bf16* kr = Ksel + hh * (DS / 2);
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < DS / 2; ++e) part = fmaf(qsv[e], to_f32(kr[e]), part);
-      part += __shfl_xor(part, 32);
-      if (j < c) bias2 = (D.sel_scale * part - lam_t) * kLog2e;
-    }
-    // S^T tile: two 32-key M-tiles x 32 queries
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // S^T tile of key tile j from K tile Ks: two 32-key M-tiles x 32 queries
+  auto scores = [&](const bf16* Ks, f32x16* sacc) __attribute__((always_inline)) {
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -162,6 +140,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         const bf16x8 a = *(const bf16x8*)&Ks[(32 * mt + l32) * KP + 16 * s + 8 * hh];
         sacc[mt] = mfma32(a, qf[s], sacc[mt]);
       }
+    }
+  };
+  f32x16 sacc[2];  // scores of the tile being finished
+  // Finish key tile j whose scores are in sacc: softmax update and O^T += V^T
+  // P^T from V tile Vs; meanwhile (NEXT) the scores of tile j + 1 are formed
+  // from K tile Kn, so the exponentials overlap those products.  MASK: causal
+  // mask and per-lane block test (only the at most two tiles that hold some
+  // lane's current block need it).
+  auto finish = [&](int j, auto mask_tag, auto next_tag, const bf16* Vs, const bf16* Ss,
+                    const bf16* Kn) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;
+    float bias2 = 0.f;  // log2-domain gate bias of this lane's row for block j
+    if (!SPARSE && j < c_hi) {
+      const bf16x2* kr = (const bf16x2*)(Ss + hh * (DS / 2));
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS / 4; ++e) part = __builtin_amdgcn_fdot2_f32_bf16(qsv[e], kr[e], part, false);
+      part += __shfl_xor(part, 32);
+      if (j < c) bias2 = (D.sel_scale * part - lam_t) * kLog2e;
     }
     // row max on the raw scores (c1 > 0, bias2 is constant over the tile)
     float mx = -INFINITY;
@@ -188,51 +186,79 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
       m_run = m_new;
     }
+    f32x16 snext[2];
+    if constexpr (NEXT) scores(Kn, snext);
     // (m_run is -inf only for a row with no visible key yet: all p are 0)
     const float off = bias2 - ((SPARSE && m_run == -INFINITY) ? 0.f : m_run);
     float psum = 0.f;
+    bf16x8 pb[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_raw(fmaf(sacc[mt][r], c1, off));
-        sacc[mt][r] = p;
+        pb[mt][r / 8][r % 8] = (bf16)p;
         psum += p;
       }
     }
     l_run += psum;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T: the B slots of a lane are keys 16 pp + 4 hh + (0..3, 8..11)
+    // of M-tile mt, and the transposing reads give V^T in the same key order
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (bf16)sacc[mt][8 * pp + e];
 #pragma unroll
         for (int dm = 0; dm < DM; ++dm) {
-          const bf16* vp = &Vt[(32 * dm + l32) * VP + 32 * mt + 16 * pp + 4 * hh];
-          const bf16x4 lo = *(const bf16x4*)vp;
-          const bf16x4 hi = *(const bf16x4*)(vp + 8);
+          const bf16* vp = &Vs[vbase + (32 * mt + 16 * pp) * VP + 32 * dm];
+          const bf16x4 lo = ds_read_tr(vp);
+          const bf16x4 hi = ds_read_tr(vp + 8 * VP);
           const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[dm] = mfma32(a, pb, oacc[dm]);
+          oacc[dm] = mfma32(a, pb[mt][pp], oacc[dm]);
         }
       }
     }
+    if constexpr (NEXT) {
+      sacc[0] = snext[0];
+      sacc[1] = snext[1];
+    }
+  };
+  auto run = [&](int j, const bf16* Vs, const bf16* Ss, const bf16* Kn)
+      __attribute__((always_inline)) {
+    if (j > c_hi) return;  // past this wave's last block
+    const bool masked = SPARSE || j >= c_lo;
+    if (j + 1 <= c_hi) {
+      if (masked)
+        finish(j, std::true_type{}, std::true_type{}, Vs, Ss, Kn);
+      else
+        finish(j, std::false_type{}, std::true_type{}, Vs, Ss, Kn);
+    } else {
+      finish(j, std::true_type{}, std::false_type{}, Vs, Ss, Kn);
+    }
   };
 
-  gload(j_begin);
-  for (int j = j_begin; j <= c_end; ++j) {
+  // Tile j's K lands one tile before its V: step j loads K of j + 2 and V
+  // (with the ks row) of j + 1, forms the scores of j + 1 and finishes j.
+  issue_k(j_begin, K0);
+  issue_v(j_begin, V0, S0);
+  if (j_begin + 1 <= c_end) issue_k(j_begin + 1, K1);
+  wait_vmem();
+  __syncthreads();
+  if (j_begin <= c_hi) scores(K0, sacc);
+  // unrolled by two so that both buffers' code sits in one loop body
+  for (int j = j_begin; j <= c_end; j += 2) {
+    if (j + 2 <= c_end) issue_k(j + 2, K0);
+    if (j + 1 <= c_end) issue_v(j + 1, V1, S1);
+    run(j, V0, S0, K1);
+    wait_vmem();
     __syncthreads();
-    sstore();
+    if (j + 1 > c_end) break;
+    if (j + 3 <= c_end) issue_k(j + 3, K1);
+    if (j + 2 <= c_end) issue_v(j + 2, V0, S0);
+    run(j + 1, V1, S1, K0);
+    wait_vmem();
     __syncthreads();
-    if (j < c_end) gload(j + 1);
-    if (j > c_hi) continue;  // past this wave's last block
-    if (!SPARSE && j < c_lo)
-      tile(j, std::false_type{});
-    else
-      tile(j, std::true_type{});
   }
 
   l_run += __shfl_xor(l_run, 32);
