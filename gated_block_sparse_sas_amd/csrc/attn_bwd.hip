@@ -984,69 +984,66 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
 
 // --------------------------------------------------------------------------
 // dks[b, s, j, :] = sel_scale * sum over rows (h of s, t with c(t) > j) of
-// dz[t, j] qs[t, :].  Grid: (64-block tile, 256-row chunk, b * hks); the
-// partial sums of a chunk go to an fp32 accumulator with atomics.
+// dz[t, j] qs[t, :]: per (32-block tile, head of the selector group, row
+// chunk) a contraction over rows on fp32 32x32x2 MFMA (A = dz^T: block x
+// row, B = qs: row x dim; dz is zero for j >= c(t), so only rows before the
+// tile's first visible one are skipped).  The four waves take alternate row
+// pairs; their tiles are summed in LDS and added to an fp32 accumulator with
+// atomics.
 // --------------------------------------------------------------------------
+constexpr int kDksChunk = 2048;  // rows per workgroup
+
 template <int DS, typename ST>
 __global__ __launch_bounds__(256) void dks_kernel(const float* __restrict__ dz,
                                                   const ST* __restrict__ qs,
                                                   float* __restrict__ acc, Dims D) {
-  __shared__ float zs[64][65];
-  __shared__ float qv[64][DS + 1];
-  const int tid = threadIdx.x;
-  const int j0 = blockIdx.x * 64;
+  constexpr int NT = (DS + 31) / 32;  // 32-dim N-tiles
+  __shared__ float red[4][NT][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j0 = blockIdx.x * 32;
   const int bs = blockIdx.z, b = bs / D.hks, s = bs % D.hks;
-  const int nrows = D.hps * D.tq;  // rows of this selector head
-  const int r0 = blockIdx.y * 256;
-  // rows before the first query that has block j0 in its history add nothing
-  const int i_min = max(0, (j0 + 1) * kBlock - D.qoff);
-  constexpr int EP = DS / 4;  // outputs per thread: block jj = tid/4, EP dims
-  const int jj = tid >> 2, e0 = (tid & 3) * EP;
-  float a[EP];
+  const int nch = (D.tq + kDksChunk - 1) / kDksChunk;
+  const int hl = blockIdx.y / nch, i0 = (blockIdx.y % nch) * kDksChunk;
+  const int i_min = max(0, (j0 + 1) * kBlock - D.qoff);  // first row with c(t) > j0
+  const int istart = max(i0, i_min), iend = min(i0 + kDksChunk, D.tq);
+  if (istart >= iend) return;  // uniform over the workgroup
+  const size_t hrow = ((size_t)b * D.hq + s * D.hps + hl) * D.tq;
+  const int blk = j0 + (lane & 31), rsub = lane >> 5;
+  f32x16 dacc[NT];
 #pragma unroll
-  for (int e = 0; e < EP; ++e) a[e] = 0.f;
-  for (int sub = 0; sub < 256; sub += 64) {
-    const int rbase = r0 + sub;
-    if (rbase >= nrows) break;
-    __syncthreads();
-    // stage 64 rows x 64 blocks of dz and 64 rows of qs
-    for (int x = tid; x < 64 * 64; x += 256) {
-      const int r = x >> 6, jc = x & 63;
-      const int rr = rbase + r;
-      float val = 0.f;
-      if (rr < nrows) {
-        const int hl = rr / D.tq, i = rr % D.tq;
-        if (i >= i_min && j0 + jc < D.nb) {
-          const size_t row = ((size_t)b * D.hq + s * D.hps + hl) * D.tq + i;
-          val = dz[row * D.nb + j0 + jc];
-        }
-      }
-      zs[r][jc] = val;
-    }
-    for (int x = tid; x < 64 * DS; x += 256) {
-      const int r = x / DS, e = x % DS;
-      const int rr = rbase + r;
-      float val = 0.f;
-      if (rr < nrows) {
-        const int hl = rr / D.tq, i = rr % D.tq;
-        const size_t row = ((size_t)b * D.hq + s * D.hps + hl) * D.tq + i;
-        val = to_f32(qs[row * DS + e]);
-      }
-      qv[r][e] = val;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int r = 0; r < 64; ++r) {
-      const float zv = zs[r][jj];
+  for (int nt = 0; nt < NT; ++nt) dacc[nt] = f32x16{};
+  constexpr int U = 8;  // row pairs whose loads are in flight together
+  for (int i = istart + 2 * wave; i < iend; i += 8 * U) {
+    float a[U], bq[U][NT];
 #pragma unroll
-      for (int e = 0; e < EP; ++e) a[e] = fmaf(zv, qv[r][e0 + e], a[e]);
+    for (int u = 0; u < U; ++u) {
+      const int ii = i + 8 * u + rsub;
+      const bool ok = ii < iend;
+      a[u] = ok && blk < D.nb ? dz[(hrow + ii) * D.nb + blk] : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int dim = 32 * nt + (lane & 31);
+        bq[u][nt] = ok && dim < DS ? to_f32(qs[(hrow + ii) * DS + dim]) : 0.f;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        dacc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], bq[u][nt], dacc[nt], 0, 0, 0);
   }
-  if (j0 + jj < D.nb) {
-    float* out = acc + (((size_t)b * D.hks + s) * D.nb + j0 + jj) * DS + e0;
 #pragma unroll
-    for (int e = 0; e < EP; ++e)
-      if (a[e] != 0.f) atomicAdd(out + e, a[e]);
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave][nt][r][lane] = dacc[nt][r];
+  __syncthreads();
+  // accumulator lane l, register r: dim 32 nt + l % 32, block 8 (r / 4) + 4 (l / 32) + r % 4
+  for (int x = threadIdx.x; x < NT * 16 * 64; x += 256) {
+    const int nt = x / 1024, r = (x / 64) % 16, l = x % 64;
+    const float v = red[0][nt][r][l] + red[1][nt][r][l] + red[2][nt][r][l] + red[3][nt][r][l];
+    const int j = j0 + 8 * (r / 4) + 4 * (l / 32) + r % 4, dim = 32 * nt + l % 32;
+    if (j < D.nb && dim < DS && v != 0.f)
+      atomicAdd(acc + (((size_t)b * D.hks + s) * D.nb + j) * DS + dim, v);
   }
 }
 
@@ -1086,7 +1083,7 @@ hipError_t launch_dks(const float* dz, const void* qs, float* acc, void* dks, co
   const size_t n = (size_t)D.batch * D.hks * D.nb * D.ds;
   const unsigned fg = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(fill_zero_kernel, dim3(fg), dim3(256), 0, st, acc, n);
-  dim3 grid((D.nb + 63) / 64, (D.hps * D.tq + 255) / 256, D.batch * D.hks);
+  dim3 grid((D.nb + 31) / 32, D.hps * ((D.tq + kDksChunk - 1) / kDksChunk), D.batch * D.hks);
   switch (D.ds) {
     case 16:
       hipLaunchKernelGGL((dks_kernel<16, ST>), grid, dim3(256), 0, st, dz, (const ST*)qs, acc, D);
