@@ -110,8 +110,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Selector score dot product <qs, ks> over ds elements, accumulated in fp32
-// in index order with fused multiply-adds.  Every kernel that ranks or
-// normalises scores uses this one routine so that they agree bit for bit.
+// in index order with fused multiply-adds (the top-K kernels rank with it;
+// other kernels may use packed bf16 dot products, which differ only in
+// rounding).
 template <int DS, typename ST>
 __device__ __forceinline__ float sel_dot(const float* qsv, const ST* ksrow) {
   float acc = 0.f;
