@@ -10,8 +10,9 @@
 // FlashAttention-style kernel so the T x T matrix is never materialised.
 //
 // gfx950 design (bf16 in, fp32 accumulate):
-//  * workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
-//    32 consecutive rows.  Key tiles are 64 keys = one gate block, so the gate
+//  * workgroup = 8 waves = 256 query rows of one (batch, head); each wave owns
+//    32 consecutive rows (two waves per SIMD; eight waves share each K/V
+//    tile, which halves the registers that stage the next tile).  Key tiles are 64 keys = one gate block, so the gate
 //    bias is a single scalar per (row, tile).
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the accumulator puts one query
 //    per lane (column) and 16 keys per 32-key M-tile in registers, so the
@@ -21,10 +22,10 @@
 //  * O^T = V^T P^T: P never leaves registers.  The B-operand k slots of a lane
 //    are exactly the keys its S^T accumulator holds (two runs of 4), and the
 //    V^T operand is read from LDS with the same key order.
-//  * LDS: K and V tiles row-major, double-buffered, filled by direct
-//    global -> LDS loads issued one tile ahead; V^T operands come from
-//    transposing LDS reads.  Row pitches keep both kinds of operand read
-//    bank-conflict free.
+//  * LDS: K and V tiles row-major, double-buffered; the next tile is loaded
+//    into registers at the start of a tile and stored to LDS at its end (one
+//    barrier per tile); V^T operands come from transposing LDS reads.  A
+//    72-dword row pitch keeps both kinds of operand read bank-conflict free.
 //  * the gate bias of (row, tile) is recomputed in-kernel: the lane's half of
 //    qs (ds/2 values in registers) times the block's ks row (staged in LDS
 //    with the tile), one cross-half add; lam comes from the gate kernel.
@@ -41,24 +42,27 @@ namespace sas {
 // forward: each row attends only its current block (causal), then folds in
 // the K per-block partials (log-sum-exp, normalised output) computed by the
 // block-stationary kernel in sparse.hip.
+// workgroup: kFwdWaves waves of 32 query rows (kFwdRows rows) sharing each K/V tile
+constexpr int kFwdWaves = 8, kFwdThreads = 64 * kFwdWaves, kFwdRows = 32 * kFwdWaves;
+
 template <int HD, int DS, bool SPARSE = false>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
     bf16* __restrict__ o, float* __restrict__ lse, Dims D, int nqt, int xcd_groups,
     const int* __restrict__ sp_idx = nullptr, const float* __restrict__ sp_lse = nullptr,
     const bf16* __restrict__ sp_o = nullptr, int sp_k = 0) {
-  constexpr int DC = HD / 8;             // 16-byte chunks of a row
-  constexpr int SK = DC + 1;             // LDS slots per K row (one pad slot)
-  constexpr int SV = HD == 128 ? 18 : 10;  // LDS slots per V row (pads)
-  constexpr int KP = SK * 8, VP = SV * 8;  // row pitches (elements)
-  constexpr int NK = kBlock * SK / 64, NV = kBlock * SV / 64;  // direct loads per tile
+  constexpr int DC = HD / 8;                 // 16-byte chunks of a row
+  constexpr int SP = HD == 128 ? 18 : 10;    // LDS row pitch in 16-byte slots (K and V)
+  constexpr int KP = SP * 8, VP = KP;        // row pitches (elements)
+  constexpr int NCH = kBlock * DC / kFwdThreads;  // 16-byte chunks per thread and tensor
   constexpr int KS = HD / 16;      // k-steps over the head dim
   constexpr int DM = HD / 32;      // 32-row M-tiles of O^T
-  // Key tiles are double-buffered and filled by direct global -> LDS loads:
-  // K row-major at a 17/9-slot pitch (conflict-free 16-byte operand reads),
-  // V row-major at an 18/10-slot pitch, read transposed (V^T operand) by
-  // transposing 8-byte reads that are conflict-free at that pitch.
+  // Key tiles are double-buffered in LDS, K and V row-major (V read
+  // transposed, as the V^T operand, by transposing 8-byte reads).  The next
+  // tile goes global -> registers at the start of a tile and registers ->
+  // LDS at its end: the LDS operand reads then never wait behind an
+  // outstanding global -> LDS transfer.
   __shared__ __align__(16) bf16 K0[kBlock * KP];
   __shared__ __align__(16) bf16 K1[kBlock * KP];
   __shared__ __align__(16) bf16 V0[kBlock * VP];
@@ -72,17 +76,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const QTile tm = map_q_tile(blockIdx.x, nqt, D, xcd_groups);
   const int b = tm.b, h = tm.h, qt = tm.qt;
   const int g = h / D.hpg, sh = h / D.hps;
-  const int wq0 = qt * 128 + wave * 32;
+  const int wq0 = qt * kFwdRows + wave * 32;
   const int qi = wq0 + l32;
   const int qc = min(qi, D.tq - 1);
   const int t = D.qoff + qc;
   const int c = t / kBlock;
   const int c_lo = (D.qoff + min(wq0, D.tq - 1)) / kBlock;
   const int c_hi = (D.qoff + min(wq0 + 31, D.tq - 1)) / kBlock;
-  const int c_end = (D.qoff + min(qt * 128 + 127, D.tq - 1)) / kBlock;
+  const int c_end = (D.qoff + min(qt * kFwdRows + kFwdRows - 1, D.tq - 1)) / kBlock;
 
   // first tile: 0, or in sparse mode the first current block of the workgroup
-  const int j_begin = SPARSE ? (D.qoff + min(qt * 128, D.tq - 1)) / kBlock : 0;
+  const int j_begin = SPARSE ? (D.qoff + min(qt * kFwdRows, D.tq - 1)) / kBlock : 0;
 
   const size_t qrow = ((size_t)b * D.hq + h) * D.tq + qc;
   bf16x8 qf[KS];
@@ -105,53 +109,39 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // direct loads of key tile j (every wave takes every fourth instruction):
-  // K, and separately V with the block's ks row
-  auto issue_k = [&](int j, bf16* Kd) __attribute__((always_inline)) {
+  // next tile staged in registers: thread tid holds 16-byte chunks tid + kFwdThreads x
+  // (row = chunk / DC, column chunk = chunk % DC) of K and of V, and threads
+  // 0 .. DS/8-1 a chunk of the block's ks row
+  bf16x8 kreg[NCH], vreg[NCH], sreg = bf16x8{};
+  auto gload = [&](int j) __attribute__((always_inline)) {
     const bf16* kt = kb + (size_t)j * kBlock * HD;
-    for (int x = wave; x < NK; x += 4) {
-      const int sl = x * 64 + lane, r = sl / SK, ch = sl % SK;
-      __builtin_amdgcn_global_load_lds(kt + r * HD + (ch < DC ? ch : 0) * 8, Kd + x * 512, 16, 0,
-                                       0);
-    }
-  };
-  auto issue_v = [&](int j, bf16* Vd, bf16* Sd) __attribute__((always_inline)) {
     const bf16* vt = vb + (size_t)j * kBlock * HD;
-    for (int x = wave; x < NV; x += 4) {
-      const int sl = x * 64 + lane, r = sl / SV, ch = sl % SV;
-      __builtin_amdgcn_global_load_lds(vt + r * HD + (ch < DC ? ch : 0) * 8, Vd + x * 512, 16, 0,
-                                       0);
+#pragma unroll
+    for (int x = 0; x < NCH; ++x) {
+      const int id = tid + kFwdThreads * x;
+      kreg[x] = *(const bf16x8*)(kt + (id / DC) * HD + (id % DC) * 8);
+      vreg[x] = *(const bf16x8*)(vt + (id / DC) * HD + (id % DC) * 8);
     }
-    if (!SPARSE && tid < DS / 8)
-      __builtin_amdgcn_global_load_lds(ksb0 + (size_t)j * DS + tid * 8, Sd, 16, 0, 0);
+    if (!SPARSE && tid < DS / 8) sreg = *(const bf16x8*)(ksb0 + (size_t)j * DS + tid * 8);
+  };
+  auto sstore = [&](bf16* Kd, bf16* Vd, bf16* Sd) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < NCH; ++x) {
+      const int id = tid + kFwdThreads * x;
+      *(bf16x8*)&Kd[(id / DC) * KP + (id % DC) * 8] = kreg[x];
+      *(bf16x8*)&Vd[(id / DC) * VP + (id % DC) * 8] = vreg[x];
+    }
+    if (!SPARSE && tid < DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
   };
   // per-lane part of the transposing V^T reads: lane 4k + a of each 16-lane
   // group points at key row 4 hh + k, columns 16 ((lane >> 4) & 1) + 4 a
   const int vbase = (4 * hh + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // S^T tile of key tile j from K tile Ks: two 32-key M-tiles x 32 queries
-  auto scores = [&](const bf16* Ks, f32x16* sacc) __attribute__((always_inline)) {
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a = *(const bf16x8*)&Ks[(32 * mt + l32) * KP + 16 * s + 8 * hh];
-        sacc[mt] = mfma32(a, qf[s], sacc[mt]);
-      }
-    }
-  };
-  f32x16 sacc[2];  // scores of the tile being finished
-  // Finish key tile j whose scores are in sacc: softmax update and O^T += V^T
-  // P^T from V tile Vs; meanwhile (NEXT) the scores of tile j + 1 are formed
-  // from K tile Kn, so the exponentials overlap those products.  MASK: causal
-  // mask and per-lane block test (only the at most two tiles that hold some
-  // lane's current block need it).
-  auto finish = [&](int j, auto mask_tag, auto next_tag, const bf16* Vs, const bf16* Ss,
-                    const bf16* Kn) __attribute__((always_inline)) {
+  // One key tile.  MASK: causal mask and per-lane block test (only the at
+  // most two tiles that hold some lane's current block need it).
+  auto tile = [&](int j, auto mask_tag, const bf16* Ks, const bf16* Vs, const bf16* Ss)
+      __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool NEXT = decltype(next_tag)::value;
     float bias2 = 0.f;  // log2-domain gate bias of this lane's row for block j
     if (!SPARSE && j < c_hi) {
       const bf16x2* kr = (const bf16x2*)(Ss + hh * (DS / 2));
@@ -160,6 +150,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int e = 0; e < DS / 4; ++e) part = __builtin_amdgcn_fdot2_f32_bf16(qsv[e], kr[e], part, false);
       part += __shfl_xor(part, 32);
       if (j < c) bias2 = (D.sel_scale * part - lam_t) * kLog2e;
+    }
+    // S^T tile: two 32-key M-tiles x 32 queries
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 a = *(const bf16x8*)&Ks[(32 * mt + l32) * KP + 16 * s + 8 * hh];
+        sacc[mt] = mfma32(a, qf[s], sacc[mt]);
+      }
     }
     // row max on the raw scores (c1 > 0, bias2 is constant over the tile)
     float mx = -INFINITY;
@@ -186,8 +186,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
       m_run = m_new;
     }
-    f32x16 snext[2];
-    if constexpr (NEXT) scores(Kn, snext);
     // (m_run is -inf only for a row with no visible key yet: all p are 0)
     const float off = bias2 - ((SPARSE && m_run == -INFINITY) ? 0.f : m_run);
     float psum = 0.f;
@@ -219,45 +217,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         }
       }
     }
-    if constexpr (NEXT) {
-      sacc[0] = snext[0];
-      sacc[1] = snext[1];
-    }
   };
-  auto run = [&](int j, const bf16* Vs, const bf16* Ss, const bf16* Kn)
+  auto run = [&](int j, const bf16* Ks, const bf16* Vs, const bf16* Ss)
       __attribute__((always_inline)) {
     if (j > c_hi) return;  // past this wave's last block
-    const bool masked = SPARSE || j >= c_lo;
-    if (j + 1 <= c_hi) {
-      if (masked)
-        finish(j, std::true_type{}, std::true_type{}, Vs, Ss, Kn);
-      else
-        finish(j, std::false_type{}, std::true_type{}, Vs, Ss, Kn);
-    } else {
-      finish(j, std::true_type{}, std::false_type{}, Vs, Ss, Kn);
-    }
+    if (!SPARSE && j < c_lo)
+      tile(j, std::false_type{}, Ks, Vs, Ss);
+    else
+      tile(j, std::true_type{}, Ks, Vs, Ss);
   };
 
-  // Tile j's K lands one tile before its V: step j loads K of j + 2 and V
-  // (with the ks row) of j + 1, forms the scores of j + 1 and finishes j.
-  issue_k(j_begin, K0);
-  issue_v(j_begin, V0, S0);
-  if (j_begin + 1 <= c_end) issue_k(j_begin + 1, K1);
-  wait_vmem();
+  gload(j_begin);
+  sstore(K0, V0, S0);
   __syncthreads();
-  if (j_begin <= c_hi) scores(K0, sacc);
   // unrolled by two so that both buffers' code sits in one loop body
   for (int j = j_begin; j <= c_end; j += 2) {
-    if (j + 2 <= c_end) issue_k(j + 2, K0);
-    if (j + 1 <= c_end) issue_v(j + 1, V1, S1);
-    run(j, V0, S0, K1);
-    wait_vmem();
+    if (j + 1 <= c_end) gload(j + 1);
+    run(j, K0, V0, S0);
+    if (j + 1 <= c_end) sstore(K1, V1, S1);
     __syncthreads();
     if (j + 1 > c_end) break;
-    if (j + 3 <= c_end) issue_k(j + 3, K1);
-    if (j + 2 <= c_end) issue_v(j + 2, V0, S0);
-    run(j + 1, V1, S1, K0);
-    wait_vmem();
+    if (j + 2 <= c_end) gload(j + 2);
+    run(j + 1, K1, V1, S1);
+    if (j + 2 <= c_end) sstore(K0, V0, S0);
     __syncthreads();
   }
 
@@ -319,11 +301,11 @@ template <int HD, int DS>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const void* qs,
                                const void* ks, const float* lam, void* o, float* lse,
                                const Dims& D, hipStream_t st) {
-  const int nqt = (D.tq + 127) / 128;
+  const int nqt = (D.tq + kFwdRows - 1) / kFwdRows;
   const int groups = D.batch * D.hkv;
   const int xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
   const unsigned grid = (unsigned)(D.batch * D.hq * nqt);
-  hipLaunchKernelGGL((attn_fwd_kernel<HD, DS>), dim3(grid), dim3(256), 0, st, (const bf16*)q,
+  hipLaunchKernelGGL((attn_fwd_kernel<HD, DS>), dim3(grid), dim3(kFwdThreads), 0, st, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (const bf16*)qs, (const bf16*)ks, lam,
                      (bf16*)o, lse, D, nqt, xcd_groups);
   return hipGetLastError();
@@ -334,11 +316,11 @@ static hipError_t launch_sparse_merge_t(const void* q, const void* k, const void
                                         const int* idx, const float* plse, const void* po,
                                         void* o, float* lse_out, int K, const Dims& D,
                                         hipStream_t st) {
-  const int nqt = (D.tq + 127) / 128;
+  const int nqt = (D.tq + kFwdRows - 1) / kFwdRows;
   const int groups = D.batch * D.hkv;
   const int xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
   const unsigned grid = (unsigned)(D.batch * D.hq * nqt);
-  hipLaunchKernelGGL((attn_fwd_kernel<HD, 16, true>), dim3(grid), dim3(256), 0, st,
+  hipLaunchKernelGGL((attn_fwd_kernel<HD, 16, true>), dim3(grid), dim3(kFwdThreads), 0, st,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)nullptr,
                      (const bf16*)nullptr, (const float*)nullptr, (bf16*)o, lse_out, D, nqt,
                      xcd_groups, idx, plse, (const bf16*)po, K);
