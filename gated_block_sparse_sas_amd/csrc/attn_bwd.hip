@@ -259,16 +259,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 // stream global -> LDS with direct loads into two buffers, diagonal tile
 // first; K^T for dQ^T = K^T dS^T comes from transposing reads of the K tile.
 // --------------------------------------------------------------------------
+constexpr int kDqWaves = 8, kDqThreads = 64 * kDqWaves, kDqRows = 16 * kDqWaves;
+
 template <int DS>
-__global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
     const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
     bf16* __restrict__ dq, bf16* __restrict__ dqs, float* __restrict__ dz,
     float* __restrict__ delta, Dims D, int nqt, int xcd_groups) {
-  constexpr int HD = 128, TS = kBlock * 18, TE = TS * 8;  // tile slots, elements
-  constexpr int NI = TS / 64;                  // direct loads per tile and tensor
-  constexpr int WI = (NI + 3) / 4;             // ... per wave
+  constexpr int HD = 128, TE = kBlock * 144;  // tile elements (72-dword rows)
+  constexpr int NCH = kBlock * 16 / kDqThreads;  // 16-byte chunks per thread and tensor
   constexpr int DQ = DS / 4;                   // selector dims per lane group
   __shared__ __align__(16) bf16 K0[TE];
   __shared__ __align__(16) bf16 K1[TE];
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
   const QTile tm = map_q_tile(blockIdx.x, nqt, D, xcd_groups);
   const int b = tm.b, h = tm.h, qt = tm.qt;
   const int g = h / D.hpg, sh = h / D.hps;
-  const int wq0 = qt * 64 + wave * 16;
+  const int wq0 = qt * kDqRows + wave * 16;
   const int qi = wq0 + i16;
   const bool valid = qi < D.tq;
   const int qc = min(qi, D.tq - 1);
@@ -292,16 +293,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
   const int c = t / kBlock;
   const int c_lo = (D.qoff + min(wq0, D.tq - 1)) / kBlock;
   const int c_hi = (D.qoff + min(wq0 + 15, D.tq - 1)) / kBlock;
-  const int c_end = (D.qoff + min(qt * 64 + 63, D.tq - 1)) / kBlock;
+  const int c_end = (D.qoff + min(qt * kDqRows + kDqRows - 1, D.tq - 1)) / kBlock;
   const size_t row = ((size_t)b * D.hq + h) * D.tq + qc;
 
   // zero dz[row, j] for j >= c(row) (coalesced over the workgroup's rows)
-  for (int r = 0; r < 64; ++r) {
-    const int i = qt * 64 + r;
+  for (int r = 0; r < kDqRows; ++r) {
+    const int i = qt * kDqRows + r;
     if (i >= D.tq) break;
     const int cr = (D.qoff + i) / kBlock;
     float* zr = dz + (((size_t)b * D.hq + h) * D.tq + i) * D.nb;
-    for (int jj = cr + tid; jj < D.nb; jj += 256) zr[jj] = 0.f;
+    for (int jj = cr + tid; jj < D.nb; jj += kDqThreads) zr[jj] = 0.f;
   }
 
   bf16x8 qf[4], df[4];
@@ -334,22 +335,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
   for (int dm = 0; dm < 8; ++dm) dqa[dm] = f32x4{};
   float sdb = 0.f;
 
-  unsigned toff[WI];  // per-lane element offsets of this wave's direct loads in a tile
-#pragma unroll
-  for (int x = 0; x < WI; ++x) toff[x] = tslot_src(min((wave + 4 * x) * 64 + lane, TS - 1));
-  auto issue = [&](int j, bf16* Kd, bf16* Vd, bf16* Sd) {
-    if (wave == 0 && lane < DS / 8)
-      __builtin_amdgcn_global_load_lds(ksb + (size_t)j * DS + lane * 8, Sd, 16, 0, 0);
+  // the next tile goes global -> registers at the start of a step and
+  // registers -> LDS at its end: thread tid holds 16-byte chunks
+  // tid + kDqThreads x of K and V (row = chunk / 16), threads 0 .. DS/8-1 a
+  // chunk of the block's ks row
+  bf16x8 kreg[NCH], vreg[NCH], sreg = bf16x8{};
+  auto gload = [&](int j) {
     const bf16* kt = kb + (size_t)j * kBlock * HD;
     const bf16* vt = vb + (size_t)j * kBlock * HD;
 #pragma unroll
-    for (int x = 0; x < WI; ++x) {
-      const int ins = wave + 4 * x;
-      if (ins < NI) {
-        __builtin_amdgcn_global_load_lds(kt + toff[x], Kd + ins * 512, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + toff[x], Vd + ins * 512, 16, 0, 0);
-      }
+    for (int x = 0; x < NCH; ++x) {
+      const int id = tid + kDqThreads * x;
+      kreg[x] = *(const bf16x8*)(kt + (id >> 4) * HD + (id & 15) * 8);
+      vreg[x] = *(const bf16x8*)(vt + (id >> 4) * HD + (id & 15) * 8);
     }
+    if (tid < DS / 8) sreg = *(const bf16x8*)(ksb + (size_t)j * DS + tid * 8);
+  };
+  auto sstore = [&](bf16* Kd, bf16* Vd, bf16* Sd) {
+#pragma unroll
+    for (int x = 0; x < NCH; ++x) {
+      const int id = tid + kDqThreads * x;
+      *(bf16x8*)&Kd[trow(id >> 4) + (id & 15) * 8] = kreg[x];
+      *(bf16x8*)&Vd[trow(id >> 4) + (id & 15) * 8] = vreg[x];
+    }
+    if (tid < DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
   };
 
   auto compute = [&](int j, const bf16* Ks, const bf16* Vs, const bf16* Ss) {
@@ -435,18 +444,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq16_kernel(
   };
 
   const int ntiles = c_end + 1;  // tiles c_end, c_end - 1, ..., 0
-  issue(c_end, K0, V0, S0);
-  wait_vmem();
+  gload(c_end);
+  sstore(K0, V0, S0);
   __syncthreads();
   for (int it = 0; it < ntiles; it += 2) {
-    if (it + 1 < ntiles) issue(c_end - it - 1, K1, V1, S1);
+    if (it + 1 < ntiles) gload(c_end - it - 1);
     compute(c_end - it, K0, V0, S0);
-    wait_vmem();
+    if (it + 1 < ntiles) sstore(K1, V1, S1);
     __syncthreads();
     if (it + 1 >= ntiles) break;
-    if (it + 2 < ntiles) issue(c_end - it - 2, K0, V0, S0);
+    if (it + 2 < ntiles) gload(c_end - it - 2);
     compute(c_end - it - 1, K1, V1, S1);
-    wait_vmem();
+    if (it + 2 < ntiles) sstore(K0, V0, S0);
     __syncthreads();
   }
 
@@ -1117,11 +1126,11 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   const int xg = groups % 8 == 0 ? groups / 8 : 0;
   hipError_t e;
   if constexpr (HD == 128) {
-    const int nqt64 = (D.tq + 63) / 64;
-    hipLaunchKernelGGL((bwd_dq16_kernel<DS>), dim3(D.batch * D.hq * nqt64), dim3(256), 0, st,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)o,
+    const int nqtw = (D.tq + kDqRows - 1) / kDqRows;
+    hipLaunchKernelGGL((bwd_dq16_kernel<DS>), dim3(D.batch * D.hq * nqtw), dim3(kDqThreads), 0,
+                       st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)o,
                        (const bf16*)dout, lse, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dq,
-                       (bf16*)dqs, dzp, delta, D, nqt64, xg);
+                       (bf16*)dqs, dzp, delta, D, nqtw, xg);
   } else {
   const int nqt = (D.tq + 127) / 128;
   hipLaunchKernelGGL((bwd_dq_kernel<HD, DS>), dim3(D.batch * D.hq * nqt), dim3(256), 0, st,
