@@ -15,6 +15,7 @@ from .oracle import (  # noqa: F401
     attn_fwd,
     attn_bwd,
     topk_blocks,
+    topk_budget,
     sparse_fwd,
     num_threads,
 )

@@ -82,9 +82,11 @@ def _load():
         lib.oracle_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, P, P, P, P, I64, P, P, P,
                                         I64, P, P]
         lib.oracle_topk_blocks.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
+        lib.oracle_topk_budget.argtypes = [P, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, P,
+                                           P, P, P, P]
         lib.oracle_sparse_fwd.argtypes = [P, ctypes.c_int32, P, P, P, P, P, I64, P, P, P]
         for f in (lib.oracle_gate_scores, lib.oracle_attn_fwd, lib.oracle_attn_bwd,
-                  lib.oracle_topk_blocks, lib.oracle_sparse_fwd):
+                  lib.oracle_topk_blocks, lib.oracle_topk_budget, lib.oracle_sparse_fwd):
             f.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -199,6 +201,20 @@ def topk_blocks(shape: OracleShape, topk: int, qs=None, ks=None, z=None, renorm:
     st = shape.c_struct()
     _check(_load().oracle_topk_blocks(ctypes.byref(st), int(topk), int(renorm), _ptr(qs), _ptr(ks),
                                       _ptr(z), _ptr(idx), _ptr(bias)), "topk_blocks")
+    return idx, bias
+
+
+def topk_budget(shape: OracleShape, kmax: int, frac: float, qs=None, ks=None, z=None,
+                renorm: int = 0):
+    """Top-K with n_t = min(kmax, ceil(frac * c(t))) blocks per row (frac <= 0:
+    the fixed budget).  Returns (idx int32 [B,Hq,Tq,kmax], bias float64)."""
+    qs, ks, z = map(_f64, (qs, ks, z))
+    idx = np.empty((shape.batch, shape.hq, shape.tq, kmax), dtype=np.int32)
+    bias = np.empty((shape.batch, shape.hq, shape.tq, kmax))
+    st = shape.c_struct()
+    _check(_load().oracle_topk_budget(ctypes.byref(st), int(kmax), ctypes.c_float(frac),
+                                      int(renorm), _ptr(qs), _ptr(ks), _ptr(z), _ptr(idx),
+                                      _ptr(bias)), "topk_budget")
     return idx, bias
 
 

@@ -431,8 +431,28 @@ static int by_score_desc(const void* pa, const void* pb) {
   return a->j < b->j ? -1 : (a->j > b->j ? 1 : 0);
 }
 
+static int topk_impl(const oracle_shape* s, int32_t topk, double frac, int32_t renorm,
+                     const double* qs, const double* ks, const double* zin, int32_t* idx,
+                     double* bias);
+
 int oracle_topk_blocks(const oracle_shape* s, int32_t topk, int32_t renorm, const double* qs,
                        const double* ks, const double* zin, int32_t* idx, double* bias) {
+  return topk_impl(s, topk, 0.0, renorm, qs, ks, zin, idx, bias);
+}
+
+/* Budget proportional to the history: row t keeps n_t = min(kmax, ceil(frac *
+ * c(t))) blocks (frac <= 0: n_t = min(kmax, c(t)), the fixed budget).  The
+ * blog's "top 25%" of the context at 32k is frac = 0.25.  idx / bias have
+ * kmax slots per row, padded as for the fixed budget. */
+int oracle_topk_budget(const oracle_shape* s, int32_t kmax, float frac, int32_t renorm,
+                       const double* qs, const double* ks, const double* zin, int32_t* idx,
+                       double* bias) {
+  return topk_impl(s, kmax, (double)frac, renorm, qs, ks, zin, idx, bias);
+}
+
+static int topk_impl(const oracle_shape* s, int32_t topk, double frac, int32_t renorm,
+                     const double* qs, const double* ks, const double* zin, int32_t* idx,
+                     double* bias) {
   if (check_shape(s) || topk < 1) return -1;
   const int64_t nrows = (int64_t)s->batch * s->hq * s->tq;
 #pragma omp parallel for schedule(dynamic, 64)
@@ -447,7 +467,11 @@ int oracle_topk_blocks(const oracle_shape* s, int32_t topk, int32_t renorm, cons
       cand[j].j = j;
     }
     qsort(cand, (size_t)c, sizeof(scored), by_score_desc);
-    const int64_t n = c < topk ? c : topk;
+    int64_t n = c < topk ? c : topk;
+    if (frac > 0.0) {
+      const int64_t nb = (int64_t)ceil(frac * (double)c);
+      if (nb < n) n = nb;
+    }
     /* Bias of a selected block.  renorm = 0 (default): the training log-gate
      * z - lambda with lambda over the whole history, i.e. the same logits as
      * dense training with the unselected blocks masked out; renorm = 1: the

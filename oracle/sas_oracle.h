@@ -74,6 +74,12 @@ int oracle_attn_bwd(const oracle_shape* s, const double* q, const double* k, con
 int oracle_topk_blocks(const oracle_shape* s, int32_t topk, int32_t renorm,
                        const double* qs, const double* ks, const double* zin,
                        int32_t* idx, double* bias);
+/* Top-K with a budget proportional to the history: n_t = min(kmax,
+ * ceil(frac * c(t))) blocks per row (frac <= 0: min(kmax, c(t))); kmax slots
+ * per row, padded with -1 / -inf. */
+int oracle_topk_budget(const oracle_shape* s, int32_t kmax, float frac, int32_t renorm,
+                       const double* qs, const double* ks, const double* zin, int32_t* idx,
+                       double* bias);
 
 /* Sparse attention forward: each row attends its current block (causal,
  * bias 0) plus the blocks listed in idx with the given bias.

@@ -328,6 +328,43 @@ def test_topk_tie_goes_to_smaller_block():
         np.testing.assert_array_equal(idx[0, 0, t, :min(3, c)], np.arange(min(3, c)))
 
 
+@pytest.mark.parametrize("renorm", [0, 1])
+@pytest.mark.parametrize("frac", [0.25, 0.3])
+def test_topk_budget_vs_sort(renorm, frac):
+    S, x = make(hq=4, hkv=2, tq=90, tk=90, block=4)
+    kmax = 5
+    idx, bias = oracle.topk_budget(S, kmax, frac, x["qs"], x["ks"], renorm=renorm)
+    z, lam, _ = oracle.gate_scores(S, x["qs"], x["ks"])
+    f = float(np.float32(frac))  # the budget fraction travels as a float
+    for h in range(S.hq):
+        for t in range(S.tq):
+            c = t // S.block
+            n = min(kmax, c, math.ceil(f * c))
+            zz = z[0, h, t, :c]
+            order = np.lexsort((np.arange(c), -zz))[:n]
+            np.testing.assert_array_equal(idx[0, h, t, :n], order)
+            assert np.all(idx[0, h, t, n:] == -1) and np.all(np.isneginf(bias[0, h, t, n:]))
+            norm = logsumexp(zz[order]) if renorm else lam[0, h, t]
+            np.testing.assert_allclose(bias[0, h, t, :n], zz[order] - norm, rtol=1e-12, atol=1e-12)
+
+
+def test_topk_budget_quarter_counts():
+    # frac = 1/4: a row with c = 4m historical blocks keeps exactly m (cap aside)
+    S, x = make(hq=1, hkv=1, tq=130, tk=130, block=4)
+    idx, _ = oracle.topk_budget(S, 64, 0.25, x["qs"], x["ks"])
+    for t in range(130):
+        c = t // 4
+        assert int((idx[0, 0, t] >= 0).sum()) == -(-c // 4)
+
+
+def test_topk_budget_nonpositive_frac_is_fixed_budget():
+    S, x = make(hq=2, hkv=1, tq=50, tk=50, block=4)
+    a = oracle.topk_budget(S, 4, 0.0, x["qs"], x["ks"], renorm=1)
+    b = oracle.topk_blocks(S, 4, x["qs"], x["ks"], renorm=1)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
 # -------------------------------------------------------------------- sparse
 @pytest.mark.parametrize("renorm", [0, 1])
 def test_sparse_full_budget_equals_dense(renorm):
@@ -346,6 +383,25 @@ def test_sparse_vs_bruteforce(renorm):
     K = 3
     idx, bias = oracle.topk_blocks(S, K, x["qs"], x["ks"], renorm=renorm)
     o, l = oracle.sparse_fwd(S, K, x["q"], x["k"], x["v"], idx, bias)
+    keep = torch.zeros(1, S.hq, S.tq, S.nb, dtype=torch.bool)
+    for h in range(S.hq):
+        for t in range(S.tq):
+            for j in idx[0, h, t]:
+                if j >= 0:
+                    keep[0, h, t, j] = True
+    z = bf.scores(T(x["qs"]), T(x["ks"]), S.hq, 1.0 / math.sqrt(S.ds))
+    bias_m = bf.bias_matrix(z, S.tq, S.tk, S.block, restrict=keep, renorm=bool(renorm))
+    ob, lb = bf.attention(T(x["q"]), T(x["k"]), T(x["v"]), bias_m, 1.0 / math.sqrt(S.d))
+    np.testing.assert_allclose(o, ob.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(l, lb.numpy(), rtol=1e-12)
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_sparse_budget_vs_bruteforce(renorm):
+    S, x = make(hq=4, hkv=2, tq=61, tk=61, block=4)
+    kmax = 6
+    idx, bias = oracle.topk_budget(S, kmax, 0.25, x["qs"], x["ks"], renorm=renorm)
+    o, l = oracle.sparse_fwd(S, kmax, x["q"], x["k"], x["v"], idx, bias)
     keep = torch.zeros(1, S.hq, S.tq, S.nb, dtype=torch.bool)
     for h in range(S.hq):
         for t in range(S.tq):
