@@ -48,6 +48,10 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
 
 // Step 5: top-K blocks.
 bool topk_supported(const Dims& D, int K);
+bool topk_budget_supported(const Dims& D, int kmax);
+hipError_t launch_topk_budget(const void* qs, const void* ks, int kmax, float frac, int renorm,
+                              int* idx, float* bias, const Dims& D, bool sel_bf16,
+                              hipStream_t st);
 hipError_t launch_topk(const void* qs, const void* ks, int K, int renorm, int* idx, float* bias,
                        const Dims& D, bool sel_bf16, hipStream_t st);
 

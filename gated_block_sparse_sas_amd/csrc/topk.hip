@@ -206,6 +206,210 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
   }
 }
 
+// Budgeted / large-K variant: one wavefront per query row keeps the
+// n_t = min(kmax, c(t), ceil(frac c(t))) best blocks (frac <= 0: no
+// fraction).  Scores go to LDS (same fp32 dot product as above) and become
+// order-preserving 32-bit keys; a 4-pass radix select (8 bits per pass,
+// LDS histogram) finds the n_t-th largest key, ties at it are taken in block
+// order; the n_t winners are then sorted (bitonic network in LDS) by key
+// descending, block ascending — the same order as the other kernels.
+__device__ __forceinline__ unsigned ord_key(float z) {
+  const unsigned u = __float_as_uint(z);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ bool key_before(unsigned ka, int ja, unsigned kb, int jb) {
+  return ka > kb || (ka == kb && ja < jb);
+}
+
+template <int DS, typename ST>
+__global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__ qs,
+                                                          const ST* __restrict__ ks, int kmax,
+                                                          float frac, int renorm,
+                                                          int* __restrict__ idx,
+                                                          float* __restrict__ bias, Dims D,
+                                                          int kp2) {
+  extern __shared__ unsigned tsm[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int per = D.nb + 256 + 2 * kp2;
+  float* zc = (float*)(tsm + (size_t)wave * per);  // scores of this row's blocks
+  unsigned* hist = tsm + (size_t)wave * per + D.nb;  // radix histogram
+  unsigned* sk = hist + 256;                         // selected keys
+  int* sj = (int*)(sk + kp2);                        // selected blocks
+  const size_t nrows = (size_t)D.batch * D.hq * D.tq;
+  const size_t row = (size_t)blockIdx.x * 4 + wave;
+  if (row >= nrows) return;  // whole wave (no workgroup barrier below)
+  const int i = (int)(row % D.tq);
+  const int h = (int)((row / D.tq) % D.hq);
+  const int b = (int)(row / ((size_t)D.tq * D.hq));
+  const int c = (D.qoff + i) / kBlock;
+  int n = min(kmax, c);
+  if (frac > 0.f) n = min(n, (int)ceil((double)frac * (double)c));
+  // scores and the gate normaliser over the whole history
+  float qsv[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
+  const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
+  float m = -INFINITY;
+  for (int j = lane; j < c; j += 64) {
+    const float z = D.sel_scale * sel_dot<DS>(qsv, ksb + (size_t)j * DS);
+    zc[j] = z;
+    m = fmaxf(m, z);
+  }
+  m = wave_max(m);
+  float sum = 0.f;
+  if (m != -INFINITY)
+    for (int j = lane; j < c; j += 64) sum += exp2f((zc[j] - m) * kLog2e);
+  sum = wave_sum(sum);
+  const float lam = c == 0 ? -INFINITY : m + log2f(sum) * kLn2;
+  // radix select of the n-th largest key
+  unsigned prefix = 0, pmask = 0;
+  int need = n;
+  if (n > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int x = lane; x < 256; x += 64) hist[x] = 0;
+      for (int j = lane; j < c; j += 64) {
+        const unsigned kk = ord_key(zc[j]);
+        if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+      }
+      // lane l owns digits 255 - 4l .. 252 - 4l (from the top)
+      unsigned cnt[4], tot = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        cnt[u] = hist[255 - 4 * lane - u];
+        tot += cnt[u];
+      }
+      // inclusive prefix of tot over lanes (from the top digit down)
+      unsigned inc = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+      }
+      const unsigned exc = inc - tot;
+      // the digit where the count from the top first reaches need
+      int dsel = -1;
+      unsigned above = 0;
+      if (exc < (unsigned)need && inc >= (unsigned)need) {
+        unsigned run = exc;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (dsel < 0 && run + cnt[u] >= (unsigned)need) {
+            dsel = 255 - 4 * lane - u;
+            above = run;
+          }
+          run += cnt[u];
+        }
+      }
+      const unsigned long long bal = __ballot(dsel >= 0);
+      const int src = __ffsll((long long)bal) - 1;
+      const int dg = __shfl(dsel, src);
+      need -= (int)__shfl(above, src);
+      prefix |= (unsigned)dg << shift;
+      pmask |= 255u << shift;
+    }
+  }
+  // gather: keys above the threshold, then the first `need` ties by block
+  int cnt_sel = 0, ties_left = need;
+  for (int j0 = 0; j0 < c; j0 += 64) {
+    const int j = j0 + lane;
+    const unsigned kk = j < c ? ord_key(zc[j]) : 0u;
+    const bool above = n > 0 && j < c && kk > prefix;
+    const bool tie = n > 0 && j < c && kk == prefix;
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const unsigned long long bt = __ballot(tie);
+    const int trank = __popcll(bt & lt);
+    const bool take = above || (tie && trank < ties_left);
+    const unsigned long long bs = __ballot(take);
+    if (take) {
+      const int pos = cnt_sel + __popcll(bs & lt);
+      sk[pos] = kk;
+      sj[pos] = j;
+    }
+    cnt_sel += __popcll(bs);
+    ties_left -= min(ties_left, __popcll(bt));
+  }
+  // bitonic sort of the n winners (padded to a power of two with the worst key)
+  int p2 = 1;
+  while (p2 < n) p2 <<= 1;
+  for (int x = n + lane; x < p2; x += 64) {
+    sk[x] = 0u;
+    sj[x] = 0x7fffffff;
+  }
+  for (int size = 2; size <= p2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int pr = lane; pr < (p2 >> 1); pr += 64) {
+        const int lo = 2 * stride * (pr / stride) + (pr % stride), hi = lo + stride;
+        const unsigned ka = sk[lo], kb2 = sk[hi];
+        const int ja = sj[lo], jb = sj[hi];
+        const bool first_better = key_before(ka, ja, kb2, jb);
+        const bool want_better_first = (lo & size) == 0;
+        if (first_better != want_better_first) {
+          sk[lo] = kb2;
+          sk[hi] = ka;
+          sj[lo] = jb;
+          sj[hi] = ja;
+        }
+      }
+    }
+  }
+  // outputs
+  float norm = lam;
+  if (renorm) {
+    float mm = -INFINITY;
+    for (int r = lane; r < n; r += 64) mm = fmaxf(mm, zc[sj[r]]);
+    mm = wave_max(mm);
+    float ss = 0.f;
+    for (int r = lane; r < n; r += 64) ss += exp2f((zc[sj[r]] - mm) * kLog2e);
+    ss = wave_sum(ss);
+    norm = n == 0 ? -INFINITY : mm + log2f(ss) * kLn2;
+  }
+  for (int r = lane; r < kmax; r += 64) {
+    if (r < n) {
+      const int j = sj[r];
+      idx[row * kmax + r] = j;
+      bias[row * kmax + r] = zc[j] - norm;
+    } else {
+      idx[row * kmax + r] = -1;
+      bias[row * kmax + r] = -INFINITY;
+    }
+  }
+}
+
+template <int DS, typename ST>
+static hipError_t launch_select_t(const void* qs, const void* ks, int kmax, float frac, int renorm,
+                                  int* idx, float* bias, const Dims& D, hipStream_t st) {
+  int kp2 = 1;
+  while (kp2 < kmax) kp2 <<= 1;
+  const size_t per = (size_t)(D.nb + 256 + 2 * kp2) * sizeof(unsigned);
+  const size_t nrows = (size_t)D.batch * D.hq * D.tq;
+  hipLaunchKernelGGL((topk_select_kernel<DS, ST>), dim3((unsigned)((nrows + 3) / 4)), dim3(256),
+                     per * 4, st, (const ST*)qs, (const ST*)ks, kmax, frac, renorm, idx, bias, D,
+                     kp2);
+  return hipGetLastError();
+}
+
+bool topk_budget_supported(const Dims& D, int kmax) {
+  int kp2 = 1;
+  while (kp2 < kmax) kp2 <<= 1;
+  return kmax <= 1024 && (size_t)(D.nb + 256 + 2 * kp2) * sizeof(unsigned) * 4 <= 65536;
+}
+
+hipError_t launch_topk_budget(const void* qs, const void* ks, int kmax, float frac, int renorm,
+                              int* idx, float* bias, const Dims& D, bool sel_bf16,
+                              hipStream_t st) {
+#define SAS_SEL_CASE(DSV)                                                                     \
+  case DSV:                                                                                   \
+    return sel_bf16 ? launch_select_t<DSV, bf16>(qs, ks, kmax, frac, renorm, idx, bias, D, st) \
+                    : launch_select_t<DSV, float>(qs, ks, kmax, frac, renorm, idx, bias, D, st);
+  switch (D.ds) {
+    SAS_SEL_CASE(16)
+    SAS_SEL_CASE(32)
+    SAS_SEL_CASE(64)
+  }
+#undef SAS_SEL_CASE
+  return hipErrorInvalidValue;
+}
+
 template <int DS, typename ST>
 static hipError_t launch_topk_t(const void* qs, const void* ks, int K, int renorm, int* idx,
                                 float* bias, const Dims& D, hipStream_t st) {

@@ -23,8 +23,8 @@ _STATUS = {0: "SAS_OK", 1: "SAS_ERR_NULL", 2: "SAS_ERR_SHAPE", 3: "SAS_ERR_DTYPE
            4: "SAS_ERR_ALIGN", 5: "SAS_ERR_UNSUPPORTED", 6: "SAS_ERR_WORKSPACE",
            7: "SAS_ERR_HIP"}
 EXPORTS = ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_attn_bwd_ev",
-           "sas_topk_blocks", "sas_sparse_fwd", "sas_sparse_fwd_ev", "sas_status_string",
-           "sas_last_hip_error")
+           "sas_topk_blocks", "sas_topk_blocks_budget", "sas_sparse_fwd", "sas_sparse_fwd_ev",
+           "sas_status_string", "sas_last_hip_error")
 
 
 class SasError(RuntimeError):
@@ -58,11 +58,13 @@ def load():
         lib.sas_attn_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P]
         lib.sas_attn_bwd.argtypes = [P] * 17 + [SZ, P]
         lib.sas_topk_blocks.argtypes = [P, I32, I32, P, P, P, P, P]
+        lib.sas_topk_blocks_budget.argtypes = [P, I32, ctypes.c_float, I32, P, P, P, P, P]
         lib.sas_sparse_fwd.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P]
         lib.sas_attn_bwd_ev.argtypes = [P] * 17 + [SZ, P, I32, P]
         lib.sas_sparse_fwd_ev.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P, I32, P]
         for n in ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_topk_blocks",
-                  "sas_sparse_fwd", "sas_attn_bwd_ev", "sas_sparse_fwd_ev"):
+                  "sas_topk_blocks_budget", "sas_sparse_fwd", "sas_attn_bwd_ev",
+                  "sas_sparse_fwd_ev"):
             getattr(lib, n).restype = ctypes.c_int
         lib.sas_status_string.argtypes = [ctypes.c_int]
         lib.sas_status_string.restype = ctypes.c_char_p
@@ -192,6 +194,21 @@ def topk_blocks(qs, ks, topk, tk, block=64, renorm=0, sel_scale=None):
     _check("sas_topk_blocks", load().sas_topk_blocks(ctypes.byref(sh), int(topk), int(renorm),
                                                      _p(qs), _p(ks), _p(idx), _p(bias),
                                                      _stream(qs)))
+    return idx, bias
+
+
+def topk_blocks_budget(qs, ks, kmax, frac, tk, block=64, renorm=0, sel_scale=None):
+    """Top-K with n_t = min(kmax, c(t), ceil(frac c(t))) blocks per row (frac <= 0:
+    the fixed budget).  Returns (idx int32, bias float32), kmax slots per row."""
+    b, hq, tq, ds = qs.shape
+    hks = ks.shape[1]
+    sh = make_shape(b, hq, hks, tq, tk, 64, ds, block, hks, 0.0, sel_scale, _dt(qs), _dt(qs))
+    idx = torch.empty((b, hq, tq, kmax), dtype=torch.int32, device=qs.device)
+    bias = torch.empty((b, hq, tq, kmax), dtype=torch.float32, device=qs.device)
+    _check("sas_topk_blocks_budget",
+           load().sas_topk_blocks_budget(ctypes.byref(sh), int(kmax), ctypes.c_float(frac),
+                                         int(renorm), _p(qs), _p(ks), _p(idx), _p(bias),
+                                         _stream(qs)))
     return idx, bias
 
 

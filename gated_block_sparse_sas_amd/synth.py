@@ -40,7 +40,8 @@ class Workload:
     block: int
     dtype: str  # "f32" or "bf16"
     mode: str  # "train", "prefill" or "decode"
-    topk: int = 0
+    topk: int = 0  # fixed budget, or the cap kmax of a proportional one
+    frac: float = 0.0  # > 0: row t keeps min(topk, ceil(frac * c(t))) blocks
     hks: int = 0  # 0 -> hkv
     scales: dict = field(default_factory=dict)
 
@@ -74,8 +75,10 @@ class Workload:
 
 _HALF = {"q": 0.5, "k": 0.5, "v": 0.5}
 
-# The five workloads: a tiny fp32 case, dense-active training at 8k and 32k,
-# top-K sparse prefill at 32k and top-K sparse decode at 64k.
+# The workloads: a tiny fp32 case, dense-active training at 8k and 32k,
+# top-K sparse prefill at 32k (fixed budget of 16 blocks, and a budget of a
+# quarter of each row's history, capped at 128 blocks) and top-K sparse
+# decode at 64k.
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", 1, 1, 1, 1, 512, 512, 64, 16, 64, "f32", "train"),
     "train_8k": Workload("train_8k", 2, 1, 32, 8, 8192, 8192, 128, 32, 64, "bf16", "train",
@@ -86,6 +89,8 @@ WORKLOADS = {
                                   "bf16", "prefill", topk=16, scales=_HALF),
     "decode_64k_top8": Workload("decode_64k_top8", 5, 16, 32, 8, 1, 65536, 128, 32, 64, "bf16",
                                 "decode", topk=8, scales=_HALF),
+    "prefill_32k_top25pct": Workload("prefill_32k_top25pct", 6, 1, 32, 8, 32768, 32768, 128, 32,
+                                     64, "bf16", "prefill", topk=128, frac=0.25, scales=_HALF),
 }
 
 

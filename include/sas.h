@@ -121,6 +121,21 @@ sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, co
 sas_status sas_topk_blocks(const sas_shape* shape, int32_t topk, int32_t renorm, const void* qs,
                            const void* ks, int32_t* idx, float* bias, void* stream);
 
+/* Hard Top-K with a budget proportional to each row's history: row t keeps
+ * n_t = min(kmax, c(t), ceil(frac * c(t))) blocks (the ceiling taken in
+ * double precision on (double)frac * c(t)); frac <= 0 means no fraction
+ * (n_t = min(kmax, c(t)), the fixed budget of sas_topk_blocks, any kmax).
+ * Order, padding (idx -1, bias -inf in slots n_t .. kmax-1) and the two bias
+ * modes are those of sas_topk_blocks.  idx, bias: [batch, hq, tq, kmax].
+ * 1 <= kmax <= 1024; frac must not be NaN (SAS_ERR_SHAPE).  Needs
+ * 16 (nb + 256 + 2 * next_pow2(kmax)) bytes of LDS per workgroup, at most
+ * 64 KiB (SAS_ERR_UNSUPPORTED beyond).  Source: blog, "Implementation and
+ * Efficiency" (attention restricted to the top 25% of the context at 32k);
+ * both abstracts (hard Top-K under an attention budget). */
+sas_status sas_topk_blocks_budget(const sas_shape* shape, int32_t kmax, float frac,
+                                  int32_t renorm, const void* qs, const void* ks, int32_t* idx,
+                                  float* bias, void* stream);
+
 /* Top-K sparse attention forward (prefill: tq == tk; decode: tq == 1; any
  * 1 <= tq <= tk): every row attends its current block (causal, bias 0) plus
  * the blocks in idx with the matching bias.  idx entries must be -1 or

@@ -120,6 +120,25 @@ def test_topk_checks(lib):
     assert lib.sas_topk_blocks(ctypes.byref(big), 4, 0, A, A, A, A, STREAM) == 5
 
 
+def test_topk_budget_checks(lib):
+    sh = shape()
+    f = ctypes.c_float
+    lib.sas_topk_blocks_budget.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+                                           ctypes.c_int32] + [ctypes.c_void_p] * 5
+    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 0, f(0.25), 0, A, A, A, A, STREAM) == 2
+    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 8, f(0.25), 2, A, A, A, A, STREAM) == 2
+    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 8, f(float("nan")), 0, A, A, A, A,
+                                      STREAM) == 2
+    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 8, f(0.25), 0, None, A, A, A, STREAM) == 1
+    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 8, f(0.25), 0, A, A, A, MIS, STREAM) == 4
+    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 2048, f(0.25), 0, A, A, A, A,
+                                      STREAM) == 5
+    big = shape(tk=1 << 20, tq=64)  # the row's scores no longer fit the kernel's LDS
+    assert lib.sas_topk_blocks_budget(ctypes.byref(big), 8, f(0.25), 0, A, A, A, A, STREAM) == 5
+    assert lib.sas_topk_blocks_budget(ctypes.byref(shape(batch=0)), 8, f(0.25), 0, A, A, A, A,
+                                      STREAM) == 0
+
+
 def bwd(lib, sh, ws, n, **ptrs):
     names = ("q", "k", "v", "o", "dout", "lse", "qs", "ks", "lam", "dq", "dk", "dv", "dqs", "dks")
     p = {k: A for k in names}

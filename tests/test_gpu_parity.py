@@ -116,6 +116,48 @@ def test_topk_small(renorm, tq, tk, K):
     assert max_abs(bg[ok][fin], br[ok][fin]) <= 1e-4
 
 
+@pytest.mark.parametrize("renorm", [0, 1])
+@pytest.mark.parametrize("tq,tk,kmax,frac", [(640, 640, 6, 0.25), (300, 1088, 40, 0.3),
+                                             (256, 4096, 64, 0.0), (512, 512, 3, 2.0)])
+def test_topk_budget_small(renorm, tq, tk, kmax, frac):
+    w = W["prefill_32k_top25pct"].with_(batch=2, hq=8, hkv=2, tq=tq, tk=tk, topk=kmax, frac=frac)
+    say("topk budget", tq, tk, kmax, frac, renorm)
+    cpu, dev, f = inputs(w, ("qs", "ks"))
+    idx, bias = ops.topk_blocks_budget(dev["qs"], dev["ks"], kmax, frac, w.tk, renorm=renorm)
+    torch.cuda.synchronize()
+    S = oshape(w)
+    idx_ref, bias_ref = oracle.topk_budget(S, kmax, frac, f["qs"], f["ks"], renorm=renorm)
+    z, _, _ = oracle.gate_scores(S, f["qs"], f["ks"])
+    zf = z.reshape(-1, w.nb)
+    c = (np.arange(w.tq) + w.tk - w.tq) // 64
+    cr = np.tile(c, w.batch * w.hq)
+    ok = tie_free_rows(zf, cr, kmax)
+    ig = idx.cpu().numpy().reshape(-1, kmax)
+    ir = idx_ref.reshape(-1, kmax)
+    say("  tie-free rows", int(ok.sum()), "of", len(ok))
+    assert ok.mean() > 0.8  # 65 sorted scores per row leave fewer tie-free rows
+    assert np.array_equal(ig[ok], ir[ok])
+    # the per-row counts follow from c(t) alone: equal on every row
+    assert np.array_equal((ig >= 0).sum(-1), (ir >= 0).sum(-1))
+    bg = bias.cpu().numpy().reshape(-1, kmax)
+    br = bias_ref.reshape(-1, kmax)
+    assert np.array_equal(np.isneginf(bg[ok]), np.isneginf(br[ok]))
+    fin = np.isfinite(br[ok])
+    assert max_abs(bg[ok][fin], br[ok][fin]) <= 1e-4
+
+
+def test_topk_budget_fixed_equals_topk():
+    # frac <= 0 with kmax <= 32: the same selection as the fixed-budget kernel
+    w = W["prefill_32k_top16"].with_(batch=1, hq=4, hkv=2, tq=2048, tk=2048)
+    say("topk budget vs fixed")
+    cpu, dev, f = inputs(w, ("qs", "ks"))
+    a, ab = ops.topk_blocks_budget(dev["qs"], dev["ks"], 16, 0.0, w.tk)
+    b, bb = ops.topk_blocks(dev["qs"], dev["ks"], 16, w.tk)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert max_abs(ab.cpu().numpy()[a.cpu().numpy() >= 0], bb.cpu().numpy()[b.cpu().numpy() >= 0]) <= 1e-5
+
+
 @pytest.mark.parametrize("name", ["prefill_32k_top16", "decode_64k_top8"])
 def test_topk_full_size(name):
     w = W[name]
