@@ -7,6 +7,8 @@ One step is one pass of the whole hot path on resident synthetic inputs:
                      T 32768, 64-token blocks, selector dim 32, bf16
   prefill_32k_top16  top-K block selection -> top-K sparse forward (K = 16)
   decode_64k_top8    top-K selection -> sparse decode, 16 sequences x 64k keys
+  prefill_32k_top25pct  budgeted top-K selection (a quarter of each query's
+                     history, at most 128 blocks) -> top-K sparse forward
 The headline value is the training fwd+bwd rate at 32k in TFLOP/s counting
 attended (row, key) pairs only (forward 4*d flop per pair, backward 10*d).
 Times come from HIP events recorded on the stream the kernels run on.
@@ -45,12 +47,16 @@ def causal_pairs(tq, tk):
 
 def sparse_pairs(w):
     """Attended pairs of one head under a top-K block budget (current block
-    causal + min(K, c) full historical blocks)."""
+    causal + n(t) full historical blocks, n(t) = min(K, c), further capped at
+    ceil(frac * c) for a budget proportional to the history)."""
     tot = 0
     for i in range(w.tq):
         t = w.tk - w.tq + i
         c = t // w.block
-        tot += min(w.topk, c) * w.block + (t - c * w.block + 1)
+        n = min(w.topk, c)
+        if w.frac > 0:
+            n = min(n, math.ceil(w.frac * c))
+        tot += n * w.block + (t - c * w.block + 1)
     return tot
 
 
@@ -153,11 +159,13 @@ def main():
     torch.cuda.set_device(dev)
     W = synth.WORKLOADS
     wt, wp, wd = W["train_32k"], W["prefill_32k_top16"], W["decode_64k_top8"]
+    wq = W["prefill_32k_top25pct"]
 
     t0 = time.time()
     tr = {n: t.to(dev) for n, t in synth.draw_all(wt).items()}
     pf = {n: t.to(dev) for n, t in synth.draw_all(wp, ("q", "k", "v", "qs", "ks")).items()}
     dc = {n: t.to(dev) for n, t in synth.draw_all(wd, ("q", "k", "v", "qs", "ks")).items()}
+    pq = {n: t.to(dev) for n, t in synth.draw_all(wq, ("q", "k", "v", "qs", "ks")).items()}
     torch.cuda.synchronize()
     log("inputs resident in HBM (%.1f s)" % (time.time() - t0))
 
@@ -167,9 +175,12 @@ def main():
     ws_p = torch.empty(ops.sparse_workspace_bytes(sh_p, wp.topk), dtype=torch.uint8, device=dev)
     sh_d = ops.make_shape(wd.batch, wd.hq, wd.hkv, wd.tq, wd.tk, wd.d, wd.ds, 64, wd.hkv)
     ws_d = torch.empty(ops.sparse_workspace_bytes(sh_d, wd.topk), dtype=torch.uint8, device=dev)
+    sh_q = ops.make_shape(1, wq.hq, wq.hkv, wq.tq, wq.tk, wq.d, wq.ds, 64, wq.hkv)
+    ws_q = torch.empty(ops.sparse_workspace_bytes(sh_q, wq.topk), dtype=torch.uint8, device=dev)
 
     names = ["start", "gate", "fwd", "bwd_dq", "bwd_dkdv", "bwd_dks", "bwd", "pf_topk",
-             "pf_partial", "pf_sparse", "dc_topk", "dc_partial", "dc_sparse"]
+             "pf_partial", "pf_sparse", "dc_topk", "dc_partial", "dc_sparse", "pq_topk",
+             "pq_partial", "pq_sparse"]
 
     def step(ev):
         E = {n: ev[n] for n in names}
@@ -189,6 +200,10 @@ def main():
         E["dc_topk"].record()
         ops.sparse_fwd(dc["q"], dc["k"], dc["v"], idx, bias, ws=ws_d, events=[E["dc_partial"]])
         E["dc_sparse"].record()
+        idx, bias = ops.topk_blocks_budget(pq["qs"], pq["ks"], wq.topk, wq.frac, wq.tk)
+        E["pq_topk"].record()
+        ops.sparse_fwd(pq["q"], pq["k"], pq["v"], idx, bias, ws=ws_q, events=[E["pq_partial"]])
+        E["pq_sparse"].record()
 
     def new_events():
         return {n: torch.cuda.Event(enable_timing=True) for n in names}
@@ -218,8 +233,11 @@ def main():
         "prefill_sparse": dur("pf_topk", "pf_sparse"), "decode_topk": dur("pf_sparse", "dc_topk"),
         "decode_partial": dur("dc_topk", "dc_partial"),
         "decode_sparse": dur("dc_topk", "dc_sparse"),
+        "quarter_topk": dur("dc_sparse", "pq_topk"),
+        "quarter_partial": dur("pq_topk", "pq_partial"),
+        "quarter_sparse": dur("pq_topk", "pq_sparse"),
     }
-    step_ms = dur("start", "dc_sparse")
+    step_ms = dur("start", "pq_sparse")
 
     pairs_t = wt.batch * wt.hq * causal_pairs(wt.tq, wt.tk)
     fl_fwd = 4.0 * wt.d * pairs_t
@@ -229,6 +247,9 @@ def main():
     pairs_p = wp.batch * wp.hq * sparse_pairs(wp)
     fl_sp = 4.0 * wp.d * pairs_p
     sp_tflops = fl_sp / (part["prefill_sparse"] * 1e-3) / 1e12
+    pairs_q = wq.batch * wq.hq * sparse_pairs(wq)
+    fl_q = 4.0 * wq.d * pairs_q
+    q_tflops = fl_q / (part["quarter_sparse"] * 1e-3) / 1e12
     dec_blocks = wd.batch * wd.hq * (min(wd.topk, (wd.tk - 1) // 64) + 1)
     dec_bytes = dec_blocks * 2 * 64 * wd.d * 2  # K and V of every attended block, bf16
     dec_gbps = dec_bytes / (part["decode_sparse"] * 1e-3) / 1e9
@@ -269,7 +290,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs shaped like the pages' 32k workloads)",
         "config": {"workload": "train_32k", "batch": wt.batch, "hq": wt.hq, "hkv": wt.hkv,
                    "seq_len": wt.tq, "d": wt.d, "block": wt.block, "ds": wt.ds,
-                   "also_in_step": ["prefill_32k_top16", "decode_64k_top8"]},
+                   "also_in_step": ["prefill_32k_top16", "decode_64k_top8",
+                                    "prefill_32k_top25pct"]},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "train_ms": round(t_train, 3),
         "parts_ms": {k: round(v, 4) for k, v in part.items()},
@@ -277,6 +299,12 @@ def main():
                            "ms": round(part["prefill_sparse"], 3),
                            "topk_ms": round(part["prefill_topk"], 3),
                            "attended_pairs": pairs_p},
+        "sparse_prefill_quarter": {"workload": "prefill_32k_top25pct",
+                                   "budget": "min(%d, ceil(%.2f c(t)))" % (wq.topk, wq.frac),
+                                   "tflops": round(q_tflops, 2),
+                                   "ms": round(part["quarter_sparse"], 3),
+                                   "topk_ms": round(part["quarter_topk"], 3),
+                                   "attended_pairs": pairs_q},
         "decode": {"workload": "decode_64k_top8", "ms": round(part["decode_sparse"], 4),
                    "topk_ms": round(part["decode_topk"], 4), "kv_bytes": dec_bytes,
                    "GBps": round(dec_gbps, 1),

@@ -195,3 +195,54 @@ def test_topk_full_size(name):
         assert max_abs(bg[a][fin], br.reshape(-1)[fin]) <= 1e-4
     say("  tie-free sampled rows", n_ok, "of", len(rows))
     assert n_ok >= 0.8 * len(rows)
+
+
+def test_topk_budget_full_size():
+    # 32k prefill, a quarter of each row's history capped at 128 blocks.  With up to
+    # 128 winners a row rarely has every sorted gap clear of rounding, so each sampled
+    # row is judged at its own budget boundary: same count always; where the n-th and
+    # (n+1)-th scores are apart, the same set of blocks, the same biases in the same
+    # descending order; elsewhere every winner scores at least the best loser.
+    w = W["prefill_32k_top25pct"]
+    say("topk budget full", w.name)
+    cpu, dev, f = inputs(w, ("qs", "ks"))
+    idx, bias = ops.topk_blocks_budget(dev["qs"], dev["ks"], w.topk, w.frac, w.tk)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 1000, seed=6)
+    ig = idx.cpu().numpy().reshape(-1, w.topk)[rows]
+    bg = bias.cpu().numpy().reshape(-1, w.topk)[rows]
+    qs = f["qs"].reshape(-1, w.ds)
+    ks = f["ks"]
+    n_sep = 0
+    for a, r in enumerate(rows):
+        i = r % w.tq
+        h = (r // w.tq) % w.hq
+        b = r // (w.tq * w.hq)
+        t = w.tk - w.tq + i
+        c = t // 64
+        nb1 = (t + 1 + 63) // 64
+        ks1 = ks[b, h // (w.hq // w.kheads)][None, None, :nb1]
+        q1 = qs[r][None, None, None, :]
+        S1 = oracle.OracleShape(1, 1, 1, 1, t + 1, w.d, w.ds, 64)
+        ir, br = oracle.topk_budget(S1, w.topk, w.frac, q1, ks1)
+        ir, br = ir.reshape(-1), br.reshape(-1)
+        n = int((ir >= 0).sum())
+        assert int((ig[a] >= 0).sum()) == n, (r, n)
+        assert np.all(ig[a][n:] == -1)
+        if n == 0:
+            continue
+        z, _, _ = oracle.gate_scores(S1, q1, ks1)
+        zc = z.reshape(-1)[:c]
+        zs = np.sort(zc)[::-1]
+        sel = ig[a][:n]
+        assert len(set(sel.tolist())) == n and sel.min() >= 0 and sel.max() < c
+        # biases come out in descending order
+        assert np.all(np.diff(bg[a][:n]) <= 1e-6)
+        if n < c and zs[n - 1] - zs[n] <= 1e-5 * max(1.0, abs(zs[n])):
+            assert zc[sel].min() >= zs[n] - 1e-5
+            continue
+        n_sep += 1
+        assert set(sel.tolist()) == set(ir[:n].tolist()), r
+        assert max_abs(bg[a][:n], br[:n]) <= 1e-4
+    say("  rows separated at the budget boundary", n_sep, "of", len(rows))
+    assert n_sep >= 0.9 * len(rows)

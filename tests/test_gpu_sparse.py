@@ -28,11 +28,16 @@ SMALL = {
                                                tk=640, topk=12),
     "d64": W["prefill_32k_top16"].with_(name="d64", batch=1, hq=4, hkv=2, tq=512, tk=512, d=64,
                                         topk=3),
+    "quarter_2048": W["prefill_32k_top25pct"].with_(name="quarter_2048", batch=1, hq=8, hkv=2,
+                                                    tq=2048, tk=2048, topk=8),
 }
 
 
 def _oracle_selection(w, f, renorm=0):
-    idx, bias = oracle.topk_blocks(oshape(w), w.topk, f["qs"], f["ks"], renorm=renorm)
+    if w.frac > 0:
+        idx, bias = oracle.topk_budget(oshape(w), w.topk, w.frac, f["qs"], f["ks"], renorm=renorm)
+    else:
+        idx, bias = oracle.topk_blocks(oshape(w), w.topk, f["qs"], f["ks"], renorm=renorm)
     bias32 = bias.astype(np.float32)
     return idx, bias32
 
@@ -109,6 +114,25 @@ def test_sparse_prefill_full_size_sampled():
                             torch.from_numpy(bias32).to(DEV))
     torch.cuda.synchronize()
     rows = sample_rows(w, 256, seed=17)
+    o_ref, l_ref = oracle.sparse_fwd(oshape(w), w.topk, f["q"], f["k"], f["v"], idx,
+                                     bias32.astype(np.float64), rows=rows)
+    e = max_abs(host(o).reshape(-1, w.d)[rows], o_ref)
+    say("  O max-abs", e)
+    assert e <= 2e-2
+    assert max_abs(host(lse).reshape(-1)[rows], l_ref) <= 1e-3
+    assert torch.isfinite(o).all().item()
+
+
+def test_sparse_quarter_budget_full_size_sampled():
+    # 32k prefill at a quarter of each row's history (up to 128 blocks per row)
+    w = W["prefill_32k_top25pct"]
+    say("sparse prefill 25% full")
+    cpu, dev, f = inputs(w, ("q", "k", "v", "qs", "ks"))
+    idx, bias32 = _oracle_selection(w, f, renorm=1)
+    o, lse = ops.sparse_fwd(dev["q"], dev["k"], dev["v"], torch.from_numpy(idx).to(DEV),
+                            torch.from_numpy(bias32).to(DEV))
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 192, seed=23)
     o_ref, l_ref = oracle.sparse_fwd(oshape(w), w.topk, f["q"], f["k"], f["v"], idx,
                                      bias32.astype(np.float64), rows=rows)
     e = max_abs(host(o).reshape(-1, w.d)[rows], o_ref)
