@@ -200,7 +200,9 @@ def main():
         E["dc_topk"].record()
         ops.sparse_fwd(dc["q"], dc["k"], dc["v"], idx, bias, ws=ws_d, events=[E["dc_partial"]])
         E["dc_sparse"].record()
-        idx, bias = ops.topk_blocks_budget(pq["qs"], pq["ks"], wq.topk, wq.frac, wq.tk)
+        # the gate renormalised over the kept blocks (renorm = 1); the other
+        # sparse workloads use the training gate (renorm = 0)
+        idx, bias = ops.topk_blocks_budget(pq["qs"], pq["ks"], wq.topk, wq.frac, wq.tk, renorm=1)
         E["pq_topk"].record()
         ops.sparse_fwd(pq["q"], pq["k"], pq["v"], idx, bias, ws=ws_q, events=[E["pq_partial"]])
         E["pq_sparse"].record()
@@ -301,6 +303,7 @@ def main():
                            "attended_pairs": pairs_p},
         "sparse_prefill_quarter": {"workload": "prefill_32k_top25pct",
                                    "budget": "min(%d, ceil(%.2f c(t)))" % (wq.topk, wq.frac),
+                                   "renorm": 1,
                                    "tflops": round(q_tflops, 2),
                                    "ms": round(part["quarter_sparse"], 3),
                                    "topk_ms": round(part["quarter_topk"], 3),
