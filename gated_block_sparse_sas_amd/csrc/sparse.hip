@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void sparse_combine_kernel(const float* __rest
 // ---------------------------------------------------------------------------
 // Block-stationary prefill.
 // ---------------------------------------------------------------------------
-constexpr int kChunk = 128;  // pairs per workgroup of the partial kernel
+constexpr int kChunk = 128;  // pairs per chunk of the partial kernel (32 per wave)
 
 __global__ void sp_zero_kernel(int* __restrict__ p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -214,7 +214,8 @@ __global__ __launch_bounds__(1024) void sp_scan_kernel(const int* __restrict__ c
 __global__ __launch_bounds__(256) void sp_fill_kernel(const int* __restrict__ idx,
                                                       const int* __restrict__ start,
                                                       int* __restrict__ cursor,
-                                                      int* __restrict__ list, Dims D, int K) {
+                                                      int* __restrict__ list,
+                                                      int* __restrict__ inv, Dims D, int K) {
   extern __shared__ int sh[];  // hist[nb] then base[nb]
   int* hist = sh;
   int* base = sh + D.nb;
@@ -241,142 +242,308 @@ __global__ __launch_bounds__(256) void sp_fill_kernel(const int* __restrict__ id
   for (size_t pp = p0 + threadIdx.x; pp < p1; pp += 256) {
     const int j = ib[pp];
     const int c = (D.qoff + (int)(pp / K)) / kBlock;
-    if (j >= 0 && j < c) list[base[j] + atomicAdd(&hist[j], 1)] = (int)((size_t)bh * per_bh + pp);
+    if (j >= 0 && j < c) {
+      const int x = base[j] + atomicAdd(&hist[j], 1);
+      const int pair = (int)((size_t)bh * per_bh + pp);
+      list[x] = pair;
+      inv[pair] = x;
+    }
   }
 }
 
-// One workgroup = one chunk of <= 128 pairs of one (batch, kv head, block):
-// wave w takes pairs 32w .. 32w+31; K row-major and V transposed in LDS.
+// Historical chunk -> bucket map (chunks are numbered bucket by bucket).
+__global__ __launch_bounds__(256) void sp_chunkmap_kernel(const int* __restrict__ cstart,
+                                                          int* __restrict__ cbk, int nbk) {
+  const int bk = blockIdx.x * 256 + threadIdx.x;
+  if (bk >= nbk) return;
+  for (int x = cstart[bk]; x < cstart[bk + 1]; ++x) cbk[x] = bk;
+}
+
+// Partials of one (row, block) pair per lane-query.  The chunk sequence is
+// [current-block chunks | historical chunks]: a current-block chunk holds 128
+// (head, token) rows of one (batch, kv head, query block) and attends that
+// block causally with bias 0; a historical chunk holds up to 128 listed pairs
+// of one (batch, kv head, block) with their bias.  Partials are stored in
+// chunk order (position = chunk * 128 + pair in chunk), so every chunk writes
+// one contiguous 32 KB run; the merge finds a listed pair's partial through
+// the inverse of the list.  A workgroup walks kChunksPerWG consecutive chunks and
+// restages K and V only when the block changes (consecutive chunks mostly
+// share it).  Wave w takes pairs 32w .. 32w+31 of a chunk; K row-major and V
+// transposed in LDS; S^T = K Q^T and O^T = V^T P^T on 32x32x16 MFMA, so each
+// lane owns one query.
+constexpr int kChunksPerWG = 8;
+
 template <int HD>
 __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ bias, const int* __restrict__ list, const int* __restrict__ start,
-    const int* __restrict__ count, const int* __restrict__ cstart, float* __restrict__ plse,
-    bf16* __restrict__ po, Dims D, int K, int nbk) {
+    const int* __restrict__ count, const int* __restrict__ cstart, const int* __restrict__ cbk,
+    float* __restrict__ plse, bf16* __restrict__ po, Dims D, int K, int nbk, int nqb, int dcpb) {
   constexpr int KP = HD + 8, VP = kBlock + 4, KS = HD / 16, DM = HD / 32;
+  constexpr int OP = 72;  // pitch (bf16) of the per-wave output staging rows: 16-byte aligned
   __shared__ __align__(16) bf16 Ks[kBlock * KP];
   __shared__ __align__(16) bf16 Vt[HD * VP];
+  __shared__ __align__(16) bf16 Os[4 * 32 * OP];  // per wave: 32 queries x 64 columns
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int w = blockIdx.x;
-  if (w >= cstart[nbk]) return;
-  // bucket of this chunk: largest bk with cstart[bk] <= w (uniform binary search)
-  int lo = 0, hi = nbk - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cstart[mid] <= w) lo = mid; else hi = mid - 1;
-  }
-  const int bk = lo;
-  const int ci = w - cstart[bk];
-  const int n = min(kChunk, count[bk] - ci * kChunk);
-  const int j = bk % D.nb, bg = bk / D.nb;  // bg = b * hkv + g
-  const bf16* kb = k + ((size_t)bg * D.tk + (size_t)j * kBlock) * HD;
-  const bf16* vb = v + ((size_t)bg * D.tk + (size_t)j * kBlock) * HD;
-  // stage K (row-major) and V (transposed)
-  for (int x = tid; x < kBlock * HD / 8; x += 256) {
-    const int r = x / (HD / 8), cc = x % (HD / 8);
-    *(bf16x8*)&Ks[r * KP + cc * 8] = *(const bf16x8*)(kb + (size_t)r * HD + cc * 8);
-  }
-  for (int x = tid; x < 16 * (HD / 8); x += 256) {
-    const int kg = x % 16, dc = x / 16;
-    bf16x8 rv[4];
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) rv[i2] = *(const bf16x8*)(vb + (size_t)(kg * 4 + i2) * HD + dc * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16x4 wv = {rv[0][e], rv[1][e], rv[2][e], rv[3][e]};
-      *(bf16x4*)&Vt[(dc * 8 + e) * VP + kg * 4] = wv;
-    }
-  }
-  // this lane's pair
-  const int pi = wave * 32 + l32;
-  const bool valid = pi < n;
-  const int pair = list[start[bk] + ci * kChunk + (valid ? pi : 0)];
-  const size_t row = (size_t)pair / K;
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(q + row * HD + 16 * s + 8 * hh);
-  const float bias2 = bias[pair] * kLog2e;
+  bf16* ow = Os + wave * 32 * OP;
+  const int ndiag = D.batch * D.hkv * nqb * dcpb;
+  const int total = ndiag + cstart[nbk];
+  const int ch0 = blockIdx.x * kChunksPerWG;
+  if (ch0 >= total) return;
+  const int ch1 = min(total, ch0 + kChunksPerWG);
   const float c1 = D.sm_scale * kLog2e;
-  __syncthreads();
-  if (wave * 32 >= n) return;  // no pair for this wave
-
-  f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 a = *(const bf16x8*)&Ks[(32 * mt + l32) * KP + 16 * s + 8 * hh];
-      sacc[mt] = mfma32(a, qf[s], sacc[mt]);
+  const int qb0 = D.qoff / kBlock;  // first block holding a query row
+  const int pi = wave * 32 + l32;   // this lane's pair within a chunk
+  int cur = -1;
+  for (int ch = ch0; ch < ch1; ++ch) {
+    int kv, tmax, pos;  // pos: where the partial goes (chunk order)
+    size_t row;
+    float bv;
+    bool valid;
+    if (ch < ndiag) {
+      const int db = ch / dcpb, dc = ch - db * dcpb;
+      const int bg = db / nqb, j = qb0 + db % nqb;
+      kv = bg * D.nb + j;
+      const int p = dc * kChunk + pi;
+      const int hl = p / kBlock, tok = j * kBlock + p % kBlock;
+      valid = hl < D.hpg && tok >= D.qoff && tok < D.tk;
+      const int b = bg / D.hkv, g = bg - b * D.hkv;
+      const int h = g * D.hpg + (valid ? hl : 0);
+      row = ((size_t)b * D.hq + h) * D.tq + (valid ? tok - D.qoff : 0);
+      pos = ch * kChunk + pi;
+      bv = 0.f;
+      tmax = tok;
+    } else {
+      const int hc = ch - ndiag;
+      const int bk = cbk[hc];
+      kv = bk;
+      const int ci = hc - cstart[bk];
+      const int n = min(kChunk, count[bk] - ci * kChunk);
+      valid = pi < n;
+      const int pair = list[start[bk] + ci * kChunk + (valid ? pi : 0)];
+      row = (size_t)pair / K;
+      pos = ndiag * kChunk + start[bk] + ci * kChunk + pi;
+      bv = bias[pair];
+      tmax = 0x7fffffff;  // a historical block lies wholly before the query
     }
-  }
-  float mx = -INFINITY;
+    bf16x8 qf[KS];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(q + row * HD + 16 * s + 8 * hh);
+    kv = __builtin_amdgcn_readfirstlane(kv);
+    if (kv != cur) {
+      __syncthreads();  // every wave is done with the previous block
+      const int j = kv % D.nb, bg = kv / D.nb;
+      const bf16* kb = k + ((size_t)bg * D.tk + (size_t)j * kBlock) * HD;
+      const bf16* vb = v + ((size_t)bg * D.tk + (size_t)j * kBlock) * HD;
+      for (int x = tid; x < kBlock * HD / 8; x += 256) {
+        const int r = x / (HD / 8), cc = x % (HD / 8);
+        *(bf16x8*)&Ks[r * KP + cc * 8] = *(const bf16x8*)(kb + (size_t)r * HD + cc * 8);
+      }
+      for (int x = tid; x < 16 * (HD / 8); x += 256) {
+        const int kg = x % 16, dcol = x / 16;
+        bf16x8 rv[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m2 = fmaf(mx, c1, bias2);  // row max in log2 units (finite unless bias is -inf)
-  const float off = bias2 - (m2 == -INFINITY ? 0.f : m2);
-  float l = 0.f;
+        for (int i2 = 0; i2 < 4; ++i2)
+          rv[i2] = *(const bf16x8*)(vb + (size_t)(kg * 4 + i2) * HD + dcol * 8);
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = exp2_raw(fmaf(sacc[mt][r], c1, off));
-      sacc[mt][r] = p;
-      l += p;
+        for (int e = 0; e < 8; ++e) {
+          bf16x4 wv = {rv[0][e], rv[1][e], rv[2][e], rv[3][e]};
+          *(bf16x4*)&Vt[(dcol * 8 + e) * VP + kg * 4] = wv;
+        }
+      }
+      __syncthreads();
+      cur = kv;
     }
-  l += __shfl_xor(l, 32);
-  f32x16 oacc[DM];
+    if (!__any(valid)) continue;  // wave-uniform: no pair of this chunk for this wave
+    const float bias2 = bv * kLog2e;
+    const int u0 = (kv % D.nb) * kBlock;
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-  for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
+    for (int s = 0; s < KS; ++s) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (bf16)sacc[mt][8 * pp + e];
-#pragma unroll
-      for (int dm = 0; dm < DM; ++dm) {
-        const bf16* vp = &Vt[(32 * dm + l32) * VP + 32 * mt + 16 * pp + 4 * hh];
-        const bf16x4 lo4 = *(const bf16x4*)vp;
-        const bf16x4 hi4 = *(const bf16x4*)(vp + 8);
-        oacc[dm] = mfma32(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[dm]);
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 a = *(const bf16x8*)&Ks[(32 * mt + l32) * KP + 16 * s + 8 * hh];
+        sacc[mt] = mfma32(a, qf[s], sacc[mt]);
       }
     }
-  }
-  if (!valid) return;
-  const bool live = l > 0.f && m2 != -INFINITY;
-  const float inv = live ? 1.f / l : 0.f;
-  bf16* dst = po + (size_t)pair * HD;
+    float mx = -INFINITY;
 #pragma unroll
-  for (int dm = 0; dm < DM; ++dm) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      bf16x4 wv;
+      for (int r = 0; r < 16; ++r) {
+        const int u = u0 + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
+        if (u > tmax) sacc[mt][r] = -INFINITY;
+        mx = fmaxf(mx, sacc[mt][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m2 = fmaf(mx, c1, bias2);  // row max in log2 units (-inf only if bias is -inf)
+    const float off = bias2 - (m2 == -INFINITY ? 0.f : m2);
+    float l = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wv[e] = (bf16)(oacc[dm][4 * rr + e] * inv);
-      *(bf16x4*)(dst + 32 * dm + 8 * rr + 4 * hh) = wv;
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = exp2_raw(fmaf(sacc[mt][r], c1, off));
+        sacc[mt][r] = pv;
+        l += pv;
+      }
+    l += __shfl_xor(l, 32);
+    f32x16 oacc[DM];
+#pragma unroll
+    for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (bf16)sacc[mt][8 * pp + e];
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) {
+          const bf16* vp = &Vt[(32 * dm + l32) * VP + 32 * mt + 16 * pp + 4 * hh];
+          const bf16x4 lo4 = *(const bf16x4*)vp;
+          const bf16x4 hi4 = *(const bf16x4*)(vp + 8);
+          oacc[dm] = mfma32(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[dm]);
+        }
+      }
+    }
+    const bool live = l > 0.f && m2 != -INFINITY;
+    const float inv = live ? 1.f / l : 0.f;
+    const int ps = valid ? pos : -1;
+    if (valid && hh == 0) plse[ps] = live ? (m2 + log2f(l)) * kLn2 : -INFINITY;
+    // Normalised partial rows go out through LDS, 64 columns at a time, so that
+    // eight lanes write one contiguous 128-byte run of a row.
+    const int rq = lane >> 3, c8 = (lane & 7) * 8;
+#pragma unroll
+    for (int hf = 0; hf < DM / 2; ++hf) {
+#pragma unroll
+      for (int d2 = 0; d2 < 2; ++d2) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          bf16x4 wv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wv[e] = (bf16)(oacc[2 * hf + d2][4 * rr + e] * inv);
+          *(bf16x4*)&ow[l32 * OP + 32 * d2 + 8 * rr + 4 * hh] = wv;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = rq + 8 * it;
+        const int pr = __shfl(ps, r);
+        const bf16x8 ov = *(const bf16x8*)&ow[r * OP + c8];
+        if (pr >= 0) *(bf16x8*)(po + (size_t)pr * HD + 64 * hf + c8) = ov;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   }
-  if (hh == 0) plse[pair] = live ? (m2 + log2f(l)) * kLn2 : -INFINITY;
 }
 
-// The block path histograms blocks in LDS: nb <= 8192 (64 KB for the fill).
-static bool use_block_path(const Dims& D) { return D.tq >= 128 && D.nb <= 8192; }
+// Merge of a row's partials: its current block (always present) and every
+// slot s < K whose block idx[row, s] lies before c(t).  L = log sum exp(lse_s),
+// O = sum_s exp(lse_s - L) O_s.  One wavefront per row; a partial row is read
+// by HD/8 lanes, 16 bytes each, so one load instruction covers 64/(HD/8) slots.
+template <int HD>
+__global__ __launch_bounds__(256) void sp_merge_kernel(const int* __restrict__ idx,
+                                                       const int* __restrict__ inv,
+                                                       const float* __restrict__ plse,
+                                                       const bf16* __restrict__ po,
+                                                       bf16* __restrict__ o,
+                                                       float* __restrict__ lse, Dims D, int K,
+                                                       int nqb, int dcpb) {
+  constexpr int LPP = HD / 8, SPW = 64 / LPP;
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t nrows = (size_t)D.batch * D.hq * D.tq;
+  if (row >= nrows) return;
+  const int i = (int)(row % D.tq), t = D.qoff + i, c = t / kBlock;
+  const int h = (int)((row / D.tq) % D.hq), b = (int)(row / ((size_t)D.tq * D.hq));
+  const int g = h / D.hpg, hl = h - g * D.hpg;
+  // chunk-order position of the current block's partial and of the listed ones
+  const int dpos = ((b * D.hkv + g) * nqb + (c - D.qoff / kBlock)) * dcpb * kChunk +
+                   hl * kBlock + t % kBlock;
+  const int hbase = D.batch * D.hkv * nqb * dcpb * kChunk;
+  const int* ir = idx + row * K;
+  const int* iv = inv + row * K;
+  const int grp = lane / LPP, col = (lane % LPP) * 8;
+  const bf16* pr = po + col;
+  // online merge in log2 units: m running max, sm = sum of 2^(lse - m),
+  // acc = sum of 2^(lse - m) O (group g of lanes holds the slots it loaded)
+  float m = plse[dpos] * kLog2e, sm = 1.f;
+  float acc[8];
+  {
+    const bf16x8 cv = *(const bf16x8*)(pr + (size_t)dpos * HD);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = grp == 0 ? to_f32(cv[e]) : 0.f;
+  }
+  // the listed slots, 64 at a time: each lane reads one slot's block, position and lse
+  for (int w0 = 0; w0 < K; w0 += 64) {
+    const int x = w0 + lane;
+    const int j = x < K ? ir[x] : -1;
+    const bool ok = j >= 0 && j < c;
+    const int px = ok ? hbase + iv[x] : dpos;
+    const float lx = ok ? plse[px] * kLog2e : -INFINITY;
+    const unsigned long long bal = __ballot(ok);
+    if (bal == 0) continue;
+    const float m_new = fmaxf(m, wave_max(lx));
+    const float alpha = exp2_raw(m - m_new);
+    m = m_new;
+    const float pw = ok ? exp2_raw(lx - m) : 0.f;
+    sm = sm * alpha + wave_sum(pw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+    const int nval = 64 - __builtin_clzll(bal);  // slots past the last valid one are skipped
+#pragma unroll 4
+    for (int q0 = 0; q0 < nval; q0 += SPW) {
+      const int sl = q0 + grp;
+      const float w = __shfl(pw, sl);
+      const int pp = __shfl(px, sl);
+      const bf16x8 pv = *(const bf16x8*)(pr + (size_t)pp * HD);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, w != 0.f ? to_f32(pv[e]) : 0.f, acc[e]);
+    }
+  }
+#pragma unroll
+  for (int of = LPP; of < 64; of <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], of);
+  if (grp == 0) {
+    const float inv_s = 1.f / sm;
+    bf16x8 ov;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] = (bf16)(acc[e] * inv_s);
+    *(bf16x8*)(o + row * HD + col) = ov;
+  }
+  if (lane == 0 && lse) lse[row] = (m + log2f(sm)) * kLn2;
+}
+
+static int diag_chunks_per_block(const Dims& D) { return (D.hpg * kBlock + kChunk - 1) / kChunk; }
+static int query_blocks(const Dims& D) { return D.nb - D.qoff / kBlock; }
+// Partial slots of the block path: current-block chunks, then one per listed pair.
+static size_t block_path_slots(const Dims& D, int K) {
+  return (size_t)D.batch * D.hkv * query_blocks(D) * diag_chunks_per_block(D) * kChunk +
+         (size_t)D.batch * D.hq * D.tq * K;
+}
+
+// The block path histograms blocks in LDS: nb <= 8192 (64 KB for the fill);
+// partial positions are int.
+static bool use_block_path(const Dims& D, int K) {
+  return D.tq >= 128 && D.nb <= 8192 && block_path_slots(D, K) < ((size_t)1 << 31);
+}
 
 // Workspace: pair path  [plse (rows x (K+1)) | po (rows x (K+1) x d)];
-// block path [count | cursor | start | cstart | list (rows x K) | plse | po (rows x K x d)].
+// block path [count | cursor | start | cstart | cbk | list (rows x K) | inv (rows x K) |
+//             plse (slots) | po (slots x d)].
 size_t sparse_workspace(const Dims& D, int K) {
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
-  if (use_block_path(D)) {
+  if (use_block_path(D, K)) {
     const size_t nbk = (size_t)D.batch * D.hkv * D.nb;
-    const size_t pairs = rows * K;
-    return 3 * align256s(nbk * 4) + align256s((nbk + 1) * 4) + align256s(pairs * 4) +
-           align256s(pairs * 4) + align256s(pairs * D.d * 2);
+    const size_t pairs = rows * K, slots = block_path_slots(D, K);
+    const size_t max_chunks = pairs / kChunk + nbk;
+    return 3 * align256s(nbk * 4) + align256s((nbk + 1) * 4) + align256s(max_chunks * 4) +
+           2 * align256s(pairs * 4) + align256s(slots * 4) + align256s(slots * D.d * 2);
   }
   const size_t pairs = rows * (K + 1);
   const size_t esz = 4;  // partial outputs are stored in the io dtype (<= 4 bytes)
@@ -388,15 +555,18 @@ static hipError_t launch_block_path(const void* q, const void* k, const void* v,
                                     const float* bias, void* o, float* lse, char* ws, int K,
                                     const Dims& D, const StageEvents& E, hipStream_t st) {
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
-  const size_t pairs = rows * K;
+  const size_t pairs = rows * K, slots = block_path_slots(D, K);
   const int nbk = D.batch * D.hkv * D.nb;
+  const size_t max_chunks = pairs / kChunk + (size_t)nbk;
   char* p = ws;
   int* count = (int*)p;  p += align256s((size_t)nbk * 4);
   int* cursor = (int*)p; p += align256s((size_t)nbk * 4);
   int* start = (int*)p;  p += align256s((size_t)nbk * 4);
   int* cstart = (int*)p; p += align256s((size_t)(nbk + 1) * 4);
+  int* cbk = (int*)p;    p += align256s(max_chunks * 4);
   int* list = (int*)p;   p += align256s(pairs * 4);
-  float* plse = (float*)p; p += align256s(pairs * 4);
+  int* inv = (int*)p;    p += align256s(pairs * 4);
+  float* plse = (float*)p; p += align256s(slots * 4);
   bf16* po = (bf16*)p;
   const unsigned zg = (unsigned)std::min<size_t>((2 * (size_t)nbk + 255) / 256, 4096);
   hipLaunchKernelGGL(sp_zero_kernel, dim3(zg), dim3(256), 0, st, count, (size_t)nbk);
@@ -406,17 +576,24 @@ static hipError_t launch_block_path(const void* q, const void* k, const void* v,
   hipLaunchKernelGGL(sp_scan_kernel, dim3(1), dim3(1024), 0, st, (const int*)count, start, cstart,
                      nbk);
   hipLaunchKernelGGL(sp_fill_kernel, ig, dim3(256), (size_t)D.nb * 8, st, idx, (const int*)start,
-                     cursor, list, D, K);
+                     cursor, list, inv, D, K);
+  hipLaunchKernelGGL(sp_chunkmap_kernel, dim3((unsigned)((nbk + 255) / 256)), dim3(256), 0, st,
+                     (const int*)cstart, cbk, nbk);
   // upper bound on the number of chunks; workgroups past the real count exit
-  const size_t max_chunks = pairs / kChunk + (size_t)nbk;
-  hipLaunchKernelGGL((sp_partial_kernel<HD>), dim3((unsigned)max_chunks), dim3(256), 0, st,
+  const int nqb = query_blocks(D), dcpb = diag_chunks_per_block(D);
+  const size_t ndiag = (size_t)D.batch * D.hkv * nqb * dcpb;
+  const size_t wgs = (ndiag + max_chunks + kChunksPerWG - 1) / kChunksPerWG;
+  hipLaunchKernelGGL((sp_partial_kernel<HD>), dim3((unsigned)wgs), dim3(256), 0, st,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, bias, (const int*)list,
-                     (const int*)start, (const int*)count, (const int*)cstart, plse, po, D, K,
-                     nbk);
+                     (const int*)start, (const int*)count, (const int*)cstart, (const int*)cbk,
+                     plse, po, D, K, nbk, nqb, dcpb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   E.record(0, st);
-  return launch_sparse_merge(q, k, v, idx, plse, po, o, lse, K, D, st);
+  hipLaunchKernelGGL((sp_merge_kernel<HD>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                     idx, (const int*)inv, (const float*)plse, (const bf16*)po, (bf16*)o, lse, D,
+                     K, nqb, dcpb);
+  return hipGetLastError();
 }
 
 template <int HD, typename T>
@@ -444,7 +621,7 @@ hipError_t launch_sparse(const void* q, const void* k, const void* v, const int*
                          int K, const Dims& D, bool bf16_io, const StageEvents& E,
                          hipStream_t st) {
   (void)ws_bytes;
-  if (bf16_io && use_block_path(D)) {
+  if (bf16_io && use_block_path(D, K)) {
     if (D.d == 128) return launch_block_path<128>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
     if (D.d == 64) return launch_block_path<64>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
   }
