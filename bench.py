@@ -102,7 +102,7 @@ def cpu_baseline(T: int):
 KERNELS = {
     "bwd_dkdv": ("bwd_dkdv16_kernel<32>", ("attn_bwd.hip", "sas_device.h", "sas_internal.h")),
     "bwd_dq": ("bwd_dq16_kernel<32>", ("attn_bwd.hip", "sas_device.h", "sas_internal.h")),
-    "fwd": ("attn_fwd_kernel<128, 32, false>", ("attn_fwd.hip", "sas_device.h", "sas_internal.h")),
+    "fwd": ("attn_fwd_kernel<128, 32>", ("attn_fwd.hip", "sas_device.h", "sas_internal.h")),
 }
 
 

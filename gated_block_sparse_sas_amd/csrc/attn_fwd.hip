@@ -38,20 +38,14 @@
 
 namespace sas {
 
-// SPARSE = true turns the kernel into the merge step of the top-K sparse
-// forward: each row attends only its current block (causal), then folds in
-// the K per-block partials (log-sum-exp, normalised output) computed by the
-// block-stationary kernel in sparse.hip.
 // workgroup: kFwdWaves waves of 32 query rows (kFwdRows rows) sharing each K/V tile
 constexpr int kFwdWaves = 8, kFwdThreads = 64 * kFwdWaves, kFwdRows = 32 * kFwdWaves;
 
-template <int HD, int DS, bool SPARSE = false>
+template <int HD, int DS>
 __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
-    bf16* __restrict__ o, float* __restrict__ lse, Dims D, int nqt, int xcd_groups,
-    const int* __restrict__ sp_idx = nullptr, const float* __restrict__ sp_lse = nullptr,
-    const bf16* __restrict__ sp_o = nullptr, int sp_k = 0) {
+    bf16* __restrict__ o, float* __restrict__ lse, Dims D, int nqt, int xcd_groups) {
   constexpr int DC = HD / 8;                 // 16-byte chunks of a row
   constexpr int SP = HD == 128 ? 18 : 10;    // LDS row pitch in 16-byte slots (K and V)
   constexpr int KP = SP * 8, VP = KP;        // row pitches (elements)
@@ -85,8 +79,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   const int c_hi = (D.qoff + min(wq0 + 31, D.tq - 1)) / kBlock;
   const int c_end = (D.qoff + min(qt * kFwdRows + kFwdRows - 1, D.tq - 1)) / kBlock;
 
-  // first tile: 0, or in sparse mode the first current block of the workgroup
-  const int j_begin = SPARSE ? (D.qoff + min(qt * kFwdRows, D.tq - 1)) / kBlock : 0;
 
   const size_t qrow = ((size_t)b * D.hq + h) * D.tq + qc;
   bf16x8 qf[KS];
@@ -97,9 +89,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   bf16x2 qsv[DS / 4];
 #pragma unroll
   for (int e = 0; e < DS / 4; ++e)
-    qsv[e] = SPARSE ? bf16x2{} : *(const bf16x2*)(qs + qrow * DS + hh * (DS / 2) + 2 * e);
-  const float lam_t = (!SPARSE && c > 0) ? lam[qrow] : 0.f;
-  const bf16* ksb0 = SPARSE ? ks : ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS;
+    qsv[e] = *(const bf16x2*)(qs + qrow * DS + hh * (DS / 2) + 2 * e);
+  const float lam_t = c > 0 ? lam[qrow] : 0.f;
+  const bf16* ksb0 = ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS;
   const bf16* kb = k + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
   const bf16* vb = v + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
   const float c1 = D.sm_scale * kLog2e;
@@ -122,7 +114,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       kreg[x] = *(const bf16x8*)(kt + (id / DC) * HD + (id % DC) * 8);
       vreg[x] = *(const bf16x8*)(vt + (id / DC) * HD + (id % DC) * 8);
     }
-    if (!SPARSE && tid < DS / 8) sreg = *(const bf16x8*)(ksb0 + (size_t)j * DS + tid * 8);
+    if (tid < DS / 8) sreg = *(const bf16x8*)(ksb0 + (size_t)j * DS + tid * 8);
   };
   auto sstore = [&](bf16* Kd, bf16* Vd, bf16* Sd) __attribute__((always_inline)) {
 #pragma unroll
@@ -131,7 +123,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       *(bf16x8*)&Kd[(id / DC) * KP + (id % DC) * 8] = kreg[x];
       *(bf16x8*)&Vd[(id / DC) * VP + (id % DC) * 8] = vreg[x];
     }
-    if (!SPARSE && tid < DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
+    if (tid < DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
   };
   // per-lane part of the transposing V^T reads: lane 4k + a of each 16-lane
   // group points at key row 4 hh + k, columns 16 ((lane >> 4) & 1) + 4 a
@@ -143,7 +135,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     float bias2 = 0.f;  // log2-domain gate bias of this lane's row for block j
-    if (!SPARSE && j < c_hi) {
+    if (j < c_hi) {
       const bf16x2* kr = (const bf16x2*)(Ss + hh * (DS / 2));
       float part = 0.f;
 #pragma unroll
@@ -169,7 +161,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       for (int r = 0; r < 16; ++r) {
         if constexpr (MASK) {
           const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
-          if (u > t || (SPARSE && j != c)) sacc[mt][r] = -INFINITY;
+          if (u > t) sacc[mt][r] = -INFINITY;
         }
         mx = fmaxf(mx, sacc[mt][r]);
       }
@@ -187,7 +179,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       m_run = m_new;
     }
     // (m_run is -inf only for a row with no visible key yet: all p are 0)
-    const float off = bias2 - ((SPARSE && m_run == -INFINITY) ? 0.f : m_run);
+    const float off = bias2 - m_run;
     float psum = 0.f;
     bf16x8 pb[2][2];
 #pragma unroll
@@ -221,17 +213,17 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   auto run = [&](int j, const bf16* Ks, const bf16* Vs, const bf16* Ss)
       __attribute__((always_inline)) {
     if (j > c_hi) return;  // past this wave's last block
-    if (!SPARSE && j < c_lo)
+    if (j < c_lo)
       tile(j, std::false_type{}, Ks, Vs, Ss);
     else
       tile(j, std::true_type{}, Ks, Vs, Ss);
   };
 
-  gload(j_begin);
+  gload(0);
   sstore(K0, V0, S0);
   __syncthreads();
   // unrolled by two so that both buffers' code sits in one loop body
-  for (int j = j_begin; j <= c_end; j += 2) {
+  for (int j = 0; j <= c_end; j += 2) {
     if (j + 1 <= c_end) gload(j + 1);
     run(j, K0, V0, S0);
     if (j + 1 <= c_end) sstore(K1, V1, S1);
@@ -244,42 +236,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   }
 
   l_run += __shfl_xor(l_run, 32);
-  if constexpr (SPARSE) {
-    // merge the current block (m_run, l_run, oacc) with the row's partials
-    const float lcur = m_run + log2f(l_run);
-    const int* ir = sp_idx + qrow * sp_k;
-    float M = lcur;
-    for (int s2 = 0; s2 < sp_k; ++s2) {
-      const int jj = ir[s2];
-      if (jj >= 0 && jj < c) M = fmaxf(M, sp_lse[qrow * sp_k + s2] * kLog2e);
-    }
-    float S = exp2_raw(lcur - M);
-    for (int s2 = 0; s2 < sp_k; ++s2) {
-      const int jj = ir[s2];
-      if (jj >= 0 && jj < c) S += exp2_raw(sp_lse[qrow * sp_k + s2] * kLog2e - M);
-    }
-    const float L2 = M + log2f(S);
-    const float wcur = exp2_raw(lcur - L2) / l_run;
-#pragma unroll
-    for (int dm = 0; dm < DM; ++dm) oacc[dm] *= wcur;
-    for (int s2 = 0; s2 < sp_k; ++s2) {
-      const int jj = ir[s2];
-      if (!(jj >= 0 && jj < c)) continue;
-      const float wsl = exp2_raw(sp_lse[qrow * sp_k + s2] * kLog2e - L2);
-      const bf16* src = sp_o + (qrow * sp_k + s2) * HD;
-#pragma unroll
-      for (int dm = 0; dm < DM; ++dm) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const bf16x4 pv = *(const bf16x4*)(src + 32 * dm + 8 * rr + 4 * hh);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) oacc[dm][4 * rr + e] = fmaf(wsl, to_f32(pv[e]), oacc[dm][4 * rr + e]);
-        }
-      }
-    }
-    m_run = L2;
-    l_run = 1.f;
-  }
   if (qi < D.tq) {
     const float inv = 1.f / l_run;
     bf16* orow = o + qrow * HD;
@@ -309,30 +265,6 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, cons
                      (const bf16*)k, (const bf16*)v, (const bf16*)qs, (const bf16*)ks, lam,
                      (bf16*)o, lse, D, nqt, xcd_groups);
   return hipGetLastError();
-}
-
-template <int HD>
-static hipError_t launch_sparse_merge_t(const void* q, const void* k, const void* v,
-                                        const int* idx, const float* plse, const void* po,
-                                        void* o, float* lse_out, int K, const Dims& D,
-                                        hipStream_t st) {
-  const int nqt = (D.tq + kFwdRows - 1) / kFwdRows;
-  const int groups = D.batch * D.hkv;
-  const int xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
-  const unsigned grid = (unsigned)(D.batch * D.hq * nqt);
-  hipLaunchKernelGGL((attn_fwd_kernel<HD, 16, true>), dim3(grid), dim3(kFwdThreads), 0, st,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)nullptr,
-                     (const bf16*)nullptr, (const float*)nullptr, (bf16*)o, lse_out, D, nqt,
-                     xcd_groups, idx, plse, (const bf16*)po, K);
-  return hipGetLastError();
-}
-
-hipError_t launch_sparse_merge(const void* q, const void* k, const void* v, const int* idx,
-                               const float* plse, const void* po, void* o, float* lse,
-                               int K, const Dims& D, hipStream_t st) {
-  if (D.d == 128) return launch_sparse_merge_t<128>(q, k, v, idx, plse, po, o, lse, K, D, st);
-  if (D.d == 64) return launch_sparse_merge_t<64>(q, k, v, idx, plse, po, o, lse, K, D, st);
-  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const void* qs,

@@ -55,10 +55,7 @@ hipError_t launch_topk_budget(const void* qs, const void* ks, int kmax, float fr
 hipError_t launch_topk(const void* qs, const void* ks, int K, int renorm, int* idx, float* bias,
                        const Dims& D, bool sel_bf16, hipStream_t st);
 
-// Steps 6-7: sparse forward.  The merge step reuses the forward kernel.
-hipError_t launch_sparse_merge(const void* q, const void* k, const void* v, const int* idx,
-                               const float* plse, const void* po, void* o, float* lse,
-                               int K, const Dims& D, hipStream_t st);
+// Steps 6-7: sparse forward.
 size_t sparse_workspace(const Dims& D, int K);
 hipError_t launch_sparse(const void* q, const void* k, const void* v, const int* idx,
                          const float* bias, void* o, float* lse, char* ws, size_t ws_bytes,
