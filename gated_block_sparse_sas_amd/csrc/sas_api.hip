@@ -61,6 +61,45 @@ sas_status resolve(const sas_shape* s, sas::Dims* D) {
   return SAS_OK;
 }
 
+// Paged-cache shape -> Dims with tq = 1, nb = max_blocks, tk = 64 * max_blocks.
+sas_status resolve_paged(const sas_paged_shape* s, sas::Dims* D) {
+  if (!s) return SAS_ERR_NULL;
+  if ((s->dtype != SAS_F32 && s->dtype != SAS_BF16) ||
+      (s->sel_dtype != SAS_F32 && s->sel_dtype != SAS_BF16))
+    return SAS_ERR_DTYPE;
+  if (s->dtype != s->sel_dtype) return SAS_ERR_DTYPE;
+  const int hks = s->hks > 0 ? s->hks : s->hkv;
+  if (s->batch < 0 || s->hq < 1 || s->hkv < 1 || hks < 1 || s->d < 1 || s->ds < 1 ||
+      s->block < 1 || s->max_blocks < 1 || s->pages < 1)
+    return SAS_ERR_SHAPE;
+  if (s->hq % s->hkv != 0 || s->hq % hks != 0) return SAS_ERR_SHAPE;
+  if (isnan(s->sm_scale) || isnan(s->sel_scale) ||
+      !(s->sm_scale <= 0.f || isfinite(s->sm_scale)) ||
+      !(s->sel_scale <= 0.f || isfinite(s->sel_scale)))
+    return SAS_ERR_SHAPE;
+  if (s->block != sas::kBlock) return SAS_ERR_UNSUPPORTED;
+  if (s->d != 64 && s->d != 128) return SAS_ERR_UNSUPPORTED;
+  if (s->ds != 16 && s->ds != 32 && s->ds != 64) return SAS_ERR_UNSUPPORTED;
+  if ((int64_t)s->max_blocks * sas::kBlock >= (int64_t)1 << 31 ||
+      (int64_t)s->batch * s->hq >= (int64_t)1 << 31)
+    return SAS_ERR_UNSUPPORTED;
+  D->batch = s->batch;
+  D->hq = s->hq;
+  D->hkv = s->hkv;
+  D->hks = hks;
+  D->tq = 1;
+  D->tk = s->max_blocks * sas::kBlock;
+  D->d = s->d;
+  D->ds = s->ds;
+  D->nb = s->max_blocks;
+  D->qoff = D->tk - 1;
+  D->hpg = s->hq / s->hkv;
+  D->hps = s->hq / hks;
+  D->sm_scale = s->sm_scale > 0.f ? s->sm_scale : 1.0f / sqrtf((float)s->d);
+  D->sel_scale = s->sel_scale > 0.f ? s->sel_scale : 1.0f / sqrtf((float)s->ds);
+  return SAS_OK;
+}
+
 sas_status check_ptrs(std::initializer_list<const void*> req) {
   for (const void* p : req)
     if (!p) return SAS_ERR_NULL;
@@ -237,6 +276,63 @@ sas_status sas_sparse_fwd_ev(const sas_shape* shape, int32_t topk, const void* q
   if (n_events < 0 || n_events > 1) return SAS_ERR_SHAPE;
   return sparse_fwd_impl(shape, topk, q, k, v, idx, bias, o, lse, ws, ws_bytes,
                          sas::StageEvents{events, n_events}, stream);
+}
+
+sas_status sas_paged_append(const sas_paged_shape* shape, const int32_t* pos,
+                            const int32_t* block_table, const void* k_new, const void* v_new,
+                            const void* ks_new, void* k_pool, void* v_pool, void* ks_pool,
+                            void* stream) {
+  sas::Dims D;
+  sas_status r = resolve_paged(shape, &D);
+  if (r != SAS_OK) return r;
+  if ((r = check_ptrs({pos, block_table, k_new, v_new, k_pool, v_pool})) != SAS_OK) return r;
+  if (ks_new && !ks_pool) return SAS_ERR_NULL;
+  if ((r = check_opt({ks_new, ks_pool})) != SAS_OK) return r;
+  if (D.batch == 0) return SAS_OK;
+  return hip_status(sas::launch_paged_append(pos, block_table, k_new, v_new, ks_new, k_pool,
+                                             v_pool, ks_pool, D, shape->pages,
+                                             shape->dtype == SAS_BF16, (hipStream_t)stream));
+}
+
+sas_status sas_paged_topk(const sas_paged_shape* shape, int32_t topk, int32_t renorm,
+                          const int32_t* seq_len, const int32_t* block_table, const void* qs,
+                          const void* ks_pool, int32_t* idx, float* bias, void* stream) {
+  sas::Dims D;
+  sas_status r = resolve_paged(shape, &D);
+  if (r != SAS_OK) return r;
+  if (topk < 1 || (renorm != 0 && renorm != 1)) return SAS_ERR_SHAPE;
+  if ((r = check_ptrs({seq_len, block_table, qs, ks_pool, idx, bias})) != SAS_OK) return r;
+  if ((size_t)(D.nb + topk) * sizeof(float) > 65536) return SAS_ERR_UNSUPPORTED;
+  if ((int64_t)D.batch * D.hq * topk >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
+  if (D.batch == 0) return SAS_OK;
+  return hip_status(sas::launch_paged_topk(qs, ks_pool, block_table, seq_len, shape->pages, topk,
+                                           renorm, idx, bias, D, shape->sel_dtype == SAS_BF16,
+                                           (hipStream_t)stream));
+}
+
+sas_status sas_paged_decode(const sas_paged_shape* shape, int32_t topk, const int32_t* seq_len,
+                            const int32_t* block_table, const void* q, const void* k_pool,
+                            const void* v_pool, const int32_t* idx, const float* bias, void* o,
+                            float* lse, void* ws, size_t* ws_bytes, void* stream) {
+  sas::Dims D;
+  sas_status r = resolve_paged(shape, &D);
+  if (r != SAS_OK) return r;
+  if (topk < 1) return SAS_ERR_SHAPE;
+  if (!ws_bytes) return SAS_ERR_NULL;
+  if ((int64_t)D.batch * D.hq * (topk + 1) >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
+  const size_t need = sas::paged_workspace(D, topk);
+  if (!ws) {
+    *ws_bytes = need;
+    return SAS_OK;
+  }
+  if ((r = check_ptrs({seq_len, block_table, q, k_pool, v_pool, idx, bias, o, ws})) != SAS_OK)
+    return r;
+  if ((r = check_opt({lse})) != SAS_OK) return r;
+  if (*ws_bytes < need) return SAS_ERR_WORKSPACE;
+  if (D.batch == 0) return SAS_OK;
+  return hip_status(sas::launch_paged_decode(q, k_pool, v_pool, block_table, seq_len,
+                                             shape->pages, idx, bias, o, lse, (char*)ws, topk, D,
+                                             shape->dtype == SAS_BF16, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -62,4 +62,19 @@ hipError_t launch_sparse(const void* q, const void* k, const void* v, const int*
                          int K, const Dims& D, bool bf16_io, const StageEvents& E,
                          hipStream_t st);
 
+// Paged decode cache (serving): append, selection and decode over page pools.
+// Dims: tq = 1, nb = max_blocks, tk = 64 * max_blocks.
+hipError_t launch_paged_append(const int* pos, const int* table, const void* k_new,
+                               const void* v_new, const void* ks_new, void* k_pool, void* v_pool,
+                               void* ks_pool, const Dims& D, int pages, bool is_bf16,
+                               hipStream_t st);
+hipError_t launch_paged_topk(const void* qs, const void* ks_pool, const int* table,
+                             const int* lens, int pages, int K, int renorm, int* idx, float* bias,
+                             const Dims& D, bool sel_bf16, hipStream_t st);
+size_t paged_workspace(const Dims& D, int K);
+hipError_t launch_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                               const int* table, const int* lens, int pages, const int* idx,
+                               const float* bias, void* o, float* lse, char* ws, int K,
+                               const Dims& D, bool bf16_io, hipStream_t st);
+
 }  // namespace sas

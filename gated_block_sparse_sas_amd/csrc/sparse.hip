@@ -34,11 +34,45 @@ namespace sas {
 
 static size_t align256s(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Where a row's keys live.  DenseKV: contiguous [B, Hkv, Tk, d] caches, row
+// i of the query block at t = q_off + i.  PagedKV: pools [pages, Hkv, 64, d]
+// (one 64-key block per page, 16 KB per head at d = 128), a sequence's block
+// j on page table[b, j], its decode row at t = len[b] - 1.  A row whose length
+// is out of range has no keys (t = -1); a block whose page id is out of range
+// is never read.
 template <int HD, typename T>
+struct DenseKV {
+  const T* k;
+  const T* v;
+  __device__ int t_of(const Dims& D, size_t row) const { return D.qoff + (int)(row % D.tq); }
+  // element offset of block j of (b, kv head g) in k and v; -1: not readable
+  __device__ long long block(const Dims& D, int b, int g, int j) const {
+    return (long long)((((size_t)b * D.hkv + g) * D.tk + (size_t)j * kBlock) * HD);
+  }
+};
+
+template <int HD, typename T>
+struct PagedKV {
+  const T* k;
+  const T* v;
+  const int* table;
+  const int* lens;
+  int pages;
+  __device__ int t_of(const Dims& D, size_t row) const {
+    const int len = lens[row / D.hq];
+    return (len >= 1 && len <= D.nb * kBlock) ? len - 1 : -1;
+  }
+  __device__ long long block(const Dims& D, int b, int g, int j) const {
+    const int pg = table[(size_t)b * D.nb + j];
+    if (pg < 0 || pg >= pages) return -1;
+    return (long long)(((size_t)pg * D.hkv + g) * kBlock * HD);
+  }
+};
+
+template <int HD, typename T, typename Src>
 __global__ __launch_bounds__(64) void sparse_pair_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int* __restrict__ idx, const float* __restrict__ bias, float* __restrict__ plse,
-    T* __restrict__ po, Dims D, int K) {
+    const T* __restrict__ q, Src S, const int* __restrict__ idx, const float* __restrict__ bias,
+    float* __restrict__ plse, T* __restrict__ po, Dims D, int K) {
   __shared__ float qsh[HD];
   __shared__ float ps[64];
   const int lane = threadIdx.x;
@@ -47,10 +81,14 @@ __global__ __launch_bounds__(64) void sparse_pair_kernel(
   if (pair >= nrows * (K + 1)) return;
   const size_t row = pair / (K + 1);
   const int slot = (int)(pair % (K + 1));
-  const int i = (int)(row % D.tq);
   const int h = (int)((row / D.tq) % D.hq);
   const int b = (int)(row / ((size_t)D.tq * D.hq));
-  const int t = D.qoff + i, c = t / kBlock;
+  const int t = S.t_of(D, row);
+  if (t < 0) {
+    if (lane == 0) plse[pair] = -INFINITY;
+    return;
+  }
+  const int c = t / kBlock;
   const int g = h / D.hpg;
   int j;
   float add;
@@ -65,11 +103,15 @@ __global__ __launch_bounds__(64) void sparse_pair_kernel(
     j = c;
     add = 0.f;
   }
+  const long long boff = S.block(D, b, g, j);
+  if (boff < 0) {
+    if (lane == 0) plse[pair] = -INFINITY;
+    return;
+  }
   for (int e = lane; e < HD; e += 64) qsh[e] = to_f32(q[row * HD + e]);
   __syncthreads();
-  const size_t kvbase = ((size_t)b * D.hkv + g) * D.tk;
   const int key = j * kBlock + lane;
-  const T* kr = k + (kvbase + key) * HD;
+  const T* kr = S.k + boff + (size_t)lane * HD;
   float s = 0.f;
 #pragma unroll 16
   for (int e = 0; e < HD; ++e) s = fmaf(qsh[e], to_f32(kr[e]), s);
@@ -84,7 +126,7 @@ __global__ __launch_bounds__(64) void sparse_pair_kernel(
   float acc[DPL];
 #pragma unroll
   for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
-  const T* vb = v + (kvbase + (size_t)j * kBlock) * HD;
+  const T* vb = S.v + boff;
 #pragma unroll 8
   for (int u = 0; u < kBlock; ++u) {
     const float pu = ps[u];
@@ -117,6 +159,11 @@ __global__ __launch_bounds__(256) void sparse_combine_kernel(const float* __rest
   float s = 0.f;
   for (int x = lane; x < np; x += 64) s += exp2f((pl[x] - m) * kLog2e);
   s = wave_sum(s);
+  if (m == -INFINITY) {  // no readable key (paged row out of range): zeros, lse -inf
+    for (int x = lane; x < HD; x += 64) o[row * HD + x] = from_f32<T>(0.f);
+    if (lse && lane == 0) lse[row] = -INFINITY;
+    return;
+  }
   const float L = m + logf(s);
   constexpr int DPL = HD / 64;
   float acc[DPL];
@@ -606,8 +653,9 @@ static hipError_t launch_sparse_t(const void* q, const void* k, const void* v, c
   T* po = (T*)(ws + align256s(pairs * sizeof(float)));
   const unsigned gx = pairs < 65536 ? (unsigned)pairs : 65536u;
   const unsigned gy = (unsigned)((pairs + gx - 1) / gx);
-  hipLaunchKernelGGL((sparse_pair_kernel<HD, T>), dim3(gx, gy), dim3(64), 0, st, (const T*)q,
-                     (const T*)k, (const T*)v, idx, bias, plse, po, D, K);
+  hipLaunchKernelGGL((sparse_pair_kernel<HD, T, DenseKV<HD, T>>), dim3(gx, gy), dim3(64), 0, st,
+                     (const T*)q, DenseKV<HD, T>{(const T*)k, (const T*)v}, idx, bias, plse, po,
+                     D, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   E.record(0, st);
@@ -631,6 +679,52 @@ hipError_t launch_sparse(const void* q, const void* k, const void* v, const int*
   if (D.d == 64)
     return bf16_io ? launch_sparse_t<64, bf16>(q, k, v, idx, bias, o, lse, ws, K, D, E, st)
                    : launch_sparse_t<64, float>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
+  return hipErrorInvalidValue;
+}
+
+// Paged decode: one row per (sequence, query head), the pair path over the
+// page pools.  Workspace as for the pair path with tq = 1.
+template <int HD, typename T>
+static hipError_t launch_paged_t(const void* q, const void* k_pool, const void* v_pool,
+                                 const int* table, const int* lens, int pages, const int* idx,
+                                 const float* bias, void* o, float* lse, char* ws, int K,
+                                 const Dims& D, hipStream_t st) {
+  const size_t rows = (size_t)D.batch * D.hq;
+  const size_t pairs = rows * (K + 1);
+  float* plse = (float*)ws;
+  T* po = (T*)(ws + align256s(pairs * sizeof(float)));
+  const unsigned gx = pairs < 65536 ? (unsigned)pairs : 65536u;
+  const unsigned gy = (unsigned)((pairs + gx - 1) / gx);
+  hipLaunchKernelGGL((sparse_pair_kernel<HD, T, PagedKV<HD, T>>), dim3(gx, gy), dim3(64), 0, st,
+                     (const T*)q,
+                     PagedKV<HD, T>{(const T*)k_pool, (const T*)v_pool, table, lens, pages}, idx,
+                     bias, plse, po, D, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((sparse_combine_kernel<HD, T>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
+                     0, st, (const float*)plse, (const T*)po, (T*)o, lse, D, K);
+  return hipGetLastError();
+}
+
+size_t paged_workspace(const Dims& D, int K) {
+  const size_t pairs = (size_t)D.batch * D.hq * (K + 1);
+  return align256s(pairs * sizeof(float)) + align256s(pairs * D.d * 4);
+}
+
+hipError_t launch_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                               const int* table, const int* lens, int pages, const int* idx,
+                               const float* bias, void* o, float* lse, char* ws, int K,
+                               const Dims& D, bool bf16_io, hipStream_t st) {
+  if (D.d == 128)
+    return bf16_io ? launch_paged_t<128, bf16>(q, k_pool, v_pool, table, lens, pages, idx, bias,
+                                               o, lse, ws, K, D, st)
+                   : launch_paged_t<128, float>(q, k_pool, v_pool, table, lens, pages, idx,
+                                                bias, o, lse, ws, K, D, st);
+  if (D.d == 64)
+    return bf16_io ? launch_paged_t<64, bf16>(q, k_pool, v_pool, table, lens, pages, idx, bias,
+                                              o, lse, ws, K, D, st)
+                   : launch_paged_t<64, float>(q, k_pool, v_pool, table, lens, pages, idx, bias,
+                                               o, lse, ws, K, D, st);
   return hipErrorInvalidValue;
 }
 

@@ -23,9 +23,42 @@ __device__ __forceinline__ bool better(float za, int ja, float zb, int jb) {
   return za > zb || (za == zb && ja < jb);
 }
 
-template <int DS, typename ST>
-__global__ __launch_bounds__(256) void topk_wave_kernel(const ST* __restrict__ qs,
-                                                        const ST* __restrict__ ks, int K,
+// Where a row's selector keys live.  DenseSel: contiguous [B, Hks, NB, ds]
+// rows, row t has c(t) = t / 64 historical blocks.  PagedSel: one ks row per
+// page in a pool [pages, Hks, ds], a sequence's block j on page
+// table[b, j]; the decode row of sequence b sits at t = len[b] - 1.  A row
+// with a length out of range has no history; a block whose page id is out of
+// range is never read and scores -inf.
+template <typename ST>
+struct DenseSel {
+  const ST* ks;
+  __device__ int hist(const Dims& D, size_t row) const {
+    return (D.qoff + (int)(row % D.tq)) / kBlock;
+  }
+  __device__ const ST* ks_row(const Dims& D, int b, int h, int j) const {
+    return ks + (((size_t)b * D.hks + h / D.hps) * (size_t)D.nb + j) * D.ds;
+  }
+};
+
+template <typename ST>
+struct PagedSel {
+  const ST* ks;
+  const int* table;
+  const int* lens;
+  int pages;
+  __device__ int hist(const Dims& D, size_t row) const {
+    const int len = lens[row / D.hq];
+    return (len >= 1 && len <= D.nb * kBlock) ? (len - 1) / kBlock : 0;
+  }
+  __device__ const ST* ks_row(const Dims& D, int b, int h, int j) const {
+    const int pg = table[(size_t)b * D.nb + j];
+    if (pg < 0 || pg >= pages) return nullptr;
+    return ks + ((size_t)pg * D.hks + h / D.hps) * D.ds;
+  }
+};
+
+template <int DS, typename ST, typename Sel>
+__global__ __launch_bounds__(256) void topk_wave_kernel(const ST* __restrict__ qs, Sel S, int K,
                                                         int renorm, int* __restrict__ idx,
                                                         float* __restrict__ bias, Dims D,
                                                         int wpg) {
@@ -39,17 +72,16 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const ST* __restrict__ q
   int n = 0;
   float lam = -INFINITY;
   if (active) {
-    const int i = (int)(row % D.tq);
     const int h = (int)((row / D.tq) % D.hq);
     const int b = (int)(row / ((size_t)D.tq * D.hq));
-    const int c = (D.qoff + i) / kBlock;
+    const int c = S.hist(D, row);
     float qsv[DS];
 #pragma unroll
     for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
-    const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
     float m = -INFINITY;
     for (int j = lane; j < c; j += 64) {
-      const float z = D.sel_scale * sel_dot<DS>(qsv, ksb + (size_t)j * DS);
+      const ST* kr = S.ks_row(D, b, h, j);
+      const float z = kr ? D.sel_scale * sel_dot<DS>(qsv, kr) : -INFINITY;
       zc[j] = z;
       m = fmaxf(m, z);
     }
@@ -433,9 +465,45 @@ static hipError_t launch_topk_t(const void* qs, const void* ks, int K, int renor
   if (per * wpg > 65536) return hipErrorInvalidValue;
   const size_t nrows = (size_t)D.batch * D.hq * D.tq;
   const unsigned grid = (unsigned)((nrows + wpg - 1) / wpg);
-  hipLaunchKernelGGL((topk_wave_kernel<DS, ST>), dim3(grid), dim3(64 * wpg), per * wpg, st,
-                     (const ST*)qs, (const ST*)ks, K, renorm, idx, bias, D, wpg);
+  hipLaunchKernelGGL((topk_wave_kernel<DS, ST, DenseSel<ST>>), dim3(grid), dim3(64 * wpg),
+                     per * wpg, st, (const ST*)qs, DenseSel<ST>{(const ST*)ks}, K, renorm, idx,
+                     bias, D, wpg);
   return hipGetLastError();
+}
+
+template <int DS, typename ST>
+static hipError_t launch_paged_topk_t(const void* qs, const void* ks_pool, const int* table,
+                                      const int* lens, int pages, int K, int renorm, int* idx,
+                                      float* bias, const Dims& D, hipStream_t st) {
+  const size_t per = (size_t)(D.nb + K) * sizeof(float);
+  int wpg = 4;
+  while (wpg > 1 && per * wpg > 65536) wpg >>= 1;
+  if (per * wpg > 65536) return hipErrorInvalidValue;
+  const size_t nrows = (size_t)D.batch * D.hq;
+  const unsigned grid = (unsigned)((nrows + wpg - 1) / wpg);
+  hipLaunchKernelGGL((topk_wave_kernel<DS, ST, PagedSel<ST>>), dim3(grid), dim3(64 * wpg),
+                     per * wpg, st, (const ST*)qs,
+                     PagedSel<ST>{(const ST*)ks_pool, table, lens, pages}, K, renorm, idx, bias,
+                     D, wpg);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_topk(const void* qs, const void* ks_pool, const int* table,
+                             const int* lens, int pages, int K, int renorm, int* idx, float* bias,
+                             const Dims& D, bool sel_bf16, hipStream_t st) {
+#define SAS_PTOPK_CASE(DSV)                                                                  \
+  case DSV:                                                                                  \
+    return sel_bf16 ? launch_paged_topk_t<DSV, bf16>(qs, ks_pool, table, lens, pages, K,     \
+                                                     renorm, idx, bias, D, st)               \
+                    : launch_paged_topk_t<DSV, float>(qs, ks_pool, table, lens, pages, K,    \
+                                                      renorm, idx, bias, D, st);
+  switch (D.ds) {
+    SAS_PTOPK_CASE(16)
+    SAS_PTOPK_CASE(32)
+    SAS_PTOPK_CASE(64)
+  }
+#undef SAS_PTOPK_CASE
+  return hipErrorInvalidValue;
 }
 
 bool topk_supported(const Dims& D, int K) {

@@ -24,6 +24,7 @@ _STATUS = {0: "SAS_OK", 1: "SAS_ERR_NULL", 2: "SAS_ERR_SHAPE", 3: "SAS_ERR_DTYPE
            7: "SAS_ERR_HIP"}
 EXPORTS = ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_attn_bwd_ev",
            "sas_topk_blocks", "sas_topk_blocks_budget", "sas_sparse_fwd", "sas_sparse_fwd_ev",
+           "sas_paged_append", "sas_paged_topk", "sas_paged_decode",
            "sas_status_string", "sas_last_hip_error")
 
 
@@ -40,6 +41,18 @@ class Shape(ctypes.Structure):
         ("batch", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
         ("hks", ctypes.c_int32), ("tq", ctypes.c_int32), ("tk", ctypes.c_int32),
         ("d", ctypes.c_int32), ("ds", ctypes.c_int32), ("block", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float), ("sel_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32), ("sel_dtype", ctypes.c_int32),
+    ]
+
+
+class PagedShape(ctypes.Structure):
+    """Mirror of ``sas_paged_shape``."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+        ("hks", ctypes.c_int32), ("d", ctypes.c_int32), ("ds", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("pages", ctypes.c_int32),
         ("sm_scale", ctypes.c_float), ("sel_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32), ("sel_dtype", ctypes.c_int32),
     ]
@@ -62,9 +75,13 @@ def load():
         lib.sas_sparse_fwd.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P]
         lib.sas_attn_bwd_ev.argtypes = [P] * 17 + [SZ, P, I32, P]
         lib.sas_sparse_fwd_ev.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P, I32, P]
+        lib.sas_paged_append.argtypes = [P] * 10
+        lib.sas_paged_topk.argtypes = [P, I32, I32, P, P, P, P, P, P, P]
+        lib.sas_paged_decode.argtypes = [P, I32] + [P] * 10 + [SZ, P]
         for n in ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_topk_blocks",
                   "sas_topk_blocks_budget", "sas_sparse_fwd", "sas_attn_bwd_ev",
-                  "sas_sparse_fwd_ev"):
+                  "sas_sparse_fwd_ev", "sas_paged_append", "sas_paged_topk",
+                  "sas_paged_decode"):
             getattr(lib, n).restype = ctypes.c_int
         lib.sas_status_string.argtypes = [ctypes.c_int]
         lib.sas_status_string.restype = ctypes.c_char_p
@@ -236,4 +253,70 @@ def sparse_fwd(q, k, v, idx, bias, block=64, sm_scale=None, ws=None, with_lse=Tr
     _check("sas_sparse_fwd", load().sas_sparse_fwd_ev(
         ctypes.byref(sh), int(topk), _p(q), _p(k), _p(v), _p(idx), _p(bias), _p(o), _p(lse),
         _p(ws), ctypes.byref(n), ev, nev, _stream(q)))
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Paged decode cache: pools [pages, hkv, 64, d] (K, V) and [pages, hks, ds]
+# (selector keys), block_table [batch, max_blocks] int32, seq_len [batch] int32.
+
+def make_paged_shape(batch, hq, hkv, d, ds, max_blocks, pages, hks=0, block=64, sm_scale=0.0,
+                     sel_scale=0.0, dtype=SAS_BF16) -> PagedShape:
+    return PagedShape(batch, hq, hkv, hks, d, ds, block, max_blocks, pages,
+                      float(sm_scale or 0.0), float(sel_scale or 0.0), dtype, dtype)
+
+
+def paged_append(pos, block_table, k_new, v_new, k_pool, v_pool, ks_new=None, ks_pool=None):
+    """Write one token per sequence (k_new, v_new [batch, hkv, d]) at position pos[b];
+    with ks_new [batch, hks, ds], store the selector key of every block completed."""
+    pages, hkv, _, d = k_pool.shape
+    batch, max_blocks = block_table.shape
+    hks, ds = (ks_pool.shape[1], ks_pool.shape[2]) if ks_pool is not None else (hkv, 16)
+    sh = make_paged_shape(batch, hkv, hkv, d, ds, max_blocks, pages, hks, dtype=_dt(k_pool))
+    _check("sas_paged_append", load().sas_paged_append(
+        ctypes.byref(sh), _p(pos), _p(block_table), _p(k_new), _p(v_new), _p(ks_new),
+        _p(k_pool), _p(v_pool), _p(ks_pool), _stream(k_pool)))
+
+
+def paged_topk(qs, ks_pool, block_table, seq_len, topk, renorm=0, sel_scale=None):
+    """Top-K historical blocks of each sequence's query: qs [batch, hq, ds].
+    Returns (idx [batch, hq, topk] int32, bias float32)."""
+    batch, hq, ds = qs.shape
+    pages, hks, _ = ks_pool.shape
+    max_blocks = block_table.shape[1]
+    sh = make_paged_shape(batch, hq, hks, 64, ds, max_blocks, pages, hks, sel_scale=sel_scale,
+                          dtype=_dt(qs))
+    idx = torch.empty((batch, hq, topk), dtype=torch.int32, device=qs.device)
+    bias = torch.empty((batch, hq, topk), dtype=torch.float32, device=qs.device)
+    _check("sas_paged_topk", load().sas_paged_topk(
+        ctypes.byref(sh), int(topk), int(renorm), _p(seq_len), _p(block_table), _p(qs),
+        _p(ks_pool), _p(idx), _p(bias), _stream(qs)))
+    return idx, bias
+
+
+def paged_workspace_bytes(sh: PagedShape, topk: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("sas_paged_decode", load().sas_paged_decode(ctypes.byref(sh), int(topk), *([None] * 10),
+                                                       ctypes.byref(n), None))
+    return n.value
+
+
+def paged_decode(q, k_pool, v_pool, block_table, seq_len, idx, bias, sm_scale=None, ws=None,
+                 with_lse=True):
+    """Top-K sparse decode over the pools: q [batch, hq, d].  Returns (o, lse)."""
+    batch, hq, d = q.shape
+    pages, hkv, _, _ = k_pool.shape
+    max_blocks = block_table.shape[1]
+    topk = idx.shape[-1]
+    sh = make_paged_shape(batch, hq, hkv, d, 16, max_blocks, pages, sm_scale=sm_scale,
+                          dtype=_dt(q))
+    o = torch.empty_like(q)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device) if with_lse else None
+    need = paged_workspace_bytes(sh, topk)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(ws.numel())
+    _check("sas_paged_decode", load().sas_paged_decode(
+        ctypes.byref(sh), int(topk), _p(seq_len), _p(block_table), _p(q), _p(k_pool), _p(v_pool),
+        _p(idx), _p(bias), _p(o), _p(lse), _p(ws), ctypes.byref(n), _stream(q)))
     return o, lse

@@ -127,3 +127,97 @@ def draw_all(w: Workload, names=("q", "k", "v", "qs", "ks", "dout"), seed_base=N
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a stored tensor for the oracle."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# Serving-shaped decode over a block-paged cache.  Sequence lengths are drawn
+# log-uniformly between min_len and max_len (a mix of short and long
+# contexts, as a decode batch of a serving engine holds), every sequence's
+# blocks go to pages in a seeded random order, and the pools hold exactly
+# the pages in use plus `spare` unused ones.  Extra tensor ids: lengths = 10,
+# page order = 11; q, qs as above ([batch, hq, d] / [batch, hq, ds]), the K,
+# V and ks pools with the ids of k, v and ks.
+
+@dataclass(frozen=True)
+class PagedWorkload:
+    name: str
+    wid: int
+    batch: int
+    hq: int
+    hkv: int
+    d: int
+    ds: int
+    min_len: int
+    max_len: int
+    topk: int
+    dtype: str = "bf16"
+    hks: int = 0
+    spare: int = 3
+    block: int = 64
+    scales: dict = field(default_factory=lambda: dict(_HALF))
+
+    @property
+    def kheads(self) -> int:
+        return self.hks if self.hks else self.hkv
+
+    @property
+    def max_blocks(self) -> int:
+        return (self.max_len + self.block - 1) // self.block
+
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def with_(self, **kw) -> "PagedWorkload":
+        return replace(self, **kw)
+
+
+PAGED_WORKLOADS = {
+    "decode_paged_mix": PagedWorkload("decode_paged_mix", 7, 32, 32, 8, 128, 32, 64, 65536, 8),
+}
+
+
+def _normals(seed: int, shape, scale: float, dtype: str) -> torch.Tensor:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = math.prod(shape)
+    out = torch.empty(n, dtype=torch.float32 if dtype == "f32" else torch.bfloat16)
+    chunk = 1 << 26
+    for s in range(0, n, chunk):
+        m = min(chunk, n - s)
+        a = rng.standard_normal(m, dtype=np.float32)
+        if scale != 1.0:
+            a *= np.float32(scale)
+        out[s:s + m] = _round(a, dtype)
+    return out.view(shape)
+
+
+def draw_paged(pw: PagedWorkload, lens=None) -> dict:
+    """CPU tensors of a paged decode batch: seq_len [batch] int32, block_table
+    [batch, max_blocks] int32 (-1 past a sequence's last block), k_pool,
+    v_pool [pages, hkv, 64, d], ks_pool [pages, hks, ds], q [batch, hq, d],
+    qs [batch, hq, ds].  `lens` overrides the drawn lengths."""
+    base = 1000 * pw.wid
+    if lens is None:
+        rng = np.random.Generator(np.random.PCG64(base + 10))
+        u = rng.random(pw.batch)
+        lo, hi = math.log(pw.min_len), math.log(pw.max_len)
+        lens = np.minimum(pw.max_len, np.floor(np.exp(lo + u * (hi - lo)))).astype(np.int64)
+        lens = np.maximum(lens, pw.min_len)
+    lens = np.asarray(lens, dtype=np.int64)
+    nblk = (lens + pw.block - 1) // pw.block
+    pages = int(nblk.sum()) + pw.spare
+    order = np.random.Generator(np.random.PCG64(base + 11)).permutation(pages)
+    table = np.full((pw.batch, pw.max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(pw.batch):
+        table[b, :nblk[b]] = order[off:off + nblk[b]]
+        off += int(nblk[b])
+    sc = pw.scales
+    return {
+        "seq_len": torch.from_numpy(lens.astype(np.int32)),
+        "block_table": torch.from_numpy(table),
+        "k_pool": _normals(base + 1, (pages, pw.hkv, pw.block, pw.d), sc.get("k", 1.0), pw.dtype),
+        "v_pool": _normals(base + 2, (pages, pw.hkv, pw.block, pw.d), sc.get("v", 1.0), pw.dtype),
+        "ks_pool": _normals(base + 4, (pages, pw.kheads, pw.ds), sc.get("ks", 1.0), pw.dtype),
+        "q": _normals(base + 0, (pw.batch, pw.hq, pw.d), sc.get("q", 1.0), pw.dtype),
+        "qs": _normals(base + 3, (pw.batch, pw.hq, pw.ds), sc.get("qs", 1.0), pw.dtype),
+    }

@@ -166,6 +166,70 @@ sas_status sas_sparse_fwd_ev(const sas_shape* shape, int32_t topk, const void* q
                              float* lse, void* ws, size_t* ws_bytes, void* const* events,
                              int32_t n_events, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Decode over a paged cache (serving).  A page holds one 64-key block of one
+ * sequence for every kv head; sequences have their own lengths and a block
+ * table maps their blocks to pages, so caches grow a block at a time without
+ * moving data.  Layouts (device buffers, caller-owned):
+ *   k_pool, v_pool [pages, hkv, 64, d]   (dtype; one head's block = 64 x d)
+ *   ks_pool        [pages, hks, ds]      (sel_dtype; the selector key of the
+ *                                         block stored on the page)
+ *   block_table    [batch, max_blocks]   int32 page ids
+ *   seq_len        [batch]               int32 cached tokens per sequence,
+ *                                         the current query's token included
+ *   q [batch, hq, d], qs [batch, hq, ds], o [batch, hq, d], lse [batch, hq],
+ *   idx, bias [batch, hq, topk]
+ * Sequence b's query sits at t = seq_len[b] - 1 (block c(t) = t / 64) and
+ * attends its current block (causal, bias 0) plus the selected historical
+ * blocks, exactly as sas_sparse_fwd at tq == 1 with the sequence's blocks
+ * laid out contiguously.  Device-side contents are not checked on the host:
+ * a sequence with seq_len outside 1 .. max_blocks * 64 has no keys (o = 0,
+ * lse = -inf, no blocks selected); a block whose page id is outside
+ * 0 .. pages-1 is never read (it scores -inf in the selection and is skipped
+ * in the attention).  Supported: block == 64, d in {64, 128},
+ * ds in {16, 32, 64}, hq % hkv == 0, hq % hks == 0, dtype == sel_dtype.
+ * Source: the method's inference mode (both abstracts: a small set of
+ * context units per query under a fixed budget) applied to the usual
+ * block-paged serving cache; the pages leave the cache layout open. */
+typedef struct {
+  int32_t batch, hq, hkv, hks; /* hks <= 0 means hks = hkv                 */
+  int32_t d, ds, block;        /* block must be 64 (the page size)          */
+  int32_t max_blocks;          /* columns of block_table                    */
+  int32_t pages;               /* pages in the pools                        */
+  float sm_scale;              /* <= 0 means 1/sqrt(d)                      */
+  float sel_scale;             /* <= 0 means 1/sqrt(ds)                     */
+  int32_t dtype, sel_dtype;    /* sas_dtype                                 */
+} sas_paged_shape;
+
+/* Appends one token per sequence: the rows k_new, v_new [batch, hkv, d] go to
+ * position pos[b] of sequence b (page block_table[b, pos[b] / 64], row
+ * pos[b] % 64).  When that token completes its block (pos[b] % 64 == 63) and
+ * ks_new [batch, hks, ds] is not NULL, ks_new[b] is stored as the block's
+ * selector key on the same page: the selector scores a block once it is
+ * complete, and only complete blocks are ever historical.  ks_pool is
+ * required when ks_new is given.  Sequences with pos outside
+ * 0 .. max_blocks*64-1 or an out-of-range page are skipped.  Two sequences
+ * must not write the same page row in one call. */
+sas_status sas_paged_append(const sas_paged_shape* shape, const int32_t* pos,
+                            const int32_t* block_table, const void* k_new, const void* v_new,
+                            const void* ks_new, void* k_pool, void* v_pool, void* ks_pool,
+                            void* stream);
+
+/* Hard Top-K of the historical blocks of each sequence's query (semantics,
+ * order, padding and renorm as sas_topk_blocks).  Needs
+ * 4 (max_blocks + topk) bytes of LDS per row, at most 64 KiB
+ * (SAS_ERR_UNSUPPORTED beyond). */
+sas_status sas_paged_topk(const sas_paged_shape* shape, int32_t topk, int32_t renorm,
+                          const int32_t* seq_len, const int32_t* block_table, const void* qs,
+                          const void* ks_pool, int32_t* idx, float* bias, void* stream);
+
+/* Top-K sparse decode over the paged pools (semantics of sas_sparse_fwd at
+ * tq == 1 per sequence).  lse may be NULL.  Workspace by size query. */
+sas_status sas_paged_decode(const sas_paged_shape* shape, int32_t topk, const int32_t* seq_len,
+                            const int32_t* block_table, const void* q, const void* k_pool,
+                            const void* v_pool, const int32_t* idx, const float* bias, void* o,
+                            float* lse, void* ws, size_t* ws_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* sas_status_string(sas_status status);
 

@@ -179,3 +179,58 @@ def test_sparse_workspace_query_and_checks(lib):
                               ctypes.byref(n), STREAM) == 2
     assert lib.sas_sparse_fwd(ctypes.byref(sh), 4, A, A, A, None, A, A, None, A,
                               ctypes.byref(n), STREAM) == 1
+
+
+def pshape(**kw):
+    a = dict(batch=2, hq=4, hkv=2, d=128, ds=32, max_blocks=8, pages=20)
+    a.update(kw)
+    return ops.make_paged_shape(a["batch"], a["hq"], a["hkv"], a["d"], a["ds"], a["max_blocks"],
+                                a["pages"], hks=a.get("hks", 0), block=a.get("block", 64))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block=32), 5), (dict(d=96), 5), (dict(ds=48), 5), (dict(hq=3), 2),
+    (dict(max_blocks=0), 2), (dict(pages=0), 2), (dict(batch=-1), 2), (dict(hks=3), 2),
+])
+def test_paged_shape_checks(lib, kw, code):
+    sh = pshape(**kw)
+    n = ctypes.c_size_t(0)
+    assert lib.sas_paged_decode(ctypes.byref(sh), 4, *([None] * 10), ctypes.byref(n),
+                                STREAM) == code
+    assert lib.sas_paged_topk(ctypes.byref(sh), 4, 0, A, A, A, A, A, A, STREAM) == code
+    assert lib.sas_paged_append(ctypes.byref(sh), A, A, A, A, None, A, A, None, STREAM) == code
+
+
+def test_paged_checks(lib):
+    sh = pshape()
+    n = ctypes.c_size_t(0)
+    assert lib.sas_paged_decode(ctypes.byref(sh), 4, *([None] * 10), ctypes.byref(n),
+                                STREAM) == 0
+    assert n.value >= 2 * 4 * 5 * 128 * 2
+    small = ctypes.c_size_t(n.value - 1)
+    args = [A] * 8 + [None, A]  # lse NULL is allowed
+    assert lib.sas_paged_decode(ctypes.byref(sh), 4, *args, ctypes.byref(small), STREAM) == 6
+    assert lib.sas_paged_decode(ctypes.byref(sh), 0, *args, ctypes.byref(n), STREAM) == 2
+    bad = list(args)
+    bad[2] = None  # q
+    assert lib.sas_paged_decode(ctypes.byref(sh), 4, *bad, ctypes.byref(n), STREAM) == 1
+    bad[2] = MIS
+    assert lib.sas_paged_decode(ctypes.byref(sh), 4, *bad, ctypes.byref(n), STREAM) == 4
+    assert lib.sas_paged_decode(ctypes.byref(sh), 4, *args, None, STREAM) == 1
+    # top-K: budget, renorm, pointers, LDS limit
+    assert lib.sas_paged_topk(ctypes.byref(sh), 0, 0, A, A, A, A, A, A, STREAM) == 2
+    assert lib.sas_paged_topk(ctypes.byref(sh), 4, 2, A, A, A, A, A, A, STREAM) == 2
+    assert lib.sas_paged_topk(ctypes.byref(sh), 4, 0, A, None, A, A, A, A, STREAM) == 1
+    big = pshape(max_blocks=20000)
+    assert lib.sas_paged_topk(ctypes.byref(big), 4, 0, A, A, A, A, A, A, STREAM) == 5
+    # append: ks_new without ks_pool, misaligned pool
+    assert lib.sas_paged_append(ctypes.byref(sh), A, A, A, A, A, A, A, None, STREAM) == 1
+    assert lib.sas_paged_append(ctypes.byref(sh), A, A, A, A, None, MIS, A, None, STREAM) == 4
+    # dtype mismatch
+    sh2 = pshape()
+    sh2.sel_dtype = ops.SAS_F32
+    assert lib.sas_paged_topk(ctypes.byref(sh2), 4, 0, A, A, A, A, A, A, STREAM) == 3
+    # empty batch: nothing launched
+    e = pshape(batch=0)
+    assert lib.sas_paged_append(ctypes.byref(e), A, A, A, A, None, A, A, None, STREAM) == 0
+    assert lib.sas_paged_topk(ctypes.byref(e), 4, 0, A, A, A, A, A, A, STREAM) == 0
