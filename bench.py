@@ -9,6 +9,8 @@ One step is one pass of the whole hot path on resident synthetic inputs:
   decode_64k_top8    top-K selection -> sparse decode, 16 sequences x 64k keys
   prefill_32k_top25pct  budgeted top-K selection (a quarter of each query's
                      history, at most 128 blocks) -> top-K sparse forward
+  decode_paged_mix   decode over a block-paged cache: 32 sequences of mixed
+                     lengths (64 .. 65536 tokens), top-K selection -> decode
 The headline value is the training fwd+bwd rate at 32k in TFLOP/s counting
 attended (row, key) pairs only (forward 4*d flop per pair, backward 10*d).
 Times come from HIP events recorded on the stream the kernels run on.
@@ -166,6 +168,8 @@ def main():
     pf = {n: t.to(dev) for n, t in synth.draw_all(wp, ("q", "k", "v", "qs", "ks")).items()}
     dc = {n: t.to(dev) for n, t in synth.draw_all(wd, ("q", "k", "v", "qs", "ks")).items()}
     pq = {n: t.to(dev) for n, t in synth.draw_all(wq, ("q", "k", "v", "qs", "ks")).items()}
+    wg = synth.PAGED_WORKLOADS["decode_paged_mix"]
+    pg = {n: t.to(dev) for n, t in synth.draw_paged(wg).items()}
     torch.cuda.synchronize()
     log("inputs resident in HBM (%.1f s)" % (time.time() - t0))
 
@@ -177,10 +181,13 @@ def main():
     ws_d = torch.empty(ops.sparse_workspace_bytes(sh_d, wd.topk), dtype=torch.uint8, device=dev)
     sh_q = ops.make_shape(1, wq.hq, wq.hkv, wq.tq, wq.tk, wq.d, wq.ds, 64, wq.hkv)
     ws_q = torch.empty(ops.sparse_workspace_bytes(sh_q, wq.topk), dtype=torch.uint8, device=dev)
+    sh_g = ops.make_paged_shape(wg.batch, wg.hq, wg.hkv, wg.d, wg.ds, wg.max_blocks,
+                                pg["k_pool"].shape[0])
+    ws_g = torch.empty(ops.paged_workspace_bytes(sh_g, wg.topk), dtype=torch.uint8, device=dev)
 
     names = ["start", "gate", "fwd", "bwd_dq", "bwd_dkdv", "bwd_dks", "bwd", "pf_topk",
              "pf_partial", "pf_sparse", "dc_topk", "dc_partial", "dc_sparse", "pq_topk",
-             "pq_partial", "pq_sparse"]
+             "pq_partial", "pq_sparse", "pg_topk", "pg_decode"]
 
     def step(ev):
         E = {n: ev[n] for n in names}
@@ -206,6 +213,12 @@ def main():
         E["pq_topk"].record()
         ops.sparse_fwd(pq["q"], pq["k"], pq["v"], idx, bias, ws=ws_q, events=[E["pq_partial"]])
         E["pq_sparse"].record()
+        idx, bias = ops.paged_topk(pg["qs"], pg["ks_pool"], pg["block_table"], pg["seq_len"],
+                                   wg.topk)
+        E["pg_topk"].record()
+        ops.paged_decode(pg["q"], pg["k_pool"], pg["v_pool"], pg["block_table"], pg["seq_len"],
+                         idx, bias, ws=ws_g)
+        E["pg_decode"].record()
 
     def new_events():
         return {n: torch.cuda.Event(enable_timing=True) for n in names}
@@ -238,8 +251,10 @@ def main():
         "quarter_topk": dur("dc_sparse", "pq_topk"),
         "quarter_partial": dur("pq_topk", "pq_partial"),
         "quarter_sparse": dur("pq_topk", "pq_sparse"),
+        "paged_topk": dur("pq_sparse", "pg_topk"),
+        "paged_decode": dur("pg_topk", "pg_decode"),
     }
-    step_ms = dur("start", "pq_sparse")
+    step_ms = dur("start", "pg_decode")
 
     pairs_t = wt.batch * wt.hq * causal_pairs(wt.tq, wt.tk)
     fl_fwd = 4.0 * wt.d * pairs_t
@@ -255,6 +270,10 @@ def main():
     dec_blocks = wd.batch * wd.hq * (min(wd.topk, (wd.tk - 1) // 64) + 1)
     dec_bytes = dec_blocks * 2 * 64 * wd.d * 2  # K and V of every attended block, bf16
     dec_gbps = dec_bytes / (part["decode_sparse"] * 1e-3) / 1e9
+    lens_g = pg["seq_len"].cpu().tolist()
+    pg_blocks = wg.hq * sum(min(wg.topk, (n - 1) // 64) + 1 for n in lens_g)
+    pg_bytes = pg_blocks * 2 * 64 * wg.d * 2  # K and V of every attended block, bf16
+    pg_gbps = pg_bytes / (part["paged_decode"] * 1e-3) / 1e9
 
     # dominant kernel: the key-stationary backward kernel (dK, dV): S, dP, dV
     # and dK over every attended pair = 8*d flop per pair
@@ -293,7 +312,7 @@ def main():
         "config": {"workload": "train_32k", "batch": wt.batch, "hq": wt.hq, "hkv": wt.hkv,
                    "seq_len": wt.tq, "d": wt.d, "block": wt.block, "ds": wt.ds,
                    "also_in_step": ["prefill_32k_top16", "decode_64k_top8",
-                                    "prefill_32k_top25pct"]},
+                                    "prefill_32k_top25pct", "decode_paged_mix"]},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "train_ms": round(t_train, 3),
         "parts_ms": {k: round(v, 4) for k, v in part.items()},
@@ -312,6 +331,12 @@ def main():
                    "topk_ms": round(part["decode_topk"], 4), "kv_bytes": dec_bytes,
                    "GBps": round(dec_gbps, 1),
                    "frac_hbm": round(dec_gbps / PEAK_HBM_GBPS, 4)},
+        "paged_decode": {"workload": "decode_paged_mix", "sequences": wg.batch,
+                         "len_min": min(lens_g), "len_max": max(lens_g),
+                         "tokens": sum(lens_g), "ms": round(part["paged_decode"], 4),
+                         "topk_ms": round(part["paged_topk"], 4), "kv_bytes": pg_bytes,
+                         "GBps": round(pg_gbps, 1),
+                         "frac_hbm": round(pg_gbps / PEAK_HBM_GBPS, 4)},
         "roofline": roofline,
         "wall_s_timed": round(wall, 3),
     }
