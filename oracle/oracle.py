@@ -84,9 +84,12 @@ def _load():
         lib.oracle_topk_blocks.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
         lib.oracle_topk_budget.argtypes = [P, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, P,
                                            P, P, P, P]
+        lib.oracle_threshold_blocks.argtypes = [P, ctypes.c_float, ctypes.c_int32, P, P, P, P,
+                                                P, P]
         lib.oracle_sparse_fwd.argtypes = [P, ctypes.c_int32, P, P, P, P, P, I64, P, P, P]
         for f in (lib.oracle_gate_scores, lib.oracle_attn_fwd, lib.oracle_attn_bwd,
-                  lib.oracle_topk_blocks, lib.oracle_topk_budget, lib.oracle_sparse_fwd):
+                  lib.oracle_topk_blocks, lib.oracle_topk_budget, lib.oracle_threshold_blocks,
+                  lib.oracle_sparse_fwd):
             f.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -216,6 +219,21 @@ def topk_budget(shape: OracleShape, kmax: int, frac: float, qs=None, ks=None, z=
                                       int(renorm), _ptr(qs), _ptr(ks), _ptr(z), _ptr(idx),
                                       _ptr(bias)), "topk_budget")
     return idx, bias
+
+
+def threshold_blocks(shape: OracleShape, theta: float, qs=None, ks=None, z=None,
+                     renorm: int = 0):
+    """Blocks whose normalised gate is >= theta, ascending.  Returns (count int32
+    [B,Hq,Tq], idx int32 [B,Hq,Tq,NB] padded -1, bias float64 padded -inf)."""
+    qs, ks, z = map(_f64, (qs, ks, z))
+    count = np.empty((shape.batch, shape.hq, shape.tq), dtype=np.int32)
+    idx = np.empty((shape.batch, shape.hq, shape.tq, shape.nb), dtype=np.int32)
+    bias = np.empty((shape.batch, shape.hq, shape.tq, shape.nb))
+    st = shape.c_struct()
+    _check(_load().oracle_threshold_blocks(ctypes.byref(st), ctypes.c_float(theta), int(renorm),
+                                           _ptr(qs), _ptr(ks), _ptr(z), _ptr(count), _ptr(idx),
+                                           _ptr(bias)), "threshold_blocks")
+    return count, idx, bias
 
 
 def sparse_fwd(shape: OracleShape, topk: int, q, k, v, idx, bias, rows=None):

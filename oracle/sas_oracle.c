@@ -541,3 +541,52 @@ int oracle_sparse_fwd(const oracle_shape* s, int32_t topk, const double* q, cons
   }
   return 0;
 }
+
+/* Dynamic-threshold selection [C] ("Implementation and Efficiency": attention
+ * is computed only for the blocks whose selector score clears a threshold
+ * that moves with the query).  Reading: the threshold applies to the
+ * normalised gate g_j = exp(z_j - lambda) of step 2; a historical block j < c
+ * is kept when g_j >= theta, i.e. z_j - lambda >= log(theta); theta <= 0
+ * keeps every historical block.  Kept blocks are listed in ascending block
+ * order: count[r] of them in idx[r, 0 .. count-1], the rest of the nb slots
+ * padded with -1 / -inf.  Bias as in Top-K: renorm = 0 gives z - lambda
+ * (= log g), renorm = 1 gives z - log sum_{kept} exp z. */
+int oracle_threshold_blocks(const oracle_shape* s, float theta, int32_t renorm, const double* qs,
+                            const double* ks, const double* zin, int32_t* count, int32_t* idx,
+                            double* bias) {
+  if (check_shape(s)) return -1;
+  const int64_t nb = nblocks(s);
+  const int64_t nrows = (int64_t)s->batch * s->hq * s->tq;
+  const double th = (double)theta;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t r = 0; r < nrows; ++r) {
+    rowinfo x = row_info(s, r);
+    const int64_t c = x.c;
+    double* z = (double*)malloc(sizeof(double) * (size_t)(c > 0 ? c : 1));
+    for (int64_t j = 0; j < c; ++j) z[j] = score(s, qs, ks, zin, &x, j);
+    const double lam = log_sum_exp(z, c);
+    int64_t n = 0;
+    double* kept = (double*)malloc(sizeof(double) * (size_t)(c > 0 ? c : 1));
+    for (int64_t j = 0; j < c; ++j) {
+      const int keep = th <= 0.0 ? 1 : (z[j] - lam >= log(th));
+      if (keep) {
+        idx[r * nb + n] = (int32_t)j;
+        kept[n] = z[j];
+        ++n;
+      }
+    }
+    const double norm = renorm ? log_sum_exp(kept, n) : lam;
+    for (int64_t a = 0; a < nb; ++a) {
+      if (a < n) {
+        bias[r * nb + a] = kept[a] - norm;
+      } else {
+        idx[r * nb + a] = -1;
+        bias[r * nb + a] = -INFINITY;
+      }
+    }
+    count[r] = (int32_t)n;
+    free(kept);
+    free(z);
+  }
+  return 0;
+}

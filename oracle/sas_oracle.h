@@ -81,6 +81,15 @@ int oracle_topk_budget(const oracle_shape* s, int32_t kmax, float frac, int32_t 
                        const double* qs, const double* ks, const double* zin, int32_t* idx,
                        double* bias);
 
+/* Dynamic-threshold selection: a historical block j < c is kept when its
+ * normalised gate exp(z_j - lambda) >= theta (theta <= 0 keeps all).
+ * count [batch,hq,tq]; idx [batch,hq,tq,nb] lists the kept blocks in
+ * ascending order (pad -1), bias the same slots (pad -inf); renorm as for
+ * Top-K. */
+int oracle_threshold_blocks(const oracle_shape* s, float theta, int32_t renorm, const double* qs,
+                            const double* ks, const double* zin, int32_t* count, int32_t* idx,
+                            double* bias);
+
 /* Sparse attention forward: each row attends its current block (causal,
  * bias 0) plus the blocks listed in idx with the given bias.
  * rows / o / lse as in oracle_attn_fwd. */

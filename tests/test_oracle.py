@@ -439,3 +439,105 @@ def test_sparse_rejects_bad_index():
     idx[0, 0, 12, :] = [1, 1]  # duplicate
     with pytest.raises(ValueError):
         oracle.sparse_fwd(S, 2, x["q"], x["k"], x["v"], idx, bias)
+
+
+# ------------------------------------------------------- dynamic threshold
+def _log_gates_bruteforce(S, x):
+    """log g [B,Hq,Tq,NB] from torch: scores by matmul, masked log_softmax over
+    the historical blocks of each query (-inf elsewhere)."""
+    z = bf.scores(T(x["qs"]), T(x["ks"]), S.hq, 1.0 / math.sqrt(S.ds))
+    t, _, ct, _ = bf.positions(S.tq, S.tk, S.block)
+    hist = torch.arange(S.nb)[None, :] < ct[:, None]
+    zm = torch.where(hist, z, torch.full_like(z, -math.inf))
+    ls = torch.log_softmax(zm, dim=-1)
+    return torch.where(hist, ls, torch.full_like(ls, -math.inf)).numpy(), ct.numpy()
+
+
+@pytest.mark.parametrize("theta", [0.02, 0.1, 0.3])
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_threshold_vs_bruteforce(theta, renorm):
+    S, x = make(hq=4, hkv=2, tq=90, tk=90, block=4)
+    cnt, idx, bias = oracle.threshold_blocks(S, theta, x["qs"], x["ks"], renorm=renorm)
+    lg, ct = _log_gates_bruteforce(S, x)
+    th = math.log(float(np.float32(theta)))
+    checked = 0
+    for h in range(S.hq):
+        for i in range(S.tq):
+            c = int(ct[i])
+            g = lg[0, h, i, :c]
+            if c and np.min(np.abs(g - th)) < 1e-9:
+                continue  # a gate on the threshold: either answer is right
+            checked += 1
+            want = np.nonzero(g >= th)[0]
+            n = len(want)
+            assert cnt[0, h, i] == n
+            np.testing.assert_array_equal(idx[0, h, i, :n], want)
+            assert np.all(idx[0, h, i, n:] == -1) and np.all(np.isneginf(bias[0, h, i, n:]))
+            ref = g[want] - (logsumexp(g[want]) if renorm else 0.0)
+            np.testing.assert_allclose(bias[0, h, i, :n], ref, rtol=1e-11, atol=1e-11)
+    assert checked > 0.95 * S.hq * S.tq
+
+
+def test_threshold_special_cases():
+    S, x = make(hq=2, hkv=1, tq=70, tk=70, block=4)
+    ct = (np.arange(S.tq)) // S.block
+    # theta <= 0 keeps every historical block, in order
+    cnt, idx, _ = oracle.threshold_blocks(S, 0.0, x["qs"], x["ks"])
+    for i in range(S.tq):
+        assert cnt[0, 0, i] == ct[i]
+        np.testing.assert_array_equal(idx[0, 0, i, :ct[i]], np.arange(ct[i]))
+    # a gate never exceeds 1, and equals 1 only with a single historical block
+    cnt, _, _ = oracle.threshold_blocks(S, 1.5, x["qs"], x["ks"])
+    assert not cnt.any()
+    cnt, _, _ = oracle.threshold_blocks(S, 1.0, x["qs"], x["ks"])
+    np.testing.assert_array_equal(cnt[0, 0], (ct == 1).astype(np.int32))
+    # ks = 0: every gate is 1/c, kept iff 1/c >= theta (0.13: c <= 7)
+    z0 = dict(x, ks=np.zeros_like(x["ks"]))
+    cnt, _, bias = oracle.threshold_blocks(S, 0.13, z0["qs"], z0["ks"])
+    np.testing.assert_array_equal(cnt[0, 0], np.where(ct <= 7, ct, 0))
+    for i in range(S.tq):
+        if 0 < ct[i] <= 7:
+            np.testing.assert_allclose(bias[0, 0, i, :ct[i]], -math.log(ct[i]), rtol=1e-13)
+
+
+def test_threshold_nested_and_topk_prefix():
+    S, x = make(hq=2, hkv=1, tq=120, tk=120, block=4, seed=3)
+    c1, i1, _ = oracle.threshold_blocks(S, 0.05, x["qs"], x["ks"])
+    c2, i2, _ = oracle.threshold_blocks(S, 0.12, x["qs"], x["ks"])
+    ik, _ = oracle.topk_blocks(S, S.nb, x["qs"], x["ks"])
+    for h in range(S.hq):
+        for i in range(S.tq):
+            s1 = set(i1[0, h, i, :c1[0, h, i]].tolist())
+            s2 = set(i2[0, h, i, :c2[0, h, i]].tolist())
+            assert s2 <= s1  # a higher threshold keeps a subset
+            # the kept set is the best-scored prefix of the Top-K order
+            n = int(c1[0, h, i])
+            assert s1 == set(ik[0, h, i, :n].tolist())
+
+
+def test_threshold_renorm_bias_sums_to_one():
+    S, x = make(hq=2, hkv=1, tq=80, tk=80, block=4, seed=5)
+    cnt, _, bias = oracle.threshold_blocks(S, 0.04, x["qs"], x["ks"], renorm=1)
+    for h in range(S.hq):
+        for i in range(S.tq):
+            n = int(cnt[0, h, i])
+            if n:
+                assert abs(logsumexp(bias[0, h, i, :n])) < 1e-12
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_sparse_threshold_vs_bruteforce(renorm):
+    S, x = make(hq=4, hkv=2, tq=45, tk=45, block=4)
+    cnt, idx, bias = oracle.threshold_blocks(S, 0.08, x["qs"], x["ks"], renorm=renorm)
+    o, l = oracle.sparse_fwd(S, S.nb, x["q"], x["k"], x["v"], idx, bias)
+    keep = torch.zeros(1, S.hq, S.tq, S.nb, dtype=torch.bool)
+    for h in range(S.hq):
+        for t in range(S.tq):
+            for j in idx[0, h, t]:
+                if j >= 0:
+                    keep[0, h, t, j] = True
+    z = bf.scores(T(x["qs"]), T(x["ks"]), S.hq, 1.0 / math.sqrt(S.ds))
+    bias_m = bf.bias_matrix(z, S.tq, S.tk, S.block, restrict=keep, renorm=bool(renorm))
+    ob, lb = bf.attention(T(x["q"]), T(x["k"]), T(x["v"]), bias_m, 1.0 / math.sqrt(S.d))
+    np.testing.assert_allclose(o, ob.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(l, lb.numpy(), rtol=1e-12)
