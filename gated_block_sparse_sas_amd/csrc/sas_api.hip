@@ -278,6 +278,87 @@ sas_status sas_sparse_fwd_ev(const sas_shape* shape, int32_t topk, const void* q
                          sas::StageEvents{events, n_events}, stream);
 }
 
+sas_status sas_threshold_count(const sas_shape* shape, float theta, const void* qs,
+                               const void* ks, int64_t* row_ptr, void* ws, size_t* ws_bytes,
+                               void* stream) {
+  sas::Dims D;
+  sas_status r = resolve(shape, &D);
+  if (r != SAS_OK) return r;
+  if (theta != theta) return SAS_ERR_SHAPE;
+  if (!ws_bytes) return SAS_ERR_NULL;
+  if (D.hq > 65535 || D.batch > 65535) return SAS_ERR_UNSUPPORTED;  // grid y / z
+  const size_t need = sas::threshold_workspace(D);
+  if (!ws) {
+    *ws_bytes = need;
+    return SAS_OK;
+  }
+  if ((r = check_ptrs({qs, ks, row_ptr, ws})) != SAS_OK) return r;
+  if (*ws_bytes < need) return SAS_ERR_WORKSPACE;
+  if (D.batch == 0) return SAS_OK;
+  return hip_status(sas::launch_threshold(qs, ks, theta, 0, 0, (long long*)row_ptr, nullptr,
+                                          nullptr, 0, (char*)ws, D, shape->sel_dtype == SAS_BF16,
+                                          (hipStream_t)stream));
+}
+
+sas_status sas_threshold_fill(const sas_shape* shape, float theta, int32_t renorm, const void* qs,
+                              const void* ks, const int64_t* row_ptr, int64_t nnz, int32_t* col,
+                              float* bias, void* stream) {
+  sas::Dims D;
+  sas_status r = resolve(shape, &D);
+  if (r != SAS_OK) return r;
+  if (theta != theta || nnz < 0 || (renorm != 0 && renorm != 1)) return SAS_ERR_SHAPE;
+  if (D.hq > 65535 || D.batch > 65535) return SAS_ERR_UNSUPPORTED;  // grid y / z
+  if ((r = check_ptrs({qs, ks, row_ptr})) != SAS_OK) return r;
+  if (nnz > 0 && (r = check_ptrs({col, bias})) != SAS_OK) return r;
+  if (D.batch == 0 || nnz == 0) return SAS_OK;
+  return hip_status(sas::launch_threshold(qs, ks, theta, renorm, 1, (long long*)row_ptr, col,
+                                          bias, nnz, nullptr, D, shape->sel_dtype == SAS_BF16,
+                                          (hipStream_t)stream));
+}
+
+static sas_status sparse_csr_impl(const sas_shape* shape, int64_t nnz, const int64_t* row_ptr,
+                                  const int32_t* col, const float* bias, const void* q,
+                                  const void* k, const void* v, void* o, float* lse, void* ws,
+                                  size_t* ws_bytes, const sas::StageEvents& E, void* stream) {
+  sas::Dims D;
+  sas_status r = resolve(shape, &D);
+  if (r != SAS_OK) return r;
+  if (nnz < 0) return SAS_ERR_SHAPE;
+  if (!ws_bytes) return SAS_ERR_NULL;
+  if (shape->dtype != SAS_BF16) return SAS_ERR_UNSUPPORTED;
+  if (!sas::sparse_csr_supported(D, nnz)) return SAS_ERR_UNSUPPORTED;
+  const size_t need = sas::sparse_csr_workspace(D, nnz);
+  if (!ws) {
+    *ws_bytes = need;
+    return SAS_OK;
+  }
+  if ((r = check_ptrs({row_ptr, q, k, v, o, ws})) != SAS_OK) return r;
+  if (nnz > 0 && (r = check_ptrs({col, bias})) != SAS_OK) return r;
+  if ((r = check_opt({lse})) != SAS_OK) return r;
+  if (*ws_bytes < need) return SAS_ERR_WORKSPACE;
+  if (D.batch == 0) return SAS_OK;
+  return hip_status(sas::launch_sparse_csr(q, k, v, (const long long*)row_ptr, col, bias, nnz, o,
+                                           lse, (char*)ws, D, E, (hipStream_t)stream));
+}
+
+sas_status sas_sparse_fwd_csr(const sas_shape* shape, int64_t nnz, const int64_t* row_ptr,
+                              const int32_t* col, const float* bias, const void* q, const void* k,
+                              const void* v, void* o, float* lse, void* ws, size_t* ws_bytes,
+                              void* stream) {
+  return sparse_csr_impl(shape, nnz, row_ptr, col, bias, q, k, v, o, lse, ws, ws_bytes,
+                         sas::StageEvents{nullptr, 0}, stream);
+}
+
+sas_status sas_sparse_fwd_csr_ev(const sas_shape* shape, int64_t nnz, const int64_t* row_ptr,
+                                 const int32_t* col, const float* bias, const void* q,
+                                 const void* k, const void* v, void* o, float* lse, void* ws,
+                                 size_t* ws_bytes, void* const* events, int32_t n_events,
+                                 void* stream) {
+  if (n_events < 0 || n_events > 1) return SAS_ERR_SHAPE;
+  return sparse_csr_impl(shape, nnz, row_ptr, col, bias, q, k, v, o, lse, ws, ws_bytes,
+                         sas::StageEvents{events, n_events}, stream);
+}
+
 sas_status sas_paged_append(const sas_paged_shape* shape, const int32_t* pos,
                             const int32_t* block_table, const void* k_new, const void* v_new,
                             const void* ks_new, void* k_pool, void* v_pool, void* ks_pool,

@@ -62,6 +62,18 @@ hipError_t launch_sparse(const void* q, const void* k, const void* v, const int*
                          int K, const Dims& D, bool bf16_io, const StageEvents& E,
                          hipStream_t st);
 
+// Dynamic-threshold selection (CSR) and the sparse forward over a CSR selection.
+size_t threshold_workspace(const Dims& D);
+hipError_t launch_threshold(const void* qs, const void* ks, float theta, int renorm, int fill,
+                            long long* row_ptr, int* col, float* bias, long long nnz, char* ws,
+                            const Dims& D, bool sel_bf16, hipStream_t st);
+bool sparse_csr_supported(const Dims& D, long long nnz);
+size_t sparse_csr_workspace(const Dims& D, long long nnz);
+hipError_t launch_sparse_csr(const void* q, const void* k, const void* v, const long long* row_ptr,
+                             const int* col, const float* bias, long long nnz, void* o,
+                             float* lse, char* ws, const Dims& D, const StageEvents& E,
+                             hipStream_t st);
+
 // Paged decode cache (serving): append, selection and decode over page pools.
 // Dims: tq = 1, nb = max_blocks, tk = 64 * max_blocks.
 hipError_t launch_paged_append(const int* pos, const int* table, const void* k_new,

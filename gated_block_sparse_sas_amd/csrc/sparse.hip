@@ -193,26 +193,86 @@ __global__ void sp_zero_kernel(int* __restrict__ p, size_t n) {
     p[i] = 0;
 }
 
-// Inversion of the (row, slot) pairs into per-(batch, kv head, block) lists.
-// A workgroup takes kPairsWG consecutive pairs of one (batch, query head), so
-// every pair it sees falls in the nb buckets of one (batch, kv head): it
-// histograms them in LDS and touches each global counter once.
-constexpr int kPairsWG = 4096;
+// Where the (row, block) pairs of a sparse forward come from.  FixedSel: idx
+// and bias [rows, K], pair p = row * K + slot.  CsrSel: a row's pairs are
+// p = row_ptr[row] .. row_ptr[row + 1] - 1 of col / bias [nnz]; rowof[p] is
+// the row whose segment holds p (-1 if none), built from row_ptr, so even an
+// inconsistent row_ptr never sends a pair outside [0, nnz) or to two rows.
+struct FixedSel {
+  const int* idx;
+  const float* bias;
+  int K;
+  __device__ size_t lo(const Dims& D, int bh) const { return (size_t)bh * D.tq * K; }
+  __device__ size_t hi(const Dims& D, int bh) const { return (size_t)(bh + 1) * D.tq * K; }
+  __device__ int j_of(size_t p) const { return idx[p]; }
+  __device__ long long row_of(size_t p) const { return (long long)(p / K); }
+  __device__ float bias_of(size_t p) const { return bias[p]; }
+  __device__ size_t seg_lo(size_t row) const { return row * K; }
+  __device__ size_t seg_hi(size_t row) const { return (row + 1) * K; }
+};
 
-__global__ __launch_bounds__(256) void sp_count_kernel(const int* __restrict__ idx,
-                                                       int* __restrict__ count, Dims D, int K) {
+struct CsrSel {
+  const long long* row_ptr;
+  const int* col;
+  const float* bias;
+  const int* rowof;
+  long long nnz;
+  __device__ size_t cl(long long v) const { return (size_t)min(max(v, 0LL), nnz); }
+  __device__ size_t lo(const Dims& D, int bh) const { return cl(row_ptr[(size_t)bh * D.tq]); }
+  __device__ size_t hi(const Dims& D, int bh) const {
+    return max(lo(D, bh), cl(row_ptr[(size_t)(bh + 1) * D.tq]));
+  }
+  __device__ int j_of(size_t p) const { return col[p]; }
+  __device__ long long row_of(size_t p) const { return rowof[p]; }
+  __device__ float bias_of(size_t p) const { return bias[p]; }
+  __device__ size_t seg_lo(size_t row) const { return cl(row_ptr[row]); }
+  __device__ size_t seg_hi(size_t row) const { return max(seg_lo(row), cl(row_ptr[row + 1])); }
+};
+
+// rowof for CsrSel: -1 everywhere, then each row stamps its segment.
+__global__ __launch_bounds__(256) void sp_fill_value_kernel(int* __restrict__ p, size_t n,
+                                                            int value) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+__global__ __launch_bounds__(256) void sp_rowof_kernel(CsrSel S, int* __restrict__ rowof,
+                                                       size_t nrows) {
+  const size_t r = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= nrows) return;
+  const size_t a = S.seg_lo(r), e = S.seg_hi(r);
+  for (size_t p = a; p < e; ++p) rowof[p] = (int)r;
+}
+
+// A pair is listed when its row lies in the (batch, query head) being
+// scanned and its block is historical for that row.
+template <typename Src>
+__device__ __forceinline__ int listed_block(const Src& S, const Dims& D, int bh, size_t p) {
+  const long long row = S.row_of(p);
+  if (row < 0 || row / D.tq != bh) return -1;
+  const int j = S.j_of(p);
+  const int c = (D.qoff + (int)(row % D.tq)) / kBlock;
+  return (j >= 0 && j < c) ? j : -1;
+}
+
+// Inversion of the (row, slot) pairs into per-(batch, kv head, block) lists.
+// The workgroups of one (batch, query head) share its pairs (grid-strided),
+// so every pair a workgroup sees falls in the nb buckets of one (batch, kv
+// head): it histograms them in LDS and touches each global counter once.
+constexpr int kInvWGs = 64;  // workgroups per (batch, query head)
+
+template <typename Src>
+__global__ __launch_bounds__(256) void sp_count_kernel(Src S, int* __restrict__ count, Dims D) {
   extern __shared__ int hist[];  // nb counters
   const int bh = blockIdx.y, b = bh / D.hq, h = bh % D.hq;
-  const size_t per_bh = (size_t)D.tq * K;
-  const size_t p0 = (size_t)blockIdx.x * kPairsWG;
-  const size_t p1 = min(per_bh, p0 + kPairsWG);
+  const size_t p1 = S.hi(D, bh);
   for (int x = threadIdx.x; x < D.nb; x += 256) hist[x] = 0;
   __syncthreads();
-  const int* ib = idx + (size_t)bh * per_bh;
-  for (size_t pp = p0 + threadIdx.x; pp < p1; pp += 256) {
-    const int j = ib[pp];
-    const int c = (D.qoff + (int)(pp / K)) / kBlock;
-    if (j >= 0 && j < c) atomicAdd(&hist[j], 1);
+  for (size_t p = S.lo(D, bh) + (size_t)blockIdx.x * 256 + threadIdx.x; p < p1;
+       p += (size_t)gridDim.x * 256) {
+    const int j = listed_block(S, D, bh, p);
+    if (j >= 0) atomicAdd(&hist[j], 1);
   }
   __syncthreads();
   int* cb = count + (size_t)(b * D.hkv + h / D.hpg) * D.nb;
@@ -258,25 +318,23 @@ __global__ __launch_bounds__(1024) void sp_scan_kernel(const int* __restrict__ c
 
 // Same decomposition as sp_count_kernel: local histogram, one global
 // reservation per (workgroup, block), then each pair takes a local rank.
-__global__ __launch_bounds__(256) void sp_fill_kernel(const int* __restrict__ idx,
-                                                      const int* __restrict__ start,
+// list[x] = pair, inv[pair] = x.
+template <typename Src>
+__global__ __launch_bounds__(256) void sp_fill_kernel(Src S, const int* __restrict__ start,
                                                       int* __restrict__ cursor,
                                                       int* __restrict__ list,
-                                                      int* __restrict__ inv, Dims D, int K) {
+                                                      int* __restrict__ inv, Dims D) {
   extern __shared__ int sh[];  // hist[nb] then base[nb]
   int* hist = sh;
   int* base = sh + D.nb;
   const int bh = blockIdx.y, b = bh / D.hq, h = bh % D.hq;
-  const size_t per_bh = (size_t)D.tq * K;
-  const size_t p0 = (size_t)blockIdx.x * kPairsWG;
-  const size_t p1 = min(per_bh, p0 + kPairsWG);
+  const size_t p0 = S.lo(D, bh) + (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t p1 = S.hi(D, bh), step = (size_t)gridDim.x * 256;
   for (int x = threadIdx.x; x < D.nb; x += 256) hist[x] = 0;
   __syncthreads();
-  const int* ib = idx + (size_t)bh * per_bh;
-  for (size_t pp = p0 + threadIdx.x; pp < p1; pp += 256) {
-    const int j = ib[pp];
-    const int c = (D.qoff + (int)(pp / K)) / kBlock;
-    if (j >= 0 && j < c) atomicAdd(&hist[j], 1);
+  for (size_t p = p0; p < p1; p += step) {
+    const int j = listed_block(S, D, bh, p);
+    if (j >= 0) atomicAdd(&hist[j], 1);
   }
   __syncthreads();
   const size_t bucket0 = (size_t)(b * D.hkv + h / D.hpg) * D.nb;
@@ -286,14 +344,12 @@ __global__ __launch_bounds__(256) void sp_fill_kernel(const int* __restrict__ id
     hist[x] = 0;
   }
   __syncthreads();
-  for (size_t pp = p0 + threadIdx.x; pp < p1; pp += 256) {
-    const int j = ib[pp];
-    const int c = (D.qoff + (int)(pp / K)) / kBlock;
-    if (j >= 0 && j < c) {
+  for (size_t p = p0; p < p1; p += step) {
+    const int j = listed_block(S, D, bh, p);
+    if (j >= 0) {
       const int x = base[j] + atomicAdd(&hist[j], 1);
-      const int pair = (int)((size_t)bh * per_bh + pp);
-      list[x] = pair;
-      inv[pair] = x;
+      list[x] = (int)p;
+      inv[p] = x;
     }
   }
 }
@@ -320,12 +376,12 @@ __global__ __launch_bounds__(256) void sp_chunkmap_kernel(const int* __restrict_
 // lane owns one query.
 constexpr int kChunksPerWG = 8;
 
-template <int HD>
+template <int HD, typename Src>
 __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ bias, const int* __restrict__ list, const int* __restrict__ start,
+    Src S, const int* __restrict__ list, const int* __restrict__ start,
     const int* __restrict__ count, const int* __restrict__ cstart, const int* __restrict__ cbk,
-    float* __restrict__ plse, bf16* __restrict__ po, Dims D, int K, int nbk, int nqb, int dcpb) {
+    float* __restrict__ plse, bf16* __restrict__ po, Dims D, int nbk, int nqb, int dcpb) {
   constexpr int KP = HD + 8, VP = kBlock + 4, KS = HD / 16, DM = HD / 32;
   constexpr int OP = 72;  // pitch (bf16) of the per-wave output staging rows: 16-byte aligned
   __shared__ __align__(16) bf16 Ks[kBlock * KP];
@@ -370,9 +426,9 @@ __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
       const int n = min(kChunk, count[bk] - ci * kChunk);
       valid = pi < n;
       const int pair = list[start[bk] + ci * kChunk + (valid ? pi : 0)];
-      row = (size_t)pair / K;
+      row = (size_t)S.row_of(pair);  // a listed pair has a valid row
       pos = ndiag * kChunk + start[bk] + ci * kChunk + pi;
-      bv = bias[pair];
+      bv = S.bias_of(pair);
       tmax = 0x7fffffff;  // a historical block lies wholly before the query
     }
     bf16x8 qf[KS];
@@ -492,14 +548,13 @@ __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
 // slot s < K whose block idx[row, s] lies before c(t).  L = log sum exp(lse_s),
 // O = sum_s exp(lse_s - L) O_s.  One wavefront per row; a partial row is read
 // by HD/8 lanes, 16 bytes each, so one load instruction covers 64/(HD/8) slots.
-template <int HD>
-__global__ __launch_bounds__(256) void sp_merge_kernel(const int* __restrict__ idx,
-                                                       const int* __restrict__ inv,
+template <int HD, typename Src>
+__global__ __launch_bounds__(256) void sp_merge_kernel(Src S, const int* __restrict__ inv,
                                                        const float* __restrict__ plse,
                                                        const bf16* __restrict__ po,
                                                        bf16* __restrict__ o,
-                                                       float* __restrict__ lse, Dims D, int K,
-                                                       int nqb, int dcpb) {
+                                                       float* __restrict__ lse, Dims D, int nqb,
+                                                       int dcpb) {
   constexpr int LPP = HD / 8, SPW = 64 / LPP;
   const int lane = threadIdx.x & 63;
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -512,8 +567,8 @@ __global__ __launch_bounds__(256) void sp_merge_kernel(const int* __restrict__ i
   const int dpos = ((b * D.hkv + g) * nqb + (c - D.qoff / kBlock)) * dcpb * kChunk +
                    hl * kBlock + t % kBlock;
   const int hbase = D.batch * D.hkv * nqb * dcpb * kChunk;
-  const int* ir = idx + row * K;
-  const int* iv = inv + row * K;
+  const size_t a0 = S.seg_lo(row);
+  const int len = (int)(S.seg_hi(row) - a0);
   const int grp = lane / LPP, col = (lane % LPP) * 8;
   const bf16* pr = po + col;
   // online merge in log2 units: m running max, sm = sum of 2^(lse - m),
@@ -526,11 +581,11 @@ __global__ __launch_bounds__(256) void sp_merge_kernel(const int* __restrict__ i
     for (int e = 0; e < 8; ++e) acc[e] = grp == 0 ? to_f32(cv[e]) : 0.f;
   }
   // the listed slots, 64 at a time: each lane reads one slot's block, position and lse
-  for (int w0 = 0; w0 < K; w0 += 64) {
+  for (int w0 = 0; w0 < len; w0 += 64) {
     const int x = w0 + lane;
-    const int j = x < K ? ir[x] : -1;
-    const bool ok = j >= 0 && j < c;
-    const int px = ok ? hbase + iv[x] : dpos;
+    const int j = x < len ? S.j_of(a0 + x) : -1;
+    const bool ok = j >= 0 && j < c && S.row_of(a0 + x) == (long long)row;
+    const int px = ok ? hbase + inv[a0 + x] : dpos;
     const float lx = ok ? plse[px] * kLog2e : -INFINITY;
     const unsigned long long bal = __ballot(ok);
     if (bal == 0) continue;
@@ -568,79 +623,131 @@ __global__ __launch_bounds__(256) void sp_merge_kernel(const int* __restrict__ i
 
 static int diag_chunks_per_block(const Dims& D) { return (D.hpg * kBlock + kChunk - 1) / kChunk; }
 static int query_blocks(const Dims& D) { return D.nb - D.qoff / kBlock; }
-// Partial slots of the block path: current-block chunks, then one per listed pair.
-static size_t block_path_slots(const Dims& D, int K) {
-  return (size_t)D.batch * D.hkv * query_blocks(D) * diag_chunks_per_block(D) * kChunk +
-         (size_t)D.batch * D.hq * D.tq * K;
+// Partial slots of the block path: current-block chunks, then one per pair.
+static size_t block_path_slots(const Dims& D, size_t npairs) {
+  return (size_t)D.batch * D.hkv * query_blocks(D) * diag_chunks_per_block(D) * kChunk + npairs;
 }
 
 // The block path histograms blocks in LDS: nb <= 8192 (64 KB for the fill);
 // partial positions are int.
+static bool block_path_fits(const Dims& D, size_t npairs) {
+  return D.nb <= 8192 && block_path_slots(D, npairs) < ((size_t)1 << 31);
+}
 static bool use_block_path(const Dims& D, int K) {
-  return D.tq >= 128 && D.nb <= 8192 && block_path_slots(D, K) < ((size_t)1 << 31);
+  return D.tq >= 128 && block_path_fits(D, (size_t)D.batch * D.hq * D.tq * K);
 }
 
-// Workspace: pair path  [plse (rows x (K+1)) | po (rows x (K+1) x d)];
-// block path [count | cursor | start | cstart | cbk | list (rows x K) | inv (rows x K) |
-//             plse (slots) | po (slots x d)].
+// Block path workspace: [count | cursor | start | cstart | cbk | list | inv |
+// plse (slots) | po (slots x d)], then rowof (npairs) for a CSR selection.
+static size_t block_path_workspace(const Dims& D, size_t npairs, bool csr) {
+  const size_t nbk = (size_t)D.batch * D.hkv * D.nb;
+  const size_t slots = block_path_slots(D, npairs);
+  const size_t max_chunks = npairs / kChunk + nbk;
+  return 3 * align256s(nbk * 4) + align256s((nbk + 1) * 4) + align256s(max_chunks * 4) +
+         2 * align256s(npairs * 4) + align256s(slots * 4) + align256s(slots * D.d * 2) +
+         (csr ? align256s(npairs * 4) : 0);
+}
+
+// Workspace: pair path  [plse (rows x (K+1)) | po (rows x (K+1) x d)]; block path above.
 size_t sparse_workspace(const Dims& D, int K) {
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
-  if (use_block_path(D, K)) {
-    const size_t nbk = (size_t)D.batch * D.hkv * D.nb;
-    const size_t pairs = rows * K, slots = block_path_slots(D, K);
-    const size_t max_chunks = pairs / kChunk + nbk;
-    return 3 * align256s(nbk * 4) + align256s((nbk + 1) * 4) + align256s(max_chunks * 4) +
-           2 * align256s(pairs * 4) + align256s(slots * 4) + align256s(slots * D.d * 2);
-  }
+  if (use_block_path(D, K)) return block_path_workspace(D, rows * K, false);
   const size_t pairs = rows * (K + 1);
   const size_t esz = 4;  // partial outputs are stored in the io dtype (<= 4 bytes)
   return align256s(pairs * sizeof(float)) + align256s(pairs * D.d * esz);
 }
 
-template <int HD>
-static hipError_t launch_block_path(const void* q, const void* k, const void* v, const int* idx,
-                                    const float* bias, void* o, float* lse, char* ws, int K,
+bool sparse_csr_supported(const Dims& D, long long nnz) {
+  return nnz >= 0 && block_path_fits(D, (size_t)nnz);
+}
+size_t sparse_csr_workspace(const Dims& D, long long nnz) {
+  return block_path_workspace(D, (size_t)nnz, true);
+}
+
+template <int HD, typename Src>
+static hipError_t launch_block_path(const void* q, const void* k, const void* v, const Src& S,
+                                    size_t npairs, size_t per_bh, void* o, float* lse, char* ws,
                                     const Dims& D, const StageEvents& E, hipStream_t st) {
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
-  const size_t pairs = rows * K, slots = block_path_slots(D, K);
+  const size_t slots = block_path_slots(D, npairs);
   const int nbk = D.batch * D.hkv * D.nb;
-  const size_t max_chunks = pairs / kChunk + (size_t)nbk;
+  const size_t max_chunks = npairs / kChunk + (size_t)nbk;
   char* p = ws;
   int* count = (int*)p;  p += align256s((size_t)nbk * 4);
   int* cursor = (int*)p; p += align256s((size_t)nbk * 4);
   int* start = (int*)p;  p += align256s((size_t)nbk * 4);
   int* cstart = (int*)p; p += align256s((size_t)(nbk + 1) * 4);
   int* cbk = (int*)p;    p += align256s(max_chunks * 4);
-  int* list = (int*)p;   p += align256s(pairs * 4);
-  int* inv = (int*)p;    p += align256s(pairs * 4);
+  int* list = (int*)p;   p += align256s(npairs * 4);
+  int* inv = (int*)p;    p += align256s(npairs * 4);
   float* plse = (float*)p; p += align256s(slots * 4);
   bf16* po = (bf16*)p;
   const unsigned zg = (unsigned)std::min<size_t>((2 * (size_t)nbk + 255) / 256, 4096);
   hipLaunchKernelGGL(sp_zero_kernel, dim3(zg), dim3(256), 0, st, count, (size_t)nbk);
   hipLaunchKernelGGL(sp_zero_kernel, dim3(zg), dim3(256), 0, st, cursor, (size_t)nbk);
-  const dim3 ig((unsigned)(((size_t)D.tq * K + kPairsWG - 1) / kPairsWG), D.batch * D.hq);
-  hipLaunchKernelGGL(sp_count_kernel, ig, dim3(256), (size_t)D.nb * 4, st, idx, count, D, K);
+  // workgroups per (batch, query head): one per 4096 pairs, at most kInvWGs
+  const unsigned gx = (unsigned)std::max<size_t>(1, std::min<size_t>(kInvWGs,
+                                                                     (per_bh + 4095) / 4096));
+  const dim3 ig(gx, D.batch * D.hq);
+  hipLaunchKernelGGL((sp_count_kernel<Src>), ig, dim3(256), (size_t)D.nb * 4, st, S, count, D);
   hipLaunchKernelGGL(sp_scan_kernel, dim3(1), dim3(1024), 0, st, (const int*)count, start, cstart,
                      nbk);
-  hipLaunchKernelGGL(sp_fill_kernel, ig, dim3(256), (size_t)D.nb * 8, st, idx, (const int*)start,
-                     cursor, list, inv, D, K);
+  hipLaunchKernelGGL((sp_fill_kernel<Src>), ig, dim3(256), (size_t)D.nb * 8, st, S,
+                     (const int*)start, cursor, list, inv, D);
   hipLaunchKernelGGL(sp_chunkmap_kernel, dim3((unsigned)((nbk + 255) / 256)), dim3(256), 0, st,
                      (const int*)cstart, cbk, nbk);
   // upper bound on the number of chunks; workgroups past the real count exit
   const int nqb = query_blocks(D), dcpb = diag_chunks_per_block(D);
   const size_t ndiag = (size_t)D.batch * D.hkv * nqb * dcpb;
   const size_t wgs = (ndiag + max_chunks + kChunksPerWG - 1) / kChunksPerWG;
-  hipLaunchKernelGGL((sp_partial_kernel<HD>), dim3((unsigned)wgs), dim3(256), 0, st,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, bias, (const int*)list,
+  hipLaunchKernelGGL((sp_partial_kernel<HD, Src>), dim3((unsigned)wgs), dim3(256), 0, st,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, S, (const int*)list,
                      (const int*)start, (const int*)count, (const int*)cstart, (const int*)cbk,
-                     plse, po, D, K, nbk, nqb, dcpb);
+                     plse, po, D, nbk, nqb, dcpb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   E.record(0, st);
-  hipLaunchKernelGGL((sp_merge_kernel<HD>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
-                     idx, (const int*)inv, (const float*)plse, (const bf16*)po, (bf16*)o, lse, D,
-                     K, nqb, dcpb);
+  hipLaunchKernelGGL((sp_merge_kernel<HD, Src>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                     st, S, (const int*)inv, (const float*)plse, (const bf16*)po, (bf16*)o, lse, D,
+                     nqb, dcpb);
   return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t launch_fixed_block_path(const void* q, const void* k, const void* v,
+                                          const int* idx, const float* bias, void* o, float* lse,
+                                          char* ws, int K, const Dims& D, const StageEvents& E,
+                                          hipStream_t st) {
+  const size_t rows = (size_t)D.batch * D.hq * D.tq;
+  return launch_block_path<HD, FixedSel>(q, k, v, FixedSel{idx, bias, K}, rows * K,
+                                         (size_t)D.tq * K, o, lse, ws, D, E, st);
+}
+
+template <int HD>
+static hipError_t launch_csr_t(const void* q, const void* k, const void* v,
+                               const long long* row_ptr, const int* col, const float* bias,
+                               long long nnz, void* o, float* lse, char* ws, const Dims& D,
+                               const StageEvents& E, hipStream_t st) {
+  const size_t rows = (size_t)D.batch * D.hq * D.tq;
+  int* rowof = (int*)(ws + block_path_workspace(D, (size_t)nnz, false));
+  const CsrSel S{row_ptr, col, bias, rowof, nnz};
+  if (nnz > 0) {
+    const unsigned g = (unsigned)std::min<size_t>(((size_t)nnz + 255) / 256, 8192);
+    hipLaunchKernelGGL(sp_fill_value_kernel, dim3(g), dim3(256), 0, st, rowof, (size_t)nnz, -1);
+    hipLaunchKernelGGL(sp_rowof_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, S,
+                       rowof, rows);
+  }
+  const size_t per_bh = ((size_t)nnz + (size_t)D.batch * D.hq - 1) / ((size_t)D.batch * D.hq);
+  return launch_block_path<HD, CsrSel>(q, k, v, S, (size_t)nnz, per_bh, o, lse, ws, D, E, st);
+}
+
+hipError_t launch_sparse_csr(const void* q, const void* k, const void* v, const long long* row_ptr,
+                             const int* col, const float* bias, long long nnz, void* o,
+                             float* lse, char* ws, const Dims& D, const StageEvents& E,
+                             hipStream_t st) {
+  if (D.d == 128) return launch_csr_t<128>(q, k, v, row_ptr, col, bias, nnz, o, lse, ws, D, E, st);
+  if (D.d == 64) return launch_csr_t<64>(q, k, v, row_ptr, col, bias, nnz, o, lse, ws, D, E, st);
+  return hipErrorInvalidValue;
 }
 
 template <int HD, typename T>
@@ -670,8 +777,9 @@ hipError_t launch_sparse(const void* q, const void* k, const void* v, const int*
                          hipStream_t st) {
   (void)ws_bytes;
   if (bf16_io && use_block_path(D, K)) {
-    if (D.d == 128) return launch_block_path<128>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
-    if (D.d == 64) return launch_block_path<64>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
+    if (D.d == 128)
+      return launch_fixed_block_path<128>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
+    if (D.d == 64) return launch_fixed_block_path<64>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
   }
   if (D.d == 128)
     return bf16_io ? launch_sparse_t<128, bf16>(q, k, v, idx, bias, o, lse, ws, K, D, E, st)

@@ -25,6 +25,8 @@ _STATUS = {0: "SAS_OK", 1: "SAS_ERR_NULL", 2: "SAS_ERR_SHAPE", 3: "SAS_ERR_DTYPE
 EXPORTS = ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_attn_bwd_ev",
            "sas_topk_blocks", "sas_topk_blocks_budget", "sas_sparse_fwd", "sas_sparse_fwd_ev",
            "sas_paged_append", "sas_paged_topk", "sas_paged_decode",
+           "sas_threshold_count", "sas_threshold_fill", "sas_sparse_fwd_csr",
+           "sas_sparse_fwd_csr_ev",
            "sas_status_string", "sas_last_hip_error")
 
 
@@ -75,13 +77,19 @@ def load():
         lib.sas_sparse_fwd.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P]
         lib.sas_attn_bwd_ev.argtypes = [P] * 17 + [SZ, P, I32, P]
         lib.sas_sparse_fwd_ev.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P, I32, P]
+        I64 = ctypes.c_int64
+        lib.sas_threshold_count.argtypes = [P, ctypes.c_float, P, P, P, P, SZ, P]
+        lib.sas_threshold_fill.argtypes = [P, ctypes.c_float, I32, P, P, P, I64, P, P, P]
+        lib.sas_sparse_fwd_csr.argtypes = [P, I64] + [P] * 9 + [SZ, P]
+        lib.sas_sparse_fwd_csr_ev.argtypes = [P, I64] + [P] * 9 + [SZ, P, I32, P]
         lib.sas_paged_append.argtypes = [P] * 10
         lib.sas_paged_topk.argtypes = [P, I32, I32, P, P, P, P, P, P, P]
         lib.sas_paged_decode.argtypes = [P, I32] + [P] * 10 + [SZ, P]
         for n in ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_topk_blocks",
                   "sas_topk_blocks_budget", "sas_sparse_fwd", "sas_attn_bwd_ev",
                   "sas_sparse_fwd_ev", "sas_paged_append", "sas_paged_topk",
-                  "sas_paged_decode"):
+                  "sas_paged_decode", "sas_threshold_count", "sas_threshold_fill",
+                  "sas_sparse_fwd_csr", "sas_sparse_fwd_csr_ev"):
             getattr(lib, n).restype = ctypes.c_int
         lib.sas_status_string.argtypes = [ctypes.c_int]
         lib.sas_status_string.restype = ctypes.c_char_p
@@ -319,4 +327,62 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_len, idx, bias, sm_scale=No
     _check("sas_paged_decode", load().sas_paged_decode(
         ctypes.byref(sh), int(topk), _p(seq_len), _p(block_table), _p(q), _p(k_pool), _p(v_pool),
         _p(idx), _p(bias), _p(o), _p(lse), _p(ws), ctypes.byref(n), _stream(q)))
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Dynamic-threshold selection (CSR) and the sparse forward over it.
+
+def threshold_blocks(qs, ks, theta, tk, block=64, renorm=0, sel_scale=None):
+    """Blocks whose normalised gate is >= theta.  Returns (row_ptr int64 [rows+1],
+    col int32 [nnz], bias float32 [nnz]); rows = batch*hq*tq in BHSD order.  Reads
+    nnz back to the host between the two passes (one stream synchronisation)."""
+    b, hq, tq, ds = qs.shape
+    hks = ks.shape[1]
+    sh = make_shape(b, hq, hks, tq, tk, 64, ds, block, hks, 0.0, sel_scale, _dt(qs), _dt(qs))
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check("sas_threshold_count", lib.sas_threshold_count(
+        ctypes.byref(sh), ctypes.c_float(theta), None, None, None, None, ctypes.byref(n), None))
+    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=qs.device)
+    row_ptr = torch.empty(b * hq * tq + 1, dtype=torch.int64, device=qs.device)
+    n = ctypes.c_size_t(ws.numel())
+    _check("sas_threshold_count", lib.sas_threshold_count(
+        ctypes.byref(sh), ctypes.c_float(theta), _p(qs), _p(ks), _p(row_ptr), _p(ws),
+        ctypes.byref(n), _stream(qs)))
+    nnz = int(row_ptr[-1].item())
+    col = torch.empty(max(nnz, 1), dtype=torch.int32, device=qs.device)
+    bias = torch.empty(max(nnz, 1), dtype=torch.float32, device=qs.device)
+    _check("sas_threshold_fill", lib.sas_threshold_fill(
+        ctypes.byref(sh), ctypes.c_float(theta), int(renorm), _p(qs), _p(ks), _p(row_ptr),
+        ctypes.c_int64(nnz), _p(col), _p(bias), _stream(qs)))
+    return row_ptr, col[:nnz], bias[:nnz]
+
+
+def sparse_csr_workspace_bytes(sh: Shape, nnz: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("sas_sparse_fwd_csr", load().sas_sparse_fwd_csr(
+        ctypes.byref(sh), ctypes.c_int64(nnz), *([None] * 9), ctypes.byref(n), None))
+    return n.value
+
+
+def sparse_fwd_csr(q, k, v, row_ptr, col, bias, block=64, sm_scale=None, ws=None, with_lse=True,
+                   events=None):
+    """Sparse forward over a CSR selection (rows in BHSD order).  Returns (o, lse)."""
+    b, hq, tq, d = q.shape
+    _, hkv, tk, _ = k.shape
+    nnz = int(col.numel())
+    sh = make_shape(b, hq, hkv, tq, tk, d, 32, block, hkv, sm_scale, 0.0, _dt(q), _dt(q))
+    o = torch.empty_like(q)
+    lse = torch.empty((b, hq, tq), dtype=torch.float32, device=q.device) if with_lse else None
+    need = sparse_csr_workspace_bytes(sh, nnz)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(ws.numel())
+    ev, nev = _events(events)
+    colp = _p(col) if nnz else None
+    biasp = _p(bias) if nnz else None
+    _check("sas_sparse_fwd_csr", load().sas_sparse_fwd_csr_ev(
+        ctypes.byref(sh), ctypes.c_int64(nnz), _p(row_ptr), colp, biasp, _p(q), _p(k), _p(v),
+        _p(o), _p(lse), _p(ws), ctypes.byref(n), ev, nev, _stream(q)))
     return o, lse

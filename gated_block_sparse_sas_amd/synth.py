@@ -42,6 +42,7 @@ class Workload:
     mode: str  # "train", "prefill" or "decode"
     topk: int = 0  # fixed budget, or the cap kmax of a proportional one
     frac: float = 0.0  # > 0: row t keeps min(topk, ceil(frac * c(t))) blocks
+    theta: float = 0.0  # dynamic threshold on the normalised gate (selection by threshold)
     hks: int = 0  # 0 -> hkv
     scales: dict = field(default_factory=dict)
 
@@ -91,6 +92,9 @@ WORKLOADS = {
                                 "decode", topk=8, scales=_HALF),
     "prefill_32k_top25pct": Workload("prefill_32k_top25pct", 6, 1, 32, 8, 32768, 32768, 128, 32,
                                      64, "bf16", "prefill", topk=128, frac=0.25, scales=_HALF),
+    # selection by a dynamic threshold: blocks whose normalised gate is >= 0.01
+    "prefill_32k_theta": Workload("prefill_32k_theta", 8, 1, 32, 8, 32768, 32768, 128, 32, 64,
+                                  "bf16", "prefill", theta=0.01, scales=_HALF),
 }
 
 

@@ -167,6 +167,56 @@ sas_status sas_sparse_fwd_ev(const sas_shape* shape, int32_t topk, const void* q
                              int32_t n_events, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Dynamic-threshold selection.  Instead of a fixed budget, row t keeps every
+ * historical block whose normalised gate g = exp(z - lam) is at least theta
+ * (z - lam >= log theta, evaluated in float32; theta <= 0 keeps every
+ * historical block, theta > 1 none).  The count varies per row, so the
+ * selection is CSR over the rows r = (b * hq + h) * tq + i:
+ *   row_ptr [batch*hq*tq + 1] int64, row_ptr[0] = 0, row_ptr[rows] = nnz;
+ *   col, bias [nnz]: row r's kept blocks in ascending order in
+ *   row_ptr[r] .. row_ptr[r+1]-1, bias as in sas_topk_blocks (renorm 0:
+ *   z - lam = log g; renorm 1: z - log sum_{kept} exp z).
+ * Source: blog, "Implementation and Efficiency" (attention only for the
+ * blocks whose score clears a dynamic threshold); the pages do not say what
+ * the threshold is compared with: here the normalised gate of the NeurIPS
+ * abstract's softmax gating. */
+
+/* Pass 1: counts and their scan into row_ptr (device).  The caller reads
+ * nnz = row_ptr[rows] after the stream reaches it and sizes col / bias.
+ * theta must not be NaN.  Workspace by size query (8 bytes per 4096 rows). */
+sas_status sas_threshold_count(const sas_shape* shape, float theta, const void* qs,
+                               const void* ks, int64_t* row_ptr, void* ws, size_t* ws_bytes,
+                               void* stream);
+
+/* Pass 2: the kept blocks and their bias.  row_ptr from pass 1 with the same
+ * shape, theta, qs and ks (the same kernel evaluates the predicate, so the
+ * counts match); nnz = row_ptr[rows] is the capacity of col / bias (entries
+ * are never written past it).  nnz == 0 writes nothing. */
+sas_status sas_threshold_fill(const sas_shape* shape, float theta, int32_t renorm, const void* qs,
+                              const void* ks, const int64_t* row_ptr, int64_t nnz, int32_t* col,
+                              float* bias, void* stream);
+
+/* Sparse forward over a CSR selection (any 1 <= tq <= tk, dtype SAS_BF16):
+ * row r attends its current block (causal, bias 0) plus the blocks
+ * col[row_ptr[r] .. row_ptr[r+1]-1] with their bias.  Entries that are not
+ * historical blocks of the row, and positions outside 0 .. nnz-1, are
+ * skipped; a block listed twice in a row counts twice.  Semantics otherwise
+ * those of sas_sparse_fwd.  Needs nb <= 8192 and nnz plus about batch * hkv
+ * * tk * hq / hkv current-block slots below 2^31 (SAS_ERR_UNSUPPORTED).
+ * lse may be NULL.  Workspace by size query (grows with nnz). */
+sas_status sas_sparse_fwd_csr(const sas_shape* shape, int64_t nnz, const int64_t* row_ptr,
+                              const int32_t* col, const float* bias, const void* q, const void* k,
+                              const void* v, void* o, float* lse, void* ws, size_t* ws_bytes,
+                              void* stream);
+
+/* Same as sas_sparse_fwd_csr, and records events[0] after the partial kernel. */
+sas_status sas_sparse_fwd_csr_ev(const sas_shape* shape, int64_t nnz, const int64_t* row_ptr,
+                                 const int32_t* col, const float* bias, const void* q,
+                                 const void* k, const void* v, void* o, float* lse, void* ws,
+                                 size_t* ws_bytes, void* const* events, int32_t n_events,
+                                 void* stream);
+
+/* ---------------------------------------------------------------------------
  * Decode over a paged cache (serving).  A page holds one 64-key block of one
  * sequence for every kv head; sequences have their own lengths and a block
  * table maps their blocks to pages, so caches grow a block at a time without

@@ -234,3 +234,44 @@ def test_paged_checks(lib):
     e = pshape(batch=0)
     assert lib.sas_paged_append(ctypes.byref(e), A, A, A, A, None, A, A, None, STREAM) == 0
     assert lib.sas_paged_topk(ctypes.byref(e), 4, 0, A, A, A, A, A, A, STREAM) == 0
+
+
+def test_threshold_and_csr_checks(lib):
+    sh = shape()
+    n = ctypes.c_size_t(0)
+    F = ctypes.c_float
+    # size queries
+    assert lib.sas_threshold_count(ctypes.byref(sh), F(0.1), None, None, None, None,
+                                   ctypes.byref(n), STREAM) == 0
+    assert n.value >= 8
+    small = ctypes.c_size_t(n.value - 1)
+    assert lib.sas_threshold_count(ctypes.byref(sh), F(0.1), A, A, A, A, ctypes.byref(small),
+                                   STREAM) == 6
+    assert lib.sas_threshold_count(ctypes.byref(sh), F(float("nan")), A, A, A, A,
+                                   ctypes.byref(n), STREAM) == 2
+    assert lib.sas_threshold_count(ctypes.byref(sh), F(0.1), A, None, A, A, ctypes.byref(n),
+                                   STREAM) == 1
+    assert lib.sas_threshold_count(ctypes.byref(sh), F(0.1), A, A, MIS, A, ctypes.byref(n),
+                                   STREAM) == 4
+    # fill: nnz < 0, renorm, NULL col with nnz > 0; nnz == 0 launches nothing
+    assert lib.sas_threshold_fill(ctypes.byref(sh), F(0.1), 0, A, A, A, -1, A, A, STREAM) == 2
+    assert lib.sas_threshold_fill(ctypes.byref(sh), F(0.1), 3, A, A, A, 5, A, A, STREAM) == 2
+    assert lib.sas_threshold_fill(ctypes.byref(sh), F(0.1), 0, A, A, A, 5, None, A, STREAM) == 1
+    assert lib.sas_threshold_fill(ctypes.byref(sh), F(0.1), 0, A, A, A, 0, None, None,
+                                  STREAM) == 0
+    # CSR sparse forward: size query grows with nnz, checks
+    n0, n1 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.sas_sparse_fwd_csr(ctypes.byref(sh), 0, *([None] * 9), ctypes.byref(n0),
+                                  STREAM) == 0
+    assert lib.sas_sparse_fwd_csr(ctypes.byref(sh), 1000, *([None] * 9), ctypes.byref(n1),
+                                  STREAM) == 0
+    assert n1.value > n0.value
+    assert lib.sas_sparse_fwd_csr(ctypes.byref(sh), -1, *([None] * 9), ctypes.byref(n0),
+                                  STREAM) == 2
+    args = [A, A, A, A, A, A, A, None, A]  # row_ptr col bias q k v o lse ws
+    assert lib.sas_sparse_fwd_csr(ctypes.byref(sh), 1000, *args, ctypes.byref(n0), STREAM) == 6
+    bad = list(args)
+    bad[0] = None
+    assert lib.sas_sparse_fwd_csr(ctypes.byref(sh), 1000, *bad, ctypes.byref(n1), STREAM) == 1
+    f32 = shape(dtype=ops.SAS_F32, d=64)
+    assert lib.sas_sparse_fwd_csr(ctypes.byref(f32), 10, *args, ctypes.byref(n1), STREAM) == 5
