@@ -11,6 +11,8 @@ One step is one pass of the whole hot path on resident synthetic inputs:
                      history, at most 128 blocks) -> top-K sparse forward
   decode_paged_mix   decode over a block-paged cache: 32 sequences of mixed
                      lengths (64 .. 65536 tokens), top-K selection -> decode
+  prefill_32k_theta  dynamic-threshold selection (normalised gate >= 0.01, CSR:
+                     count, host read of nnz, fill) -> sparse forward over CSR
 The headline value is the training fwd+bwd rate at 32k in TFLOP/s counting
 attended (row, key) pairs only (forward 4*d flop per pair, backward 10*d).
 Times come from HIP events recorded on the stream the kernels run on.
@@ -170,6 +172,8 @@ def main():
     pq = {n: t.to(dev) for n, t in synth.draw_all(wq, ("q", "k", "v", "qs", "ks")).items()}
     wg = synth.PAGED_WORKLOADS["decode_paged_mix"]
     pg = {n: t.to(dev) for n, t in synth.draw_paged(wg).items()}
+    wh = W["prefill_32k_theta"]
+    ph = {n: t.to(dev) for n, t in synth.draw_all(wh, ("q", "k", "v", "qs", "ks")).items()}
     torch.cuda.synchronize()
     log("inputs resident in HBM (%.1f s)" % (time.time() - t0))
 
@@ -184,10 +188,17 @@ def main():
     sh_g = ops.make_paged_shape(wg.batch, wg.hq, wg.hkv, wg.d, wg.ds, wg.max_blocks,
                                 pg["k_pool"].shape[0])
     ws_g = torch.empty(ops.paged_workspace_bytes(sh_g, wg.topk), dtype=torch.uint8, device=dev)
+    ws_h = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    nnz_h = int(ops.threshold_count(ph["qs"], ph["ks"], wh.theta, wh.tk, ws=ws_h)[-1].item())
+    sh_h = ops.make_shape(1, wh.hq, wh.hkv, wh.tq, wh.tk, wh.d, wh.ds, 64, wh.hkv)
+    ws_hs = torch.empty(ops.sparse_csr_workspace_bytes(sh_h, nnz_h), dtype=torch.uint8,
+                        device=dev)
+    nnz_seen = []
 
     names = ["start", "gate", "fwd", "bwd_dq", "bwd_dkdv", "bwd_dks", "bwd", "pf_topk",
              "pf_partial", "pf_sparse", "dc_topk", "dc_partial", "dc_sparse", "pq_topk",
-             "pq_partial", "pq_sparse", "pg_topk", "pg_decode"]
+             "pq_partial", "pq_sparse", "pg_topk", "pg_decode", "th_start", "th_count",
+             "th_fill0", "th_fill", "th_partial", "th_sparse"]
 
     def step(ev):
         E = {n: ev[n] for n in names}
@@ -219,6 +230,17 @@ def main():
         ops.paged_decode(pg["q"], pg["k_pool"], pg["v_pool"], pg["block_table"], pg["seq_len"],
                          idx, bias, ws=ws_g)
         E["pg_decode"].record()
+        E["th_start"].record()
+        row_ptr = ops.threshold_count(ph["qs"], ph["ks"], wh.theta, wh.tk, ws=ws_h)
+        E["th_count"].record()
+        nnz = int(row_ptr[-1].item())  # the host sizes the CSR arrays
+        E["th_fill0"].record()
+        col, bias = ops.threshold_fill(ph["qs"], ph["ks"], wh.theta, wh.tk, row_ptr, nnz)
+        E["th_fill"].record()
+        ops.sparse_fwd_csr(ph["q"], ph["k"], ph["v"], row_ptr, col, bias, ws=ws_hs,
+                           events=[E["th_partial"]])
+        E["th_sparse"].record()
+        nnz_seen.append(nnz)
 
     def new_events():
         return {n: torch.cuda.Event(enable_timing=True) for n in names}
@@ -253,8 +275,12 @@ def main():
         "quarter_sparse": dur("pq_topk", "pq_sparse"),
         "paged_topk": dur("pq_sparse", "pg_topk"),
         "paged_decode": dur("pg_topk", "pg_decode"),
+        "theta_count": dur("th_start", "th_count"),
+        "theta_fill": dur("th_fill0", "th_fill"),
+        "theta_partial": dur("th_fill", "th_partial"),
+        "theta_sparse": dur("th_fill", "th_sparse"),
     }
-    step_ms = dur("start", "pg_decode")
+    step_ms = dur("start", "th_sparse")
 
     pairs_t = wt.batch * wt.hq * causal_pairs(wt.tq, wt.tk)
     fl_fwd = 4.0 * wt.d * pairs_t
@@ -274,6 +300,12 @@ def main():
     pg_blocks = wg.hq * sum(min(wg.topk, (n - 1) // 64) + 1 for n in lens_g)
     pg_bytes = pg_blocks * 2 * 64 * wg.d * 2  # K and V of every attended block, bf16
     pg_gbps = pg_bytes / (part["paged_decode"] * 1e-3) / 1e9
+    assert all(n == nnz_h for n in nnz_seen)
+    rows_h = wh.batch * wh.hq * wh.tq
+    # attended pairs: 64 keys per selected block + the causal part of the current block
+    pairs_h = nnz_h * 64 + wh.batch * wh.hq * sum(
+        (wh.tk - wh.tq + i) % 64 + 1 for i in range(wh.tq))
+    h_tflops = 4.0 * wh.d * pairs_h / (part["theta_sparse"] * 1e-3) / 1e12
 
     # dominant kernel: the key-stationary backward kernel (dK, dV): S, dP, dV
     # and dK over every attended pair = 8*d flop per pair
@@ -312,7 +344,8 @@ def main():
         "config": {"workload": "train_32k", "batch": wt.batch, "hq": wt.hq, "hkv": wt.hkv,
                    "seq_len": wt.tq, "d": wt.d, "block": wt.block, "ds": wt.ds,
                    "also_in_step": ["prefill_32k_top16", "decode_64k_top8",
-                                    "prefill_32k_top25pct", "decode_paged_mix"]},
+                                    "prefill_32k_top25pct", "decode_paged_mix",
+                                    "prefill_32k_theta"]},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "train_ms": round(t_train, 3),
         "parts_ms": {k: round(v, 4) for k, v in part.items()},
@@ -337,6 +370,12 @@ def main():
                          "topk_ms": round(part["paged_topk"], 4), "kv_bytes": pg_bytes,
                          "GBps": round(pg_gbps, 1),
                          "frac_hbm": round(pg_gbps / PEAK_HBM_GBPS, 4)},
+        "sparse_prefill_theta": {"workload": "prefill_32k_theta", "theta": wh.theta,
+                                 "nnz": nnz_h, "blocks_per_row": round(nnz_h / rows_h, 2),
+                                 "count_ms": round(part["theta_count"], 3),
+                                 "fill_ms": round(part["theta_fill"], 3),
+                                 "ms": round(part["theta_sparse"], 3),
+                                 "tflops": round(h_tflops, 2), "attended_pairs": pairs_h},
         "roofline": roofline,
         "wall_s_timed": round(wall, 3),
     }

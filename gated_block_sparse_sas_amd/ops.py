@@ -333,30 +333,50 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_len, idx, bias, sm_scale=No
 # ---------------------------------------------------------------------------
 # Dynamic-threshold selection (CSR) and the sparse forward over it.
 
-def threshold_blocks(qs, ks, theta, tk, block=64, renorm=0, sel_scale=None):
-    """Blocks whose normalised gate is >= theta.  Returns (row_ptr int64 [rows+1],
-    col int32 [nnz], bias float32 [nnz]); rows = batch*hq*tq in BHSD order.  Reads
-    nnz back to the host between the two passes (one stream synchronisation)."""
+def _thr_shape(qs, ks, tk, block, sel_scale):
     b, hq, tq, ds = qs.shape
     hks = ks.shape[1]
-    sh = make_shape(b, hq, hks, tq, tk, 64, ds, block, hks, 0.0, sel_scale, _dt(qs), _dt(qs))
+    return make_shape(b, hq, hks, tq, tk, 64, ds, block, hks, 0.0, sel_scale, _dt(qs), _dt(qs))
+
+
+def threshold_count(qs, ks, theta, tk, block=64, sel_scale=None, ws=None):
+    """Pass 1 of the threshold selection: row_ptr int64 [rows+1] (device), rows in
+    BHSD order; nnz = row_ptr[-1] once the stream reaches it."""
+    b, hq, tq, _ = qs.shape
+    sh = _thr_shape(qs, ks, tk, block, sel_scale)
     lib = load()
     n = ctypes.c_size_t(0)
     _check("sas_threshold_count", lib.sas_threshold_count(
         ctypes.byref(sh), ctypes.c_float(theta), None, None, None, None, ctypes.byref(n), None))
-    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=qs.device)
+    if ws is None or ws.numel() < n.value:
+        ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=qs.device)
     row_ptr = torch.empty(b * hq * tq + 1, dtype=torch.int64, device=qs.device)
     n = ctypes.c_size_t(ws.numel())
     _check("sas_threshold_count", lib.sas_threshold_count(
         ctypes.byref(sh), ctypes.c_float(theta), _p(qs), _p(ks), _p(row_ptr), _p(ws),
         ctypes.byref(n), _stream(qs)))
-    nnz = int(row_ptr[-1].item())
+    return row_ptr
+
+
+def threshold_fill(qs, ks, theta, tk, row_ptr, nnz, block=64, renorm=0, sel_scale=None):
+    """Pass 2: (col int32 [nnz], bias float32 [nnz]) for the row_ptr of pass 1."""
+    sh = _thr_shape(qs, ks, tk, block, sel_scale)
     col = torch.empty(max(nnz, 1), dtype=torch.int32, device=qs.device)
     bias = torch.empty(max(nnz, 1), dtype=torch.float32, device=qs.device)
-    _check("sas_threshold_fill", lib.sas_threshold_fill(
+    _check("sas_threshold_fill", load().sas_threshold_fill(
         ctypes.byref(sh), ctypes.c_float(theta), int(renorm), _p(qs), _p(ks), _p(row_ptr),
         ctypes.c_int64(nnz), _p(col), _p(bias), _stream(qs)))
-    return row_ptr, col[:nnz], bias[:nnz]
+    return col[:nnz], bias[:nnz]
+
+
+def threshold_blocks(qs, ks, theta, tk, block=64, renorm=0, sel_scale=None):
+    """Blocks whose normalised gate is >= theta.  Returns (row_ptr int64 [rows+1],
+    col int32 [nnz], bias float32 [nnz]); rows = batch*hq*tq in BHSD order.  Reads
+    nnz back to the host between the two passes (one stream synchronisation)."""
+    row_ptr = threshold_count(qs, ks, theta, tk, block, sel_scale)
+    nnz = int(row_ptr[-1].item())
+    col, bias = threshold_fill(qs, ks, theta, tk, row_ptr, nnz, block, renorm, sel_scale)
+    return row_ptr, col, bias
 
 
 def sparse_csr_workspace_bytes(sh: Shape, nnz: int) -> int:
