@@ -16,12 +16,15 @@
 // by the same instructions and the counts always match the entries.
 //
 // One lane per row, the 64 rows of a wave consecutive positions of one
-// (batch, head) as in the lane-per-row Top-K kernel: every ks row is a
-// wave-uniform load, scores are recomputed per pass (ds multiply-adds each).
+// (batch, head) as in the gate kernel: every ks row is a wave-uniform load,
+// scores (packed bf16 dot products, log2 units) are recomputed per pass: the
+// normaliser in one online pass, then the count, or the (renormalised) bias
+// and the entries.
 #include "sas_device.h"
 #include "sas_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace sas {
 
@@ -41,56 +44,88 @@ __global__ __launch_bounds__(256) void thr_kernel(const ST* __restrict__ qs,
   const int c = active ? (D.qoff + ic) / kBlock : 0;
   const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / kBlock;  // wave max of c
   const size_t row = ((size_t)b * D.hq + h) * D.tq + ic;
-  float qsv[DS];
+  // bf16 scores use packed bf16 dot products (products exact in fp32)
+  constexpr bool PACKED = std::is_same<ST, bf16>::value;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  float qsv[PACKED ? 1 : DS];
+  bf16x2 qs2[PACKED ? DS / 2 : 1];
+  if constexpr (PACKED) {
 #pragma unroll
-  for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
+    for (int e = 0; e < DS / 2; ++e) qs2[e] = *(const bf16x2*)(qs + row * DS + 2 * e);
+  } else {
+#pragma unroll
+    for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
+  }
   const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
-  auto zat = [&](int j) __attribute__((always_inline)) {
-    return D.sel_scale * sel_dot<DS>(qsv, ksb + (size_t)j * DS);
+  const float zs = D.sel_scale * kLog2e;  // scores in log2 units
+  auto z2 = [&](int j) __attribute__((always_inline)) {
+    const ST* kr = ksb + (size_t)j * DS;
+    float acc = 0.f;
+    if constexpr (PACKED) {
+#pragma unroll
+      for (int e = 0; e < DS / 2; ++e)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(qs2[e], *(const bf16x2*)(kr + 2 * e), acc, false);
+    } else {
+      acc = sel_dot<DS>(qsv, kr);
+    }
+    return zs * acc;
   };
-  // lam = m + log sum exp(z - m) over j < c
-  float m = -INFINITY;
-  for (int j = 0; j < cw; ++j) {
-    const float z = zat(j);
-    if (j < c) m = fmaxf(m, z);
+  // lam2 = m + log2 sum 2^(z2 - m) over j < c, online in chunks of 8 blocks
+  float m = -INFINITY, s = 0.f;
+  for (int j0 = 0; j0 < cw; j0 += 8) {
+    float zz[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = j0 + k;
+      zz[k] = -INFINITY;
+      if (j < cw) {
+        const float z = z2(j);
+        if (j < c) zz[k] = z;
+      }
+    }
+    float mc = zz[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mc = fmaxf(mc, zz[k]);
+    const float mn = fmaxf(m, mc);
+    if (mn == -INFINITY) continue;
+    float acc = s * exp2f(m - mn);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += exp2f(zz[k] - mn);
+    s = acc;
+    m = mn;
   }
-  float s = 0.f;
-  for (int j = 0; j < cw; ++j) {
-    const float z = zat(j);
-    if (j < c) s += expf(z - m);
-  }
-  const float lam = c > 0 ? m + logf(s) : -INFINITY;
-  const float lt = theta > 0.f ? logf(theta) : -INFINITY;
+  const float lam2 = c > 0 ? m + log2f(s) : -INFINITY;
+  const float lt2 = theta > 0.f ? log2f(theta) : -INFINITY;
   auto keep = [&](int j, float z) __attribute__((always_inline)) {
-    return j < c && (theta <= 0.f || z - lam >= lt);
+    return j < c && (theta <= 0.f || z - lam2 >= lt2);
   };
   if (!fill) {
     long long n = 0;
-    for (int j = 0; j < cw; ++j) n += keep(j, zat(j)) ? 1 : 0;
+    for (int j = 0; j < cw; ++j) n += keep(j, z2(j)) ? 1 : 0;
     if (active) {
       row_ptr[row + 1] = n;
       if (row == 0) row_ptr[0] = 0;
     }
     return;
   }
-  float norm = lam;
+  float norm2 = lam2;
   if (renorm) {
     float sk = 0.f;
     for (int j = 0; j < cw; ++j) {
-      const float z = zat(j);
-      if (keep(j, z)) sk += expf(z - m);
+      const float z = z2(j);
+      if (keep(j, z)) sk += exp2f(z - m);
     }
-    norm = sk > 0.f ? m + logf(sk) : -INFINITY;
+    norm2 = sk > 0.f ? m + log2f(sk) : -INFINITY;
   }
   if (!active) return;
   // this row's entries: [row_ptr[row], row_ptr[row + 1]) clamped to [0, nnz)
   long long p = min(max(row_ptr[row], 0LL), nnz);
   const long long e = max(p, min(row_ptr[row + 1], nnz));
   for (int j = 0; j < c && p < e; ++j) {
-    const float z = zat(j);
+    const float z = z2(j);
     if (keep(j, z)) {
       col[p] = j;
-      bias[p] = z - norm;
+      bias[p] = (z - norm2) * kLn2;
       ++p;
     }
   }
