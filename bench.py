@@ -11,6 +11,7 @@ One step is one pass of the whole hot path on resident synthetic inputs:
                      history, at most 128 blocks) -> top-K sparse forward
   decode_paged_mix   decode over a block-paged cache: 32 sequences of mixed
                      lengths (64 .. 65536 tokens), top-K selection -> decode
+  decode_64k_b16_top32  16-token context units: top-K (K = 32) -> sparse decode
   prefill_32k_theta  dynamic-threshold selection (normalised gate >= 0.01, CSR:
                      count, host read of nnz, fill) -> sparse forward over CSR
 The headline value is the training fwd+bwd rate at 32k in TFLOP/s counting
@@ -172,6 +173,8 @@ def main():
     pq = {n: t.to(dev) for n, t in synth.draw_all(wq, ("q", "k", "v", "qs", "ks")).items()}
     wg = synth.PAGED_WORKLOADS["decode_paged_mix"]
     pg = {n: t.to(dev) for n, t in synth.draw_paged(wg).items()}
+    wu = W["decode_64k_b16_top32"]
+    du = {n: t.to(dev) for n, t in synth.draw_all(wu, ("q", "k", "v", "qs", "ks")).items()}
     wh = W["prefill_32k_theta"]
     ph = {n: t.to(dev) for n, t in synth.draw_all(wh, ("q", "k", "v", "qs", "ks")).items()}
     torch.cuda.synchronize()
@@ -194,11 +197,13 @@ def main():
     ws_hs = torch.empty(ops.sparse_csr_workspace_bytes(sh_h, nnz_h), dtype=torch.uint8,
                         device=dev)
     nnz_seen = []
+    sh_u = ops.make_shape(wu.batch, wu.hq, wu.hkv, wu.tq, wu.tk, wu.d, wu.ds, wu.block, wu.hkv)
+    ws_u = torch.empty(ops.sparse_workspace_bytes(sh_u, wu.topk), dtype=torch.uint8, device=dev)
 
     names = ["start", "gate", "fwd", "bwd_dq", "bwd_dkdv", "bwd_dks", "bwd", "pf_topk",
              "pf_partial", "pf_sparse", "dc_topk", "dc_partial", "dc_sparse", "pq_topk",
              "pq_partial", "pq_sparse", "pg_topk", "pg_decode", "th_start", "th_count",
-             "th_fill0", "th_fill", "th_partial", "th_sparse"]
+             "th_fill0", "th_fill", "th_partial", "th_sparse", "u_topk", "u_sparse"]
 
     def step(ev):
         E = {n: ev[n] for n in names}
@@ -241,6 +246,10 @@ def main():
                            events=[E["th_partial"]])
         E["th_sparse"].record()
         nnz_seen.append(nnz)
+        idx, bias = ops.topk_blocks(du["qs"], du["ks"], wu.topk, wu.tk, block=wu.block)
+        E["u_topk"].record()
+        ops.sparse_fwd(du["q"], du["k"], du["v"], idx, bias, block=wu.block, ws=ws_u)
+        E["u_sparse"].record()
 
     def new_events():
         return {n: torch.cuda.Event(enable_timing=True) for n in names}
@@ -279,8 +288,10 @@ def main():
         "theta_fill": dur("th_fill0", "th_fill"),
         "theta_partial": dur("th_fill", "th_partial"),
         "theta_sparse": dur("th_fill", "th_sparse"),
+        "units_topk": dur("th_sparse", "u_topk"),
+        "units_decode": dur("u_topk", "u_sparse"),
     }
-    step_ms = dur("start", "th_sparse")
+    step_ms = dur("start", "u_sparse")
 
     pairs_t = wt.batch * wt.hq * causal_pairs(wt.tq, wt.tk)
     fl_fwd = 4.0 * wt.d * pairs_t
@@ -306,6 +317,8 @@ def main():
     pairs_h = nnz_h * 64 + wh.batch * wh.hq * sum(
         (wh.tk - wh.tq + i) % 64 + 1 for i in range(wh.tq))
     h_tflops = 4.0 * wh.d * pairs_h / (part["theta_sparse"] * 1e-3) / 1e12
+    u_bytes = wu.batch * wu.hq * (min(wu.topk, (wu.tk - 1) // wu.block) + 1) * 2 * wu.block * wu.d * 2
+    u_gbps = u_bytes / (part["units_decode"] * 1e-3) / 1e9
 
     # dominant kernel: the key-stationary backward kernel (dK, dV): S, dP, dV
     # and dK over every attended pair = 8*d flop per pair
@@ -345,7 +358,7 @@ def main():
                    "seq_len": wt.tq, "d": wt.d, "block": wt.block, "ds": wt.ds,
                    "also_in_step": ["prefill_32k_top16", "decode_64k_top8",
                                     "prefill_32k_top25pct", "decode_paged_mix",
-                                    "prefill_32k_theta"]},
+                                    "prefill_32k_theta", "decode_64k_b16_top32"]},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "train_ms": round(t_train, 3),
         "parts_ms": {k: round(v, 4) for k, v in part.items()},
@@ -376,6 +389,10 @@ def main():
                                  "fill_ms": round(part["theta_fill"], 3),
                                  "ms": round(part["theta_sparse"], 3),
                                  "tflops": round(h_tflops, 2), "attended_pairs": pairs_h},
+        "decode_units16": {"workload": "decode_64k_b16_top32", "block": wu.block,
+                           "ms": round(part["units_decode"], 4),
+                           "topk_ms": round(part["units_topk"], 4), "kv_bytes": u_bytes,
+                           "GBps": round(u_gbps, 1), "frac_hbm": round(u_gbps / PEAK_HBM_GBPS, 4)},
         "roofline": roofline,
         "wall_s_timed": round(wall, 3),
     }

@@ -1013,7 +1013,7 @@ __global__ __launch_bounds__(256) void dks_kernel(const float* __restrict__ dz,
   const int bs = blockIdx.z, b = bs / D.hks, s = bs % D.hks;
   const int nch = (D.tq + kDksChunk - 1) / kDksChunk;
   const int hl = blockIdx.y / nch, i0 = (blockIdx.y % nch) * kDksChunk;
-  const int i_min = max(0, (j0 + 1) * kBlock - D.qoff);  // first row with c(t) > j0
+  const int i_min = max(0, (j0 + 1) * D.blk - D.qoff);  // first row with c(t) > j0
   const int istart = max(i0, i_min), iend = min(i0 + kDksChunk, D.tq);
   if (istart >= iend) return;  // uniform over the workgroup
   const size_t hrow = ((size_t)b * D.hq + s * D.hps + hl) * D.tq;

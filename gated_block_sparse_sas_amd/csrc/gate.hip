@@ -26,8 +26,8 @@ __global__ __launch_bounds__(256) void gate_lse_kernel(const ST* __restrict__ qs
   const int wave_first = blockIdx.x * 256 + (threadIdx.x & ~63);
   if (wave_first >= D.tq) return;  // whole wave past the end
   const int ic = i < D.tq ? i : D.tq - 1;
-  const int c = (D.qoff + ic) / kBlock;
-  const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / kBlock;  // wave max of c
+  const int c = (D.qoff + ic) / D.blk;
+  const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / D.blk;  // wave max of c
   const size_t row = ((size_t)b * D.hq + h) * D.tq + ic;
   // bf16 scores use packed bf16 dot products (products exact in fp32)
   constexpr bool PACKED = std::is_same<ST, bf16>::value;
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void gate_bias_kernel(const ST* __restrict__ q
   const int i = (int)(row % D.tq);
   const int h = (int)((row / D.tq) % D.hq);
   const int b = (int)(row / ((size_t)D.tq * D.hq));
-  const int c = (D.qoff + i) / kBlock;
+  const int c = (D.qoff + i) / D.blk;
   float out;
   if (j < c) {
     float qsv[DS];

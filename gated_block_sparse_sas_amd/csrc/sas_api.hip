@@ -38,7 +38,9 @@ sas_status resolve(const sas_shape* s, sas::Dims* D) {
       !(s->sel_scale <= 0.f || isfinite(s->sel_scale)) || isnan(s->sm_scale) ||
       isnan(s->sel_scale))
     return SAS_ERR_SHAPE;
-  if (s->block != sas::kBlock || s->tk % sas::kBlock != 0) return SAS_ERR_UNSUPPORTED;
+  // gate blocks of 1, 2, 4, ..., 64 tokens; keys come in 64-key tiles
+  if (s->block > sas::kBlock || (s->block & (s->block - 1)) != 0 || s->tk % sas::kBlock != 0)
+    return SAS_ERR_UNSUPPORTED;
   if (s->d != 64 && s->d != 128) return SAS_ERR_UNSUPPORTED;
   if (s->ds != 16 && s->ds != 32 && s->ds != 64) return SAS_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)s->batch * s->hq * s->tq;
@@ -52,7 +54,8 @@ sas_status resolve(const sas_shape* s, sas::Dims* D) {
   D->tk = s->tk;
   D->d = s->d;
   D->ds = s->ds;
-  D->nb = s->tk / sas::kBlock;
+  D->nb = s->tk / s->block;
+  D->blk = s->block;
   D->qoff = s->tk - s->tq;
   D->hpg = s->hq / s->hkv;
   D->hps = s->hq / hks;
@@ -92,6 +95,7 @@ sas_status resolve_paged(const sas_paged_shape* s, sas::Dims* D) {
   D->d = s->d;
   D->ds = s->ds;
   D->nb = s->max_blocks;
+  D->blk = sas::kBlock;
   D->qoff = D->tk - 1;
   D->hpg = s->hq / s->hkv;
   D->hps = s->hq / hks;
@@ -154,6 +158,7 @@ sas_status sas_attn_fwd(const sas_shape* shape, const void* q, const void* k, co
   if (r != SAS_OK) return r;
   if ((r = check_ptrs({q, k, v, qs, ks, gate_lse, o, lse})) != SAS_OK) return r;
   if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
+  if (shape->dtype == SAS_BF16 && D.blk != sas::kBlock) return SAS_ERR_UNSUPPORTED;
   if (D.batch == 0) return SAS_OK;
   hipStream_t st = (hipStream_t)stream;
   if (shape->dtype == SAS_BF16)
@@ -171,6 +176,7 @@ static sas_status attn_bwd_impl(const sas_shape* shape, const void* q, const voi
   if (r != SAS_OK) return r;
   if (!ws_bytes) return SAS_ERR_NULL;
   if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
+  if (shape->dtype == SAS_BF16 && D.blk != sas::kBlock) return SAS_ERR_UNSUPPORTED;
   const sas::BwdWs W = sas::bwd_workspace(D, dz == nullptr);
   if (!ws) {
     *ws_bytes = W.total;

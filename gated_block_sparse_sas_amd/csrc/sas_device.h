@@ -13,12 +13,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kBlock = 64;  // keys per gate block == keys per LDS tile
+constexpr int kBlock = 64;  // keys per LDS tile; the gate block size of the MFMA kernels
 
 // Resolved problem description passed by value to every kernel.
 struct Dims {
   int batch, hq, hkv, hks;
   int tq, tk, d, ds, nb, qoff;
+  int blk;   // gate block (context unit) size: 1, 2, 4, ..., 64; nb = tk / blk
   int hpg;   // query heads per kv head   (hq / hkv)
   int hps;   // query heads per selector head (hq / hks)
   float sm_scale, sel_scale;

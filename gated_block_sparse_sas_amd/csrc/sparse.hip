@@ -47,7 +47,7 @@ struct DenseKV {
   __device__ int t_of(const Dims& D, size_t row) const { return D.qoff + (int)(row % D.tq); }
   // element offset of block j of (b, kv head g) in k and v; -1: not readable
   __device__ long long block(const Dims& D, int b, int g, int j) const {
-    return (long long)((((size_t)b * D.hkv + g) * D.tk + (size_t)j * kBlock) * HD);
+    return (long long)((((size_t)b * D.hkv + g) * D.tk + (size_t)j * D.blk) * HD);
   }
 };
 
@@ -88,7 +88,8 @@ __global__ __launch_bounds__(64) void sparse_pair_kernel(
     if (lane == 0) plse[pair] = -INFINITY;
     return;
   }
-  const int c = t / kBlock;
+  const int B = D.blk;  // keys per block: lanes 0 .. B-1 hold one each
+  const int c = t / B;
   const int g = h / D.hpg;
   int j;
   float add;
@@ -110,12 +111,15 @@ __global__ __launch_bounds__(64) void sparse_pair_kernel(
   }
   for (int e = lane; e < HD; e += 64) qsh[e] = to_f32(q[row * HD + e]);
   __syncthreads();
-  const int key = j * kBlock + lane;
-  const T* kr = S.k + boff + (size_t)lane * HD;
-  float s = 0.f;
+  const int key = j * B + lane;
+  float s = -INFINITY;
+  if (lane < B) {
+    const T* kr = S.k + boff + (size_t)lane * HD;
+    float a = 0.f;
 #pragma unroll 16
-  for (int e = 0; e < HD; ++e) s = fmaf(qsh[e], to_f32(kr[e]), s);
-  s = s * D.sm_scale + add;
+    for (int e = 0; e < HD; ++e) a = fmaf(qsh[e], to_f32(kr[e]), a);
+    s = a * D.sm_scale + add;
+  }
   if (key > t) s = -INFINITY;
   const float m = wave_max(s);
   const float p = (m == -INFINITY) ? 0.f : exp2f((s - m) * kLog2e);
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(64) void sparse_pair_kernel(
   for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
   const T* vb = S.v + boff;
 #pragma unroll 8
-  for (int u = 0; u < kBlock; ++u) {
+  for (int u = 0; u < B; ++u) {
     const float pu = ps[u];
 #pragma unroll
     for (int x = 0; x < DPL; ++x) acc[x] = fmaf(pu, to_f32(vb[(size_t)u * HD + lane * DPL + x]), acc[x]);
@@ -628,10 +632,10 @@ static size_t block_path_slots(const Dims& D, size_t npairs) {
   return (size_t)D.batch * D.hkv * query_blocks(D) * diag_chunks_per_block(D) * kChunk + npairs;
 }
 
-// The block path histograms blocks in LDS: nb <= 8192 (64 KB for the fill);
-// partial positions are int.
+// The block path works on 64-key gate blocks (one LDS tile each), histograms
+// blocks in LDS: nb <= 8192 (64 KB for the fill); partial positions are int.
 static bool block_path_fits(const Dims& D, size_t npairs) {
-  return D.nb <= 8192 && block_path_slots(D, npairs) < ((size_t)1 << 31);
+  return D.blk == kBlock && D.nb <= 8192 && block_path_slots(D, npairs) < ((size_t)1 << 31);
 }
 static bool use_block_path(const Dims& D, int K) {
   return D.tq >= 128 && block_path_fits(D, (size_t)D.batch * D.hq * D.tq * K);

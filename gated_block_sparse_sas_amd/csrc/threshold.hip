@@ -41,8 +41,8 @@ __global__ __launch_bounds__(256) void thr_kernel(const ST* __restrict__ qs,
   if (wave_first >= D.tq) return;
   const bool active = i < D.tq;
   const int ic = min(i, D.tq - 1);
-  const int c = active ? (D.qoff + ic) / kBlock : 0;
-  const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / kBlock;  // wave max of c
+  const int c = active ? (D.qoff + ic) / D.blk : 0;
+  const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / D.blk;  // wave max of c
   const size_t row = ((size_t)b * D.hq + h) * D.tq + ic;
   // bf16 scores use packed bf16 dot products (products exact in fp32)
   constexpr bool PACKED = std::is_same<ST, bf16>::value;

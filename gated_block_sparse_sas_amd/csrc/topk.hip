@@ -33,7 +33,7 @@ template <typename ST>
 struct DenseSel {
   const ST* ks;
   __device__ int hist(const Dims& D, size_t row) const {
-    return (D.qoff + (int)(row % D.tq)) / kBlock;
+    return (D.qoff + (int)(row % D.tq)) / D.blk;
   }
   __device__ const ST* ks_row(const Dims& D, int b, int h, int j) const {
     return ks + (((size_t)b * D.hks + h / D.hps) * (size_t)D.nb + j) * D.ds;
@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
   const int wave_first = __builtin_amdgcn_readfirstlane(blockIdx.x * 256 + (threadIdx.x & ~63));
   if (wave_first >= D.tq) return;
   const int ic = min(i, D.tq - 1);
-  const int c = (D.qoff + ic) / kBlock;
-  const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / kBlock;  // wave max of c
+  const int c = (D.qoff + ic) / D.blk;
+  const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / D.blk;  // wave max of c
   const size_t row = ((size_t)b * D.hq + h) * D.tq + ic;
   float qsv[DS];
 #pragma unroll
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
   const int i = (int)(row % D.tq);
   const int h = (int)((row / D.tq) % D.hq);
   const int b = (int)(row / ((size_t)D.tq * D.hq));
-  const int c = (D.qoff + i) / kBlock;
+  const int c = (D.qoff + i) / D.blk;
   int n = min(kmax, c);
   if (frac > 0.f) n = min(n, (int)ceil((double)frac * (double)c));
   // scores and the gate normaliser over the whole history
@@ -442,11 +442,16 @@ hipError_t launch_topk_budget(const void* qs, const void* ks, int kmax, float fr
   return hipErrorInvalidValue;
 }
 
+// The lane-per-row kernel needs no LDS: many rows, K <= 32.
+static bool use_lane_kernel(const Dims& D, int K) {
+  const size_t nrows = (size_t)D.batch * D.hq * D.tq;
+  return nrows >= 16384 && K <= 32 && D.hq <= 65535 && D.batch <= 65535;
+}
+
 template <int DS, typename ST>
 static hipError_t launch_topk_t(const void* qs, const void* ks, int K, int renorm, int* idx,
                                 float* bias, const Dims& D, hipStream_t st) {
-  const size_t nrows_all = (size_t)D.batch * D.hq * D.tq;
-  if (nrows_all >= 16384 && K <= 32 && D.hq <= 65535 && D.batch <= 65535) {
+  if (use_lane_kernel(D, K)) {
     dim3 grid((D.tq + 255) / 256, D.hq, D.batch);
     if (K <= 8)
       hipLaunchKernelGGL((topk_lane_kernel<DS, ST, 8>), grid, dim3(256), 0, st, (const ST*)qs,
@@ -507,7 +512,7 @@ hipError_t launch_paged_topk(const void* qs, const void* ks_pool, const int* tab
 }
 
 bool topk_supported(const Dims& D, int K) {
-  return (size_t)(D.nb + K) * sizeof(float) <= 65536;
+  return use_lane_kernel(D, K) || (size_t)(D.nb + K) * sizeof(float) <= 65536;
 }
 
 hipError_t launch_topk(const void* qs, const void* ks, int K, int renorm, int* idx, float* bias,

@@ -47,8 +47,14 @@
  *    nothing.  Valid but unsupported shapes return SAS_ERR_UNSUPPORTED (there
  *    is no slow fallback).  A failed launch returns SAS_ERR_HIP; faults inside
  *    kernels surface at the caller's next synchronisation.
- *  - Supported: block == 64, tk % 64 == 0, d in {64, 128}, ds in {16, 32, 64},
+ *  - Supported: tk % 64 == 0, d in {64, 128}, ds in {16, 32, 64},
  *    hq % hkv == 0, hq % hks == 0, 1 <= tq <= tk.  batch == 0 is an empty call.
+ *  - Context units (block): 64 tokens everywhere; smaller units of 1, 2, 4,
+ *    8, 16 or 32 tokens (a unit may be a single token: NeurIPS abstract,
+ *    "tokens or blocks") for sas_gate_scores, the Top-K, budget and threshold
+ *    selections, sas_sparse_fwd (bf16 or f32) and, in f32 (d = 64),
+ *    sas_attn_fwd / sas_attn_bwd; the bf16 training kernels and
+ *    sas_sparse_fwd_csr take 64-token blocks (SAS_ERR_UNSUPPORTED otherwise).
  */
 #ifndef SAS_H
 #define SAS_H
@@ -115,7 +121,10 @@ sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, co
  * the min(topk, c(t)) blocks with the largest z, ordered by z descending and
  * block index ascending on ties; idx pads with -1 and bias with -inf.
  * bias = z - lam (renorm == 0, the training log-gate of the block) or
- * z - log sum_{selected} exp z (renorm == 1).  1 <= topk.
+ * z - log sum_{selected} exp z (renorm == 1).  1 <= topk.  Needs
+ * 4 (nb + topk) bytes of LDS per row, at most 64 KiB, unless there are at
+ * least 16384 rows and topk <= 32 (a kernel without LDS); SAS_ERR_UNSUPPORTED
+ * otherwise.
  * Source: both abstracts (selector + hard Top-K; budget = attended units per
  * query); the budget counts historical blocks, the current block is extra. */
 sas_status sas_topk_blocks(const sas_shape* shape, int32_t topk, int32_t renorm, const void* qs,

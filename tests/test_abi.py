@@ -275,3 +275,22 @@ def test_threshold_and_csr_checks(lib):
     assert lib.sas_sparse_fwd_csr(ctypes.byref(sh), 1000, *bad, ctypes.byref(n1), STREAM) == 1
     f32 = shape(dtype=ops.SAS_F32, d=64)
     assert lib.sas_sparse_fwd_csr(ctypes.byref(f32), 10, *args, ctypes.byref(n1), STREAM) == 5
+
+
+def test_block_size_support(lib):
+    # gate blocks of 1 .. 64 tokens (powers of two); bf16 training kernels: 64 only
+    for blk, ok in ((1, True), (16, True), (32, True), (64, True), (48, False), (128, False)):
+        for dt, d in ((ops.SAS_F32, 64), (ops.SAS_BF16, 128)):
+            sh = shape(batch=0, block=blk, dtype=dt, d=d)
+            r_gate = lib.sas_gate_scores(ctypes.byref(sh), A, A, A, None, STREAM)
+            r_fwd = fwd(lib, sh)
+            assert r_gate == (0 if ok else 5), (blk, dt)
+            want_fwd = 0 if ok and (dt == ops.SAS_F32 or blk == 64) else 5
+            assert r_fwd == want_fwd, (blk, dt, r_fwd)
+    # CSR forward: 64-token blocks; fixed-budget sparse forward: any supported size
+    n = ctypes.c_size_t(0)
+    sh = shape(block=16)
+    assert lib.sas_sparse_fwd_csr(ctypes.byref(sh), 10, *([None] * 9), ctypes.byref(n),
+                                  STREAM) == 5
+    assert lib.sas_sparse_fwd(ctypes.byref(sh), 4, *([None] * 7), None, ctypes.byref(n),
+                              STREAM) == 0
