@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
                                                           float frac, int renorm,
                                                           int* __restrict__ idx,
                                                           float* __restrict__ bias, Dims D,
-                                                          int kp2) {
+                                                          int kp2, int wpg) {
   extern __shared__ unsigned tsm[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int per = D.nb + 256 + 2 * kp2;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
   unsigned* sk = hist + 256;                         // selected keys
   int* sj = (int*)(sk + kp2);                        // selected blocks
   const size_t nrows = (size_t)D.batch * D.hq * D.tq;
-  const size_t row = (size_t)blockIdx.x * 4 + wave;
+  const size_t row = (size_t)blockIdx.x * wpg + wave;
   if (row >= nrows) return;  // whole wave (no workgroup barrier below)
   const int i = (int)(row % D.tq);
   const int h = (int)((row / D.tq) % D.hq);
@@ -413,17 +413,19 @@ static hipError_t launch_select_t(const void* qs, const void* ks, int kmax, floa
   int kp2 = 1;
   while (kp2 < kmax) kp2 <<= 1;
   const size_t per = (size_t)(D.nb + 256 + 2 * kp2) * sizeof(unsigned);
+  int wpg = 4;  // rows (waves) per workgroup, as many as 64 KiB of LDS holds
+  while (wpg > 1 && per * wpg > 65536) wpg >>= 1;
   const size_t nrows = (size_t)D.batch * D.hq * D.tq;
-  hipLaunchKernelGGL((topk_select_kernel<DS, ST>), dim3((unsigned)((nrows + 3) / 4)), dim3(256),
-                     per * 4, st, (const ST*)qs, (const ST*)ks, kmax, frac, renorm, idx, bias, D,
-                     kp2);
+  hipLaunchKernelGGL((topk_select_kernel<DS, ST>), dim3((unsigned)((nrows + wpg - 1) / wpg)),
+                     dim3(64 * wpg), per * wpg, st, (const ST*)qs, (const ST*)ks, kmax, frac,
+                     renorm, idx, bias, D, kp2, wpg);
   return hipGetLastError();
 }
 
 bool topk_budget_supported(const Dims& D, int kmax) {
   int kp2 = 1;
   while (kp2 < kmax) kp2 <<= 1;
-  return kmax <= 1024 && (size_t)(D.nb + 256 + 2 * kp2) * sizeof(unsigned) * 4 <= 65536;
+  return kmax <= 1024 && (size_t)(D.nb + 256 + 2 * kp2) * sizeof(unsigned) <= 65536;
 }
 
 hipError_t launch_topk_budget(const void* qs, const void* ks, int kmax, float frac, int renorm,
@@ -464,6 +466,10 @@ static hipError_t launch_topk_t(const void* qs, const void* ks, int K, int renor
                          (const ST*)ks, K, renorm, idx, bias, D);
     return hipGetLastError();
   }
+  // K >= 16: the radix-select kernel (same order and tie rule, frac = 0) costs
+  // a few passes over a row's scores instead of K argmax rounds
+  if (K >= 16 && topk_budget_supported(D, K))
+    return launch_select_t<DS, ST>(qs, ks, K, 0.f, renorm, idx, bias, D, st);
   const size_t per = (size_t)(D.nb + K) * sizeof(float);
   int wpg = 4;
   while (wpg > 1 && per * wpg > 65536) wpg >>= 1;
@@ -512,7 +518,8 @@ hipError_t launch_paged_topk(const void* qs, const void* ks_pool, const int* tab
 }
 
 bool topk_supported(const Dims& D, int K) {
-  return use_lane_kernel(D, K) || (size_t)(D.nb + K) * sizeof(float) <= 65536;
+  return use_lane_kernel(D, K) || (K >= 16 && topk_budget_supported(D, K)) ||
+         (size_t)(D.nb + K) * sizeof(float) <= 65536;
 }
 
 hipError_t launch_topk(const void* qs, const void* ks, int K, int renorm, int* idx, float* bias,

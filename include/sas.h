@@ -122,7 +122,8 @@ sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, co
  * block index ascending on ties; idx pads with -1 and bias with -inf.
  * bias = z - lam (renorm == 0, the training log-gate of the block) or
  * z - log sum_{selected} exp z (renorm == 1).  1 <= topk.  Needs
- * 4 (nb + topk) bytes of LDS per row, at most 64 KiB, unless there are at
+ * 4 (nb + topk) bytes of LDS per row (topk >= 16: 4 (nb + 256 +
+ * 2 next_pow2(topk)), topk <= 1024), at most 64 KiB, unless there are at
  * least 16384 rows and topk <= 32 (a kernel without LDS); SAS_ERR_UNSUPPORTED
  * otherwise.
  * Source: both abstracts (selector + hard Top-K; budget = attended units per
@@ -137,7 +138,7 @@ sas_status sas_topk_blocks(const sas_shape* shape, int32_t topk, int32_t renorm,
  * Order, padding (idx -1, bias -inf in slots n_t .. kmax-1) and the two bias
  * modes are those of sas_topk_blocks.  idx, bias: [batch, hq, tq, kmax].
  * 1 <= kmax <= 1024; frac must not be NaN (SAS_ERR_SHAPE).  Needs
- * 16 (nb + 256 + 2 * next_pow2(kmax)) bytes of LDS per workgroup, at most
+ * 4 (nb + 256 + 2 * next_pow2(kmax)) bytes of LDS per row, at most
  * 64 KiB (SAS_ERR_UNSUPPORTED beyond).  Source: blog, "Implementation and
  * Efficiency" (attention restricted to the top 25% of the context at 32k);
  * both abstracts (hard Top-K under an attention budget). */
