@@ -41,7 +41,9 @@ namespace sas {
 // workgroup: kFwdWaves waves of 32 query rows (kFwdRows rows) sharing each K/V tile
 constexpr int kFwdWaves = 8, kFwdThreads = 64 * kFwdWaves, kFwdRows = 32 * kFwdWaves;
 
-template <int HD, int DS>
+// UB gate units per 64-key tile (UB = 1: 64-token blocks; 2, 4: units of 32,
+// 16 tokens, whose bias then changes inside the tile).
+template <int HD, int DS, int UB>
 __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
@@ -52,6 +54,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   constexpr int NCH = kBlock * DC / kFwdThreads;  // 16-byte chunks per thread and tensor
   constexpr int KS = HD / 16;      // k-steps over the head dim
   constexpr int DM = HD / 32;      // 32-row M-tiles of O^T
+  constexpr int BU = kBlock / UB;  // tokens per gate unit
   // Key tiles are double-buffered in LDS, K and V row-major (V read
   // transposed, as the V^T operand, by transposing 8-byte reads).  The next
   // tile goes global -> registers at the start of a tile and registers ->
@@ -61,8 +64,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   __shared__ __align__(16) bf16 K1[kBlock * KP];
   __shared__ __align__(16) bf16 V0[kBlock * VP];
   __shared__ __align__(16) bf16 V1[kBlock * VP];
-  __shared__ __align__(16) bf16 S0[DS];  // ks row of the tile's block
-  __shared__ __align__(16) bf16 S1[DS];
+  __shared__ __align__(16) bf16 S0[UB * DS];  // ks rows of the tile's units
+  __shared__ __align__(16) bf16 S1[UB * DS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;  // (a wave-uniform copy here costs registers: keep it per lane)
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   const int qi = wq0 + l32;
   const int qc = min(qi, D.tq - 1);
   const int t = D.qoff + qc;
-  const int c = t / kBlock;
+  const int c = t / BU;  // historical units of this row (tile bounds below are in 64-key tiles)
   const int c_lo = (D.qoff + min(wq0, D.tq - 1)) / kBlock;
   const int c_hi = (D.qoff + min(wq0 + 31, D.tq - 1)) / kBlock;
   const int c_end = (D.qoff + min(qt * kFwdRows + kFwdRows - 1, D.tq - 1)) / kBlock;
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       kreg[x] = *(const bf16x8*)(kt + (id / DC) * HD + (id % DC) * 8);
       vreg[x] = *(const bf16x8*)(vt + (id / DC) * HD + (id % DC) * 8);
     }
-    if (tid < DS / 8) sreg = *(const bf16x8*)(ksb0 + (size_t)j * DS + tid * 8);
+    if (tid < UB * DS / 8) sreg = *(const bf16x8*)(ksb0 + (size_t)j * UB * DS + tid * 8);
   };
   auto sstore = [&](bf16* Kd, bf16* Vd, bf16* Sd) __attribute__((always_inline)) {
 #pragma unroll
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       *(bf16x8*)&Kd[(id / DC) * KP + (id % DC) * 8] = kreg[x];
       *(bf16x8*)&Vd[(id / DC) * VP + (id % DC) * 8] = vreg[x];
     }
-    if (tid < DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
+    if (tid < UB * DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
   };
   // per-lane part of the transposing V^T reads: lane 4k + a of each 16-lane
   // group points at key row 4 hh + k, columns 16 ((lane >> 4) & 1) + 4 a
@@ -134,14 +137,20 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   auto tile = [&](int j, auto mask_tag, const bf16* Ks, const bf16* Vs, const bf16* Ss)
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    float bias2 = 0.f;  // log2-domain gate bias of this lane's row for block j
-    if (j < c_hi) {
-      const bf16x2* kr = (const bf16x2*)(Ss + hh * (DS / 2));
-      float part = 0.f;
+    float bias2[UB];  // log2-domain gate bias of this lane's row for each unit of tile j
 #pragma unroll
-      for (int e = 0; e < DS / 4; ++e) part = __builtin_amdgcn_fdot2_f32_bf16(qsv[e], kr[e], part, false);
-      part += __shfl_xor(part, 32);
-      if (j < c) bias2 = (D.sel_scale * part - lam_t) * kLog2e;
+    for (int ub = 0; ub < UB; ++ub) bias2[ub] = 0.f;
+    if (UB == 1 ? j < c_hi : j <= c_hi) {
+#pragma unroll
+      for (int ub = 0; ub < UB; ++ub) {
+        const bf16x2* kr = (const bf16x2*)(Ss + ub * DS + hh * (DS / 2));
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < DS / 4; ++e)
+          part = __builtin_amdgcn_fdot2_f32_bf16(qsv[e], kr[e], part, false);
+        part += __shfl_xor(part, 32);
+        if (j * UB + ub < c) bias2[ub] = (D.sel_scale * part - lam_t) * kLog2e;
+      }
     }
     // S^T tile: two 32-key M-tiles x 32 queries
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -153,7 +162,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
         sacc[mt] = mfma32(a, qf[s], sacc[mt]);
       }
     }
-    // row max on the raw scores (c1 > 0, bias2 is constant over the tile)
+    // row max: with one unit per tile on the raw scores (c1 > 0, the bias is
+    // constant over the tile); with several, on the biased log2 logits, which
+    // then replace the raw scores in sacc
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -163,11 +174,16 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
           const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
           if (u > t) sacc[mt][r] = -INFINITY;
         }
+        if constexpr (UB > 1) {
+          // unit of key 32 mt + 8 (r / 4) + 4 hh + r % 4 within the tile
+          const int ub = UB == 2 ? mt : 2 * mt + r / 8;
+          sacc[mt][r] = fmaf(sacc[mt][r], c1, bias2[ub]);
+        }
         mx = fmaxf(mx, sacc[mt][r]);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    mx = fmaf(mx, c1, bias2);
+    if constexpr (UB == 1) mx = fmaf(mx, c1, bias2[0]);
     // Lazy rescaling: the running max only moves when it grows by more than
     // 8 (log2 units) in some row of the wave, so P <= 2^8 between updates.
     if (__any(mx > m_run + 8.f)) {
@@ -179,14 +195,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       m_run = m_new;
     }
     // (m_run is -inf only for a row with no visible key yet: all p are 0)
-    const float off = bias2 - m_run;
+    const float off = bias2[0] - m_run;
     float psum = 0.f;
     bf16x8 pb[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_raw(fmaf(sacc[mt][r], c1, off));
+        const float p = UB == 1 ? exp2_raw(fmaf(sacc[mt][r], c1, off))
+                                : exp2_raw(sacc[mt][r] - m_run);
         pb[mt][r / 8][r % 8] = (bf16)p;
         psum += p;
       }
@@ -253,7 +270,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   }
 }
 
-template <int HD, int DS>
+template <int HD, int DS, int UB>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const void* qs,
                                const void* ks, const float* lam, void* o, float* lse,
                                const Dims& D, hipStream_t st) {
@@ -261,7 +278,7 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, cons
   const int groups = D.batch * D.hkv;
   const int xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
   const unsigned grid = (unsigned)(D.batch * D.hq * nqt);
-  hipLaunchKernelGGL((attn_fwd_kernel<HD, DS>), dim3(grid), dim3(kFwdThreads), 0, st, (const bf16*)q,
+  hipLaunchKernelGGL((attn_fwd_kernel<HD, DS, UB>), dim3(grid), dim3(kFwdThreads), 0, st, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (const bf16*)qs, (const bf16*)ks, lam,
                      (bf16*)o, lse, D, nqt, xcd_groups);
   return hipGetLastError();
@@ -270,8 +287,13 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, cons
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const void* qs,
                            const void* ks, const float* lam, void* o, float* lse, const Dims& D,
                            hipStream_t st) {
-#define SAS_FWD_CASE(HDV, DSV) \
-  if (D.d == HDV && D.ds == DSV) return launch_fwd_t<HDV, DSV>(q, k, v, qs, ks, lam, o, lse, D, st);
+#define SAS_FWD_CASE(HDV, DSV)                                                           \
+  if (D.d == HDV && D.ds == DSV) {                                                       \
+    if (D.blk == 64) return launch_fwd_t<HDV, DSV, 1>(q, k, v, qs, ks, lam, o, lse, D, st); \
+    if (D.blk == 32) return launch_fwd_t<HDV, DSV, 2>(q, k, v, qs, ks, lam, o, lse, D, st); \
+    if (D.blk == 16) return launch_fwd_t<HDV, DSV, 4>(q, k, v, qs, ks, lam, o, lse, D, st); \
+    return hipErrorInvalidValue;                                                         \
+  }
   SAS_FWD_CASE(128, 32)
   SAS_FWD_CASE(128, 16)
   SAS_FWD_CASE(128, 64)

@@ -158,7 +158,7 @@ sas_status sas_attn_fwd(const sas_shape* shape, const void* q, const void* k, co
   if (r != SAS_OK) return r;
   if ((r = check_ptrs({q, k, v, qs, ks, gate_lse, o, lse})) != SAS_OK) return r;
   if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
-  if (shape->dtype == SAS_BF16 && D.blk != sas::kBlock) return SAS_ERR_UNSUPPORTED;
+  if (shape->dtype == SAS_BF16 && D.blk < 16) return SAS_ERR_UNSUPPORTED;  // 16, 32, 64
   if (D.batch == 0) return SAS_OK;
   hipStream_t st = (hipStream_t)stream;
   if (shape->dtype == SAS_BF16)

@@ -83,7 +83,7 @@ def fwd(lib, sh, **ptrs):
     (dict(batch=-1), 2),
     (dict(dtype=7), 3),
     (dict(sel_dtype=ops.SAS_F32), 3),  # mixed dtypes
-    (dict(block=32), 5),
+    (dict(block=8), 5),                # bf16 forward: units of 16, 32, 64
     (dict(tk=250, tq=250), 5),       # tk % 64
     (dict(d=96), 5),
     (dict(ds=24), 5),
@@ -279,14 +279,19 @@ def test_threshold_and_csr_checks(lib):
 
 def test_block_size_support(lib):
     # gate blocks of 1 .. 64 tokens (powers of two); bf16 training kernels: 64 only
-    for blk, ok in ((1, True), (16, True), (32, True), (64, True), (48, False), (128, False)):
+    for blk, ok in ((1, True), (8, True), (16, True), (32, True), (64, True), (48, False),
+                    (128, False)):
         for dt, d in ((ops.SAS_F32, 64), (ops.SAS_BF16, 128)):
             sh = shape(batch=0, block=blk, dtype=dt, d=d)
             r_gate = lib.sas_gate_scores(ctypes.byref(sh), A, A, A, None, STREAM)
             r_fwd = fwd(lib, sh)
             assert r_gate == (0 if ok else 5), (blk, dt)
-            want_fwd = 0 if ok and (dt == ops.SAS_F32 or blk == 64) else 5
+            want_fwd = 0 if ok and (dt == ops.SAS_F32 or blk >= 16) else 5
             assert r_fwd == want_fwd, (blk, dt, r_fwd)
+    # bf16 backward: 64-token blocks only
+    bw = shape(batch=0, block=32)
+    n = ctypes.c_size_t(0)
+    assert lib.sas_attn_bwd(ctypes.byref(bw), *([A] * 15), A, ctypes.byref(n), STREAM) == 5
     # CSR forward: 64-token blocks; fixed-budget sparse forward: any supported size
     n = ctypes.c_size_t(0)
     sh = shape(block=16)

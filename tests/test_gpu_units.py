@@ -140,3 +140,40 @@ def test_units_full_budget_equals_dense_f32():
     torch.cuda.synchronize()
     assert max_abs(host(o_s), host(o_d)) <= 1e-4
     assert max_abs(host(l_s), host(l_d)) <= 1e-4
+
+
+@pytest.mark.parametrize("blk", [16, 32])
+@pytest.mark.parametrize("shape", [(1024, 1024), (300, 1024), (1088, 1088)])
+def test_bf16_units_fwd(blk, shape):
+    # the bf16 MFMA forward with 2 or 4 gate units per 64-key tile
+    tq, tk = shape
+    w = W["train_8k"].with_(name="fwd_b%d" % blk, batch=2, hq=4, hkv=2, tq=tq, tk=tk, block=blk)
+    if tk % 64:
+        w = w.with_(tk=((tk + 63) // 64) * 64, tq=tq)
+    say("bf16 units fwd", blk, w.tq, w.tk)
+    cpu, dev, f = inputs(w, ("q", "k", "v", "qs", "ks"))
+    lam = ops.gate_scores(dev["qs"], dev["ks"], w.tk, block=blk)
+    o, lse = ops.attn_fwd(dev["q"], dev["k"], dev["v"], dev["qs"], dev["ks"], lam, block=blk)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn_fwd(oshape(w), f["q"], f["k"], f["v"], f["qs"], f["ks"])
+    e = max_abs(host(o), o_ref)
+    say("  O max-abs", e)
+    assert e <= 2e-2
+    assert max_abs(host(lse), l_ref) <= 1e-3
+
+
+@pytest.mark.parametrize("blk", [16, 32])
+def test_bf16_units_fwd_full_size_sampled(blk):
+    w = W["train_32k"].with_(block=blk)
+    say("bf16 units fwd 32k", blk)
+    cpu, dev, f = inputs(w, ("q", "k", "v", "qs", "ks"))
+    lam = ops.gate_scores(dev["qs"], dev["ks"], w.tk, block=blk)
+    o, lse = ops.attn_fwd(dev["q"], dev["k"], dev["v"], dev["qs"], dev["ks"], lam, block=blk)
+    torch.cuda.synchronize()
+    from gpu_common import sample_rows
+    rows = sample_rows(w, 96, seed=31)
+    o_ref, l_ref = oracle.attn_fwd(oshape(w), f["q"], f["k"], f["v"], f["qs"], f["ks"], rows=rows)
+    e = max_abs(host(o).reshape(-1, w.d)[rows], o_ref)
+    say("  O max-abs", e)
+    assert e <= 2e-2
+    assert max_abs(host(lse).reshape(-1)[rows], l_ref) <= 1e-3
