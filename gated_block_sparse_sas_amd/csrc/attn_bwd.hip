@@ -261,7 +261,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 // --------------------------------------------------------------------------
 constexpr int kDqWaves = 8, kDqThreads = 64 * kDqWaves, kDqRows = 16 * kDqWaves;
 
-template <int DS>
+// UB gate units per 64-key tile (1: 64-token blocks; 2, 4: 32, 16 tokens).
+template <int DS, int UB>
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
@@ -275,8 +276,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
   __shared__ __align__(16) bf16 K1[TE];
   __shared__ __align__(16) bf16 V0[TE];
   __shared__ __align__(16) bf16 V1[TE];
-  __shared__ __align__(16) bf16 S0[DS];
-  __shared__ __align__(16) bf16 S1[DS];
+  __shared__ __align__(16) bf16 S0[UB * DS];
+  __shared__ __align__(16) bf16 S1[UB * DS];
+  constexpr int BU = kBlock / UB;  // tokens per gate unit
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -290,7 +292,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
   const bool valid = qi < D.tq;
   const int qc = min(qi, D.tq - 1);
   const int t = D.qoff + qc;
-  const int c = t / kBlock;
+  const int c = t / BU;       // historical units of the row
+  const int ct = t / kBlock;  // the row's own 64-key tile
   const int c_lo = (D.qoff + min(wq0, D.tq - 1)) / kBlock;
   const int c_hi = (D.qoff + min(wq0 + 15, D.tq - 1)) / kBlock;
   const int c_end = (D.qoff + min(qt * kDqRows + kDqRows - 1, D.tq - 1)) / kBlock;
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
   for (int r = 0; r < kDqRows; ++r) {
     const int i = qt * kDqRows + r;
     if (i >= D.tq) break;
-    const int cr = (D.qoff + i) / kBlock;
+    const int cr = (D.qoff + i) / BU;
     float* zr = dz + (((size_t)b * D.hq + h) * D.tq + i) * D.nb;
     for (int jj = cr + tid; jj < D.nb; jj += kDqThreads) zr[jj] = 0.f;
   }
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
       kreg[x] = *(const bf16x8*)(kt + (id >> 4) * HD + (id & 15) * 8);
       vreg[x] = *(const bf16x8*)(vt + (id >> 4) * HD + (id & 15) * 8);
     }
-    if (tid < DS / 8) sreg = *(const bf16x8*)(ksb + (size_t)j * DS + tid * 8);
+    if (tid < UB * DS / 8) sreg = *(const bf16x8*)(ksb + (size_t)j * UB * DS + tid * 8);
   };
   auto sstore = [&](bf16* Kd, bf16* Vd, bf16* Sd) {
 #pragma unroll
@@ -358,24 +361,32 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
       *(bf16x8*)&Kd[trow(id >> 4) + (id & 15) * 8] = kreg[x];
       *(bf16x8*)&Vd[trow(id >> 4) + (id & 15) * 8] = vreg[x];
     }
-    if (tid < DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
+    if (tid < UB * DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
   };
 
   auto compute = [&](int j, const bf16* Ks, const bf16* Vs, const bf16* Ss) {
     if (j > c_hi) return;
-    float bias2 = 0.f;
-    float ksv[DQ];
+    float bias2[UB];
+    float ksv[UB][DQ];
 #pragma unroll
-    for (int e = 0; e < DQ; ++e) ksv[e] = to_f32(Ss[g4 * DQ + e]);
-    if (j < c_hi) {
-      float part = 0.f;
+    for (int ub = 0; ub < UB; ++ub) {
+      bias2[ub] = 0.f;
 #pragma unroll
-      for (int e = 0; e < DQ; ++e) part = fmaf(qsv[e], ksv[e], part);
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      if (j < c) bias2 = (D.sel_scale * part - lam_t) * kLog2e;
+      for (int e = 0; e < DQ; ++e) ksv[ub][e] = to_f32(Ss[ub * DS + g4 * DQ + e]);
     }
-    const float off = bias2 - l2;
+    if (UB == 1 ? j < c_hi : j <= c_hi) {
+#pragma unroll
+      for (int ub = 0; ub < UB; ++ub) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < DQ; ++e) part = fmaf(qsv[e], ksv[ub][e], part);
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (j * UB + ub < c) bias2[ub] = (D.sel_scale * part - lam_t) * kLog2e;
+      }
+    }
+    // unit of this lane's keys 16 mk + 4 g4 + r within the tile
+    auto unit = [](int mk) { return UB == 1 ? 0 : (UB == 2 ? mk / 2 : mk); };
     f32x4 sacc[4], pacc[4];
 #pragma unroll
     for (int mk = 0; mk < 4; ++mk) {
@@ -395,34 +406,58 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
 #pragma unroll
     for (int mk = 0; mk < 4; ++mk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pv[mk][r] = exp2_raw(fmaf(sacc[mk][r], c1, off));
-    if (j >= c_lo) {  // tile meets some row's block: cut keys after the row (or the block)
-      const int mlim = j < c ? kBlock : (j > c ? -1 : t - j * kBlock - 4 * g4);
+      for (int r = 0; r < 4; ++r) pv[mk][r] = exp2_raw(fmaf(sacc[mk][r], c1, bias2[unit(mk)] - l2));
+    if (j >= c_lo) {  // tile meets some row's own tile: cut keys after the row (or the tile)
+      const int mlim = j < ct ? kBlock : (j > ct ? -1 : t - j * kBlock - 4 * g4);
 #pragma unroll
       for (int mk = 0; mk < 4; ++mk)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (16 * mk + r > mlim) pv[mk][r] = 0.f;
     }
-    float dsum = 0.f;
+    float dsum[UB];
+#pragma unroll
+    for (int ub = 0; ub < UB; ++ub) dsum[ub] = 0.f;
 #pragma unroll
     for (int mk = 0; mk < 4; ++mk) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float ds = pv[mk][r] * (pacc[mk][r] - dlt);
         sacc[mk][r] = ds;
-        dsum += ds;
+        dsum[unit(mk)] += ds;
       }
     }
-    dsum += __shfl_xor(dsum, 16);
-    dsum += __shfl_xor(dsum, 32);
-    if (j == c) {
-      sdb = -dsum;  // sum_{j'<c} dbeta = - sum over the current block of dS
-    } else if (j < c) {
-      const float dzv = dsum - exp2_raw(bias2) * sdb;
-      if (valid && g4 == 0) dz[row * D.nb + j] = dzv;
 #pragma unroll
-      for (int e = 0; e < DQ; ++e) dqsa[e] = fmaf(dzv, ksv[e], dqsa[e]);
+    for (int ub = 0; ub < UB; ++ub) {
+      dsum[ub] += __shfl_xor(dsum[ub], 16);
+      dsum[ub] += __shfl_xor(dsum[ub], 32);
+    }
+    if constexpr (UB == 1) {
+      if (j == c) {
+        sdb = -dsum[0];  // sum_{j'<c} dbeta = - sum over the current block of dS
+      } else if (j < c) {
+        const float dzv = dsum[0] - exp2_raw(bias2[0]) * sdb;
+        if (valid && g4 == 0) dz[row * D.nb + j] = dzv;
+#pragma unroll
+        for (int e = 0; e < DQ; ++e) dqsa[e] = fmaf(dzv, ksv[0][e], dqsa[e]);
+      }
+    } else {
+      // the row's own tile comes first (tiles run from the diagonal down):
+      // its current unit gives sum_{j'<c} dbeta before any historical unit
+      if (j == ct) {
+#pragma unroll
+        for (int ub = 0; ub < UB; ++ub)
+          if (j * UB + ub == c) sdb = -dsum[ub];
+      }
+#pragma unroll
+      for (int ub = 0; ub < UB; ++ub) {
+        if (j * UB + ub < c) {
+          const float dzv = dsum[ub] - exp2_raw(bias2[ub]) * sdb;
+          if (valid && g4 == 0) dz[row * D.nb + j * UB + ub] = dzv;
+#pragma unroll
+          for (int e = 0; e < DQ; ++e) dqsa[e] = fmaf(dzv, ksv[ub][e], dqsa[e]);
+        }
+      }
     }
     // dQ^T += K^T dS^T over two 32-key steps; B slots: keys 32ks + 4g4 + r, +16
 #pragma unroll
@@ -727,7 +762,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // two items ahead and turns it into the row offsets of the next item after
 // its products, so no wave waits on a global load inside the loop.
 // --------------------------------------------------------------------------
-template <int DS>
+template <int DS, int UB>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse,
@@ -738,17 +773,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
   constexpr int NI = TS / 64;              // direct-load instructions per tile and tensor
   constexpr int XI = (NI + 3) / 4;         // ... per wave (at most)
   constexpr int CH = DS / 8;               // 16-byte chunks of a selector row
+  constexpr int BU = kBlock / UB;          // tokens per gate unit (UB units per 64-key tile)
   __shared__ __align__(16) bf16 Q0[TE];
   __shared__ __align__(16) bf16 Q1[TE];
   __shared__ __align__(16) bf16 O0[TE];
   __shared__ __align__(16) bf16 O1[TE];
-  __shared__ __align__(16) float F0[2 * QT];  // log2 offset of each row, then D
-  __shared__ __align__(16) float F1[2 * QT];
+  __shared__ __align__(16) float F0[(UB + 1) * QT];  // log2 offset of (unit, row), then D
+  __shared__ __align__(16) float F1[(UB + 1) * QT];
   // raw row data of the next two items (two buffers), each wave its own 8
-  // rows: qs rows, the ks row of block j for the item's selector head, and
-  // lse, lam, D
+  // rows: qs rows, the ks rows of tile j's units for the item's selector
+  // head, and lse, lam, D
   __shared__ __align__(16) bf16 RQ[2][4 * 8 * DS];
-  __shared__ __align__(16) bf16 RK[2][4 * DS];
+  __shared__ __align__(16) bf16 RK[2][4 * UB * DS];
   __shared__ __align__(16) float RS[2][4 * 32];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -841,15 +877,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     const int i0 = row0(x);
     const size_t hr = head_row(x);
     bf16* const rq = RQ[rb] + wave * 8 * DS;
-    bf16* const rk = RK[rb] + wave * DS;
+    bf16* const rk = RK[rb] + wave * UB * DS;
     float* const rs = RS[rb] + wave * 32;
     const size_t rw0 = hr + min(i0 + 8 * wave + lane / CH, D.tq - 1);
     if (lane < 8 * CH)
       __builtin_amdgcn_global_load_lds(qs + rw0 * DS + (lane % CH) * 8, rq, 16, 0, 0);
-    if (lane < CH) {
+    if (lane < UB * CH) {
       const int h = g * D.hpg + x.hl;
       __builtin_amdgcn_global_load_lds(
-          ks + (((size_t)b * D.hks + h / D.hps) * D.nb + j) * DS + lane * 8, rk, 16, 0, 0);
+          ks + (((size_t)b * D.hks + h / D.hps) * D.nb + (size_t)j * UB) * DS + lane * 8, rk, 16,
+          0, 0);
     }
     // lanes 0-7 lse, 8-15 lam, 16-23 D of the wave's rows (4 bytes per lane)
     const size_t rw = hr + min(i0 + 8 * wave + (lane & 7), D.tq - 1);
@@ -861,39 +898,45 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
       __builtin_amdgcn_global_load_lds(delta + rw, rs, 4, 0, 0);
   };
   // row data of an item from this wave's raw buffer rb (after its loads have
-  // landed): F[r] = log2 offset of row r (gate bias of block j minus the row's
-  // log-sum-exp; -inf where the block is not visible), F[QT + r] = D.  Eight
-  // lanes share a row's selector dot product.
+  // landed): F[u QT + r] = log2 offset of row r for unit u of tile j (gate
+  // bias minus the row's log-sum-exp; -inf where the unit is not visible),
+  // F[UB QT + r] = D.  Eight lanes share a row's selector dot products.
   auto rowdata = [&](Item x, int rb, float* Fd) {
     const int i0 = row0(x);
     constexpr int PE = DS / 8;  // selector dims per lane
     const int rr = lane >> 3, part = lane & 7;
     const bf16* const rq = RQ[rb] + wave * 8 * DS + rr * DS + part * PE;
-    const bf16* const rk = RK[rb] + wave * DS + part * PE;
     const float* const rs = RS[rb] + wave * 32;
-    float acc = 0.f;
+    const int r = 8 * wave + rr, i = i0 + r;
+    const int c = (D.qoff + i) / BU;
+    const float l2 = rs[rr] * kLog2e;
 #pragma unroll
-    for (int e = 0; e < PE; e += 2) {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      acc = __builtin_amdgcn_fdot2_f32_bf16(*(const bf16x2*)(rq + e), *(const bf16x2*)(rk + e),
-                                            acc, false);
+    for (int ub = 0; ub < UB; ++ub) {
+      const bf16* const rk = RK[rb] + wave * UB * DS + ub * DS + part * PE;
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < PE; e += 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        acc = __builtin_amdgcn_fdot2_f32_bf16(*(const bf16x2*)(rq + e), *(const bf16x2*)(rk + e),
+                                              acc, false);
+      }
+      acc = sum8_dpp(acc);
+      if (part == 0) {
+        const int ju = j * UB + ub;
+        float off;
+        if (i >= D.tq || ju > c)
+          off = -INFINITY;
+        else if (ju == c)
+          off = -l2;
+        else
+          off = (D.sel_scale * acc - rs[8 + rr]) * kLog2e - l2;
+        Fd[ub * QT + r] = off;
+      }
     }
-    acc = sum8_dpp(acc);
-    if (part == 0) {
-      const int r = 8 * wave + rr, i = i0 + r;
-      const int c = (D.qoff + i) / kBlock;
-      const float l2 = rs[rr] * kLog2e;
-      float off;
-      if (i >= D.tq || j > c)
-        off = -INFINITY;
-      else if (j == c)
-        off = -l2;
-      else
-        off = (D.sel_scale * acc - rs[8 + rr]) * kLog2e - l2;
-      Fd[r] = off;
-      Fd[QT + r] = rs[16 + rr];
-    }
+    if (part == 0) Fd[UB * QT + r] = rs[16 + rr];
   };
+  // the unit of this wave's 16 keys within the tile
+  const int uw = UB == 1 ? 0 : (wave * 16) / BU;
 
   auto compute = [&](Item x, const bf16* Qs, const bf16* Os, const float* Fs) {
     const int i0 = row0(x);
@@ -914,8 +957,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     }
 #pragma unroll
     for (int mq = 0; mq < 2; ++mq) {
-      const f32x4 of = *(const f32x4*)&Fs[16 * mq + 4 * g4];
-      const f32x4 dl = *(const f32x4*)&Fs[QT + 16 * mq + 4 * g4];
+      const f32x4 of = *(const f32x4*)&Fs[uw * QT + 16 * mq + 4 * g4];
+      const f32x4 dl = *(const f32x4*)&Fs[UB * QT + 16 * mq + 4 * g4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float p = exp2_raw(fmaf(sacc[mq][r], c1, of[r]));
@@ -1113,7 +1156,7 @@ hipError_t launch_dks(const float* dz, const void* qs, float* acc, void* dks, co
 template hipError_t launch_dks<float>(const float*, const void*, float*, void*, const Dims&,
                                       hipStream_t);
 
-template <int HD, int DS>
+template <int HD, int DS, int UB>
 static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o,
                                const void* dout, const float* lse, const void* qs,
                                const void* ks, const float* lam, void* dq, void* dk, void* dv,
@@ -1127,8 +1170,8 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   hipError_t e;
   if constexpr (HD == 128) {
     const int nqtw = (D.tq + kDqRows - 1) / kDqRows;
-    hipLaunchKernelGGL((bwd_dq16_kernel<DS>), dim3(D.batch * D.hq * nqtw), dim3(kDqThreads), 0,
-                       st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)o,
+    hipLaunchKernelGGL((bwd_dq16_kernel<DS, UB>), dim3(D.batch * D.hq * nqtw), dim3(kDqThreads),
+                       0, st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)o,
                        (const bf16*)dout, lse, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dq,
                        (bf16*)dqs, dzp, delta, D, nqtw, xg);
   } else {
@@ -1142,8 +1185,8 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   if (e != hipSuccess) return e;
   E.record(0, st);
   if constexpr (HD == 128) {
-    hipLaunchKernelGGL((bwd_dkdv16_kernel<DS>), dim3(groups * D.nb), dim3(256), 0, st,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
+    hipLaunchKernelGGL((bwd_dkdv16_kernel<DS, UB>), dim3(groups * (D.tk / kBlock)), dim3(256), 0,
+                       st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)delta, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dk,
                        (bf16*)dv, D, xg);
     e = hipGetLastError();
@@ -1171,17 +1214,28 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            const float* lam, void* dq, void* dk, void* dv, void* dqs, void* dks,
                            float* dz, char* ws, const BwdWs& W, const Dims& D,
                            const StageEvents& E, hipStream_t st) {
-#define SAS_BWD_CASE(HDV, DSV)                                                                  \
-  if (D.d == HDV && D.ds == DSV)                                                                \
-    return launch_bwd_t<HDV, DSV>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, dz, \
-                                  ws, W, D, E, st);
-  SAS_BWD_CASE(128, 32)
-  SAS_BWD_CASE(128, 16)
-  SAS_BWD_CASE(128, 64)
-  SAS_BWD_CASE(64, 32)
-  SAS_BWD_CASE(64, 16)
-  SAS_BWD_CASE(64, 64)
-#undef SAS_BWD_CASE
+#define SAS_BWD_CALL(HDV, DSV, UBV)                                                           \
+  return launch_bwd_t<HDV, DSV, UBV>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, \
+                                     dz, ws, W, D, E, st);
+  // d = 128: gate units of 64, 32 or 16 tokens; d = 64: 64
+#define SAS_BWD_CASE128(DSV)                        \
+  if (D.d == 128 && D.ds == DSV) {                  \
+    if (D.blk == 64) SAS_BWD_CALL(128, DSV, 1)      \
+    if (D.blk == 32) SAS_BWD_CALL(128, DSV, 2)      \
+    if (D.blk == 16) SAS_BWD_CALL(128, DSV, 4)      \
+    return hipErrorInvalidValue;                    \
+  }
+#define SAS_BWD_CASE64(DSV) \
+  if (D.d == 64 && D.ds == DSV && D.blk == 64) SAS_BWD_CALL(64, DSV, 1)
+  SAS_BWD_CASE128(32)
+  SAS_BWD_CASE128(16)
+  SAS_BWD_CASE128(64)
+  SAS_BWD_CASE64(32)
+  SAS_BWD_CASE64(16)
+  SAS_BWD_CASE64(64)
+#undef SAS_BWD_CASE128
+#undef SAS_BWD_CASE64
+#undef SAS_BWD_CALL
   return hipErrorInvalidValue;
 }
 

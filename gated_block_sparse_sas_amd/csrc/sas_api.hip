@@ -176,7 +176,9 @@ static sas_status attn_bwd_impl(const sas_shape* shape, const void* q, const voi
   if (r != SAS_OK) return r;
   if (!ws_bytes) return SAS_ERR_NULL;
   if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
-  if (shape->dtype == SAS_BF16 && D.blk != sas::kBlock) return SAS_ERR_UNSUPPORTED;
+  // bf16: units of 16, 32, 64 tokens at d = 128, 64 at d = 64
+  if (shape->dtype == SAS_BF16 && (D.d == 128 ? D.blk < 16 : D.blk != sas::kBlock))
+    return SAS_ERR_UNSUPPORTED;
   const sas::BwdWs W = sas::bwd_workspace(D, dz == nullptr);
   if (!ws) {
     *ws_bytes = W.total;

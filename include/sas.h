@@ -53,8 +53,10 @@
  *    8, 16 or 32 tokens (a unit may be a single token: NeurIPS abstract,
  *    "tokens or blocks") for sas_gate_scores, the Top-K, budget and threshold
  *    selections, sas_sparse_fwd (bf16 or f32) and, in f32 (d = 64),
- *    sas_attn_fwd / sas_attn_bwd; the bf16 training kernels and
- *    sas_sparse_fwd_csr take 64-token blocks (SAS_ERR_UNSUPPORTED otherwise).
+ *    sas_attn_fwd / sas_attn_bwd.  bf16 sas_attn_fwd takes units of 16, 32
+ *    or 64 tokens, bf16 sas_attn_bwd 16, 32 or 64 at d = 128 and 64 at
+ *    d = 64; sas_sparse_fwd_csr and the paged cache take 64
+ *    (SAS_ERR_UNSUPPORTED otherwise).
  */
 #ifndef SAS_H
 #define SAS_H

@@ -288,10 +288,12 @@ def test_block_size_support(lib):
             assert r_gate == (0 if ok else 5), (blk, dt)
             want_fwd = 0 if ok and (dt == ops.SAS_F32 or blk >= 16) else 5
             assert r_fwd == want_fwd, (blk, dt, r_fwd)
-    # bf16 backward: 64-token blocks only
-    bw = shape(batch=0, block=32)
-    n = ctypes.c_size_t(0)
-    assert lib.sas_attn_bwd(ctypes.byref(bw), *([A] * 15), A, ctypes.byref(n), STREAM) == 5
+    # bf16 backward: units of 16, 32, 64 tokens at d = 128, 64 tokens at d = 64
+    n = ctypes.c_size_t(1 << 30)
+    for blk, d, want in ((32, 128, 0), (16, 128, 0), (8, 128, 5), (32, 64, 5), (64, 64, 0)):
+        bw = shape(batch=0, block=blk, d=d)
+        assert lib.sas_attn_bwd(ctypes.byref(bw), *([A] * 15), A, ctypes.byref(n),
+                                STREAM) == want, (blk, d)
     # CSR forward: 64-token blocks; fixed-budget sparse forward: any supported size
     n = ctypes.c_size_t(0)
     sh = shape(block=16)

@@ -177,3 +177,67 @@ def test_bf16_units_fwd_full_size_sampled(blk):
     say("  O max-abs", e)
     assert e <= 2e-2
     assert max_abs(host(lse).reshape(-1)[rows], l_ref) <= 1e-3
+
+
+def _fwd_bwd_units(dev, w, blk):
+    lam = ops.gate_scores(dev["qs"], dev["ks"], w.tk, block=blk)
+    o, lse = ops.attn_fwd(dev["q"], dev["k"], dev["v"], dev["qs"], dev["ks"], lam, block=blk)
+    g = ops.attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, dev["qs"], dev["ks"], lam,
+                     block=blk)
+    torch.cuda.synchronize()
+    return g
+
+
+BWD_SMALL = {
+    "gqa_576": dict(batch=2, hq=8, hkv=2, tq=576, tk=576),
+    "q_offset": dict(batch=1, hq=4, hkv=1, tq=160, tk=1024),
+    "ragged_q": dict(batch=1, hq=4, hkv=2, tq=200, tk=448),
+    "ds64_hks": dict(batch=1, hq=4, hkv=2, hks=4, tq=320, tk=320, ds=64),
+}
+
+
+@pytest.mark.parametrize("blk", [16, 32])
+@pytest.mark.parametrize("name", list(BWD_SMALL))
+def test_bf16_units_bwd(name, blk):
+    # the bf16 MFMA backward (dq/dz/dqs and dk/dv kernels, dks) with 2 or 4 units per tile
+    w = W["train_8k"].with_(name=name, block=blk, **BWD_SMALL[name])
+    say("bf16 units bwd", name, blk)
+    cpu, dev, f = inputs(w)
+    g = _fwd_bwd_units(dev, w, blk)
+    ref = oracle.attn_bwd(oshape(w), f["q"], f["k"], f["v"], f["dout"], f["qs"], f["ks"])
+    for n in ("dq", "dk", "dv", "dz", "dqs", "dks"):
+        e = rel_l2(host(g[n]), ref[n])
+        say("  %s rel-L2 %.3e" % (n, e))
+        assert e <= 5e-2, n
+    dz = host(g["dz"])
+    c = (np.arange(w.tq) + w.tk - w.tq) // blk
+    for i in range(w.tq):
+        assert np.all(dz[:, :, i, c[i]:] == 0.0)
+
+
+@pytest.mark.parametrize("blk", [16, 32])
+def test_bf16_units_bwd_full_size_sampled(blk):
+    w = W["train_32k"].with_(block=blk)
+    say("bf16 units bwd 32k", blk)
+    cpu, dev, f = inputs(w)
+    g = _fwd_bwd_units(dev, w, blk)
+    from gpu_common import sample_rows
+    rows = sample_rows(w, 16, seed=13)
+    keys = np.array([(b * w.hkv + kh) * w.tk + u for b in range(w.batch) for kh in range(w.hkv)
+                     for u in range(w.tk - 128, w.tk, 9)], dtype=np.int64)
+    sblk = np.array([(b * w.kheads + s) * w.nb + j for b in range(w.batch)
+                     for s in range(w.kheads) for j in (w.nb - 2, w.nb - 5)], dtype=np.int64)
+    ref = oracle.attn_bwd(oshape(w), f["q"], f["k"], f["v"], f["dout"], f["qs"], f["ks"],
+                          rows=rows, keys=keys, sblocks=sblk)
+    got = {
+        "dq": host(g["dq"]).reshape(-1, w.d)[rows],
+        "dz": host(g["dz"]).reshape(-1, w.nb)[rows],
+        "dqs": host(g["dqs"]).reshape(-1, w.ds)[rows],
+        "dk": host(g["dk"]).reshape(-1, w.d)[keys],
+        "dv": host(g["dv"]).reshape(-1, w.d)[keys],
+        "dks": host(g["dks"]).reshape(-1, w.ds)[sblk],
+    }
+    for n in got:
+        e = rel_l2(got[n], ref[n])
+        say("  %s rel-L2 %.3e" % (n, e))
+        assert e <= 5e-2, n
