@@ -69,11 +69,21 @@ struct PagedKV {
   }
 };
 
+// One wavefront per (row, slot).  K and V rows are read with 16-byte loads,
+// LPK lanes per key row (a key row of d elements is LPK * 16 bytes), so one
+// load instruction covers KPI = 64 / LPK whole consecutive rows: every access
+// is a contiguous run.  A lane's partial dot product over its 16 bytes is
+// summed over the key's LPK lanes; scores go through LDS (one per key) for the
+// softmax; P V accumulates per lane over its keys and is then summed over the
+// KPI key groups.
 template <int HD, typename T, typename Src>
 __global__ __launch_bounds__(64) void sparse_pair_kernel(
     const T* __restrict__ q, Src S, const int* __restrict__ idx, const float* __restrict__ bias,
     float* __restrict__ plse, T* __restrict__ po, Dims D, int K) {
-  __shared__ float qsh[HD];
+  constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane and load
+  constexpr int LPK = HD / EPL;             // lanes per key row
+  constexpr int KPI = 64 / LPK;             // key rows per load instruction
+  typedef T vec_t __attribute__((ext_vector_type(EPL)));
   __shared__ float ps[64];
   const int lane = threadIdx.x;
   const size_t pair = blockIdx.x + (size_t)gridDim.x * blockIdx.y;
@@ -88,7 +98,7 @@ __global__ __launch_bounds__(64) void sparse_pair_kernel(
     if (lane == 0) plse[pair] = -INFINITY;
     return;
   }
-  const int B = D.blk;  // keys per block: lanes 0 .. B-1 hold one each
+  const int B = D.blk;  // keys per block
   const int c = t / B;
   const int g = h / D.hpg;
   int j;
@@ -109,37 +119,58 @@ __global__ __launch_bounds__(64) void sparse_pair_kernel(
     if (lane == 0) plse[pair] = -INFINITY;
     return;
   }
-  for (int e = lane; e < HD; e += 64) qsh[e] = to_f32(q[row * HD + e]);
-  __syncthreads();
-  const int key = j * B + lane;
-  float s = -INFINITY;
-  if (lane < B) {
-    const T* kr = S.k + boff + (size_t)lane * HD;
+  const int kl = lane / LPK;        // key of this lane within a load instruction
+  const int d0 = (lane % LPK) * EPL;  // its first column
+  float qv[EPL];
+  {
+    const vec_t x = *(const vec_t*)(q + row * HD + d0);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[e] = to_f32(x[e]);
+  }
+  const int nin = (B + KPI - 1) / KPI;  // load instructions per block
+  for (int it = 0; it < nin; ++it) {
+    const int u = it * KPI + kl;
     float a = 0.f;
-#pragma unroll 16
-    for (int e = 0; e < HD; ++e) a = fmaf(qsh[e], to_f32(kr[e]), a);
-    s = a * D.sm_scale + add;
+    if (u < B) {
+      const vec_t x = *(const vec_t*)(S.k + boff + (size_t)u * HD + d0);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a = fmaf(qv[e], to_f32(x[e]), a);
+    }
+#pragma unroll
+    for (int o = 1; o < LPK; o <<= 1) a += __shfl_xor(a, o);
+    if (lane % LPK == 0 && u < B) ps[u] = (j * B + u > t) ? -INFINITY : a * D.sm_scale + add;
   }
-  if (key > t) s = -INFINITY;
+  __builtin_amdgcn_wave_barrier();
+  const float s = lane < B ? ps[lane] : -INFINITY;
   const float m = wave_max(s);
-  const float p = (m == -INFINITY) ? 0.f : exp2f((s - m) * kLog2e);
-  const float l = wave_sum(p);
-  ps[lane] = p;
-  __syncthreads();
-  constexpr int DPL = HD / 64;  // output columns per lane
-  float acc[DPL];
+  const float pl = (m == -INFINITY) ? 0.f : exp2f((s - m) * kLog2e);
+  const float l = wave_sum(pl);
+  __builtin_amdgcn_wave_barrier();
+  if (lane < B) ps[lane] = pl;
+  __builtin_amdgcn_wave_barrier();
+  float acc[EPL];
 #pragma unroll
-  for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
-  const T* vb = S.v + boff;
-#pragma unroll 8
-  for (int u = 0; u < B; ++u) {
-    const float pu = ps[u];
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int it = 0; it < nin; ++it) {
+    const int u = it * KPI + kl;
+    if (u < B) {
+      const float pu = ps[u];
+      const vec_t x = *(const vec_t*)(S.v + boff + (size_t)u * HD + d0);
 #pragma unroll
-    for (int x = 0; x < DPL; ++x) acc[x] = fmaf(pu, to_f32(vb[(size_t)u * HD + lane * DPL + x]), acc[x]);
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pu, to_f32(x[e]), acc[e]);
+    }
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int x = 0; x < DPL; ++x) po[pair * HD + lane * DPL + x] = from_f32<T>(acc[x] * inv);
+  for (int o = LPK; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (lane < LPK) {
+    vec_t w;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) w[e] = from_f32<T>(acc[e] * inv);
+    *(vec_t*)(po + pair * HD + d0) = w;
+  }
   if (lane == 0) plse[pair] = (l > 0.f) ? m + logf(l) : -INFINITY;
 }
 
