@@ -8,23 +8,21 @@
 // Attention", "Implementation and Efficiency": attention is computed only for
 // part of the blocks.
 //
-// Pair path (decode and any shape): one wavefront per (row, slot), slot K
-// being the current block.  A lane owns one key of the block (its q.k dot
-// product over d), the wave reduces max / sum, and the lane then owns d/64
-// output columns for P V.  The partial (log-sum-exp, normalised output) goes
-// to the workspace; a combine pass merges the K+1 partials of each row by
-// their log-sum-exp.  Entries of idx that are not blocks before c(t) are
+// Row path (decode, and any shape with units below 64 tokens): one workgroup
+// per query row whose waves take the row's slots (the K listed blocks and the
+// current block) and merge their online softmax states by log-sum-exp in LDS
+// (sparse_row_kernel).  Entries of idx that are not blocks before c(t) are
 // skipped, so no out-of-range block is ever read.
 //
-// Block-stationary path (prefill, tq >= 128): selection is per token, so the
-// rows of a query tile pick nearly disjoint blocks and a per-tile union of
-// blocks would stream almost all of K/V.  Instead the (row, slot) pairs are
-// inverted into per-(batch, kv head, block) lists (count, scan, scatter);
-// one workgroup per 128-pair chunk of a list loads that block's K and V once,
-// gathers the 128 query rows and runs S^T = K Q^T and O^T = V^T P^T on the
-// MFMA units, writing a normalised partial and its log-sum-exp per pair.  The
-// merge pass (the forward kernel in sparse mode) attends each row's causal
-// current block and folds the partials in.
+// Block-stationary path (prefill, tq >= 128, 64-token blocks): selection is
+// per token, so the rows of a query tile pick nearly disjoint blocks and a
+// per-tile union of blocks would stream almost all of K/V.  Instead the
+// (row, slot) pairs are inverted into per-(batch, kv head, block) lists
+// (count, scan, scatter); a chunk of up to 128 pairs of one list (or 128
+// rows of one query block, for the current blocks) loads that block's K and
+// V once, gathers the rows and runs S^T = K Q^T and O^T = V^T P^T on the MFMA
+// units, writing a normalised partial and its log-sum-exp per pair; a merge
+// kernel folds each row's partials by log-sum-exp.
 #include "sas_device.h"
 #include "sas_internal.h"
 
@@ -69,57 +67,38 @@ struct PagedKV {
   }
 };
 
-// One wavefront per (row, slot).  K and V rows are read with 16-byte loads,
+// Row kernel (decode, and prefill with units below 64 tokens): one workgroup
+// per query row, W = min(K + 1, 16) waves; wave w takes slots w, w + W, ...
+// (slot K is the current block).  K and V rows are read with 16-byte loads,
 // LPK lanes per key row (a key row of d elements is LPK * 16 bytes), so one
-// load instruction covers KPI = 64 / LPK whole consecutive rows: every access
-// is a contiguous run.  A lane's partial dot product over its 16 bytes is
-// summed over the key's LPK lanes; scores go through LDS (one per key) for the
-// softmax; P V accumulates per lane over its keys and is then summed over the
-// KPI key groups.
+// load instruction covers KPI = 64 / LPK whole consecutive rows.  A lane's
+// partial dot product is summed over the key's LPK lanes; scores go through
+// LDS for the softmax; each wave keeps an online (max, sum, P V) over its
+// slots, and the waves' results are merged by their log-sum-exp in LDS.
+constexpr int kRowWaves = 16;
+
 template <int HD, typename T, typename Src>
-__global__ __launch_bounds__(64) void sparse_pair_kernel(
+__global__ __launch_bounds__(64 * kRowWaves) void sparse_row_kernel(
     const T* __restrict__ q, Src S, const int* __restrict__ idx, const float* __restrict__ bias,
-    float* __restrict__ plse, T* __restrict__ po, Dims D, int K) {
+    T* __restrict__ o, float* __restrict__ lse, Dims D, int K) {
   constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane and load
   constexpr int LPK = HD / EPL;             // lanes per key row
   constexpr int KPI = 64 / LPK;             // key rows per load instruction
   typedef T vec_t __attribute__((ext_vector_type(EPL)));
-  __shared__ float ps[64];
-  const int lane = threadIdx.x;
-  const size_t pair = blockIdx.x + (size_t)gridDim.x * blockIdx.y;
-  const size_t nrows = (size_t)D.batch * D.hq * D.tq;
-  if (pair >= nrows * (K + 1)) return;
-  const size_t row = pair / (K + 1);
-  const int slot = (int)(pair % (K + 1));
+  __shared__ float ps[kRowWaves][64];
+  __shared__ float ow[kRowWaves][HD];
+  __shared__ float mw[kRowWaves], lw[kRowWaves];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = blockDim.x >> 6;
+  const size_t row = blockIdx.x;
   const int h = (int)((row / D.tq) % D.hq);
   const int b = (int)(row / ((size_t)D.tq * D.hq));
   const int t = S.t_of(D, row);
-  if (t < 0) {
-    if (lane == 0) plse[pair] = -INFINITY;
-    return;
-  }
   const int B = D.blk;  // keys per block
-  const int c = t / B;
+  const int c = t < 0 ? -1 : t / B;
   const int g = h / D.hpg;
-  int j;
-  float add;
-  if (slot < K) {
-    j = idx[row * K + slot];
-    add = bias[row * K + slot];
-    if (j < 0 || j >= c) {
-      if (lane == 0) plse[pair] = -INFINITY;
-      return;
-    }
-  } else {
-    j = c;
-    add = 0.f;
-  }
-  const long long boff = S.block(D, b, g, j);
-  if (boff < 0) {
-    if (lane == 0) plse[pair] = -INFINITY;
-    return;
-  }
-  const int kl = lane / LPK;        // key of this lane within a load instruction
+  const int kl = lane / LPK;          // key of this lane within a load instruction
   const int d0 = (lane % LPK) * EPL;  // its first column
   float qv[EPL];
   {
@@ -128,93 +107,107 @@ __global__ __launch_bounds__(64) void sparse_pair_kernel(
     for (int e = 0; e < EPL; ++e) qv[e] = to_f32(x[e]);
   }
   const int nin = (B + KPI - 1) / KPI;  // load instructions per block
-  for (int it = 0; it < nin; ++it) {
-    const int u = it * KPI + kl;
-    float a = 0.f;
-    if (u < B) {
-      const vec_t x = *(const vec_t*)(S.k + boff + (size_t)u * HD + d0);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) a = fmaf(qv[e], to_f32(x[e]), a);
-    }
-#pragma unroll
-    for (int o = 1; o < LPK; o <<= 1) a += __shfl_xor(a, o);
-    if (lane % LPK == 0 && u < B) ps[u] = (j * B + u > t) ? -INFINITY : a * D.sm_scale + add;
-  }
-  __builtin_amdgcn_wave_barrier();
-  const float s = lane < B ? ps[lane] : -INFINITY;
-  const float m = wave_max(s);
-  const float pl = (m == -INFINITY) ? 0.f : exp2f((s - m) * kLog2e);
-  const float l = wave_sum(pl);
-  __builtin_amdgcn_wave_barrier();
-  if (lane < B) ps[lane] = pl;
-  __builtin_amdgcn_wave_barrier();
-  float acc[EPL];
+  float m_w = -INFINITY, l_w = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int it = 0; it < nin; ++it) {
-    const int u = it * KPI + kl;
-    if (u < B) {
-      const float pu = ps[u];
-      const vec_t x = *(const vec_t*)(S.v + boff + (size_t)u * HD + d0);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pu, to_f32(x[e]), acc[e]);
+  float* const pw = ps[wave];
+  for (int slot = wave; t >= 0 && slot <= K; slot += W) {
+    int j;
+    float add;
+    if (slot < K) {
+      j = idx[row * K + slot];
+      add = bias[row * K + slot];
+      if (j < 0 || j >= c) continue;  // not a historical block: skipped, never read
+    } else {
+      j = c;
+      add = 0.f;
     }
+    const long long boff = S.block(D, b, g, j);
+    if (boff < 0) continue;
+    for (int it = 0; it < nin; ++it) {
+      const int u = it * KPI + kl;
+      float a = 0.f;
+      if (u < B) {
+        const vec_t x = *(const vec_t*)(S.k + boff + (size_t)u * HD + d0);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a = fmaf(qv[e], to_f32(x[e]), a);
+      }
+#pragma unroll
+      for (int of = 1; of < LPK; of <<= 1) a += __shfl_xor(a, of);
+      if (lane % LPK == 0 && u < B) pw[u] = (j * B + u > t) ? -INFINITY : a * D.sm_scale + add;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const float sc = lane < B ? pw[lane] : -INFINITY;
+    const float ms = wave_max(sc);
+    if (ms == -INFINITY) continue;  // every key masked (a bias of -inf)
+    const float m_new = fmaxf(m_w, ms);
+    const float alpha = exp2f((m_w - m_new) * kLog2e);
+    const float pl = exp2f((sc - m_new) * kLog2e);
+    l_w = l_w * alpha + wave_sum(pl);
+    m_w = m_new;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < B) pw[lane] = pl;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+    for (int it = 0; it < nin; ++it) {
+      const int u = it * KPI + kl;
+      if (u < B) {
+        const float pu = pw[u];
+        const vec_t x = *(const vec_t*)(S.v + boff + (size_t)u * HD + d0);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pu, to_f32(x[e]), acc[e]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
+  // sum this wave's P V over its key groups, then merge the waves
 #pragma unroll
-  for (int o = LPK; o < 64; o <<= 1)
+  for (int of = LPK; of < 64; of <<= 1)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], of);
   if (lane < LPK) {
-    vec_t w;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) w[e] = from_f32<T>(acc[e] * inv);
-    *(vec_t*)(po + pair * HD + d0) = w;
+    for (int e = 0; e < EPL; ++e) ow[wave][d0 + e] = acc[e];
   }
-  if (lane == 0) plse[pair] = (l > 0.f) ? m + logf(l) : -INFINITY;
-}
-
-// Merge the K+1 partials of each row: L = log sum_k exp(lse_k),
-// O = sum_k exp(lse_k - L) O_k.  One wavefront per row.
-template <int HD, typename T>
-__global__ __launch_bounds__(256) void sparse_combine_kernel(const float* __restrict__ plse,
-                                                             const T* __restrict__ po,
-                                                             T* __restrict__ o,
-                                                             float* __restrict__ lse, Dims D,
-                                                             int K) {
-  const int lane = threadIdx.x & 63;
-  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const size_t nrows = (size_t)D.batch * D.hq * D.tq;
-  if (row >= nrows) return;
-  const int np = K + 1;
-  const float* pl = plse + row * np;
-  float m = -INFINITY;
-  for (int x = lane; x < np; x += 64) m = fmaxf(m, pl[x]);
-  m = wave_max(m);
-  float s = 0.f;
-  for (int x = lane; x < np; x += 64) s += exp2f((pl[x] - m) * kLog2e);
-  s = wave_sum(s);
-  if (m == -INFINITY) {  // no readable key (paged row out of range): zeros, lse -inf
-    for (int x = lane; x < HD; x += 64) o[row * HD + x] = from_f32<T>(0.f);
-    if (lse && lane == 0) lse[row] = -INFINITY;
+  if (lane == 0) {
+    mw[wave] = m_w;
+    lw[wave] = l_w;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float M = -INFINITY;
+  for (int w = 0; w < W; ++w) M = fmaxf(M, mw[w]);
+  if (M == -INFINITY) {  // no readable key: zeros, lse -inf
+    if (lane < LPK) {
+      vec_t z;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) z[e] = from_f32<T>(0.f);
+      *(vec_t*)(o + row * HD + d0) = z;
+    }
+    if (lane == 0 && lse) lse[row] = -INFINITY;
     return;
   }
-  const float L = m + logf(s);
-  constexpr int DPL = HD / 64;
-  float acc[DPL];
+  float L = 0.f, out[EPL];
 #pragma unroll
-  for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float lp = pl[p];
-    if (lp == -INFINITY) continue;
-    const float w = exp2f((lp - L) * kLog2e);
-    const T* src = po + (row * np + p) * HD + lane * DPL;
+  for (int e = 0; e < EPL; ++e) out[e] = 0.f;
+  for (int w = 0; w < W; ++w) {
+    if (mw[w] == -INFINITY) continue;
+    const float sw = exp2f((mw[w] - M) * kLog2e);
+    L += lw[w] * sw;
+    if (lane < LPK) {
 #pragma unroll
-    for (int x = 0; x < DPL; ++x) acc[x] = fmaf(w, to_f32(src[x]), acc[x]);
+      for (int e = 0; e < EPL; ++e) out[e] = fmaf(sw, ow[w][d0 + e], out[e]);
+    }
   }
+  if (lane < LPK) {
+    const float inv = 1.f / L;
+    vec_t r;
 #pragma unroll
-  for (int x = 0; x < DPL; ++x) o[row * HD + lane * DPL + x] = from_f32<T>(acc[x]);
-  if (lse && lane == 0) lse[row] = L;
+    for (int e = 0; e < EPL; ++e) r[e] = from_f32<T>(out[e] * inv);
+    *(vec_t*)(o + row * HD + d0) = r;
+  }
+  if (lane == 0 && lse) lse[row] = M + logf(L);
 }
 
 // ---------------------------------------------------------------------------
@@ -687,9 +680,7 @@ static size_t block_path_workspace(const Dims& D, size_t npairs, bool csr) {
 size_t sparse_workspace(const Dims& D, int K) {
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
   if (use_block_path(D, K)) return block_path_workspace(D, rows * K, false);
-  const size_t pairs = rows * (K + 1);
-  const size_t esz = 4;  // partial outputs are stored in the io dtype (<= 4 bytes)
-  return align256s(pairs * sizeof(float)) + align256s(pairs * D.d * esz);
+  return 256;  // the row kernel needs none
 }
 
 bool sparse_csr_supported(const Dims& D, long long nnz) {
@@ -785,24 +776,17 @@ hipError_t launch_sparse_csr(const void* q, const void* k, const void* v, const 
   return hipErrorInvalidValue;
 }
 
+static int row_waves(int K) { return K + 1 < kRowWaves ? K + 1 : kRowWaves; }
+
 template <int HD, typename T>
 static hipError_t launch_sparse_t(const void* q, const void* k, const void* v, const int* idx,
-                                  const float* bias, void* o, float* lse, char* ws, int K,
-                                  const Dims& D, const StageEvents& E, hipStream_t st) {
+                                  const float* bias, void* o, float* lse, int K, const Dims& D,
+                                  const StageEvents& E, hipStream_t st) {
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
-  const size_t pairs = rows * (K + 1);
-  float* plse = (float*)ws;
-  T* po = (T*)(ws + align256s(pairs * sizeof(float)));
-  const unsigned gx = pairs < 65536 ? (unsigned)pairs : 65536u;
-  const unsigned gy = (unsigned)((pairs + gx - 1) / gx);
-  hipLaunchKernelGGL((sparse_pair_kernel<HD, T, DenseKV<HD, T>>), dim3(gx, gy), dim3(64), 0, st,
-                     (const T*)q, DenseKV<HD, T>{(const T*)k, (const T*)v}, idx, bias, plse, po,
-                     D, K);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((sparse_row_kernel<HD, T, DenseKV<HD, T>>), dim3((unsigned)rows),
+                     dim3(64 * row_waves(K)), 0, st, (const T*)q,
+                     DenseKV<HD, T>{(const T*)k, (const T*)v}, idx, bias, (T*)o, lse, D, K);
   E.record(0, st);
-  hipLaunchKernelGGL((sparse_combine_kernel<HD, T>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
-                     0, st, (const float*)plse, (const T*)po, (T*)o, lse, D, K);
   return hipGetLastError();
 }
 
@@ -817,11 +801,11 @@ hipError_t launch_sparse(const void* q, const void* k, const void* v, const int*
     if (D.d == 64) return launch_fixed_block_path<64>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
   }
   if (D.d == 128)
-    return bf16_io ? launch_sparse_t<128, bf16>(q, k, v, idx, bias, o, lse, ws, K, D, E, st)
-                   : launch_sparse_t<128, float>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
+    return bf16_io ? launch_sparse_t<128, bf16>(q, k, v, idx, bias, o, lse, K, D, E, st)
+                   : launch_sparse_t<128, float>(q, k, v, idx, bias, o, lse, K, D, E, st);
   if (D.d == 64)
-    return bf16_io ? launch_sparse_t<64, bf16>(q, k, v, idx, bias, o, lse, ws, K, D, E, st)
-                   : launch_sparse_t<64, float>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);
+    return bf16_io ? launch_sparse_t<64, bf16>(q, k, v, idx, bias, o, lse, K, D, E, st)
+                   : launch_sparse_t<64, float>(q, k, v, idx, bias, o, lse, K, D, E, st);
   return hipErrorInvalidValue;
 }
 
@@ -830,44 +814,38 @@ hipError_t launch_sparse(const void* q, const void* k, const void* v, const int*
 template <int HD, typename T>
 static hipError_t launch_paged_t(const void* q, const void* k_pool, const void* v_pool,
                                  const int* table, const int* lens, int pages, const int* idx,
-                                 const float* bias, void* o, float* lse, char* ws, int K,
-                                 const Dims& D, hipStream_t st) {
+                                 const float* bias, void* o, float* lse, int K, const Dims& D,
+                                 hipStream_t st) {
   const size_t rows = (size_t)D.batch * D.hq;
-  const size_t pairs = rows * (K + 1);
-  float* plse = (float*)ws;
-  T* po = (T*)(ws + align256s(pairs * sizeof(float)));
-  const unsigned gx = pairs < 65536 ? (unsigned)pairs : 65536u;
-  const unsigned gy = (unsigned)((pairs + gx - 1) / gx);
-  hipLaunchKernelGGL((sparse_pair_kernel<HD, T, PagedKV<HD, T>>), dim3(gx, gy), dim3(64), 0, st,
-                     (const T*)q,
+  hipLaunchKernelGGL((sparse_row_kernel<HD, T, PagedKV<HD, T>>), dim3((unsigned)rows),
+                     dim3(64 * row_waves(K)), 0, st, (const T*)q,
                      PagedKV<HD, T>{(const T*)k_pool, (const T*)v_pool, table, lens, pages}, idx,
-                     bias, plse, po, D, K);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((sparse_combine_kernel<HD, T>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
-                     0, st, (const float*)plse, (const T*)po, (T*)o, lse, D, K);
+                     bias, (T*)o, lse, D, K);
   return hipGetLastError();
 }
 
+// The row kernel needs no workspace; the size query still answers.
 size_t paged_workspace(const Dims& D, int K) {
-  const size_t pairs = (size_t)D.batch * D.hq * (K + 1);
-  return align256s(pairs * sizeof(float)) + align256s(pairs * D.d * 4);
+  (void)D;
+  (void)K;
+  return 256;
 }
 
 hipError_t launch_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                                const int* table, const int* lens, int pages, const int* idx,
                                const float* bias, void* o, float* lse, char* ws, int K,
                                const Dims& D, bool bf16_io, hipStream_t st) {
+  (void)ws;
   if (D.d == 128)
     return bf16_io ? launch_paged_t<128, bf16>(q, k_pool, v_pool, table, lens, pages, idx, bias,
-                                               o, lse, ws, K, D, st)
+                                               o, lse, K, D, st)
                    : launch_paged_t<128, float>(q, k_pool, v_pool, table, lens, pages, idx,
-                                                bias, o, lse, ws, K, D, st);
+                                                bias, o, lse, K, D, st);
   if (D.d == 64)
     return bf16_io ? launch_paged_t<64, bf16>(q, k_pool, v_pool, table, lens, pages, idx, bias,
-                                              o, lse, ws, K, D, st)
+                                              o, lse, K, D, st)
                    : launch_paged_t<64, float>(q, k_pool, v_pool, table, lens, pages, idx, bias,
-                                               o, lse, ws, K, D, st);
+                                               o, lse, K, D, st);
   return hipErrorInvalidValue;
 }
 
