@@ -12,6 +12,7 @@ One step is one pass of the whole hot path on resident synthetic inputs:
   decode_paged_mix   decode over a block-paged cache: 32 sequences of mixed
                      lengths (64 .. 65536 tokens), top-K selection -> decode
   decode_64k_b16_top32  16-token context units: top-K (K = 32) -> sparse decode
+  prefill_32k_b16_top64 16-token context units: top-K (K = 64) -> sparse prefill
   prefill_32k_theta  dynamic-threshold selection (normalised gate >= 0.01, CSR:
                      count, host read of nnz, fill) -> sparse forward over CSR
 The headline value is the training fwd+bwd rate at 32k in TFLOP/s counting
@@ -175,6 +176,8 @@ def main():
     pg = {n: t.to(dev) for n, t in synth.draw_paged(wg).items()}
     wu = W["decode_64k_b16_top32"]
     du = {n: t.to(dev) for n, t in synth.draw_all(wu, ("q", "k", "v", "qs", "ks")).items()}
+    wv = W["prefill_32k_b16_top64"]
+    pv = {n: t.to(dev) for n, t in synth.draw_all(wv, ("q", "k", "v", "qs", "ks")).items()}
     wh = W["prefill_32k_theta"]
     ph = {n: t.to(dev) for n, t in synth.draw_all(wh, ("q", "k", "v", "qs", "ks")).items()}
     torch.cuda.synchronize()
@@ -199,11 +202,14 @@ def main():
     nnz_seen = []
     sh_u = ops.make_shape(wu.batch, wu.hq, wu.hkv, wu.tq, wu.tk, wu.d, wu.ds, wu.block, wu.hkv)
     ws_u = torch.empty(ops.sparse_workspace_bytes(sh_u, wu.topk), dtype=torch.uint8, device=dev)
+    sh_v = ops.make_shape(wv.batch, wv.hq, wv.hkv, wv.tq, wv.tk, wv.d, wv.ds, wv.block, wv.hkv)
+    ws_v = torch.empty(ops.sparse_workspace_bytes(sh_v, wv.topk), dtype=torch.uint8, device=dev)
 
     names = ["start", "gate", "fwd", "bwd_dq", "bwd_dkdv", "bwd_dks", "bwd", "pf_topk",
              "pf_partial", "pf_sparse", "dc_topk", "dc_partial", "dc_sparse", "pq_topk",
              "pq_partial", "pq_sparse", "pg_topk", "pg_decode", "th_start", "th_count",
-             "th_fill0", "th_fill", "th_partial", "th_sparse", "u_topk", "u_sparse"]
+             "th_fill0", "th_fill", "th_partial", "th_sparse", "u_topk", "u_sparse",
+             "v_topk", "v_sparse"]
 
     def step(ev):
         E = {n: ev[n] for n in names}
@@ -250,6 +256,10 @@ def main():
         E["u_topk"].record()
         ops.sparse_fwd(du["q"], du["k"], du["v"], idx, bias, block=wu.block, ws=ws_u)
         E["u_sparse"].record()
+        idx, bias = ops.topk_blocks(pv["qs"], pv["ks"], wv.topk, wv.tk, block=wv.block)
+        E["v_topk"].record()
+        ops.sparse_fwd(pv["q"], pv["k"], pv["v"], idx, bias, block=wv.block, ws=ws_v)
+        E["v_sparse"].record()
 
     def new_events():
         return {n: torch.cuda.Event(enable_timing=True) for n in names}
@@ -290,8 +300,10 @@ def main():
         "theta_sparse": dur("th_fill", "th_sparse"),
         "units_topk": dur("th_sparse", "u_topk"),
         "units_decode": dur("u_topk", "u_sparse"),
+        "units_prefill_topk": dur("u_sparse", "v_topk"),
+        "units_prefill": dur("v_topk", "v_sparse"),
     }
-    step_ms = dur("start", "u_sparse")
+    step_ms = dur("start", "v_sparse")
 
     pairs_t = wt.batch * wt.hq * causal_pairs(wt.tq, wt.tk)
     fl_fwd = 4.0 * wt.d * pairs_t
@@ -319,6 +331,8 @@ def main():
     h_tflops = 4.0 * wh.d * pairs_h / (part["theta_sparse"] * 1e-3) / 1e12
     u_bytes = wu.batch * wu.hq * (min(wu.topk, (wu.tk - 1) // wu.block) + 1) * 2 * wu.block * wu.d * 2
     u_gbps = u_bytes / (part["units_decode"] * 1e-3) / 1e9
+    pairs_v = wv.batch * wv.hq * sparse_pairs(wv)
+    v_tflops = 4.0 * wv.d * pairs_v / (part["units_prefill"] * 1e-3) / 1e12
 
     # dominant kernel: the key-stationary backward kernel (dK, dV): S, dP, dV
     # and dK over every attended pair = 8*d flop per pair
@@ -358,7 +372,8 @@ def main():
                    "seq_len": wt.tq, "d": wt.d, "block": wt.block, "ds": wt.ds,
                    "also_in_step": ["prefill_32k_top16", "decode_64k_top8",
                                     "prefill_32k_top25pct", "decode_paged_mix",
-                                    "prefill_32k_theta", "decode_64k_b16_top32"]},
+                                    "prefill_32k_theta", "decode_64k_b16_top32",
+                                    "prefill_32k_b16_top64"]},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "train_ms": round(t_train, 3),
         "parts_ms": {k: round(v, 4) for k, v in part.items()},
@@ -393,6 +408,10 @@ def main():
                            "ms": round(part["units_decode"], 4),
                            "topk_ms": round(part["units_topk"], 4), "kv_bytes": u_bytes,
                            "GBps": round(u_gbps, 1), "frac_hbm": round(u_gbps / PEAK_HBM_GBPS, 4)},
+        "prefill_units16": {"workload": "prefill_32k_b16_top64", "block": wv.block,
+                            "ms": round(part["units_prefill"], 3),
+                            "topk_ms": round(part["units_prefill_topk"], 3),
+                            "tflops": round(v_tflops, 2), "attended_pairs": pairs_v},
         "roofline": roofline,
         "wall_s_timed": round(wall, 3),
     }

@@ -280,7 +280,7 @@ __device__ __forceinline__ int listed_block(const Src& S, const Dims& D, int bh,
   const long long row = S.row_of(p);
   if (row < 0 || row / D.tq != bh) return -1;
   const int j = S.j_of(p);
-  const int c = (D.qoff + (int)(row % D.tq)) / kBlock;
+  const int c = (D.qoff + (int)(row % D.tq)) / D.blk;
   return (j >= 0 && j < c) ? j : -1;
 }
 
@@ -425,9 +425,11 @@ __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
   if (ch0 >= total) return;
   const int ch1 = min(total, ch0 + kChunksPerWG);
   const float c1 = D.sm_scale * kLog2e;
-  const int qb0 = D.qoff / kBlock;  // first block holding a query row
+  const int B = D.blk;              // keys per gate unit (a 64-key tile holds 64 / B)
+  const int qb0 = D.qoff / B;       // first unit holding a query row
+  const int ntl = D.tk / kBlock;    // 64-key tiles per (batch, kv head)
   const int pi = wave * 32 + l32;   // this lane's pair within a chunk
-  int cur = -1;
+  int cur = -1;                     // tile staged in LDS
   for (int ch = ch0; ch < ch1; ++ch) {
     int kv, tmax, pos;  // pos: where the partial goes (chunk order)
     size_t row;
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
       const int bg = db / nqb, j = qb0 + db % nqb;
       kv = bg * D.nb + j;
       const int p = dc * kChunk + pi;
-      const int hl = p / kBlock, tok = j * kBlock + p % kBlock;
+      const int hl = p / B, tok = j * B + p % B;
       valid = hl < D.hpg && tok >= D.qoff && tok < D.tk;
       const int b = bg / D.hkv, g = bg - b * D.hkv;
       const int h = g * D.hpg + (valid ? hl : 0);
@@ -463,11 +465,13 @@ __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(q + row * HD + 16 * s + 8 * hh);
     kv = __builtin_amdgcn_readfirstlane(kv);
-    if (kv != cur) {
-      __syncthreads();  // every wave is done with the previous block
-      const int j = kv % D.nb, bg = kv / D.nb;
-      const bf16* kb = k + ((size_t)bg * D.tk + (size_t)j * kBlock) * HD;
-      const bf16* vb = v + ((size_t)bg * D.tk + (size_t)j * kBlock) * HD;
+    const int ulo = (kv % D.nb) * B;  // the unit's keys ulo .. ulo + B - 1
+    const int tile = (kv / D.nb) * ntl + ulo / kBlock;
+    if (tile != cur) {
+      __syncthreads();  // every wave is done with the previous tile
+      const int jt = tile % ntl, bg = tile / ntl;
+      const bf16* kb = k + ((size_t)bg * D.tk + (size_t)jt * kBlock) * HD;
+      const bf16* vb = v + ((size_t)bg * D.tk + (size_t)jt * kBlock) * HD;
       for (int x = tid; x < kBlock * HD / 8; x += 256) {
         const int r = x / (HD / 8), cc = x % (HD / 8);
         *(bf16x8*)&Ks[r * KP + cc * 8] = *(const bf16x8*)(kb + (size_t)r * HD + cc * 8);
@@ -485,11 +489,11 @@ __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
         }
       }
       __syncthreads();
-      cur = kv;
+      cur = tile;
     }
     if (!__any(valid)) continue;  // wave-uniform: no pair of this chunk for this wave
     const float bias2 = bv * kLog2e;
-    const int u0 = (kv % D.nb) * kBlock;
+    const int u0 = (ulo / kBlock) * kBlock;  // first key of the staged tile
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int u = u0 + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
-        if (u > tmax) sacc[mt][r] = -INFINITY;
+        if (u > tmax || u < ulo || u >= ulo + B) sacc[mt][r] = -INFINITY;  // causal, unit
         mx = fmaxf(mx, sacc[mt][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -588,12 +592,12 @@ __global__ __launch_bounds__(256) void sp_merge_kernel(Src S, const int* __restr
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const size_t nrows = (size_t)D.batch * D.hq * D.tq;
   if (row >= nrows) return;
-  const int i = (int)(row % D.tq), t = D.qoff + i, c = t / kBlock;
+  const int i = (int)(row % D.tq), t = D.qoff + i, c = t / D.blk;
   const int h = (int)((row / D.tq) % D.hq), b = (int)(row / ((size_t)D.tq * D.hq));
   const int g = h / D.hpg, hl = h - g * D.hpg;
   // chunk-order position of the current block's partial and of the listed ones
-  const int dpos = ((b * D.hkv + g) * nqb + (c - D.qoff / kBlock)) * dcpb * kChunk +
-                   hl * kBlock + t % kBlock;
+  const int dpos = ((b * D.hkv + g) * nqb + (c - D.qoff / D.blk)) * dcpb * kChunk +
+                   hl * D.blk + t % D.blk;
   const int hbase = D.batch * D.hkv * nqb * dcpb * kChunk;
   const size_t a0 = S.seg_lo(row);
   const int len = (int)(S.seg_hi(row) - a0);
@@ -649,20 +653,22 @@ __global__ __launch_bounds__(256) void sp_merge_kernel(Src S, const int* __restr
   if (lane == 0 && lse) lse[row] = (m + log2f(sm)) * kLn2;
 }
 
-static int diag_chunks_per_block(const Dims& D) { return (D.hpg * kBlock + kChunk - 1) / kChunk; }
-static int query_blocks(const Dims& D) { return D.nb - D.qoff / kBlock; }
+static int diag_chunks_per_block(const Dims& D) { return (D.hpg * D.blk + kChunk - 1) / kChunk; }
+static int query_blocks(const Dims& D) { return D.nb - D.qoff / D.blk; }
 // Partial slots of the block path: current-block chunks, then one per pair.
 static size_t block_path_slots(const Dims& D, size_t npairs) {
   return (size_t)D.batch * D.hkv * query_blocks(D) * diag_chunks_per_block(D) * kChunk + npairs;
 }
 
-// The block path works on 64-key gate blocks (one LDS tile each), histograms
-// blocks in LDS: nb <= 8192 (64 KB for the fill); partial positions are int.
+// The block path stages the 64-key tile that holds a gate unit (keys outside
+// the unit masked), histograms units in LDS: nb <= 8192 (64 KB for the
+// fill); partial positions are int.
 static bool block_path_fits(const Dims& D, size_t npairs) {
-  return D.blk == kBlock && D.nb <= 8192 && block_path_slots(D, npairs) < ((size_t)1 << 31);
+  return D.nb <= 8192 && block_path_slots(D, npairs) < ((size_t)1 << 31);
 }
+// units below 16 tokens would waste most of each 64-key tile: the row path
 static bool use_block_path(const Dims& D, int K) {
-  return D.tq >= 128 && block_path_fits(D, (size_t)D.batch * D.hq * D.tq * K);
+  return D.tq >= 128 && D.blk >= 16 && block_path_fits(D, (size_t)D.batch * D.hq * D.tq * K);
 }
 
 // Block path workspace: [count | cursor | start | cstart | cbk | list | inv |

@@ -92,6 +92,9 @@ WORKLOADS = {
                                 "decode", topk=8, scales=_HALF),
     "prefill_32k_top25pct": Workload("prefill_32k_top25pct", 6, 1, 32, 8, 32768, 32768, 128, 32,
                                      64, "bf16", "prefill", topk=128, frac=0.25, scales=_HALF),
+    # 16-token context units at prefill: 64 units = the 1024-token budget of K = 16 x 64
+    "prefill_32k_b16_top64": Workload("prefill_32k_b16_top64", 10, 1, 32, 8, 32768, 32768, 128,
+                                      32, 16, "bf16", "prefill", topk=64, scales=_HALF),
     # 16-token context units at decode: 32 units = the 512-token budget of K = 8 x 64
     "decode_64k_b16_top32": Workload("decode_64k_b16_top32", 9, 16, 32, 8, 1, 65536, 128, 32,
                                      16, "bf16", "decode", topk=32, scales=_HALF),

@@ -55,8 +55,7 @@
  *    selections, sas_sparse_fwd (bf16 or f32) and, in f32 (d = 64),
  *    sas_attn_fwd / sas_attn_bwd.  bf16 sas_attn_fwd takes units of 16, 32
  *    or 64 tokens, bf16 sas_attn_bwd 16, 32 or 64 at d = 128 and 64 at
- *    d = 64; sas_sparse_fwd_csr and the paged cache take 64
- *    (SAS_ERR_UNSUPPORTED otherwise).
+ *    d = 64; the paged cache takes 64 (SAS_ERR_UNSUPPORTED otherwise).
  */
 #ifndef SAS_H
 #define SAS_H

@@ -241,3 +241,37 @@ def test_bf16_units_bwd_full_size_sampled(blk):
         e = rel_l2(got[n], ref[n])
         say("  %s rel-L2 %.3e" % (n, e))
         assert e <= 5e-2, n
+
+
+@pytest.mark.parametrize("blk", [16, 32])
+def test_units_csr_and_full_budget_bf16(blk):
+    # block-stationary path at 16 / 32-token units: a threshold (CSR) selection
+    # against the oracle, and K covering every unit == the dense forward
+    w = W["prefill_32k_top16"].with_(batch=1, hq=4, hkv=2, tq=640, tk=1024, block=blk)
+    cpu, dev, f = inputs(w, ("q", "k", "v", "qs", "ks"))
+    S = oshape(w)
+    rows = w.batch * w.hq * w.tq
+    rp, col, tb = ops.threshold_blocks(dev["qs"], dev["ks"], 0.01, w.tk, block=blk)
+    o, lse = ops.sparse_fwd_csr(dev["q"], dev["k"], dev["v"], rp, col, tb, block=blk)
+    torch.cuda.synchronize()
+    rph, colh, tbh = rp.cpu().numpy(), col.cpu().numpy(), tb.cpu().numpy()
+    width = max(1, int(np.diff(rph).max()))
+    pi = np.full((rows, width), -1, dtype=np.int32)
+    pb = np.full((rows, width), -np.inf)
+    for r in range(rows):
+        n = rph[r + 1] - rph[r]
+        pi[r, :n] = colh[rph[r]:rph[r + 1]]
+        pb[r, :n] = tbh[rph[r]:rph[r + 1]]
+    o_ref, l_ref = oracle.sparse_fwd(S, width, f["q"], f["k"], f["v"], pi, pb)
+    e = max_abs(host(o).reshape(rows, -1), o_ref.reshape(rows, -1))
+    say("  csr O max-abs", e, "nnz", len(colh))
+    assert e <= 2e-2
+    assert max_abs(host(lse).reshape(-1), l_ref.reshape(-1)) <= 1e-3
+    K = w.tk // blk
+    idx, bias = ops.topk_blocks(dev["qs"], dev["ks"], K, w.tk, block=blk)
+    o_s, l_s = ops.sparse_fwd(dev["q"], dev["k"], dev["v"], idx, bias, block=blk)
+    lam = ops.gate_scores(dev["qs"], dev["ks"], w.tk, block=blk)
+    o_d, l_d = ops.attn_fwd(dev["q"], dev["k"], dev["v"], dev["qs"], dev["ks"], lam, block=blk)
+    torch.cuda.synchronize()
+    assert max_abs(host(o_s), host(o_d)) <= 2e-2
+    assert max_abs(host(l_s), host(l_d)) <= 1e-3
