@@ -13,7 +13,6 @@
 #include "sas_device.h"
 #include "sas_internal.h"
 
-#include <type_traits>
 
 namespace sas {
 
@@ -29,30 +28,9 @@ __global__ __launch_bounds__(256) void gate_lse_kernel(const ST* __restrict__ qs
   const int c = (D.qoff + ic) / D.blk;
   const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / D.blk;  // wave max of c
   const size_t row = ((size_t)b * D.hq + h) * D.tq + ic;
-  // bf16 scores use packed bf16 dot products (products exact in fp32)
-  constexpr bool PACKED = std::is_same<ST, bf16>::value;
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  float qsv[PACKED ? 1 : DS];
-  bf16x2 qs2[PACKED ? DS / 2 : 1];
-  if constexpr (PACKED) {
-#pragma unroll
-    for (int e = 0; e < DS / 2; ++e) qs2[e] = *(const bf16x2*)(qs + row * DS + 2 * e);
-  } else {
-#pragma unroll
-    for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
-  }
+  SelQ<DS, ST> qsv;  // bf16 rows: packed bf16 dot products
+  qsv.load(qs + row * DS);
   const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
-  auto dot = [&](const ST* kr) {
-    if constexpr (PACKED) {
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < DS / 2; ++e)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(qs2[e], *(const bf16x2*)(kr + 2 * e), acc, false);
-      return acc;
-    } else {
-      return sel_dot<DS>(qsv, kr);
-    }
-  };
   const float zs = D.sel_scale * kLog2e;  // scores kept in log2 units
   float m = -INFINITY, s = 0.f;
   for (int j0 = 0; j0 < cw; j0 += 8) {
@@ -62,7 +40,7 @@ __global__ __launch_bounds__(256) void gate_lse_kernel(const ST* __restrict__ qs
       const int j = j0 + k;
       zz[k] = -INFINITY;
       if (j < cw) {
-        const float z = zs * dot(ksb + (size_t)j * DS);
+        const float z = zs * qsv.dot(ksb + (size_t)j * DS);
         if (j < c) zz[k] = z;
       }
     }
@@ -95,11 +73,10 @@ __global__ __launch_bounds__(256) void gate_bias_kernel(const ST* __restrict__ q
   const int c = (D.qoff + i) / D.blk;
   float out;
   if (j < c) {
-    float qsv[DS];
-#pragma unroll
-    for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
+    SelQ<DS, ST> qsv;
+    qsv.load(qs + row * DS);
     const ST* ksr = ks + (((size_t)b * D.hks + h / D.hps) * D.nb + j) * DS;
-    out = D.sel_scale * sel_dot<DS>(qsv, ksr) - lam[row];
+    out = D.sel_scale * qsv.dot(ksr) - lam[row];
   } else {
     out = j == c ? 0.f : -INFINITY;
   }

@@ -111,9 +111,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Selector score dot product <qs, ks> over ds elements, accumulated in fp32
-// in index order with fused multiply-adds (the top-K kernels rank with it;
-// other kernels may use packed bf16 dot products, which differ only in
-// rounding).
+// in index order with fused multiply-adds.
 template <int DS, typename ST>
 __device__ __forceinline__ float sel_dot(const float* qsv, const ST* ksrow) {
   float acc = 0.f;
@@ -121,6 +119,37 @@ __device__ __forceinline__ float sel_dot(const float* qsv, const ST* ksrow) {
   for (int e = 0; e < DS; ++e) acc = fmaf(qsv[e], to_f32(ksrow[e]), acc);
   return acc;
 }
+
+// A query's selector row held in registers for scoring many ks rows: bf16
+// rows as bf16 pairs, scored with packed bf16 dot products (each pair of
+// products exact, the chain summed in fp32 in index order); f32 rows with
+// sel_dot.  The gate, threshold and top-K kernels all score with it, so a
+// block's score is the same number whichever of them computes it.
+template <int DS, typename ST>
+struct SelQ {
+  float v[DS];
+  __device__ __forceinline__ void load(const ST* p) {
+#pragma unroll
+    for (int e = 0; e < DS; ++e) v[e] = to_f32(p[e]);
+  }
+  __device__ __forceinline__ float dot(const ST* kr) const { return sel_dot<DS>(v, kr); }
+};
+template <int DS>
+struct SelQ<DS, bf16> {
+  typedef __bf16 pair_t __attribute__((ext_vector_type(2)));
+  pair_t v[DS / 2];
+  __device__ __forceinline__ void load(const bf16* p) {
+#pragma unroll
+    for (int e = 0; e < DS / 2; ++e) v[e] = *(const pair_t*)(p + 2 * e);
+  }
+  __device__ __forceinline__ float dot(const bf16* kr) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < DS / 2; ++e)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(v[e], *(const pair_t*)(kr + 2 * e), acc, false);
+    return acc;
+  }
+};
 
 // Query-tile scheduling for the causal kernels.  Tiles are issued longest
 // first (the last query tile attends the most keys).  When the (batch, kv

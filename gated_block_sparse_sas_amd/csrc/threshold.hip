@@ -24,7 +24,6 @@
 #include "sas_internal.h"
 
 #include <algorithm>
-#include <type_traits>
 
 namespace sas {
 
@@ -44,31 +43,12 @@ __global__ __launch_bounds__(256) void thr_kernel(const ST* __restrict__ qs,
   const int c = active ? (D.qoff + ic) / D.blk : 0;
   const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / D.blk;  // wave max of c
   const size_t row = ((size_t)b * D.hq + h) * D.tq + ic;
-  // bf16 scores use packed bf16 dot products (products exact in fp32)
-  constexpr bool PACKED = std::is_same<ST, bf16>::value;
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  float qsv[PACKED ? 1 : DS];
-  bf16x2 qs2[PACKED ? DS / 2 : 1];
-  if constexpr (PACKED) {
-#pragma unroll
-    for (int e = 0; e < DS / 2; ++e) qs2[e] = *(const bf16x2*)(qs + row * DS + 2 * e);
-  } else {
-#pragma unroll
-    for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
-  }
+  SelQ<DS, ST> qsv;  // bf16 rows: packed bf16 dot products
+  qsv.load(qs + row * DS);
   const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
   const float zs = D.sel_scale * kLog2e;  // scores in log2 units
   auto z2 = [&](int j) __attribute__((always_inline)) {
-    const ST* kr = ksb + (size_t)j * DS;
-    float acc = 0.f;
-    if constexpr (PACKED) {
-#pragma unroll
-      for (int e = 0; e < DS / 2; ++e)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(qs2[e], *(const bf16x2*)(kr + 2 * e), acc, false);
-    } else {
-      acc = sel_dot<DS>(qsv, kr);
-    }
-    return zs * acc;
+    return zs * qsv.dot(ksb + (size_t)j * DS);
   };
   // lam2 = m + log2 sum 2^(z2 - m) over j < c, online in chunks of 8 blocks
   float m = -INFINITY, s = 0.f;

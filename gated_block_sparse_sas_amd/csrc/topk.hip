@@ -12,8 +12,8 @@
 // (lane j % 64 owns block j), lam comes from a wave max + sum, then K rounds
 // each pick the best remaining block with a 64-lane argmax on (z, -j): round
 // r takes the best candidate strictly after round r-1's winner in that total
-// order, so no "already taken" set is needed.  Scores use the same fp32 dot
-// product routine as the gate kernel.
+// order, so no "already taken" set is needed.  Scores use the selector dot
+// product of the gate kernel (SelQ: packed bf16 products for bf16 inputs).
 #include "sas_device.h"
 #include "sas_internal.h"
 
@@ -75,13 +75,12 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const ST* __restrict__ q
     const int h = (int)((row / D.tq) % D.hq);
     const int b = (int)(row / ((size_t)D.tq * D.hq));
     const int c = S.hist(D, row);
-    float qsv[DS];
-#pragma unroll
-    for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
+    SelQ<DS, ST> qsv;
+    qsv.load(qs + row * DS);
     float m = -INFINITY;
     for (int j = lane; j < c; j += 64) {
       const ST* kr = S.ks_row(D, b, h, j);
-      const float z = kr ? D.sel_scale * sel_dot<DS>(qsv, kr) : -INFINITY;
+      const float z = kr ? D.sel_scale * qsv.dot(kr) : -INFINITY;
       zc[j] = z;
       m = fmaxf(m, z);
     }
@@ -153,7 +152,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const ST* __restrict__ q
 // wave-uniform load.  Each lane keeps its best KMAX (>= K) blocks sorted in
 // registers; blocks arrive in ascending order and enter only when strictly
 // better than the current last entry, which reproduces the (z desc, j asc)
-// order of the wave-per-row kernel.  Scores use the same sel_dot routine.
+// order of the wave-per-row kernel.  Scores use the same SelQ dot product.
 template <int DS, typename ST, int KMAX>
 __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ qs,
                                                         const ST* __restrict__ ks, int K,
@@ -167,9 +166,8 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
   const int c = (D.qoff + ic) / D.blk;
   const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / D.blk;  // wave max of c
   const size_t row = ((size_t)b * D.hq + h) * D.tq + ic;
-  float qsv[DS];
-#pragma unroll
-  for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
+  SelQ<DS, ST> qsv;
+  qsv.load(qs + row * DS);
   const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
   float tz[KMAX];
   int tj[KMAX];
@@ -184,7 +182,7 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int j = j0 + kk;
-      zz[kk] = (j < cw) ? D.sel_scale * sel_dot<DS>(qsv, ksb + (size_t)j * DS) : -INFINITY;
+      zz[kk] = (j < cw) ? D.sel_scale * qsv.dot(ksb + (size_t)j * DS) : -INFINITY;
       if (j >= c) zz[kk] = -INFINITY;
     }
     float mc = zz[0];
@@ -240,7 +238,7 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
 
 // Budgeted / large-K variant: one wavefront per query row keeps the
 // n_t = min(kmax, c(t), ceil(frac c(t))) best blocks (frac <= 0: no
-// fraction).  Scores go to LDS (same fp32 dot product as above) and become
+// fraction).  Scores go to LDS (same SelQ dot product as above) and become
 // order-preserving 32-bit keys; a 4-pass radix select (8 bits per pass,
 // LDS histogram) finds the n_t-th largest key, ties at it are taken in block
 // order; the n_t winners are then sorted (bitonic network in LDS) by key
@@ -277,13 +275,12 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
   int n = min(kmax, c);
   if (frac > 0.f) n = min(n, (int)ceil((double)frac * (double)c));
   // scores and the gate normaliser over the whole history
-  float qsv[DS];
-#pragma unroll
-  for (int e = 0; e < DS; ++e) qsv[e] = to_f32(qs[row * DS + e]);
+  SelQ<DS, ST> qsv;
+  qsv.load(qs + row * DS);
   const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
   float m = -INFINITY;
   for (int j = lane; j < c; j += 64) {
-    const float z = D.sel_scale * sel_dot<DS>(qsv, ksb + (size_t)j * DS);
+    const float z = D.sel_scale * qsv.dot(ksb + (size_t)j * DS);
     zc[j] = z;
     m = fmaxf(m, z);
   }
