@@ -760,7 +760,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // trow() so that both kinds of read hit disjoint banks.  Each wave also loads
 // the raw per-row data (qs, the block's ks row, lse, lam, D) of its 8 rows
 // two items ahead and turns it into the row offsets of the next item after
-// its products, so no wave waits on a global load inside the loop.
+// its products, so no wave waits on a global load inside the loop.  In the
+// S / dP products each 16-byte operand read is issued one product ahead (two
+// operand registers in turn: the register budget of three waves per SIMD
+// leaves no room for more), and a wave raises its issue priority while it
+// runs its matrix products so that the other waves of the SIMD fill the gaps
+// with their exponentials.
 // --------------------------------------------------------------------------
 template <int DS, int UB>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
@@ -946,15 +951,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     const int mlim = D.qoff + i0 < key0 + 15 ? key - (D.qoff + i0 + 4 * g4) : -1;
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
     f32x4 pacc[2] = {f32x4{}, f32x4{}};
+    __builtin_amdgcn_s_setprio(1);
+    // operand i (step i / 4, M-tile (i / 2) % 2, Q or dO by i % 2) is read
+    // while product i - 1 runs: two operand registers in turn
+    auto opnd = [&](int i) __attribute__((always_inline)) {
+      const int o = trow(i16) + 2304 * ((i >> 1) & 1) + 32 * (i >> 2) + 8 * g4;
+      return *(const bf16x8*)&((i & 1) ? Os : Qs)[o];
+    };
+    bf16x8 ob[2];
+    ob[0] = opnd(0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int mq = 0; mq < 2; ++mq) {
-        const int o = trow(i16) + 2304 * mq + 32 * s + 8 * g4;
-        sacc[mq] = mfma16(*(const bf16x8*)&Qs[o], kf[s], sacc[mq]);
-        pacc[mq] = mfma16(*(const bf16x8*)&Os[o], vf[s], pacc[mq]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      if (i < 15) ob[(i + 1) & 1] = opnd(i + 1);
+      const int s = i >> 2, mq = (i >> 1) & 1;
+      if (i & 1)
+        pacc[mq] = mfma16(ob[i & 1], vf[s], pacc[mq]);
+      else
+        sacc[mq] = mfma16(ob[i & 1], kf[s], sacc[mq]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 15; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int mq = 0; mq < 2; ++mq) {
       const f32x4 of = *(const f32x4*)&Fs[uw * QT + 16 * mq + 4 * g4];
@@ -977,6 +999,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
       sb[4 + r] = (bf16)pacc[1][r];
     }
     const int t0 = trow(4 * g4 + k4) + 4 * a4, t1 = t0 + 2304;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dm = 0; dm < 8; ++dm) {
       const bf16x4 olo = ds_read_tr(&Os[t0 + 16 * dm]);
@@ -986,6 +1009,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
       const bf16x4 qhi = ds_read_tr(&Qs[t1 + 16 * dm]);
       dka[dm] = mfma16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), sb, dka[dm]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   if (nitems > 0) {
