@@ -22,10 +22,14 @@
 //  * O^T = V^T P^T: P never leaves registers.  The B-operand k slots of a lane
 //    are exactly the keys its S^T accumulator holds (two runs of 4), and the
 //    V^T operand is read from LDS with the same key order.
-//  * LDS: K and V tiles row-major, double-buffered; the next tile is loaded
-//    into registers at the start of a tile and stored to LDS at its end (one
-//    barrier per tile); V^T operands come from transposing LDS reads.  A
-//    72-dword row pitch keeps both kinds of operand read bank-conflict free.
+//  * LDS: K and V tiles row-major (K in two buffers, V in three); the next
+//    tile is loaded into registers at the start of a tile and stored to LDS
+//    at its end (one barrier per tile); V^T operands come from transposing
+//    LDS reads.  A 72-dword row pitch keeps both kinds of operand read
+//    bank-conflict free.
+//  * the two waves of a SIMD come from different halves of the workgroup,
+//    and the second half runs each tile's PV product one tile late, so that
+//    one wave's softmax overlaps the other's matrix products.
 //  * the gate bias of (row, tile) is recomputed in-kernel: the lane's half of
 //    qs (ds/2 values in registers) times the block's ks row (staged in LDS
 //    with the tile), one cross-half add; lam comes from the gate kernel.
@@ -55,8 +59,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   constexpr int KS = HD / 16;      // k-steps over the head dim
   constexpr int DM = HD / 32;      // 32-row M-tiles of O^T
   constexpr int BU = kBlock / UB;  // tokens per gate unit
-  // Key tiles are double-buffered in LDS, K and V row-major (V read
-  // transposed, as the V^T operand, by transposing 8-byte reads).  The next
+  // Key tiles in LDS, K and V row-major (V read transposed, as the V^T
+  // operand, by transposing 8-byte reads); K in two buffers, V in three
+  // (the PV products of half the waves run one tile late).  The next
   // tile goes global -> registers at the start of a tile and registers ->
   // LDS at its end: the LDS operand reads then never wait behind an
   // outstanding global -> LDS transfer.
@@ -64,6 +69,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   __shared__ __align__(16) bf16 K1[kBlock * KP];
   __shared__ __align__(16) bf16 V0[kBlock * VP];
   __shared__ __align__(16) bf16 V1[kBlock * VP];
+  __shared__ __align__(16) bf16 V2[kBlock * VP];
   __shared__ __align__(16) bf16 S0[UB * DS];  // ks rows of the tile's units
   __shared__ __align__(16) bf16 S1[UB * DS];
 
@@ -132,9 +138,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   // group points at key row 4 hh + k, columns 16 ((lane >> 4) & 1) + 4 a
   const int vbase = (4 * hh + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // One key tile.  MASK: causal mask and per-lane block test (only the at
-  // most two tiles that hold some lane's current block need it).
-  auto tile = [&](int j, auto mask_tag, const bf16* Ks, const bf16* Vs, const bf16* Ss)
+  bf16x8 pb[2][2];  // P of the last softmax, the B operand of the PV products
+
+  // Scores and softmax of one key tile (P into pb).  MASK: causal mask and
+  // per-lane block test (only the at most two tiles that hold some lane's
+  // current block need it).
+  auto tile = [&](int j, auto mask_tag, const bf16* Ks, const bf16* Ss)
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     float bias2[UB];  // log2-domain gate bias of this lane's row for each unit of tile j
@@ -197,7 +206,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
     // (m_run is -inf only for a row with no visible key yet: all p are 0)
     const float off = bias2[0] - m_run;
     float psum = 0.f;
-    bf16x8 pb[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -209,9 +217,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       }
     }
     l_run += psum;
-
-    // O^T += V^T P^T: the B slots of a lane are keys 16 pp + 4 hh + (0..3, 8..11)
-    // of M-tile mt, and the transposing reads give V^T in the same key order
+  };
+  // O^T += V^T P^T: the B slots of a lane are keys 16 pp + 4 hh + (0..3, 8..11)
+  // of M-tile mt, and the transposing reads give V^T in the same key order
+  auto pv = [&](const bf16* Vs) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -226,31 +236,56 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
-  auto run = [&](int j, const bf16* Ks, const bf16* Vs, const bf16* Ss)
-      __attribute__((always_inline)) {
-    if (j > c_hi) return;  // past this wave's last block
+  auto run = [&](int j) __attribute__((always_inline)) {
+    const bf16* Ks = (j & 1) ? K1 : K0;
+    const bf16* Ss = (j & 1) ? S1 : S0;
     if (j < c_lo)
-      tile(j, std::false_type{}, Ks, Vs, Ss);
+      tile(j, std::false_type{}, Ks, Ss);
     else
-      tile(j, std::true_type{}, Ks, Vs, Ss);
+      tile(j, std::true_type{}, Ks, Ss);
+  };
+  auto vbuf = [&](int j) __attribute__((always_inline)) {
+    const int r = j % 3;
+    return r == 0 ? V0 : (r == 1 ? V1 : V2);
   };
 
+  // The two waves of a SIMD belong to different halves of the workgroup
+  // (waves 0-3 and 4-7).  Half 0 takes each tile in the order scores,
+  // softmax, PV; half 1 runs the PV of the previous tile first, then the
+  // scores and softmax of this one.  Between two barriers one half is then
+  // in its softmax while the other multiplies for two of the three phases,
+  // so the matrix cores and the vector ALUs of a SIMD work at the same time.
+  // K tiles alternate between two buffers, V tiles rotate over three (half
+  // 1 still reads V of tile j - 1 while tile j + 1 is staged).
+  auto loop = [&](auto half_tag) __attribute__((always_inline)) {
+    constexpr int H = decltype(half_tag)::value;
+    for (int j = 0; j <= c_end; ++j) {
+      if (j + 1 <= c_end) gload(j + 1);
+      if constexpr (H == 0) {
+        if (j <= c_hi) {
+          run(j);
+          pv(vbuf(j));
+        }
+      } else {
+        if (j >= 1 && j - 1 <= c_hi) pv(vbuf(j - 1));
+        if (j <= c_hi) run(j);
+      }
+      if (j + 1 <= c_end) sstore((j & 1) ? K0 : K1, vbuf(j + 1), (j & 1) ? S0 : S1);
+      __syncthreads();
+    }
+    if constexpr (H == 1) {
+      if (c_end <= c_hi) pv(vbuf(c_end));
+    }
+  };
   gload(0);
   sstore(K0, V0, S0);
   __syncthreads();
-  // unrolled by two so that both buffers' code sits in one loop body
-  for (int j = 0; j <= c_end; j += 2) {
-    if (j + 1 <= c_end) gload(j + 1);
-    run(j, K0, V0, S0);
-    if (j + 1 <= c_end) sstore(K1, V1, S1);
-    __syncthreads();
-    if (j + 1 > c_end) break;
-    if (j + 2 <= c_end) gload(j + 2);
-    run(j + 1, K1, V1, S1);
-    if (j + 2 <= c_end) sstore(K0, V0, S0);
-    __syncthreads();
-  }
+  if (__builtin_amdgcn_readfirstlane(tid >> 8) == 0)
+    loop(std::integral_constant<int, 0>{});
+  else
+    loop(std::integral_constant<int, 1>{});
 
   l_run += __shfl_xor(l_run, 32);
   if (qi < D.tq) {
