@@ -147,17 +147,46 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const ST* __restrict__ q
   }
 }
 
+// Order-preserving 32-bit key of a score (larger z, larger key; -0 counts as
+// +0, as in a floating-point comparison), and the selection order on (key,
+// block): key descending, then block ascending.
+__device__ __forceinline__ unsigned ord_key(float z) {
+  unsigned u = __float_as_uint(z);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ bool key_before(unsigned ka, int ja, unsigned kb, int jb) {
+  return ka > kb || (ka == kb && ja < jb);
+}
+
 // Lane-per-row variant for many rows and K <= 32: the 64 rows of a wave are
 // consecutive positions of one (batch, head), so every ks row is a
-// wave-uniform load.  Each lane keeps its best KMAX (>= K) blocks sorted in
-// registers; blocks arrive in ascending order and enter only when strictly
-// better than the current last entry, which reproduces the (z desc, j asc)
-// order of the wave-per-row kernel.  Scores use the same SelQ dot product.
+// wave-uniform load.  Each lane keeps its best KMAX (>= K) blocks in
+// registers as 64-bit keys (ord_key of z above, the complement of the block
+// below), so that one unsigned comparison gives the selection order (z
+// descending, block ascending) and no two candidates tie.  Candidates come in
+// batches of 8: the batch is sorted by a 19-comparator network, each of the
+// last 8 list entries keeps the larger of itself and its mirror in the batch
+// (the list then holds the best KMAX of both, in bitonic order), and a
+// bitonic merge sorts it again; every step is branch-free, so the lanes of a
+// wave never wait on each other's insertions.  Scores use the same SelQ dot
+// product.
+__device__ __forceinline__ void ce_desc(unsigned long long& a, unsigned long long& b) {
+  const bool sw = b > a;
+  const unsigned long long hi = sw ? b : a, lo = sw ? a : b;
+  a = hi;
+  b = lo;
+}
+
 template <int DS, typename ST, int KMAX>
 __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ qs,
                                                         const ST* __restrict__ ks, int K,
                                                         int renorm, int* __restrict__ idx,
                                                         float* __restrict__ bias, Dims D) {
+  static_assert(KMAX >= 8 && (KMAX & (KMAX - 1)) == 0, "KMAX: a power of two >= 8");
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int wave_first = __builtin_amdgcn_readfirstlane(blockIdx.x * 256 + (threadIdx.x & ~63));
@@ -169,13 +198,9 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
   SelQ<DS, ST> qsv;
   qsv.load(qs + row * DS);
   const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
-  float tz[KMAX];
-  int tj[KMAX];
+  unsigned long long tk[KMAX];  // best blocks, key descending; 0 = empty
 #pragma unroll
-  for (int r = 0; r < KMAX; ++r) {
-    tz[r] = -INFINITY;
-    tj[r] = -1;
-  }
+  for (int r = 0; r < KMAX; ++r) tk[r] = 0ull;
   float m = -INFINITY, s = 0.f;  // log2-domain running log-sum-exp of z
   for (int j0 = 0; j0 < cw; j0 += 8) {
     float zz[8];
@@ -196,42 +221,48 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
       s = acc;
       m = mn;
     }
+    // the batch as keys (blocks at or after c: 0, never selected), sorted
+    unsigned long long bk[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const float z = zz[kk];
-      if (z > tz[KMAX - 1]) {
-        tz[KMAX - 1] = z;
-        tj[KMAX - 1] = j0 + kk;
-#pragma unroll
-        for (int r = KMAX - 1; r > 0; --r) {
-          if (tz[r] > tz[r - 1]) {
-            const float fz = tz[r];
-            tz[r] = tz[r - 1];
-            tz[r - 1] = fz;
-            const int fj = tj[r];
-            tj[r] = tj[r - 1];
-            tj[r - 1] = fj;
-          }
-        }
-      }
+      const int j = j0 + kk;
+      bk[kk] = j < c ? ((unsigned long long)ord_key(zz[kk]) << 32) | (unsigned)~j : 0ull;
     }
+    ce_desc(bk[0], bk[2]); ce_desc(bk[1], bk[3]); ce_desc(bk[4], bk[6]); ce_desc(bk[5], bk[7]);
+    ce_desc(bk[0], bk[4]); ce_desc(bk[1], bk[5]); ce_desc(bk[2], bk[6]); ce_desc(bk[3], bk[7]);
+    ce_desc(bk[0], bk[1]); ce_desc(bk[2], bk[3]); ce_desc(bk[4], bk[5]); ce_desc(bk[6], bk[7]);
+    ce_desc(bk[2], bk[4]); ce_desc(bk[3], bk[5]);
+    ce_desc(bk[1], bk[4]); ce_desc(bk[3], bk[6]);
+    ce_desc(bk[1], bk[2]); ce_desc(bk[3], bk[4]); ce_desc(bk[5], bk[6]);
+    // best KMAX of list and batch: the list descends, the mirrored batch
+    // ascends, their larger elements form a bitonic sequence
+#pragma unroll
+    for (int r = KMAX - 8; r < KMAX; ++r) {
+      const unsigned long long o = bk[KMAX - 1 - r];
+      tk[r] = o > tk[r] ? o : tk[r];
+    }
+#pragma unroll
+    for (int st = KMAX / 2; st >= 1; st >>= 1)
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r)
+        if ((r & st) == 0) ce_desc(tk[r], tk[r + st]);
   }
   if (i >= D.tq) return;
   const int n = c < K ? c : K;
   float norm = c == 0 ? -INFINITY : (m + log2f(s)) * kLn2;
   if (renorm) {
-    float mm = tz[0];
+    float mm = key_value((unsigned)(tk[0] >> 32));
     float ss = 0.f;
 #pragma unroll
     for (int r = 0; r < KMAX; ++r)
-      if (r < n) ss += exp2f((tz[r] - mm) * kLog2e);
+      if (r < n) ss += exp2f((key_value((unsigned)(tk[r] >> 32)) - mm) * kLog2e);
     norm = n == 0 ? -INFINITY : mm + log2f(ss) * kLn2;
   }
 #pragma unroll
   for (int r = 0; r < KMAX; ++r) {
     if (r < K) {
-      idx[row * K + r] = r < n ? tj[r] : -1;
-      bias[row * K + r] = r < n ? tz[r] - norm : -INFINITY;
+      idx[row * K + r] = r < n ? (int)~(unsigned)tk[r] : -1;
+      bias[row * K + r] = r < n ? key_value((unsigned)(tk[r] >> 32)) - norm : -INFINITY;
     }
   }
 }
@@ -243,13 +274,6 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
 // LDS histogram) finds the n_t-th largest key, ties at it are taken in block
 // order; the n_t winners are then sorted (bitonic network in LDS) by key
 // descending, block ascending — the same order as the other kernels.
-__device__ __forceinline__ unsigned ord_key(float z) {
-  const unsigned u = __float_as_uint(z);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ bool key_before(unsigned ka, int ja, unsigned kb, int jb) {
-  return ka > kb || (ka == kb && ja < jb);
-}
 
 template <int DS, typename ST>
 __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__ qs,
