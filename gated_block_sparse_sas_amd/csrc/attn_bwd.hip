@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
     const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
     const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
     bf16* __restrict__ dq, bf16* __restrict__ dqs, float* __restrict__ dz,
-    float* __restrict__ delta, Dims D, int nqt, int xcd_groups) {
+    float* __restrict__ rowd, int tqp, Dims D, int nqt, int xcd_groups) {
   constexpr int HD = 128, TE = kBlock * 144;  // tile elements (72-dword rows)
   constexpr int NCH = kBlock * 16 / kDqThreads;  // 16-byte chunks per thread and tensor
   constexpr int DQ = DS / 4;                   // selector dims per lane group
@@ -320,7 +320,14 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
   }
   dlt += __shfl_xor(dlt, 16);
   dlt += __shfl_xor(dlt, 32);
-  if (valid && g4 == 0) delta[row] = dlt;
+  // Row data for the dK/dV kernel, unit-major so that the rows of one unit
+  // are contiguous: slot u < nb holds, for each row, the log2-domain offset
+  // of unit u's logits (gate bias minus the row's log-sum-exp; -inf past the
+  // row's own unit), slot nb the row's D; rows padded to tqp (padding: -inf,
+  // D 0).  The offsets are the ones this kernel applies itself.
+  const size_t rbase = ((size_t)b * D.hq + h) * (size_t)(D.nb + 1) * tqp + qi;
+  const bool rw = g4 == 0 && qi < tqp;
+  if (rw) rowd[rbase + (size_t)D.nb * tqp] = valid ? dlt : 0.f;
   float qsv[DQ], dqsa[DQ];
 #pragma unroll
   for (int e = 0; e < DQ; ++e) {
@@ -383,6 +390,13 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
         part += __shfl_xor(part, 16);
         part += __shfl_xor(part, 32);
         if (j * UB + ub < c) bias2[ub] = (D.sel_scale * part - lam_t) * kLog2e;
+      }
+    }
+    if (rw) {
+#pragma unroll
+      for (int ub = 0; ub < UB; ++ub) {
+        const int ju = j * UB + ub;
+        rowd[rbase + (size_t)ju * tqp] = valid && ju <= c ? bias2[ub] - l2 : -INFINITY;
       }
     }
     // unit of this lane's keys 16 mk + 4 g4 + r within the tile
@@ -757,10 +771,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // tile).  The Q and dO tiles of an item stream global -> LDS with direct
 // loads into two buffers; the transposed operands (dO^T for dV, Q^T for dK)
 // come from transposing LDS reads of the same row-major tiles, laid out by
-// trow() so that both kinds of read hit disjoint banks.  Each wave also loads
-// the raw per-row data (qs, the block's ks row, lse, lam, D) of its 8 rows
-// two items ahead and turns it into the row offsets of the next item after
-// its products, so no wave waits on a global load inside the loop.  In the
+// trow() so that both kinds of read hit disjoint banks.  The per-row data of
+// an item (each unit's log2 logit offset and D, written unit-major by the dQ
+// kernel) arrives the same way: one direct load of (UB + 1) x 128 bytes, so
+// the item loop does no per-row arithmetic of its own.  In the
 // S / dP products each 16-byte operand read is issued one product ahead (two
 // operand registers in turn: the register budget of three waves per SIMD
 // leaves no room for more), and a wave raises its issue priority while it
@@ -770,14 +784,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 template <int DS, int UB>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, const bf16* __restrict__ qs, const bf16* __restrict__ ks,
-    const float* __restrict__ lam, bf16* __restrict__ dk, bf16* __restrict__ dv, Dims D,
-    int xcd_groups) {
+    const bf16* __restrict__ dout, const float* __restrict__ rowd, int tqp,
+    bf16* __restrict__ dk, bf16* __restrict__ dv, Dims D, int xcd_groups) {
   constexpr int HD = 128, QT = 32, TS = QT * 18, TE = TS * 8;  // tile slots, elements
   constexpr int NI = TS / 64;              // direct-load instructions per tile and tensor
   constexpr int XI = (NI + 3) / 4;         // ... per wave (at most)
-  constexpr int CH = DS / 8;               // 16-byte chunks of a selector row
   constexpr int BU = kBlock / UB;          // tokens per gate unit (UB units per 64-key tile)
   __shared__ __align__(16) bf16 Q0[TE];
   __shared__ __align__(16) bf16 Q1[TE];
@@ -785,12 +796,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
   __shared__ __align__(16) bf16 O1[TE];
   __shared__ __align__(16) float F0[(UB + 1) * QT];  // log2 offset of (unit, row), then D
   __shared__ __align__(16) float F1[(UB + 1) * QT];
-  // raw row data of the next two items (two buffers), each wave its own 8
-  // rows: qs rows, the ks rows of tile j's units for the item's selector
-  // head, and lse, lam, D
-  __shared__ __align__(16) bf16 RQ[2][4 * 8 * DS];
-  __shared__ __align__(16) bf16 RK[2][4 * UB * DS];
-  __shared__ __align__(16) float RS[2][4 * 32];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -856,10 +861,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
   auto row0 = [&](Item x) { return (qt0 + x.t) * QT; };
   auto head_row = [&](Item x) { return ((size_t)b * D.hq + g * D.hpg + x.hl) * D.tq; };
 
-  // direct loads of an item's Q and dO tiles (all waves); rows past the end
-  // reload the last row
-  auto issue = [&](Item x, bf16* Qd, bf16* Od) {
+  // direct loads of an item's Q and dO tiles (all waves; rows past the end
+  // reload the last row) and of its row data (wave 0: lane 8 s + e carries
+  // rows 4 e .. 4 e + 3 of slot s, unit s of tile j or, for s = UB, D)
+  auto issue = [&](Item x, bf16* Qd, bf16* Od, float* Fd) {
     const int i0 = row0(x);
+    if (wave == 0 && lane < 8 * (UB + 1)) {
+      const int sl = lane >> 3;
+      const size_t slot = sl < UB ? (size_t)j * UB + sl : (size_t)D.nb;
+      const size_t hb = (size_t)b * D.hq + g * D.hpg + x.hl;
+      __builtin_amdgcn_global_load_lds(rowd + (hb * (D.nb + 1) + slot) * tqp + i0 + 4 * (lane & 7),
+                                       Fd, 16, 0, 0);
+    }
     const size_t base = (head_row(x) + i0) * HD * 2;
     const char* const qb = (const char*)q + base;
     const char* const ob = (const char*)dout + base;
@@ -875,70 +888,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
         __builtin_amdgcn_global_load_lds(ob + off, Od + ins * 512, 16, 0, 0);
       }
     }
-  };
-  // direct loads of this wave's raw row data of an item (rows 8 wave ..
-  // 8 wave + 7 of the tile) into raw buffer rb
-  auto issue_raw = [&](Item x, int rb) {
-    const int i0 = row0(x);
-    const size_t hr = head_row(x);
-    bf16* const rq = RQ[rb] + wave * 8 * DS;
-    bf16* const rk = RK[rb] + wave * UB * DS;
-    float* const rs = RS[rb] + wave * 32;
-    const size_t rw0 = hr + min(i0 + 8 * wave + lane / CH, D.tq - 1);
-    if (lane < 8 * CH)
-      __builtin_amdgcn_global_load_lds(qs + rw0 * DS + (lane % CH) * 8, rq, 16, 0, 0);
-    if (lane < UB * CH) {
-      const int h = g * D.hpg + x.hl;
-      __builtin_amdgcn_global_load_lds(
-          ks + (((size_t)b * D.hks + h / D.hps) * D.nb + (size_t)j * UB) * DS + lane * 8, rk, 16,
-          0, 0);
-    }
-    // lanes 0-7 lse, 8-15 lam, 16-23 D of the wave's rows (4 bytes per lane)
-    const size_t rw = hr + min(i0 + 8 * wave + (lane & 7), D.tq - 1);
-    if (lane < 8)
-      __builtin_amdgcn_global_load_lds(lse + rw, rs, 4, 0, 0);
-    else if (lane < 16)
-      __builtin_amdgcn_global_load_lds(lam + rw, rs, 4, 0, 0);
-    else if (lane < 24)
-      __builtin_amdgcn_global_load_lds(delta + rw, rs, 4, 0, 0);
-  };
-  // row data of an item from this wave's raw buffer rb (after its loads have
-  // landed): F[u QT + r] = log2 offset of row r for unit u of tile j (gate
-  // bias minus the row's log-sum-exp; -inf where the unit is not visible),
-  // F[UB QT + r] = D.  Eight lanes share a row's selector dot products.
-  auto rowdata = [&](Item x, int rb, float* Fd) {
-    const int i0 = row0(x);
-    constexpr int PE = DS / 8;  // selector dims per lane
-    const int rr = lane >> 3, part = lane & 7;
-    const bf16* const rq = RQ[rb] + wave * 8 * DS + rr * DS + part * PE;
-    const float* const rs = RS[rb] + wave * 32;
-    const int r = 8 * wave + rr, i = i0 + r;
-    const int c = (D.qoff + i) / BU;
-    const float l2 = rs[rr] * kLog2e;
-#pragma unroll
-    for (int ub = 0; ub < UB; ++ub) {
-      const bf16* const rk = RK[rb] + wave * UB * DS + ub * DS + part * PE;
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < PE; e += 2) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        acc = __builtin_amdgcn_fdot2_f32_bf16(*(const bf16x2*)(rq + e), *(const bf16x2*)(rk + e),
-                                              acc, false);
-      }
-      acc = sum8_dpp(acc);
-      if (part == 0) {
-        const int ju = j * UB + ub;
-        float off;
-        if (i >= D.tq || ju > c)
-          off = -INFINITY;
-        else if (ju == c)
-          off = -l2;
-        else
-          off = (D.sel_scale * acc - rs[8 + rr]) * kLog2e - l2;
-        Fd[ub * QT + r] = off;
-      }
-    }
-    if (part == 0) Fd[UB * QT + r] = rs[16 + rr];
   };
   // the unit of this wave's 16 keys within the tile
   const int uw = UB == 1 ? 0 : (wave * 16) / BU;
@@ -1014,30 +963,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
 
   if (nitems > 0) {
     Item cur{0, 0};
-    const Item second = next(cur);
-    issue_raw(cur, 0);
-    if (nitems > 1) issue_raw(second, 1);
-    issue(cur, Q0, O0);
+    issue(cur, Q0, O0, F0);
     wait_vmem();
-    rowdata(cur, 0, F0);
     __syncthreads();
-    // Item it: the tiles of it + 1 and the raw row data of it + 2 load while
-    // it computes; then the row data of it + 1 is formed from raw data that
-    // landed in the previous item, with no wait on this item's loads.
+    // Item it: the tiles and row data of it + 1 load while it computes.
     // Unrolled by two so that both buffers' code sits in one loop body.
     for (int it = 0; it < nitems; it += 2) {
-      const Item n1 = next(cur), n2 = next(n1), n3 = next(n2);
-      if (it + 1 < nitems) issue(n1, Q1, O1);
-      if (it + 2 < nitems) issue_raw(n2, 0);
+      const Item n1 = next(cur), n2 = next(n1);
+      if (it + 1 < nitems) issue(n1, Q1, O1, F1);
       compute(cur, Q0, O0, F0);
-      if (it + 1 < nitems) rowdata(n1, 1, F1);
       wait_vmem();
       __syncthreads();
       if (it + 1 >= nitems) break;
-      if (it + 2 < nitems) issue(n2, Q0, O0);
-      if (it + 3 < nitems) issue_raw(n3, 1);
+      if (it + 2 < nitems) issue(n2, Q0, O0, F0);
       compute(n1, Q1, O1, F1);
-      if (it + 2 < nitems) rowdata(n2, 0, F0);
       wait_vmem();
       __syncthreads();
       cur = n2;
@@ -1149,6 +1088,10 @@ BwdWs bwd_workspace(const Dims& D, bool need_dz) {
   if (need_dz) off += align256(rows * (size_t)D.nb * sizeof(float));
   W.off_dks = off;
   off += align256((size_t)D.batch * D.hks * D.nb * D.ds * sizeof(float));
+  W.tqp = (D.tq + 31) / 32 * 32;
+  W.off_rows = off;
+  if (D.d == 128)
+    off += align256((size_t)D.batch * D.hq * (D.nb + 1) * W.tqp * sizeof(float));
   W.total = off;
   return W;
 }
@@ -1189,6 +1132,7 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   float* delta = (float*)(ws + W.off_delta);
   float* dzp = dz ? dz : (float*)(ws + W.off_dz);
   float* acc = (float*)(ws + W.off_dks);
+  float* rowd = (float*)(ws + W.off_rows);
   const int groups = D.batch * D.hkv;
   const int xg = groups % 8 == 0 ? groups / 8 : 0;
   hipError_t e;
@@ -1197,7 +1141,7 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
     hipLaunchKernelGGL((bwd_dq16_kernel<DS, UB>), dim3(D.batch * D.hq * nqtw), dim3(kDqThreads),
                        0, st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)o,
                        (const bf16*)dout, lse, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dq,
-                       (bf16*)dqs, dzp, delta, D, nqtw, xg);
+                       (bf16*)dqs, dzp, rowd, W.tqp, D, nqtw, xg);
   } else {
   const int nqt = (D.tq + 127) / 128;
   hipLaunchKernelGGL((bwd_dq_kernel<HD, DS>), dim3(D.batch * D.hq * nqt), dim3(256), 0, st,
@@ -1210,9 +1154,8 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   E.record(0, st);
   if constexpr (HD == 128) {
     hipLaunchKernelGGL((bwd_dkdv16_kernel<DS, UB>), dim3(groups * (D.tk / kBlock)), dim3(256), 0,
-                       st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
-                       (const float*)delta, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dk,
-                       (bf16*)dv, D, xg);
+                       st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
+                       (const float*)rowd, W.tqp, (bf16*)dk, (bf16*)dv, D, xg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     E.record(1, st);

@@ -33,6 +33,8 @@ struct BwdWs {
   size_t off_delta;  // float [rows]          D = <dO, O>
   size_t off_dz;     // float [rows, nb]      only when the caller passes no dz
   size_t off_dks;    // float [b, hks, nb, ds] fp32 accumulator of dks
+  size_t off_rows;   // d = 128: float [b, hq, nb + 1, tqp] per-row data of the dK/dV kernel
+  int tqp;           // tq rounded up to 32
 };
 BwdWs bwd_workspace(const Dims& D, bool need_dz);
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
