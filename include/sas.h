@@ -110,8 +110,11 @@ sas_status sas_attn_fwd(const sas_shape* shape, const void* q, const void* k, co
  * over the query heads of each kv head), dqs, dks (summed over the heads
  * sharing a selector head) and dz = dL/dz [batch,hq,tq,nb] (0 for j >= c(t)),
  * the gradient reaching the selector scores.  dz may be NULL (it then lives in
- * the workspace).  Source: blog, "The Logit Injection Mechanism" (gradients
- * reach the selector through the softmax), NeurIPS abstract. */
+ * the workspace).  The workspace also holds D = <dO, O> per row, an fp32 dks
+ * accumulator and, at d = 128, per-row logit offsets for every (row, gate
+ * unit): batch * hq * (nb + 1) * ceil32(tq) floats.  Source: blog, "The Logit
+ * Injection Mechanism" (gradients reach the selector through the softmax),
+ * NeurIPS abstract. */
 sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, const void* v,
                         const void* o, const void* dout, const float* lse, const void* qs,
                         const void* ks, const float* gate_lse, void* dq, void* dk, void* dv,
