@@ -897,7 +897,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     if (D.qoff + min(i0 + QT - 1, D.tq - 1) < key0) return;  // every row before these keys
     // keys after a row's position are cut: slot (16 mq + r) of this lane is
     // cut when it is below mlim (no cut away from the diagonal)
-    const int mlim = D.qoff + i0 < key0 + 15 ? key - (D.qoff + i0 + 4 * g4) : -1;
+    const bool mlim_on = D.qoff + i0 < key0 + 15;  // uniform over the workgroup
+    const int mlim = key - (D.qoff + i0 + 4 * g4);
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
     f32x4 pacc[2] = {f32x4{}, f32x4{}};
     __builtin_amdgcn_s_setprio(1);
@@ -926,18 +927,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_s_setprio(0);
+    // P and dS; the causal cut only on items that meet the diagonal
+    auto softmax_ds = [&](auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int mq = 0; mq < 2; ++mq) {
-      const f32x4 of = *(const f32x4*)&Fs[uw * QT + 16 * mq + 4 * g4];
-      const f32x4 dl = *(const f32x4*)&Fs[UB * QT + 16 * mq + 4 * g4];
+      for (int mq = 0; mq < 2; ++mq) {
+        const f32x4 of = *(const f32x4*)&Fs[uw * QT + 16 * mq + 4 * g4];
+        const f32x4 dl = *(const f32x4*)&Fs[UB * QT + 16 * mq + 4 * g4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float p = exp2_raw(fmaf(sacc[mq][r], c1, of[r]));
-        if (16 * mq + r < mlim) p = 0.f;
-        sacc[mq][r] = p;
-        pacc[mq][r] = p * (pacc[mq][r] - dl[r]);
+        for (int r = 0; r < 4; ++r) {
+          float p = exp2_raw(fmaf(sacc[mq][r], c1, of[r]));
+          if (MASK && 16 * mq + r < mlim) p = 0.f;
+          sacc[mq][r] = p;
+          pacc[mq][r] = p * (pacc[mq][r] - dl[r]);
+        }
       }
-    }
+    };
+    if (mlim_on)
+      softmax_ds(std::true_type{});
+    else
+      softmax_ds(std::false_type{});
     // B operands over the 32 rows: slots 0..3 = rows 4*g4 + r, 4..7 = 16 + 4*g4 + r
     bf16x8 pb, sb;
 #pragma unroll
