@@ -847,45 +847,65 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     toff[x] = so * 2;
   }
 
-  // work item: head hl of the group, query tile t (rows i0 = (qt0 + t) QT ..)
+  // work item: head hl of the group, query tile t (rows i0 = (qt0 + t) QT ..);
+  // qo: element offset of its first row in q / dout, fo: of its first row in
+  // slot 0 of the row data (both advanced by additions from item to item)
   struct Item {
     int hl, t;
+    size_t qo, fo;
+  };
+  const size_t hq0 = (size_t)b * D.hq + g * D.hpg;  // first query head of the group
+  auto first = [&](int hl) {
+    Item x;
+    x.hl = hl;
+    x.t = 0;
+    x.qo = ((hq0 + hl) * D.tq + (size_t)qt0 * QT) * HD;
+    x.fo = (hq0 + hl) * (size_t)(D.nb + 1) * tqp + (size_t)qt0 * QT;
+    return x;
   };
   auto next = [&](Item x) {
-    if (++x.t == per_h) {
-      x.t = 0;
-      ++x.hl;
-    }
+    if (++x.t == per_h) return first(x.hl + 1);
+    x.qo += (size_t)QT * HD;
+    x.fo += QT;
     return x;
   };
   auto row0 = [&](Item x) { return (qt0 + x.t) * QT; };
-  auto head_row = [&](Item x) { return ((size_t)b * D.hq + g * D.hpg + x.hl) * D.tq; };
+  // this lane's part of the row-data address: slot (unit s of tile j, or D
+  // for s = UB) and rows 4 e .. 4 e + 3 for lane 8 s + e
+  const int fsl = min(lane >> 3, UB);
+  const size_t flane = (fsl < UB ? (size_t)j * UB + fsl : (size_t)D.nb) * tqp + 4 * (lane & 7);
 
   // direct loads of an item's Q and dO tiles (all waves; rows past the end
-  // reload the last row) and of its row data (wave 0: lane 8 s + e carries
-  // rows 4 e .. 4 e + 3 of slot s, unit s of tile j or, for s = UB, D)
+  // reload the last row) and of its row data (wave 0, lanes 0 .. 8 UB + 7)
   auto issue = [&](Item x, bf16* Qd, bf16* Od, float* Fd) {
-    const int i0 = row0(x);
     if (wave == 0 && lane < 8 * (UB + 1)) {
-      const int sl = lane >> 3;
-      const size_t slot = sl < UB ? (size_t)j * UB + sl : (size_t)D.nb;
-      const size_t hb = (size_t)b * D.hq + g * D.hpg + x.hl;
-      __builtin_amdgcn_global_load_lds(rowd + (hb * (D.nb + 1) + slot) * tqp + i0 + 4 * (lane & 7),
-                                       Fd, 16, 0, 0);
+      // (through a named pointer: passing the sum straight to the builtin
+      // makes the host pass drop this kernel's launch stub)
+      const float* const src = rowd + x.fo + flane;
+      __builtin_amdgcn_global_load_lds(src, Fd, 16, 0, 0);
     }
-    const size_t base = (head_row(x) + i0) * HD * 2;
-    const char* const qb = (const char*)q + base;
-    const char* const ob = (const char*)dout + base;
-    const bool tail = i0 + QT > D.tq;
-    const int rmax = D.tq - 1 - i0;
+    const bf16* const qb = q + x.qo;
+    const bf16* const ob = dout + x.qo;
+    const int rmax = D.tq - 1 - row0(x);
+    if (rmax >= QT - 1) {  // uniform: every row of the tile exists
 #pragma unroll
-    for (int xi = 0; xi < XI; ++xi) {
-      const int ins = wave + 4 * xi;
-      if (ins < NI) {
-        unsigned off = toff[xi];
-        if (tail && trw[xi] > rmax) off -= (unsigned)(trw[xi] - rmax) * HD * 2;
-        __builtin_amdgcn_global_load_lds(qb + off, Qd + ins * 512, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(ob + off, Od + ins * 512, 16, 0, 0);
+      for (int xi = 0; xi < XI; ++xi) {
+        const int ins = wave + 4 * xi;
+        if (ins < NI) {
+          __builtin_amdgcn_global_load_lds((const char*)qb + toff[xi], Qd + ins * 512, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const char*)ob + toff[xi], Od + ins * 512, 16, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int xi = 0; xi < XI; ++xi) {
+        const int ins = wave + 4 * xi;
+        if (ins < NI) {
+          unsigned off = toff[xi];
+          if (trw[xi] > rmax) off -= (unsigned)(trw[xi] - rmax) * HD * 2;
+          __builtin_amdgcn_global_load_lds((const char*)qb + off, Qd + ins * 512, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const char*)ob + off, Od + ins * 512, 16, 0, 0);
+        }
       }
     }
   };
@@ -971,7 +991,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
   };
 
   if (nitems > 0) {
-    Item cur{0, 0};
+    Item cur = first(0);
     issue(cur, Q0, O0, F0);
     wait_vmem();
     __syncthreads();
