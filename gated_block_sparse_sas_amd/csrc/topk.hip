@@ -8,12 +8,18 @@
 // kept block is its training log-gate z - lam (renorm = 0) or the gate
 // renormalised over the kept set (renorm = 1).
 //
-// One wavefront per query row.  The row's scores are computed once into LDS
-// (lane j % 64 owns block j), lam comes from a wave max + sum, then K rounds
-// each pick the best remaining block with a 64-lane argmax on (z, -j): round
-// r takes the best candidate strictly after round r-1's winner in that total
-// order, so no "already taken" set is needed.  Scores use the selector dot
-// product of the gate kernel (SelQ: packed bf16 products for bf16 inputs).
+// Three kernels, chosen by shape (launch_topk_t): a lane per row with the
+// best blocks in registers for many rows and K <= 32 (topk_lane_kernel), a
+// wave per row with an LDS radix select for budgets and K >= 16 otherwise
+// (topk_select_kernel), and the wave-per-row kernel below for the rest.  All
+// rank the same fp32 scores (SelQ: packed bf16 products for bf16 inputs, as
+// in the gate kernel) in the same order, so they pick the same blocks.
+//
+// Wave per row: the row's scores are computed once into LDS (lane j % 64
+// owns block j), lam comes from a wave max + sum, then K rounds each pick the
+// best remaining block with a 64-lane argmax on (z, -j): round r takes the
+// best candidate strictly after round r-1's winner in that total order, so
+// no "already taken" set is needed.
 #include "sas_device.h"
 #include "sas_internal.h"
 
