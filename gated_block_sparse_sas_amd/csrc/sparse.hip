@@ -653,6 +653,92 @@ __global__ __launch_bounds__(256) void sp_merge_kernel(Src S, const int* __restr
   if (lane == 0 && lse) lse[row] = (m + log2f(sm)) * kLn2;
 }
 
+// d = 128: the same merge with a 16-lane group per row, four rows per wave.
+// A partial row is exactly 16 lanes x 16 bytes, so a group reads one of its
+// row's partials per load while the other groups read theirs; the chain of
+// dependent loads (slot list, inverse position, lse, partial rows) is paid
+// once per four rows instead of once per row.  Group-local max and sum by
+// DPP inside the 16-lane row; slots 16 at a time.
+__device__ __forceinline__ float max16_dpp(float x) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
+  return x;
+}
+__device__ __forceinline__ float sum16_dpp(float x) {
+  x = sum8_dpp(x);  // pairs, quads, halves of 8
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+template <typename Src>
+__global__ __launch_bounds__(256) void sp_merge16_kernel(Src S, const int* __restrict__ inv,
+                                                         const float* __restrict__ plse,
+                                                         const bf16* __restrict__ po,
+                                                         bf16* __restrict__ o,
+                                                         float* __restrict__ lse, Dims D, int nqb,
+                                                         int dcpb) {
+  constexpr int HD = 128;
+  const int lane = threadIdx.x & 63, grp = lane >> 4, sl = lane & 15;
+  const size_t nrows = (size_t)D.batch * D.hq * D.tq;
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 6) * 4 + grp;
+  if (__builtin_amdgcn_readfirstlane((size_t)blockIdx.x * 16 + (threadIdx.x >> 6) * 4) >= nrows)
+    return;  // whole wave past the end
+  const bool live = row < nrows;  // uniform over the group
+  const size_t rw = live ? row : nrows - 1;
+  const int i = (int)(rw % D.tq), t = D.qoff + i, c = t / D.blk;
+  const int h = (int)((rw / D.tq) % D.hq), b = (int)(rw / ((size_t)D.tq * D.hq));
+  const int g = h / D.hpg, hl = h - g * D.hpg;
+  const int dpos = ((b * D.hkv + g) * nqb + (c - D.qoff / D.blk)) * dcpb * kChunk +
+                   hl * D.blk + t % D.blk;
+  const int hbase = D.batch * D.hkv * nqb * dcpb * kChunk;
+  const size_t a0 = S.seg_lo(rw);
+  const int len = live ? (int)(S.seg_hi(rw) - a0) : 0;
+  const bf16* pr = po + sl * 8;
+  // online merge in log2 units, as in sp_merge_kernel; lane sl of a group
+  // holds columns 8 sl .. 8 sl + 7 of its row
+  float m = plse[dpos] * kLog2e, sm = 1.f;
+  float acc[8];
+  {
+    const bf16x8 cv = *(const bf16x8*)(pr + (size_t)dpos * HD);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = to_f32(cv[e]);
+  }
+  for (int w0 = 0; w0 < len; w0 += 16) {
+    const int x = w0 + sl;
+    const int j = x < len ? S.j_of(a0 + x) : -1;
+    const bool ok = j >= 0 && j < c && S.row_of(a0 + x) == (long long)rw;
+    const int px = ok ? hbase + inv[a0 + x] : dpos;
+    const float lx = ok ? plse[px] * kLog2e : -INFINITY;
+    const unsigned gb = (unsigned)(__ballot(ok) >> (16 * grp)) & 0xFFFFu;
+    if (gb == 0) continue;
+    const float m_new = fmaxf(m, max16_dpp(lx));
+    const float alpha = exp2_raw(m - m_new);
+    m = m_new;
+    const float pw = ok ? exp2_raw(lx - m) : 0.f;
+    sm = sm * alpha + sum16_dpp(pw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+    const int nval = 32 - __builtin_clz(gb);  // slots past the group's last valid one skipped
+#pragma unroll 4
+    for (int q = 0; q < nval; ++q) {
+      const float w = __shfl(pw, q, 16);
+      const int pp = __shfl(px, q, 16);
+      const bf16x8 pv = *(const bf16x8*)(pr + (size_t)pp * HD);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, w != 0.f ? to_f32(pv[e]) : 0.f, acc[e]);
+    }
+  }
+  if (!live) return;
+  const float inv_s = 1.f / sm;
+  bf16x8 ov;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ov[e] = (bf16)(acc[e] * inv_s);
+  *(bf16x8*)(o + row * HD + sl * 8) = ov;
+  if (sl == 0 && lse) lse[row] = (m + log2f(sm)) * kLn2;
+}
+
 static int diag_chunks_per_block(const Dims& D) { return (D.hpg * D.blk + kChunk - 1) / kChunk; }
 static int query_blocks(const Dims& D) { return D.nb - D.qoff / D.blk; }
 // Partial slots of the block path: current-block chunks, then one per pair.
@@ -739,9 +825,16 @@ static hipError_t launch_block_path(const void* q, const void* k, const void* v,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   E.record(0, st);
-  hipLaunchKernelGGL((sp_merge_kernel<HD, Src>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                     st, S, (const int*)inv, (const float*)plse, (const bf16*)po, (bf16*)o, lse, D,
-                     nqb, dcpb);
+  // grouped merge while rows list 16 slots or fewer on average; a wave per
+  // row (64 slots per pass) for larger selections
+  if (HD == 128 && npairs <= 16 * rows)
+    hipLaunchKernelGGL((sp_merge16_kernel<Src>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                       st, S, (const int*)inv, (const float*)plse, (const bf16*)po, (bf16*)o, lse,
+                       D, nqb, dcpb);
+  else
+    hipLaunchKernelGGL((sp_merge_kernel<HD, Src>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                       st, S, (const int*)inv, (const float*)plse, (const bf16*)po, (bf16*)o, lse,
+                       D, nqb, dcpb);
   return hipGetLastError();
 }
 
