@@ -116,6 +116,60 @@ def test_topk_small(renorm, tq, tk, K):
     assert max_abs(bg[ok][fin], br[ok][fin]) <= 1e-4
 
 
+# (tq, tk, K, frac, kernel the shape runs on)
+EXACT_TIE_CASES = [
+    (1088, 4096, 5, 0.0, "lane, 8-entry list"),
+    (1088, 4096, 12, 0.0, "lane, 16-entry list"),
+    (1088, 4096, 24, 0.0, "lane, 32-entry list"),
+    (200, 8192, 40, 0.0, "radix select"),
+    (1, 4096, 8, 0.0, "wave per row"),
+    (640, 4096, 64, 0.25, "budgeted radix select"),
+]
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+@pytest.mark.parametrize("tq,tk,K,frac,kernel", EXACT_TIE_CASES)
+def test_topk_exact_ties(renorm, tq, tk, K, frac, kernel):
+    """Selector keys made of five distinct vectors repeated along the blocks
+    (block j carries vector j % 5): every row's scores take five values, each
+    on many blocks, and equal vectors give bit-equal scores on both sides.
+    With ties going to the smaller block (z descending, block ascending), the
+    GPU's blocks must equal the oracle's on every row, whichever selection
+    kernel the shape dispatches to."""
+    w = W["prefill_32k_top16"].with_(batch=2, hq=8, hkv=2, tq=tq, tk=tk, topk=K)
+    say("topk exact ties", tq, tk, K, frac, renorm, kernel)
+    cpu, dev, f = inputs(w, ("qs", "ks"))
+    ks = cpu["ks"][:, :, torch.arange(w.nb) % 5, :].contiguous()
+    ks_dev = ks.to(DEV)
+    if frac > 0:
+        idx, bias = ops.topk_blocks_budget(dev["qs"], ks_dev, K, frac, w.tk, renorm=renorm)
+    else:
+        idx, bias = ops.topk_blocks(dev["qs"], ks_dev, K, w.tk, renorm=renorm)
+    torch.cuda.synchronize()
+    S = oshape(w)
+    ks64 = ks.to(torch.float64).numpy()
+    if frac > 0:
+        idx_ref, bias_ref = oracle.topk_budget(S, K, frac, f["qs"], ks64, renorm=renorm)
+    else:
+        idx_ref, bias_ref = oracle.topk_blocks(S, K, f["qs"], ks64, renorm=renorm)
+    # rows whose five distinct scores (blocks 0..4) lie apart by more than the
+    # fp32 score error: there the tie order alone decides, on both sides
+    z, _, _ = oracle.gate_scores(S, f["qs"], ks64)
+    zf = z.reshape(-1, w.nb)
+    c = np.tile((np.arange(w.tq) + w.tk - w.tq) // 64, w.batch * w.hq)
+    ok = tie_free_rows(zf[:, :5], np.minimum(c, 5), 5)
+    say("  rows with separated distinct scores", int(ok.sum()), "of", len(ok))
+    assert ok.mean() > 0.99
+    ig = idx.cpu().numpy().reshape(-1, K)
+    ir = idx_ref.reshape(-1, K)
+    assert np.array_equal(ig[ok], ir[ok])
+    bg = bias.cpu().numpy().reshape(-1, K)[ok]
+    br = bias_ref.reshape(-1, K)[ok]
+    assert np.array_equal(np.isneginf(bg), np.isneginf(br))
+    fin = np.isfinite(br)
+    assert max_abs(bg[fin], br[fin]) <= 1e-4
+
+
 @pytest.mark.parametrize("renorm", [0, 1])
 @pytest.mark.parametrize("tq,tk,kmax,frac", [(640, 640, 6, 0.25), (300, 1088, 40, 0.3),
                                              (256, 4096, 64, 0.0), (512, 512, 3, 2.0)])
