@@ -276,9 +276,10 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
 // Budgeted / large-K variant: one wavefront per query row keeps the
 // n_t = min(kmax, c(t), ceil(frac c(t))) best blocks (frac <= 0: no
 // fraction).  Scores go to LDS (same SelQ dot product as above) and become
-// order-preserving 32-bit keys; a 4-pass radix select (8 bits per pass,
-// LDS histogram) finds the n_t-th largest key, ties at it are taken in block
-// order; the n_t winners are then sorted (bitonic network in LDS) by key
+// order-preserving 32-bit keys; a radix select (8 bits per pass, LDS
+// histogram) narrows down the n_t-th largest key, stopping early once the bin
+// that holds it is needed whole; keys tied with it are taken in block order;
+// the n_t winners are then sorted (bitonic network in LDS) by key
 // descending, block ascending — the same order as the other kernels.
 
 template <int DS, typename ST>
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
       const unsigned exc = inc - tot;
       // the digit where the count from the top first reaches need
       int dsel = -1;
-      unsigned above = 0;
+      unsigned above = 0, inbin = 0;
       if (exc < (unsigned)need && inc >= (unsigned)need) {
         unsigned run = exc;
 #pragma unroll
@@ -355,6 +356,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
           if (dsel < 0 && run + cnt[u] >= (unsigned)need) {
             dsel = 255 - 4 * lane - u;
             above = run;
+            inbin = cnt[u];
           }
           run += cnt[u];
         }
@@ -365,13 +367,16 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
       need -= (int)__shfl(above, src);
       prefix |= (unsigned)dg << shift;
       pmask |= 255u << shift;
+      // every key of the digit's bin is needed: the selection is settled
+      if (__shfl(inbin, src) == (unsigned)need) break;
     }
   }
-  // gather: keys above the threshold, then the first `need` ties by block
+  // gather: keys whose resolved bits lie above the prefix, then the first
+  // `need` keys on it by block (all of them when the passes stopped early)
   int cnt_sel = 0, ties_left = need;
   for (int j0 = 0; j0 < c; j0 += 64) {
     const int j = j0 + lane;
-    const unsigned kk = j < c ? ord_key(zc[j]) : 0u;
+    const unsigned kfull = j < c ? ord_key(zc[j]) : 0u, kk = kfull & pmask;
     const bool above = n > 0 && j < c && kk > prefix;
     const bool tie = n > 0 && j < c && kk == prefix;
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -381,7 +386,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
     const unsigned long long bs = __ballot(take);
     if (take) {
       const int pos = cnt_sel + __popcll(bs & lt);
-      sk[pos] = kk;
+      sk[pos] = kfull;
       sj[pos] = j;
     }
     cnt_sel += __popcll(bs);
