@@ -24,6 +24,9 @@
 //    dS feed dV^T += dO^T P and dK^T += Q^T dS straight from registers; Q and
 //    dO are staged in LDS both row-major and transposed.
 //  * dks: a reduction over rows of dz^T qs into an fp32 accumulator.
+// At d = 128 the same steps run on gfx950 MFMA tiles: bwd_dq32 (32 query rows
+// per wave, 32x32x16; selectors up to ds = 32), bwd_dq16 (16 rows per wave,
+// 16x16x32; wider selectors) and bwd_dkdv16 (16 keys per wave, 16x16x32).
 #include "sas_device.h"
 #include "sas_internal.h"
 
@@ -519,6 +522,280 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq16_kernel(
     }
 #pragma unroll
     for (int e = 0; e < DQ; ++e) dqs[row * DS + g4 * DQ + e] = (bf16)(dqsa[e] * D.sel_scale);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Query-stationary dQ, D, dz, dqs for d = 128 on 32x32x16 MFMA tiles: a
+// workgroup owns 256 query rows, each wave 32 (two waves per SIMD).  Each K,
+// V or K^T operand read from LDS feeds 32 query columns, so the LDS bytes per
+// product are about 0.6 of the 16-row kernel's (whose Q sits in registers).
+// The query sits in the MFMA column: D, the dS
+// row sums and the selector terms are per-lane values plus one exchange
+// between the two 32-lane halves.  Q sits in LDS, dO in registers.  64-key K
+// and V tiles (and the ks rows of the tile's units) arrive by direct global ->
+// LDS loads into two buffers, diagonal tile first; K^T for dQ^T = K^T dS^T
+// comes from transposing reads in the key order of the dS^T operand slots.
+// --------------------------------------------------------------------------
+constexpr int kDq32Waves = 8, kDq32Threads = 64 * kDq32Waves, kDq32Rows = 32 * kDq32Waves;
+
+template <int DS, int UB>
+__global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
+    const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
+    bf16* __restrict__ dq, bf16* __restrict__ dqs, float* __restrict__ dz,
+    float* __restrict__ rowd, int tqp, Dims D, int nqt, int xcd_groups) {
+  constexpr int HD = 128, KP = 144, TE = kBlock * KP;  // 72-dword LDS rows
+  constexpr int NI = TE / 512;                         // 1 KB direct loads per tile and tensor
+  constexpr int XI = (NI + kDq32Waves - 1) / kDq32Waves;
+  constexpr int DH = DS / 2;                           // selector dims per lane half
+  constexpr int BU = kBlock / UB;                      // tokens per gate unit
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  __shared__ __align__(16) bf16 K0[TE];
+  __shared__ __align__(16) bf16 K1[TE];
+  __shared__ __align__(16) bf16 V0[TE];
+  __shared__ __align__(16) bf16 V1[TE];
+  __shared__ __align__(16) bf16 S0[UB * DS];
+  __shared__ __align__(16) bf16 S1[UB * DS];
+  __shared__ __align__(16) bf16 Qs[kDq32Rows * KP];  // the workgroup's Q rows
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const QTile tm = map_q_tile(blockIdx.x, nqt, D, xcd_groups);
+  const int b = tm.b, h = tm.h, qt = tm.qt;
+  const int g = h / D.hpg, sh = h / D.hps;
+  const int wq0 = qt * kDq32Rows + wave * 32;
+  const int qi = wq0 + l32;
+  const bool valid = qi < D.tq;
+  const int qc = min(qi, D.tq - 1);
+  const int t = D.qoff + qc;
+  const int c = t / BU;       // historical units of the row
+  const int ct = t / kBlock;  // the row's own 64-key tile
+  const int c_lo = (D.qoff + min(wq0, D.tq - 1)) / kBlock;
+  const int c_hi = (D.qoff + min(wq0 + 31, D.tq - 1)) / kBlock;
+  const int c_end = (D.qoff + min(qt * kDq32Rows + kDq32Rows - 1, D.tq - 1)) / kBlock;
+  const size_t row = ((size_t)b * D.hq + h) * D.tq + qc;
+
+  // zero dz[row, j] for j >= c(row) (coalesced over the workgroup's rows)
+  for (int r = 0; r < kDq32Rows; ++r) {
+    const int i = qt * kDq32Rows + r;
+    if (i >= D.tq) break;
+    const int cr = (D.qoff + i) / BU;
+    float* zr = dz + (((size_t)b * D.hq + h) * D.tq + i) * D.nb;
+    for (int jj = cr + tid; jj < D.nb; jj += kDq32Threads) zr[jj] = 0.f;
+  }
+
+  // Q and dO as B operands (lane: query l32, dims 16 s + 8 hh .. + 7): dO in
+  // registers, Q in LDS (each lane reads back only what it wrote), which
+  // leaves the registers for two waves per SIMD
+  const int qbase = (32 * wave + l32) * KP + 8 * hh;
+  bf16x8 df[8];
+  float dlt = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    *(bf16x8*)&Qs[qbase + 16 * s] = *(const bf16x8*)(q + row * HD + 16 * s + 8 * hh);
+    df[s] = *(const bf16x8*)(dout + row * HD + 16 * s + 8 * hh);
+    const bf16x8 of = *(const bf16x8*)(o + row * HD + 16 * s + 8 * hh);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dlt = fmaf(to_f32(df[s][e]), to_f32(of[e]), dlt);
+  }
+  dlt += __shfl_xor(dlt, 32);
+  // Row data for the dK/dV kernel, unit-major so that the rows of one unit
+  // are contiguous: slot u < nb holds, for each row, the log2-domain offset
+  // of unit u's logits (gate bias minus the row's log-sum-exp; -inf past the
+  // row's own unit), slot nb the row's D; rows padded to tqp (padding: -inf,
+  // D 0).  The offsets are the ones this kernel applies itself.
+  const size_t rbase = ((size_t)b * D.hq + h) * (size_t)(D.nb + 1) * tqp + qi;
+  const bool rw = hh == 0 && qi < tqp;
+  if (rw) rowd[rbase + (size_t)D.nb * tqp] = valid ? dlt : 0.f;
+  // this lane's half of the row's qs as bf16 pairs (packed dot products, as
+  // in the forward), and its half of the dqs accumulator
+  bf16x2 qsv[DS / 4];
+  float dqsa[DH];
+#pragma unroll
+  for (int e = 0; e < DS / 4; ++e) qsv[e] = *(const bf16x2*)(qs + row * DS + hh * DH + 2 * e);
+#pragma unroll
+  for (int e = 0; e < DH; ++e) dqsa[e] = 0.f;
+  const float lam_t = c > 0 ? lam[row] : 0.f;
+  const float l2 = lse[row] * kLog2e;
+  const bf16* ksb = ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS;
+  const bf16* kb = k + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
+  const bf16* vb = v + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
+  const float c1 = D.sm_scale * kLog2e;
+  f32x16 dqa[4];
+#pragma unroll
+  for (int dm = 0; dm < 4; ++dm) dqa[dm] = f32x16{};
+  float sdb = 0.f;
+
+  // Tiles go global -> LDS by direct loads: 1 KB instruction ins = wave +
+  // kDq32Waves x fills LDS slots 64 ins .. 64 ins + 63 of K and of V (18
+  // 16-byte slots per row, the two padding slots reloading chunk 0); wave 0
+  // loads the ks rows of the tile's units.
+  unsigned toff[XI];
+#pragma unroll
+  for (int x = 0; x < XI; ++x)
+    toff[x] = 2 * tslot_src(min((wave + kDq32Waves * x) * 64 + lane, kBlock * 18 - 1));
+  auto issue = [&](int j, bf16* Kd, bf16* Vd, bf16* Sd) {
+    const char* const kt = (const char*)(kb + (size_t)j * kBlock * HD);
+    const char* const vt = (const char*)(vb + (size_t)j * kBlock * HD);
+#pragma unroll
+    for (int x = 0; x < XI; ++x) {
+      const int ins = wave + kDq32Waves * x;
+      if (ins < NI) {
+        __builtin_amdgcn_global_load_lds(kt + toff[x], Kd + ins * 512, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + toff[x], Vd + ins * 512, 16, 0, 0);
+      }
+    }
+    if (wave == 0 && lane < UB * DS / 8) {
+      const bf16* const src = ksb + (size_t)j * UB * DS + lane * 8;
+      __builtin_amdgcn_global_load_lds(src, Sd, 16, 0, 0);
+    }
+  };
+  // per-lane part of the transposing K^T reads: lane 4 kk + a of each 16-lane
+  // group points at key row 4 hh + kk, columns 16 ((lane >> 4) & 1) + 4 a
+  const int kbase = (4 * hh + ((lane & 15) >> 2)) * KP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // unit of this lane's key 32 mt + 8 (r / 4) + 4 hh + r % 4 within the tile
+  auto unit = [](int mt, int r) { return UB == 1 ? 0 : (UB == 2 ? mt : 2 * mt + r / 8); };
+
+  auto compute = [&](int j, const bf16* Ks, const bf16* Vs, const bf16* Ss) {
+    if (j > c_hi) return;
+    float bias2[UB];
+#pragma unroll
+    for (int ub = 0; ub < UB; ++ub) bias2[ub] = 0.f;
+    if (UB == 1 ? j < c_hi : j <= c_hi) {
+#pragma unroll
+      for (int ub = 0; ub < UB; ++ub) {
+        const bf16x2* kr = (const bf16x2*)(Ss + ub * DS + hh * DH);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < DS / 4; ++e)
+          part = __builtin_amdgcn_fdot2_f32_bf16(qsv[e], kr[e], part, false);
+        part += __shfl_xor(part, 32);
+        if (j * UB + ub < c) bias2[ub] = (D.sel_scale * part - lam_t) * kLog2e;
+      }
+    }
+    if (rw) {
+#pragma unroll
+      for (int ub = 0; ub < UB; ++ub) {
+        const int ju = j * UB + ub;
+        rowd[rbase + (size_t)ju * tqp] = valid && ju <= c ? bias2[ub] - l2 : -INFINITY;
+      }
+    }
+    // S^T and dP^T: two 32-key M-tiles x 32 queries each
+    f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 qb = *(const bf16x8*)&Qs[qbase + 16 * s];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int oo = (32 * mt + l32) * KP + 16 * s + 8 * hh;
+        sacc[mt] = mfma32(*(const bf16x8*)&Ks[oo], qb, sacc[mt]);
+        pacc[mt] = mfma32(*(const bf16x8*)&Vs[oo], df[s], pacc[mt]);
+      }
+    }
+    float pv[2][16];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pv[mt][r] = exp2_raw(fmaf(sacc[mt][r], c1, bias2[unit(mt, r)] - l2));
+    if (j >= c_lo) {  // tile meets some row's own tile: cut keys after the row (or the tile)
+      const int mlim = j < ct ? kBlock : (j > ct ? -1 : t - j * kBlock - 4 * hh);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * mt + 8 * (r / 4) + (r % 4) > mlim) pv[mt][r] = 0.f;
+    }
+    float dsum[UB];
+#pragma unroll
+    for (int ub = 0; ub < UB; ++ub) dsum[ub] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ds = pv[mt][r] * (pacc[mt][r] - dlt);
+        sacc[mt][r] = ds;
+        dsum[unit(mt, r)] += ds;
+      }
+    }
+#pragma unroll
+    for (int ub = 0; ub < UB; ++ub) dsum[ub] += __shfl_xor(dsum[ub], 32);
+    // the row's own tile comes first (tiles run from the diagonal down): its
+    // current unit gives sum_{j'<c} dbeta before any historical unit
+    if (j == ct) {
+#pragma unroll
+      for (int ub = 0; ub < UB; ++ub)
+        if (j * UB + ub == c) sdb = -dsum[ub];
+    }
+#pragma unroll
+    for (int ub = 0; ub < UB; ++ub) {
+      if (j * UB + ub < c) {
+        const float dzv = dsum[ub] - exp2_raw(bias2[ub]) * sdb;
+        if (valid && hh == 0) dz[row * D.nb + j * UB + ub] = dzv;
+        const bf16x2* kr = (const bf16x2*)(Ss + ub * DS + hh * DH);
+#pragma unroll
+        for (int e = 0; e < DS / 4; ++e) {
+          const bf16x2 kv = kr[e];
+          dqsa[2 * e] = fmaf(dzv, to_f32(kv[0]), dqsa[2 * e]);
+          dqsa[2 * e + 1] = fmaf(dzv, to_f32(kv[1]), dqsa[2 * e + 1]);
+        }
+      }
+    }
+    // dQ^T += K^T dS^T: the B slots of a lane are keys 16 pp + 4 hh + (0..3,
+    // 8..11) of M-tile mt, and the transposing reads give K^T in that order
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        bf16x8 sb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sb[e] = (bf16)sacc[mt][8 * pp + e];
+#pragma unroll
+        for (int dm = 0; dm < 4; ++dm) {
+          const bf16* kp = &Ks[kbase + (32 * mt + 16 * pp) * KP + 32 * dm];
+          const bf16x4 lo = ds_read_tr(kp);
+          const bf16x4 hi = ds_read_tr(kp + 8 * KP);
+          dqa[dm] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), sb, dqa[dm]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  const int ntiles = c_end + 1;  // tiles c_end, c_end - 1, ..., 0
+  issue(c_end, K0, V0, S0);
+  wait_vmem();
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    if (it + 1 < ntiles) issue(c_end - it - 1, K1, V1, S1);
+    compute(c_end - it, K0, V0, S0);
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 >= ntiles) break;
+    if (it + 2 < ntiles) issue(c_end - it - 2, K0, V0, S0);
+    compute(c_end - it - 1, K1, V1, S1);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  if (valid) {
+    bf16* qr = dq + row * HD + 4 * hh;
+#pragma unroll
+    for (int dm = 0; dm < 4; ++dm) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(dqa[dm][4 * rr + e] * D.sm_scale);
+        *(bf16x4*)(qr + 32 * dm + 8 * rr) = w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < DH; ++e) dqs[row * DS + hh * DH + e] = (bf16)(dqsa[e] * D.sel_scale);
   }
 }
 
@@ -1166,11 +1443,24 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   const int xg = groups % 8 == 0 ? groups / 8 : 0;
   hipError_t e;
   if constexpr (HD == 128) {
-    const int nqtw = (D.tq + kDqRows - 1) / kDqRows;
-    hipLaunchKernelGGL((bwd_dq16_kernel<DS, UB>), dim3(D.batch * D.hq * nqtw), dim3(kDqThreads),
-                       0, st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)o,
-                       (const bf16*)dout, lse, (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dq,
-                       (bf16*)dqs, dzp, rowd, W.tqp, D, nqtw, xg);
+    // The 32-row kernel fits two waves per SIMD (256 registers each) while
+    // the selector terms of a tile (ds / 2 qs and dqs values per lane, UB ks
+    // rows) stay small; wider selectors take the 16-row kernel.
+    if constexpr (DS <= 32 && DS * UB <= 64) {
+      const int nqtw = (D.tq + kDq32Rows - 1) / kDq32Rows;
+      hipLaunchKernelGGL((bwd_dq32_kernel<DS, UB>), dim3(D.batch * D.hq * nqtw),
+                         dim3(kDq32Threads), 0, st, (const bf16*)q, (const bf16*)k,
+                         (const bf16*)v, (const bf16*)o, (const bf16*)dout, lse,
+                         (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dq, (bf16*)dqs, dzp, rowd,
+                         W.tqp, D, nqtw, xg);
+    } else {
+      const int nqtw = (D.tq + kDqRows - 1) / kDqRows;
+      hipLaunchKernelGGL((bwd_dq16_kernel<DS, UB>), dim3(D.batch * D.hq * nqtw),
+                         dim3(kDqThreads), 0, st, (const bf16*)q, (const bf16*)k,
+                         (const bf16*)v, (const bf16*)o, (const bf16*)dout, lse,
+                         (const bf16*)qs, (const bf16*)ks, lam, (bf16*)dq, (bf16*)dqs, dzp, rowd,
+                         W.tqp, D, nqtw, xg);
+    }
   } else {
   const int nqt = (D.tq + 127) / 128;
   hipLaunchKernelGGL((bwd_dq_kernel<HD, DS>), dim3(D.batch * D.hq * nqt), dim3(256), 0, st,
