@@ -107,7 +107,7 @@ def cpu_baseline(T: int):
 # is built from (a change to any of them voids stored HBM-traffic counters).
 KERNELS = {
     "bwd_dkdv": ("bwd_dkdv16_kernel<32, 1>", ("attn_bwd.hip", "sas_device.h", "sas_internal.h")),
-    "bwd_dq": ("bwd_dq16_kernel<32, 1>", ("attn_bwd.hip", "sas_device.h", "sas_internal.h")),
+    "bwd_dq": ("bwd_dq32_kernel<32, 1>", ("attn_bwd.hip", "sas_device.h", "sas_internal.h")),
     "fwd": ("attn_fwd_kernel<128, 32, 1>", ("attn_fwd.hip", "sas_device.h", "sas_internal.h")),
 }
 
