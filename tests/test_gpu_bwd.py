@@ -24,6 +24,10 @@ SMALL = {
     "ds64_hks": W["train_8k"].with_(name="ds64_hks", batch=1, hq=4, hkv=2, hks=4, tq=320,
                                     tk=320, ds=64),
     "one_block": W["train_8k"].with_(name="one_block", batch=1, hq=2, hkv=1, tq=64, tk=64),
+    # d = 128 with a 16-dim selector: three 256-row dQ workgroups, the last
+    # with 8 rows, and a query offset of 56
+    "ds16_q520": W["train_8k"].with_(name="ds16_q520", batch=1, hq=4, hkv=2, tq=520, tk=576,
+                                     ds=16),
 }
 
 

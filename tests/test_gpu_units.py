@@ -193,6 +193,7 @@ BWD_SMALL = {
     "q_offset": dict(batch=1, hq=4, hkv=1, tq=160, tk=1024),
     "ragged_q": dict(batch=1, hq=4, hkv=2, tq=200, tk=448),
     "ds64_hks": dict(batch=1, hq=4, hkv=2, hks=4, tq=320, tk=320, ds=64),
+    "ds16_q520": dict(batch=1, hq=4, hkv=2, tq=520, tk=576, ds=16),
 }
 
 
