@@ -685,15 +685,23 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
     }
     // S^T and dP^T: two 32-key M-tiles x 32 queries each
     f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+    // operand i (step i / 4, M-tile (i / 2) % 2, K or V by i % 2) is read
+    // while product i - 1 runs; the step's Q operand after its last use
+    auto opnd = [&](int i) __attribute__((always_inline)) {
+      const int oo = (32 * ((i >> 1) & 1) + l32) * KP + 16 * (i >> 2) + 8 * hh;
+      return *(const bf16x8*)&((i & 1) ? Vs : Ks)[oo];
+    };
+    bf16x8 ob[2], qb = *(const bf16x8*)&Qs[qbase];
+    ob[0] = opnd(0);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 qb = *(const bf16x8*)&Qs[qbase + 16 * s];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int oo = (32 * mt + l32) * KP + 16 * s + 8 * hh;
-        sacc[mt] = mfma32(*(const bf16x8*)&Ks[oo], qb, sacc[mt]);
-        pacc[mt] = mfma32(*(const bf16x8*)&Vs[oo], df[s], pacc[mt]);
-      }
+    for (int i = 0; i < 32; ++i) {
+      if (i < 31) ob[(i + 1) & 1] = opnd(i + 1);
+      if ((i & 3) == 3 && i < 31) qb = *(const bf16x8*)&Qs[qbase + 16 * ((i >> 2) + 1)];
+      const int s = i >> 2, mt = (i >> 1) & 1;
+      if (i & 1)
+        pacc[mt] = mfma32(ob[i & 1], df[s], pacc[mt]);
+      else
+        sacc[mt] = mfma32(ob[i & 1], qb, sacc[mt]);
     }
     float pv[2][16];
 #pragma unroll
