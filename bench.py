@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import math
+from fractions import Fraction
 import os
 import platform
 import sys
@@ -54,14 +55,15 @@ def causal_pairs(tq, tk):
 def sparse_pairs(w):
     """Attended pairs of one head under a top-K block budget (current block
     causal + n(t) full historical blocks, n(t) = min(K, c), further capped at
-    ceil(frac * c) for a budget proportional to the history)."""
+    ceil(num c / den) for a budget that is the fraction num / den of the history)."""
     tot = 0
+    fr = Fraction(repr(w.frac)) if w.frac > 0 else None
     for i in range(w.tq):
         t = w.tk - w.tq + i
         c = t // w.block
         n = min(w.topk, c)
-        if w.frac > 0:
-            n = min(n, math.ceil(w.frac * c))
+        if fr is not None:
+            n = min(n, -(-fr.numerator * c // fr.denominator))
         tot += n * w.block + (t - c * w.block + 1)
     return tot
 

@@ -231,19 +231,20 @@ sas_status sas_topk_blocks(const sas_shape* shape, int32_t topk, int32_t renorm,
                                      shape->sel_dtype == SAS_BF16, (hipStream_t)stream));
 }
 
-sas_status sas_topk_blocks_budget(const sas_shape* shape, int32_t kmax, float frac,
-                                  int32_t renorm, const void* qs, const void* ks, int32_t* idx,
-                                  float* bias, void* stream) {
+sas_status sas_topk_blocks_budget(const sas_shape* shape, int32_t kmax, int32_t frac_num,
+                                  int32_t frac_den, int32_t renorm, const void* qs,
+                                  const void* ks, int32_t* idx, float* bias, void* stream) {
   sas::Dims D;
   sas_status r = resolve(shape, &D);
   if (r != SAS_OK) return r;
-  if (kmax < 1 || (renorm != 0 && renorm != 1) || frac != frac) return SAS_ERR_SHAPE;
+  if (kmax < 1 || (renorm != 0 && renorm != 1) || frac_den < 1) return SAS_ERR_SHAPE;
   if ((r = check_ptrs({qs, ks, idx, bias})) != SAS_OK) return r;
   if (!sas::topk_budget_supported(D, kmax)) return SAS_ERR_UNSUPPORTED;
   if ((int64_t)D.batch * D.hq * D.tq * kmax >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
   if (D.batch == 0) return SAS_OK;
-  return hip_status(sas::launch_topk_budget(qs, ks, kmax, frac, renorm, idx, bias, D,
-                                            shape->sel_dtype == SAS_BF16, (hipStream_t)stream));
+  return hip_status(sas::launch_topk_budget(qs, ks, kmax, frac_num, frac_den, renorm, idx, bias,
+                                            D, shape->sel_dtype == SAS_BF16,
+                                            (hipStream_t)stream));
 }
 
 static sas_status sparse_fwd_impl(const sas_shape* shape, int32_t topk, const void* q,

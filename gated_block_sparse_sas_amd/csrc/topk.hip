@@ -274,8 +274,8 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
 }
 
 // Budgeted / large-K variant: one wavefront per query row keeps the
-// n_t = min(kmax, c(t), ceil(frac c(t))) best blocks (frac <= 0: no
-// fraction).  Scores go to LDS (same SelQ dot product as above) and become
+// n_t = min(kmax, c(t), ceil(num c(t) / den)) best blocks (num <= 0: no
+// fraction; the ceiling in exact integer arithmetic).  Scores go to LDS (same SelQ dot product as above) and become
 // order-preserving 32-bit keys; a radix select (8 bits per pass, LDS
 // histogram) narrows down the n_t-th largest key, stopping early once the bin
 // that holds it is needed whole; keys tied with it are taken in block order;
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
 template <int DS, typename ST>
 __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__ qs,
                                                           const ST* __restrict__ ks, int kmax,
-                                                          float frac, int renorm,
+                                                          int fnum, int fden, int renorm,
                                                           int* __restrict__ idx,
                                                           float* __restrict__ bias, Dims D,
                                                           int kp2, int wpg) {
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
   const int b = (int)(row / ((size_t)D.tq * D.hq));
   const int c = (D.qoff + i) / D.blk;
   int n = min(kmax, c);
-  if (frac > 0.f) n = min(n, (int)ceil((double)frac * (double)c));
+  if (fnum > 0) n = (int)min((long long)n, ((long long)fnum * c + fden - 1) / fden);
   // scores and the gate normaliser over the whole history
   SelQ<DS, ST> qsv;
   qsv.load(qs + row * DS);
@@ -440,7 +440,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
 }
 
 template <int DS, typename ST>
-static hipError_t launch_select_t(const void* qs, const void* ks, int kmax, float frac, int renorm,
+static hipError_t launch_select_t(const void* qs, const void* ks, int kmax, int fnum, int fden,
+                                  int renorm,
                                   int* idx, float* bias, const Dims& D, hipStream_t st) {
   int kp2 = 1;
   while (kp2 < kmax) kp2 <<= 1;
@@ -449,8 +450,8 @@ static hipError_t launch_select_t(const void* qs, const void* ks, int kmax, floa
   while (wpg > 1 && per * wpg > 65536) wpg >>= 1;
   const size_t nrows = (size_t)D.batch * D.hq * D.tq;
   hipLaunchKernelGGL((topk_select_kernel<DS, ST>), dim3((unsigned)((nrows + wpg - 1) / wpg)),
-                     dim3(64 * wpg), per * wpg, st, (const ST*)qs, (const ST*)ks, kmax, frac,
-                     renorm, idx, bias, D, kp2, wpg);
+                     dim3(64 * wpg), per * wpg, st, (const ST*)qs, (const ST*)ks, kmax, fnum,
+                     fden, renorm, idx, bias, D, kp2, wpg);
   return hipGetLastError();
 }
 
@@ -460,13 +461,15 @@ bool topk_budget_supported(const Dims& D, int kmax) {
   return kmax <= 1024 && (size_t)(D.nb + 256 + 2 * kp2) * sizeof(unsigned) <= 65536;
 }
 
-hipError_t launch_topk_budget(const void* qs, const void* ks, int kmax, float frac, int renorm,
+hipError_t launch_topk_budget(const void* qs, const void* ks, int kmax, int fnum, int fden,
+                              int renorm,
                               int* idx, float* bias, const Dims& D, bool sel_bf16,
                               hipStream_t st) {
 #define SAS_SEL_CASE(DSV)                                                                     \
   case DSV:                                                                                   \
-    return sel_bf16 ? launch_select_t<DSV, bf16>(qs, ks, kmax, frac, renorm, idx, bias, D, st) \
-                    : launch_select_t<DSV, float>(qs, ks, kmax, frac, renorm, idx, bias, D, st);
+    return sel_bf16                                                                           \
+               ? launch_select_t<DSV, bf16>(qs, ks, kmax, fnum, fden, renorm, idx, bias, D, st) \
+               : launch_select_t<DSV, float>(qs, ks, kmax, fnum, fden, renorm, idx, bias, D, st);
   switch (D.ds) {
     SAS_SEL_CASE(16)
     SAS_SEL_CASE(32)
@@ -501,7 +504,7 @@ static hipError_t launch_topk_t(const void* qs, const void* ks, int K, int renor
   // K >= 16: the radix-select kernel (same order and tie rule, frac = 0) costs
   // a few passes over a row's scores instead of K argmax rounds
   if (K >= 16 && topk_budget_supported(D, K))
-    return launch_select_t<DS, ST>(qs, ks, K, 0.f, renorm, idx, bias, D, st);
+    return launch_select_t<DS, ST>(qs, ks, K, 0, 1, renorm, idx, bias, D, st);
   const size_t per = (size_t)(D.nb + K) * sizeof(float);
   int wpg = 4;
   while (wpg > 1 && per * wpg > 65536) wpg >>= 1;

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from fractions import Fraction
 
 import torch
 
@@ -73,7 +74,7 @@ def load():
         lib.sas_attn_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P]
         lib.sas_attn_bwd.argtypes = [P] * 17 + [SZ, P]
         lib.sas_topk_blocks.argtypes = [P, I32, I32, P, P, P, P, P]
-        lib.sas_topk_blocks_budget.argtypes = [P, I32, ctypes.c_float, I32, P, P, P, P, P]
+        lib.sas_topk_blocks_budget.argtypes = [P, I32, I32, I32, I32, P, P, P, P, P]
         lib.sas_sparse_fwd.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P]
         lib.sas_attn_bwd_ev.argtypes = [P] * 17 + [SZ, P, I32, P]
         lib.sas_sparse_fwd_ev.argtypes = [P, I32, P, P, P, P, P, P, P, P, SZ, P, I32, P]
@@ -222,16 +223,28 @@ def topk_blocks(qs, ks, topk, tk, block=64, renorm=0, sel_scale=None):
     return idx, bias
 
 
+def _ratio(frac):
+    """(numerator, denominator) of a budget fraction: a float is taken as the
+    decimal it prints as (0.25 -> 1/4), a Fraction or int as is, a pair as given."""
+    if isinstance(frac, tuple):
+        num, den = int(frac[0]), int(frac[1])
+    else:
+        f = Fraction(repr(frac)) if isinstance(frac, float) else Fraction(frac)
+        num, den = f.numerator, f.denominator
+    return (0, 1) if num <= 0 else (num, den)
+
+
 def topk_blocks_budget(qs, ks, kmax, frac, tk, block=64, renorm=0, sel_scale=None):
-    """Top-K with n_t = min(kmax, c(t), ceil(frac c(t))) blocks per row (frac <= 0:
-    the fixed budget).  Returns (idx int32, bias float32), kmax slots per row."""
+    """Top-K with n_t = min(kmax, c(t), ceil(num c(t) / den)) blocks per row for
+    the exact fraction num / den of ``frac`` (<= 0: the fixed budget).  Returns
+    (idx int32, bias float32), kmax slots per row."""
     b, hq, tq, ds = qs.shape
     hks = ks.shape[1]
     sh = make_shape(b, hq, hks, tq, tk, 64, ds, block, hks, 0.0, sel_scale, _dt(qs), _dt(qs))
     idx = torch.empty((b, hq, tq, kmax), dtype=torch.int32, device=qs.device)
     bias = torch.empty((b, hq, tq, kmax), dtype=torch.float32, device=qs.device)
     _check("sas_topk_blocks_budget",
-           load().sas_topk_blocks_budget(ctypes.byref(sh), int(kmax), ctypes.c_float(frac),
+           load().sas_topk_blocks_budget(ctypes.byref(sh), int(kmax), *_ratio(frac),
                                          int(renorm), _p(qs), _p(ks), _p(idx), _p(bias),
                                          _stream(qs)))
     return idx, bias

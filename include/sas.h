@@ -136,19 +136,20 @@ sas_status sas_topk_blocks(const sas_shape* shape, int32_t topk, int32_t renorm,
                            const void* ks, int32_t* idx, float* bias, void* stream);
 
 /* Hard Top-K with a budget proportional to each row's history: row t keeps
- * n_t = min(kmax, c(t), ceil(frac * c(t))) blocks (the ceiling taken in
- * double precision on (double)frac * c(t)); frac <= 0 means no fraction
- * (n_t = min(kmax, c(t)), the fixed budget of sas_topk_blocks, any kmax).
- * Order, padding (idx -1, bias -inf in slots n_t .. kmax-1) and the two bias
- * modes are those of sas_topk_blocks.  idx, bias: [batch, hq, tq, kmax].
- * 1 <= kmax <= 1024; frac must not be NaN (SAS_ERR_SHAPE).  Needs
- * 4 (nb + 256 + 2 * next_pow2(kmax)) bytes of LDS per row, at most
+ * n_t = min(kmax, c(t), ceil(frac_num * c(t) / frac_den)) blocks, the
+ * fraction given as an exact ratio and the ceiling taken in integer
+ * arithmetic (1/4 keeps a quarter of the history); frac_num <= 0 means no
+ * fraction (n_t = min(kmax, c(t)), the fixed budget of sas_topk_blocks, any
+ * kmax).  Order, padding (idx -1, bias -inf in slots n_t .. kmax-1) and the
+ * two bias modes are those of sas_topk_blocks.  idx, bias: [batch, hq, tq,
+ * kmax].  1 <= kmax <= 1024 and frac_den >= 1 (SAS_ERR_SHAPE otherwise).
+ * Needs 4 (nb + 256 + 2 * next_pow2(kmax)) bytes of LDS per row, at most
  * 64 KiB (SAS_ERR_UNSUPPORTED beyond).  Source: blog, "Implementation and
  * Efficiency" (attention restricted to the top 25% of the context at 32k);
  * both abstracts (hard Top-K under an attention budget). */
-sas_status sas_topk_blocks_budget(const sas_shape* shape, int32_t kmax, float frac,
-                                  int32_t renorm, const void* qs, const void* ks, int32_t* idx,
-                                  float* bias, void* stream);
+sas_status sas_topk_blocks_budget(const sas_shape* shape, int32_t kmax, int32_t frac_num,
+                                  int32_t frac_den, int32_t renorm, const void* qs,
+                                  const void* ks, int32_t* idx, float* bias, void* stream);
 
 /* Top-K sparse attention forward (prefill: tq == tk; decode: tq == 1; any
  * 1 <= tq <= tk): every row attends its current block (causal, bias 0) plus

@@ -16,6 +16,7 @@ from .oracle import (  # noqa: F401
     attn_bwd,
     topk_blocks,
     topk_budget,
+    budget_ratio,
     threshold_blocks,
     sparse_fwd,
     num_threads,

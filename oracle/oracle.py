@@ -8,6 +8,7 @@ layout described in ``sas_oracle.h`` and returns float64 results.
 from __future__ import annotations
 
 import ctypes
+from fractions import Fraction
 import math
 import os
 import subprocess
@@ -82,8 +83,8 @@ def _load():
         lib.oracle_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, P, P, P, P, I64, P, P, P,
                                         I64, P, P]
         lib.oracle_topk_blocks.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
-        lib.oracle_topk_budget.argtypes = [P, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, P,
-                                           P, P, P, P]
+        lib.oracle_topk_budget.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, P, P, P, P, P]
         lib.oracle_threshold_blocks.argtypes = [P, ctypes.c_float, ctypes.c_int32, P, P, P, P,
                                                 P, P]
         lib.oracle_sparse_fwd.argtypes = [P, ctypes.c_int32, P, P, P, P, P, I64, P, P, P]
@@ -207,15 +208,33 @@ def topk_blocks(shape: OracleShape, topk: int, qs=None, ks=None, z=None, renorm:
     return idx, bias
 
 
-def topk_budget(shape: OracleShape, kmax: int, frac: float, qs=None, ks=None, z=None,
+def budget_ratio(frac):
+    """The budget fraction as an exact (numerator, denominator): a float is
+    read as the decimal it prints as (0.3 -> 3/10), a Fraction or an int as
+    is, a (num, den) pair as given; frac <= 0 -> (0, 1), no fraction."""
+    if isinstance(frac, tuple):
+        num, den = int(frac[0]), int(frac[1])
+    else:
+        f = Fraction(repr(frac)) if isinstance(frac, float) else Fraction(frac)
+        num, den = f.numerator, f.denominator
+    if num <= 0:
+        return 0, 1
+    if den < 1 or num >= 2 ** 31 or den >= 2 ** 31:
+        raise ValueError("budget fraction %r does not fit int32" % (frac,))
+    return num, den
+
+
+def topk_budget(shape: OracleShape, kmax: int, frac, qs=None, ks=None, z=None,
                 renorm: int = 0):
-    """Top-K with n_t = min(kmax, ceil(frac * c(t))) blocks per row (frac <= 0:
-    the fixed budget).  Returns (idx int32 [B,Hq,Tq,kmax], bias float64)."""
+    """Top-K with n_t = min(kmax, ceil(num * c(t) / den)) blocks per row, the
+    fraction num / den taken exactly (see budget_ratio; frac <= 0: the fixed
+    budget).  Returns (idx int32 [B,Hq,Tq,kmax], bias float64)."""
     qs, ks, z = map(_f64, (qs, ks, z))
+    num, den = budget_ratio(frac)
     idx = np.empty((shape.batch, shape.hq, shape.tq, kmax), dtype=np.int32)
     bias = np.empty((shape.batch, shape.hq, shape.tq, kmax))
     st = shape.c_struct()
-    _check(_load().oracle_topk_budget(ctypes.byref(st), int(kmax), ctypes.c_float(frac),
+    _check(_load().oracle_topk_budget(ctypes.byref(st), int(kmax), num, den,
                                       int(renorm), _ptr(qs), _ptr(ks), _ptr(z), _ptr(idx),
                                       _ptr(bias)), "topk_budget")
     return idx, bias

@@ -431,28 +431,31 @@ static int by_score_desc(const void* pa, const void* pb) {
   return a->j < b->j ? -1 : (a->j > b->j ? 1 : 0);
 }
 
-static int topk_impl(const oracle_shape* s, int32_t topk, double frac, int32_t renorm,
-                     const double* qs, const double* ks, const double* zin, int32_t* idx,
-                     double* bias);
+static int topk_impl(const oracle_shape* s, int32_t topk, int64_t fnum, int64_t fden,
+                     int32_t renorm, const double* qs, const double* ks, const double* zin,
+                     int32_t* idx, double* bias);
 
 int oracle_topk_blocks(const oracle_shape* s, int32_t topk, int32_t renorm, const double* qs,
                        const double* ks, const double* zin, int32_t* idx, double* bias) {
-  return topk_impl(s, topk, 0.0, renorm, qs, ks, zin, idx, bias);
+  return topk_impl(s, topk, 0, 1, renorm, qs, ks, zin, idx, bias);
 }
 
-/* Budget proportional to the history: row t keeps n_t = min(kmax, ceil(frac *
- * c(t))) blocks (frac <= 0: n_t = min(kmax, c(t)), the fixed budget).  The
- * blog's "top 25%" of the context at 32k is frac = 0.25.  idx / bias have
- * kmax slots per row, padded as for the fixed budget. */
-int oracle_topk_budget(const oracle_shape* s, int32_t kmax, float frac, int32_t renorm,
-                       const double* qs, const double* ks, const double* zin, int32_t* idx,
-                       double* bias) {
-  return topk_impl(s, kmax, (double)frac, renorm, qs, ks, zin, idx, bias);
+/* Budget proportional to the history: row t keeps n_t = min(kmax,
+ * ceil(frac_num * c(t) / frac_den)) blocks (frac_num <= 0: n_t = min(kmax,
+ * c(t)), the fixed budget).  The blog's "top 25%" of the context at 32k is
+ * the ratio 1/4; the ceiling of the exact ratio is taken in integers, so no
+ * rounding of the fraction changes a count.  idx / bias have kmax slots per
+ * row, padded as for the fixed budget. */
+int oracle_topk_budget(const oracle_shape* s, int32_t kmax, int32_t frac_num, int32_t frac_den,
+                       int32_t renorm, const double* qs, const double* ks, const double* zin,
+                       int32_t* idx, double* bias) {
+  if (frac_den < 1) return -1;
+  return topk_impl(s, kmax, frac_num, frac_den, renorm, qs, ks, zin, idx, bias);
 }
 
-static int topk_impl(const oracle_shape* s, int32_t topk, double frac, int32_t renorm,
-                     const double* qs, const double* ks, const double* zin, int32_t* idx,
-                     double* bias) {
+static int topk_impl(const oracle_shape* s, int32_t topk, int64_t fnum, int64_t fden,
+                     int32_t renorm, const double* qs, const double* ks, const double* zin,
+                     int32_t* idx, double* bias) {
   if (check_shape(s) || topk < 1) return -1;
   const int64_t nrows = (int64_t)s->batch * s->hq * s->tq;
 #pragma omp parallel for schedule(dynamic, 64)
@@ -468,8 +471,8 @@ static int topk_impl(const oracle_shape* s, int32_t topk, double frac, int32_t r
     }
     qsort(cand, (size_t)c, sizeof(scored), by_score_desc);
     int64_t n = c < topk ? c : topk;
-    if (frac > 0.0) {
-      const int64_t nb = (int64_t)ceil(frac * (double)c);
+    if (fnum > 0) {
+      const int64_t nb = (fnum * c + fden - 1) / fden; /* ceil(fnum c / fden), c >= 0 */
       if (nb < n) n = nb;
     }
     /* Bias of a selected block.  renorm = 0 (default): the training log-gate

@@ -75,11 +75,12 @@ int oracle_topk_blocks(const oracle_shape* s, int32_t topk, int32_t renorm,
                        const double* qs, const double* ks, const double* zin,
                        int32_t* idx, double* bias);
 /* Top-K with a budget proportional to the history: n_t = min(kmax,
- * ceil(frac * c(t))) blocks per row (frac <= 0: min(kmax, c(t))); kmax slots
- * per row, padded with -1 / -inf. */
-int oracle_topk_budget(const oracle_shape* s, int32_t kmax, float frac, int32_t renorm,
-                       const double* qs, const double* ks, const double* zin, int32_t* idx,
-                       double* bias);
+ * ceil(frac_num * c(t) / frac_den)) blocks per row, the ceiling of an exact
+ * ratio in integers (frac_num <= 0: min(kmax, c(t))); kmax slots per row,
+ * padded with -1 / -inf. */
+int oracle_topk_budget(const oracle_shape* s, int32_t kmax, int32_t frac_num, int32_t frac_den,
+                       int32_t renorm, const double* qs, const double* ks, const double* zin,
+                       int32_t* idx, double* bias);
 
 /* Dynamic-threshold selection: a historical block j < c is kept when its
  * normalised gate exp(z_j - lambda) >= theta (theta <= 0 keeps all).

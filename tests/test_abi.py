@@ -122,21 +122,23 @@ def test_topk_checks(lib):
 
 def test_topk_budget_checks(lib):
     sh = shape()
-    f = ctypes.c_float
-    lib.sas_topk_blocks_budget.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
-                                           ctypes.c_int32] + [ctypes.c_void_p] * 5
-    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 0, f(0.25), 0, A, A, A, A, STREAM) == 2
-    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 8, f(0.25), 2, A, A, A, A, STREAM) == 2
-    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 8, f(float("nan")), 0, A, A, A, A,
-                                      STREAM) == 2
-    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 8, f(0.25), 0, None, A, A, A, STREAM) == 1
-    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 8, f(0.25), 0, A, A, A, MIS, STREAM) == 4
-    assert lib.sas_topk_blocks_budget(ctypes.byref(sh), 2048, f(0.25), 0, A, A, A, A,
-                                      STREAM) == 5
+    i32 = ctypes.c_int32
+    lib.sas_topk_blocks_budget.argtypes = [ctypes.c_void_p, i32, i32, i32,
+                                           i32] + [ctypes.c_void_p] * 5
+    fn = lib.sas_topk_blocks_budget
+    assert fn(ctypes.byref(sh), 0, 1, 4, 0, A, A, A, A, STREAM) == 2       # kmax < 1
+    assert fn(ctypes.byref(sh), 8, 1, 4, 2, A, A, A, A, STREAM) == 2       # renorm
+    assert fn(ctypes.byref(sh), 8, 1, 0, 0, A, A, A, A, STREAM) == 2       # denominator 0
+    assert fn(ctypes.byref(sh), 8, 1, -4, 0, A, A, A, A, STREAM) == 2      # negative denominator
+    assert fn(ctypes.byref(sh), 8, 1, 4, 0, None, A, A, A, STREAM) == 1
+    assert fn(ctypes.byref(sh), 8, 1, 4, 0, A, A, A, MIS, STREAM) == 4
+    assert fn(ctypes.byref(sh), 2048, 1, 4, 0, A, A, A, A, STREAM) == 5
     big = shape(tk=1 << 20, tq=64)  # the row's scores no longer fit the kernel's LDS
-    assert lib.sas_topk_blocks_budget(ctypes.byref(big), 8, f(0.25), 0, A, A, A, A, STREAM) == 5
-    assert lib.sas_topk_blocks_budget(ctypes.byref(shape(batch=0)), 8, f(0.25), 0, A, A, A, A,
-                                      STREAM) == 0
+    assert fn(ctypes.byref(big), 8, 1, 4, 0, A, A, A, A, STREAM) == 5
+    assert fn(ctypes.byref(shape(batch=0)), 8, 1, 4, 0, A, A, A, A, STREAM) == 0
+    # no fraction (numerator <= 0) and fractions above one are valid
+    assert fn(ctypes.byref(shape(batch=0)), 8, 0, 1, 0, A, A, A, A, STREAM) == 0
+    assert fn(ctypes.byref(shape(batch=0)), 8, 5, 2, 0, A, A, A, A, STREAM) == 0
 
 
 def bwd(lib, sh, ws, n, **ptrs):

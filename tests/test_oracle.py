@@ -329,17 +329,16 @@ def test_topk_tie_goes_to_smaller_block():
 
 
 @pytest.mark.parametrize("renorm", [0, 1])
-@pytest.mark.parametrize("frac", [0.25, 0.3])
-def test_topk_budget_vs_sort(renorm, frac):
+@pytest.mark.parametrize("num,den", [(1, 4), (3, 10), (7, 10)])
+def test_topk_budget_vs_sort(renorm, num, den):
     S, x = make(hq=4, hkv=2, tq=90, tk=90, block=4)
     kmax = 5
-    idx, bias = oracle.topk_budget(S, kmax, frac, x["qs"], x["ks"], renorm=renorm)
+    idx, bias = oracle.topk_budget(S, kmax, (num, den), x["qs"], x["ks"], renorm=renorm)
     z, lam, _ = oracle.gate_scores(S, x["qs"], x["ks"])
-    f = float(np.float32(frac))  # the budget fraction travels as a float
     for h in range(S.hq):
         for t in range(S.tq):
             c = t // S.block
-            n = min(kmax, c, math.ceil(f * c))
+            n = min(kmax, c, -(-num * c // den))  # exact ceiling of num c / den
             zz = z[0, h, t, :c]
             order = np.lexsort((np.arange(c), -zz))[:n]
             np.testing.assert_array_equal(idx[0, h, t, :n], order)
@@ -355,6 +354,21 @@ def test_topk_budget_quarter_counts():
     for t in range(130):
         c = t // 4
         assert int((idx[0, 0, t] >= 0).sum()) == -(-c // 4)
+
+
+def test_topk_budget_exact_decimal_counts():
+    # the fraction is an exact ratio: 30 % of 10 blocks is 3 (a float32 0.3 is
+    # slightly above 3/10 and would round the count up to 4); 70 % of 10 is 7
+    # (0.7 * 10 is 7.000000000000001 in double)
+    S, x = make(hq=1, hkv=1, tq=64, tk=64, block=2)
+    for frac, want in ((0.3, {10: 3, 20: 6, 30: 9, 31: 10}), (0.7, {10: 7, 20: 14, 31: 22}),
+                       ((1, 3), {3: 1, 9: 3, 10: 4})):
+        idx, _ = oracle.topk_budget(S, 32, frac, x["qs"], x["ks"])
+        for c, n in want.items():
+            for t in (2 * c, 2 * c + 1):
+                assert int((idx[0, 0, t] >= 0).sum()) == n, (frac, c)
+    assert oracle.budget_ratio(0.3) == (3, 10) and oracle.budget_ratio(0.25) == (1, 4)
+    assert oracle.budget_ratio(0.0) == (0, 1) and oracle.budget_ratio(-1.0) == (0, 1)
 
 
 def test_topk_budget_nonpositive_frac_is_fixed_budget():
