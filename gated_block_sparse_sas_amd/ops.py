@@ -16,7 +16,8 @@ from fractions import Fraction
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsas.so")
+# SAS_LIBRARY names another build of the same library (the sanitizer run)
+LIB_PATH = os.environ.get("SAS_LIBRARY") or os.path.join(_HERE, "libsas.so")
 _lib = None
 
 SAS_F32, SAS_BF16 = 0, 1

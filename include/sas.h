@@ -75,7 +75,9 @@ typedef enum {
   SAS_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned            */
   SAS_ERR_UNSUPPORTED = 5, /* valid but not implemented for this shape    */
   SAS_ERR_WORKSPACE = 6,   /* workspace missing or too small              */
-  SAS_ERR_HIP = 7          /* a HIP launch failed                         */
+  SAS_ERR_HIP = 7,         /* a HIP launch failed                         */
+  SAS_STATUS_INT32 = 0x7FFFFFFF /* not a status: makes every int32 a valid value
+                                   of the type (status strings of unknown codes) */
 } sas_status;
 
 typedef enum { SAS_F32 = 0, SAS_BF16 = 1 } sas_dtype;

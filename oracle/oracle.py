@@ -19,12 +19,16 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sas_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# a separately built copy (the sanitizer run) may be named by the environment
+_LIB_ENV = os.environ.get("SAS_ORACLE_LIB")
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile ``sas_oracle.c`` into ``liboracle.so`` with gcc (fp64, OpenMP)."""
     global _lib
+    if _LIB_ENV:
+        return _LIB_ENV
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
@@ -73,9 +77,12 @@ class OracleShape:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_ENV:
+            lib = ctypes.CDLL(_LIB_ENV)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         lib.oracle_gate_scores.argtypes = [P, P, P, P, P, P]

@@ -1,0 +1,238 @@
+"""GPU vs oracle where the default workloads do not reach.
+
+* Long accumulations at full size: at train_32k, dK / dV of keys in blocks 0,
+  1 and 256 of kv group 0 (every one of the group's 4 x 32768 rows, or half of
+  them, feeds each such key) and dks of selector blocks 0, 1 and 256 (summed
+  over many 2048-row chunks of the dks reduction); the same at train_8k for
+  another group; a mid-size case (4 heads, 4608 tokens: three dks row chunks,
+  72 key blocks, 18 dQ workgroups per head) compared over whole tensors.
+* A bound per row next to the per-tensor relative L2, so that a few wholly
+  wrong rows cannot hide in a tensor norm: every row of dq, dz, dqs (per query
+  row), dk, dv (per key) and dks (per selector block) within 0.1 of its own
+  norm, or of 5 % of the tensor's median row norm for rows near zero.
+* Inputs that stress the softmax: explicit non-default scales, near one-hot
+  gates (qs, ks x 4), large logits (q, k x 4: logit std 4), and the
+  shift invariance of the gate through an augmented selector
+  (qs' = [qs, a / sigma], ks' = [ks, 1] adds a_t to every score of row t and
+  must change no output; Hugging Face abstract: the gates are normalised
+  over the historical context).
+Bars as elsewhere: bf16 O max-abs <= 2e-2, lse <= 1e-3, gradients rel-L2 <=
+5e-2, top-K bit-exact on tie-free rows.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gated_block_sparse_sas_amd import ops, synth
+import oracle
+from gpu_common import DEV, host, inputs, max_abs, oshape, rel_l2, say, tie_free_rows
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+GRADS = ("dq", "dk", "dv", "dz", "dqs", "dks")
+
+
+def row_bound(name, got, ref, rel=0.1, floor=0.05):
+    """Every row of got within rel * max(|ref row|, floor * median |ref row|)."""
+    g = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+    r = np.asarray(ref, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+    nr = np.linalg.norm(r, axis=1)
+    err = np.linalg.norm(g - r, axis=1)
+    pos = nr[nr > 0]
+    fl = floor * (np.median(pos) if pos.size else 1.0)
+    lim = rel * np.maximum(nr, fl) + 1e-30
+    worst = float(np.max(err / lim)) if err.size else 0.0
+    say("  %s worst row error / bound %.3f" % (name, worst))
+    assert worst <= 1.0, name
+
+
+def gpu_train(dev, w, sm_scale=None, sel_scale=None):
+    lam = ops.gate_scores(dev["qs"], dev["ks"], w.tk, block=w.block, sel_scale=sel_scale)
+    o, lse = ops.attn_fwd(dev["q"], dev["k"], dev["v"], dev["qs"], dev["ks"], lam, block=w.block,
+                          sm_scale=sm_scale, sel_scale=sel_scale)
+    g = ops.attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, dev["qs"], dev["ks"], lam,
+                     block=w.block, sm_scale=sm_scale, sel_scale=sel_scale)
+    torch.cuda.synchronize()
+    return lam, o, lse, g
+
+
+def check_train(w, f, lam, o, lse, g, S):
+    _, lam_ref, _ = oracle.gate_scores(S, f["qs"], f["ks"])
+    fin = np.isfinite(lam_ref)
+    assert np.array_equal(np.isneginf(host(lam)), np.isneginf(lam_ref))
+    e = max_abs(host(lam)[fin], lam_ref[fin])
+    say("  lam max-abs %.2e" % e)
+    assert e <= 1e-4 * max(1.0, float(np.max(np.abs(lam_ref[fin]))))
+    o_ref, l_ref = oracle.attn_fwd(S, f["q"], f["k"], f["v"], f["qs"], f["ks"])
+    eo, el = max_abs(host(o), o_ref), max_abs(host(lse), l_ref)
+    say("  O max-abs %.2e  lse max-abs %.2e" % (eo, el))
+    assert eo <= 2e-2 and el <= 1e-3
+    ref = oracle.attn_bwd(S, f["q"], f["k"], f["v"], f["dout"], f["qs"], f["ks"])
+    for n in GRADS:
+        e = rel_l2(host(g[n]), ref[n])
+        say("  %s rel-L2 %.3e" % (n, e))
+        assert e <= 5e-2, n
+        row_bound(n, host(g[n]), ref[n])
+    return ref
+
+
+# ---------------------------------------------------------------- mid size
+def test_bwd_mid_full_tensor():
+    w = W["train_8k"].with_(name="mid_4608", hq=4, hkv=1, tq=4608, tk=4608)
+    say("mid-size full tensors", w)
+    cpu, dev, f = inputs(w)
+    lam, o, lse, g = gpu_train(dev, w)
+    check_train(w, f, lam, o, lse, g, oshape(w))
+
+
+# ------------------------------------------------------ early keys, full size
+def _group_slice(w, cpu, grp):
+    """fp64 copies of one kv group's tensors (its hq / hkv query heads)."""
+    hpg = w.hq // w.hkv
+    qh = slice(grp * hpg, (grp + 1) * hpg)
+    kh = slice(grp, grp + 1)
+    pick = {"q": qh, "qs": qh, "dout": qh, "k": kh, "v": kh, "ks": kh}
+    return {n: synth.to_f64(cpu[n][:, pick[n]].contiguous()) for n in pick}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,grp", [("train_8k", 5), ("train_32k", 0)])
+def test_bwd_full_size_early_keys(name, grp):
+    w = W[name]
+    say("early keys", name, "kv group", grp)
+    cpu, dev, _ = inputs(w)
+    lam, o, lse, g = gpu_train(dev, w)
+    hpg = w.hq // w.hkv
+    f = _group_slice(w, cpu, grp)
+    S = oracle.OracleShape(1, hpg, 1, w.tq, w.tk, w.d, w.ds, w.block, hks=1)
+    blocks = (0, 1, w.nb // 2)
+    keys = np.array([u for j in blocks for u in range(j * w.block, (j + 1) * w.block)],
+                    dtype=np.int64)
+    sbl = np.array(blocks, dtype=np.int64)
+    ref = oracle.attn_bwd(S, f["q"], f["k"], f["v"], f["dout"], f["qs"], f["ks"], rows=None,
+                          keys=keys, sblocks=sbl)
+    dk = host(g["dk"][0, grp])[keys]
+    dv = host(g["dv"][0, grp])[keys]
+    dks = host(g["dks"][0, grp])[sbl]
+    for n, got in (("dk", dk), ("dv", dv), ("dks", dks)):
+        e = rel_l2(got, ref[n])
+        say("  %s rel-L2 %.3e" % (n, e))
+        assert e <= 5e-2, n
+        row_bound(n, got, ref[n])
+
+
+# ----------------------------------------------------------- stressed inputs
+BASE = W["train_8k"].with_(batch=1, hq=8, hkv=2, tq=704, tk=768)
+STRESS = {
+    # explicit scales (sm_scale 0.3, sel_scale 2.0) instead of 1/sqrt(d), 1/sqrt(ds)
+    "scales": (BASE.with_(name="scales"), 0.3, 2.0),
+    # selector vectors x 4: score spread ~ 16, near one-hot gates
+    "sharp_gates": (BASE.with_(name="sharp", scales={"q": 0.5, "k": 0.5, "v": 0.5, "qs": 4.0,
+                                                     "ks": 4.0}), None, None),
+    # q, k x 4 (N(0, 4) each): logits 16 times the workloads' spread (std 4, row
+    # maxima ~ 15), the running max moving by several units between tiles
+    "large_logits": (BASE.with_(name="large", scales={"q": 2.0, "k": 2.0, "v": 0.5}), None,
+                     None),
+}
+
+
+@pytest.mark.parametrize("name", list(STRESS))
+def test_stressed_inputs(name):
+    w, sm, sel = STRESS[name]
+    say("stressed", name)
+    cpu, dev, f = inputs(w)
+    S = oshape(w)
+    if sm is not None:
+        # the library takes float32 scales: give the oracle the same numbers
+        S = oracle.OracleShape(w.batch, w.hq, w.hkv, w.tq, w.tk, w.d, w.ds, w.block,
+                               hks=w.kheads, sm_scale=float(np.float32(sm)),
+                               sel_scale=float(np.float32(sel)))
+    lam, o, lse, g = gpu_train(dev, w, sm, sel)
+    check_train(w, f, lam, o, lse, g, S)
+    # Top-K on tie-free rows and the sparse forward over the oracle's selection
+    K = 5
+    rows = w.batch * w.hq * w.tq
+    idx, bias = ops.topk_blocks(dev["qs"], dev["ks"], K, w.tk, sel_scale=sel)
+    torch.cuda.synchronize()
+    idx_ref, bias_ref = oracle.topk_blocks(S, K, f["qs"], f["ks"])
+    z, _, _ = oracle.gate_scores(S, f["qs"], f["ks"])
+    c = np.tile((np.arange(w.tq) + w.tk - w.tq) // w.block, w.batch * w.hq)
+    ok = tie_free_rows(z.reshape(rows, -1), c, K)
+    say("  tie-free rows %.3f" % ok.mean())
+    assert ok.mean() > 0.8
+    ig, bg = idx.cpu().numpy().reshape(rows, -1), host(bias).reshape(rows, -1)
+    assert np.array_equal(ig[ok], idx_ref.reshape(rows, -1)[ok])
+    br = bias_ref.reshape(rows, -1)[ok]
+    fin = np.isfinite(br)
+    assert np.array_equal(np.isfinite(bg[ok]), fin)
+    assert max_abs(bg[ok][fin], br[fin]) <= 1e-4 * max(1.0, float(np.max(np.abs(br[fin]))))
+    b32 = bias_ref.astype(np.float32)
+    os_, ls_ = ops.sparse_fwd(dev["q"], dev["k"], dev["v"], torch.from_numpy(idx_ref).to(DEV),
+                              torch.from_numpy(b32).to(DEV), sm_scale=sm)
+    torch.cuda.synchronize()
+    os_ref, ls_ref = oracle.sparse_fwd(S, K, f["q"], f["k"], f["v"], idx_ref,
+                                       b32.astype(np.float64))
+    eo, el = max_abs(host(os_), os_ref), max_abs(host(ls_), ls_ref)
+    say("  sparse O max-abs %.2e lse %.2e" % (eo, el))
+    assert eo <= 2e-2 and el <= 1e-3
+
+
+# -------------------------------------------------------- shift invariance
+def test_shift_invariance_augmented_selector():
+    """Adding a_t to every score of row t changes no output: with ds = 32, the
+    last selector dimension carries a_t / sigma in qs and 1 in ks."""
+    w = BASE.with_(name="shift")
+    cpu, dev, f = inputs(w)
+    sigma = 1.0 / np.sqrt(w.ds)
+    rng = np.random.default_rng(77)
+    # per-row shift a_t = sigma * s_t with s_t an integer in [-12, 12] (exact in bf16)
+    s = torch.from_numpy(rng.integers(-12, 13, size=(w.batch, w.hq, w.tq)).astype(np.float32))
+    qs0 = cpu["qs"].clone()
+    qs0[..., -1] = 0
+    ks1 = cpu["ks"].clone()
+    ks1[..., -1] = 1
+    qsa = qs0.clone()
+    qsa[..., -1] = s.to(qsa.dtype)
+    runs = {}
+    for tag, qsx in (("plain", qs0), ("shift", qsa)):
+        d = dict(dev)
+        d["qs"], d["ks"] = qsx.to(DEV), ks1.to(DEV)
+        lam, o, lse, g = gpu_train(d, w)
+        idx, bias = ops.topk_blocks(d["qs"], d["ks"], 6, w.tk)
+        torch.cuda.synchronize()
+        runs[tag] = (lam, o, lse, g, idx, bias)
+    # the shifted run against the oracle on the same (augmented) inputs
+    fa = dict(f)
+    fa["qs"], fa["ks"] = synth.to_f64(qsa), synth.to_f64(ks1)
+    lam, o, lse, g, _, _ = runs["shift"]
+    check_train(w, fa, lam, o, lse, g, oshape(w))
+    # and the two GPU runs against each other: the shift changes nothing but lam
+    _, o0, l0, g0, i0, b0 = runs["plain"]
+    _, o1, l1, g1, i1, b1 = runs["shift"]
+    assert max_abs(host(o1), host(o0)) <= 2e-2
+    assert max_abs(host(l1), host(l0)) <= 1e-3
+    for n in ("dq", "dk", "dv", "dz"):
+        e = rel_l2(host(g1[n]), host(g0[n]))
+        say("  shift vs plain %s rel-L2 %.2e" % (n, e))
+        assert e <= 5e-2, n
+    for n in ("dqs", "dks"):  # the first ds - 1 dimensions (the last one carries the shift)
+        e = rel_l2(host(g1[n])[..., :-1], host(g0[n])[..., :-1])
+        say("  shift vs plain %s rel-L2 %.2e" % (n, e))
+        assert e <= 5e-2, n
+    # Top-K is shift invariant: same blocks on tie-free rows, renorm-0 bias z - lam equal
+    S = oshape(w)
+    z, _, _ = oracle.gate_scores(S, fa["qs"], fa["ks"])
+    rows = w.batch * w.hq * w.tq
+    c = np.tile((np.arange(w.tq) + w.tk - w.tq) // w.block, w.batch * w.hq)
+    ok = tie_free_rows(z.reshape(rows, -1), c, 6)
+    assert ok.mean() > 0.8
+    ia, ib = i0.cpu().numpy().reshape(rows, -1), i1.cpu().numpy().reshape(rows, -1)
+    assert np.array_equal(ia[ok], ib[ok])
+    ba, bb = host(b0).reshape(rows, -1)[ok], host(b1).reshape(rows, -1)[ok]
+    fin = np.isfinite(ba)
+    assert np.array_equal(fin, np.isfinite(bb))
+    assert max_abs(ba[fin], bb[fin]) <= 1e-4 * max(1.0, float(np.max(np.abs(ba[fin]))))

@@ -2,7 +2,7 @@
 
 fp32 training path (gate, forward, backward incl. dz, dqs, dks) at blocks
 1, 4, 16, 32; bf16 selection (gate, Top-K, threshold) and the sparse forward
-(pair path) at blocks 16 and 32, prefill and decode.  Same bars as the
+at blocks 1, 2, 4, 8, 16 and 32, prefill, chunked prefill and decode.  Same bars as the
 64-token cases: fp32 max-abs / rel-L2 <= 1e-4; bf16 O <= 2e-2, lse <= 1e-3;
 selections exact on rows clear of ties / of the threshold.
 """
@@ -59,6 +59,16 @@ SMALL = {
     "chunk_b16": W["prefill_32k_top16"].with_(batch=1, hq=4, hkv=2, tq=200, tk=1024, block=16,
                                              topk=8),
     "decode_b16": W["decode_64k_top8"].with_(batch=3, tk=4096, block=16, topk=16),
+    # bf16 token-level and 2 .. 8-token units (pair path for the sparse forward)
+    "prefill_b1": W["prefill_32k_top16"].with_(batch=1, hq=4, hkv=2, tq=320, tk=320, block=1,
+                                               topk=24),
+    "chunk_b2": W["prefill_32k_top16"].with_(batch=1, hq=4, hkv=2, tq=136, tk=448, block=2,
+                                             topk=40),
+    "prefill_b4": W["prefill_32k_top16"].with_(batch=2, hq=4, hkv=1, tq=512, tk=512, block=4,
+                                               topk=16),
+    "prefill_b8": W["prefill_32k_top16"].with_(batch=1, hq=4, hkv=2, tq=640, tk=640, block=8,
+                                               topk=10),
+    "decode_b1": W["decode_64k_top8"].with_(batch=2, tk=1024, block=1, topk=32),
 }
 
 
