@@ -68,6 +68,18 @@ def sparse_pairs(w):
     return tot
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(T: int):
     """The fp64 oracle, timed on a bounded sample of the 32k training job."""
     import numpy as np
@@ -101,7 +113,7 @@ def cpu_baseline(T: int):
                    "prefix of %d tokens of kv group 0 (4 query heads) of train_32k; %.1f s; "
                    "attended flop counted as on the GPU" % (T, dt)),
         "seconds": dt,
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
     }
 
 
