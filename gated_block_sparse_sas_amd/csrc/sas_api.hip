@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/sas.h"
 #include "sas_internal.h"
 
@@ -247,18 +249,28 @@ sas_status sas_topk_blocks_budget(const sas_shape* shape, int32_t kmax, int32_t 
                                             (hipStream_t)stream));
 }
 
+// Checks shared by the sparse forward entry points; *need = workspace bytes.
+static sas_status sparse_fwd_check(const sas_shape* shape, int32_t topk, sas::Dims* D,
+                                   size_t* need) {
+  sas_status r = resolve(shape, D);
+  if (r != SAS_OK) return r;
+  if (topk < 1) return SAS_ERR_SHAPE;
+  if (shape->dtype == SAS_F32 && D->d != 64) return SAS_ERR_UNSUPPORTED;
+  if ((int64_t)D->batch * D->hq * D->tq * (topk + 1) >= (int64_t)1 << 31)
+    return SAS_ERR_UNSUPPORTED;
+  *need = sas::sparse_workspace(*D, topk);
+  return SAS_OK;
+}
+
 static sas_status sparse_fwd_impl(const sas_shape* shape, int32_t topk, const void* q,
                                   const void* k, const void* v, const int32_t* idx,
                                   const float* bias, void* o, float* lse, void* ws,
                                   size_t* ws_bytes, const sas::StageEvents& E, void* stream) {
   sas::Dims D;
-  sas_status r = resolve(shape, &D);
+  size_t need = 0;
+  sas_status r = sparse_fwd_check(shape, topk, &D, &need);
   if (r != SAS_OK) return r;
-  if (topk < 1) return SAS_ERR_SHAPE;
   if (!ws_bytes) return SAS_ERR_NULL;
-  if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
-  if ((int64_t)D.batch * D.hq * D.tq * (topk + 1) >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
-  const size_t need = sas::sparse_workspace(D, topk);
   if (!ws) {
     *ws_bytes = need;
     return SAS_OK;
@@ -285,6 +297,64 @@ sas_status sas_sparse_fwd_ev(const sas_shape* shape, int32_t topk, const void* q
   if (n_events < 0 || n_events > 1) return SAS_ERR_SHAPE;
   return sparse_fwd_impl(shape, topk, q, k, v, idx, bias, o, lse, ws, ws_bytes,
                          sas::StageEvents{events, n_events}, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch of sas_sparse_fwd_noalloc: a fixed array in device memory, one per
+// GPU (each GPU's copy of the code object holds its own), so the call needs
+// no allocation.  Host code never passes `scratch` itself to a kernel (on the
+// host it only names the symbol): the device address of each GPU's copy is
+// looked up once per device, with that device current, and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)256 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current GPU's scratch array.
+hipError_t scratch_on_current_device(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  if (s.err != hipSuccess) return s.err;
+  if (!s.ptr) return hipErrorInvalidSymbol;
+  *out = (char*)s.ptr;
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+size_t sas_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+sas_status sas_sparse_fwd_noalloc(const sas_shape* shape, int32_t topk, const void* q,
+                                  const void* k, const void* v, const int32_t* idx,
+                                  const float* bias, void* o, float* lse, void* stream) {
+  sas::Dims D;
+  size_t need = 0;
+  sas_status r = sparse_fwd_check(shape, topk, &D, &need);
+  if (r != SAS_OK) return r;
+  if ((r = check_ptrs({q, k, v, idx, bias, o})) != SAS_OK) return r;
+  if ((r = check_opt({lse})) != SAS_OK) return r;
+  if (need > kNoAllocScratchBytes) return SAS_ERR_WORKSPACE;
+  if (D.batch == 0) return SAS_OK;
+  char* ws = nullptr;
+  hipError_t e = scratch_on_current_device(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(sas::launch_sparse(q, k, v, idx, bias, o, lse, ws, kNoAllocScratchBytes,
+                                       topk, D, shape->dtype == SAS_BF16,
+                                       sas::StageEvents{nullptr, 0}, (hipStream_t)stream));
 }
 
 sas_status sas_threshold_count(const sas_shape* shape, float theta, const void* qs,

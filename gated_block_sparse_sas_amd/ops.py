@@ -28,7 +28,7 @@ EXPORTS = ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_attn_bwd_ev",
            "sas_topk_blocks", "sas_topk_blocks_budget", "sas_sparse_fwd", "sas_sparse_fwd_ev",
            "sas_paged_append", "sas_paged_topk", "sas_paged_decode",
            "sas_threshold_count", "sas_threshold_fill", "sas_sparse_fwd_csr",
-           "sas_sparse_fwd_csr_ev",
+           "sas_sparse_fwd_csr_ev", "sas_sparse_fwd_noalloc", "sas_noalloc_scratch_bytes",
            "sas_status_string", "sas_last_hip_error")
 
 
@@ -87,11 +87,14 @@ def load():
         lib.sas_paged_append.argtypes = [P] * 10
         lib.sas_paged_topk.argtypes = [P, I32, I32, P, P, P, P, P, P, P]
         lib.sas_paged_decode.argtypes = [P, I32] + [P] * 10 + [SZ, P]
+        lib.sas_sparse_fwd_noalloc.argtypes = [P, I32] + [P] * 8
+        lib.sas_noalloc_scratch_bytes.argtypes = []
+        lib.sas_noalloc_scratch_bytes.restype = ctypes.c_size_t
         for n in ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_topk_blocks",
                   "sas_topk_blocks_budget", "sas_sparse_fwd", "sas_attn_bwd_ev",
                   "sas_sparse_fwd_ev", "sas_paged_append", "sas_paged_topk",
                   "sas_paged_decode", "sas_threshold_count", "sas_threshold_fill",
-                  "sas_sparse_fwd_csr", "sas_sparse_fwd_csr_ev"):
+                  "sas_sparse_fwd_csr", "sas_sparse_fwd_csr_ev", "sas_sparse_fwd_noalloc"):
             getattr(lib, n).restype = ctypes.c_int
         lib.sas_status_string.argtypes = [ctypes.c_int]
         lib.sas_status_string.restype = ctypes.c_char_p
@@ -275,6 +278,21 @@ def sparse_fwd(q, k, v, idx, bias, block=64, sm_scale=None, ws=None, with_lse=Tr
     _check("sas_sparse_fwd", load().sas_sparse_fwd_ev(
         ctypes.byref(sh), int(topk), _p(q), _p(k), _p(v), _p(idx), _p(bias), _p(o), _p(lse),
         _p(ws), ctypes.byref(n), ev, nev, _stream(q)))
+    return o, lse
+
+
+def sparse_fwd_noalloc(q, k, v, idx, bias, block=64, sm_scale=None, with_lse=True):
+    """:func:`sparse_fwd` through ``sas_sparse_fwd_noalloc``: the library's fixed
+    scratch array instead of a workspace.  Returns (o, lse)."""
+    b, hq, tq, d = q.shape
+    _, hkv, tk, _ = k.shape
+    topk = idx.shape[-1]
+    sh = make_shape(b, hq, hkv, tq, tk, d, 32, block, hkv, sm_scale, 0.0, _dt(q), _dt(q))
+    o = torch.empty_like(q)
+    lse = torch.empty((b, hq, tq), dtype=torch.float32, device=q.device) if with_lse else None
+    _check("sas_sparse_fwd_noalloc", load().sas_sparse_fwd_noalloc(
+        ctypes.byref(sh), int(topk), _p(q), _p(k), _p(v), _p(idx), _p(bias), _p(o), _p(lse),
+        _stream(q)))
     return o, lse
 
 

@@ -183,6 +183,23 @@ sas_status sas_sparse_fwd_ev(const sas_shape* shape, int32_t topk, const void* q
                              float* lse, void* ws, size_t* ws_bytes, void* const* events,
                              int32_t n_events, void* stream);
 
+/* Same as sas_sparse_fwd, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the workspace is a fixed array of sas_noalloc_scratch_bytes()
+ * (256 MiB) that the library holds in each GPU's memory from the first call
+ * on that GPU until the process ends; the call itself allocates nothing.
+ * Shapes whose workspace (the size query of sas_sparse_fwd) exceeds it return
+ * SAS_ERR_WORKSPACE before anything is enqueued; tq == 1 needs none.  Every
+ * call on one GPU shares that array: calls that overlap in time on one GPU
+ * (two streams, or two threads) race and must be serialised by the caller.
+ * The call clears the scratch it needs itself. */
+sas_status sas_sparse_fwd_noalloc(const sas_shape* shape, int32_t topk, const void* q,
+                                  const void* k, const void* v, const int32_t* idx,
+                                  const float* bias, void* o, float* lse, void* stream);
+
+/* Bytes of the fixed workspace of sas_sparse_fwd_noalloc. */
+size_t sas_noalloc_scratch_bytes(void);
+
 /* ---------------------------------------------------------------------------
  * Dynamic-threshold selection.  Instead of a fixed budget, row t keeps every
  * historical block whose normalised gate g = exp(z - lam) is at least theta
