@@ -46,12 +46,18 @@ namespace sas {
 constexpr int kFwdWaves = 8, kFwdThreads = 64 * kFwdWaves, kFwdRows = 32 * kFwdWaves;
 
 // UB gate units per 64-key tile (UB = 1: 64-token blocks; 2, 4: units of 32,
-// 16 tokens, whose bias then changes inside the tile).
-template <int HD, int DS, int UB>
+// 16 tokens, whose bias then changes inside the tile).  GIVEN: the bias of
+// each historical (row, block) is read from bt [b * hq][tq / 8][nb][8]
+// (-inf for a block the row does not attend) instead of being computed from
+// the selector: the same kernel then runs a sparse forward whose selection is
+// dense enough that streaming every block beats gathering the selected ones
+// (qs, ks and lam are unused).
+template <int HD, int DS, int UB, bool GIVEN>
 __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ qs, const bf16* __restrict__ ks, const float* __restrict__ lam,
-    bf16* __restrict__ o, float* __restrict__ lse, Dims D, int nqt, int xcd_groups) {
+    const float* __restrict__ bt, bf16* __restrict__ o, float* __restrict__ lse, Dims D,
+    int nqt, int xcd_groups) {
   constexpr int DC = HD / 8;                 // 16-byte chunks of a row
   constexpr int SP = HD == 128 ? 18 : 10;    // LDS row pitch in 16-byte slots (K and V)
   constexpr int KP = SP * 8, VP = KP;        // row pitches (elements)
@@ -98,9 +104,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   bf16x2 qsv[DS / 4];
 #pragma unroll
   for (int e = 0; e < DS / 4; ++e)
-    qsv[e] = *(const bf16x2*)(qs + qrow * DS + hh * (DS / 2) + 2 * e);
-  const float lam_t = c > 0 ? lam[qrow] : 0.f;
-  const bf16* ksb0 = ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS;
+    qsv[e] = GIVEN ? bf16x2{} : *(const bf16x2*)(qs + qrow * DS + hh * (DS / 2) + 2 * e);
+  const float lam_t = !GIVEN && c > 0 ? lam[qrow] : 0.f;
+  const bf16* ksb0 = GIVEN ? ks : ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS;
+  // GIVEN: this row's bias of block j is btr[8 j]
+  const float* btr =
+      GIVEN ? bt + ((((size_t)b * D.hq + h) * ((D.tq + 7) / 8) + qc / 8) * D.nb) * 8 + qc % 8
+            : nullptr;
+  // GIVEN: the bias of the tile being scored and of the next one (loaded a tile ahead)
+  float bcur = 0.f, bnext = GIVEN && 0 < c ? btr[0] : 0.f;
   const bf16* kb = k + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
   const bf16* vb = v + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
   const float c1 = D.sm_scale * kLog2e;
@@ -108,7 +120,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   f32x16 oacc[DM];
 #pragma unroll
   for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // GIVEN: a large finite start, so a block with bias -inf before the row's
+  // first visible key gives exp2(-inf) = 0 rather than -inf - -inf
+  float m_run = GIVEN ? -1e30f : -INFINITY, l_run = 0.f;
 
   // next tile staged in registers: thread tid holds 16-byte chunks tid + kFwdThreads x
   // (row = chunk / DC, column chunk = chunk % DC) of K and of V, and threads
@@ -123,7 +137,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       kreg[x] = *(const bf16x8*)(kt + (id / DC) * HD + (id % DC) * 8);
       vreg[x] = *(const bf16x8*)(vt + (id / DC) * HD + (id % DC) * 8);
     }
-    if (tid < UB * DS / 8) sreg = *(const bf16x8*)(ksb0 + (size_t)j * UB * DS + tid * 8);
+    if (!GIVEN && tid < UB * DS / 8) sreg = *(const bf16x8*)(ksb0 + (size_t)j * UB * DS + tid * 8);
   };
   auto sstore = [&](bf16* Kd, bf16* Vd, bf16* Sd) __attribute__((always_inline)) {
 #pragma unroll
@@ -132,7 +146,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       *(bf16x8*)&Kd[(id / DC) * KP + (id % DC) * 8] = kreg[x];
       *(bf16x8*)&Vd[(id / DC) * VP + (id % DC) * 8] = vreg[x];
     }
-    if (tid < UB * DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
+    if (!GIVEN && tid < UB * DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
   };
   // per-lane part of the transposing V^T reads: lane 4k + a of each 16-lane
   // group points at key row 4 hh + k, columns 16 ((lane >> 4) & 1) + 4 a
@@ -149,7 +163,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
     float bias2[UB];  // log2-domain gate bias of this lane's row for each unit of tile j
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) bias2[ub] = 0.f;
-    if (UB == 1 ? j < c_hi : j <= c_hi) {
+    if constexpr (GIVEN) {
+      bias2[0] = j < c ? bcur * kLog2e : 0.f;
+    } else if (UB == 1 ? j < c_hi : j <= c_hi) {
 #pragma unroll
       for (int ub = 0; ub < UB; ++ub) {
         const bf16x2* kr = (const bf16x2*)(Ss + ub * DS + hh * (DS / 2));
@@ -262,6 +278,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   auto loop = [&](auto half_tag) __attribute__((always_inline)) {
     constexpr int H = decltype(half_tag)::value;
     for (int j = 0; j <= c_end; ++j) {
+      // (the bias load goes out before the next tile's loads, so waiting for
+      // it does not wait for them)
+      if constexpr (GIVEN) {
+        bcur = bnext;
+        bnext = j + 1 < c ? btr[(size_t)(j + 1) * 8] : 0.f;
+      }
       if (j + 1 <= c_end) gload(j + 1);
       if constexpr (H == 0) {
         if (j <= c_hi) {
@@ -305,29 +327,44 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   }
 }
 
-template <int HD, int DS, int UB>
+template <int HD, int DS, int UB, bool GIVEN>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const void* qs,
-                               const void* ks, const float* lam, void* o, float* lse,
-                               const Dims& D, hipStream_t st) {
+                               const void* ks, const float* lam, const float* bt, void* o,
+                               float* lse, const Dims& D, hipStream_t st) {
   const int nqt = (D.tq + kFwdRows - 1) / kFwdRows;
   const int groups = D.batch * D.hkv;
   const int xcd_groups = groups % 8 == 0 ? groups / 8 : 0;
   const unsigned grid = (unsigned)(D.batch * D.hq * nqt);
-  hipLaunchKernelGGL((attn_fwd_kernel<HD, DS, UB>), dim3(grid), dim3(kFwdThreads), 0, st, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, (const bf16*)qs, (const bf16*)ks, lam,
-                     (bf16*)o, lse, D, nqt, xcd_groups);
+  hipLaunchKernelGGL((attn_fwd_kernel<HD, DS, UB, GIVEN>), dim3(grid), dim3(kFwdThreads), 0, st,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)qs,
+                     (const bf16*)ks, lam, bt, (bf16*)o, lse, D, nqt, xcd_groups);
   return hipGetLastError();
+}
+
+// Sparse forward through the dense kernel: bt [b * hq][nb][tq] holds each
+// (row, historical block) bias, -inf where the row does not attend the block.
+hipError_t launch_fwd_given_bias(const void* q, const void* k, const void* v, const float* bt,
+                                 void* o, float* lse, const Dims& D, hipStream_t st) {
+  if (D.blk != kBlock) return hipErrorInvalidValue;
+  if (D.d == 128)
+    return launch_fwd_t<128, 16, 1, true>(q, k, v, nullptr, nullptr, nullptr, bt, o, lse, D, st);
+  if (D.d == 64)
+    return launch_fwd_t<64, 16, 1, true>(q, k, v, nullptr, nullptr, nullptr, bt, o, lse, D, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const void* qs,
                            const void* ks, const float* lam, void* o, float* lse, const Dims& D,
                            hipStream_t st) {
-#define SAS_FWD_CASE(HDV, DSV)                                                           \
-  if (D.d == HDV && D.ds == DSV) {                                                       \
-    if (D.blk == 64) return launch_fwd_t<HDV, DSV, 1>(q, k, v, qs, ks, lam, o, lse, D, st); \
-    if (D.blk == 32) return launch_fwd_t<HDV, DSV, 2>(q, k, v, qs, ks, lam, o, lse, D, st); \
-    if (D.blk == 16) return launch_fwd_t<HDV, DSV, 4>(q, k, v, qs, ks, lam, o, lse, D, st); \
-    return hipErrorInvalidValue;                                                         \
+#define SAS_FWD_CASE(HDV, DSV)                                                                  \
+  if (D.d == HDV && D.ds == DSV) {                                                              \
+    if (D.blk == 64)                                                                            \
+      return launch_fwd_t<HDV, DSV, 1, false>(q, k, v, qs, ks, lam, nullptr, o, lse, D, st);   \
+    if (D.blk == 32)                                                                            \
+      return launch_fwd_t<HDV, DSV, 2, false>(q, k, v, qs, ks, lam, nullptr, o, lse, D, st);   \
+    if (D.blk == 16)                                                                            \
+      return launch_fwd_t<HDV, DSV, 4, false>(q, k, v, qs, ks, lam, nullptr, o, lse, D, st);   \
+    return hipErrorInvalidValue;                                                                \
   }
   SAS_FWD_CASE(128, 32)
   SAS_FWD_CASE(128, 16)

@@ -23,6 +23,8 @@ hipError_t launch_gate(const void* qs, const void* ks, float* lam, float* beta, 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const void* qs,
                            const void* ks, const float* lam, void* o, float* lse, const Dims& D,
                            hipStream_t st);
+hipError_t launch_fwd_given_bias(const void* q, const void* k, const void* v, const float* bt,
+                                 void* o, float* lse, const Dims& D, hipStream_t st);
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, const void* qs,
                           const void* ks, const float* lam, void* o, float* lse, const Dims& D,
                           hipStream_t st);

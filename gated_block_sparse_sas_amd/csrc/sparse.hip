@@ -77,21 +77,37 @@ struct PagedKV {
 // slots, and the waves' results are merged by their log-sum-exp in LDS.
 constexpr int kRowWaves = 16;
 
-template <int HD, typename T, typename Src>
-__global__ __launch_bounds__(64 * kRowWaves) void sparse_row_kernel(
-    const T* __restrict__ q, Src S, const int* __restrict__ idx, const float* __restrict__ bias,
-    T* __restrict__ o, float* __restrict__ lse, Dims D, int K) {
+// Slots of a row read from the idx / bias arrays.
+struct GlobalSlots {
+  const int* idx;
+  const float* bias;
+  __device__ void get(size_t row, int K, int slot, int* j, float* add) const {
+    *j = idx[row * K + slot];
+    *add = bias[row * K + slot];
+  }
+};
+
+// LDS used by attend_row.
+template <int HD>
+struct RowLds {
+  float ps[kRowWaves][64];
+  float ow[kRowWaves][HD];
+  float mw[kRowWaves], lw[kRowWaves];
+};
+
+// Attention of one query row over its K slots and its current block (slot
+// K), W waves per row; every thread of the workgroup calls it.
+template <int HD, typename T, typename Src, typename Slots>
+__device__ __forceinline__ void attend_row(const T* __restrict__ q, const Src& S,
+                                           const Slots& SL, T* __restrict__ o,
+                                           float* __restrict__ lse, const Dims& D, int K,
+                                           size_t row, int W, RowLds<HD>& L) {
   constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane and load
   constexpr int LPK = HD / EPL;             // lanes per key row
   constexpr int KPI = 64 / LPK;             // key rows per load instruction
   typedef T vec_t __attribute__((ext_vector_type(EPL)));
-  __shared__ float ps[kRowWaves][64];
-  __shared__ float ow[kRowWaves][HD];
-  __shared__ float mw[kRowWaves], lw[kRowWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int W = blockDim.x >> 6;
-  const size_t row = blockIdx.x;
   const int h = (int)((row / D.tq) % D.hq);
   const int b = (int)(row / ((size_t)D.tq * D.hq));
   const int t = S.t_of(D, row);
@@ -110,13 +126,12 @@ __global__ __launch_bounds__(64 * kRowWaves) void sparse_row_kernel(
   float m_w = -INFINITY, l_w = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  float* const pw = ps[wave];
+  float* const pw = L.ps[wave];
   for (int slot = wave; t >= 0 && slot <= K; slot += W) {
     int j;
     float add;
     if (slot < K) {
-      j = idx[row * K + slot];
-      add = bias[row * K + slot];
+      SL.get(row, K, slot, &j, &add);
       if (j < 0 || j >= c) continue;  // not a historical block: skipped, never read
     } else {
       j = c;
@@ -168,16 +183,16 @@ __global__ __launch_bounds__(64 * kRowWaves) void sparse_row_kernel(
     for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], of);
   if (lane < LPK) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) ow[wave][d0 + e] = acc[e];
+    for (int e = 0; e < EPL; ++e) L.ow[wave][d0 + e] = acc[e];
   }
   if (lane == 0) {
-    mw[wave] = m_w;
-    lw[wave] = l_w;
+    L.mw[wave] = m_w;
+    L.lw[wave] = l_w;
   }
   __syncthreads();
   if (wave != 0) return;
   float M = -INFINITY;
-  for (int w = 0; w < W; ++w) M = fmaxf(M, mw[w]);
+  for (int w = 0; w < W; ++w) M = fmaxf(M, L.mw[w]);
   if (M == -INFINITY) {  // no readable key: zeros, lse -inf
     if (lane < LPK) {
       vec_t z;
@@ -188,26 +203,35 @@ __global__ __launch_bounds__(64 * kRowWaves) void sparse_row_kernel(
     if (lane == 0 && lse) lse[row] = -INFINITY;
     return;
   }
-  float L = 0.f, out[EPL];
+  float Ls = 0.f, out[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) out[e] = 0.f;
   for (int w = 0; w < W; ++w) {
-    if (mw[w] == -INFINITY) continue;
-    const float sw = exp2f((mw[w] - M) * kLog2e);
-    L += lw[w] * sw;
+    if (L.mw[w] == -INFINITY) continue;
+    const float sw = exp2f((L.mw[w] - M) * kLog2e);
+    Ls += L.lw[w] * sw;
     if (lane < LPK) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) out[e] = fmaf(sw, ow[w][d0 + e], out[e]);
+      for (int e = 0; e < EPL; ++e) out[e] = fmaf(sw, L.ow[w][d0 + e], out[e]);
     }
   }
   if (lane < LPK) {
-    const float inv = 1.f / L;
+    const float inv = 1.f / Ls;
     vec_t r;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) r[e] = from_f32<T>(out[e] * inv);
     *(vec_t*)(o + row * HD + d0) = r;
   }
-  if (lane == 0 && lse) lse[row] = M + logf(L);
+  if (lane == 0 && lse) lse[row] = M + logf(Ls);
+}
+
+
+template <int HD, typename T, typename Src>
+__global__ __launch_bounds__(64 * kRowWaves) void sparse_row_kernel(
+    const T* __restrict__ q, Src S, const int* __restrict__ idx, const float* __restrict__ bias,
+    T* __restrict__ o, float* __restrict__ lse, Dims D, int K) {
+  __shared__ RowLds<HD> L;
+  attend_row<HD, T>(q, S, GlobalSlots{idx, bias}, o, lse, D, K, blockIdx.x, blockDim.x >> 6, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -739,6 +763,63 @@ __global__ __launch_bounds__(256) void sp_merge16_kernel(Src S, const int* __res
   if (sl == 0 && lse) lse[row] = (m + log2f(sm)) * kLn2;
 }
 
+// ---------------------------------------------------------------------------
+// Dense selections (prefill whose rows keep a large share of their history,
+// e.g. a quarter of it): the query-stationary dense kernel runs with the
+// selection as a bias matrix, -inf where a row does not attend a block.  The
+// matrix is tiled by 8-row chunks, bt [b * hq][tq / 8][nb][8]: a chunk's
+// biases of one block are one 32-byte run (a wave's 32 rows read four), and a
+// chunk's whole matrix is one contiguous run.  Built per (batch x head,
+// 8-row chunk, 512-block range) in LDS: every slot of the chunk's rows lands
+// in its LDS cell, then the cells of the blocks some row of the chunk can see
+// (j < c of the chunk's last row) go out contiguously.  Entries that are not
+// historical blocks of their row are skipped, as in the other paths.
+constexpr int kBtRows = 8, kBtBlocks = 512;
+
+__global__ __launch_bounds__(256) void sp_bias_matrix_kernel(const int* __restrict__ idx,
+                                                             const float* __restrict__ bias,
+                                                             int K, float* __restrict__ bt,
+                                                             Dims D) {
+  __shared__ __align__(16) float cell[kBtBlocks][kBtRows];
+  const int i0 = blockIdx.x * kBtRows, j0 = blockIdx.y * kBtBlocks;
+  const size_t bh = blockIdx.z;
+  const int nrow = min(kBtRows, D.tq - i0);
+  // blocks visible to some row of the chunk: j < c(last row)
+  const int jend = min(min(j0 + kBtBlocks, D.nb), (D.qoff + i0 + nrow - 1) / kBlock);
+  if (jend <= j0) return;  // uniform: no row of the chunk sees these blocks
+  const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int x = threadIdx.x; x < kBtBlocks * kBtRows / 4; x += 256)
+    *(f32x4*)&cell[x / (kBtRows / 4)][4 * (x % (kBtRows / 4))] = ninf;
+  __syncthreads();
+  const size_t r0 = bh * D.tq + i0;
+  for (int x = threadIdx.x; x < nrow * K; x += 256) {
+    const int r = x / K;  // slot fastest: the chunk's idx / bias are one contiguous run
+    const int j = idx[r0 * K + x];
+    const int c = (D.qoff + i0 + r) / kBlock;
+    if (j >= j0 && j < jend && j < c) cell[j - j0][r] = bias[r0 * K + x];
+  }
+  __syncthreads();
+  const int nch = (D.tq + kBtRows - 1) / kBtRows;
+  float* dst = bt + ((bh * nch + blockIdx.x) * (size_t)D.nb + j0) * kBtRows;
+  for (int x = threadIdx.x; x < (jend - j0) * (kBtRows / 4); x += 256)
+    *(f32x4*)&dst[4 * x] = *(const f32x4*)&cell[x / (kBtRows / 4)][4 * (x % (kBtRows / 4))];
+}
+
+// The dense-kernel path pays every block of the causal triangle; the
+// block-stationary path pays per selected pair (gather, partial, merge), about
+// six times the cost of a dense pair on MI355X (top-16 at 32k: 3.1 ms for
+// 1.09e9 pairs; dense: 9.0 ms for 1.72e10).  Selections keeping at least
+// 3/16 of the average row's history take the dense kernel.
+static bool use_given_bias_path(const Dims& D, int K) {
+  if (D.blk != kBlock || D.tq < 256 || (D.d != 128 && D.d != 64)) return false;
+  const double avg_keys = (double)D.qoff + 0.5 * (double)(D.tq + 1);
+  return 16.0 * (double)K * kBlock >= 3.0 * avg_keys;
+}
+static size_t given_bias_workspace(const Dims& D) {
+  const size_t nch = (D.tq + kBtRows - 1) / kBtRows;
+  return align256s((size_t)D.batch * D.hq * nch * kBtRows * D.nb * sizeof(float));
+}
+
 static int diag_chunks_per_block(const Dims& D) { return (D.hpg * D.blk + kChunk - 1) / kChunk; }
 static int query_blocks(const Dims& D) { return D.nb - D.qoff / D.blk; }
 // Partial slots of the block path: current-block chunks, then one per pair.
@@ -771,6 +852,7 @@ static size_t block_path_workspace(const Dims& D, size_t npairs, bool csr) {
 // Workspace: pair path  [plse (rows x (K+1)) | po (rows x (K+1) x d)]; block path above.
 size_t sparse_workspace(const Dims& D, int K) {
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
+  if (use_given_bias_path(D, K)) return given_bias_workspace(D);
   if (use_block_path(D, K)) return block_path_workspace(D, rows * K, false);
   return 256;  // the row kernel needs none
 }
@@ -894,6 +976,16 @@ hipError_t launch_sparse(const void* q, const void* k, const void* v, const int*
                          int K, const Dims& D, bool bf16_io, const StageEvents& E,
                          hipStream_t st) {
   (void)ws_bytes;
+  if (bf16_io && use_given_bias_path(D, K)) {
+    float* bt = (float*)ws;
+    const dim3 grid((unsigned)((D.tq + kBtRows - 1) / kBtRows),
+                    (unsigned)((D.nb + kBtBlocks - 1) / kBtBlocks), (unsigned)(D.batch * D.hq));
+    hipLaunchKernelGGL(sp_bias_matrix_kernel, grid, dim3(256), 0, st, idx, bias, K, bt, D);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    E.record(0, st);
+    return launch_fwd_given_bias(q, k, v, bt, o, lse, D, st);
+  }
   if (bf16_io && use_block_path(D, K)) {
     if (D.d == 128)
       return launch_fixed_block_path<128>(q, k, v, idx, bias, o, lse, ws, K, D, E, st);

@@ -173,7 +173,14 @@ def test_sparse_workspace_query_and_checks(lib):
     n = ctypes.c_size_t(0)
     assert lib.sas_sparse_fwd(ctypes.byref(sh), 4, *([None] * 7), None, ctypes.byref(n),
                               STREAM) == 0
-    assert n.value >= 1 * 4 * 256 * 5 * 4
+    # 4 of the 2 historical blocks on average: the dense-kernel path, whose
+    # workspace is the per-(block, row) bias matrix (batch * hq * nb * tq floats)
+    assert n.value >= 1 * 4 * 4 * 256 * 4
+    sparse = shape(tq=4096, tk=4096)  # 2 of 32 blocks on average: partials per (row, slot)
+    m = ctypes.c_size_t(0)
+    assert lib.sas_sparse_fwd(ctypes.byref(sparse), 2, *([None] * 7), None, ctypes.byref(m),
+                              STREAM) == 0
+    assert m.value >= 1 * 4 * 4096 * 2 * (2 * 128 + 4)
     small = ctypes.c_size_t(n.value - 1)
     assert lib.sas_sparse_fwd(ctypes.byref(sh), 4, A, A, A, A, A, A, None, A,
                               ctypes.byref(small), STREAM) == 6

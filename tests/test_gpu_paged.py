@@ -42,9 +42,8 @@ def _f64(t):
     return {n: synth.to_f64(t[n]) for n in ("k_pool", "v_pool", "ks_pool", "q", "qs")}
 
 
-def _oracle_rows(pw, t, renorm=0, idx_gpu=None, bias_gpu=None, f=None):
-    """Per sequence: the oracle's selection and decode output.  With idx_gpu /
-    bias_gpu given, the oracle attends that selection instead of its own."""
+def _oracle_rows(pw, t, renorm=0, f=None):
+    """Per sequence: the oracle's selection and its decode output over it."""
     lens = t["seq_len"].numpy()
     table = t["block_table"].numpy()
     f = _f64(t) if f is None else f
@@ -58,11 +57,7 @@ def _oracle_rows(pw, t, renorm=0, idx_gpu=None, bias_gpu=None, f=None):
         q = f["q"][b][None, :, None, :]
         qs = f["qs"][b][None, :, None, :]
         idx, bias = oracle.topk_blocks(S, pw.topk, qs, ks, renorm=renorm)
-        if idx_gpu is not None:
-            idx = idx_gpu[b][None, :, None, :]
-            bias = bias_gpu[b][None, :, None, :].astype(np.float64)
-        else:
-            bias = bias.astype(np.float32).astype(np.float64)
+        bias = bias.astype(np.float32).astype(np.float64)
         o, lse = oracle.sparse_fwd(S, pw.topk, q, k, v, idx, bias)
         z, _, _ = oracle.gate_scores(S, qs, ks)
         out.append(dict(idx=idx.reshape(pw.hq, pw.topk), bias=bias.reshape(pw.hq, pw.topk),
@@ -212,8 +207,9 @@ def test_paged_edge_lengths():
 
 def test_paged_full_size_end_to_end():
     # 32 sequences, lengths 64 .. 65536 (log-uniform), 32 query / 8 kv heads,
-    # K = 8: GPU selection then GPU decode; every row against the oracle
-    # decode over the GPU's selection, and the selection itself on tie-free rows
+    # K = 8: GPU selection then GPU decode.  On every tie-free row the GPU's
+    # selection must be the oracle's, and its output the oracle's decode over
+    # that (its own) selection
     pw = PW["decode_paged_mix"]
     say("paged full", pw.batch, "sequences")
     t = synth.draw_paged(pw)
@@ -222,17 +218,16 @@ def test_paged_full_size_end_to_end():
     o, lse = ops.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_len"],
                               idx, bias)
     torch.cuda.synchronize()
-    ig, bg = idx.cpu().numpy(), bias.cpu().numpy()
-    f = _f64(t)
-    ref_sel = _oracle_rows(pw, t, f=f)
-    ref = _oracle_rows(pw, t, idx_gpu=ig, bias_gpu=bg, f=f)
-    e = max_abs(host(o), np.stack([r["o"] for r in ref]))
-    say("  O max-abs", e, "lens", t["seq_len"].min().item(), "..", t["seq_len"].max().item())
-    assert e <= 2e-2
-    assert max_abs(host(lse), np.stack([r["lse"] for r in ref])) <= 1e-3
-    n_ok = 0
-    for b, r in enumerate(ref_sel):
+    ig = idx.cpu().numpy()
+    og, lg = host(o), host(lse)
+    ref = _oracle_rows(pw, t, f=_f64(t))
+    n_ok, e = 0, 0.0
+    for b, r in enumerate(ref):
         ok = tie_free_rows(r["z"], np.full(pw.hq, r["c"]), pw.topk)
         n_ok += int(ok.sum())
         assert np.array_equal(ig[b][ok], r["idx"][ok])
+        e = max(e, max_abs(og[b][ok], r["o"][ok]))
+        assert max_abs(lg[b][ok], r["lse"][ok]) <= 1e-3
+    say("  O max-abs", e, "lens", t["seq_len"].min().item(), "..", t["seq_len"].max().item())
+    assert e <= 2e-2
     assert n_ok >= 0.9 * pw.batch * pw.hq

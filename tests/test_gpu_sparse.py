@@ -1,5 +1,12 @@
 """GPU top-K sparse forward (prefill and decode) vs fp64 oracle.
 
+Prefill takes one of two paths by the share of history the selection keeps:
+selections keeping at least 3/16 of the average row's history run the dense
+query-stationary kernel with the selection as a per-(block, row) bias
+(-inf where not attended); sparser ones the block-stationary path (gather,
+partials, merge).  The small cases below sit on both sides of that line
+(block path: "block_4096_k2", "chunk_block").
+
 Both sides attend the same selection: the oracle's top-K (idx, bias) is the
 input to the GPU kernel and to the oracle's sparse forward (bias rounded to
 fp32 for both).  End-to-end GPU top-K -> GPU sparse is compared on the rows
@@ -30,6 +37,15 @@ SMALL = {
                                         topk=3),
     "quarter_2048": W["prefill_32k_top25pct"].with_(name="quarter_2048", batch=1, hq=8, hkv=2,
                                                     tq=2048, tk=2048, topk=8),
+    # block-stationary path: 2 blocks of a 2048-key average history
+    "block_4096_k2": W["prefill_32k_top16"].with_(name="block_4096_k2", batch=1, hq=4, hkv=1,
+                                                  tq=4096, tk=4096, topk=2),
+    # chunked prefill on the block-stationary path (query offset 3584)
+    "chunk_block": W["prefill_32k_top16"].with_(name="chunk_block", batch=1, hq=4, hkv=2,
+                                                tq=512, tk=4096, topk=4),
+    # chunked prefill on the dense-kernel path (query offset 768, 6 of ~14 blocks)
+    "chunk_dense": W["prefill_32k_top16"].with_(name="chunk_dense", batch=2, hq=4, hkv=1,
+                                                tq=256, tk=1024, topk=6),
 }
 
 
@@ -105,6 +121,29 @@ def test_sparse_skips_invalid_entries():
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("name", ["prefill_1088", "block_4096_k2"])
+def test_sparse_prefill_skips_invalid_entries(name):
+    # both prefill paths: entries that are -1, past the row's history or out of
+    # range are skipped
+    w = SMALL[name]
+    cpu, dev, f = inputs(w, ("q", "k", "v", "qs", "ks"))
+    idx, bias32 = _oracle_selection(w, f)
+    c = (np.arange(w.tq) + w.tk - w.tq) // 64
+    bad = idx.copy()
+    bad[..., -1] = np.where(np.arange(w.tq) % 2 == 0, 10_000, c)[None, None, :]
+    o1, l1 = ops.sparse_fwd(dev["q"], dev["k"], dev["v"], torch.from_numpy(bad).to(DEV),
+                            torch.from_numpy(bias32).to(DEV))
+    good = idx.copy()
+    good[..., -1] = -1
+    o2, l2 = ops.sparse_fwd(dev["q"], dev["k"], dev["v"], torch.from_numpy(good).to(DEV),
+                            torch.from_numpy(bias32).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o_ref, l_ref = oracle.sparse_fwd(oshape(w), w.topk, f["q"], f["k"], f["v"], good,
+                                     bias32.astype(np.float64))
+    assert max_abs(host(o2), o_ref) <= 2e-2 and max_abs(host(l2), l_ref) <= 1e-3
+
+
 def test_sparse_prefill_full_size_sampled():
     w = W["prefill_32k_top16"]
     say("sparse prefill full")
@@ -164,3 +203,4 @@ def test_sparse_decode_full_size():
             assert max_abs(lg[b, hs], l_ref) <= 1e-3
     say("  O max-abs", worst)
     assert worst <= 2e-2
+

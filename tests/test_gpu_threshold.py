@@ -121,9 +121,13 @@ def test_sparse_csr_small(name, renorm):
     assert max_abs(host(lse).reshape(-1), l_ref.reshape(-1)) <= 1e-3
 
 
-def test_sparse_csr_equals_fixed():
-    # a Top-K selection, written as CSR (pads dropped), gives the fixed-budget path's bits
-    w = W["prefill_32k_top16"].with_(batch=1, hq=8, hkv=2, tq=2048, tk=2048, topk=8)
+@pytest.mark.parametrize("tq,topk,bits", [(4096, 4, True), (2048, 8, False)])
+def test_sparse_csr_equals_fixed(tq, topk, bits):
+    # a Top-K selection written as CSR (pads dropped): where the fixed-budget
+    # call takes the block-stationary path too (4096 tokens, 4 blocks) the
+    # bits are equal; where it takes the dense-kernel path (2048 tokens, 8 of
+    # ~16 blocks) the two paths agree to the bf16 bar
+    w = W["prefill_32k_top16"].with_(batch=1, hq=8, hkv=2, tq=tq, tk=tq, topk=topk)
     cpu, dev, f = inputs(w, ("q", "k", "v", "qs", "ks"))
     idx, bias = ops.topk_blocks(dev["qs"], dev["ks"], w.topk, w.tk)
     o1, l1 = ops.sparse_fwd(dev["q"], dev["k"], dev["v"], idx, bias)
@@ -134,8 +138,12 @@ def test_sparse_csr_equals_fixed():
     b = bias.reshape(-1, w.topk)[keep].contiguous()
     o2, l2 = ops.sparse_fwd_csr(dev["q"], dev["k"], dev["v"], rp, col, b)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2)
-    assert torch.equal(l1, l2)
+    if bits:
+        assert torch.equal(o1, o2)
+        assert torch.equal(l1, l2)
+    else:
+        assert max_abs(host(o1), host(o2)) <= 2e-2
+        assert max_abs(host(l1), host(l2)) <= 1e-3
 
 
 def test_sparse_csr_empty_selection():
@@ -168,7 +176,8 @@ def test_threshold_full_size():
     say("  nnz", int(rp[-1]), "mean per row", float(rp[-1]) / rows_all)
     rows = sample_rows(w, 600, seed=11)
     qs = f["qs"].reshape(-1, w.ds)
-    n_clear = 0
+    o_gpu, l_gpu = host(o).reshape(-1, w.d), host(lse).reshape(-1)
+    n_clear, e_o = 0, 0.0
     for r in rows:
         i = r % w.tq
         h = (r // w.tq) % w.hq
@@ -187,12 +196,18 @@ def test_threshold_full_size():
         assert rp[r + 1] - rp[r] == n, r
         assert np.array_equal(col[rp[r]:rp[r + 1]], idx.reshape(-1)[:n])
         assert max_abs(bias[rp[r]:rp[r + 1]], br.reshape(-1)[:n]) <= 1e-4
+        # the row's output: the oracle's forward over its own selection (the
+        # GPU's equals it on this row), on the row's key prefix
+        g = h // (w.hq // w.hkv)
+        k1 = f["k"][b, g][None, None, :t + 1]
+        v1 = f["v"][b, g][None, None, :t + 1]
+        qq = f["q"].reshape(-1, w.d)[r][None, None, None, :]
+        width = max(n, 1)
+        pi = idx.reshape(1, 1, 1, -1)[..., :width].astype(np.int32)
+        pb = br.reshape(1, 1, 1, -1)[..., :width].astype(np.float32).astype(np.float64)
+        o1, l1 = oracle.sparse_fwd(S1, width, qq, k1, v1, pi, pb)
+        e_o = max(e_o, max_abs(o_gpu[r], o1.reshape(-1)))
+        assert abs(l_gpu[r] - float(l1.reshape(-1)[0])) <= 1e-3
     assert n_clear >= 0.9 * len(rows)
-    # the forward over the GPU's own selection, sampled rows
-    width = int(np.diff(rp).max())
-    pi, pb = _padded(rp, col, bias.astype(np.float64), rows_all, width)
-    o_ref, l_ref = oracle.sparse_fwd(oshape(w), width, f["q"], f["k"], f["v"], pi, pb, rows=rows)
-    e = max_abs(host(o).reshape(-1, w.d)[rows], o_ref)
-    say("  O max-abs", e, "max per row", width)
-    assert e <= 2e-2
-    assert max_abs(host(lse).reshape(-1)[rows], l_ref) <= 1e-3
+    say("  O max-abs", e_o, "over", n_clear, "rows")
+    assert e_o <= 2e-2
