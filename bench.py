@@ -122,7 +122,7 @@ def cpu_baseline(T: int):
 KERNELS = {
     "bwd_dkdv": ("bwd_dkdv16_kernel<32, 1>", ("attn_bwd.hip", "sas_device.h", "sas_internal.h")),
     "bwd_dq": ("bwd_dq32_kernel<32, 1>", ("attn_bwd.hip", "sas_device.h", "sas_internal.h")),
-    "fwd": ("attn_fwd_kernel<128, 32, 1>", ("attn_fwd.hip", "sas_device.h", "sas_internal.h")),
+    "fwd": ("attn_fwd_kernel<128, 32, 1, false>", ("attn_fwd.hip", "sas_device.h", "sas_internal.h")),
 }
 
 
@@ -152,6 +152,25 @@ def stored_traffic(part):
         return None
     return round(rec["fetch_kib"] * rec["fetch_factor"] * 1024 +
                  rec["write_kib"] * rec["write_factor"] * 1024)
+
+
+def stored_mfma(part):
+    """Matrix-core busy share and shader clock of a training kernel from the
+    committed rocprofv3 counter summary (SQ_VALU_MFMA_BUSY_CYCLES over
+    GRBM_GUI_ACTIVE); None when absent or the kernel's sources changed."""
+    name, files = KERNELS[part]
+    path = os.path.join(ROOT, "profiles", "mfma_util_train_32k.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("record: "):
+                rec = json.loads(line[len("record: "):])
+                if rec.get("part") == part:
+                    if rec.get("kernel") != name or rec.get("src") != source_digest(files):
+                        return None
+                    return {"mfma_busy": rec["busy"], "clock_ghz": rec["clock_ghz"]}
+    return None
 
 
 def main():
@@ -367,6 +386,8 @@ def main():
                      "fwd": "4*d flop per attended pair (S, PV)",
                      "bwd_dq": "6*d flop per attended pair (S, dP, dQ)"}[dom],
         "units_per_launch": pairs_t,
+        # the profiled launch's matrix-core busy share and clock (counters)
+        "counters": stored_mfma(dom),
     }
 
     out = {
