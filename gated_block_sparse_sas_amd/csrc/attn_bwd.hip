@@ -550,14 +550,20 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
   constexpr int NI = TE / 512;                         // 1 KB direct loads per tile and tensor
   constexpr int XI = (NI + kDq32Waves - 1) / kDq32Waves;
   constexpr int DH = DS / 2;                           // selector dims per lane half
-  constexpr int BU = kBlock / UB;                      // tokens per gate unit
+  constexpr int BU = UB > 0 ? kBlock / UB : 1;         // tokens per gate unit (UB > 0)
+  // UB = 0 (units of D.blk = 1 .. 8 tokens): the tile's 64 per-key ks rows
+  // (each key's unit row, expanded beforehand) sit in LDS, XS 16-byte slots
+  // per row (one padding slot), read as Z^T operands and transposed for dqs
+  constexpr int XS = DS / 8 + 1, XP = XS * 8;
+  constexpr int SN = UB > 0 ? UB * DS : kBlock * XP;
+  static_assert(UB > 0 || DS == 32, "token units: ds = 32 (five waves load the ks tile)");
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   __shared__ __align__(16) bf16 K0[TE];
   __shared__ __align__(16) bf16 K1[TE];
   __shared__ __align__(16) bf16 V0[TE];
   __shared__ __align__(16) bf16 V1[TE];
-  __shared__ __align__(16) bf16 S0[UB * DS];
-  __shared__ __align__(16) bf16 S1[UB * DS];
+  __shared__ __align__(16) bf16 S0[SN];
+  __shared__ __align__(16) bf16 S1[SN];
   __shared__ __align__(16) bf16 Qs[kDq32Rows * KP];  // the workgroup's Q rows
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -571,20 +577,25 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
   const bool valid = qi < D.tq;
   const int qc = min(qi, D.tq - 1);
   const int t = D.qoff + qc;
-  const int c = t / BU;       // historical units of the row
+  const int lb = __builtin_ctz(UB > 0 ? BU : D.blk);  // log2 of the unit size
+  const int c = t >> lb;       // historical units of the row
+  const int tcur0 = c << lb;   // first key of the row's own unit
   const int ct = t / kBlock;  // the row's own 64-key tile
   const int c_lo = (D.qoff + min(wq0, D.tq - 1)) / kBlock;
   const int c_hi = (D.qoff + min(wq0 + 31, D.tq - 1)) / kBlock;
   const int c_end = (D.qoff + min(qt * kDq32Rows + kDq32Rows - 1, D.tq - 1)) / kBlock;
   const size_t row = ((size_t)b * D.hq + h) * D.tq + qc;
 
-  // zero dz[row, j] for j >= c(row) (coalesced over the workgroup's rows)
-  for (int r = 0; r < kDq32Rows; ++r) {
-    const int i = qt * kDq32Rows + r;
-    if (i >= D.tq) break;
-    const int cr = (D.qoff + i) / BU;
-    float* zr = dz + (((size_t)b * D.hq + h) * D.tq + i) * D.nb;
-    for (int jj = cr + tid; jj < D.nb; jj += kDq32Threads) zr[jj] = 0.f;
+  // zero dz[row, j] for j >= c(row) (coalesced over the workgroup's rows);
+  // UB = 0 writes dz only when the caller asks for it
+  if (UB > 0 || dz != nullptr) {
+    for (int r = 0; r < kDq32Rows; ++r) {
+      const int i = qt * kDq32Rows + r;
+      if (i >= D.tq) break;
+      const int cr = (D.qoff + i) >> lb;
+      float* zr = dz + (((size_t)b * D.hq + h) * D.tq + i) * D.nb;
+      for (int jj = cr + tid; jj < D.nb; jj += kDq32Threads) zr[jj] = 0.f;
+    }
   }
 
   // Q and dO as B operands (lane: query l32, dims 16 s + 8 hh .. + 7): dO in
@@ -607,9 +618,11 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
   // of unit u's logits (gate bias minus the row's log-sum-exp; -inf past the
   // row's own unit), slot nb the row's D; rows padded to tqp (padding: -inf,
   // D 0).  The offsets are the ones this kernel applies itself.
-  const size_t rbase = ((size_t)b * D.hq + h) * (size_t)(D.nb + 1) * tqp + qi;
+  // UB = 0: four slots per row instead (written at the end): lam log2 e,
+  // lse log2 e (+inf for padding rows), D, and sum_j dbeta / blk.
+  const size_t rbase = ((size_t)b * D.hq + h) * (size_t)(UB > 0 ? D.nb + 1 : 4) * tqp + qi;
   const bool rw = hh == 0 && qi < tqp;
-  if (rw) rowd[rbase + (size_t)D.nb * tqp] = valid ? dlt : 0.f;
+  if (UB > 0 && rw) rowd[rbase + (size_t)D.nb * tqp] = valid ? dlt : 0.f;
   // this lane's half of the row's qs as bf16 pairs (packed dot products, as
   // in the forward), and its half of the dqs accumulator
   bf16x2 qsv[DS / 4];
@@ -620,7 +633,20 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
   for (int e = 0; e < DH; ++e) dqsa[e] = 0.f;
   const float lam_t = c > 0 ? lam[row] : 0.f;
   const float l2 = lse[row] * kLog2e;
-  const bf16* ksb = ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS;
+  // UB > 0: ks rows of the selector head; UB = 0: the per-key rows [tk][DS]
+  const bf16* ksb = ks + ((size_t)b * D.hks + sh) * (size_t)(UB > 0 ? D.nb : D.tk) * DS;
+  // UB = 0: the row's qs as Z^T B operands, the dqs^T accumulator, and the
+  // log2-domain selector constants
+  bf16x8 qsf[UB == 0 ? DS / 16 : 1];
+  f32x16 dqsz[UB == 0 ? DS / 32 : 1];
+  if constexpr (UB == 0) {
+#pragma unroll
+    for (int s = 0; s < DS / 16; ++s) qsf[s] = *(const bf16x8*)(qs + row * DS + 16 * s + 8 * hh);
+#pragma unroll
+    for (int x = 0; x < DS / 32; ++x) dqsz[x] = f32x16{};
+  }
+  const float zs2 = D.sel_scale * kLog2e, lam2 = lam_t * kLog2e;
+  const float inv_blk = 1.f / (float)(1 << lb);
   const bf16* kb = k + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
   const bf16* vb = v + ((size_t)b * D.hkv + g) * (size_t)D.tk * HD;
   const float c1 = D.sm_scale * kLog2e;
@@ -648,7 +674,15 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
         __builtin_amdgcn_global_load_lds(vt + toff[x], Vd + ins * 512, 16, 0, 0);
       }
     }
-    if (wave == 0 && lane < UB * DS / 8) {
+    if constexpr (UB == 0) {
+      // slot s = 64 wave + lane: key row s / XS, chunk s % XS (the padding
+      // chunk reloads chunk 0)
+      if (wave < XS) {
+        const int sl = 64 * wave + lane, kr = sl / XS, ch = sl % XS;
+        const bf16* const src = ksb + ((size_t)j * kBlock + kr) * DS + (ch < DS / 8 ? ch : 0) * 8;
+        __builtin_amdgcn_global_load_lds(src, Sd + wave * 512, 16, 0, 0);
+      }
+    } else if (wave == 0 && lane < UB * DS / 8) {
       const bf16* const src = ksb + (size_t)j * UB * DS + lane * 8;
       __builtin_amdgcn_global_load_lds(src, Sd, 16, 0, 0);
     }
@@ -657,14 +691,67 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
   // group points at key row 4 hh + kk, columns 16 ((lane >> 4) & 1) + 4 a
   const int kbase = (4 * hh + ((lane & 15) >> 2)) * KP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   // unit of this lane's key 32 mt + 8 (r / 4) + 4 hh + r % 4 within the tile
-  auto unit = [](int mt, int r) { return UB == 1 ? 0 : (UB == 2 ? mt : 2 * mt + r / 8); };
+  auto unit = [](int mt, int r) { return UB <= 1 ? 0 : (UB == 2 ? mt : 2 * mt + r / 8); };
+  // UB = 0: the same transposing reads over the per-key ks rows (pitch XP)
+  const int xbase = (4 * hh + ((lane & 15) >> 2)) * XP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // UB = 0, dz requested: dz[row, unit] = sum of e over the unit's keys.  A
+  // lane holds runs of 4 consecutive keys (32 mt + 8 q + 4 hh + 0..3); units
+  // of 8 keys join the runs of the two lane halves.
+  auto write_dz_units = [&](const float (&e)[UB == 0 ? 2 : 1][16], int j, size_t rw_, bool ok) {
+    const int bsz = 1 << lb;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int k0 = j * kBlock + 32 * mt + 8 * q4 + 4 * hh;  // first key of the run
+        const float* er = &e[mt][4 * q4];
+        float* zr = dz + rw_ * D.nb;
+        if (bsz == 8) {
+          float v = er[0] + er[1] + er[2] + er[3];
+          v += __shfl_xor(v, 32);
+          if (ok && hh == 0 && k0 < tcur0) zr[k0 >> 3] = v;
+        } else if (bsz == 4) {
+          if (ok && k0 < tcur0) zr[k0 >> 2] = er[0] + er[1] + er[2] + er[3];
+        } else if (bsz == 2) {
+          if (ok && k0 < tcur0) zr[k0 >> 1] = er[0] + er[1];
+          if (ok && k0 + 2 < tcur0) zr[(k0 >> 1) + 1] = er[2] + er[3];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (ok && k0 + i < tcur0) zr[k0 + i] = er[i];
+        }
+      }
+    }
+  };
 
   auto compute = [&](int j, const bf16* Ks, const bf16* Vs, const bf16* Ss) {
     if (j > c_hi) return;
-    float bias2[UB];
+    constexpr int NU = UB > 0 ? UB : 1;
+    float bias2[NU];
 #pragma unroll
-    for (int ub = 0; ub < UB; ++ub) bias2[ub] = 0.f;
-    if (UB == 1 ? j < c_hi : j <= c_hi) {
+    for (int ub = 0; ub < NU; ++ub) bias2[ub] = 0.f;
+    // UB = 0: log2-domain gate bias of each (key, row) of the tile, zero on
+    // the row's own unit and past it
+    float zb[UB == 0 ? 2 : 1][16];
+    if constexpr (UB == 0) {
+      f32x16 zacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < DS / 16; ++s) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 a = *(const bf16x8*)&Ss[(32 * mt + l32) * XP + 16 * s + 8 * hh];
+          zacc[mt] = mfma32(a, qsf[s], zacc[mt]);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
+          zb[mt][r] = u < tcur0 ? fmaf(zacc[mt][r], zs2, -lam2) : 0.f;
+        }
+      }
+    } else if (UB == 1 ? j < c_hi : j <= c_hi) {
 #pragma unroll
       for (int ub = 0; ub < UB; ++ub) {
         const bf16x2* kr = (const bf16x2*)(Ss + ub * DS + hh * DH);
@@ -676,9 +763,9 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
         if (j * UB + ub < c) bias2[ub] = (D.sel_scale * part - lam_t) * kLog2e;
       }
     }
-    if (rw) {
+    if (UB > 0 && rw) {
 #pragma unroll
-      for (int ub = 0; ub < UB; ++ub) {
+      for (int ub = 0; ub < NU; ++ub) {
         const int ju = j * UB + ub;
         rowd[rbase + (size_t)ju * tqp] = valid && ju <= c ? bias2[ub] - l2 : -INFINITY;
       }
@@ -708,7 +795,7 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        pv[mt][r] = exp2_raw(fmaf(sacc[mt][r], c1, bias2[unit(mt, r)] - l2));
+        pv[mt][r] = exp2_raw(fmaf(sacc[mt][r], c1, (UB == 0 ? zb[mt][r] : bias2[unit(mt, r)]) - l2));
     if (j >= c_lo) {  // tile meets some row's own tile: cut keys after the row (or the tile)
       const int mlim = j < ct ? kBlock : (j > ct ? -1 : t - j * kBlock - 4 * hh);
 #pragma unroll
@@ -717,29 +804,76 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
         for (int r = 0; r < 16; ++r)
           if (32 * mt + 8 * (r / 4) + (r % 4) > mlim) pv[mt][r] = 0.f;
     }
-    float dsum[UB];
+    float dsum[NU];
 #pragma unroll
-    for (int ub = 0; ub < UB; ++ub) dsum[ub] = 0.f;
+    for (int ub = 0; ub < NU; ++ub) dsum[ub] = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float ds = pv[mt][r] * (pacc[mt][r] - dlt);
         sacc[mt][r] = ds;
-        dsum[unit(mt, r)] += ds;
+        if constexpr (UB == 0) {
+          // the row's own unit (keys tcur0 .. t; later keys have ds = 0)
+          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
+          if (u >= tcur0) dsum[0] += ds;
+        } else {
+          dsum[unit(mt, r)] += ds;
+        }
       }
     }
 #pragma unroll
-    for (int ub = 0; ub < UB; ++ub) dsum[ub] += __shfl_xor(dsum[ub], 32);
+    for (int ub = 0; ub < NU; ++ub) dsum[ub] += __shfl_xor(dsum[ub], 32);
     // the row's own tile comes first (tiles run from the diagonal down): its
     // current unit gives sum_{j'<c} dbeta before any historical unit
     if (j == ct) {
+      if constexpr (UB == 0) {
+        sdb = -dsum[0];
+      } else {
 #pragma unroll
-      for (int ub = 0; ub < UB; ++ub)
-        if (j * UB + ub == c) sdb = -dsum[ub];
+        for (int ub = 0; ub < NU; ++ub)
+          if (j * UB + ub == c) sdb = -dsum[ub];
+      }
+    }
+    if constexpr (UB == 0) {
+      // e = dS - g sdb / blk on historical keys (0 elsewhere): summed over a
+      // unit's keys it is dz; dqs^T += KS^T e^T over the tile's keys
+      const float sb_k = sdb * inv_blk;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
+          zb[mt][r] = u < tcur0 ? sacc[mt][r] - exp2_raw(zb[mt][r]) * sb_k : 0.f;
+        }
+      }
+      if (dz != nullptr) write_dz_units(zb, j, row, valid);
+      // e enters as a bf16 pair (e_hi + e_lo: 16 mantissa bits), so that dqs
+      // keeps fp32-like accuracy where its terms cancel
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          bf16x8 eh, el;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            eh[e] = (bf16)zb[mt][8 * pp + e];
+            el[e] = (bf16)(zb[mt][8 * pp + e] - (float)eh[e]);
+          }
+#pragma unroll
+          for (int x = 0; x < DS / 32; ++x) {
+            const bf16* xp = &Ss[xbase + (32 * mt + 16 * pp) * XP + 32 * x];
+            const bf16x4 lo = ds_read_tr(xp);
+            const bf16x4 hi = ds_read_tr(xp + 8 * XP);
+            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            dqsz[x] = mfma32(a, eh, dqsz[x]);
+            dqsz[x] = mfma32(a, el, dqsz[x]);
+          }
+        }
+      }
     }
 #pragma unroll
-    for (int ub = 0; ub < UB; ++ub) {
+    for (int ub = 0; ub < (UB > 0 ? UB : 0); ++ub) {
       if (j * UB + ub < c) {
         const float dzv = dsum[ub] - exp2_raw(bias2[ub]) * sdb;
         if (valid && hh == 0) dz[row * D.nb + j * UB + ub] = dzv;
@@ -802,8 +936,29 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
         *(bf16x4*)(qr + 32 * dm + 8 * rr) = w;
       }
     }
+    if constexpr (UB == 0) {
+      bf16* sr = dqs + row * DS + 4 * hh;
 #pragma unroll
-    for (int e = 0; e < DH; ++e) dqs[row * DS + hh * DH + e] = (bf16)(dqsa[e] * D.sel_scale);
+      for (int x = 0; x < DS / 32; ++x) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)(dqsz[x][4 * rr + e] * D.sel_scale);
+          *(bf16x4*)(sr + 32 * x + 8 * rr) = w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DH; ++e) dqs[row * DS + hh * DH + e] = (bf16)(dqsa[e] * D.sel_scale);
+    }
+  }
+  if (UB == 0 && rw) {
+    const size_t sl = (size_t)tqp;
+    rowd[rbase] = valid ? lam2 : 0.f;
+    rowd[rbase + sl] = valid ? l2 : INFINITY;
+    rowd[rbase + 2 * sl] = valid ? dlt : 0.f;
+    rowd[rbase + 3 * sl] = valid ? sdb * inv_blk : 0.f;
   }
 }
 
@@ -1070,17 +1225,28 @@ template <int DS, int UB>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ rowd, int tqp,
+    const bf16* __restrict__ qs, const bf16* __restrict__ ks, float* __restrict__ dks_acc,
     bf16* __restrict__ dk, bf16* __restrict__ dv, Dims D, int xcd_groups) {
   constexpr int HD = 128, QT = 32, TS = QT * 18, TE = TS * 8;  // tile slots, elements
   constexpr int NI = TS / 64;              // direct-load instructions per tile and tensor
   constexpr int XI = (NI + 3) / 4;         // ... per wave (at most)
-  constexpr int BU = kBlock / UB;          // tokens per gate unit (UB units per 64-key tile)
+  constexpr int BU = UB > 0 ? kBlock / UB : 1;  // tokens per gate unit (UB units per 64-key tile)
+  // UB = 0 (units of D.blk = 1 .. 8 tokens): an item also brings its 32 qs
+  // rows (XS 16-byte slots per row, one of them padding; three direct loads)
+  // and four row values (lam log2 e, lse log2 e, D, sum_j dbeta / blk); the
+  // kernel forms Z = QS KS^T, the gate g and e = dS - g sum_j dbeta / blk per
+  // (row, key), and dks^T += QS^T e, summed over each unit's keys at the end.
+  constexpr int XS = DS / 8 + 1, XP = XS * 8, XN = UB > 0 ? 8 : 3 * 512;
+  constexpr int NF = UB > 0 ? UB + 1 : 4;
+  static_assert(UB > 0 || DS == 32, "token units: ds = 32 (three waves load the qs tile)");
   __shared__ __align__(16) bf16 Q0[TE];
   __shared__ __align__(16) bf16 Q1[TE];
   __shared__ __align__(16) bf16 O0[TE];
   __shared__ __align__(16) bf16 O1[TE];
-  __shared__ __align__(16) float F0[(UB + 1) * QT];  // log2 offset of (unit, row), then D
-  __shared__ __align__(16) float F1[(UB + 1) * QT];
+  __shared__ __align__(16) float F0[NF * QT];  // log2 offset of (unit, row), then D
+  __shared__ __align__(16) float F1[NF * QT];
+  __shared__ __align__(16) bf16 X0[XN];
+  __shared__ __align__(16) bf16 X1[XN];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1118,6 +1284,39 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     dva[dm] = f32x4{};
   }
   const float c1 = D.sm_scale * kLog2e;
+  const int lb = __builtin_ctz(UB > 0 ? BU : D.blk);
+  // UB = 0: this lane's key's unit row of ks (the Z B operand), reloaded when
+  // the selector head changes from one query head of the group to the next;
+  // dks^T of the wave's 16 keys (16 dims x 16 keys per block)
+  bf16x8 xf[UB == 0 ? DS / 32 : 1];
+  f32x4 dksa[UB == 0 ? DS / 16 : 1];
+  int shc = -1;
+  const float zs2 = D.sel_scale * kLog2e;
+  auto load_x = [&](int shn) {
+    const bf16* kr = ks + (((size_t)b * D.hks + shn) * D.nb + (key >> lb)) * DS + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < DS / 32; ++s) xf[s] = *(const bf16x8*)(kr + 32 * s);
+#pragma unroll
+    for (int x = 0; x < DS / 16; ++x) dksa[x] = f32x4{};
+    shc = shn;
+  };
+  // sum dks^T over each unit's keys (lanes i16 of one unit are adjacent) and
+  // add it to the fp32 accumulator of selector head shc
+  auto flush_x = [&]() {
+    const int bsz = 1 << lb;
+#pragma unroll
+    for (int x = 0; x < DS / 16; ++x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = dksa[x][r];
+        for (int o = 1; o < bsz; o <<= 1) v += __shfl_xor(v, o);
+        if ((i16 & (bsz - 1)) == 0)
+          atomicAdd(dks_acc + (((size_t)b * D.hks + shc) * D.nb + (key >> lb)) * DS + 16 * x +
+                        4 * g4 + r,
+                    v);
+      }
+    }
+  };
   const int qt0 = max(0, j * kBlock - D.qoff) / QT;
   const int per_h = (D.tq + QT - 1) / QT - qt0;
   const int nitems = D.hpg * per_h;
@@ -1145,7 +1344,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     x.hl = hl;
     x.t = 0;
     x.qo = ((hq0 + hl) * D.tq + (size_t)qt0 * QT) * HD;
-    x.fo = (hq0 + hl) * (size_t)(D.nb + 1) * tqp + (size_t)qt0 * QT;
+    x.fo = (hq0 + hl) * (size_t)(UB > 0 ? D.nb + 1 : 4) * tqp + (size_t)qt0 * QT;
     return x;
   };
   auto next = [&](Item x) {
@@ -1157,13 +1356,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
   auto row0 = [&](Item x) { return (qt0 + x.t) * QT; };
   // this lane's part of the row-data address: slot (unit s of tile j, or D
   // for s = UB) and rows 4 e .. 4 e + 3 for lane 8 s + e
-  const int fsl = min(lane >> 3, UB);
-  const size_t flane = (fsl < UB ? (size_t)j * UB + fsl : (size_t)D.nb) * tqp + 4 * (lane & 7);
+  const int fsl = min(lane >> 3, NF - 1);
+  const size_t flane =
+      (UB == 0 ? (size_t)fsl : (fsl < UB ? (size_t)j * UB + fsl : (size_t)D.nb)) * tqp +
+      4 * (lane & 7);
+  // UB = 0: slot s = 64 (wave - 1) + lane of the qs tile: row s / XS, chunk
+  // s % XS (padding chunk and slots past the tile reload chunk 0 / row 31)
+  const int xsl = max(64 * (wave - 1) + lane, 0);
+  const int xrow = min(xsl / XS, QT - 1), xch = xsl < QT * XS ? xsl % XS : 0;
+  const int xoff = xrow * DS + (xch < DS / 8 ? xch : 0) * 8;
 
   // direct loads of an item's Q and dO tiles (all waves; rows past the end
   // reload the last row) and of its row data (wave 0, lanes 0 .. 8 UB + 7)
-  auto issue = [&](Item x, bf16* Qd, bf16* Od, float* Fd) {
-    if (wave == 0 && lane < 8 * (UB + 1)) {
+  auto issue = [&](Item x, bf16* Qd, bf16* Od, float* Fd, bf16* Xd) {
+    if constexpr (UB == 0) {
+      if (wave >= 1) {  // waves 1 .. 3: one 1 KB load each of the qs tile
+        const int r0 = row0(x);
+        const int rr = min(xrow, D.tq - 1 - r0);
+        const bf16* const src =
+            qs + ((hq0 + x.hl) * D.tq + r0 + rr) * (size_t)DS + (xoff - xrow * DS);
+        __builtin_amdgcn_global_load_lds(src, Xd + (wave - 1) * 512, 16, 0, 0);
+      }
+    }
+    if (wave == 0 && lane < 8 * NF) {
       // (through a named pointer: passing the sum straight to the builtin
       // makes the host pass drop this kernel's launch stub)
       const float* const src = rowd + x.fo + flane;
@@ -1195,10 +1410,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     }
   };
   // the unit of this wave's 16 keys within the tile
-  const int uw = UB == 1 ? 0 : (wave * 16) / BU;
+  const int uw = UB <= 1 ? 0 : (wave * 16) / BU;
 
-  auto compute = [&](Item x, const bf16* Qs, const bf16* Os, const float* Fs) {
+  auto compute = [&](Item x, const bf16* Qs, const bf16* Os, const float* Fs, const bf16* Xs) {
     const int i0 = row0(x);
+    if constexpr (UB == 0) {
+      const int shn = (int)((hq0 + x.hl - (size_t)b * D.hq) / D.hps);
+      if (shn != shc) {
+        if (shc >= 0) flush_x();
+        load_x(shn);
+      }
+    }
     if (D.qoff + min(i0 + QT - 1, D.tq - 1) < key0) return;  // every row before these keys
     // keys after a row's position are cut: slot (16 mq + r) of this lane is
     // cut when it is below mlim (no cut away from the diagonal)
@@ -1233,8 +1455,40 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_s_setprio(0);
     // P and dS; the causal cut only on items that meet the diagonal
+    // UB = 0: Z = QS KS^T for the same (row, key) slots, and e (in zacc)
+    f32x4 zacc[2] = {f32x4{}, f32x4{}};
+    if constexpr (UB == 0) {
+#pragma unroll
+      for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+        for (int s = 0; s < DS / 32; ++s)
+          zacc[mq] = mfma16(*(const bf16x8*)&Xs[(16 * mq + i16) * XP + 32 * s + 8 * g4], xf[s],
+                            zacc[mq]);
+    }
     auto softmax_ds = [&](auto mask_tag) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
+      if constexpr (UB == 0) {
+        const int tr0 = D.qoff + i0 + 4 * g4;  // position of row 4 g4 (M-tile 0)
+#pragma unroll
+        for (int mq = 0; mq < 2; ++mq) {
+          const f32x4 la = *(const f32x4*)&Fs[16 * mq + 4 * g4];
+          const f32x4 ll = *(const f32x4*)&Fs[QT + 16 * mq + 4 * g4];
+          const f32x4 dl = *(const f32x4*)&Fs[2 * QT + 16 * mq + 4 * g4];
+          const f32x4 sb = *(const f32x4*)&Fs[3 * QT + 16 * mq + 4 * g4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool hist = (key >> lb) < ((tr0 + 16 * mq + r) >> lb);
+            const float zl = fmaf(zacc[mq][r], zs2, -la[r]);
+            float p = exp2_raw(fmaf(sacc[mq][r], c1, (hist ? zl : 0.f) - ll[r]));
+            if (MASK && 16 * mq + r < mlim) p = 0.f;
+            sacc[mq][r] = p;
+            const float ds = p * (pacc[mq][r] - dl[r]);
+            pacc[mq][r] = ds;
+            zacc[mq][r] = hist ? ds - exp2_raw(zl) * sb[r] : 0.f;
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int mq = 0; mq < 2; ++mq) {
         const f32x4 of = *(const f32x4*)&Fs[uw * QT + 16 * mq + 4 * g4];
@@ -1272,29 +1526,54 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv16_kernel(
       const bf16x4 qhi = ds_read_tr(&Qs[t1 + 16 * dm]);
       dka[dm] = mfma16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), sb, dka[dm]);
     }
+    if constexpr (UB == 0) {
+      // dks^T += QS^T e: the same transposing reads over the qs tile; e as a
+      // bf16 pair (e_hi + e_lo), so that dks keeps fp32-like accuracy where
+      // the terms of a unit cancel
+      bf16x8 eh, el;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        eh[r] = (bf16)zacc[0][r];
+        eh[4 + r] = (bf16)zacc[1][r];
+        el[r] = (bf16)(zacc[0][r] - (float)eh[r]);
+        el[4 + r] = (bf16)(zacc[1][r] - (float)eh[4 + r]);
+      }
+      const int x0 = (4 * g4 + k4) * XP + 4 * a4, x1 = x0 + 16 * XP;
+#pragma unroll
+      for (int x = 0; x < DS / 16; ++x) {
+        const bf16x4 slo = ds_read_tr(&Xs[x0 + 16 * x]);
+        const bf16x4 shi = ds_read_tr(&Xs[x1 + 16 * x]);
+        const bf16x8 a = __builtin_shufflevector(slo, shi, 0, 1, 2, 3, 4, 5, 6, 7);
+        dksa[x] = mfma16(a, eh, dksa[x]);
+        dksa[x] = mfma16(a, el, dksa[x]);
+      }
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
   if (nitems > 0) {
     Item cur = first(0);
-    issue(cur, Q0, O0, F0);
+    issue(cur, Q0, O0, F0, X0);
     wait_vmem();
     __syncthreads();
     // Item it: the tiles and row data of it + 1 load while it computes.
     // Unrolled by two so that both buffers' code sits in one loop body.
     for (int it = 0; it < nitems; it += 2) {
       const Item n1 = next(cur), n2 = next(n1);
-      if (it + 1 < nitems) issue(n1, Q1, O1, F1);
-      compute(cur, Q0, O0, F0);
+      if (it + 1 < nitems) issue(n1, Q1, O1, F1, X1);
+      compute(cur, Q0, O0, F0, X0);
       wait_vmem();
       __syncthreads();
       if (it + 1 >= nitems) break;
-      if (it + 2 < nitems) issue(n2, Q0, O0, F0);
-      compute(n1, Q1, O1, F1);
+      if (it + 2 < nitems) issue(n2, Q0, O0, F0, X0);
+      compute(n1, Q1, O1, F1, X1);
       wait_vmem();
       __syncthreads();
       cur = n2;
     }
+  }
+  if constexpr (UB == 0) {
+    if (shc >= 0) flush_x();
   }
   bf16* kr = dk + kvrow * HD + 4 * g4;
   bf16* vr = dv + kvrow * HD + 4 * g4;
@@ -1390,22 +1669,40 @@ __global__ void scale_convert_kernel(const float* __restrict__ src, ST* __restri
     dst[i] = from_f32<ST>(src[i] * scale);
 }
 
+// Per-key selector rows for token-level units: ksx[b, s, u, :] = ks[b, s, u / blk, :].
+__global__ void ks_expand_kernel(const bf16* __restrict__ ks, bf16* __restrict__ ksx, int lb,
+                                 int tk, int ds8, size_t n8) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t ch = i % ds8, u = (i / ds8) % tk, bs = i / ((size_t)ds8 * tk);
+    const size_t src = (bs * (size_t)(tk >> lb) + (u >> lb)) * ds8 + ch;
+    ((bf16x8*)ksx)[i] = ((const bf16x8*)ks)[src];
+  }
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// bf16, d = 128 with units of fewer than 16 tokens: the token-unit kernels
+static bool token_units(const Dims& D) { return D.d == 128 && D.blk < 16; }
 
 BwdWs bwd_workspace(const Dims& D, bool need_dz) {
   BwdWs W;
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
+  const bool tok = token_units(D);
   size_t off = 0;
   W.off_delta = off;
   off += align256(rows * sizeof(float));
   W.off_dz = off;
-  if (need_dz) off += align256(rows * (size_t)D.nb * sizeof(float));
+  if (need_dz && !tok) off += align256(rows * (size_t)D.nb * sizeof(float));
   W.off_dks = off;
   off += align256((size_t)D.batch * D.hks * D.nb * D.ds * sizeof(float));
   W.tqp = (D.tq + 31) / 32 * 32;
   W.off_rows = off;
   if (D.d == 128)
-    off += align256((size_t)D.batch * D.hq * (D.nb + 1) * W.tqp * sizeof(float));
+    off += align256((size_t)D.batch * D.hq * (tok ? 4 : D.nb + 1) * W.tqp * sizeof(float));
+  W.off_ksx = off;
+  if (tok && D.blk > 1)
+    off += align256((size_t)D.batch * D.hks * D.tk * D.ds * sizeof(bf16));
   W.total = off;
   return W;
 }
@@ -1450,7 +1747,40 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   const int groups = D.batch * D.hkv;
   const int xg = groups % 8 == 0 ? groups / 8 : 0;
   hipError_t e;
-  if constexpr (HD == 128) {
+  if constexpr (UB == 0) {
+    // token-level units: dz only when the caller asks for it; dks from the
+    // dK/dV kernel (fp32 accumulator, scaled and converted at the end)
+    const size_t nacc = (size_t)D.batch * D.hks * D.nb * D.ds;
+    const unsigned fg = (unsigned)std::min<size_t>((nacc + 255) / 256, 4096);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(fg), dim3(256), 0, st, acc, nacc);
+    const bf16* ksx = (const bf16*)ks;
+    if (D.blk > 1) {
+      const size_t n8 = (size_t)D.batch * D.hks * D.tk * (D.ds / 8);
+      const unsigned xgd = (unsigned)std::min<size_t>((n8 + 255) / 256, 4096);
+      hipLaunchKernelGGL(ks_expand_kernel, dim3(xgd), dim3(256), 0, st, (const bf16*)ks,
+                         (bf16*)(ws + W.off_ksx), __builtin_ctz(D.blk), D.tk, D.ds / 8, n8);
+      ksx = (const bf16*)(ws + W.off_ksx);
+    }
+    const int nqtw = (D.tq + kDq32Rows - 1) / kDq32Rows;
+    hipLaunchKernelGGL((bwd_dq32_kernel<DS, 0>), dim3(D.batch * D.hq * nqtw), dim3(kDq32Threads),
+                       0, st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)o,
+                       (const bf16*)dout, lse, (const bf16*)qs, ksx, lam, (bf16*)dq,
+                       (bf16*)dqs, dz, rowd, W.tqp, D, nqtw, xg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    E.record(0, st);
+    hipLaunchKernelGGL((bwd_dkdv16_kernel<DS, 0>), dim3(groups * (D.tk / kBlock)), dim3(256), 0,
+                       st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
+                       (const float*)rowd, W.tqp, (const bf16*)qs, (const bf16*)ks, acc,
+                       (bf16*)dk, (bf16*)dv, D, xg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    E.record(1, st);
+    hipLaunchKernelGGL((scale_convert_kernel<bf16>), dim3(fg), dim3(256), 0, st,
+                       (const float*)acc, (bf16*)dks, D.sel_scale, nacc);
+    E.record(2, st);
+    return hipGetLastError();
+  } else if constexpr (HD == 128) {
     // The 32-row kernel fits two waves per SIMD (256 registers each) while
     // the selector terms of a tile (ds / 2 qs and dqs values per lane, UB ks
     // rows) stay small; wider selectors take the 16-row kernel.
@@ -1482,7 +1812,8 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   if constexpr (HD == 128) {
     hipLaunchKernelGGL((bwd_dkdv16_kernel<DS, UB>), dim3(groups * (D.tk / kBlock)), dim3(256), 0,
                        st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
-                       (const float*)rowd, W.tqp, (bf16*)dk, (bf16*)dv, D, xg);
+                       (const float*)rowd, W.tqp, nullptr, nullptr, nullptr, (bf16*)dk,
+                       (bf16*)dv, D, xg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     E.record(1, st);
@@ -1511,7 +1842,9 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
 #define SAS_BWD_CALL(HDV, DSV, UBV)                                                           \
   return launch_bwd_t<HDV, DSV, UBV>(q, k, v, o, dout, lse, qs, ks, lam, dq, dk, dv, dqs, dks, \
                                      dz, ws, W, D, E, st);
-  // d = 128: gate units of 64, 32 or 16 tokens; d = 64: 64
+  // d = 128: gate units of 64, 32 or 16 tokens, and (ds = 32) of 8, 4, 2 or
+  // 1 token; d = 64: 64
+  if (D.d == 128 && D.ds == 32 && D.blk < 16) SAS_BWD_CALL(128, 32, 0)
 #define SAS_BWD_CASE128(DSV)                        \
   if (D.d == 128 && D.ds == DSV) {                  \
     if (D.blk == 64) SAS_BWD_CALL(128, DSV, 1)      \

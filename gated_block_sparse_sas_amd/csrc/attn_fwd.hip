@@ -46,7 +46,11 @@ namespace sas {
 constexpr int kFwdWaves = 8, kFwdThreads = 64 * kFwdWaves, kFwdRows = 32 * kFwdWaves;
 
 // UB gate units per 64-key tile (UB = 1: 64-token blocks; 2, 4: units of 32,
-// 16 tokens, whose bias then changes inside the tile).  GIVEN: the bias of
+// 16 tokens, whose bias then changes inside the tile).  UB = 0: units of
+// D.blk = 1, 2, 4 or 8 tokens (token-level units), where the bias changes
+// from key to key: the selector scores of a tile, Z^T = KS QS^T over the ks
+// rows of its 64 / blk units, come from matrix products too, and the key
+// products accumulate on top of the historical keys' bias (see tile()).  GIVEN: the bias of
 // each historical (row, block) is read from bt [b * hq][tq / 8][nb][8]
 // (-inf for a block the row does not attend) instead of being computed from
 // the selector: the same kernel then runs a sparse forward whose selection is
@@ -64,7 +68,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   constexpr int NCH = kBlock * DC / kFwdThreads;  // 16-byte chunks per thread and tensor
   constexpr int KS = HD / 16;      // k-steps over the head dim
   constexpr int DM = HD / 32;      // 32-row M-tiles of O^T
-  constexpr int BU = kBlock / UB;  // tokens per gate unit
+  constexpr int BU = UB > 0 ? kBlock / UB : 1;  // tokens per gate unit (UB > 0)
+  constexpr int XP = DS + 8;  // UB = 0: LDS pitch of the tile's ks rows (elements)
+  constexpr int SN = UB > 0 ? UB * DS : kBlock * XP;
   // Key tiles in LDS, K and V row-major (V read transposed, as the V^T
   // operand, by transposing 8-byte reads); K in two buffers, V in three
   // (the PV products of half the waves run one tile late).  The next
@@ -76,8 +82,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   __shared__ __align__(16) bf16 V0[kBlock * VP];
   __shared__ __align__(16) bf16 V1[kBlock * VP];
   __shared__ __align__(16) bf16 V2[kBlock * VP];
-  __shared__ __align__(16) bf16 S0[UB * DS];  // ks rows of the tile's units
-  __shared__ __align__(16) bf16 S1[UB * DS];
+  __shared__ __align__(16) bf16 S0[SN];  // ks rows of the tile's units
+  __shared__ __align__(16) bf16 S1[SN];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;  // (a wave-uniform copy here costs registers: keep it per lane)
@@ -89,7 +95,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   const int qi = wq0 + l32;
   const int qc = min(qi, D.tq - 1);
   const int t = D.qoff + qc;
-  const int c = t / BU;  // historical units of this row (tile bounds below are in 64-key tiles)
+  const int blk = UB > 0 ? BU : D.blk;
+  const int lb = __builtin_ctz(blk);  // blk is a power of two
+  const int c = t >> lb;  // historical units of this row (tile bounds below are in 64-key tiles)
+  const int tcur0 = c << lb;  // UB = 0: first key of the row's own unit
   const int c_lo = (D.qoff + min(wq0, D.tq - 1)) / kBlock;
   const int c_hi = (D.qoff + min(wq0 + 31, D.tq - 1)) / kBlock;
   const int c_end = (D.qoff + min(qt * kFwdRows + kFwdRows - 1, D.tq - 1)) / kBlock;
@@ -106,7 +115,16 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   for (int e = 0; e < DS / 4; ++e)
     qsv[e] = GIVEN ? bf16x2{} : *(const bf16x2*)(qs + qrow * DS + hh * (DS / 2) + 2 * e);
   const float lam_t = !GIVEN && c > 0 ? lam[qrow] : 0.f;
+  // UB = 0: the lane's k-slots of the row's qs, the B operand of Z^T
+  bf16x8 qsf[UB == 0 ? DS / 16 : 1];
+  if constexpr (UB == 0) {
+#pragma unroll
+    for (int s = 0; s < DS / 16; ++s) qsf[s] = *(const bf16x8*)(qs + qrow * DS + 16 * s + 8 * hh);
+  }
+  // (UB = 0 keeps the selector constants in score units: see tile())
+  const float zsc = D.sel_scale / D.sm_scale;
   const bf16* ksb0 = GIVEN ? ks : ks + ((size_t)b * D.hks + sh) * (size_t)D.nb * DS;
+  const int urows = kBlock >> lb;  // UB = 0: units (ks rows) per tile
   // GIVEN: this row's bias of block j is btr[8 j]
   const float* btr =
       GIVEN ? bt + ((((size_t)b * D.hq + h) * ((D.tq + 7) / 8) + qc / 8) * D.nb) * 8 + qc % 8
@@ -137,7 +155,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       kreg[x] = *(const bf16x8*)(kt + (id / DC) * HD + (id % DC) * 8);
       vreg[x] = *(const bf16x8*)(vt + (id / DC) * HD + (id % DC) * 8);
     }
-    if (!GIVEN && tid < UB * DS / 8) sreg = *(const bf16x8*)(ksb0 + (size_t)j * UB * DS + tid * 8);
+    if constexpr (UB == 0) {
+      if (tid < urows * (DS / 8)) sreg = *(const bf16x8*)(ksb0 + (size_t)j * urows * DS + tid * 8);
+    } else if (!GIVEN && tid < UB * DS / 8) {
+      sreg = *(const bf16x8*)(ksb0 + (size_t)j * UB * DS + tid * 8);
+    }
   };
   auto sstore = [&](bf16* Kd, bf16* Vd, bf16* Sd) __attribute__((always_inline)) {
 #pragma unroll
@@ -146,7 +168,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       *(bf16x8*)&Kd[(id / DC) * KP + (id % DC) * 8] = kreg[x];
       *(bf16x8*)&Vd[(id / DC) * VP + (id % DC) * 8] = vreg[x];
     }
-    if (!GIVEN && tid < UB * DS / 8) *(bf16x8*)&Sd[tid * 8] = sreg;
+    if constexpr (UB == 0) {
+      if (tid < urows * (DS / 8)) *(bf16x8*)&Sd[(tid / (DS / 8)) * XP + (tid % (DS / 8)) * 8] = sreg;
+    } else if (!GIVEN && tid < UB * DS / 8) {
+      *(bf16x8*)&Sd[tid * 8] = sreg;
+    }
   };
   // per-lane part of the transposing V^T reads: lane 4k + a of each 16-lane
   // group points at key row 4 hh + k, columns 16 ((lane >> 4) & 1) + 4 a
@@ -160,12 +186,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   auto tile = [&](int j, auto mask_tag, const bf16* Ks, const bf16* Ss)
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    float bias2[UB];  // log2-domain gate bias of this lane's row for each unit of tile j
+    // log2-domain gate bias of this lane's row for each unit of tile j (UB = 0:
+    // zero, the bias is in the score accumulator)
+    float bias2[UB > 0 ? UB : 1];
 #pragma unroll
-    for (int ub = 0; ub < UB; ++ub) bias2[ub] = 0.f;
+    for (int ub = 0; ub < (UB > 0 ? UB : 1); ++ub) bias2[ub] = 0.f;
     if constexpr (GIVEN) {
       bias2[0] = j < c ? bcur * kLog2e : 0.f;
-    } else if (UB == 1 ? j < c_hi : j <= c_hi) {
+    } else if (UB > 0 && (UB == 1 ? j < c_hi : j <= c_hi)) {
 #pragma unroll
       for (int ub = 0; ub < UB; ++ub) {
         const bf16x2* kr = (const bf16x2*)(Ss + ub * DS + hh * (DS / 2));
@@ -179,6 +207,34 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
     }
     // S^T tile: two 32-key M-tiles x 32 queries
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    if constexpr (UB == 0) {
+      // Z^T = KS QS^T: key 32 mt + l32 of the tile reads its unit's ks row.
+      // A historical key's logit is sm_scale (s + (sel_scale z - lam) /
+      // sm_scale): its accumulator starts at the second term and the key
+      // products add s; keys of the row's own unit start at 0.
+#pragma unroll
+      for (int s = 0; s < DS / 16; ++s) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 a = *(const bf16x8*)&Ss[((32 * mt + l32) >> lb) * XP + 16 * s + 8 * hh];
+          sacc[mt] = mfma32(a, qsf[s], sacc[mt]);
+        }
+      }
+      const float zoff = -lam_t / D.sm_scale;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float zb = fmaf(sacc[mt][r], zsc, zoff);
+          if constexpr (MASK) {
+            const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
+            sacc[mt][r] = u < tcur0 ? zb : 0.f;
+          } else {
+            sacc[mt][r] = zb;  // every key of a tile before the wave's first block is historical
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -208,7 +264,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if constexpr (UB == 1) mx = fmaf(mx, c1, bias2[0]);
+    if constexpr (UB <= 1) mx = fmaf(mx, c1, bias2[0]);
     // Lazy rescaling: the running max only moves when it grows by more than
     // 8 (log2 units) in some row of the wave, so P <= 2^8 between updates.
     if (__any(mx > m_run + 8.f)) {
@@ -226,7 +282,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = UB == 1 ? exp2_raw(fmaf(sacc[mt][r], c1, off))
+        const float p = UB <= 1 ? exp2_raw(fmaf(sacc[mt][r], c1, off))
                                 : exp2_raw(sacc[mt][r] - m_run);
         pb[mt][r / 8][r % 8] = (bf16)p;
         psum += p;
@@ -364,6 +420,8 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const vo
       return launch_fwd_t<HDV, DSV, 2, false>(q, k, v, qs, ks, lam, nullptr, o, lse, D, st);   \
     if (D.blk == 16)                                                                            \
       return launch_fwd_t<HDV, DSV, 4, false>(q, k, v, qs, ks, lam, nullptr, o, lse, D, st);   \
+    if (D.blk == 8 || D.blk == 4 || D.blk == 2 || D.blk == 1)                                   \
+      return launch_fwd_t<HDV, DSV, 0, false>(q, k, v, qs, ks, lam, nullptr, o, lse, D, st);   \
     return hipErrorInvalidValue;                                                                \
   }
   SAS_FWD_CASE(128, 32)

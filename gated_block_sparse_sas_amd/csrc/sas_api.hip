@@ -160,7 +160,6 @@ sas_status sas_attn_fwd(const sas_shape* shape, const void* q, const void* k, co
   if (r != SAS_OK) return r;
   if ((r = check_ptrs({q, k, v, qs, ks, gate_lse, o, lse})) != SAS_OK) return r;
   if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
-  if (shape->dtype == SAS_BF16 && D.blk < 16) return SAS_ERR_UNSUPPORTED;  // 16, 32, 64
   if (D.batch == 0) return SAS_OK;
   hipStream_t st = (hipStream_t)stream;
   if (shape->dtype == SAS_BF16)
@@ -178,8 +177,10 @@ static sas_status attn_bwd_impl(const sas_shape* shape, const void* q, const voi
   if (r != SAS_OK) return r;
   if (!ws_bytes) return SAS_ERR_NULL;
   if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
-  // bf16: units of 16, 32, 64 tokens at d = 128, 64 at d = 64
-  if (shape->dtype == SAS_BF16 && (D.d == 128 ? D.blk < 16 : D.blk != sas::kBlock))
+  // bf16: units of 16, 32, 64 tokens at d = 128 (and of 1 .. 8 tokens with
+  // ds = 32), 64 at d = 64
+  if (shape->dtype == SAS_BF16 &&
+      (D.d == 128 ? D.blk < 16 && D.ds != 32 : D.blk != sas::kBlock))
     return SAS_ERR_UNSUPPORTED;
   const sas::BwdWs W = sas::bwd_workspace(D, dz == nullptr);
   if (!ws) {

@@ -36,6 +36,8 @@ struct BwdWs {
   size_t off_dz;     // float [rows, nb]      only when the caller passes no dz
   size_t off_dks;    // float [b, hks, nb, ds] fp32 accumulator of dks
   size_t off_rows;   // d = 128: float [b, hq, nb + 1, tqp] per-row data of the dK/dV kernel
+                     // (units under 16 tokens: [b, hq, 4, tqp])
+  size_t off_ksx;    // units of 2 .. 8 tokens: bf16 [b, hks, tk, ds] per-key selector rows
   int tqp;           // tq rounded up to 32
 };
 BwdWs bwd_workspace(const Dims& D, bool need_dz);

@@ -52,10 +52,13 @@
  *  - Context units (block): 64 tokens everywhere; smaller units of 1, 2, 4,
  *    8, 16 or 32 tokens (a unit may be a single token: NeurIPS abstract,
  *    "tokens or blocks") for sas_gate_scores, the Top-K, budget and threshold
- *    selections, sas_sparse_fwd (bf16 or f32) and, in f32 (d = 64),
- *    sas_attn_fwd / sas_attn_bwd.  bf16 sas_attn_fwd takes units of 16, 32
- *    or 64 tokens, bf16 sas_attn_bwd 16, 32 or 64 at d = 128 and 64 at
- *    d = 64; the paged cache takes 64 (SAS_ERR_UNSUPPORTED otherwise).
+ *    selections, sas_sparse_fwd (bf16 or f32), sas_attn_fwd (bf16, or f32
+ *    at d = 64) and sas_attn_bwd (f32 at d = 64; bf16 at d = 128 with any
+ *    ds for units of 16, 32 or 64 tokens and ds = 32 for units of 1, 2, 4
+ *    or 8; bf16 at d = 64 with 64-token units only).  The paged cache takes
+ *    64-token units (SAS_ERR_UNSUPPORTED otherwise).  With units under 16
+ *    tokens the bf16 backward writes dz only when the caller passes it (its
+ *    dks is formed without the dense [rows, nb] matrix).
  */
 #ifndef SAS_H
 #define SAS_H
@@ -114,7 +117,8 @@ sas_status sas_attn_fwd(const sas_shape* shape, const void* q, const void* k, co
  * the gradient reaching the selector scores.  dz may be NULL (it then lives in
  * the workspace).  The workspace also holds D = <dO, O> per row, an fp32 dks
  * accumulator and, at d = 128, per-row logit offsets for every (row, gate
- * unit): batch * hq * (nb + 1) * ceil32(tq) floats.  Source: blog, "The Logit
+ * unit): batch * hq * (nb + 1) * ceil32(tq) floats (units under 16 tokens:
+ * four values per row, the per-key selector rows and no dz).  Source: blog, "The Logit
  * Injection Mechanism" (gradients reach the selector through the softmax),
  * NeurIPS abstract. */
 sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, const void* v,

@@ -83,7 +83,8 @@ def fwd(lib, sh, **ptrs):
     (dict(batch=-1), 2),
     (dict(dtype=7), 3),
     (dict(sel_dtype=ops.SAS_F32), 3),  # mixed dtypes
-    (dict(block=8), 5),                # bf16 forward: units of 16, 32, 64
+    (dict(block=128), 5),              # units of at most 64 tokens
+    (dict(block=24), 5),               # units: powers of two
     (dict(tk=250, tq=250), 5),       # tk % 64
     (dict(d=96), 5),
     (dict(ds=24), 5),
@@ -287,22 +288,24 @@ def test_threshold_and_csr_checks(lib):
 
 
 def test_block_size_support(lib):
-    # gate blocks of 1 .. 64 tokens (powers of two); bf16 training kernels: 64 only
-    for blk, ok in ((1, True), (8, True), (16, True), (32, True), (64, True), (48, False),
-                    (128, False)):
-        for dt, d in ((ops.SAS_F32, 64), (ops.SAS_BF16, 128)):
+    # gate blocks of 1 .. 64 tokens (powers of two), in the gate and the forward
+    for blk, ok in ((1, True), (2, True), (8, True), (16, True), (32, True), (64, True),
+                    (48, False), (128, False)):
+        for dt, d in ((ops.SAS_F32, 64), (ops.SAS_BF16, 128), (ops.SAS_BF16, 64)):
             sh = shape(batch=0, block=blk, dtype=dt, d=d)
             r_gate = lib.sas_gate_scores(ctypes.byref(sh), A, A, A, None, STREAM)
             r_fwd = fwd(lib, sh)
             assert r_gate == (0 if ok else 5), (blk, dt)
-            want_fwd = 0 if ok and (dt == ops.SAS_F32 or blk >= 16) else 5
-            assert r_fwd == want_fwd, (blk, dt, r_fwd)
-    # bf16 backward: units of 16, 32, 64 tokens at d = 128, 64 tokens at d = 64
+            assert r_fwd == (0 if ok else 5), (blk, dt, r_fwd)
+    # bf16 backward: units of 16, 32, 64 tokens at d = 128 (and 1 .. 8 with
+    # ds = 32), 64 tokens at d = 64
     n = ctypes.c_size_t(1 << 30)
-    for blk, d, want in ((32, 128, 0), (16, 128, 0), (8, 128, 5), (32, 64, 5), (64, 64, 0)):
-        bw = shape(batch=0, block=blk, d=d)
+    for blk, d, ds, want in ((32, 128, 32, 0), (16, 128, 32, 0), (8, 128, 32, 0),
+                             (1, 128, 32, 0), (4, 128, 16, 5), (2, 128, 64, 5), (32, 64, 32, 5),
+                             (64, 64, 32, 0)):
+        bw = shape(batch=0, block=blk, d=d, ds=ds)
         assert lib.sas_attn_bwd(ctypes.byref(bw), *([A] * 15), A, ctypes.byref(n),
-                                STREAM) == want, (blk, d)
+                                STREAM) == want, (blk, d, ds)
     # CSR and fixed-budget sparse forwards: any supported unit size
     n = ctypes.c_size_t(0)
     sh = shape(block=16)

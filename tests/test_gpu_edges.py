@@ -15,9 +15,12 @@
   is off by |dD_t| <= |dO_t| |o_t - O_t| (O the exact output), and dq_t,
   dz_t and dqs_t move with D_t at most by tau max|k|, 2 and 2 sigma max|ks|
   times that (dS = P (dP - D); dz_j = dbeta_j - g_j sum dbeta with the sum
-  taken from the current block, whose weights sum to at most 2).  Rows whose
+  taken from the current block, whose weights sum to at most 2); dks of unit
+  j moves by at most sel_scale sum_t (P_{t,j} + g_{t,j} P_{t,cur}) |dD_t|
+  |qs_t| (P_{t,j} the attention weight of the unit's keys).  Rows whose
   exact gradient is near zero (a row's first key, near one-hot attention or
-  gates) are the ones this covers.
+  gates, a token unit near the end whose dks sums a few rows) are the ones
+  this covers.
 * Inputs that stress the softmax: explicit non-default scales, near one-hot
   gates (qs, ks x 4), large logits (q, k x 4: logit std 4), and the
   shift invariance of the gate through an augmented selector
@@ -36,67 +39,12 @@ import torch
 
 from gated_block_sparse_sas_amd import ops, synth
 import oracle
-from gpu_common import DEV, host, inputs, max_abs, oshape, rel_l2, say, tie_free_rows
+from gpu_common import (DEV, GRADS, check_train, gpu_train, host, inputs, max_abs, oshape,
+                        rel_l2, row_bound, say, tie_free_rows)
 
 pytestmark = pytest.mark.gpu
 
 W = synth.WORKLOADS
-GRADS = ("dq", "dk", "dv", "dz", "dqs", "dks")
-
-
-def row_bound(name, got, ref, rel=0.1, floor=0.05, extra=None):
-    """Every row of got within rel * max(|ref row|, floor * median |ref row|),
-    plus extra[row] (an absolute allowance per row) when given."""
-    g = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
-    r = np.asarray(ref, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
-    nr = np.linalg.norm(r, axis=1)
-    err = np.linalg.norm(g - r, axis=1)
-    pos = nr[nr > 0]
-    fl = floor * (np.median(pos) if pos.size else 1.0)
-    lim = rel * np.maximum(nr, fl) + 1e-30
-    if extra is not None:
-        lim = lim + np.asarray(extra, dtype=np.float64).reshape(-1)
-    worst = float(np.max(err / lim)) if err.size else 0.0
-    say("  %s worst row error / bound %.3f" % (name, worst))
-    assert worst <= 1.0, name
-
-
-def gpu_train(dev, w, sm_scale=None, sel_scale=None):
-    lam = ops.gate_scores(dev["qs"], dev["ks"], w.tk, block=w.block, sel_scale=sel_scale)
-    o, lse = ops.attn_fwd(dev["q"], dev["k"], dev["v"], dev["qs"], dev["ks"], lam, block=w.block,
-                          sm_scale=sm_scale, sel_scale=sel_scale)
-    g = ops.attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, dev["qs"], dev["ks"], lam,
-                     block=w.block, sm_scale=sm_scale, sel_scale=sel_scale)
-    torch.cuda.synchronize()
-    return lam, o, lse, g
-
-
-def check_train(w, f, lam, o, lse, g, S):
-    _, lam_ref, _ = oracle.gate_scores(S, f["qs"], f["ks"])
-    fin = np.isfinite(lam_ref)
-    assert np.array_equal(np.isneginf(host(lam)), np.isneginf(lam_ref))
-    e = max_abs(host(lam)[fin], lam_ref[fin])
-    say("  lam max-abs %.2e" % e)
-    assert e <= 1e-4 * max(1.0, float(np.max(np.abs(lam_ref[fin]))))
-    o_ref, l_ref = oracle.attn_fwd(S, f["q"], f["k"], f["v"], f["qs"], f["ks"])
-    eo, el = max_abs(host(o), o_ref), max_abs(host(lse), l_ref)
-    say("  O max-abs %.2e  lse max-abs %.2e" % (eo, el))
-    assert eo <= 2e-2 and el <= 1e-3
-    ref = oracle.attn_bwd(S, f["q"], f["k"], f["v"], f["dout"], f["qs"], f["ks"])
-    # error of D_t = <dO_t, o_t> inherited from the forward output (Cauchy-Schwarz)
-    dD = (np.linalg.norm(f["dout"], axis=-1)
-          * np.linalg.norm(host(o) - o_ref, axis=-1)).reshape(-1)
-    tau = S.sm_scale or 1.0 / np.sqrt(w.d)
-    sig = S.sel_scale or 1.0 / np.sqrt(w.ds)
-    kmax = float(np.max(np.linalg.norm(f["k"], axis=-1)))
-    ksmax = float(np.max(np.linalg.norm(f["ks"], axis=-1)))
-    extra = {"dq": 2 * tau * kmax * dD, "dz": 4 * dD, "dqs": 4 * sig * ksmax * dD}
-    for n in GRADS:
-        e = rel_l2(host(g[n]), ref[n])
-        say("  %s rel-L2 %.3e" % (n, e))
-        assert e <= 5e-2, n
-        row_bound(n, host(g[n]), ref[n], extra=extra.get(n))
-    return ref
 
 
 # ---------------------------------------------------------------- mid size
