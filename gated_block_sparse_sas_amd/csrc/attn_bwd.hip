@@ -697,14 +697,15 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
   // UB = 0, dz requested: dz[row, unit] = sum of e over the unit's keys.  A
   // lane holds runs of 4 consecutive keys (32 mt + 8 q + 4 hh + 0..3); units
   // of 8 keys join the runs of the two lane halves.
-  auto write_dz_units = [&](const float (&e)[UB == 0 ? 2 : 1][16], int j, size_t rw_, bool ok) {
+  auto write_dz_units = [&](const f32x16 (&e)[2], int j, size_t rw_, bool ok) {
     const int bsz = 1 << lb;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int k0 = j * kBlock + 32 * mt + 8 * q4 + 4 * hh;  // first key of the run
-        const float* er = &e[mt][4 * q4];
+        const float er[4] = {e[mt][4 * q4], e[mt][4 * q4 + 1], e[mt][4 * q4 + 2],
+                             e[mt][4 * q4 + 3]};
         float* zr = dz + rw_ * D.nb;
         if (bsz == 8) {
           float v = er[0] + er[1] + er[2] + er[3];
@@ -730,27 +731,18 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
     float bias2[NU];
 #pragma unroll
     for (int ub = 0; ub < NU; ++ub) bias2[ub] = 0.f;
-    // UB = 0: log2-domain gate bias of each (key, row) of the tile, zero on
-    // the row's own unit and past it
-    float zb[UB == 0 ? 2 : 1][16];
-    if constexpr (UB == 0) {
-      f32x16 zacc[2] = {f32x16{}, f32x16{}};
+    // UB = 0: Z^T = KS QS^T of the tile (selector scores of each (key, row))
+    auto zt = [&](f32x16 (&za)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int s = 0; s < DS / 16; ++s) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           const bf16x8 a = *(const bf16x8*)&Ss[(32 * mt + l32) * XP + 16 * s + 8 * hh];
-          zacc[mt] = mfma32(a, qsf[s], zacc[mt]);
+          za[mt] = mfma32(a, qsf[s], za[mt]);
         }
       }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
-          zb[mt][r] = u < tcur0 ? fmaf(zacc[mt][r], zs2, -lam2) : 0.f;
-        }
-      }
+    };
+    if constexpr (UB == 0) {
     } else if (UB == 1 ? j < c_hi : j <= c_hi) {
 #pragma unroll
       for (int ub = 0; ub < UB; ++ub) {
@@ -772,6 +764,22 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
     }
     // S^T and dP^T: two 32-key M-tiles x 32 queries each
     f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+    if constexpr (UB == 0) {
+      // a historical key's logit is sm_scale (s + (sel_scale z - lam) / sm_scale):
+      // its S accumulator starts at the second term (keys of the row's own
+      // unit and later ones at 0), so that no bias array stays live through
+      // the products
+      zt(sacc);
+      const float zsc = D.sel_scale / D.sm_scale, zoff = -lam_t / D.sm_scale;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
+          sacc[mt][r] = u < tcur0 ? fmaf(sacc[mt][r], zsc, zoff) : 0.f;
+        }
+      }
+    }
     // operand i (step i / 4, M-tile (i / 2) % 2, K or V by i % 2) is read
     // while product i - 1 runs; the step's Q operand after its last use
     auto opnd = [&](int i) __attribute__((always_inline)) {
@@ -795,7 +803,7 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        pv[mt][r] = exp2_raw(fmaf(sacc[mt][r], c1, (UB == 0 ? zb[mt][r] : bias2[unit(mt, r)]) - l2));
+        pv[mt][r] = exp2_raw(fmaf(sacc[mt][r], c1, (UB == 0 ? 0.f : bias2[unit(mt, r)]) - l2));
     if (j >= c_lo) {  // tile meets some row's own tile: cut keys after the row (or the tile)
       const int mlim = j < ct ? kBlock : (j > ct ? -1 : t - j * kBlock - 4 * hh);
 #pragma unroll
@@ -838,13 +846,18 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
     if constexpr (UB == 0) {
       // e = dS - g sdb / blk on historical keys (0 elsewhere): summed over a
       // unit's keys it is dz; dqs^T += KS^T e^T over the tile's keys
+      // (Z^T again, now that dP's registers are free: the gate g = 2^(z log2 e
+      // sel_scale - lam log2 e))
       const float sb_k = sdb * inv_blk;
+      f32x16 zb[2] = {f32x16{}, f32x16{}};
+      zt(zb);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
-          zb[mt][r] = u < tcur0 ? sacc[mt][r] - exp2_raw(zb[mt][r]) * sb_k : 0.f;
+          zb[mt][r] =
+              u < tcur0 ? sacc[mt][r] - exp2_raw(fmaf(zb[mt][r], zs2, -lam2)) * sb_k : 0.f;
         }
       }
       if (dz != nullptr) write_dz_units(zb, j, row, valid);
