@@ -15,6 +15,8 @@ One step is one pass of the whole hot path on resident synthetic inputs:
   prefill_32k_b16_top64 16-token context units: top-K (K = 64) -> sparse prefill
   prefill_32k_theta  dynamic-threshold selection (normalised gate >= 0.01, CSR:
                      count, host read of nnz, fill) -> sparse forward over CSR
+  train_32k_b1       train_32k with token-level context units (one selector
+                     key per token): gate -> forward -> backward (no dense dz)
 The headline value is the training fwd+bwd rate at 32k in TFLOP/s counting
 attended (row, key) pairs only (forward 4*d flop per pair, backward 10*d).
 Times come from HIP events recorded on the stream the kernels run on.
@@ -213,6 +215,10 @@ def main():
     pv = {n: t.to(dev) for n, t in synth.draw_all(wv, ("q", "k", "v", "qs", "ks")).items()}
     wh = W["prefill_32k_theta"]
     ph = {n: t.to(dev) for n, t in synth.draw_all(wh, ("q", "k", "v", "qs", "ks")).items()}
+    # training with token-level context units: the train_32k tensors with one
+    # selector key per token
+    w1 = wt.with_(name="train_32k_b1", block=1)
+    ks1 = synth.draw_all(w1, ("ks",))["ks"].to(dev)
     torch.cuda.synchronize()
     log("inputs resident in HBM (%.1f s)" % (time.time() - t0))
 
@@ -237,12 +243,14 @@ def main():
     ws_u = torch.empty(ops.sparse_workspace_bytes(sh_u, wu.topk), dtype=torch.uint8, device=dev)
     sh_v = ops.make_shape(wv.batch, wv.hq, wv.hkv, wv.tq, wv.tk, wv.d, wv.ds, wv.block, wv.hkv)
     ws_v = torch.empty(ops.sparse_workspace_bytes(sh_v, wv.topk), dtype=torch.uint8, device=dev)
+    sh_1 = ops.shape_of(tr["q"], tr["k"], tr["qs"], ks1, block=1)
+    ws_1 = torch.empty(ops.bwd_workspace_bytes(sh_1, False), dtype=torch.uint8, device=dev)
 
     names = ["start", "gate", "fwd", "bwd_dq", "bwd_dkdv", "bwd_dks", "bwd", "pf_topk",
              "pf_partial", "pf_sparse", "dc_topk", "dc_partial", "dc_sparse", "pq_topk",
              "pq_partial", "pq_sparse", "pg_topk", "pg_decode", "th_start", "th_count",
              "th_fill0", "th_fill", "th_partial", "th_sparse", "u_topk", "u_sparse",
-             "v_topk", "v_sparse"]
+             "v_topk", "v_sparse", "t1_gate", "t1_fwd", "t1_bwd"]
 
     def step(ev):
         E = {n: ev[n] for n in names}
@@ -293,6 +301,13 @@ def main():
         E["v_topk"].record()
         ops.sparse_fwd(pv["q"], pv["k"], pv["v"], idx, bias, block=wv.block, ws=ws_v)
         E["v_sparse"].record()
+        lam = ops.gate_scores(tr["qs"], ks1, wt.tk, block=1)
+        E["t1_gate"].record()
+        o, lse = ops.attn_fwd(tr["q"], tr["k"], tr["v"], tr["qs"], ks1, lam, block=1)
+        E["t1_fwd"].record()
+        ops.attn_bwd(tr["q"], tr["k"], tr["v"], o, tr["dout"], lse, tr["qs"], ks1, lam, block=1,
+                     with_dz=False, ws=ws_1)
+        E["t1_bwd"].record()
 
     def new_events():
         return {n: torch.cuda.Event(enable_timing=True) for n in names}
@@ -335,8 +350,11 @@ def main():
         "units_decode": dur("u_topk", "u_sparse"),
         "units_prefill_topk": dur("u_sparse", "v_topk"),
         "units_prefill": dur("v_topk", "v_sparse"),
+        "units1_gate": dur("v_sparse", "t1_gate"),
+        "units1_fwd": dur("t1_gate", "t1_fwd"),
+        "units1_bwd": dur("t1_fwd", "t1_bwd"),
     }
-    step_ms = dur("start", "v_sparse")
+    step_ms = dur("start", "t1_bwd")
 
     pairs_t = wt.batch * wt.hq * causal_pairs(wt.tq, wt.tk)
     fl_fwd = 4.0 * wt.d * pairs_t
@@ -364,6 +382,8 @@ def main():
     h_tflops = 4.0 * wh.d * pairs_h / (part["theta_sparse"] * 1e-3) / 1e12
     u_bytes = wu.batch * wu.hq * (min(wu.topk, (wu.tk - 1) // wu.block) + 1) * 2 * wu.block * wu.d * 2
     u_gbps = u_bytes / (part["units_decode"] * 1e-3) / 1e9
+    t_units1 = part["units1_gate"] + part["units1_fwd"] + part["units1_bwd"]
+    units1_tflops = (fl_fwd + fl_bwd) / (t_units1 * 1e-3) / 1e12
     pairs_v = wv.batch * wv.hq * sparse_pairs(wv)
     v_tflops = 4.0 * wv.d * pairs_v / (part["units_prefill"] * 1e-3) / 1e12
 
@@ -408,7 +428,7 @@ def main():
                    "also_in_step": ["prefill_32k_top16", "decode_64k_top8",
                                     "prefill_32k_top25pct", "decode_paged_mix",
                                     "prefill_32k_theta", "decode_64k_b16_top32",
-                                    "prefill_32k_b16_top64"]},
+                                    "prefill_32k_b16_top64", "train_32k_b1"]},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "train_ms": round(t_train, 3),
         "parts_ms": {k: round(v, 4) for k, v in part.items()},
@@ -447,6 +467,13 @@ def main():
                             "ms": round(part["units_prefill"], 3),
                             "topk_ms": round(part["units_prefill_topk"], 3),
                             "tflops": round(v_tflops, 2), "attended_pairs": pairs_v},
+        "train_units1": {"workload": "train_32k_b1", "block": 1, "ms": round(t_units1, 3),
+                         "gate_ms": round(part["units1_gate"], 3),
+                         "fwd_ms": round(part["units1_fwd"], 3),
+                         "bwd_ms": round(part["units1_bwd"], 3),
+                         "tflops": round(units1_tflops, 2),
+                         "flop_count": "14*d per attended pair, as train_32k (selector "
+                                       "products not counted)"},
         "roofline": roofline,
         "wall_s_timed": round(wall, 3),
     }
