@@ -401,12 +401,18 @@ def threshold_fill(qs, ks, theta, tk, row_ptr, nnz, block=64, renorm=0, sel_scal
     return col[:nnz], bias[:nnz]
 
 
-def threshold_blocks(qs, ks, theta, tk, block=64, renorm=0, sel_scale=None):
+def threshold_blocks(qs, ks, theta, tk, block=64, renorm=0, sel_scale=None, capacity=None):
     """Blocks whose normalised gate is >= theta.  Returns (row_ptr int64 [rows+1],
-    col int32 [nnz], bias float32 [nnz]); rows = batch*hq*tq in BHSD order.  Reads
-    nnz back to the host between the two passes (one stream synchronisation)."""
+    col int32 [n], bias float32 [n]); rows = batch*hq*tq in BHSD order.
+
+    capacity None: reads nnz = row_ptr[-1] back to the host between the two
+    passes (one stream synchronisation) and n = nnz.  capacity = n: nothing is
+    read back; the fill writes the entries below n and the arrays have n
+    entries, those past row_ptr[-1] belonging to no row (sparse_fwd_csr skips
+    them).  The selection is complete iff row_ptr[-1] <= n, which the caller
+    checks whenever it next synchronises."""
     row_ptr = threshold_count(qs, ks, theta, tk, block, sel_scale)
-    nnz = int(row_ptr[-1].item())
+    nnz = int(row_ptr[-1].item()) if capacity is None else int(capacity)
     col, bias = threshold_fill(qs, ks, theta, tk, row_ptr, nnz, block, renorm, sel_scale)
     return row_ptr, col, bias
 

@@ -228,8 +228,15 @@ sas_status sas_threshold_count(const sas_shape* shape, float theta, const void* 
 
 /* Pass 2: the kept blocks and their bias.  row_ptr from pass 1 with the same
  * shape, theta, qs and ks (the same kernel evaluates the predicate, so the
- * counts match); nnz = row_ptr[rows] is the capacity of col / bias (entries
- * are never written past it).  nnz == 0 writes nothing. */
+ * counts match); nnz is the capacity of col / bias: entries at positions
+ * >= nnz are never written, and nnz == 0 writes nothing.  With
+ * nnz = row_ptr[rows] (read back after pass 1) the selection is written
+ * whole.  A caller that cannot read it back in between passes an upper
+ * bound instead and enqueues pass 1, pass 2 and sas_sparse_fwd_csr with the
+ * same nnz one after the other: positions from row_ptr[rows] to nnz - 1
+ * belong to no row and are skipped by the forward, and the result is exact
+ * iff row_ptr[rows] <= nnz, which the caller checks after its next
+ * synchronisation (rows past the capacity lose their last blocks). */
 sas_status sas_threshold_fill(const sas_shape* shape, float theta, int32_t renorm, const void* qs,
                               const void* ks, const int64_t* row_ptr, int64_t nnz, int32_t* col,
                               float* bias, void* stream);

@@ -211,3 +211,44 @@ def test_threshold_full_size():
     assert n_clear >= 0.9 * len(rows)
     say("  O max-abs", e_o, "over", n_clear, "rows")
     assert e_o <= 2e-2
+
+
+def test_threshold_bounded_capacity():
+    # count -> fill -> CSR forward enqueued with a capacity instead of the
+    # count read back: with room to spare the same selection and output; with
+    # too little room nothing is written past the capacity and the forward
+    # sees each row's kept blocks below it
+    w = SMALL["prefill_1088"]
+    cpu, dev, f = inputs(w, ("q", "k", "v", "qs", "ks"))
+    rp, col, bias = ops.threshold_blocks(dev["qs"], dev["ks"], 0.01, w.tk)
+    o, lse = ops.sparse_fwd_csr(dev["q"], dev["k"], dev["v"], rp, col, bias)
+    nnz = int(rp[-1].item())
+    say("bounded capacity, nnz", nnz)
+    cap = nnz + 777
+    rp2, col2, bias2 = ops.threshold_blocks(dev["qs"], dev["ks"], 0.01, w.tk, capacity=cap)
+    assert col2.numel() == cap
+    o2, lse2 = ops.sparse_fwd_csr(dev["q"], dev["k"], dev["v"], rp2, col2, bias2)
+    torch.cuda.synchronize()
+    assert torch.equal(rp, rp2)
+    assert torch.equal(col, col2[:nnz]) and torch.equal(bias, bias2[:nnz])
+    assert max_abs(host(o2), host(o)) <= 2e-2 and max_abs(host(lse2), host(lse)) <= 1e-3
+    say("  bit-equal output:", torch.equal(o, o2) and torch.equal(lse, lse2))
+    # truncation: a sentinel-filled buffer longer than the capacity
+    cap = nnz // 2
+    sh = ops._thr_shape(dev["qs"], dev["ks"], w.tk, 64, None)
+    colx = torch.full((cap + 256,), -7, dtype=torch.int32, device=DEV)
+    biasx = torch.full((cap + 256,), 7.0, dtype=torch.float32, device=DEV)
+    ops._check("sas_threshold_fill", ops.load().sas_threshold_fill(
+        ops.ctypes.byref(sh), ops.ctypes.c_float(0.01), 0, ops._p(dev["qs"]), ops._p(dev["ks"]),
+        ops._p(rp), ops.ctypes.c_int64(cap), ops._p(colx), ops._p(biasx), ops._stream(dev["qs"])))
+    torch.cuda.synchronize()
+    assert torch.equal(colx[:cap], col[:cap]) and torch.equal(biasx[:cap], bias[:cap])
+    assert bool((colx[cap:] == -7).all()) and bool((biasx[cap:] == 7.0).all())
+    # the forward over the truncated selection == the forward over the same
+    # segments cut at the capacity
+    o3, l3 = ops.sparse_fwd_csr(dev["q"], dev["k"], dev["v"], rp, colx[:cap], biasx[:cap])
+    rpc = torch.clamp(rp, max=cap)
+    o4, l4 = ops.sparse_fwd_csr(dev["q"], dev["k"], dev["v"], rpc, col[:cap].contiguous(),
+                                bias[:cap].contiguous())
+    torch.cuda.synchronize()
+    assert max_abs(host(o3), host(o4)) <= 2e-2 and max_abs(host(l3), host(l4)) <= 1e-3
