@@ -11,6 +11,7 @@ One step is one pass of the whole hot path on resident synthetic inputs:
                      history, at most 128 blocks) -> top-K sparse forward
   decode_paged_mix   decode over a block-paged cache: 32 sequences of mixed
                      lengths (64 .. 65536 tokens), top-K selection -> decode
+  (both decodes also once more as one fused selection + decode launch)
   decode_64k_b16_top32  16-token context units: top-K (K = 32) -> sparse decode
   prefill_32k_b16_top64 16-token context units: top-K (K = 64) -> sparse prefill
   prefill_32k_theta  dynamic-threshold selection (normalised gate >= 0.01, CSR:
@@ -252,7 +253,8 @@ def main():
 
     names = ["start", "gate", "fwd", "bwd_dq", "bwd_dkdv", "bwd_dks", "bwd", "pf_topk",
              "pf_partial", "pf_sparse", "dc_topk", "dc_partial", "dc_sparse", "pq_topk",
-             "pq_partial", "pq_sparse", "pg_topk", "pg_decode", "th_start", "th_count",
+             "pq_partial", "pq_sparse", "pg_topk", "pg_decode", "dc_fused", "pg_fused",
+             "th_start", "th_count",
              "th_fill0", "th_fill", "th_partial", "th_sparse", "u_topk", "u_sparse",
              "v_topk", "v_sparse", "t1_gate", "t1_fwd", "t1_bwd"]
 
@@ -286,6 +288,12 @@ def main():
         ops.paged_decode(pg["q"], pg["k_pool"], pg["v_pool"], pg["block_table"], pg["seq_len"],
                          idx, bias, ws=ws_g)
         E["pg_decode"].record()
+        # the same two decodes with selection and attention in one launch
+        ops.topk_decode(dc["q"], dc["k"], dc["v"], dc["qs"], dc["ks"], wd.topk)
+        E["dc_fused"].record()
+        ops.paged_topk_decode(pg["q"], pg["k_pool"], pg["v_pool"], pg["qs"], pg["ks_pool"],
+                              pg["block_table"], pg["seq_len"], wg.topk)
+        E["pg_fused"].record()
         E["th_start"].record()
         row_ptr = ops.threshold_count(ph["qs"], ph["ks"], wh.theta, wh.tk, ws=ws_h)
         E["th_count"].record()
@@ -345,6 +353,8 @@ def main():
         "quarter_sparse": dur("pq_topk", "pq_sparse"),
         "paged_topk": dur("pq_sparse", "pg_topk"),
         "paged_decode": dur("pg_topk", "pg_decode"),
+        "decode_fused": dur("pg_decode", "dc_fused"),
+        "paged_fused": dur("dc_fused", "pg_fused"),
         "theta_count": dur("th_start", "th_count"),
         "theta_fill": dur("th_fill0", "th_fill"),
         "theta_partial": dur("th_fill", "th_partial"),
@@ -449,13 +459,16 @@ def main():
         "decode": {"workload": "decode_64k_top8", "ms": round(part["decode_sparse"], 4),
                    "topk_ms": round(part["decode_topk"], 4), "kv_bytes": dec_bytes,
                    "GBps": round(dec_gbps, 1),
-                   "frac_hbm": round(dec_gbps / PEAK_HBM_GBPS, 4)},
+                   "frac_hbm": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                   "fused_ms": round(part["decode_fused"], 4),
+                   "fused_note": "selection + decode in one launch (sas_topk_decode)"},
         "paged_decode": {"workload": "decode_paged_mix", "sequences": wg.batch,
                          "len_min": min(lens_g), "len_max": max(lens_g),
                          "tokens": sum(lens_g), "ms": round(part["paged_decode"], 4),
                          "topk_ms": round(part["paged_topk"], 4), "kv_bytes": pg_bytes,
                          "GBps": round(pg_gbps, 1),
-                         "frac_hbm": round(pg_gbps / PEAK_HBM_GBPS, 4)},
+                         "frac_hbm": round(pg_gbps / PEAK_HBM_GBPS, 4),
+                         "fused_ms": round(part["paged_fused"], 4)},
         "sparse_prefill_theta": {"workload": "prefill_32k_theta", "theta": wh.theta,
                                  "nnz": nnz_h, "capacity": cap_h, "host_read": False,
                                  "blocks_per_row": round(nnz_h / rows_h, 2),

@@ -463,7 +463,7 @@ sas_status sas_paged_topk(const sas_paged_shape* shape, int32_t topk, int32_t re
   if (r != SAS_OK) return r;
   if (topk < 1 || (renorm != 0 && renorm != 1)) return SAS_ERR_SHAPE;
   if ((r = check_ptrs({seq_len, block_table, qs, ks_pool, idx, bias})) != SAS_OK) return r;
-  if ((size_t)(D.nb + topk) * sizeof(float) > 65536) return SAS_ERR_UNSUPPORTED;
+  if (topk > 16 && (size_t)(D.nb + topk) * sizeof(float) > 65536) return SAS_ERR_UNSUPPORTED;
   if ((int64_t)D.batch * D.hq * topk >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
   if (D.batch == 0) return SAS_OK;
   return hip_status(sas::launch_paged_topk(qs, ks_pool, block_table, seq_len, shape->pages, topk,
@@ -494,6 +494,44 @@ sas_status sas_paged_decode(const sas_paged_shape* shape, int32_t topk, const in
   return hip_status(sas::launch_paged_decode(q, k_pool, v_pool, block_table, seq_len,
                                              shape->pages, idx, bias, o, lse, (char*)ws, topk, D,
                                              shape->dtype == SAS_BF16, (hipStream_t)stream));
+}
+
+sas_status sas_topk_decode(const sas_shape* shape, int32_t topk, int32_t renorm, const void* q,
+                           const void* k, const void* v, const void* qs, const void* ks,
+                           int32_t* idx, float* bias, void* o, float* lse, void* stream) {
+  sas::Dims D;
+  sas_status r = resolve(shape, &D);
+  if (r != SAS_OK) return r;
+  if (topk < 1 || (renorm != 0 && renorm != 1)) return SAS_ERR_SHAPE;
+  if ((r = check_ptrs({q, k, v, qs, ks, o})) != SAS_OK) return r;
+  if ((r = check_opt({idx, bias, lse})) != SAS_OK) return r;
+  if (topk > 16) return SAS_ERR_UNSUPPORTED;
+  if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
+  if ((int64_t)D.batch * D.hq * D.tq * (topk + 1) >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
+  if (D.batch == 0) return SAS_OK;
+  return hip_status(sas::launch_topk_decode(q, k, v, qs, ks, topk, renorm, idx, bias, o, lse, D,
+                                            shape->dtype == SAS_BF16, (hipStream_t)stream));
+}
+
+sas_status sas_paged_topk_decode(const sas_paged_shape* shape, int32_t topk, int32_t renorm,
+                                 const int32_t* seq_len, const int32_t* block_table,
+                                 const void* q, const void* k_pool, const void* v_pool,
+                                 const void* qs, const void* ks_pool, int32_t* idx, float* bias,
+                                 void* o, float* lse, void* stream) {
+  sas::Dims D;
+  sas_status r = resolve_paged(shape, &D);
+  if (r != SAS_OK) return r;
+  if (topk < 1 || (renorm != 0 && renorm != 1)) return SAS_ERR_SHAPE;
+  if ((r = check_ptrs({seq_len, block_table, q, k_pool, v_pool, qs, ks_pool, o})) != SAS_OK)
+    return r;
+  if ((r = check_opt({idx, bias, lse})) != SAS_OK) return r;
+  if (topk > 16) return SAS_ERR_UNSUPPORTED;
+  if (shape->dtype == SAS_F32 && D.d != 64) return SAS_ERR_UNSUPPORTED;
+  if ((int64_t)D.batch * D.hq * (topk + 1) >= (int64_t)1 << 31) return SAS_ERR_UNSUPPORTED;
+  if (D.batch == 0) return SAS_OK;
+  return hip_status(sas::launch_paged_topk_decode(
+      q, k_pool, v_pool, qs, ks_pool, block_table, seq_len, shape->pages, topk, renorm, idx, bias,
+      o, lse, D, shape->dtype == SAS_BF16, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -68,6 +68,16 @@ hipError_t launch_sparse(const void* q, const void* k, const void* v, const int*
                          int K, const Dims& D, bool bf16_io, const StageEvents& E,
                          hipStream_t st);
 
+// Selection and decode in one launch (K <= 16).
+hipError_t launch_topk_decode(const void* q, const void* k, const void* v, const void* qs,
+                              const void* ks, int K, int renorm, int* idx, float* bias, void* o,
+                              float* lse, const Dims& D, bool bf16_io, hipStream_t st);
+hipError_t launch_paged_topk_decode(const void* q, const void* k_pool, const void* v_pool,
+                                    const void* qs, const void* ks_pool, const int* table,
+                                    const int* lens, int pages, int K, int renorm, int* idx,
+                                    float* bias, void* o, float* lse, const Dims& D,
+                                    bool bf16_io, hipStream_t st);
+
 // Dynamic-threshold selection (CSR) and the sparse forward over a CSR selection.
 size_t threshold_workspace(const Dims& D);
 hipError_t launch_threshold(const void* qs, const void* ks, float theta, int renorm, int fill,

@@ -1,0 +1,203 @@
+// select_device.h -- row-selection helpers shared by the top-K kernels and
+// the fused decode kernel: where a row's selector keys live, the 64-bit
+// selection keys, and the best-K of one row by one wavefront.
+#pragma once
+#include "sas_device.h"
+
+namespace sas {
+
+// Where a row's selector keys live.  DenseSel: contiguous [B, Hks, NB, ds]
+// rows, row t has c(t) = t / 64 historical blocks.  PagedSel: one ks row per
+// page in a pool [pages, Hks, ds], a sequence's block j on page
+// table[b, j]; the decode row of sequence b sits at t = len[b] - 1.  A row
+// with a length out of range has no history; a block whose page id is out of
+// range is never read and scores -inf.
+template <typename ST>
+struct DenseSel {
+  const ST* ks;
+  __device__ int hist(const Dims& D, size_t row) const {
+    return (D.qoff + (int)(row % D.tq)) / D.blk;
+  }
+  __device__ const ST* ks_row(const Dims& D, int b, int h, int j) const {
+    return ks + (((size_t)b * D.hks + h / D.hps) * (size_t)D.nb + j) * D.ds;
+  }
+};
+
+template <typename ST>
+struct PagedSel {
+  const ST* ks;
+  const int* table;
+  const int* lens;
+  int pages;
+  __device__ int hist(const Dims& D, size_t row) const {
+    const int len = lens[row / D.hq];
+    return (len >= 1 && len <= D.nb * kBlock) ? (len - 1) / kBlock : 0;
+  }
+  __device__ const ST* ks_row(const Dims& D, int b, int h, int j) const {
+    const int pg = table[(size_t)b * D.nb + j];
+    if (pg < 0 || pg >= pages) return nullptr;
+    return ks + ((size_t)pg * D.hks + h / D.hps) * D.ds;
+  }
+};
+
+// Order-preserving 32-bit key of a score (larger z, larger key; -0 counts as
+// +0, as in a floating-point comparison), and the selection order on (key,
+// block): key descending, then block ascending.
+__device__ __forceinline__ unsigned ord_key(float z) {
+  unsigned u = __float_as_uint(z);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ bool key_before(unsigned ka, int ja, unsigned kb, int jb) {
+  return ka > kb || (ka == kb && ja < jb);
+}
+
+// Compare-exchange of two selection keys into descending order.
+__device__ __forceinline__ void ce_desc(unsigned long long& a, unsigned long long& b) {
+  const bool sw = b > a;
+  const unsigned long long hi = sw ? b : a, lo = sw ? a : b;
+  a = hi;
+  b = lo;
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o) {
+  const unsigned lo = __shfl_xor((unsigned)v, o), hi = __shfl_xor((unsigned)(v >> 32), o);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// The best KM blocks of one query row by one wavefront (few rows: decode,
+// paged decode, small calls) among blocks first, first + stride, ... below
+// c(t) (a wave alone: first = lane, stride = 64; W waves of a row: first =
+// 64 w + lane, stride = 64 W): each lane folds its candidates in batches of
+// 8 into a sorted list of its best KM keys (ord_key of z above, the
+// complemented block below: one unsigned comparison gives z descending,
+// block ascending; the batch sorted by a 19-comparator network, each of the
+// list's last 8 entries keeps the larger of itself and its mirror in the
+// batch, a bitonic merge sorts again), and six butterfly steps (lane l with
+// l ^ 1, ^ 2, ..., ^ 32) leave every lane with the wave's best KM.  The
+// log-sum-exp of the scores is kept per lane (log2 domain: *m, *s).  Scores
+// use SelQ, as every selection kernel does.
+template <int KM>
+__device__ __forceinline__ void merge_desc(unsigned long long (&tk)[KM],
+                                           const unsigned long long (&other)[KM]) {
+  // the best KM of two descending lists: the larger of each entry and its
+  // mirror (a bitonic sequence), sorted again
+#pragma unroll
+  for (int r = 0; r < KM; ++r) tk[r] = other[KM - 1 - r] > tk[r] ? other[KM - 1 - r] : tk[r];
+#pragma unroll
+  for (int st = KM / 2; st >= 1; st >>= 1)
+#pragma unroll
+    for (int r = 0; r < KM; ++r)
+      if ((r & st) == 0) ce_desc(tk[r], tk[r + st]);
+}
+
+template <int DS, typename ST, typename Sel, int KM>
+__device__ __forceinline__ void wave_best(const ST* __restrict__ qs, const Sel& S, const Dims& D,
+                                          size_t row, int c, int first, int stride,
+                                          unsigned long long (&tk)[KM], float* m_out,
+                                          float* s_out) {
+  const int h = (int)((row / D.tq) % D.hq);
+  const int b = (int)(row / ((size_t)D.tq * D.hq));
+  SelQ<DS, ST> qsv;
+  qsv.load(qs + row * DS);
+#pragma unroll
+  for (int r = 0; r < KM; ++r) tk[r] = 0ull;  // 0 = empty
+  float m = -INFINITY, s = 0.f;
+  for (int j0 = first; j0 < c; j0 += stride * 8) {
+    float zz[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int j = j0 + stride * kk;
+      const ST* kr = j < c ? S.ks_row(D, b, h, j) : nullptr;
+      zz[kk] = kr ? D.sel_scale * qsv.dot(kr) : -INFINITY;
+    }
+    float mc = zz[0];
+#pragma unroll
+    for (int kk = 1; kk < 8; ++kk) mc = fmaxf(mc, zz[kk]);
+    const float mn = fmaxf(m, mc * kLog2e);
+    if (mn != -INFINITY) {
+      float acc = s * exp2f(m - mn);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) acc += exp2f(zz[kk] * kLog2e - mn);
+      s = acc;
+      m = mn;
+    }
+    unsigned long long bk[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int j = j0 + stride * kk;
+      bk[kk] = j < c ? ((unsigned long long)ord_key(zz[kk]) << 32) | (unsigned)~j : 0ull;
+    }
+    ce_desc(bk[0], bk[2]); ce_desc(bk[1], bk[3]); ce_desc(bk[4], bk[6]); ce_desc(bk[5], bk[7]);
+    ce_desc(bk[0], bk[4]); ce_desc(bk[1], bk[5]); ce_desc(bk[2], bk[6]); ce_desc(bk[3], bk[7]);
+    ce_desc(bk[0], bk[1]); ce_desc(bk[2], bk[3]); ce_desc(bk[4], bk[5]); ce_desc(bk[6], bk[7]);
+    ce_desc(bk[2], bk[4]); ce_desc(bk[3], bk[5]);
+    ce_desc(bk[1], bk[4]); ce_desc(bk[3], bk[6]);
+    ce_desc(bk[1], bk[2]); ce_desc(bk[3], bk[4]); ce_desc(bk[5], bk[6]);
+#pragma unroll
+    for (int r = KM - 8; r < KM; ++r) {
+      const unsigned long long o = bk[KM - 1 - r];
+      tk[r] = o > tk[r] ? o : tk[r];
+    }
+#pragma unroll
+    for (int st = KM / 2; st >= 1; st >>= 1)
+#pragma unroll
+      for (int r = 0; r < KM; ++r)
+        if ((r & st) == 0) ce_desc(tk[r], tk[r + st]);
+  }
+  // merge the wave's 64 lists
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    unsigned long long p[KM];
+#pragma unroll
+    for (int r = 0; r < KM; ++r) p[r] = shfl_xor_u64(tk[r], o);
+    merge_desc<KM>(tk, p);
+  }
+  *m_out = m;
+  *s_out = s;
+}
+
+// Entry r = lane (< K) of a row's selection from its best-KM list and the
+// log2-domain log-sum-exp (M, Ssum) of all its scores: *j (-1 past min(c, K))
+// and *bs (z - lam, or z - log sum over the kept blocks of exp z when
+// renorm; -inf past min(c, K)).
+template <int KM>
+__device__ __forceinline__ void select_entry(const unsigned long long (&tk)[KM], float M,
+                                             float Ssum, int c, int K, int renorm, int lane,
+                                             int* j_out, float* bs_out) {
+  const int n = c < K ? c : K;
+  float norm = c == 0 ? -INFINITY : (M + log2f(Ssum)) * kLn2;
+  if (renorm) {
+    const float mm = key_value((unsigned)(tk[0] >> 32));
+    float ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < KM; ++r)
+      if (r < n) ss += exp2f((key_value((unsigned)(tk[r] >> 32)) - mm) * kLog2e);
+    norm = n == 0 ? -INFINITY : mm + log2f(ss) * kLn2;
+  }
+  unsigned long long mine = 0ull;
+#pragma unroll
+  for (int r = 0; r < KM; ++r)
+    if (lane == r) mine = tk[r];
+  *j_out = lane < n ? (int)~(unsigned)mine : -1;
+  *bs_out = lane < n ? key_value((unsigned)(mine >> 32)) - norm : -INFINITY;
+}
+
+// One wave selects a row alone.
+template <int DS, typename ST, typename Sel, int KM>
+__device__ __forceinline__ void wave_best_entry(const ST* __restrict__ qs, const Sel& S,
+                                                const Dims& D, size_t row, int K, int renorm,
+                                                int lane, int* j_out, float* bs_out) {
+  const int c = S.hist(D, row);
+  unsigned long long tk[KM];
+  float m, s;
+  wave_best<DS, ST, Sel, KM>(qs, S, D, row, c, lane, 64, tk, &m, &s);
+  const float M = wave_max(m);
+  const float Ssum = wave_sum(M == -INFINITY ? 0.f : s * exp2f(m - M));
+  select_entry<KM>(tk, M, Ssum, c, K, renorm, lane, j_out, bs_out);
+}
+
+}  // namespace sas

@@ -25,6 +25,7 @@
 // kernel folds each row's partials by log-sum-exp.
 #include "sas_device.h"
 #include "sas_internal.h"
+#include "select_device.h"
 
 #include <algorithm>
 
@@ -232,6 +233,48 @@ __global__ __launch_bounds__(64 * kRowWaves) void sparse_row_kernel(
     T* __restrict__ o, float* __restrict__ lse, Dims D, int K) {
   __shared__ RowLds<HD> L;
   attend_row<HD, T>(q, S, GlobalSlots{idx, bias}, o, lse, D, K, blockIdx.x, blockDim.x >> 6, L);
+}
+
+// Slots of a row chosen in the same workgroup (LDS).
+struct LdsSlots {
+  const int* j;
+  const float* b;
+  __device__ void get(size_t, int, int slot, int* jj, float* add) const {
+    *jj = j[slot];
+    *add = b[slot];
+  }
+};
+
+// Selection and attention of a row in one workgroup (decode): wave 0 picks
+// the row's K <= KM blocks (wave_best_entry, the routine sas_topk_blocks and
+// sas_paged_topk use for few rows) into LDS and optionally writes idx / bias;
+// then every wave attends its slots as the row kernel does.  One launch, and
+// no round trip of the selection through global memory.  (Splitting the
+// scoring over all the row's waves and merging their lists in LDS was
+// slower: the selection is not what bounds this kernel.)
+template <int HD, typename T, int DS, int KM, typename Sel, typename Src>
+__global__ __launch_bounds__(64 * kRowWaves) void topk_row_kernel(
+    const T* __restrict__ q, Src S, const T* __restrict__ qs, Sel SS, int K, int renorm,
+    int* __restrict__ idx, float* __restrict__ bias, T* __restrict__ o, float* __restrict__ lse,
+    Dims D) {
+  __shared__ RowLds<HD> L;
+  __shared__ int sj[KM];
+  __shared__ float sb[KM];
+  const size_t row = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    int j;
+    float bs;
+    wave_best_entry<DS, T, Sel, KM>(qs, SS, D, row, K, renorm, lane, &j, &bs);
+    if (lane < K) {
+      sj[lane] = j;
+      sb[lane] = bs;
+      if (idx) idx[row * K + lane] = j;
+      if (bias) bias[row * K + lane] = bs;
+    }
+  }
+  __syncthreads();
+  attend_row<HD, T>(q, S, LdsSlots{sj, sb}, o, lse, D, K, row, blockDim.x >> 6, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1037,6 +1080,90 @@ hipError_t launch_paged_decode(const void* q, const void* k_pool, const void* v_
                                               o, lse, K, D, st)
                    : launch_paged_t<64, float>(q, k_pool, v_pool, table, lens, pages, idx, bias,
                                                o, lse, K, D, st);
+  return hipErrorInvalidValue;
+}
+
+// Fused selection + decode (K <= 16), contiguous and paged caches.
+template <int HD, typename T, int DS, typename Sel, typename Src>
+static hipError_t launch_topk_row_t(const void* q, Src S, const void* qs, Sel SS, int K,
+                                    int renorm, int* idx, float* bias, void* o, float* lse,
+                                    const Dims& D, size_t rows, hipStream_t st) {
+  const dim3 grid((unsigned)rows), blk(64 * row_waves(K));
+  if (K <= 8)
+    hipLaunchKernelGGL((topk_row_kernel<HD, T, DS, 8, Sel, Src>), grid, blk, 0, st, (const T*)q,
+                       S, (const T*)qs, SS, K, renorm, idx, bias, (T*)o, lse, D);
+  else
+    hipLaunchKernelGGL((topk_row_kernel<HD, T, DS, 16, Sel, Src>), grid, blk, 0, st, (const T*)q,
+                       S, (const T*)qs, SS, K, renorm, idx, bias, (T*)o, lse, D);
+  return hipGetLastError();
+}
+
+template <int HD, typename T>
+static hipError_t launch_topk_decode_d(const void* q, const void* k, const void* v,
+                                       const void* qs, const void* ks, int K, int renorm,
+                                       int* idx, float* bias, void* o, float* lse, const Dims& D,
+                                       hipStream_t st) {
+  const size_t rows = (size_t)D.batch * D.hq * D.tq;
+  const DenseKV<HD, T> S{(const T*)k, (const T*)v};
+  const DenseSel<T> SS{(const T*)ks};
+  switch (D.ds) {
+    case 16: return launch_topk_row_t<HD, T, 16>(q, S, qs, SS, K, renorm, idx, bias, o, lse, D, rows, st);
+    case 32: return launch_topk_row_t<HD, T, 32>(q, S, qs, SS, K, renorm, idx, bias, o, lse, D, rows, st);
+    case 64: return launch_topk_row_t<HD, T, 64>(q, S, qs, SS, K, renorm, idx, bias, o, lse, D, rows, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_topk_decode(const void* q, const void* k, const void* v, const void* qs,
+                              const void* ks, int K, int renorm, int* idx, float* bias, void* o,
+                              float* lse, const Dims& D, bool bf16_io, hipStream_t st) {
+  if (K < 1 || K > 16) return hipErrorInvalidValue;
+  if (bf16_io) {
+    if (D.d == 128)
+      return launch_topk_decode_d<128, bf16>(q, k, v, qs, ks, K, renorm, idx, bias, o, lse, D, st);
+    if (D.d == 64)
+      return launch_topk_decode_d<64, bf16>(q, k, v, qs, ks, K, renorm, idx, bias, o, lse, D, st);
+  } else if (D.d == 64) {
+    return launch_topk_decode_d<64, float>(q, k, v, qs, ks, K, renorm, idx, bias, o, lse, D, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int HD, typename T>
+static hipError_t launch_paged_topk_decode_d(const void* q, const void* k_pool,
+                                             const void* v_pool, const void* qs,
+                                             const void* ks_pool, const int* table,
+                                             const int* lens, int pages, int K, int renorm,
+                                             int* idx, float* bias, void* o, float* lse,
+                                             const Dims& D, hipStream_t st) {
+  const size_t rows = (size_t)D.batch * D.hq;
+  const PagedKV<HD, T> S{(const T*)k_pool, (const T*)v_pool, table, lens, pages};
+  const PagedSel<T> SS{(const T*)ks_pool, table, lens, pages};
+  switch (D.ds) {
+    case 16: return launch_topk_row_t<HD, T, 16>(q, S, qs, SS, K, renorm, idx, bias, o, lse, D, rows, st);
+    case 32: return launch_topk_row_t<HD, T, 32>(q, S, qs, SS, K, renorm, idx, bias, o, lse, D, rows, st);
+    case 64: return launch_topk_row_t<HD, T, 64>(q, S, qs, SS, K, renorm, idx, bias, o, lse, D, rows, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_paged_topk_decode(const void* q, const void* k_pool, const void* v_pool,
+                                    const void* qs, const void* ks_pool, const int* table,
+                                    const int* lens, int pages, int K, int renorm, int* idx,
+                                    float* bias, void* o, float* lse, const Dims& D,
+                                    bool bf16_io, hipStream_t st) {
+  if (K < 1 || K > 16) return hipErrorInvalidValue;
+  if (bf16_io) {
+    if (D.d == 128)
+      return launch_paged_topk_decode_d<128, bf16>(q, k_pool, v_pool, qs, ks_pool, table, lens,
+                                                   pages, K, renorm, idx, bias, o, lse, D, st);
+    if (D.d == 64)
+      return launch_paged_topk_decode_d<64, bf16>(q, k_pool, v_pool, qs, ks_pool, table, lens,
+                                                  pages, K, renorm, idx, bias, o, lse, D, st);
+  } else if (D.d == 64) {
+    return launch_paged_topk_decode_d<64, float>(q, k_pool, v_pool, qs, ks_pool, table, lens,
+                                                 pages, K, renorm, idx, bias, o, lse, D, st);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -22,46 +22,13 @@
 // no "already taken" set is needed.
 #include "sas_device.h"
 #include "sas_internal.h"
+#include "select_device.h"
 
 namespace sas {
 
 __device__ __forceinline__ bool better(float za, int ja, float zb, int jb) {
   return za > zb || (za == zb && ja < jb);
 }
-
-// Where a row's selector keys live.  DenseSel: contiguous [B, Hks, NB, ds]
-// rows, row t has c(t) = t / 64 historical blocks.  PagedSel: one ks row per
-// page in a pool [pages, Hks, ds], a sequence's block j on page
-// table[b, j]; the decode row of sequence b sits at t = len[b] - 1.  A row
-// with a length out of range has no history; a block whose page id is out of
-// range is never read and scores -inf.
-template <typename ST>
-struct DenseSel {
-  const ST* ks;
-  __device__ int hist(const Dims& D, size_t row) const {
-    return (D.qoff + (int)(row % D.tq)) / D.blk;
-  }
-  __device__ const ST* ks_row(const Dims& D, int b, int h, int j) const {
-    return ks + (((size_t)b * D.hks + h / D.hps) * (size_t)D.nb + j) * D.ds;
-  }
-};
-
-template <typename ST>
-struct PagedSel {
-  const ST* ks;
-  const int* table;
-  const int* lens;
-  int pages;
-  __device__ int hist(const Dims& D, size_t row) const {
-    const int len = lens[row / D.hq];
-    return (len >= 1 && len <= D.nb * kBlock) ? (len - 1) / kBlock : 0;
-  }
-  __device__ const ST* ks_row(const Dims& D, int b, int h, int j) const {
-    const int pg = table[(size_t)b * D.nb + j];
-    if (pg < 0 || pg >= pages) return nullptr;
-    return ks + ((size_t)pg * D.hks + h / D.hps) * D.ds;
-  }
-};
 
 template <int DS, typename ST, typename Sel>
 __global__ __launch_bounds__(256) void topk_wave_kernel(const ST* __restrict__ qs, Sel S, int K,
@@ -153,21 +120,6 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const ST* __restrict__ q
   }
 }
 
-// Order-preserving 32-bit key of a score (larger z, larger key; -0 counts as
-// +0, as in a floating-point comparison), and the selection order on (key,
-// block): key descending, then block ascending.
-__device__ __forceinline__ unsigned ord_key(float z) {
-  unsigned u = __float_as_uint(z);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(unsigned k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-__device__ __forceinline__ bool key_before(unsigned ka, int ja, unsigned kb, int jb) {
-  return ka > kb || (ka == kb && ja < jb);
-}
-
 // Lane-per-row variant for many rows and K <= 32: the 64 rows of a wave are
 // consecutive positions of one (batch, head), so every ks row is a
 // wave-uniform load.  Each lane keeps its best KMAX (>= K) blocks in
@@ -180,13 +132,6 @@ __device__ __forceinline__ bool key_before(unsigned ka, int ja, unsigned kb, int
 // bitonic merge sorts it again; every step is branch-free, so the lanes of a
 // wave never wait on each other's insertions.  Scores use the same SelQ dot
 // product.
-__device__ __forceinline__ void ce_desc(unsigned long long& a, unsigned long long& b) {
-  const bool sw = b > a;
-  const unsigned long long hi = sw ? b : a, lo = sw ? a : b;
-  a = hi;
-  b = lo;
-}
-
 template <int DS, typename ST, int KMAX>
 __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ qs,
                                                         const ST* __restrict__ ks, int K,
@@ -270,6 +215,26 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
       idx[row * K + r] = r < n ? (int)~(unsigned)tk[r] : -1;
       bias[row * K + r] = r < n ? key_value((unsigned)(tk[r] >> 32)) - norm : -INFINITY;
     }
+  }
+}
+
+// Wave per row for few rows and K <= KM (decode, paged decode, small calls):
+// wave_best (select_device.h) leaves every lane with the row's best KM keys
+// and its log-sum-exp; lane r < K writes entry r.
+template <int DS, typename ST, typename Sel, int KM>
+__global__ __launch_bounds__(256) void topk_merge_kernel(const ST* __restrict__ qs, Sel S, int K,
+                                                         int renorm, int* __restrict__ idx,
+                                                         float* __restrict__ bias, Dims D) {
+  const int lane = threadIdx.x & 63;
+  const size_t nrows = (size_t)D.batch * D.hq * D.tq;
+  const size_t row = (size_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= nrows) return;  // whole wave (no workgroup barrier below)
+  int j;
+  float bs;
+  wave_best_entry<DS, ST, Sel, KM>(qs, S, D, row, K, renorm, lane, &j, &bs);
+  if (lane < K) {
+    idx[row * K + lane] = j;
+    bias[row * K + lane] = bs;
   }
 }
 
@@ -505,11 +470,21 @@ static hipError_t launch_topk_t(const void* qs, const void* ks, int K, int renor
   // a few passes over a row's scores instead of K argmax rounds
   if (K >= 16 && topk_budget_supported(D, K))
     return launch_select_t<DS, ST>(qs, ks, K, 0, 1, renorm, idx, bias, D, st);
+  const size_t nrows = (size_t)D.batch * D.hq * D.tq;
+  if (K <= 16) {
+    const unsigned grid = (unsigned)((nrows + 3) / 4);
+    if (K <= 8)
+      hipLaunchKernelGGL((topk_merge_kernel<DS, ST, DenseSel<ST>, 8>), dim3(grid), dim3(256), 0,
+                         st, (const ST*)qs, DenseSel<ST>{(const ST*)ks}, K, renorm, idx, bias, D);
+    else
+      hipLaunchKernelGGL((topk_merge_kernel<DS, ST, DenseSel<ST>, 16>), dim3(grid), dim3(256), 0,
+                         st, (const ST*)qs, DenseSel<ST>{(const ST*)ks}, K, renorm, idx, bias, D);
+    return hipGetLastError();
+  }
   const size_t per = (size_t)(D.nb + K) * sizeof(float);
   int wpg = 4;
   while (wpg > 1 && per * wpg > 65536) wpg >>= 1;
   if (per * wpg > 65536) return hipErrorInvalidValue;
-  const size_t nrows = (size_t)D.batch * D.hq * D.tq;
   const unsigned grid = (unsigned)((nrows + wpg - 1) / wpg);
   hipLaunchKernelGGL((topk_wave_kernel<DS, ST, DenseSel<ST>>), dim3(grid), dim3(64 * wpg),
                      per * wpg, st, (const ST*)qs, DenseSel<ST>{(const ST*)ks}, K, renorm, idx,
@@ -521,6 +496,17 @@ template <int DS, typename ST>
 static hipError_t launch_paged_topk_t(const void* qs, const void* ks_pool, const int* table,
                                       const int* lens, int pages, int K, int renorm, int* idx,
                                       float* bias, const Dims& D, hipStream_t st) {
+  if (K <= 16) {
+    const unsigned grid = (unsigned)(((size_t)D.batch * D.hq + 3) / 4);
+    const PagedSel<ST> sel{(const ST*)ks_pool, table, lens, pages};
+    if (K <= 8)
+      hipLaunchKernelGGL((topk_merge_kernel<DS, ST, PagedSel<ST>, 8>), dim3(grid), dim3(256), 0,
+                         st, (const ST*)qs, sel, K, renorm, idx, bias, D);
+    else
+      hipLaunchKernelGGL((topk_merge_kernel<DS, ST, PagedSel<ST>, 16>), dim3(grid), dim3(256), 0,
+                         st, (const ST*)qs, sel, K, renorm, idx, bias, D);
+    return hipGetLastError();
+  }
   const size_t per = (size_t)(D.nb + K) * sizeof(float);
   int wpg = 4;
   while (wpg > 1 && per * wpg > 65536) wpg >>= 1;
@@ -553,7 +539,7 @@ hipError_t launch_paged_topk(const void* qs, const void* ks_pool, const int* tab
 }
 
 bool topk_supported(const Dims& D, int K) {
-  return use_lane_kernel(D, K) || (K >= 16 && topk_budget_supported(D, K)) ||
+  return use_lane_kernel(D, K) || K <= 16 || (K >= 16 && topk_budget_supported(D, K)) ||
          (size_t)(D.nb + K) * sizeof(float) <= 65536;
 }
 

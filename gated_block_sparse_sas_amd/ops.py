@@ -29,7 +29,8 @@ EXPORTS = ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_attn_bwd_ev",
            "sas_paged_append", "sas_paged_topk", "sas_paged_decode",
            "sas_threshold_count", "sas_threshold_fill", "sas_sparse_fwd_csr",
            "sas_sparse_fwd_csr_ev", "sas_sparse_fwd_noalloc", "sas_noalloc_scratch_bytes",
-           "sas_status_string", "sas_last_hip_error")
+           "sas_topk_decode", "sas_paged_topk_decode", "sas_status_string",
+           "sas_last_hip_error")
 
 
 class SasError(RuntimeError):
@@ -88,13 +89,16 @@ def load():
         lib.sas_paged_topk.argtypes = [P, I32, I32, P, P, P, P, P, P, P]
         lib.sas_paged_decode.argtypes = [P, I32] + [P] * 10 + [SZ, P]
         lib.sas_sparse_fwd_noalloc.argtypes = [P, I32] + [P] * 8
+        lib.sas_topk_decode.argtypes = [P, I32, I32] + [P] * 10
+        lib.sas_paged_topk_decode.argtypes = [P, I32, I32] + [P] * 12
         lib.sas_noalloc_scratch_bytes.argtypes = []
         lib.sas_noalloc_scratch_bytes.restype = ctypes.c_size_t
         for n in ("sas_gate_scores", "sas_attn_fwd", "sas_attn_bwd", "sas_topk_blocks",
                   "sas_topk_blocks_budget", "sas_sparse_fwd", "sas_attn_bwd_ev",
                   "sas_sparse_fwd_ev", "sas_paged_append", "sas_paged_topk",
                   "sas_paged_decode", "sas_threshold_count", "sas_threshold_fill",
-                  "sas_sparse_fwd_csr", "sas_sparse_fwd_csr_ev", "sas_sparse_fwd_noalloc"):
+                  "sas_sparse_fwd_csr", "sas_sparse_fwd_csr_ev", "sas_sparse_fwd_noalloc",
+                  "sas_topk_decode", "sas_paged_topk_decode"):
             getattr(lib, n).restype = ctypes.c_int
         lib.sas_status_string.argtypes = [ctypes.c_int]
         lib.sas_status_string.restype = ctypes.c_char_p
@@ -281,6 +285,27 @@ def sparse_fwd(q, k, v, idx, bias, block=64, sm_scale=None, ws=None, with_lse=Tr
     return o, lse
 
 
+def topk_decode(q, k, v, qs, ks, topk, block=64, renorm=0, sm_scale=None, sel_scale=None,
+                with_sel=True, with_lse=True):
+    """Top-K selection and sparse forward in one call (``sas_topk_decode``):
+    the results of :func:`topk_blocks` then :func:`sparse_fwd`.  Returns (o,
+    lse, idx, bias); idx / bias None when ``with_sel`` is False."""
+    b, hq, tq, d = q.shape
+    _, hkv, tk, _ = k.shape
+    ds, hks = qs.shape[-1], ks.shape[1]
+    sh = make_shape(b, hq, hkv, tq, tk, d, ds, block, hks, sm_scale, sel_scale, _dt(q), _dt(qs))
+    o = torch.empty_like(q)
+    lse = torch.empty((b, hq, tq), dtype=torch.float32, device=q.device) if with_lse else None
+    idx = (torch.empty((b, hq, tq, topk), dtype=torch.int32, device=q.device) if with_sel
+           else None)
+    bias = (torch.empty((b, hq, tq, topk), dtype=torch.float32, device=q.device) if with_sel
+            else None)
+    _check("sas_topk_decode", load().sas_topk_decode(
+        ctypes.byref(sh), int(topk), int(renorm), _p(q), _p(k), _p(v), _p(qs), _p(ks), _p(idx),
+        _p(bias), _p(o), _p(lse), _stream(q)))
+    return o, lse, idx, bias
+
+
 def sparse_fwd_noalloc(q, k, v, idx, bias, block=64, sm_scale=None, with_lse=True):
     """:func:`sparse_fwd` through ``sas_sparse_fwd_noalloc``: the library's fixed
     scratch array instead of a workspace.  Returns (o, lse)."""
@@ -332,6 +357,29 @@ def paged_topk(qs, ks_pool, block_table, seq_len, topk, renorm=0, sel_scale=None
         ctypes.byref(sh), int(topk), int(renorm), _p(seq_len), _p(block_table), _p(qs),
         _p(ks_pool), _p(idx), _p(bias), _stream(qs)))
     return idx, bias
+
+
+def paged_topk_decode(q, k_pool, v_pool, qs, ks_pool, block_table, seq_len, topk, renorm=0,
+                      sm_scale=None, sel_scale=None, with_sel=True, with_lse=True):
+    """:func:`paged_topk` then :func:`paged_decode` in one call
+    (``sas_paged_topk_decode``).  Returns (o, lse, idx, bias)."""
+    batch, hq, d = q.shape
+    pages, hkv, _, _ = k_pool.shape
+    ds, hks = qs.shape[-1], ks_pool.shape[1]
+    max_blocks = block_table.shape[1]
+    sh = make_paged_shape(batch, hq, hkv, d, ds, max_blocks, pages, hks, sm_scale=sm_scale,
+                          sel_scale=sel_scale, dtype=_dt(q))
+    o = torch.empty_like(q)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device) if with_lse else None
+    idx = (torch.empty((batch, hq, topk), dtype=torch.int32, device=q.device) if with_sel
+           else None)
+    bias = (torch.empty((batch, hq, topk), dtype=torch.float32, device=q.device) if with_sel
+            else None)
+    _check("sas_paged_topk_decode", load().sas_paged_topk_decode(
+        ctypes.byref(sh), int(topk), int(renorm), _p(seq_len), _p(block_table), _p(q),
+        _p(k_pool), _p(v_pool), _p(qs), _p(ks_pool), _p(idx), _p(bias), _p(o), _p(lse),
+        _stream(q)))
+    return o, lse, idx, bias
 
 
 def paged_workspace_bytes(sh: PagedShape, topk: int) -> int:

@@ -131,11 +131,11 @@ sas_status sas_attn_bwd(const sas_shape* shape, const void* q, const void* k, co
  * the min(topk, c(t)) blocks with the largest z, ordered by z descending and
  * block index ascending on ties; idx pads with -1 and bias with -inf.
  * bias = z - lam (renorm == 0, the training log-gate of the block) or
- * z - log sum_{selected} exp z (renorm == 1).  1 <= topk.  Needs
- * 4 (nb + topk) bytes of LDS per row (topk >= 16: 4 (nb + 256 +
- * 2 next_pow2(topk)), topk <= 1024), at most 64 KiB, unless there are at
- * least 16384 rows and topk <= 32 (a kernel without LDS); SAS_ERR_UNSUPPORTED
- * otherwise.
+ * z - log sum_{selected} exp z (renorm == 1).  1 <= topk.  topk <= 16
+ * takes kernels without LDS (any nb); larger topk needs 4 (nb + 256 +
+ * 2 next_pow2(topk)) bytes of LDS per row (topk <= 1024), at most 64 KiB,
+ * unless there are at least 16384 rows and topk <= 32 (a kernel without
+ * LDS); SAS_ERR_UNSUPPORTED otherwise.
  * Source: both abstracts (selector + hard Top-K; budget = attended units per
  * query); the budget counts historical blocks, the current block is extra. */
 sas_status sas_topk_blocks(const sas_shape* shape, int32_t topk, int32_t renorm, const void* qs,
@@ -311,9 +311,9 @@ sas_status sas_paged_append(const sas_paged_shape* shape, const int32_t* pos,
                             void* stream);
 
 /* Hard Top-K of the historical blocks of each sequence's query (semantics,
- * order, padding and renorm as sas_topk_blocks).  Needs
- * 4 (max_blocks + topk) bytes of LDS per row, at most 64 KiB
- * (SAS_ERR_UNSUPPORTED beyond). */
+ * order, padding and renorm as sas_topk_blocks).  topk <= 16: any
+ * max_blocks; larger topk needs 4 (max_blocks + topk) bytes of LDS per row,
+ * at most 64 KiB (SAS_ERR_UNSUPPORTED beyond). */
 sas_status sas_paged_topk(const sas_paged_shape* shape, int32_t topk, int32_t renorm,
                           const int32_t* seq_len, const int32_t* block_table, const void* qs,
                           const void* ks_pool, int32_t* idx, float* bias, void* stream);
@@ -324,6 +324,28 @@ sas_status sas_paged_decode(const sas_paged_shape* shape, int32_t topk, const in
                             const int32_t* block_table, const void* q, const void* k_pool,
                             const void* v_pool, const int32_t* idx, const float* bias, void* o,
                             float* lse, void* ws, size_t* ws_bytes, void* stream);
+
+/* Selection and decode in one call: sas_topk_blocks followed by
+ * sas_sparse_fwd (identical selection, padding, bias modes and outputs),
+ * with one workgroup per query row choosing its blocks and attending them
+ * in the same launch (no round trip of the selection through global memory,
+ * one launch instead of two).  Meant for decode and other calls with few
+ * rows (one workgroup per row, any tq).  1 <= topk <= 16 (SAS_ERR_SHAPE
+ * below, SAS_ERR_UNSUPPORTED above); idx, bias [batch, hq, tq, topk] receive
+ * the selection when not NULL; lse may be NULL.  No workspace.  Source: both
+ * abstracts (a small set of context units per query at inference). */
+sas_status sas_topk_decode(const sas_shape* shape, int32_t topk, int32_t renorm, const void* q,
+                           const void* k, const void* v, const void* qs, const void* ks,
+                           int32_t* idx, float* bias, void* o, float* lse, void* stream);
+
+/* The same over the paged pools: sas_paged_topk followed by sas_paged_decode
+ * in one launch; arguments as those two calls take them (idx, bias [batch,
+ * hq, topk] may be NULL, lse may be NULL), 1 <= topk <= 16. */
+sas_status sas_paged_topk_decode(const sas_paged_shape* shape, int32_t topk, int32_t renorm,
+                                 const int32_t* seq_len, const int32_t* block_table,
+                                 const void* q, const void* k_pool, const void* v_pool,
+                                 const void* qs, const void* ks_pool, int32_t* idx, float* bias,
+                                 void* o, float* lse, void* stream);
 
 /* Static text for a status code. */
 const char* sas_status_string(sas_status status);

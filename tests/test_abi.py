@@ -117,8 +117,12 @@ def test_topk_checks(lib):
     assert lib.sas_topk_blocks(ctypes.byref(sh), 4, 2, A, A, A, A, STREAM) == 2
     assert lib.sas_topk_blocks(ctypes.byref(sh), 4, 0, A, A, None, A, STREAM) == 1
     assert lib.sas_topk_blocks(ctypes.byref(sh), 4, 0, A, A, A, MIS, STREAM) == 4
-    big = shape(tk=1 << 20, tq=64)  # nb + K floats of LDS per row exceed the kernel's limit
-    assert lib.sas_topk_blocks(ctypes.byref(big), 4, 0, A, A, A, A, STREAM) == 5
+    # topk > 16 with few rows keeps nb + 256 + 2 next_pow2(K) floats of LDS per
+    # row: past 64 KiB unsupported; topk <= 16 takes the kernel without LDS
+    big = shape(tk=1 << 20, tq=64)
+    assert lib.sas_topk_blocks(ctypes.byref(big), 40, 0, A, A, A, A, STREAM) == 5
+    assert lib.sas_topk_blocks(ctypes.byref(shape(tk=1 << 20, tq=64, batch=0)), 4, 0, A, A, A,
+                               A, STREAM) == 0
 
 
 def test_topk_budget_checks(lib):
@@ -231,8 +235,8 @@ def test_paged_checks(lib):
     assert lib.sas_paged_topk(ctypes.byref(sh), 0, 0, A, A, A, A, A, A, STREAM) == 2
     assert lib.sas_paged_topk(ctypes.byref(sh), 4, 2, A, A, A, A, A, A, STREAM) == 2
     assert lib.sas_paged_topk(ctypes.byref(sh), 4, 0, A, None, A, A, A, A, STREAM) == 1
-    big = pshape(max_blocks=20000)
-    assert lib.sas_paged_topk(ctypes.byref(big), 4, 0, A, A, A, A, A, A, STREAM) == 5
+    big = pshape(max_blocks=20000)  # topk > 16: LDS per row past 64 KiB
+    assert lib.sas_paged_topk(ctypes.byref(big), 40, 0, A, A, A, A, A, A, STREAM) == 5
     # append: ks_new without ks_pool, misaligned pool
     assert lib.sas_paged_append(ctypes.byref(sh), A, A, A, A, A, A, A, None, STREAM) == 1
     assert lib.sas_paged_append(ctypes.byref(sh), A, A, A, A, None, MIS, A, None, STREAM) == 4
@@ -313,3 +317,24 @@ def test_block_size_support(lib):
                                   STREAM) == 0
     assert lib.sas_sparse_fwd(ctypes.byref(sh), 4, *([None] * 7), None, ctypes.byref(n),
                               STREAM) == 0
+
+
+def test_fused_decode_checks(lib):
+    # sas_topk_decode: q k v qs ks idx bias o lse; idx, bias, lse optional
+    sh = shape(tq=1)
+    f = lib.sas_topk_decode
+    assert f(ctypes.byref(sh), 0, 0, *([A] * 10), STREAM) == 2       # topk < 1
+    assert f(ctypes.byref(sh), 4, 2, *([A] * 10), STREAM) == 2       # renorm
+    assert f(ctypes.byref(sh), 17, 0, *([A] * 10), STREAM) == 5      # topk > 16
+    assert f(ctypes.byref(sh), 4, 0, None, *([A] * 9), STREAM) == 1  # q NULL
+    args = [A] * 5 + [None, None, A, None]                          # no idx / bias / lse
+    assert f(ctypes.byref(shape(tq=1, batch=0)), 4, 0, *args, STREAM) == 0
+    assert f(ctypes.byref(sh), 4, 0, *([A] * 5), MIS, A, A, A, STREAM) == 4
+    assert f(None, 4, 0, *([A] * 10), STREAM) == 1
+    # sas_paged_topk_decode: seq_len table q k_pool v_pool qs ks_pool idx bias o lse
+    g = lib.sas_paged_topk_decode
+    ps = pshape()
+    assert g(ctypes.byref(ps), 0, 0, *([A] * 12), STREAM) == 2
+    assert g(ctypes.byref(ps), 17, 0, *([A] * 12), STREAM) == 5
+    assert g(ctypes.byref(ps), 4, 0, A, None, *([A] * 10), STREAM) == 1   # table NULL
+    assert g(ctypes.byref(pshape(batch=0)), 4, 0, *([A] * 7), None, None, A, None, STREAM) == 0
