@@ -1668,6 +1668,85 @@ __global__ __launch_bounds__(256) void dks_kernel(const float* __restrict__ dz,
   }
 }
 
+// The same reduction with 16-byte loads of dz (nb % 4 == 0): lane l reads
+// blocks j0 + 4 (l % 32) .. + 3 of its row in one load, and the four values
+// feed four 32-block MFMA tiles (tile q holds blocks j0 + 4 m + q), so a
+// workgroup covers 128 blocks and a load instruction moves 1 KB instead of
+// 256 bytes; the qs operand of a row pair serves all four tiles.  The
+// waves' tiles are summed through LDS one tile at a time.
+constexpr int kDks4Blocks = 128;
+
+template <int DS, typename ST>
+__global__ __launch_bounds__(256) void dks4_kernel(const float* __restrict__ dz,
+                                                   const ST* __restrict__ qs,
+                                                   float* __restrict__ acc, Dims D) {
+  constexpr int NT = (DS + 31) / 32;  // 32-dim N-tiles
+  __shared__ float red[4][NT][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j0 = blockIdx.x * kDks4Blocks;
+  const int bs = blockIdx.z, b = bs / D.hks, s = bs % D.hks;
+  const int nch = (D.tq + kDksChunk - 1) / kDksChunk;
+  const int hl = blockIdx.y / nch, i0 = (blockIdx.y % nch) * kDksChunk;
+  const int i_min = max(0, (j0 + 1) * D.blk - D.qoff);  // first row with c(t) > j0
+  const int istart = max(i0, i_min), iend = min(i0 + kDksChunk, D.tq);
+  if (istart >= iend) return;  // uniform over the workgroup
+  const size_t hrow = ((size_t)b * D.hq + s * D.hps + hl) * D.tq;
+  const int jl = j0 + 4 * (lane & 31), rsub = lane >> 5;
+  f32x16 dacc[4][NT];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) dacc[q][nt] = f32x16{};
+  constexpr int U = 4;  // row pairs whose loads are in flight together
+  for (int i = istart + 2 * wave; i < iend; i += 8 * U) {
+    f32x4 a[U];
+    float bq[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ii = i + 8 * u + rsub;
+      const bool ok = ii < iend;
+      const float* zr = dz + (hrow + ii) * D.nb + jl;
+      if (ok && jl + 3 < D.nb) {
+        a[u] = *(const f32x4*)zr;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a[u][q] = ok && jl + q < D.nb ? zr[q] : 0.f;
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int dim = 32 * nt + (lane & 31);
+        bq[u][nt] = ok && dim < DS ? to_f32(qs[(hrow + ii) * DS + dim]) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          dacc[q][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u][q], bq[u][nt], dacc[q][nt], 0,
+                                                              0, 0);
+  }
+  // accumulator of tile q, lane l, register r: dim 32 nt + l % 32, block
+  // j0 + 4 (8 (r / 4) + 4 (l / 32) + r % 4) + q
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[wave][nt][r][lane] = dacc[q][nt][r];
+    __syncthreads();
+    for (int x = threadIdx.x; x < NT * 16 * 64; x += 256) {
+      const int nt = x / 1024, r = (x / 64) % 16, l = x % 64;
+      const float v = red[0][nt][r][l] + red[1][nt][r][l] + red[2][nt][r][l] + red[3][nt][r][l];
+      const int j = j0 + 4 * (8 * (r / 4) + 4 * (l / 32) + r % 4) + q, dim = 32 * nt + l % 32;
+      if (j < D.nb && dim < DS && v != 0.f)
+        atomicAdd(acc + (((size_t)b * D.hks + s) * D.nb + j) * DS + dim, v);
+    }
+    __syncthreads();
+  }
+}
+
 __global__ void fill_zero_kernel(float* __restrict__ p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -1726,6 +1805,26 @@ hipError_t launch_dks(const float* dz, const void* qs, float* acc, void* dks, co
   const size_t n = (size_t)D.batch * D.hks * D.nb * D.ds;
   const unsigned fg = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(fill_zero_kernel, dim3(fg), dim3(256), 0, st, acc, n);
+  if (D.nb % 4 == 0) {
+    dim3 grid4((D.nb + kDks4Blocks - 1) / kDks4Blocks,
+               D.hps * ((D.tq + kDksChunk - 1) / kDksChunk), D.batch * D.hks);
+    switch (D.ds) {
+      case 16:
+        hipLaunchKernelGGL((dks4_kernel<16, ST>), grid4, dim3(256), 0, st, dz, (const ST*)qs, acc, D);
+        break;
+      case 32:
+        hipLaunchKernelGGL((dks4_kernel<32, ST>), grid4, dim3(256), 0, st, dz, (const ST*)qs, acc, D);
+        break;
+      case 64:
+        hipLaunchKernelGGL((dks4_kernel<64, ST>), grid4, dim3(256), 0, st, dz, (const ST*)qs, acc, D);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((scale_convert_kernel<ST>), dim3(fg), dim3(256), 0, st, (const float*)acc,
+                       (ST*)dks, D.sel_scale, n);
+    return hipGetLastError();
+  }
   dim3 grid((D.nb + 31) / 32, D.hps * ((D.tq + kDksChunk - 1) / kDksChunk), D.batch * D.hks);
   switch (D.ds) {
     case 16:
