@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) void gate_lse_kernel(const ST* __restrict__ qs
   if (i < D.tq) lam[row] = c == 0 ? -INFINITY : (m + log2f(s)) * kLn2;
 }
 
-// lam with matrix products, for many units per row (bf16, units under 64
-// tokens): a workgroup of 8 waves takes 256 consecutive rows of one (b, h),
+// lam with matrix products (bf16 selectors, every unit size): a workgroup
+// of 8 waves takes 256 consecutive rows of one (b, h),
 // each wave 32 rows (one per lane column, as in the attention forward).  Unit
 // tiles of 64 ks rows go global -> registers -> LDS, one tile ahead;
 // Z^T = KS QS^T on 32x32x16 MFMA puts 16 units per M-tile of a lane's row in
@@ -185,7 +185,7 @@ template <int DS, typename ST>
 static hipError_t launch_gate_t(const void* qs, const void* ks, float* lam, float* beta,
                                 const Dims& D, hipStream_t st) {
   dim3 grid((D.tq + 255) / 256, D.hq, D.batch);
-  if (std::is_same<ST, bf16>::value && D.blk < kBlock)
+  if (std::is_same<ST, bf16>::value)
     hipLaunchKernelGGL((gate_lse_mfma_kernel<DS>), dim3((D.tq + kGateRows - 1) / kGateRows,
                                                         D.hq, D.batch),
                        dim3(512), 0, st, (const bf16*)qs, (const bf16*)ks, lam, D);
