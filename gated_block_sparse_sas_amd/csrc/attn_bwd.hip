@@ -689,37 +689,50 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
   };
   // per-lane part of the transposing K^T reads: lane 4 kk + a of each 16-lane
   // group points at key row 4 hh + kk, columns 16 ((lane >> 4) & 1) + 4 a
-  const int kbase = (4 * hh + ((lane & 15) >> 2)) * KP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  // unit of this lane's key 32 mt + 8 (r / 4) + 4 hh + r % 4 within the tile
+  const int kbase = (2 * ((lane & 15) >> 2) + hh) * KP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // key row supplied as A-operand row l32 of the S^T / dP^T products: keys
+  // 8 q + 2 i + hh sit in accumulator rows 8 q + 4 hh + i, so that a
+  // transposing read gives each lane half rows of one parity
+  const int prow = (l32 & ~7) | ((l32 & 3) << 1) | ((l32 >> 2) & 1);
+  // unit of this lane's key 32 mt + 8 (r / 4) + 2 (r % 4) + hh within the tile
   auto unit = [](int mt, int r) { return UB <= 1 ? 0 : (UB == 2 ? mt : 2 * mt + r / 8); };
   // UB = 0: the same transposing reads over the per-key ks rows (pitch XP)
-  const int xbase = (4 * hh + ((lane & 15) >> 2)) * XP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int xbase = (2 * ((lane & 15) >> 2) + hh) * XP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   // UB = 0, dz requested: dz[row, unit] = sum of e over the unit's keys.  A
-  // lane holds runs of 4 consecutive keys (32 mt + 8 q + 4 hh + 0..3); units
-  // of 8 keys join the runs of the two lane halves.
+  // lane half holds the keys of one parity of each group of 8 (32 mt + 8 q +
+  // hh + 2 i); units of 2 or more keys join the two halves.
   auto write_dz_units = [&](const f32x16 (&e)[2], int j, size_t rw_, bool ok) {
+    // element (mt, 4 q + i) of lane half hh is key 32 mt + 8 q + 2 i + hh
     const int bsz = 1 << lb;
+    float* zr = dz + rw_ * D.nb;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int k0 = j * kBlock + 32 * mt + 8 * q4 + 4 * hh;  // first key of the run
-        const float er[4] = {e[mt][4 * q4], e[mt][4 * q4 + 1], e[mt][4 * q4 + 2],
-                             e[mt][4 * q4 + 3]};
-        float* zr = dz + rw_ * D.nb;
-        if (bsz == 8) {
+        const int k0 = j * kBlock + 32 * mt + 8 * q4;  // first key of the group of 8
+        float er[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) er[i] = e[mt][4 * q4 + i];
+        if (bsz == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (ok && k0 + 2 * i + hh < tcur0) zr[k0 + 2 * i + hh] = er[i];
+        } else if (bsz == 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = er[i] + __shfl_xor(er[i], 32);
+            if (ok && hh == 0 && k0 + 2 * i < tcur0) zr[(k0 + 2 * i) >> 1] = v;
+          }
+        } else if (bsz == 4) {
+          float v0 = er[0] + er[1], v1 = er[2] + er[3];
+          v0 += __shfl_xor(v0, 32);
+          v1 += __shfl_xor(v1, 32);
+          if (ok && hh == 0 && k0 < tcur0) zr[k0 >> 2] = v0;
+          if (ok && hh == 0 && k0 + 4 < tcur0) zr[(k0 >> 2) + 1] = v1;
+        } else {
           float v = er[0] + er[1] + er[2] + er[3];
           v += __shfl_xor(v, 32);
           if (ok && hh == 0 && k0 < tcur0) zr[k0 >> 3] = v;
-        } else if (bsz == 4) {
-          if (ok && k0 < tcur0) zr[k0 >> 2] = er[0] + er[1] + er[2] + er[3];
-        } else if (bsz == 2) {
-          if (ok && k0 < tcur0) zr[k0 >> 1] = er[0] + er[1];
-          if (ok && k0 + 2 < tcur0) zr[(k0 >> 1) + 1] = er[2] + er[3];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (ok && k0 + i < tcur0) zr[k0 + i] = er[i];
         }
       }
     }
@@ -737,7 +750,7 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
       for (int s = 0; s < DS / 16; ++s) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 a = *(const bf16x8*)&Ss[(32 * mt + l32) * XP + 16 * s + 8 * hh];
+          const bf16x8 a = *(const bf16x8*)&Ss[(32 * mt + prow) * XP + 16 * s + 8 * hh];
           za[mt] = mfma32(a, qsf[s], za[mt]);
         }
       }
@@ -775,7 +788,7 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
+          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 2 * (r % 4) + hh;
           sacc[mt][r] = u < tcur0 ? fmaf(sacc[mt][r], zsc, zoff) : 0.f;
         }
       }
@@ -783,7 +796,7 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
     // operand i (step i / 4, M-tile (i / 2) % 2, K or V by i % 2) is read
     // while product i - 1 runs; the step's Q operand after its last use
     auto opnd = [&](int i) __attribute__((always_inline)) {
-      const int oo = (32 * ((i >> 1) & 1) + l32) * KP + 16 * (i >> 2) + 8 * hh;
+      const int oo = (32 * ((i >> 1) & 1) + prow) * KP + 16 * (i >> 2) + 8 * hh;
       return *(const bf16x8*)&((i & 1) ? Vs : Ks)[oo];
     };
     bf16x8 ob[2], qb = *(const bf16x8*)&Qs[qbase];
@@ -805,12 +818,12 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
       for (int r = 0; r < 16; ++r)
         pv[mt][r] = exp2_raw(fmaf(sacc[mt][r], c1, (UB == 0 ? 0.f : bias2[unit(mt, r)]) - l2));
     if (j >= c_lo) {  // tile meets some row's own tile: cut keys after the row (or the tile)
-      const int mlim = j < ct ? kBlock : (j > ct ? -1 : t - j * kBlock - 4 * hh);
+      const int mlim = j < ct ? kBlock : (j > ct ? -1 : t - j * kBlock - hh);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * mt + 8 * (r / 4) + (r % 4) > mlim) pv[mt][r] = 0.f;
+          if (32 * mt + 8 * (r / 4) + 2 * (r % 4) > mlim) pv[mt][r] = 0.f;
     }
     float dsum[NU];
 #pragma unroll
@@ -823,7 +836,7 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
         sacc[mt][r] = ds;
         if constexpr (UB == 0) {
           // the row's own unit (keys tcur0 .. t; later keys have ds = 0)
-          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
+          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 2 * (r % 4) + hh;
           if (u >= tcur0) dsum[0] += ds;
         } else {
           dsum[unit(mt, r)] += ds;
@@ -855,7 +868,7 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
+          const int u = j * kBlock + 32 * mt + 8 * (r / 4) + 2 * (r % 4) + hh;
           zb[mt][r] =
               u < tcur0 ? sacc[mt][r] - exp2_raw(fmaf(zb[mt][r], zs2, -lam2)) * sb_k : 0.f;
         }
@@ -899,8 +912,9 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
         }
       }
     }
-    // dQ^T += K^T dS^T: the B slots of a lane are keys 16 pp + 4 hh + (0..3,
-    // 8..11) of M-tile mt, and the transposing reads give K^T in that order
+    // dQ^T += K^T dS^T: the B slots of a lane are keys 16 pp + hh + 2 (0..3)
+    // and 16 pp + 8 + hh + 2 (0..3) of M-tile mt, and the transposing reads
+    // give K^T in that order
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {

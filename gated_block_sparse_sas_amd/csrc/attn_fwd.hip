@@ -174,9 +174,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       *(bf16x8*)&Sd[tid * 8] = sreg;
     }
   };
-  // per-lane part of the transposing V^T reads: lane 4k + a of each 16-lane
-  // group points at key row 4 hh + k, columns 16 ((lane >> 4) & 1) + 4 a
-  const int vbase = (4 * hh + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Key order: A-operand row l32 of the S^T products is key row prow, so
+  // accumulator row 8 q + 4 hh + i of a 32-key M-tile holds key 8 q + 2 i + hh.
+  // A transposing V^T read then gives each lane half key rows of one parity
+  // (0, 2, 4, 6 or 1, 3, 5, 7: bank offsets 16 dwords apart at the 72-dword
+  // pitch) instead of four adjacent rows whose 64-byte spans overlap in the
+  // LDS banks.  Lane 4k + a of each 16-lane group points at key row 2 k + hh,
+  // columns 16 ((lane >> 4) & 1) + 4 a.
+  const int vbase = (2 * ((lane & 15) >> 2) + hh) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int prow = (l32 & ~7) | ((l32 & 3) << 1) | ((l32 >> 2) & 1);
 
   bf16x8 pb[2][2];  // P of the last softmax, the B operand of the PV products
 
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
       for (int s = 0; s < DS / 16; ++s) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 a = *(const bf16x8*)&Ss[((32 * mt + l32) >> lb) * XP + 16 * s + 8 * hh];
+          const bf16x8 a = *(const bf16x8*)&Ss[((32 * mt + prow) >> lb) * XP + 16 * s + 8 * hh];
           sacc[mt] = mfma32(a, qsf[s], sacc[mt]);
         }
       }
@@ -227,7 +233,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
         for (int r = 0; r < 16; ++r) {
           const float zb = fmaf(sacc[mt][r], zsc, zoff);
           if constexpr (MASK) {
-            const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
+            const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 2 * (r % 4) + hh;
             sacc[mt][r] = u < tcur0 ? zb : 0.f;
           } else {
             sacc[mt][r] = zb;  // every key of a tile before the wave's first block is historical
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a = *(const bf16x8*)&Ks[(32 * mt + l32) * KP + 16 * s + 8 * hh];
+        const bf16x8 a = *(const bf16x8*)&Ks[(32 * mt + prow) * KP + 16 * s + 8 * hh];
         sacc[mt] = mfma32(a, qf[s], sacc[mt]);
       }
     }
@@ -252,11 +258,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if constexpr (MASK) {
-          const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 4 * hh + (r % 4);
+          const int u = j * kBlock + 32 * mt + (r / 4) * 8 + 2 * (r % 4) + hh;
           if (u > t) sacc[mt][r] = -INFINITY;
         }
         if constexpr (UB > 1) {
-          // unit of key 32 mt + 8 (r / 4) + 4 hh + r % 4 within the tile
+          // unit of key 32 mt + 8 (r / 4) + 2 (r % 4) + hh within the tile
           const int ub = UB == 2 ? mt : 2 * mt + r / 8;
           sacc[mt][r] = fmaf(sacc[mt][r], c1, bias2[ub]);
         }
@@ -290,8 +296,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
     }
     l_run += psum;
   };
-  // O^T += V^T P^T: the B slots of a lane are keys 16 pp + 4 hh + (0..3, 8..11)
-  // of M-tile mt, and the transposing reads give V^T in the same key order
+  // O^T += V^T P^T: the B slots of a lane are keys 16 pp + hh + 2 (0..3) and
+  // 16 pp + 8 + hh + 2 (0..3) of M-tile mt (accumulator rows 16 pp + 4 hh +
+  // (0..3, 8..11)), and the transposing reads give V^T in the same key order
   auto pv = [&](const bf16* Vs) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
