@@ -4,8 +4,9 @@ filled with a sentinel byte; after the call (through the C ABI) the bands
 must be untouched, the inputs unchanged and the outputs equal to those of the
 same call on exactly sized buffers.  Shapes are ragged where stray stores
 would land: a last query tile of 8 rows (tq 520), query offsets that are not
-multiples of 64 (56, 248), d 64, 4-token units in f32, and paged sequences of
-1, 65 and 128 tokens.
+multiples of 64 (56, 248), d 64, 4-token units in f32, 1- and 2-token units
+in the bf16 training kernels, and paged sequences of 1, 65 and 128 tokens;
+the fused selection + decode calls too.
 """
 
 from __future__ import annotations
@@ -79,6 +80,10 @@ DENSE = {
                                                    tk=448, d=64, ds=16, topk=2),
     "f32_b4_tq100": synth.WORKLOADS["tiny_fp32"].with_(name="g4", batch=1, hq=2, hkv=1, tq=100,
                                                        tk=192, block=4, topk=6),
+    "tok_b1_tq520_off56": synth.WORKLOADS["train_8k"].with_(name="g5", batch=1, hq=4, hkv=2,
+                                                            tq=520, tk=576, block=1, topk=5),
+    "tok_b2_tq200_off248": synth.WORKLOADS["train_8k"].with_(name="g6", batch=1, hq=8, hkv=2,
+                                                             tq=200, tk=448, block=2, topk=4),
 }
 
 
@@ -101,6 +106,8 @@ def test_guard_bands_dense_paths(name):
                                          block=w.block, renorm=1)
     os_, ls_ = ops.sparse_fwd(dev["q"], dev["k"], dev["v"], idx, bias, block=w.block)
     rp, col, tb = ops.threshold_blocks(dev["qs"], dev["ks"], 0.02, w.tk, block=w.block)
+    of, lf, fi, fb = ops.topk_decode(dev["q"], dev["k"], dev["v"], dev["qs"], dev["ks"], w.topk,
+                                     block=w.block)
     torch.cuda.synchronize()
 
     # gate
@@ -142,6 +149,13 @@ def test_guard_bands_dense_paths(name):
                               _p(idx), _p(bias), G["o"].ptr, G["lse"].ptr, G["ws"].ptr,
                               ctypes.byref(n), st) == 0
     _check_all(G, {"o": os_, "lse": ls_}, keep, dev)
+    # selection and decode in one launch (every row of the call)
+    G = {"o": guarded_like(of), "lse": guarded_like(lf), "idx": guarded_like(fi),
+         "bias": guarded_like(fb)}
+    assert lib.sas_topk_decode(ctypes.byref(sh), w.topk, 0, _p(dev["q"]), _p(dev["k"]),
+                               _p(dev["v"]), _p(dev["qs"]), _p(dev["ks"]), G["idx"].ptr,
+                               G["bias"].ptr, G["o"].ptr, G["lse"].ptr, st) == 0
+    _check_all(G, {"o": of, "lse": lf, "idx": fi, "bias": fb}, keep, dev)
     # threshold count / fill and the CSR forward (64-token units, bf16 only)
     nnz = int(col.numel())
     if w.block == 64 and w.dtype == "bf16":
@@ -184,7 +198,16 @@ def test_guard_bands_paged():
     idx, bias = ops.paged_topk(d["qs"], d["ks_pool"], d["block_table"], d["seq_len"], pw.topk)
     o, lse = ops.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_len"],
                               idx, bias)
+    of, lf, fi, fb = ops.paged_topk_decode(d["q"], d["k_pool"], d["v_pool"], d["qs"],
+                                           d["ks_pool"], d["block_table"], d["seq_len"], pw.topk)
     torch.cuda.synchronize()
+    G = {"o": guarded_like(of), "lse": guarded_like(lf), "idx": guarded_like(fi),
+         "bias": guarded_like(fb)}
+    assert lib.sas_paged_topk_decode(ctypes.byref(sh), pw.topk, 0, _p(d["seq_len"]),
+                                     _p(d["block_table"]), _p(d["q"]), _p(d["k_pool"]),
+                                     _p(d["v_pool"]), _p(d["qs"]), _p(d["ks_pool"]), G["idx"].ptr,
+                                     G["bias"].ptr, G["o"].ptr, G["lse"].ptr, st) == 0
+    _check_all(G, {"o": of, "lse": lf, "idx": fi, "bias": fb}, keep, d)
     G = {"idx": guarded_like(idx), "bias": guarded_like(bias)}
     assert lib.sas_paged_topk(ctypes.byref(sh), pw.topk, 0, _p(d["seq_len"]),
                               _p(d["block_table"]), _p(d["qs"]), _p(d["ks_pool"]), G["idx"].ptr,
