@@ -90,7 +90,8 @@ def test_gate_and_fwd_full_size_sampled(name):
 
 
 @pytest.mark.parametrize("renorm", [0, 1])
-@pytest.mark.parametrize("tq,tk,K", [(1088, 1088, 5), (1, 4096, 8), (200, 2048, 40)])
+@pytest.mark.parametrize("tq,tk,K", [(1088, 1088, 5), (1, 4096, 8), (200, 2048, 40),
+                                     (1, 64 * 16200, 20)])
 def test_topk_small(renorm, tq, tk, K):
     w = W["prefill_32k_top16"].with_(batch=2, hq=8, hkv=2, tq=tq, tk=tk, topk=K)
     say("topk", tq, tk, K, renorm)
@@ -122,7 +123,11 @@ EXACT_TIE_CASES = [
     (1088, 4096, 12, 0.0, "lane, 16-entry list"),
     (1088, 4096, 24, 0.0, "lane, 32-entry list"),
     (200, 8192, 40, 0.0, "radix select"),
-    (1, 4096, 8, 0.0, "wave per row"),
+    (1, 4096, 8, 0.0, "wave per row, list merge, 8 entries"),
+    (1, 4096, 12, 0.0, "wave per row, list merge, 16 entries"),
+    # K > 16 with a history too long for the radix select's LDS (16200 blocks):
+    # the wave kernel's argmax rounds
+    (1, 64 * 16200, 20, 0.0, "wave per row, argmax rounds"),
     (640, 4096, 64, 0.25, "budgeted radix select"),
 ]
 
