@@ -612,7 +612,7 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) dlt = fmaf(to_f32(df[s][e]), to_f32(of[e]), dlt);
   }
-  dlt += __shfl_xor(dlt, 32);
+  dlt = halves_sum(dlt);
   // Row data for the dK/dV kernel, unit-major so that the rows of one unit
   // are contiguous: slot u < nb holds, for each row, the log2-domain offset
   // of unit u's logits (gate bias minus the row's log-sum-exp; -inf past the
@@ -720,18 +720,18 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
         } else if (bsz == 2) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v = er[i] + __shfl_xor(er[i], 32);
+            const float v = halves_sum(er[i]);
             if (ok && hh == 0 && k0 + 2 * i < tcur0) zr[(k0 + 2 * i) >> 1] = v;
           }
         } else if (bsz == 4) {
           float v0 = er[0] + er[1], v1 = er[2] + er[3];
-          v0 += __shfl_xor(v0, 32);
-          v1 += __shfl_xor(v1, 32);
+          v0 = halves_sum(v0);
+          v1 = halves_sum(v1);
           if (ok && hh == 0 && k0 < tcur0) zr[k0 >> 2] = v0;
           if (ok && hh == 0 && k0 + 4 < tcur0) zr[(k0 >> 2) + 1] = v1;
         } else {
           float v = er[0] + er[1] + er[2] + er[3];
-          v += __shfl_xor(v, 32);
+          v = halves_sum(v);
           if (ok && hh == 0 && k0 < tcur0) zr[k0 >> 3] = v;
         }
       }
@@ -764,7 +764,7 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
 #pragma unroll
         for (int e = 0; e < DS / 4; ++e)
           part = __builtin_amdgcn_fdot2_f32_bf16(qsv[e], kr[e], part, false);
-        part += __shfl_xor(part, 32);
+        part = halves_sum(part);
         if (j * UB + ub < c) bias2[ub] = (D.sel_scale * part - lam_t) * kLog2e;
       }
     }
@@ -844,7 +844,7 @@ __global__ __launch_bounds__(kDq32Threads, 1) void bwd_dq32_kernel(
       }
     }
 #pragma unroll
-    for (int ub = 0; ub < NU; ++ub) dsum[ub] += __shfl_xor(dsum[ub], 32);
+    for (int ub = 0; ub < NU; ++ub) dsum[ub] = halves_sum(dsum[ub]);
     // the row's own tile comes first (tiles run from the diagonal down): its
     // current unit gives sum_{j'<c} dbeta before any historical unit
     if (j == ct) {

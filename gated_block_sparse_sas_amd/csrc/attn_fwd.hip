@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
 #pragma unroll
         for (int e = 0; e < DS / 4; ++e)
           part = __builtin_amdgcn_fdot2_f32_bf16(qsv[e], kr[e], part, false);
-        part += __shfl_xor(part, 32);
+        part = halves_sum(part);
         if (j * UB + ub < c) bias2[ub] = (D.sel_scale * part - lam_t) * kLog2e;
       }
     }
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
         mx = fmaxf(mx, sacc[mt][r]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     if constexpr (UB <= 1) mx = fmaf(mx, c1, bias2[0]);
     // Lazy rescaling: the running max only moves when it grows by more than
     // 8 (log2 units) in some row of the wave, so P <= 2^8 between updates.
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_kernel(
   else
     loop(std::integral_constant<int, 1>{});
 
-  l_run += __shfl_xor(l_run, 32);
+  l_run = halves_sum(l_run);
   if (qi < D.tq) {
     const float inv = 1.f / l_run;
     bf16* orow = o + qrow * HD;

@@ -96,8 +96,26 @@ __device__ __forceinline__ float sum8_dpp(float x) {
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // 2^x with the hardware exponential (v_exp_f32): no range reduction, so
-// arguments below -126 give 0 or denormals; used on softmax exponents <= 8.
+// arguments below -126 give 0 or denormals; used on softmax exponents of at
+// most 16 (the forward's running max lags the true one by less than that).
 __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum / max of x over lanes l and l ^ 32 (the two 32-lane halves of a wave),
+// every lane receiving it.  v_permlane32_swap trades lanes 32..63 of its first
+// register with lanes 0..31 of its second; with x in both, one result holds
+// the low half's x in every lane and the other the high half's, so the
+// exchange needs no LDS round trip (as a lane shuffle would).  The whole wave
+// must be active.
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

@@ -157,9 +157,10 @@ def check_train(w, f, lam, o, lse, g, S):
     _, lam_ref, beta_ref = oracle.gate_scores(S, f["qs"], f["ks"])
     fin = np.isfinite(lam_ref)
     assert np.array_equal(np.isneginf(host(lam)), np.isneginf(lam_ref))
-    e = max_abs(host(lam)[fin], lam_ref[fin])
-    say("  lam max-abs %.2e" % e)
-    assert e <= 1e-4 * max(1.0, float(np.max(np.abs(lam_ref[fin]))))
+    if fin.any():  # (no row has a historical unit when tq <= the unit)
+        e = max_abs(host(lam)[fin], lam_ref[fin])
+        say("  lam max-abs %.2e" % e)
+        assert e <= 1e-4 * max(1.0, float(np.max(np.abs(lam_ref[fin]))))
     o_ref, l_ref = oracle.attn_fwd(S, f["q"], f["k"], f["v"], f["qs"], f["ks"])
     eo, el = max_abs(host(o), o_ref), max_abs(host(lse), l_ref)
     say("  O max-abs %.2e  lse max-abs %.2e" % (eo, el))
