@@ -134,7 +134,7 @@ __global__ __launch_bounds__(512) void gate_lse_mfma_kernel(const bf16* __restri
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, z[mt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * zs;
+      mx = halves_max(mx) * zs;
       if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
         if (m_new > -INFINITY) {
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(512) void gate_lse_mfma_kernel(const bf16* __restri
     if (j + 1 < ntiles) sstore((j & 1) ? X0 : X1);
     __syncthreads();
   }
-  s_run += __shfl_xor(s_run, 32);
+  s_run = halves_sum(s_run);
   if (qi < D.tq && hh == 0) lam[row] = c == 0 ? -INFINITY : (m_run + log2f(s_run)) * kLn2;
 }
 

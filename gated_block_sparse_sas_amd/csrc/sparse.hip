@@ -579,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
         if (u > tmax || u < ulo || u >= ulo + B) sacc[mt][r] = -INFINITY;  // causal, unit
         mx = fmaxf(mx, sacc[mt][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     const float m2 = fmaf(mx, c1, bias2);  // row max in log2 units (-inf only if bias is -inf)
     const float off = bias2 - (m2 == -INFINITY ? 0.f : m2);
     float l = 0.f;
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256, 2) void sp_partial_kernel(
         sacc[mt][r] = pv;
         l += pv;
       }
-    l += __shfl_xor(l, 32);
+    l = halves_sum(l);
     f32x16 oacc[DM];
 #pragma unroll
     for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
