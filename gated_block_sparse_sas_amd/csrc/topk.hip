@@ -247,6 +247,102 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const ST* __restrict__ 
 // the n_t winners are then sorted (bitonic network in LDS) by key
 // descending, block ascending — the same order as the other kernels.
 
+// Register bitonic sort of a row's winners.  The value of lane l at a
+// compare-exchange of lane distance S (partner l ^ S), without an LDS round
+// trip: DPP quad permutes (S = 1, 2), row shifts up and down by S (4, 8: the
+// row of 16 lanes holds both), and the swaps of 16-lane rows and 32-lane
+// halves (v_permlane16_swap / v_permlane32_swap with both operands x: one
+// result holds the even row (lower half) in each pair of rows, the other the
+// odd one).  The whole wave must be active.
+template <int S>
+__device__ __forceinline__ unsigned lane_xor(unsigned x, int lane) {
+  if constexpr (S == 1) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (S == 2) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (S == 4 || S == 8) {
+    const unsigned up = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x100 + S, 0xF, 0xF, true);
+    const unsigned dn = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x110 + S, 0xF, 0xF, true);
+    return (lane & S) ? dn : up;  // lane + S below, lane - S above
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(S == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+// One bitonic step at lane distance S over the E keys of each lane (key e of
+// lane l is element x = 64 e + l): x keeps the larger of itself and x ^ S
+// when x is the lower of the two in a block sorted descending ((x & size) ==
+// 0), or the higher in an ascending one; else the smaller.
+template <int S, int E>
+__device__ __forceinline__ void bitonic_lanes(unsigned long long (&v)[E], int lane, int size) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const unsigned lo = lane_xor<S>((unsigned)v[e], lane);
+    const unsigned hi = lane_xor<S>((unsigned)(v[e] >> 32), lane);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    const int x = 64 * e + lane;
+    const bool keep_max = ((x & S) == 0) == ((x & size) == 0);
+    v[e] = (keep_max ? o > v[e] : o < v[e]) ? o : v[e];
+  }
+}
+
+// Sorts the n winners sk / sj [0, n) into selection order (z descending,
+// block ascending), p2 = the power of two >= n, p2 <= 64 E: 64-bit keys
+// (ord_key << 32 | ~block) held E per lane, padding 0 (below every real
+// key); sj [0, n) gets the sorted blocks back.
+template <int E>
+__device__ __forceinline__ void sort_winners(const unsigned* sk, int* sj, int n, int p2, int lane) {
+  unsigned long long v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int x = 64 * e + lane;
+    v[e] = x < n ? ((unsigned long long)sk[x] << 32) | (unsigned)~sj[x] : 0ull;
+  }
+  for (int size = 2; size <= p2; size <<= 1) {
+    // distances of 64 elements and more: within the lane
+    if constexpr (E >= 4) {
+      if (size >= 256) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bool desc = ((64 * e + lane) & size) == 0;
+          const bool sw = desc ? v[e + 2] > v[e] : v[e + 2] < v[e];
+          const unsigned long long a = v[e], b = v[e + 2];
+          v[e] = sw ? b : a;
+          v[e + 2] = sw ? a : b;
+        }
+      }
+    }
+    if constexpr (E >= 2) {
+      if (size >= 128) {
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          const bool desc = ((64 * e + lane) & size) == 0;
+          const bool sw = desc ? v[e + 1] > v[e] : v[e + 1] < v[e];
+          const unsigned long long a = v[e], b = v[e + 1];
+          v[e] = sw ? b : a;
+          v[e + 1] = sw ? a : b;
+        }
+      }
+    }
+    if (size > 32) bitonic_lanes<32>(v, lane, size);
+    if (size > 16) bitonic_lanes<16>(v, lane, size);
+    if (size > 8) bitonic_lanes<8>(v, lane, size);
+    if (size > 4) bitonic_lanes<4>(v, lane, size);
+    if (size > 2) bitonic_lanes<2>(v, lane, size);
+    bitonic_lanes<1>(v, lane, size);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int x = 64 * e + lane;
+    if (x < n) sj[x] = (int)~(unsigned)v[e];
+  }
+}
+
 template <int DS, typename ST>
 __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__ qs,
                                                           const ST* __restrict__ ks, int kmax,
@@ -357,9 +453,17 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
     cnt_sel += __popcll(bs);
     ties_left -= min(ties_left, __popcll(bt));
   }
-  // bitonic sort of the n winners (padded to a power of two with the worst key)
+  // bitonic sort of the n winners (padded to a power of two with the worst
+  // key): in registers up to 256 of them, in LDS beyond
   int p2 = 1;
   while (p2 < n) p2 <<= 1;
+  if (p2 <= 64) {
+    sort_winners<1>(sk, sj, n, p2, lane);
+  } else if (p2 == 128) {
+    sort_winners<2>(sk, sj, n, p2, lane);
+  } else if (p2 == 256) {
+    sort_winners<4>(sk, sj, n, p2, lane);
+  } else {
   for (int x = n + lane; x < p2; x += 64) {
     sk[x] = 0u;
     sj[x] = 0x7fffffff;
@@ -380,6 +484,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
         }
       }
     }
+  }
   }
   // outputs
   float norm = lam;
