@@ -117,16 +117,100 @@ __device__ __forceinline__ float halves_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+// Reductions over aligned groups of N lanes (N = 2, 4, ..., 64), every lane
+// of a group receiving the result, with no LDS round trip: DPP quad
+// permutes (neighbours, then pairs), DPP mirrors within 8 and within 16
+// lanes (once the quads are reduced, a lane's mirror holds the other half's
+// value), then the swaps of 16-lane rows and of the wave halves.  Each step
+// combines a lane's value with its partner's, the same two numbers on both
+// lanes, so every lane of a group ends with the same bits.  The whole wave
+// must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int N, bool MAX>
+__device__ __forceinline__ float group_reduce(float x) {
+  static_assert(N >= 2 && N <= 64 && (N & (N - 1)) == 0, "group of 2 .. 64 lanes");
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  x = op(x, dpp_f<0xB1>(x));                         // lane ^ 1
+  if constexpr (N >= 4) x = op(x, dpp_f<0x4E>(x));   // lane ^ 2
+  if constexpr (N >= 8) x = op(x, dpp_f<0x141>(x));  // mirror within 8
+  if constexpr (N >= 16) x = op(x, dpp_f<0x140>(x)); // mirror within 16
+  if constexpr (N >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if constexpr (N >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
   return x;
 }
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+template <int N>
+__device__ __forceinline__ float group_sum(float x) { return group_reduce<N, false>(x); }
+template <int N>
+__device__ __forceinline__ float group_max(float x) { return group_reduce<N, true>(x); }
+
+// Sum of x over the lanes that share lane % G (G = 8, 16 or 32): lanes l ^ G,
+// l ^ 2 G, ...; distance 8 by DPP row shifts (up and down by 8 within a row
+// of 16), 16 and 32 by the row and half swaps.  Same bits in every lane of a
+// set; the whole wave must be active.
+template <int G>
+__device__ __forceinline__ float stride_sum(float x) {
+  static_assert(G == 8 || G == 16 || G == 32, "stride of 8, 16 or 32 lanes");
+  if constexpr (G == 8) {
+    const int lane = __lane_id();
+    const float up = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x108, 0xF, 0xF, true));
+    const float dn = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x118, 0xF, 0xF, true));
+    x = (lane & 8) ? dn + x : x + up;  // (the lower lane's value first on both)
+  }
+  if constexpr (G <= 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+// The value of lane l ^ S (S = 1, 2, ..., 32) for lane l, without an LDS
+// round trip: DPP quad permutes (S = 1, 2), row shifts up and down by S
+// (4, 8: the row of 16 lanes holds both), and the swaps of 16-lane rows and
+// 32-lane halves (v_permlane16_swap / v_permlane32_swap with both operands x:
+// one result holds the even row (lower half) of each pair, the other the odd
+// one).  The whole wave must be active.
+template <int S>
+__device__ __forceinline__ unsigned lane_xor(unsigned x, int lane) {
+  if constexpr (S == 1) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (S == 2) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (S == 4 || S == 8) {
+    const unsigned up = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x100 + S, 0xF, 0xF, true);
+    const unsigned dn = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x110 + S, 0xF, 0xF, true);
+    return (lane & S) ? dn : up;  // lane + S below, lane - S above
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(S == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+template <int S>
+__device__ __forceinline__ unsigned long long lane_xor_u64(unsigned long long v, int lane) {
+  const unsigned lo = lane_xor<S>((unsigned)v, lane), hi = lane_xor<S>((unsigned)(v >> 32), lane);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Whole-wave max / sum, every lane receiving it (group_reduce over 64 lanes).
+__device__ __forceinline__ float wave_max(float x) { return group_max<64>(x); }
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 
 // Selector score dot product <qs, ks> over ds elements, accumulated in fp32
 // in index order with fused multiply-adds.

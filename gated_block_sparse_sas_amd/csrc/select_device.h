@@ -63,11 +63,6 @@ __device__ __forceinline__ void ce_desc(unsigned long long& a, unsigned long lon
   b = lo;
 }
 
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o) {
-  const unsigned lo = __shfl_xor((unsigned)v, o), hi = __shfl_xor((unsigned)(v >> 32), o);
-  return ((unsigned long long)hi << 32) | lo;
-}
-
 // The best KM blocks of one query row by one wavefront (few rows: decode,
 // paged decode, small calls) among blocks first, first + stride, ... below
 // c(t) (a wave alone: first = lane, stride = 64; W waves of a row: first =
@@ -92,6 +87,15 @@ __device__ __forceinline__ void merge_desc(unsigned long long (&tk)[KM],
 #pragma unroll
     for (int r = 0; r < KM; ++r)
       if ((r & st) == 0) ce_desc(tk[r], tk[r + st]);
+}
+
+// One butterfly step: lane l merges its list with lane l ^ O's.
+template <int O, int KM>
+__device__ __forceinline__ void merge_lanes(unsigned long long (&tk)[KM], int lane) {
+  unsigned long long p[KM];
+#pragma unroll
+  for (int r = 0; r < KM; ++r) p[r] = lane_xor_u64<O>(tk[r], lane);
+  merge_desc<KM>(tk, p);
 }
 
 template <int DS, typename ST, typename Sel, int KM>
@@ -148,14 +152,14 @@ __device__ __forceinline__ void wave_best(const ST* __restrict__ qs, const Sel& 
       for (int r = 0; r < KM; ++r)
         if ((r & st) == 0) ce_desc(tk[r], tk[r + st]);
   }
-  // merge the wave's 64 lists
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    unsigned long long p[KM];
-#pragma unroll
-    for (int r = 0; r < KM; ++r) p[r] = shfl_xor_u64(tk[r], o);
-    merge_desc<KM>(tk, p);
-  }
+  // merge the wave's 64 lists (partners by register exchanges)
+  const int lane = __lane_id();
+  merge_lanes<1, KM>(tk, lane);
+  merge_lanes<2, KM>(tk, lane);
+  merge_lanes<4, KM>(tk, lane);
+  merge_lanes<8, KM>(tk, lane);
+  merge_lanes<16, KM>(tk, lane);
+  merge_lanes<32, KM>(tk, lane);
   *m_out = m;
   *s_out = s;
 }

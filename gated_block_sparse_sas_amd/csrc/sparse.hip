@@ -148,18 +148,17 @@ __device__ __forceinline__ void attend_row(const T* __restrict__ q, const Src& S
 #pragma unroll
         for (int e = 0; e < EPL; ++e) a = fmaf(qv[e], to_f32(x[e]), a);
       }
-#pragma unroll
-      for (int of = 1; of < LPK; of <<= 1) a += __shfl_xor(a, of);
+      a = group_sum<LPK>(a);
       if (lane % LPK == 0 && u < B) pw[u] = (j * B + u > t) ? -INFINITY : a * D.sm_scale + add;
     }
     __builtin_amdgcn_wave_barrier();
     const float sc = lane < B ? pw[lane] : -INFINITY;
-    const float ms = wave_max(sc);
+    const float ms = group_max<64>(sc);
     if (ms == -INFINITY) continue;  // every key masked (a bias of -inf)
     const float m_new = fmaxf(m_w, ms);
     const float alpha = exp2f((m_w - m_new) * kLog2e);
     const float pl = exp2f((sc - m_new) * kLog2e);
-    l_w = l_w * alpha + wave_sum(pl);
+    l_w = l_w * alpha + group_sum<64>(pl);
     m_w = m_new;
     __builtin_amdgcn_wave_barrier();
     if (lane < B) pw[lane] = pl;
@@ -179,9 +178,7 @@ __device__ __forceinline__ void attend_row(const T* __restrict__ q, const Src& S
   }
   // sum this wave's P V over its key groups, then merge the waves
 #pragma unroll
-  for (int of = LPK; of < 64; of <<= 1)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], of);
+  for (int e = 0; e < EPL; ++e) acc[e] = stride_sum<LPK>(acc[e]);
   if (lane < LPK) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) L.ow[wave][d0 + e] = acc[e];
@@ -688,11 +685,11 @@ __global__ __launch_bounds__(256) void sp_merge_kernel(Src S, const int* __restr
     const float lx = ok ? plse[px] * kLog2e : -INFINITY;
     const unsigned long long bal = __ballot(ok);
     if (bal == 0) continue;
-    const float m_new = fmaxf(m, wave_max(lx));
+    const float m_new = fmaxf(m, group_max<64>(lx));
     const float alpha = exp2_raw(m - m_new);
     m = m_new;
     const float pw = ok ? exp2_raw(lx - m) : 0.f;
-    sm = sm * alpha + wave_sum(pw);
+    sm = sm * alpha + group_sum<64>(pw);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= alpha;
     const int nval = 64 - __builtin_clzll(bal);  // slots past the last valid one are skipped
@@ -707,9 +704,7 @@ __global__ __launch_bounds__(256) void sp_merge_kernel(Src S, const int* __restr
     }
   }
 #pragma unroll
-  for (int of = LPP; of < 64; of <<= 1)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], of);
+  for (int e = 0; e < 8; ++e) acc[e] = stride_sum<LPP>(acc[e]);
   if (grp == 0) {
     const float inv_s = 1.f / sm;
     bf16x8 ov;

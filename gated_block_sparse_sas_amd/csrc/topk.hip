@@ -247,33 +247,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const ST* __restrict__ 
 // the n_t winners are then sorted (bitonic network in LDS) by key
 // descending, block ascending — the same order as the other kernels.
 
-// Register bitonic sort of a row's winners.  The value of lane l at a
-// compare-exchange of lane distance S (partner l ^ S), without an LDS round
-// trip: DPP quad permutes (S = 1, 2), row shifts up and down by S (4, 8: the
-// row of 16 lanes holds both), and the swaps of 16-lane rows and 32-lane
-// halves (v_permlane16_swap / v_permlane32_swap with both operands x: one
-// result holds the even row (lower half) in each pair of rows, the other the
-// odd one).  The whole wave must be active.
-template <int S>
-__device__ __forceinline__ unsigned lane_xor(unsigned x, int lane) {
-  if constexpr (S == 1) {
-    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
-  } else if constexpr (S == 2) {
-    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
-  } else if constexpr (S == 4 || S == 8) {
-    const unsigned up = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x100 + S, 0xF, 0xF, true);
-    const unsigned dn = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x110 + S, 0xF, 0xF, true);
-    return (lane & S) ? dn : up;  // lane + S below, lane - S above
-  } else if constexpr (S == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return (lane & 16) ? r[0] : r[1];
-  } else {
-    static_assert(S == 32, "lane distance");
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (lane & 32) ? r[0] : r[1];
-  }
-}
-
+// Register bitonic sort of a row's winners (partners by lane_xor).
 // One bitonic step at lane distance S over the E keys of each lane (key e of
 // lane l is element x = 64 e + l): x keeps the larger of itself and x ^ S
 // when x is the lower of the two in a block sorted descending ((x & size) ==
