@@ -63,6 +63,15 @@ def build(verbose: bool = False, jobs: int = 8, out: str = LIB, build_dir: str =
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    # A kernel whose host-side launch stub the compiler dropped leaves an
+    # undefined __device_stub__ symbol that only fails when the library
+    # registers its kernels on a GPU: refuse such a build here.
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    r = subprocess.run([nm, "-u", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the build: %s" % ", ".join(missing))
     os.replace(tmp, out)
     return out
 
