@@ -44,9 +44,8 @@ struct PagedSel {
 // +0, as in a floating-point comparison), and the selection order on (key,
 // block): key descending, then block ascending.
 __device__ __forceinline__ unsigned ord_key(float z) {
-  unsigned u = __float_as_uint(z);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const unsigned u = __float_as_uint(z + 0.0f);  // -0 + 0 = +0
+  return u ^ ((unsigned)((int)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key_value(unsigned k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
@@ -57,10 +56,14 @@ __device__ __forceinline__ bool key_before(unsigned ka, int ja, unsigned kb, int
 
 // Compare-exchange of two selection keys into descending order.
 __device__ __forceinline__ void ce_desc(unsigned long long& a, unsigned long long& b) {
-  const bool sw = b > a;
-  const unsigned long long hi = sw ? b : a, lo = sw ? a : b;
+  const unsigned long long hi = b > a ? b : a;
+  // the other one, a ^ b ^ hi: a three-input XOR (v_bitop3, table 0x96) per
+  // half, where a second 64-bit comparison would cost one more instruction
+  const unsigned lo0 = __builtin_amdgcn_bitop3_b32((unsigned)a, (unsigned)b, (unsigned)hi, 0x96);
+  const unsigned lo1 = __builtin_amdgcn_bitop3_b32((unsigned)(a >> 32), (unsigned)(b >> 32),
+                                                   (unsigned)(hi >> 32), 0x96);
+  b = ((unsigned long long)lo1 << 32) | lo0;
   a = hi;
-  b = lo;
 }
 
 // The best KM blocks of one query row by one wavefront (few rows: decode,

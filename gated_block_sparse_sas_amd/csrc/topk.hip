@@ -121,23 +121,142 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const ST* __restrict__ q
 }
 
 // Lane-per-row variant for many rows and K <= 32: the 64 rows of a wave are
-// consecutive positions of one (batch, head), so every ks row is a
-// wave-uniform load.  Each lane keeps its best KMAX (>= K) blocks in
-// registers as 64-bit keys (ord_key of z above, the complement of the block
-// below), so that one unsigned comparison gives the selection order (z
-// descending, block ascending) and no two candidates tie.  Candidates come in
-// batches of 8: the batch is sorted by a 19-comparator network, each of the
-// last 8 list entries keeps the larger of itself and its mirror in the batch
-// (the list then holds the best KMAX of both, in bitonic order), and a
-// bitonic merge sorts it again; every step is branch-free, so the lanes of a
-// wave never wait on each other's insertions.  Scores use the same SelQ dot
-// product.
+// consecutive positions of one (batch, head) and share the ks rows they
+// score.  Each lane keeps its best KMAX (>= K) blocks in registers as 64-bit
+// keys (ord_key of z above, the complement of the block below), so that one
+// unsigned comparison gives the selection order (z descending, block
+// ascending) and no two candidates tie.  Candidates come 16 at a time and
+// are folded in batches of 8: the batch is sorted by a 19-comparator
+// network, each of the last 8 list entries keeps the larger of itself and
+// its mirror in the batch (the list then holds the best KMAX of both, in
+// bitonic order), and a bitonic merge sorts it again; every step is
+// branch-free, so the lanes of a wave never wait on each other's insertions.
+//
+// Scores.  bf16 selectors: the wave's 64 x 16 score tile is a small matrix
+// product on the matrix cores (lane_tile_scores below: exact bf16 products,
+// fp32 sums in the MFMA's order, so a score may differ in its last bits from
+// the packed-dot SelQ score of the other kernels; equal selector vectors
+// still give equal scores, and the order on ties is unchanged).  f32
+// selectors: SelQ, lane by lane.
+template <int DS>
+struct LaneTile {
+  static constexpr int NK = (DS + 31) / 32;  // 16x16x32 products per 16 rows
+  bf16x8 qb[4][NK];                          // B operands: rows 16 r + lane % 16
+
+  // qs rows first .. first + 63 of the (batch, head) whose rows start at q0
+  // (rows past tq - 1 repeat it).  16x16x32 operand layout: lane l holds
+  // row / column l % 16 and k = 8 (l / 16) .. + 7 of each 32-wide k slice.
+  __device__ __forceinline__ void load(const bf16* q0, int first, int tq, int lane) {
+    const int kg = 8 * (lane >> 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bf16* p = q0 + (size_t)min(first + 16 * r + (lane & 15), tq - 1) * DS;
+#pragma unroll
+      for (int s = 0; s < NK; ++s)
+        qb[r][s] = 32 * s + kg < DS ? *(const bf16x8*)(p + 32 * s + kg) : bf16x8{};
+    }
+  }
+
+  // Unscaled scores of blocks j0 .. j0 + 15 (rows of ksb past nb - 1 repeat
+  // it) for this lane's row: z[4 g + v] for block j0 + 4 g + v.  Product r
+  // leaves lane l with row 16 r + l % 16, blocks j0 + 4 (l / 16) + v; the 4 x 4
+  // transpose of (product, 16-lane row) that gives lane l its own row is two
+  // rounds of register swaps, v_permlane32_swap (rows g, g ^ 2) and then
+  // v_permlane16_swap (rows g, g ^ 1).  The whole wave must be active.
+  __device__ __forceinline__ void score(const bf16* ksb, int j0, int nb, int lane,
+                                        float (&z)[16]) const {
+    const int kg = 8 * (lane >> 4);
+    const bf16* kp = ksb + (size_t)min(j0 + (lane & 15), nb - 1) * DS;
+    bf16x8 a[NK];
+#pragma unroll
+    for (int s = 0; s < NK; ++s)
+      a[s] = 32 * s + kg < DS ? *(const bf16x8*)(kp + 32 * s + kg) : bf16x8{};
+    f32x4 t[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      t[r] = mfma16(a[0], qb[r][0], f32x4{});
+#pragma unroll
+      for (int s = 1; s < NK; ++s) t[r] = mfma16(a[s], qb[r][s], t[r]);
+    }
+    unsigned u[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) u[r][v] = __float_as_uint(t[r][v]);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const auto x = __builtin_amdgcn_permlane32_swap(u[r][v], u[r + 2][v], false, false);
+        u[r][v] = x[0];
+        u[r + 2][v] = x[1];
+      }
+#pragma unroll
+    for (int r = 0; r < 4; r += 2)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const auto x = __builtin_amdgcn_permlane16_swap(u[r][v], u[r + 1][v], false, false);
+        u[r][v] = x[0];
+        u[r + 1][v] = x[1];
+      }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) z[4 * g + v] = __uint_as_float(u[g][v]);
+  }
+};
+
+// One batch of 8 scores zz (blocks j0 .. j0 + 7, -inf at or after c) into
+// the running log-sum-exp (log2 domain: m, s) and the list tk.
+template <int KMAX>
+__device__ __forceinline__ void lane_fold8(const float (&zz)[8], int j0, float& m,
+                                           float& s, unsigned long long (&tk)[KMAX]) {
+  float mc = zz[0];
+#pragma unroll
+  for (int kk = 1; kk < 8; ++kk) mc = fmaxf(mc, zz[kk]);
+  const float mn = fmaxf(m, mc * kLog2e);
+  if (mn != -INFINITY) {
+    float acc = s * exp2_raw(m - mn);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) acc += exp2_raw(zz[kk] * kLog2e - mn);
+    s = acc;
+    m = mn;
+  }
+  // the batch as keys, sorted.  Blocks at or after c score -inf, whose key
+  // lies below that of every finite score: they fill only list entries at or
+  // past c, which are never output.
+  unsigned long long bk[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    bk[kk] = ((unsigned long long)ord_key(zz[kk]) << 32) | (unsigned)~(j0 + kk);
+  ce_desc(bk[0], bk[2]); ce_desc(bk[1], bk[3]); ce_desc(bk[4], bk[6]); ce_desc(bk[5], bk[7]);
+  ce_desc(bk[0], bk[4]); ce_desc(bk[1], bk[5]); ce_desc(bk[2], bk[6]); ce_desc(bk[3], bk[7]);
+  ce_desc(bk[0], bk[1]); ce_desc(bk[2], bk[3]); ce_desc(bk[4], bk[5]); ce_desc(bk[6], bk[7]);
+  ce_desc(bk[2], bk[4]); ce_desc(bk[3], bk[5]);
+  ce_desc(bk[1], bk[4]); ce_desc(bk[3], bk[6]);
+  ce_desc(bk[1], bk[2]); ce_desc(bk[3], bk[4]); ce_desc(bk[5], bk[6]);
+  // best KMAX of list and batch: the list descends, the mirrored batch
+  // ascends, their larger elements form a bitonic sequence
+#pragma unroll
+  for (int r = KMAX - 8; r < KMAX; ++r) {
+    const unsigned long long o = bk[KMAX - 1 - r];
+    tk[r] = o > tk[r] ? o : tk[r];
+  }
+#pragma unroll
+  for (int st = KMAX / 2; st >= 1; st >>= 1)
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r)
+      if ((r & st) == 0) ce_desc(tk[r], tk[r + st]);
+}
+
 template <int DS, typename ST, int KMAX>
 __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ qs,
                                                         const ST* __restrict__ ks, int K,
                                                         int renorm, int* __restrict__ idx,
                                                         float* __restrict__ bias, Dims D) {
   static_assert(KMAX >= 8 && (KMAX & (KMAX - 1)) == 0, "KMAX: a power of two >= 8");
+  constexpr bool kTile = std::is_same<ST, bf16>::value;
+  const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int wave_first = __builtin_amdgcn_readfirstlane(blockIdx.x * 256 + (threadIdx.x & ~63));
@@ -145,58 +264,36 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const ST* __restrict__ q
   const int ic = min(i, D.tq - 1);
   const int c = (D.qoff + ic) / D.blk;
   const int cw = (D.qoff + min(wave_first + 63, D.tq - 1)) / D.blk;  // wave max of c
-  const size_t row = ((size_t)b * D.hq + h) * D.tq + ic;
-  SelQ<DS, ST> qsv;
-  qsv.load(qs + row * DS);
+  const size_t row0 = ((size_t)b * D.hq + h) * D.tq, row = row0 + ic;
   const ST* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
+  LaneTile<DS> tile;
+  SelQ<DS, ST> qsv;
+  if constexpr (kTile)
+    tile.load((const bf16*)qs + row0 * DS, wave_first, D.tq, lane);
+  else
+    qsv.load(qs + row * DS);
   unsigned long long tk[KMAX];  // best blocks, key descending; 0 = empty
 #pragma unroll
   for (int r = 0; r < KMAX; ++r) tk[r] = 0ull;
   float m = -INFINITY, s = 0.f;  // log2-domain running log-sum-exp of z
-  for (int j0 = 0; j0 < cw; j0 += 8) {
-    float zz[8];
+  for (int j0 = 0; j0 < cw; j0 += 16) {
+    float z[16];
+    if constexpr (kTile) {
+      tile.score((const bf16*)ksb, j0, D.nb, lane, z);
+    } else {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int j = j0 + kk;
-      zz[kk] = (j < cw) ? D.sel_scale * qsv.dot(ksb + (size_t)j * DS) : -INFINITY;
-      if (j >= c) zz[kk] = -INFINITY;
-    }
-    float mc = zz[0];
-#pragma unroll
-    for (int kk = 1; kk < 8; ++kk) mc = fmaxf(mc, zz[kk]);
-    const float mn = fmaxf(m, mc * kLog2e);
-    if (mn != -INFINITY) {
-      float acc = s * exp2f(m - mn);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) acc += exp2f(zz[kk] * kLog2e - mn);
-      s = acc;
-      m = mn;
-    }
-    // the batch as keys (blocks at or after c: 0, never selected), sorted
-    unsigned long long bk[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int j = j0 + kk;
-      bk[kk] = j < c ? ((unsigned long long)ord_key(zz[kk]) << 32) | (unsigned)~j : 0ull;
-    }
-    ce_desc(bk[0], bk[2]); ce_desc(bk[1], bk[3]); ce_desc(bk[4], bk[6]); ce_desc(bk[5], bk[7]);
-    ce_desc(bk[0], bk[4]); ce_desc(bk[1], bk[5]); ce_desc(bk[2], bk[6]); ce_desc(bk[3], bk[7]);
-    ce_desc(bk[0], bk[1]); ce_desc(bk[2], bk[3]); ce_desc(bk[4], bk[5]); ce_desc(bk[6], bk[7]);
-    ce_desc(bk[2], bk[4]); ce_desc(bk[3], bk[5]);
-    ce_desc(bk[1], bk[4]); ce_desc(bk[3], bk[6]);
-    ce_desc(bk[1], bk[2]); ce_desc(bk[3], bk[4]); ce_desc(bk[5], bk[6]);
-    // best KMAX of list and batch: the list descends, the mirrored batch
-    // ascends, their larger elements form a bitonic sequence
-#pragma unroll
-    for (int r = KMAX - 8; r < KMAX; ++r) {
-      const unsigned long long o = bk[KMAX - 1 - r];
-      tk[r] = o > tk[r] ? o : tk[r];
+      for (int kk = 0; kk < 16; ++kk)
+        z[kk] = j0 + kk < cw ? qsv.dot(ksb + (size_t)(j0 + kk) * DS) : 0.f;
     }
 #pragma unroll
-    for (int st = KMAX / 2; st >= 1; st >>= 1)
+    for (int hf = 0; hf < 2; ++hf) {
+      if (hf == 1 && j0 + 8 >= cw) break;  // wave-uniform
+      float zz[8];
 #pragma unroll
-      for (int r = 0; r < KMAX; ++r)
-        if ((r & st) == 0) ce_desc(tk[r], tk[r + st]);
+      for (int kk = 0; kk < 8; ++kk)
+        zz[kk] = j0 + 8 * hf + kk < c ? D.sel_scale * z[8 * hf + kk] : -INFINITY;
+      lane_fold8<KMAX>(zz, j0 + 8 * hf, m, s, tk);
+    }
   }
   if (i >= D.tq) return;
   const int n = c < K ? c : K;
