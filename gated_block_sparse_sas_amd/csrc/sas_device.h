@@ -177,6 +177,23 @@ __device__ __forceinline__ float stride_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Inclusive prefix sum over the lanes of a wave (lane 0 first): within each
+// 16-lane row by DPP row shifts of 1, 2, 4 and 8 (a lane shifted in from
+// outside the row adds 0), then the totals of the rows below (lanes 15, 31,
+// 47 after the first step) read into scalars and added.  No LDS round trip;
+// the whole wave must be active.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned x, int lane) {
+  x += (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const unsigned t0 = (unsigned)__builtin_amdgcn_readlane((int)x, 15);
+  const unsigned t1 = (unsigned)__builtin_amdgcn_readlane((int)x, 31);
+  const unsigned t2 = (unsigned)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
+}
+
 // The value of lane l ^ S (S = 1, 2, ..., 32) for lane l, without an LDS
 // round trip: DPP quad permutes (S = 1, 2), row shifts up and down by S
 // (4, 8: the row of 16 lanes holds both), and the swaps of 16-lane rows and

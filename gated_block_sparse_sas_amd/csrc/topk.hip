@@ -362,17 +362,18 @@ __device__ __forceinline__ void bitonic_lanes(unsigned long long (&v)[E], int la
   }
 }
 
-// Sorts the n winners sk / sj [0, n) into selection order (z descending,
-// block ascending), p2 = the power of two >= n, p2 <= 64 E: 64-bit keys
-// (ord_key << 32 | ~block) held E per lane, padding 0 (below every real
-// key); sj [0, n) gets the sorted blocks back.
+// Sorts the n winning blocks sj [0, n) (their keys: zk [block]) into
+// selection order (z descending, block ascending), p2 = the power of two
+// >= n, p2 <= 64 E: 64-bit keys (ord_key << 32 | ~block) held E per lane,
+// padding 0 (below every real key); sj [0, n) gets the sorted blocks back.
 template <int E>
-__device__ __forceinline__ void sort_winners(const unsigned* sk, int* sj, int n, int p2, int lane) {
+__device__ __forceinline__ void sort_winners(const unsigned* zk, int* sj, int n, int p2, int lane) {
   unsigned long long v[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int x = 64 * e + lane;
-    v[e] = x < n ? ((unsigned long long)sk[x] << 32) | (unsigned)~sj[x] : 0ull;
+    const int j = x < n ? sj[x] : 0;
+    v[e] = x < n ? ((unsigned long long)zk[j] << 32) | (unsigned)~j : 0ull;
   }
   for (int size = 2; size <= p2; size <<= 1) {
     // distances of 64 elements and more: within the lane
@@ -414,6 +415,206 @@ __device__ __forceinline__ void sort_winners(const unsigned* sk, int* sj, int n,
   }
 }
 
+// The selection of one query row (row) from its scores zc [0, c) in LDS
+// (m: their maximum, or -inf with c = 0), by one wavefront.  One pass over
+// the scores gives the gate normaliser lam, turns each score into its
+// ord_key in place (zk; a score comes back from its key exactly, up to the
+// sign of a zero) and counts the first radix digit: key bits 31..20 (8
+// values per octave of the score), over the 256 values at and below the
+// top key's only.  (A digit of the top 8 bits alone would put most scores
+// of a row into a handful of bins, whose LDS atomics serialise.)  When the
+// bin holding the n-th best key has at most 64 keys, one more pass writes
+// the blocks above that bin to sj and the bin's blocks after them, and each
+// of those candidates ranks itself among the others on the unique 64-bit
+// order (key, ~block) to settle which are taken.  Otherwise (a larger bin,
+// or a window holding fewer than n keys) radix passes over all keys resolve
+// the remaining bits and a gather takes the keys above the resulting
+// prefix, then the first keys on it by block.  The n winners are then sorted
+// and written out.  hist: 256 words, sj: kp2 + 64 words, this wave's own.
+__device__ __forceinline__ void select_row(float* zc, float m, int c, int n, int kmax,
+                                           int renorm, unsigned* hist, int* sj, size_t row,
+                                           int* __restrict__ idx, float* __restrict__ bias,
+                                           int lane) {
+  unsigned* zk = (unsigned*)zc;
+  const unsigned long long lt = lane == 0 ? 0ull : ~0ull >> (64 - lane);  // lanes below
+  const unsigned top = c > 0 ? ord_key(m) >> 20 : 0u;
+  if (n > 0)
+    for (int x = lane; x < 256; x += 64) hist[x] = 0;
+  float sum = 0.f;
+  for (int j = lane; j < c; j += 64) {  // c > 0: m finite
+    const float z = zc[j];
+    sum += exp2_raw((z - m) * kLog2e);
+    const unsigned k = ord_key(z);
+    zk[j] = k;
+    const unsigned d = top - (k >> 20);  // keys never exceed the top one
+    if (n > 0 && d < 256u) atomicAdd(&hist[d], 1u);
+  }
+  sum = wave_sum(sum);
+  const float lam = c == 0 ? -INFINITY : m + log2f(sum) * kLn2;
+  int need = n;
+  unsigned prefix = 0, pmask = 0;
+  // The counts in hist ranked from the top (rank r = 4 l + u on lane l, at
+  // hist [dmax - r] or, !rev, hist [r]; ranks past dmax count 0): the rank
+  // where the count from the top first reaches need, the count above it and
+  // in it; -1 when all of them together hold fewer than need.
+  auto pick = [&](bool rev, int dmax, unsigned& above, unsigned& inbin) -> int {
+    unsigned cnt[4], tot = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 4 * lane + u;
+      cnt[u] = r <= dmax ? hist[rev ? dmax - r : r] : 0u;
+      tot += cnt[u];
+    }
+    const unsigned inc = wave_incl_scan(tot, lane), exc = inc - tot;
+    int rsel = -1;
+    unsigned ab = 0, ib = 0;
+    if (exc < (unsigned)need && inc >= (unsigned)need) {
+      unsigned run = exc;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (rsel < 0 && run + cnt[u] >= (unsigned)need) {
+          rsel = 4 * lane + u;
+          ab = run;
+          ib = cnt[u];
+        }
+        run += cnt[u];
+      }
+    }
+    const unsigned long long bal = __ballot(rsel >= 0);
+    if (bal == 0ull) return -1;
+    const int src = __ffsll((long long)bal) - 1;  // one lane, wave-uniform
+    above = (unsigned)__builtin_amdgcn_readlane((int)ab, src);
+    inbin = (unsigned)__builtin_amdgcn_readlane((int)ib, src);
+    return __builtin_amdgcn_readlane(rsel, src);
+  };
+  // One radix pass over the digit (key >> shift) & (2^bits - 1) of the keys
+  // on the prefix; true once every key of the chosen digit is needed.
+  auto pass = [&](int shift, int bits) -> bool {
+    const unsigned dmask = (1u << bits) - 1u;
+    for (int x = lane; x < 256; x += 64) hist[x] = 0;
+    for (int j = lane; j < c; j += 64) {
+      const unsigned kk = zk[j];
+      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & dmask], 1u);
+    }
+    unsigned above = 0, inbin = 0;
+    const int r = pick(true, (int)dmask, above, inbin);
+    need -= (int)above;
+    prefix |= (dmask - (unsigned)r) << shift;
+    pmask |= dmask << shift;
+    return (int)inbin == need;
+  };
+  if (n > 0) {
+    unsigned above = 0, inbin = 0;
+    const int r = pick(false, 255, above, inbin);
+    if (r >= 0 && inbin <= 64u) {
+      int nw = 0, nc = 0;
+      for (int j0 = 0; j0 < c; j0 += 64) {
+        const int j = j0 + lane;
+        const unsigned d = j < c ? top - (zk[j] >> 20) : ~0u;
+        const bool w = d < (unsigned)r, cd = d == (unsigned)r;
+        const unsigned long long bw = __ballot(w), bc = __ballot(cd);
+        if (w) sj[nw + __popcll(bw & lt)] = j;
+        if (cd) sj[(int)above + nc + __popcll(bc & lt)] = j;
+        nw += __popcll(bw);
+        nc += __popcll(bc);
+      }
+      need -= (int)above;
+      if ((int)inbin > need) {
+        const bool has = lane < (int)inbin;
+        const int jt = has ? sj[(int)above + lane] : 0;
+        const unsigned kh = has ? zk[jt] : 0u, kl = ~(unsigned)jt;
+        const unsigned long long kt = ((unsigned long long)kh << 32) | kl;
+        int rank = 0;
+        for (int u = 0; u < (int)inbin; ++u) {
+          const unsigned long long ku =
+              ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)kh, u) << 32) |
+              (unsigned)__builtin_amdgcn_readlane((int)kl, u);
+          rank += ku > kt;
+        }
+        const bool take = has && rank < need;
+        const unsigned long long bt = __ballot(take);
+        if (take) sj[(int)above + __popcll(bt & lt)] = jt;
+      }
+    } else {
+      if (r >= 0) {
+        need -= (int)above;
+        prefix = (top - (unsigned)r) << 20;
+        pmask = 0xFFF00000u;
+        if ((int)inbin != need && !pass(12, 8) && !pass(4, 8)) pass(0, 4);
+      } else {
+        if (!pass(24, 8) && !pass(16, 8) && !pass(8, 8)) pass(0, 8);
+      }
+      // gather: keys whose resolved bits lie above the prefix, then the
+      // first `need` keys on it by block (all of them when the passes
+      // stopped early)
+      int cnt_sel = 0, ties_left = need;
+      for (int j0 = 0; j0 < c; j0 += 64) {
+        const int j = j0 + lane;
+        const unsigned kk = j < c ? zk[j] & pmask : 0u;
+        const bool abv = j < c && kk > prefix;
+        const bool tie = j < c && kk == prefix;
+        const unsigned long long bt = __ballot(tie);
+        const int trank = __popcll(bt & lt);
+        const bool take = abv || (tie && trank < ties_left);
+        const unsigned long long bs = __ballot(take);
+        if (take) sj[cnt_sel + __popcll(bs & lt)] = j;
+        cnt_sel += __popcll(bs);
+        ties_left -= min(ties_left, (int)__popcll(bt));
+      }
+    }
+  }
+  // bitonic sort of the n winners (padded to a power of two with the worst
+  // key): in registers up to 256 of them, in LDS beyond (padding block -1,
+  // key 0)
+  int p2 = 1;
+  while (p2 < n) p2 <<= 1;
+  if (p2 <= 64) {
+    sort_winners<1>(zk, sj, n, p2, lane);
+  } else if (p2 == 128) {
+    sort_winners<2>(zk, sj, n, p2, lane);
+  } else if (p2 == 256) {
+    sort_winners<4>(zk, sj, n, p2, lane);
+  } else {
+    for (int x = n + lane; x < p2; x += 64) sj[x] = -1;
+    for (int size = 2; size <= p2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int pr = lane; pr < (p2 >> 1); pr += 64) {
+          const int lo = 2 * stride * (pr / stride) + (pr % stride), hi = lo + stride;
+          const int ja = sj[lo], jb = sj[hi];
+          const unsigned ka = ja < 0 ? 0u : zk[ja], kb2 = jb < 0 ? 0u : zk[jb];
+          const bool first_better = key_before(ka, ja, kb2, jb);
+          const bool want_better_first = (lo & size) == 0;
+          if (first_better != want_better_first) {
+            sj[lo] = jb;
+            sj[hi] = ja;
+          }
+        }
+      }
+    }
+  }
+  // outputs
+  float norm = lam;
+  if (renorm) {
+    float mm = -INFINITY;
+    for (int r = lane; r < n; r += 64) mm = fmaxf(mm, key_value(zk[sj[r]]));
+    mm = wave_max(mm);
+    float ss = 0.f;
+    for (int r = lane; r < n; r += 64) ss += exp2f((key_value(zk[sj[r]]) - mm) * kLog2e);
+    ss = wave_sum(ss);
+    norm = n == 0 ? -INFINITY : mm + log2f(ss) * kLn2;
+  }
+  for (int r = lane; r < kmax; r += 64) {
+    if (r < n) {
+      const int j = sj[r];
+      idx[row * kmax + r] = j;
+      bias[row * kmax + r] = key_value(zk[j]) - norm;
+    } else {
+      idx[row * kmax + r] = -1;
+      bias[row * kmax + r] = -INFINITY;
+    }
+  }
+}
+
 template <int DS, typename ST>
 __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__ qs,
                                                           const ST* __restrict__ ks, int kmax,
@@ -422,12 +623,11 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
                                                           float* __restrict__ bias, Dims D,
                                                           int kp2, int wpg) {
   extern __shared__ unsigned tsm[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int per = D.nb + 256 + 2 * kp2;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int per = D.nb + 256 + kp2 + 64;
   float* zc = (float*)(tsm + (size_t)wave * per);  // scores of this row's blocks
   unsigned* hist = tsm + (size_t)wave * per + D.nb;  // radix histogram
-  unsigned* sk = hist + 256;                         // selected keys
-  int* sj = (int*)(sk + kp2);                        // selected blocks
+  int* sj = (int*)(hist + 256);                      // selected blocks
   const size_t nrows = (size_t)D.batch * D.hq * D.tq;
   const size_t row = (size_t)blockIdx.x * wpg + wave;
   if (row >= nrows) return;  // whole wave (no workgroup barrier below)
@@ -448,136 +648,75 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const ST* __restrict__
     m = fmaxf(m, z);
   }
   m = wave_max(m);
-  float sum = 0.f;
-  if (m != -INFINITY)
-    for (int j = lane; j < c; j += 64) sum += exp2f((zc[j] - m) * kLog2e);
-  sum = wave_sum(sum);
-  const float lam = c == 0 ? -INFINITY : m + log2f(sum) * kLn2;
-  // radix select of the n-th largest key
-  unsigned prefix = 0, pmask = 0;
-  int need = n;
-  if (n > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int x = lane; x < 256; x += 64) hist[x] = 0;
-      for (int j = lane; j < c; j += 64) {
-        const unsigned kk = ord_key(zc[j]);
-        if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
-      }
-      // lane l owns digits 255 - 4l .. 252 - 4l (from the top)
-      unsigned cnt[4], tot = 0;
+  select_row(zc, m, c, n, kmax, renorm, hist, sj, row, idx, bias, lane);
+}
+
+// The same selection for bf16 selectors, RW consecutive query rows of one
+// (batch, head) per workgroup of four waves.  The rows share their ks
+// history, so the workgroup reads it once: wave w scores the 16-block tiles
+// w, w + 4, ... for all RW rows with one 16x16x32 matrix product per k slice
+// (A = the tile's 16 ks rows, B = the RW qs rows, padded to 16 columns; exact
+// bf16 products summed by the MFMA, as in the lane kernel) into LDS, and
+// after one barrier each wave runs select_row on RW / 4 of the rows.
+template <int DS, int RW>
+__global__ __launch_bounds__(256) void topk_select_tile_kernel(
+    const bf16* __restrict__ qs, const bf16* __restrict__ ks, int kmax, int fnum, int fden,
+    int renorm, int* __restrict__ idx, float* __restrict__ bias, Dims D, int kp2, int nbp) {
+  static_assert(RW == 4 || RW == 8 || RW == 16, "RW: 4, 8 or 16 rows");
+  constexpr int NK = (DS + 31) / 32;  // k slices of 32
+  extern __shared__ unsigned tsm[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  float* zs = (float*)tsm;  // RW rows of nbp scores
+  unsigned* hist = tsm + (size_t)RW * nbp + (size_t)wave * (256 + kp2 + 64);
+  int* sj = (int*)(hist + 256);
+  const int tiles = (D.tq + RW - 1) / RW;
+  const int bh = blockIdx.x / tiles;  // b * hq + h
+  const int i0 = (blockIdx.x - bh * tiles) * RW;
+  const int h = bh % D.hq, b = bh / D.hq;
+  const int ilast = min(i0 + RW, D.tq) - 1;
+  const int cmax = (D.qoff + ilast) / D.blk;
+  const size_t row0 = (size_t)bh * D.tq;
+  const bf16* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
+  // 16x16x32 operands: lane l holds row / column l % 16, k = 8 (l / 16) .. + 7
+  const int kg = 8 * (lane >> 4), r16 = lane & 15;
+  bf16x8 qb[NK];
+  {
+    const bf16* p = qs + (row0 + min(i0 + r16, ilast)) * DS;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        cnt[u] = hist[255 - 4 * lane - u];
-        tot += cnt[u];
-      }
-      // inclusive prefix of tot over lanes (from the top digit down)
-      unsigned inc = tot;
+    for (int s = 0; s < NK; ++s)
+      qb[s] = 32 * s + kg < DS ? *(const bf16x8*)(p + 32 * s + kg) : bf16x8{};
+  }
+  for (int j0 = 16 * wave; j0 < cmax; j0 += 64) {
+    const bf16* kp = ksb + (size_t)min(j0 + r16, D.nb - 1) * DS;
+    f32x4 t = f32x4{};
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-      }
-      const unsigned exc = inc - tot;
-      // the digit where the count from the top first reaches need
-      int dsel = -1;
-      unsigned above = 0, inbin = 0;
-      if (exc < (unsigned)need && inc >= (unsigned)need) {
-        unsigned run = exc;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (dsel < 0 && run + cnt[u] >= (unsigned)need) {
-            dsel = 255 - 4 * lane - u;
-            above = run;
-            inbin = cnt[u];
-          }
-          run += cnt[u];
-        }
-      }
-      const unsigned long long bal = __ballot(dsel >= 0);
-      const int src = __ffsll((long long)bal) - 1;
-      const int dg = __shfl(dsel, src);
-      need -= (int)__shfl(above, src);
-      prefix |= (unsigned)dg << shift;
-      pmask |= 255u << shift;
-      // every key of the digit's bin is needed: the selection is settled
-      if (__shfl(inbin, src) == (unsigned)need) break;
+    for (int s = 0; s < NK; ++s) {
+      const bf16x8 a = 32 * s + kg < DS ? *(const bf16x8*)(kp + 32 * s + kg) : bf16x8{};
+      t = mfma16(a, qb[s], t);
     }
+    // lane: row i0 + r16, blocks j0 + 4 (lane / 16) .. + 3 (those at or past
+    // the row's c are never read)
+    if (r16 < RW) *(f32x4*)(zs + (size_t)r16 * nbp + j0 + 4 * (lane >> 4)) = D.sel_scale * t;
   }
-  // gather: keys whose resolved bits lie above the prefix, then the first
-  // `need` keys on it by block (all of them when the passes stopped early)
-  int cnt_sel = 0, ties_left = need;
-  for (int j0 = 0; j0 < c; j0 += 64) {
-    const int j = j0 + lane;
-    const unsigned kfull = j < c ? ord_key(zc[j]) : 0u, kk = kfull & pmask;
-    const bool above = n > 0 && j < c && kk > prefix;
-    const bool tie = n > 0 && j < c && kk == prefix;
-    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const unsigned long long bt = __ballot(tie);
-    const int trank = __popcll(bt & lt);
-    const bool take = above || (tie && trank < ties_left);
-    const unsigned long long bs = __ballot(take);
-    if (take) {
-      const int pos = cnt_sel + __popcll(bs & lt);
-      sk[pos] = kfull;
-      sj[pos] = j;
-    }
-    cnt_sel += __popcll(bs);
-    ties_left -= min(ties_left, __popcll(bt));
+  __syncthreads();
+  for (int q = 0; q < RW / 4; ++q) {
+    const int i = i0 + wave * (RW / 4) + q;
+    if (i > ilast) break;  // whole wave (no workgroup barrier below)
+    const int c = (D.qoff + i) / D.blk;
+    int n = min(kmax, c);
+    if (fnum > 0) n = (int)min((long long)n, ((long long)fnum * c + fden - 1) / fden);
+    float* zc = zs + (size_t)(i - i0) * nbp;
+    float m = -INFINITY;
+    for (int j = lane; j < c; j += 64) m = fmaxf(m, zc[j]);
+    m = wave_max(m);
+    select_row(zc, m, c, n, kmax, renorm, hist, sj, row0 + i, idx, bias, lane);
   }
-  // bitonic sort of the n winners (padded to a power of two with the worst
-  // key): in registers up to 256 of them, in LDS beyond
-  int p2 = 1;
-  while (p2 < n) p2 <<= 1;
-  if (p2 <= 64) {
-    sort_winners<1>(sk, sj, n, p2, lane);
-  } else if (p2 == 128) {
-    sort_winners<2>(sk, sj, n, p2, lane);
-  } else if (p2 == 256) {
-    sort_winners<4>(sk, sj, n, p2, lane);
-  } else {
-  for (int x = n + lane; x < p2; x += 64) {
-    sk[x] = 0u;
-    sj[x] = 0x7fffffff;
-  }
-  for (int size = 2; size <= p2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int pr = lane; pr < (p2 >> 1); pr += 64) {
-        const int lo = 2 * stride * (pr / stride) + (pr % stride), hi = lo + stride;
-        const unsigned ka = sk[lo], kb2 = sk[hi];
-        const int ja = sj[lo], jb = sj[hi];
-        const bool first_better = key_before(ka, ja, kb2, jb);
-        const bool want_better_first = (lo & size) == 0;
-        if (first_better != want_better_first) {
-          sk[lo] = kb2;
-          sk[hi] = ka;
-          sj[lo] = jb;
-          sj[hi] = ja;
-        }
-      }
-    }
-  }
-  }
-  // outputs
-  float norm = lam;
-  if (renorm) {
-    float mm = -INFINITY;
-    for (int r = lane; r < n; r += 64) mm = fmaxf(mm, zc[sj[r]]);
-    mm = wave_max(mm);
-    float ss = 0.f;
-    for (int r = lane; r < n; r += 64) ss += exp2f((zc[sj[r]] - mm) * kLog2e);
-    ss = wave_sum(ss);
-    norm = n == 0 ? -INFINITY : mm + log2f(ss) * kLn2;
-  }
-  for (int r = lane; r < kmax; r += 64) {
-    if (r < n) {
-      const int j = sj[r];
-      idx[row * kmax + r] = j;
-      bias[row * kmax + r] = zc[j] - norm;
-    } else {
-      idx[row * kmax + r] = -1;
-      bias[row * kmax + r] = -INFINITY;
-    }
-  }
+}
+
+// LDS bytes of the tiled selection with RW rows per workgroup.
+static size_t select_tile_bytes(const Dims& D, int kp2, int RW, int* nbp) {
+  *nbp = (D.nb + 15) / 16 * 16 + 4;  // whole 16-block tiles, rows 16 B apart off the banks
+  return ((size_t)RW * *nbp + 4 * (size_t)(256 + kp2 + 64)) * sizeof(unsigned);
 }
 
 template <int DS, typename ST>
@@ -586,7 +725,26 @@ static hipError_t launch_select_t(const void* qs, const void* ks, int kmax, int 
                                   int* idx, float* bias, const Dims& D, hipStream_t st) {
   int kp2 = 1;
   while (kp2 < kmax) kp2 <<= 1;
-  const size_t per = (size_t)(D.nb + 256 + 2 * kp2) * sizeof(unsigned);
+  if constexpr (std::is_same<ST, bf16>::value) {
+    // 16 or 8 rows per workgroup while eight workgroups (32 waves) still fit
+    // a CU's 160 KiB of LDS, else 4 rows (at most 64 KiB): the selection
+    // phase needs the waves more than the scoring needs the shared reads
+    int nbp = 0;
+    const unsigned tiles16 = (unsigned)((D.tq + 15) / 16), tiles8 = (unsigned)((D.tq + 7) / 8),
+                   tiles4 = (unsigned)((D.tq + 3) / 4), bh = (unsigned)(D.batch * D.hq);
+#define SAS_TILE_LAUNCH(RWV, TILES, CAP)                                                       \
+  if (select_tile_bytes(D, kp2, RWV, &nbp) <= CAP) {                                          \
+    hipLaunchKernelGGL((topk_select_tile_kernel<DS, RWV>), dim3(bh * TILES), dim3(256),       \
+                       select_tile_bytes(D, kp2, RWV, &nbp), st, (const bf16*)qs,             \
+                       (const bf16*)ks, kmax, fnum, fden, renorm, idx, bias, D, kp2, nbp);    \
+    return hipGetLastError();                                                                 \
+  }
+    SAS_TILE_LAUNCH(16, tiles16, 20480)
+    SAS_TILE_LAUNCH(8, tiles8, 20480)
+    SAS_TILE_LAUNCH(4, tiles4, 65536)
+#undef SAS_TILE_LAUNCH
+  }
+  const size_t per = (size_t)(D.nb + 256 + kp2 + 64) * sizeof(unsigned);
   int wpg = 4;  // rows (waves) per workgroup, as many as 64 KiB of LDS holds
   while (wpg > 1 && per * wpg > 65536) wpg >>= 1;
   const size_t nrows = (size_t)D.batch * D.hq * D.tq;
@@ -599,7 +757,7 @@ static hipError_t launch_select_t(const void* qs, const void* ks, int kmax, int 
 bool topk_budget_supported(const Dims& D, int kmax) {
   int kp2 = 1;
   while (kp2 < kmax) kp2 <<= 1;
-  return kmax <= 1024 && (size_t)(D.nb + 256 + 2 * kp2) * sizeof(unsigned) <= 65536;
+  return kmax <= 1024 && (size_t)(D.nb + 256 + kp2 + 64) * sizeof(unsigned) <= 65536;
 }
 
 hipError_t launch_topk_budget(const void* qs, const void* ks, int kmax, int fnum, int fden,
