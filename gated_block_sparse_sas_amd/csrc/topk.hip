@@ -364,10 +364,15 @@ __device__ __forceinline__ void bitonic_lanes(unsigned long long (&v)[E], int la
 
 // Sorts the n winning blocks sj [0, n) (their keys: zk [block]) into
 // selection order (z descending, block ascending), p2 = the power of two
-// >= n, p2 <= 64 E: 64-bit keys (ord_key << 32 | ~block) held E per lane,
-// padding 0 (below every real key); sj [0, n) gets the sorted blocks back.
+// >= n, p2 <= 64 E: 64-bit keys (ord_key << 32 | ~block) held E per lane
+// (position 64 e + lane in v [e]), padding 0 (below every real key), and
+// writes the row's kmax outputs from the sorted registers: block and score
+// minus the normaliser (lam, or with renorm the log-sum-exp of the winners'
+// scores), -1 and -inf past n.
 template <int E>
-__device__ __forceinline__ void sort_winners(const unsigned* zk, int* sj, int n, int p2, int lane) {
+__device__ __forceinline__ void sort_emit(const unsigned* zk, const int* sj, int n, int p2,
+                                          int lane, int kmax, int renorm, float lam, size_t row,
+                                          int* __restrict__ idx, float* __restrict__ bias) {
   unsigned long long v[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -408,10 +413,28 @@ __device__ __forceinline__ void sort_winners(const unsigned* zk, int* sj, int n,
     if (size > 2) bitonic_lanes<2>(v, lane, size);
     bitonic_lanes<1>(v, lane, size);
   }
+  float norm = lam;
+  if (renorm) {
+    // the best winner sits at position 0
+    const float mm = key_value((unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v[0] >> 32), 0));
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (64 * e + lane < n) ss += exp2f((key_value((unsigned)(v[e] >> 32)) - mm) * kLog2e);
+    ss = wave_sum(ss);
+    norm = n == 0 ? -INFINITY : mm + log2f(ss) * kLn2;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int x = 64 * e + lane;
-    if (x < n) sj[x] = (int)~(unsigned)v[e];
+    if (x < kmax) {
+      idx[row * kmax + x] = x < n ? (int)~(unsigned)v[e] : -1;
+      bias[row * kmax + x] = x < n ? key_value((unsigned)(v[e] >> 32)) - norm : -INFINITY;
+    }
+  }
+  for (int x = 64 * E + lane; x < kmax; x += 64) {  // n <= 64 E: padding only
+    idx[row * kmax + x] = -1;
+    bias[row * kmax + x] = -INFINITY;
   }
 }
 
@@ -569,11 +592,14 @@ __device__ __forceinline__ void select_row(float* zc, float m, int c, int n, int
   int p2 = 1;
   while (p2 < n) p2 <<= 1;
   if (p2 <= 64) {
-    sort_winners<1>(zk, sj, n, p2, lane);
+    sort_emit<1>(zk, sj, n, p2, lane, kmax, renorm, lam, row, idx, bias);
+    return;
   } else if (p2 == 128) {
-    sort_winners<2>(zk, sj, n, p2, lane);
+    sort_emit<2>(zk, sj, n, p2, lane, kmax, renorm, lam, row, idx, bias);
+    return;
   } else if (p2 == 256) {
-    sort_winners<4>(zk, sj, n, p2, lane);
+    sort_emit<4>(zk, sj, n, p2, lane, kmax, renorm, lam, row, idx, bias);
+    return;
   } else {
     for (int x = n + lane; x < p2; x += 64) sj[x] = -1;
     for (int size = 2; size <= p2; size <<= 1) {
@@ -686,17 +712,28 @@ __global__ __launch_bounds__(256) void topk_select_tile_kernel(
     for (int s = 0; s < NK; ++s)
       qb[s] = 32 * s + kg < DS ? *(const bf16x8*)(p + 32 * s + kg) : bf16x8{};
   }
-  for (int j0 = 16 * wave; j0 < cmax; j0 += 64) {
-    const bf16* kp = ksb + (size_t)min(j0 + r16, D.nb - 1) * DS;
-    f32x4 t = f32x4{};
+  // four tiles per round (their loads in flight together); a tile past cmax
+  // reads clamped rows and is not stored
+  for (int j00 = 16 * wave; j00 < cmax; j00 += 256) {
+    bf16x8 a[4][NK];
 #pragma unroll
-    for (int s = 0; s < NK; ++s) {
-      const bf16x8 a = 32 * s + kg < DS ? *(const bf16x8*)(kp + 32 * s + kg) : bf16x8{};
-      t = mfma16(a, qb[s], t);
+    for (int u = 0; u < 4; ++u) {
+      const bf16* kp = ksb + (size_t)min(j00 + 64 * u + r16, D.nb - 1) * DS;
+#pragma unroll
+      for (int s = 0; s < NK; ++s)
+        a[u][s] = 32 * s + kg < DS ? *(const bf16x8*)(kp + 32 * s + kg) : bf16x8{};
     }
-    // lane: row i0 + r16, blocks j0 + 4 (lane / 16) .. + 3 (those at or past
-    // the row's c are never read)
-    if (r16 < RW) *(f32x4*)(zs + (size_t)r16 * nbp + j0 + 4 * (lane >> 4)) = D.sel_scale * t;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j0 = j00 + 64 * u;
+      f32x4 t = f32x4{};
+#pragma unroll
+      for (int s = 0; s < NK; ++s) t = mfma16(a[u][s], qb[s], t);
+      // lane: row i0 + r16, blocks j0 + 4 (lane / 16) .. + 3 (those at or
+      // past the row's c are never read)
+      if (r16 < RW && j0 < cmax)
+        *(f32x4*)(zs + (size_t)r16 * nbp + j0 + 4 * (lane >> 4)) = D.sel_scale * t;
+    }
   }
   __syncthreads();
   for (int q = 0; q < RW / 4; ++q) {
