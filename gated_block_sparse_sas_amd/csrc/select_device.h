@@ -21,6 +21,12 @@ struct DenseSel {
   __device__ const ST* ks_row(const Dims& D, int b, int h, int j) const {
     return ks + (((size_t)b * D.hks + h / D.hps) * (size_t)D.nb + j) * D.ds;
   }
+  // A row that may always be read for block j (0 <= j < nb) and whether it
+  // is block j's selector key (always, for a contiguous cache).
+  __device__ const ST* ks_row_readable(const Dims& D, int b, int h, int j, bool* own) const {
+    *own = true;
+    return ks_row(D, b, h, j);
+  }
 };
 
 template <typename ST>
@@ -37,6 +43,13 @@ struct PagedSel {
     const int pg = table[(size_t)b * D.nb + j];
     if (pg < 0 || pg >= pages) return nullptr;
     return ks + ((size_t)pg * D.hks + h / D.hps) * D.ds;
+  }
+  // A row that may always be read for block j: its page's, or page 0's
+  // (pages >= 1) when the page id is out of range (*own false then).
+  __device__ const ST* ks_row_readable(const Dims& D, int b, int h, int j, bool* own) const {
+    const int pg = table[(size_t)b * D.nb + j];
+    *own = pg >= 0 && pg < pages;
+    return ks + ((size_t)(*own ? pg : 0) * D.hks + h / D.hps) * D.ds;
   }
 };
 
@@ -101,7 +114,7 @@ __device__ __forceinline__ void merge_lanes(unsigned long long (&tk)[KM], int la
   merge_desc<KM>(tk, p);
 }
 
-template <int DS, typename ST, typename Sel, int KM>
+template <int DS, typename ST, typename Sel, int KM, int RIF = 4>
 __device__ __forceinline__ void wave_best(const ST* __restrict__ qs, const Sel& S, const Dims& D,
                                           size_t row, int c, int first, int stride,
                                           unsigned long long (&tk)[KM], float* m_out,
@@ -114,12 +127,28 @@ __device__ __forceinline__ void wave_best(const ST* __restrict__ qs, const Sel& 
   for (int r = 0; r < KM; ++r) tk[r] = 0ull;  // 0 = empty
   float m = -INFINITY, s = 0.f;
   for (int j0 = first; j0 < c; j0 += stride * 8) {
+    // the batch's rows are read without branches, RIF at a time, so that
+    // RIF rows' loads are in flight together: a candidate past the history
+    // reads block c - 1 and one on an unreadable page reads a readable row;
+    // both score -inf
+    static_assert(RIF == 1 || RIF == 2 || RIF == 4 || RIF == 8, "rows in flight");
     float zz[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int j = j0 + stride * kk;
-      const ST* kr = j < c ? S.ks_row(D, b, h, j) : nullptr;
-      zz[kk] = kr ? D.sel_scale * qsv.dot(kr) : -INFINITY;
+    for (int k4 = 0; k4 < 8; k4 += RIF) {
+      const ST* kr[RIF];
+      bool own[RIF];
+#pragma unroll
+      for (int kk = 0; kk < RIF; ++kk) {
+        const int j = j0 + stride * (k4 + kk);
+        kr[kk] = S.ks_row_readable(D, b, h, j < c ? j : c - 1, &own[kk]);
+        own[kk] = own[kk] && j < c;
+      }
+#pragma unroll
+      for (int kk = 0; kk < RIF; ++kk) {
+        const float z = D.sel_scale * qsv.dot(kr[kk]);
+        zz[k4 + kk] = own[kk] ? z : -INFINITY;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     float mc = zz[0];
 #pragma unroll
@@ -193,15 +222,15 @@ __device__ __forceinline__ void select_entry(const unsigned long long (&tk)[KM],
   *bs_out = lane < n ? key_value((unsigned)(mine >> 32)) - norm : -INFINITY;
 }
 
-// One wave selects a row alone.
-template <int DS, typename ST, typename Sel, int KM>
+// One wave selects a row alone (RIF: selector rows in flight per lane).
+template <int DS, typename ST, typename Sel, int KM, int RIF = 4>
 __device__ __forceinline__ void wave_best_entry(const ST* __restrict__ qs, const Sel& S,
                                                 const Dims& D, size_t row, int K, int renorm,
                                                 int lane, int* j_out, float* bs_out) {
   const int c = S.hist(D, row);
   unsigned long long tk[KM];
   float m, s;
-  wave_best<DS, ST, Sel, KM>(qs, S, D, row, c, lane, 64, tk, &m, &s);
+  wave_best<DS, ST, Sel, KM, RIF>(qs, S, D, row, c, lane, 64, tk, &m, &s);
   const float M = wave_max(m);
   const float Ssum = wave_sum(M == -INFINITY ? 0.f : s * exp2f(m - M));
   select_entry<KM>(tk, M, Ssum, c, K, renorm, lane, j_out, bs_out);

@@ -69,8 +69,8 @@ struct PagedKV {
 };
 
 // Row kernel (decode, and prefill with units below 64 tokens): one workgroup
-// per query row, W = min(K + 1, 16) waves; wave w takes slots w, w + W, ...
-// (slot K is the current block).  K and V rows are read with 16-byte loads,
+// per query row, W = min(K + 1, 8) waves for K <= 8, else min(K + 1, 16);
+// wave w takes slots w, w + W, ... (slot K is the current block).  K and V rows are read with 16-byte loads,
 // LPK lanes per key row (a key row of d elements is LPK * 16 bytes), so one
 // load instruction covers KPI = 64 / LPK whole consecutive rows.  A lane's
 // partial dot product is summed over the key's LPK lanes; scores go through
@@ -96,9 +96,84 @@ struct RowLds {
   float mw[kRowWaves], lw[kRowWaves];
 };
 
+// One whole 64-key block of a row by one wave, the online softmax state
+// (m_w, l_w, acc) updated in place.  Every load of the block is issued
+// without a branch (a whole block has no key past its end): the NIN load
+// instructions of K, then those of V, so a wave waits for memory about
+// twice per block instead of once per instruction.  Lane l holds keys
+// it * KPI + l / LPK (it < NIN) of K and of V alike; after the sum over a
+// key's LPK lanes (an all-reduce, so each of them holds the score) the
+// lane's probabilities are exactly the ones its V rows need, and the scores
+// never go through LDS.
+template <int HD, typename T, typename Src>
+__device__ __forceinline__ void attend_block64(const Src& S, long long boff, const float* qv,
+                                               int kl, int d0, int j, int t, float add,
+                                               float sm_scale, float& m_w, float& l_w,
+                                               float* acc) {
+  constexpr int EPL = 16 / (int)sizeof(T);
+  constexpr int LPK = HD / EPL;
+  constexpr int KPI = 64 / LPK;
+  constexpr int NIN = kBlock / KPI;
+  typedef T vec_t __attribute__((ext_vector_type(EPL)));
+  const T* kb = S.k + boff + (size_t)kl * HD + d0;
+  const T* vb = S.v + boff + (size_t)kl * HD + d0;
+  vec_t kx[NIN];
+#pragma unroll
+  for (int it = 0; it < NIN; ++it) kx[it] = *(const vec_t*)(kb + (size_t)it * KPI * HD);
+  float sc[NIN];
+#pragma unroll
+  for (int it = 0; it < NIN; ++it) {
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a = fmaf(qv[e], to_f32(kx[it][e]), a);
+    sc[it] = a;
+  }
+  vec_t vx[NIN];
+#pragma unroll
+  for (int it = 0; it < NIN; ++it) vx[it] = *(const vec_t*)(vb + (size_t)it * KPI * HD);
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int it = 0; it < NIN; ++it) {
+    const float a = group_sum<LPK>(sc[it]);
+    sc[it] = (j * kBlock + it * KPI + kl > t) ? -INFINITY : a * sm_scale + add;
+    mloc = fmaxf(mloc, sc[it]);
+  }
+  // the lanes of a key group hold equal values, so the wave max is the
+  // block's and a sum over lanes l ^ LPK, l ^ 2 LPK, ... counts each key once
+  const float ms = wave_max(mloc);
+  if (ms == -INFINITY) return;  // every key masked (a bias of -inf)
+  const float m_new = fmaxf(m_w, ms);
+  const float alpha = exp2f((m_w - m_new) * kLog2e);
+  float ls = 0.f;
+#pragma unroll
+  for (int it = 0; it < NIN; ++it) {
+    sc[it] = exp2f((sc[it] - m_new) * kLog2e);
+    ls += sc[it];
+  }
+  l_w = l_w * alpha + stride_sum<LPK>(ls);
+  m_w = m_new;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+  for (int it = 0; it < NIN; ++it)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(sc[it], to_f32(vx[it][e]), acc[e]);
+}
+
+// Whether rows of HD elements of T take attend_block64 for whole 64-key
+// blocks: bf16 rows (at most 16 load instructions per block and tensor; fp32
+// rows would spill).
+template <int HD, typename T>
+constexpr bool whole_blocks_fit() {
+  return sizeof(T) == 2 && kBlock / (64 / (HD / (16 / (int)sizeof(T)))) <= 16;
+}
+
 // Attention of one query row over its K slots and its current block (slot
-// K), W waves per row; every thread of the workgroup calls it.
-template <int HD, typename T, typename Src, typename Slots>
+// K), W waves per row; every thread of the workgroup calls it.  WHOLE: every
+// unit is a whole 64-key block (D.blk == 64), taken by attend_block64; the
+// launch picks it, so the kernel for smaller units keeps its own (smaller)
+// register budget.
+template <int HD, typename T, bool WHOLE, typename Src, typename Slots>
 __device__ __forceinline__ void attend_row(const T* __restrict__ q, const Src& S,
                                            const Slots& SL, T* __restrict__ o,
                                            float* __restrict__ lse, const Dims& D, int K,
@@ -140,6 +215,11 @@ __device__ __forceinline__ void attend_row(const T* __restrict__ q, const Src& S
     }
     const long long boff = S.block(D, b, g, j);
     if (boff < 0) continue;
+    if constexpr (WHOLE) {  // whole 64-key blocks: every load of the block in flight
+      static_assert(whole_blocks_fit<HD, T>(), "bf16 rows of at most 16 loads per block");
+      attend_block64<HD, T>(S, boff, qv, kl, d0, j, t, add, D.sm_scale, m_w, l_w, acc);
+      continue;
+    }
     for (int it = 0; it < nin; ++it) {
       const int u = it * KPI + kl;
       float a = 0.f;
@@ -224,12 +304,22 @@ __device__ __forceinline__ void attend_row(const T* __restrict__ q, const Src& S
 }
 
 
-template <int HD, typename T, typename Src>
+// Row of workgroup L of n (one row per workgroup).  Consecutive workgroups
+// run on different XCDs (workgroup L on XCD L % 8); with n % 8 == 0 XCD x is
+// given the contiguous rows x n / 8 .. (x + 1) n / 8 - 1, i.e. whole
+// sequences, so each XCD's address translation caches and L2 hold the K / V
+// pages of a few sequences instead of all of them.
+__device__ __forceinline__ size_t xcd_row(size_t L, size_t n) {
+  return n % 8 ? L : (L % 8) * (n / 8) + L / 8;
+}
+
+template <int HD, typename T, typename Src, bool WHOLE>
 __global__ __launch_bounds__(64 * kRowWaves) void sparse_row_kernel(
     const T* __restrict__ q, Src S, const int* __restrict__ idx, const float* __restrict__ bias,
     T* __restrict__ o, float* __restrict__ lse, Dims D, int K) {
   __shared__ RowLds<HD> L;
-  attend_row<HD, T>(q, S, GlobalSlots{idx, bias}, o, lse, D, K, blockIdx.x, blockDim.x >> 6, L);
+  attend_row<HD, T, WHOLE>(q, S, GlobalSlots{idx, bias}, o, lse, D, K,
+                           xcd_row(blockIdx.x, gridDim.x), blockDim.x >> 6, L);
 }
 
 // Slots of a row chosen in the same workgroup (LDS).
@@ -249,7 +339,7 @@ struct LdsSlots {
 // no round trip of the selection through global memory.  (Splitting the
 // scoring over all the row's waves and merging their lists in LDS was
 // slower: the selection is not what bounds this kernel.)
-template <int HD, typename T, int DS, int KM, typename Sel, typename Src>
+template <int HD, typename T, int DS, int KM, typename Sel, typename Src, bool WHOLE>
 __global__ __launch_bounds__(64 * kRowWaves) void topk_row_kernel(
     const T* __restrict__ q, Src S, const T* __restrict__ qs, Sel SS, int K, int renorm,
     int* __restrict__ idx, float* __restrict__ bias, T* __restrict__ o, float* __restrict__ lse,
@@ -257,12 +347,14 @@ __global__ __launch_bounds__(64 * kRowWaves) void topk_row_kernel(
   __shared__ RowLds<HD> L;
   __shared__ int sj[KM];
   __shared__ float sb[KM];
-  const size_t row = blockIdx.x;
+  const size_t row = xcd_row(blockIdx.x, gridDim.x);
   const int lane = threadIdx.x & 63;
   if (threadIdx.x < 64) {
     int j;
     float bs;
-    wave_best_entry<DS, T, Sel, KM>(qs, SS, D, row, K, renorm, lane, &j, &bs);
+    // two selector rows in flight per lane: the attention waves' registers
+    // allow five waves per SIMD, so two rows' workgroups share a compute unit
+    wave_best_entry<DS, T, Sel, KM, 2>(qs, SS, D, row, K, renorm, lane, &j, &bs);
     if (lane < K) {
       sj[lane] = j;
       sb[lane] = bs;
@@ -271,7 +363,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void topk_row_kernel(
     }
   }
   __syncthreads();
-  attend_row<HD, T>(q, S, LdsSlots{sj, sb}, o, lse, D, K, row, blockDim.x >> 6, L);
+  attend_row<HD, T, WHOLE>(q, S, LdsSlots{sj, sb}, o, lse, D, K, row, blockDim.x >> 6, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -995,16 +1087,32 @@ hipError_t launch_sparse_csr(const void* q, const void* k, const void* v, const 
   return hipErrorInvalidValue;
 }
 
-static int row_waves(int K) { return K + 1 < kRowWaves ? K + 1 : kRowWaves; }
+// Waves per row of the row kernels: one per slot, at most 8 for K <= 8 and
+// 16 beyond.  The fused selection + decode kernel's registers (about 100 per
+// lane) allow four waves per SIMD, so two rows of eight waves share a compute
+// unit where two rows of nine would not (the wave that takes a second slot
+// costs less than rows waiting for a free unit); the separate decode uses the
+// same count, so that both merge the same partial states in the same order
+// and give identical results.
+static int row_waves(int K) {
+  return K <= 8 ? std::min(K + 1, 8) : std::min(K + 1, kRowWaves);
+}
 
 template <int HD, typename T>
 static hipError_t launch_sparse_t(const void* q, const void* k, const void* v, const int* idx,
                                   const float* bias, void* o, float* lse, int K, const Dims& D,
                                   const StageEvents& E, hipStream_t st) {
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
-  hipLaunchKernelGGL((sparse_row_kernel<HD, T, DenseKV<HD, T>>), dim3((unsigned)rows),
-                     dim3(64 * row_waves(K)), 0, st, (const T*)q,
-                     DenseKV<HD, T>{(const T*)k, (const T*)v}, idx, bias, (T*)o, lse, D, K);
+  const DenseKV<HD, T> S{(const T*)k, (const T*)v};
+  const dim3 grid((unsigned)rows), blk(64 * row_waves(K));
+  bool whole = false;
+  if constexpr (whole_blocks_fit<HD, T>()) whole = D.blk == kBlock;
+  if (whole)
+    hipLaunchKernelGGL((sparse_row_kernel<HD, T, DenseKV<HD, T>, whole_blocks_fit<HD, T>()>),
+                       grid, blk, 0, st, (const T*)q, S, idx, bias, (T*)o, lse, D, K);
+  else
+    hipLaunchKernelGGL((sparse_row_kernel<HD, T, DenseKV<HD, T>, false>), grid, blk, 0, st,
+                       (const T*)q, S, idx, bias, (T*)o, lse, D, K);
   E.record(0, st);
   return hipGetLastError();
 }
@@ -1046,7 +1154,9 @@ static hipError_t launch_paged_t(const void* q, const void* k_pool, const void* 
                                  const float* bias, void* o, float* lse, int K, const Dims& D,
                                  hipStream_t st) {
   const size_t rows = (size_t)D.batch * D.hq;
-  hipLaunchKernelGGL((sparse_row_kernel<HD, T, PagedKV<HD, T>>), dim3((unsigned)rows),
+  // pages hold whole 64-key blocks
+  hipLaunchKernelGGL((sparse_row_kernel<HD, T, PagedKV<HD, T>, whole_blocks_fit<HD, T>()>),
+                     dim3((unsigned)rows),
                      dim3(64 * row_waves(K)), 0, st, (const T*)q,
                      PagedKV<HD, T>{(const T*)k_pool, (const T*)v_pool, table, lens, pages}, idx,
                      bias, (T*)o, lse, D, K);
@@ -1084,12 +1194,20 @@ static hipError_t launch_topk_row_t(const void* q, Src S, const void* qs, Sel SS
                                     int renorm, int* idx, float* bias, void* o, float* lse,
                                     const Dims& D, size_t rows, hipStream_t st) {
   const dim3 grid((unsigned)rows), blk(64 * row_waves(K));
-  if (K <= 8)
-    hipLaunchKernelGGL((topk_row_kernel<HD, T, DS, 8, Sel, Src>), grid, blk, 0, st, (const T*)q,
-                       S, (const T*)qs, SS, K, renorm, idx, bias, (T*)o, lse, D);
+  constexpr bool W = whole_blocks_fit<HD, T>();
+  const bool whole = W && D.blk == kBlock;
+  if (K <= 8 && whole)
+    hipLaunchKernelGGL((topk_row_kernel<HD, T, DS, 8, Sel, Src, W>), grid, blk, 0, st,
+                       (const T*)q, S, (const T*)qs, SS, K, renorm, idx, bias, (T*)o, lse, D);
+  else if (K <= 8)
+    hipLaunchKernelGGL((topk_row_kernel<HD, T, DS, 8, Sel, Src, false>), grid, blk, 0, st,
+                       (const T*)q, S, (const T*)qs, SS, K, renorm, idx, bias, (T*)o, lse, D);
+  else if (whole)
+    hipLaunchKernelGGL((topk_row_kernel<HD, T, DS, 16, Sel, Src, W>), grid, blk, 0, st,
+                       (const T*)q, S, (const T*)qs, SS, K, renorm, idx, bias, (T*)o, lse, D);
   else
-    hipLaunchKernelGGL((topk_row_kernel<HD, T, DS, 16, Sel, Src>), grid, blk, 0, st, (const T*)q,
-                       S, (const T*)qs, SS, K, renorm, idx, bias, (T*)o, lse, D);
+    hipLaunchKernelGGL((topk_row_kernel<HD, T, DS, 16, Sel, Src, false>), grid, blk, 0, st,
+                       (const T*)q, S, (const T*)qs, SS, K, renorm, idx, bias, (T*)o, lse, D);
   return hipGetLastError();
 }
 
