@@ -177,7 +177,7 @@ template <int HD, typename T, bool WHOLE, typename Src, typename Slots>
 __device__ __forceinline__ void attend_row(const T* __restrict__ q, const Src& S,
                                            const Slots& SL, T* __restrict__ o,
                                            float* __restrict__ lse, const Dims& D, int K,
-                                           size_t row, int W, RowLds<HD>& L) {
+                                           size_t row, int W, RowLds<HD>& L, bool early) {
   constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane and load
   constexpr int LPK = HD / EPL;             // lanes per key row
   constexpr int KPI = 64 / LPK;             // key rows per load instruction
@@ -203,11 +203,25 @@ __device__ __forceinline__ void attend_row(const T* __restrict__ q, const Src& S
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
   float* const pw = L.ps[wave];
-  for (int slot = wave; t >= 0 && slot <= K; slot += W) {
+  // The last wave takes the current block (slot K) first; historical slot s
+  // goes to wave s % W, in ascending order.  early (fused selection): the
+  // slots are published by a barrier that each wave passes exactly once,
+  // before its first historical slot or after its last slot, so the wave of
+  // the current block attends it while wave 0 is still selecting.
+  const bool has_cur = wave == W - 1;
+  const int n_hist = wave < K ? (K - 1 - wave) / W + 1 : 0;
+  const int n_slots = t >= 0 ? n_hist + (has_cur ? 1 : 0) : 0;
+  bool synced = !early;
+  for (int n = 0; n < n_slots; ++n) {
+    const bool cur = has_cur && n == 0;
     int j;
     float add;
-    if (slot < K) {
-      SL.get(row, K, slot, &j, &add);
+    if (!cur) {
+      if (!synced) {  // wave-uniform
+        __syncthreads();
+        synced = true;
+      }
+      SL.get(row, K, wave + (n - (has_cur ? 1 : 0)) * W, &j, &add);
       if (j < 0 || j >= c) continue;  // not a historical block: skipped, never read
     } else {
       j = c;
@@ -256,6 +270,7 @@ __device__ __forceinline__ void attend_row(const T* __restrict__ q, const Src& S
     }
     __builtin_amdgcn_wave_barrier();
   }
+  if (!synced) __syncthreads();
   // sum this wave's P V over its key groups, then merge the waves
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = stride_sum<LPK>(acc[e]);
@@ -319,7 +334,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void sparse_row_kernel(
     T* __restrict__ o, float* __restrict__ lse, Dims D, int K) {
   __shared__ RowLds<HD> L;
   attend_row<HD, T, WHOLE>(q, S, GlobalSlots{idx, bias}, o, lse, D, K,
-                           xcd_row(blockIdx.x, gridDim.x), blockDim.x >> 6, L);
+                           xcd_row(blockIdx.x, gridDim.x), blockDim.x >> 6, L, false);
 }
 
 // Slots of a row chosen in the same workgroup (LDS).
@@ -335,8 +350,10 @@ struct LdsSlots {
 // Selection and attention of a row in one workgroup (decode): wave 0 picks
 // the row's K <= KM blocks (wave_best_entry, the routine sas_topk_blocks and
 // sas_paged_topk use for few rows) into LDS and optionally writes idx / bias;
-// then every wave attends its slots as the row kernel does.  One launch, and
-// no round trip of the selection through global memory.  (Splitting the
+// then every wave attends its slots as the row kernel does, the wave of the
+// current block (which needs no selection) starting on it while wave 0
+// selects.  One launch, and no round trip of the selection through global
+// memory.  (Splitting the
 // scoring over all the row's waves and merging their lists in LDS was
 // slower: the selection is not what bounds this kernel.)
 template <int HD, typename T, int DS, int KM, typename Sel, typename Src, bool WHOLE>
@@ -362,8 +379,8 @@ __global__ __launch_bounds__(64 * kRowWaves) void topk_row_kernel(
       if (bias) bias[row * K + lane] = bs;
     }
   }
-  __syncthreads();
-  attend_row<HD, T, WHOLE>(q, S, LdsSlots{sj, sb}, o, lse, D, K, row, blockDim.x >> 6, L);
+  // attend_row's first barrier publishes the selection
+  attend_row<HD, T, WHOLE>(q, S, LdsSlots{sj, sb}, o, lse, D, K, row, blockDim.x >> 6, L, true);
 }
 
 // ---------------------------------------------------------------------------
