@@ -15,15 +15,17 @@
 // kernel (one `fill` flag, uniform per launch), so the predicate is evaluated
 // by the same instructions and the counts always match the entries.
 //
-// One lane per row, the 64 rows of a wave consecutive positions of one
-// (batch, head) as in the gate kernel: every ks row is a wave-uniform load,
-// scores (packed bf16 dot products, log2 units) are recomputed per pass: the
+// bf16 selectors (thr_mfma_kernel): the scores of 32 rows x 64 units come
+// from matrix products, as in the gate kernel, recomputed per pass: the
 // normaliser in one online pass, then the count, or the (renormalised) bias
-// and the entries.
+// and the entries.  fp32 selectors (thr_kernel): one lane per row, the 64
+// rows of a wave consecutive positions of one (batch, head), every ks row a
+// wave-uniform load, the same passes with per-lane dot products.
 #include "sas_device.h"
 #include "sas_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace sas {
 
@@ -111,6 +113,201 @@ __global__ __launch_bounds__(256) void thr_kernel(const ST* __restrict__ qs,
   }
 }
 
+// bf16 selectors: the same passes with the scores on the matrix cores, as
+// the gate kernel forms lam.  A workgroup of 8 waves takes 256 consecutive
+// rows of one (b, h), 32 rows per wave; tiles of 64 ks rows go global ->
+// registers -> LDS one tile ahead; Z^T = KS QS^T on 32x32x16 MFMA leaves 32
+// units of a row's tile in each lane (the other 32 in lane l ^ 32).  Pass 1:
+// lam, an online log-sum-exp whose running max moves only when it grows by
+// more than 8 (log2 units).  Then the count, or (renorm: one more pass for
+// the kept units' log-sum-exp) the entries: each tile's kept units form a
+// 64-bit mask that the two lane halves share, and a lane writes a kept unit
+// at the row's running position plus the unit's rank in the mask.  Every
+// pass runs the same products in the same order, so the count and fill
+// launches take the same decisions.
+constexpr int kThrRows = 256;
+
+// (Four waves per SIMD, i.e. two workgroups per compute unit, for ds <= 32:
+// 126 registers and no spills; ds = 64 would spill and keeps three.)
+template <int DS>
+__global__ __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(DS <= 32 ? 4 : 3))) void thr_mfma_kernel(const bf16* __restrict__ qs,
+                                                       const bf16* __restrict__ ks, float theta,
+                                                       int renorm, int fill,
+                                                       long long* __restrict__ row_ptr,
+                                                       int* __restrict__ col,
+                                                       float* __restrict__ bias, long long nnz,
+                                                       Dims D) {
+  constexpr int XP = DS + 8;  // LDS row pitch (elements)
+  constexpr int CH = DS / 8;  // 16-byte chunks per ks row
+  constexpr int NL = 64 * CH; // chunks per tile (<= 512 threads)
+  __shared__ __align__(16) bf16 X0[64 * XP];
+  __shared__ __align__(16) bf16 X1[64 * XP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int r0 = blockIdx.x * kThrRows;
+  const int qi = r0 + wave * 32 + l32;
+  const bool valid = qi < D.tq;
+  const int qc = min(qi, D.tq - 1);
+  const int c = (D.qoff + qc) / D.blk;  // historical units of the row
+  const int cw = (D.qoff + min(r0 + wave * 32 + 31, D.tq - 1)) / D.blk;  // wave max of c
+  const int cg = (D.qoff + min(r0 + kThrRows - 1, D.tq - 1)) / D.blk;    // workgroup max
+  const int ntiles = (cg + 63) / 64;
+  const size_t row = ((size_t)b * D.hq + h) * D.tq + qc;
+  bf16x8 qf[DS / 16];
+#pragma unroll
+  for (int s = 0; s < DS / 16; ++s) qf[s] = *(const bf16x8*)(qs + row * DS + 16 * s + 8 * hh);
+  const bf16* ksb = ks + ((size_t)b * D.hks + h / D.hps) * (size_t)D.nb * DS;
+  const float zs = D.sel_scale * kLog2e;  // scores in log2 units
+  bf16x8 reg = bf16x8{};
+  auto gload = [&](int j) {
+    const int u = 64 * j + tid / CH;
+    if (tid < NL) reg = u < D.nb ? *(const bf16x8*)(ksb + (size_t)u * DS + (tid % CH) * 8)
+                                 : bf16x8{};
+  };
+  auto sstore = [&](bf16* Xd) {
+    if (tid < NL) *(bf16x8*)&Xd[(tid / CH) * XP + (tid % CH) * 8] = reg;
+  };
+  // unit of register r of M-tile mt in tile j, this lane half
+  auto unit = [&](int j, int mt, int r) { return 64 * j + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4); };
+  // One pass over the workgroup's tiles: fn(j, z) with z the log2-domain
+  // scores of this lane's units of tile j (waves whose rows have no unit in
+  // the tile skip it; every wave meets every barrier)
+  auto pass = [&](auto&& fn) {
+    if (ntiles > 0) {
+      gload(0);
+      sstore(X0);
+    }
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+      const bf16* Xs = (j & 1) ? X1 : X0;
+      if (j + 1 < ntiles) gload(j + 1);
+      if (64 * j < cw) {
+        f32x16 z[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int s = 0; s < DS / 16; ++s)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            z[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *(const bf16x8*)&Xs[(32 * mt + l32) * XP + 16 * s + 8 * hh], qf[s], z[mt], 0, 0,
+                0);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z[mt][r] *= zs;
+        fn(j, z);
+      }
+      if (j + 1 < ntiles) sstore((j & 1) ? X0 : X1);
+      __syncthreads();
+    }
+  };
+  // pass 1: lam2 = m + log2 sum 2^(z - m) over the row's units u < c
+  float m_run = -INFINITY, s_run = 0.f;
+  pass([&](int j, const f32x16 (&z)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (unit(j, mt, r) < c) mx = fmaxf(mx, z[mt][r]);
+    mx = halves_max(mx);
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      if (m_new > -INFINITY) {
+        s_run *= exp2_raw(m_run - m_new);
+        m_run = m_new;
+      }
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (unit(j, mt, r) < c) ps += exp2_raw(z[mt][r] - m_run);
+    s_run += m_run > -INFINITY ? ps : 0.f;
+  });
+  s_run = halves_sum(s_run);
+  const float lam2 = c > 0 ? m_run + log2f(s_run) : -INFINITY;
+  const float lt2 = theta > 0.f ? log2f(theta) : -INFINITY;
+  auto keep = [&](int u, float z) __attribute__((always_inline)) {
+    return u < c && (theta <= 0.f || z - lam2 >= lt2);
+  };
+  if (!fill) {
+    float n = 0.f;  // exact: at most nb < 2^24
+    pass([&](int j, const f32x16 (&z)[2]) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) n += keep(unit(j, mt, r), z[mt][r]) ? 1.f : 0.f;
+    });
+    n = halves_sum(n);
+    if (valid && hh == 0) {
+      row_ptr[row + 1] = (long long)n;
+      if (row == 0) row_ptr[0] = 0;
+    }
+    return;
+  }
+  float norm2 = lam2;
+  if (renorm) {
+    float sk = 0.f;
+    pass([&](int j, const f32x16 (&z)[2]) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (keep(unit(j, mt, r), z[mt][r])) sk += exp2_raw(z[mt][r] - m_run);
+    });
+    sk = halves_sum(sk);
+    norm2 = sk > 0.f ? m_run + log2f(sk) : -INFINITY;
+  }
+  // this row's entries: [row_ptr[row], row_ptr[row + 1]) clamped to [0, nnz)
+  // (at most nb of them); padding rows write nothing
+  const long long p0 = min(max(row_ptr[row], 0LL), nnz);
+  const long long e = valid ? max(p0, min(row_ptr[row + 1], nnz)) : p0;
+  int* cp = col + p0;
+  float* bp = bias + p0;
+  int room = (int)min(e - p0, (long long)D.nb);
+  pass([&](int j, const f32x16 (&z)[2]) {
+    // keep bits in register order (bit 4 n + i: register 4 (n % 4) + i of
+    // M-tile n / 4, unit 8 n + 4 hh + i of the tile), then in unit order:
+    // nibble n moves to bits 8 n .. 8 n + 3, and up by 4 in the upper half
+    unsigned kb = 0u;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        kb |= keep(unit(j, mt, r), z[mt][r]) ? 1u << (16 * mt + r) : 0u;
+    unsigned long long y = kb;
+    y = (y | (y << 16)) & 0x0000FFFF0000FFFFull;
+    y = (y | (y << 8)) & 0x00FF00FF00FF00FFull;
+    y = (y | (y << 4)) & 0x0F0F0F0F0F0F0F0Full;
+    const unsigned long long mine = hh ? y << 4 : y;
+    const unsigned long long all = mine | lane_xor_u64<32>(mine, lane);
+    // a kept unit's entry: the row's running position plus its rank in the
+    // tile (the units of the bytes below, the lower half's nibble of its own
+    // byte when hh = 1, its own nibble's bits below it)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const unsigned nib = (kb >> (4 * n)) & 15u;
+      const int base = __builtin_popcountll(all & ((1ull << (8 * n)) - 1ull)) +
+                       (hh ? __builtin_popcount((unsigned)(all >> (8 * n)) & 15u) : 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int off = base + __builtin_popcount(nib & ((1u << i) - 1u));
+        if (((nib >> i) & 1u) && off < room) {
+          cp[off] = 64 * j + 8 * n + 4 * hh + i;
+          bp[off] = (z[n / 4][4 * (n % 4) + i] - norm2) * kLn2;
+        }
+      }
+    }
+    const int nt = __builtin_popcountll(all);
+    cp += nt;
+    bp += nt;
+    room -= nt;
+  });
+}
+
 // In-place inclusive scan of a[0 .. n-1] (int64): per-workgroup scans of
 // kScanTile elements, an exclusive scan of the tile totals, then the offsets.
 constexpr int kScanTile = 4096;  // 1024 threads x 4
@@ -183,9 +380,14 @@ template <int DS, typename ST>
 static hipError_t launch_thr_t(const void* qs, const void* ks, float theta, int renorm, int fill,
                                long long* row_ptr, int* col, float* bias, long long nnz,
                                char* ws, const Dims& D, hipStream_t st) {
-  const dim3 grid((D.tq + 255) / 256, D.hq, D.batch);
-  hipLaunchKernelGGL((thr_kernel<DS, ST>), grid, dim3(256), 0, st, (const ST*)qs, (const ST*)ks,
-                     theta, renorm, fill, row_ptr, col, bias, nnz, D);
+  if (std::is_same<ST, bf16>::value)
+    hipLaunchKernelGGL((thr_mfma_kernel<DS>), dim3((D.tq + kThrRows - 1) / kThrRows, D.hq, D.batch),
+                       dim3(512), 0, st, (const bf16*)qs, (const bf16*)ks, theta, renorm, fill,
+                       row_ptr, col, bias, nnz, D);
+  else
+    hipLaunchKernelGGL((thr_kernel<DS, ST>), dim3((D.tq + 255) / 256, D.hq, D.batch), dim3(256), 0,
+                       st, (const ST*)qs, (const ST*)ks, theta, renorm, fill, row_ptr, col, bias,
+                       nnz, D);
   if (fill) return hipGetLastError();
   const size_t rows = (size_t)D.batch * D.hq * D.tq;
   const int nt = (int)((rows + kScanTile - 1) / kScanTile);
