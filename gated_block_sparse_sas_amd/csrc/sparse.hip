@@ -70,7 +70,8 @@ struct PagedKV {
 
 // Row kernel (decode, and prefill with units below 64 tokens): one workgroup
 // per query row, W = min(K + 1, 8) waves for K <= 8, else min(K + 1, 16);
-// wave w takes slots w, w + W, ... (slot K is the current block).  K and V rows are read with 16-byte loads,
+// the last wave takes the current block (slot K) first, wave w the listed
+// slots w, w + W, ...  K and V rows are read with 16-byte loads,
 // LPK lanes per key row (a key row of d elements is LPK * 16 bytes), so one
 // load instruction covers KPI = 64 / LPK whole consecutive rows.  A lane's
 // partial dot product is summed over the key's LPK lanes; scores go through

@@ -131,13 +131,10 @@ constexpr int kThrRows = 256;
 // 126 registers and no spills; ds = 64 would spill and keeps three.)
 template <int DS>
 __global__ __launch_bounds__(512)
-__attribute__((amdgpu_waves_per_eu(DS <= 32 ? 4 : 3))) void thr_mfma_kernel(const bf16* __restrict__ qs,
-                                                       const bf16* __restrict__ ks, float theta,
-                                                       int renorm, int fill,
-                                                       long long* __restrict__ row_ptr,
-                                                       int* __restrict__ col,
-                                                       float* __restrict__ bias, long long nnz,
-                                                       Dims D) {
+__attribute__((amdgpu_waves_per_eu(DS <= 32 ? 4 : 3))) void thr_mfma_kernel(
+    const bf16* __restrict__ qs, const bf16* __restrict__ ks, float theta, int renorm, int fill,
+    long long* __restrict__ row_ptr, int* __restrict__ col, float* __restrict__ bias,
+    long long nnz, Dims D) {
   constexpr int XP = DS + 8;  // LDS row pitch (elements)
   constexpr int CH = DS / 8;  // 16-byte chunks per ks row
   constexpr int NL = 64 * CH; // chunks per tile (<= 512 threads)
@@ -170,7 +167,9 @@ __attribute__((amdgpu_waves_per_eu(DS <= 32 ? 4 : 3))) void thr_mfma_kernel(cons
     if (tid < NL) *(bf16x8*)&Xd[(tid / CH) * XP + (tid % CH) * 8] = reg;
   };
   // unit of register r of M-tile mt in tile j, this lane half
-  auto unit = [&](int j, int mt, int r) { return 64 * j + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4); };
+  auto unit = [&](int j, int mt, int r) {
+    return 64 * j + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
+  };
   // One pass over the workgroup's tiles: fn(j, z) with z the log2-domain
   // scores of this lane's units of tile j (waves whose rows have no unit in
   // the tile skip it; every wave meets every barrier)
@@ -381,9 +380,10 @@ static hipError_t launch_thr_t(const void* qs, const void* ks, float theta, int 
                                long long* row_ptr, int* col, float* bias, long long nnz,
                                char* ws, const Dims& D, hipStream_t st) {
   if (std::is_same<ST, bf16>::value)
-    hipLaunchKernelGGL((thr_mfma_kernel<DS>), dim3((D.tq + kThrRows - 1) / kThrRows, D.hq, D.batch),
-                       dim3(512), 0, st, (const bf16*)qs, (const bf16*)ks, theta, renorm, fill,
-                       row_ptr, col, bias, nnz, D);
+    hipLaunchKernelGGL((thr_mfma_kernel<DS>),
+                       dim3((D.tq + kThrRows - 1) / kThrRows, D.hq, D.batch), dim3(512), 0, st,
+                       (const bf16*)qs, (const bf16*)ks, theta, renorm, fill, row_ptr, col, bias,
+                       nnz, D);
   else
     hipLaunchKernelGGL((thr_kernel<DS, ST>), dim3((D.tq + 255) / 256, D.hq, D.batch), dim3(256), 0,
                        st, (const ST*)qs, (const ST*)ks, theta, renorm, fill, row_ptr, col, bias,
