@@ -57,6 +57,11 @@ SMALL = {
     "prefill_1088": W["prefill_32k_theta"].with_(batch=2, hq=4, hkv=2, tq=1088, tk=1088),
     "chunk_q": W["prefill_32k_theta"].with_(batch=1, hq=8, hkv=2, tq=300, tk=2048),
     "decode": W["prefill_32k_theta"].with_(batch=3, hq=8, hkv=2, tq=1, tk=4096),
+    # the other selector widths of the matrix-core selection: ds 16 with a
+    # query offset, ds 64 with selector keys per query head (a ragged last
+    # 256-row workgroup in both)
+    "ds16_q504": W["prefill_32k_theta"].with_(batch=1, hq=4, hkv=2, tq=520, tk=1024, ds=16),
+    "ds64_hks": W["prefill_32k_theta"].with_(batch=1, hq=4, hkv=2, tq=640, tk=640, ds=64, hks=4),
 }
 
 
