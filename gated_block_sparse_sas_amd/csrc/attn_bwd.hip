@@ -1649,18 +1649,25 @@ __global__ __launch_bounds__(256) void dks_kernel(const float* __restrict__ dz,
   for (int nt = 0; nt < NT; ++nt) dacc[nt] = f32x16{};
   constexpr int U = 8;  // row pairs whose loads are in flight together
   for (int i = istart + 2 * wave; i < iend; i += 8 * U) {
+    // loads without branches (row, block and dim clamped into range, the
+    // values past the ends masked to 0), so that all of them are in flight
+    // together
     float a[U], bq[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ii = i + 8 * u + rsub;
       const bool ok = ii < iend;
-      a[u] = ok && blk < D.nb ? dz[(hrow + ii) * D.nb + blk] : 0.f;
+      const size_t ri = hrow + (size_t)min(ii, iend - 1);
+      const float zv = dz[ri * D.nb + min(blk, D.nb - 1)];
+      a[u] = ok && blk < D.nb ? zv : 0.f;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int dim = 32 * nt + (lane & 31);
-        bq[u][nt] = ok && dim < DS ? to_f32(qs[(hrow + ii) * DS + dim]) : 0.f;
+        const float qv = to_f32(qs[ri * DS + min(dim, DS - 1)]);
+        bq[u][nt] = ok && dim < DS ? qv : 0.f;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of the products
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -1711,27 +1718,29 @@ __global__ __launch_bounds__(256) void dks4_kernel(const float* __restrict__ dz,
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) dacc[q][nt] = f32x16{};
-  constexpr int U = 4;  // row pairs whose loads are in flight together
+  constexpr int U = 8;  // row pairs whose loads are in flight together
   for (int i = istart + 2 * wave; i < iend; i += 8 * U) {
+    // loads without branches (row and dim clamped into range, the values
+    // past the ends masked to 0), so that all of them are in flight together;
+    // with nb % 4 == 0 a lane's four blocks all exist or none does
     f32x4 a[U];
     float bq[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ii = i + 8 * u + rsub;
-      const bool ok = ii < iend;
-      const float* zr = dz + (hrow + ii) * D.nb + jl;
-      if (ok && jl + 3 < D.nb) {
-        a[u] = *(const f32x4*)zr;
-      } else {
+      const bool ok = ii < iend && jl < D.nb;
+      const size_t ri = hrow + (size_t)min(ii, iend - 1);
+      const f32x4 zv = *(const f32x4*)(dz + ri * D.nb + min(jl, D.nb - 4));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a[u][q] = ok && jl + q < D.nb ? zr[q] : 0.f;
-      }
+      for (int q = 0; q < 4; ++q) a[u][q] = ok ? zv[q] : 0.f;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int dim = 32 * nt + (lane & 31);
-        bq[u][nt] = ok && dim < DS ? to_f32(qs[(hrow + ii) * DS + dim]) : 0.f;
+        const float qv = to_f32(qs[ri * DS + min(dim, DS - 1)]);
+        bq[u][nt] = ii < iend && dim < DS ? qv : 0.f;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of the products
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll

@@ -242,8 +242,11 @@ __device__ __forceinline__ float sel_dot(const float* qsv, const ST* ksrow) {
 // A query's selector row held in registers for scoring many ks rows: bf16
 // rows as bf16 pairs, scored with packed bf16 dot products (each pair of
 // products exact, the chain summed in fp32 in index order); f32 rows with
-// sel_dot.  The gate, threshold and top-K kernels all score with it, so a
-// block's score is the same number whichever of them computes it.
+// sel_dot.  The row-wise selection kernels (the wave-per-row top-K and the
+// fused decode) and the fp32 paths score with it; the matrix-core kernels
+// (the bf16 gate normaliser, threshold selection and tiled top-K) sum the
+// same exact bf16 products on MFMA in an order of their own, so their fp32
+// scores may differ from these in the last bits.
 template <int DS, typename ST>
 struct SelQ {
   float v[DS];

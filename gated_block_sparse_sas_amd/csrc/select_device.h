@@ -53,6 +53,44 @@ struct PagedSel {
   }
 };
 
+// A selector key row held in registers, loaded ahead of its dot product
+// (16-byte loads), scored with exactly the operations of SelQ::dot in the
+// same order, so the score is the same number.
+template <int DS, typename ST>
+struct KsRow;
+template <int DS>
+struct KsRow<DS, bf16> {
+  bf16x8 x[DS / 8];
+  __device__ __forceinline__ void load(const bf16* p) {
+#pragma unroll
+    for (int c = 0; c < DS / 8; ++c) x[c] = *(const bf16x8*)(p + 8 * c);
+  }
+  __device__ __forceinline__ float dot(const SelQ<DS, bf16>& q) const {
+    typedef __bf16 pair_t __attribute__((ext_vector_type(2)));
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < DS / 2; ++e) {
+      const pair_t pr = {x[e / 4][2 * (e % 4)], x[e / 4][2 * (e % 4) + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(q.v[e], pr, acc, false);
+    }
+    return acc;
+  }
+};
+template <int DS>
+struct KsRow<DS, float> {
+  f32x4 x[DS / 4];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int c = 0; c < DS / 4; ++c) x[c] = *(const f32x4*)(p + 4 * c);
+  }
+  __device__ __forceinline__ float dot(const SelQ<DS, float>& q) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) acc = fmaf(q.v[e], x[e / 4][e % 4], acc);
+    return acc;
+  }
+};
+
 // Order-preserving 32-bit key of a score (larger z, larger key; -0 counts as
 // +0, as in a floating-point comparison), and the selection order on (key,
 // block): key descending, then block ascending.
@@ -143,9 +181,13 @@ __device__ __forceinline__ void wave_best(const ST* __restrict__ qs, const Sel& 
         kr[kk] = S.ks_row_readable(D, b, h, j < c ? j : c - 1, &own[kk]);
         own[kk] = own[kk] && j < c;
       }
+      KsRow<DS, ST> rv[RIF];
+#pragma unroll
+      for (int kk = 0; kk < RIF; ++kk) rv[kk].load(kr[kk]);
+      __builtin_amdgcn_sched_barrier(0);  // the group's loads before its products
 #pragma unroll
       for (int kk = 0; kk < RIF; ++kk) {
-        const float z = D.sel_scale * qsv.dot(kr[kk]);
+        const float z = D.sel_scale * rv[kk].dot(qsv);
         zz[k4 + kk] = own[kk] ? z : -INFINITY;
       }
       __builtin_amdgcn_sched_barrier(0);

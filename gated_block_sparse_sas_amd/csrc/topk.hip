@@ -12,8 +12,11 @@
 // best blocks in registers for many rows and K <= 32 (topk_lane_kernel), a
 // wave per row with an LDS radix select for budgets and K >= 16 otherwise
 // (topk_select_kernel), and the wave-per-row kernel below for the rest.  All
-// rank the same fp32 scores (SelQ: packed bf16 products for bf16 inputs, as
-// in the gate kernel) in the same order, so they pick the same blocks.
+// rank on (score descending, block ascending); the scores are fp32 sums of
+// the exact bf16 products, from packed dot products (SelQ) or from MFMA
+// tiles, so kernels agree on every row whose scores are apart by more than
+// the last bits of fp32, and within one kernel exactly equal scores (ties)
+// always go to the smaller block.
 //
 // Wave per row: the row's scores are computed once into LDS (lane j % 64
 // owns block j), lam comes from a wave max + sum, then K rounds each pick the
