@@ -65,6 +65,12 @@ SMALL = {
     "units16": W["decode_64k_top8"].with_(batch=2, tk=4096, block=16, topk=16),
     "d64": W["decode_64k_top8"].with_(batch=2, tk=2048, d=64, ds=16, topk=5),
     "rows5": W["decode_64k_top8"].with_(batch=1, tq=5, tk=1024, topk=6),
+    # wave counts around the slot assignment of the row kernels: K = 7 (the
+    # last of 8 waves holds only the current block), K = 9 (10 waves) and
+    # K = 16 (16 waves, the last one taking the current block and slot 15)
+    "k7": W["decode_64k_top8"].with_(batch=2, tk=4096, topk=7),
+    "k9": W["decode_64k_top8"].with_(batch=2, tk=4096, topk=9),
+    "k16": W["decode_64k_top8"].with_(batch=2, tk=4096, topk=16),
 }
 
 
